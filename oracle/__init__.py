@@ -1,0 +1,47 @@
+"""CPU oracle for the Q4_K / Q4_0 x Q8_1 GEMV path -- TEST INFRASTRUCTURE ONLY.
+
+A plain, slow statement of what the path computes, written from the realizar
+source pages (docs.rs, realizar 0.8.4/0.8.5):
+
+* ``src/cuda/executor/cached.rs``, ``transformer_layer_gpu_true_dp4a``: the
+  normed activation is quantized to Q8_1 once (step 2) and shared by the Q, K and
+  V projections, which are Q4_K x Q8_1 integer dot products (step 3); the
+  attention output is requantized before the O projection (steps 5-6); the FFN
+  is the SwiGLU chain on the same integer path (step 9).
+* ``src/gpu/adapters/using.rs``, ``GpuModelQ4::forward`` step 5: the LM head is a
+  Q4_0 GEMV over the fp32 normed hidden state; ``ffn_swiglu_gpu``: gate and up
+  GEMVs, ``silu(gate) * up``, down GEMV.
+* ``src/gguf/cuda/clone_layer_weights.rs``, ``cuda_swiglu_ffn``: SiLU applied to
+  the gate output, then multiplied elementwise by the up output.
+* ``src/cuda/executor/layers/forward_utils.rs``, ``pad_and_upload_input``: the
+  activation is zero-padded to a multiple of the 256-value super-block.
+
+The block formats are not printed on the pages; the GGML layouts the pages name
+(Q4_K super-blocks of 256 values, type id 12; Q4_0; Q8_1) are read as written in
+each module's docstring.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
+this package.  The product path never calls it.
+
+Parity pins: every function here is pinned by the ``-m "not gpu"`` tests against
+hand-worked blocks (``tests/golden/``), closed forms, exact-integer cases and the
+dequantize-then-dot identity.
+"""
+from .q8_1 import (QK8_1, Q8_1_BLOCK_BYTES, quantize_q8_1, q8_1_to_bytes,
+                   q8_1_from_bytes, dequantize_q8_1, Q8Blocks)
+from .q4k import (q4k_fields, q4k_unpack_scales, dequantize_q4k,
+                  gemv_q4k_q8_def, gemv_q4k_q8_int)
+from .q4_0 import (q4_0_fields, dequantize_q4_0, gemv_q4_0_f32,
+                   gemv_q4_0_q8_int)
+from .swiglu import silu, silu_grad, swiglu, ffn_swiglu_q4k, h_tolerance
+from .tolerance import gemv_tolerance, GEMV_REL, GEMV_ABS
+
+__all__ = [
+    "QK8_1", "Q8_1_BLOCK_BYTES", "quantize_q8_1", "q8_1_to_bytes", "q8_1_from_bytes",
+    "dequantize_q8_1", "Q8Blocks",
+    "q4k_fields", "q4k_unpack_scales", "dequantize_q4k", "gemv_q4k_q8_def",
+    "gemv_q4k_q8_int",
+    "q4_0_fields", "dequantize_q4_0", "gemv_q4_0_f32", "gemv_q4_0_q8_int",
+    "silu", "silu_grad", "swiglu", "ffn_swiglu_q4k", "h_tolerance",
+    "gemv_tolerance", "GEMV_REL", "GEMV_ABS",
+]

@@ -1,0 +1,381 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself:
+hand-worked blocks (tests/golden/), closed forms, exact-integer cases, the
+dequantize-then-dot identity, padding invariance and symmetry properties.
+
+A plausible slip in the oracle -- a wrong nibble order, 6-bit unpack, rounding
+mode, dropped min term, sign or transposed operand -- fails at least one test.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from golden_io import floats, hexbytes, ints, load, pairs
+
+U32 = 2.0 ** -24   # fp32 unit roundoff
+
+
+# ----------------------------------------------------------------- helpers
+def _q8_block_input(fx, key):
+    x = np.zeros(32, np.float32)
+    vals = floats(fx[key + ".x"])
+    x[:len(vals)] = vals
+    return x
+
+
+def _ones_q8(nblocks):
+    return oracle.Q8Blocks(np.ones(nblocks, np.float32), np.full(nblocks, 32.0, np.float32),
+                           np.ones((nblocks, 32), np.int8))
+
+
+def _onehot_q8(nblocks, k):
+    d = np.zeros(nblocks, np.float32)
+    s = np.zeros(nblocks, np.float32)
+    q = np.zeros((nblocks, 32), np.int8)
+    d[k // 32] = 1.0
+    s[k // 32] = 1.0
+    q[k // 32, k % 32] = 1
+    return oracle.Q8Blocks(d, s, q)
+
+
+def _pack_uniform_scales(S, M):
+    """12 scale bytes with every 6-bit scale = S and every min = M (the test's own
+    encoding of the packing read in q4k_superblock.txt)."""
+    lo_s = (S & 63) | ((S >> 4) << 6)
+    lo_m = (M & 63) | ((M >> 4) << 6)
+    hi = (S & 15) | ((M & 15) << 4)
+    return bytes([lo_s] * 4 + [lo_m] * 4 + [hi] * 4)
+
+
+def _f16le(v):
+    return np.array([v], np.float16).tobytes()
+
+
+# ----------------------------------------------------------------- Q8_1
+@pytest.mark.parametrize("key", ["A", "B", "C", "D"])
+def test_q8_1_hand_worked_blocks(key):
+    fx = load("q8_1_blocks.txt")
+    blk = oracle.quantize_q8_1(_q8_block_input(fx, key))
+    q_exp = np.zeros(32, np.int64)
+    qv = ints(fx[key + ".q"])
+    q_exp[:len(qv)] = qv
+    assert blk.d[0] == np.float32(float(fx[key + ".d"]))
+    assert blk.s[0] == np.float32(float(fx[key + ".s"]))
+    assert np.array_equal(blk.q[0].astype(np.int64), q_exp)
+
+
+def test_q8_1_bytes_layout():
+    fx = load("q8_1_blocks.txt")
+    raw = oracle.q8_1_to_bytes(oracle.quantize_q8_1(_q8_block_input(fx, "B")))
+    assert raw.shape == (1, 40)
+    assert raw[0, 0:4].tobytes() == np.float32(0.25).tobytes()
+    assert raw[0, 4:8].tobytes() == np.float32(32.25).tobytes()
+    assert raw[0, 8] == 127 and raw[0, 11] == 0xFE  # -2 as int8
+    back = oracle.q8_1_from_bytes(raw)
+    assert back.d[0] == np.float32(0.25) and back.q[0, 4] == -4
+
+
+def test_q8_1_padding_tail_is_zero_blocks():
+    x = synth.activation(synth.rng(0, 0), 896)
+    blk = oracle.quantize_q8_1(x, 1024)
+    assert blk.n_blocks == 32
+    assert np.all(blk.d[28:] == 0) and np.all(blk.s[28:] == 0) and np.all(blk.q[28:] == 0)
+    same = oracle.quantize_q8_1(np.concatenate([x, np.zeros(128, np.float32)]), 1024)
+    assert np.array_equal(oracle.q8_1_to_bytes(blk), oracle.q8_1_to_bytes(same))
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_q8_1_properties(seed):
+    g = np.random.default_rng(100 + seed)
+    x = (g.standard_normal(32 * 16) * np.exp(g.uniform(-8, 8, 32 * 16))).astype(np.float32)
+    blk = oracle.quantize_q8_1(x)
+    xb = x.reshape(16, 32).astype(np.float64)
+    d = blk.d.astype(np.float64)
+    q = blk.q.astype(np.int64)
+    # codes inside the int8 range, and the largest magnitude maps to +-127
+    assert np.all(np.abs(q) <= 127)
+    amax_idx = np.argmax(np.abs(xb), axis=1)
+    assert np.all(np.abs(q[np.arange(16), amax_idx]) == 127)
+    # d is amax/127 up to one fp32 rounding
+    amax = np.abs(xb).max(axis=1)
+    assert np.all(np.abs(d - amax / 127) <= U32 * amax / 127)
+    # reconstruction error of a nearest rounding: at most d/2 (plus fp32 slack)
+    assert np.all(np.abs(xb - d[:, None] * q) <= d[:, None] * (0.5 + 1e-5))
+    # s is d * sum(q) up to one fp32 rounding
+    exact = d * q.sum(axis=1)
+    assert np.all(np.abs(blk.s - exact) <= U32 * np.abs(exact))
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_q8_1_sign_and_power_of_two_symmetry(seed):
+    x = synth.activation(np.random.default_rng(7 + seed), 256)
+    a = oracle.quantize_q8_1(x)
+    neg = oracle.quantize_q8_1(-x)
+    assert np.array_equal(neg.q, -a.q) and np.array_equal(neg.d, a.d) and np.array_equal(neg.s, -a.s)
+    for k in (-3, 5):
+        sc = oracle.quantize_q8_1((x * np.float32(2.0 ** k)).astype(np.float32))
+        assert np.array_equal(sc.q, a.q)
+        assert np.array_equal(sc.d, (a.d * np.float32(2.0 ** k)).astype(np.float32))
+        assert np.array_equal(sc.s, (a.s * np.float32(2.0 ** k)).astype(np.float32))
+
+
+def test_q8_1_batch_is_per_token():
+    X = synth.activation(synth.rng(4, 0), 256, n_tokens=3)
+    b = oracle.quantize_q8_1(X)
+    for t in range(3):
+        one = oracle.quantize_q8_1(X[t])
+        assert np.array_equal(oracle.q8_1_to_bytes(b.token(t)), oracle.q8_1_to_bytes(one))
+
+
+# ----------------------------------------------------------------- Q4_K
+def _fixture_superblock():
+    fx = load("q4k_superblock.txt")
+    raw = hexbytes(fx["header_hex"]) + hexbytes(fx["qs_fill_hex"]) * 128
+    return fx, np.frombuffer(raw, np.uint8).reshape(1, 1, 144).copy()
+
+
+def test_q4k_hand_worked_superblock():
+    fx, blob = _fixture_superblock()
+    d, dmin, sc, m, q = oracle.q4k_fields(blob)
+    assert d[0, 0] == 1.0 and dmin[0, 0] == 0.5
+    assert sc[0, 0].tolist() == ints(fx["sc"])
+    assert m[0, 0].tolist() == ints(fx["m"])
+    w = oracle.dequantize_q4k(blob).reshape(8, 32)
+    w_sub = floats(fx["w_sub"])
+    for j in range(8):
+        assert np.all(w[j] == w_sub[j])
+    ones = _ones_q8(8)
+    y_int, _ = oracle.gemv_q4k_q8_int(blob, ones)
+    y_def = oracle.gemv_q4k_q8_def(blob, ones)
+    assert y_int[0] == float(fx["y_ones"]) and y_def[0] == float(fx["y_ones"])
+
+
+def test_q4k_hand_worked_nibble_order():
+    fx = load("q4k_nibble_order.txt")
+    raw = bytearray(hexbytes(fx["header_hex"]) + bytes(128))
+    for k, v in pairs(fx["qs_set"], int, lambda s: int(s, 16)):
+        raw[16 + k] = v
+    blob = np.frombuffer(bytes(raw), np.uint8).reshape(1, 1, 144).copy()
+    w = oracle.dequantize_q4k(blob)[0]
+    for idx, val in pairs(fx["w_at"]):
+        assert w[idx] == val, (idx, w[idx], val)
+    x = _onehot_q8(8, 32)
+    assert oracle.gemv_q4k_q8_int(blob, x)[0][0] == float(fx["y_onehot32"])
+    assert oracle.gemv_q4k_q8_def(blob, x)[0] == float(fx["y_onehot32"])
+
+
+@pytest.mark.parametrize("qn,S,M,Q,D", [(3, 5, 9, 7, 0.25), (15, 63, 63, -127, 0.5),
+                                        (0, 40, 17, 100, 2.0), (9, 18, 0, -3, 1.0)])
+def test_q4k_closed_form(qn, S, M, Q, D):
+    """All nibbles qn, all scales S, all mins M, all activation codes Q with scale D:
+    y = n_sub * 32 * Q * D * (d*S*qn - dmin*M)."""
+    d, dmin, nsb = 0.0078125, 0.001953125, 3       # exact fp16 values
+    sb = _f16le(d) + _f16le(dmin) + _pack_uniform_scales(S, M) + bytes([qn | (qn << 4)] * 128)
+    blob = np.frombuffer(sb * nsb, np.uint8).reshape(1, nsb, 144).copy()
+    nb = nsb * 8
+    x = oracle.Q8Blocks(np.full(nb, D, np.float32), np.full(nb, 32 * Q * D, np.float32),
+                        np.full((nb, 32), Q, np.int8))
+    expect = nb * 32 * Q * D * (d * S * qn - dmin * M)
+    y_int, _ = oracle.gemv_q4k_q8_int(blob, x)
+    y_def = oracle.gemv_q4k_q8_def(blob, x)
+    assert y_int[0] == pytest.approx(expect, rel=1e-13, abs=1e-12)
+    assert y_def[0] == pytest.approx(expect, rel=1e-13, abs=1e-12)
+
+
+@pytest.mark.parametrize("out_dim,in_dim,seed", [(1, 256, 0), (3, 512, 1), (65, 256, 2),
+                                                 (257, 1024, 3), (40, 4096, 4)])
+def test_q4k_integer_form_equals_definition(out_dim, in_dim, seed):
+    """Dequantize-then-dot equals the integer formulation; the only gap is the
+    fp32 rounding of s, at most 2**-24 * sum dmin*m*|s| (plus float64 slack)."""
+    blob = synth.q4k_weights(synth.rng(50 + seed, 1), out_dim, in_dim)
+    x = oracle.quantize_q8_1(synth.activation(synth.rng(50 + seed, 0), in_dim))
+    y_int, terms = oracle.gemv_q4k_q8_int(blob, x)
+    y_def = oracle.gemv_q4k_q8_def(blob, x)
+    d, dmin, sc, m, q = oracle.q4k_fields(blob)
+    min_mass = (dmin[..., None] * m * np.abs(x.s.astype(np.float64)).reshape(-1, 8)[None]).sum(axis=(1, 2))
+    assert np.all(np.abs(y_int - y_def) <= U32 * min_mass + 1e-12 * terms)
+
+
+def test_q4k_integer_exact_inputs():
+    """d = dmin = 1, activation scale 1, codes in [-8, 8]: every term is an integer
+    below 2**24, so the int form is exact and equals the definition exactly."""
+    blob = synth.q4k_weights(synth.rng(60, 1), 37, 2048, d_fixed=1.0, dmin_fixed=1.0)
+    g = np.random.default_rng(61)
+    q = g.integers(-8, 9, size=(64, 32)).astype(np.int8)
+    x = oracle.Q8Blocks(np.ones(64, np.float32), q.sum(axis=1).astype(np.float32), q)
+    y_int, _ = oracle.gemv_q4k_q8_int(blob, x)
+    y_def = oracle.gemv_q4k_q8_def(blob, x)
+    assert np.array_equal(y_int, y_def)
+    assert np.all(y_int == np.round(y_int)) and np.all(np.abs(y_int) < 2 ** 24)
+
+
+def test_q4k_padding_invariance():
+    """in_dim 896 padded to 1024: the last super-block's sub-blocks 4..7 meet zero
+    activation blocks, so re-randomising their nibbles and 6-bit fields leaves y
+    unchanged, and y equals the product over the first 896 values only."""
+    n, in_dim, rows = 896, 1024, 64
+    blob = synth.q4k_weights(synth.rng(0, 1), rows, in_dim)
+    x = synth.activation(synth.rng(0, 0), n)
+    xq = oracle.quantize_q8_1(x, in_dim)
+    y, _ = oracle.gemv_q4k_q8_int(blob, xq)
+    g = np.random.default_rng(99)
+    b2 = blob.copy()
+    b2[:, -1, 16 + 64:144] = g.integers(0, 256, (rows, 64), dtype=np.uint8)   # chunks 2,3
+    # keep the low 6 bits of scale bytes 0..7 (sc/m of sub-blocks 0..3); their top
+    # two bits and bytes 8..11 belong to sub-blocks 4..7 only
+    r = g.integers(0, 256, (rows, 12), dtype=np.uint8)
+    b2[:, -1, 4:12] = (blob[:, -1, 4:12] & 63) | (r[:, 0:8] & 0xC0)
+    b2[:, -1, 12:16] = r[:, 8:12]
+    sc0, m0 = oracle.q4k_unpack_scales(blob[:, -1, 4:16])
+    sc1, m1 = oracle.q4k_unpack_scales(b2[:, -1, 4:16])
+    assert np.array_equal(sc0[:, :4], sc1[:, :4]) and np.array_equal(m0[:, :4], m1[:, :4])
+    assert not np.array_equal(sc0[:, 4:], sc1[:, 4:])
+    y2, _ = oracle.gemv_q4k_q8_int(b2, xq)
+    assert np.array_equal(y, y2)
+    w = oracle.dequantize_q4k(blob)[:, :n]
+    xh = oracle.dequantize_q8_1(xq)[:n]
+    assert np.allclose(y, w @ xh, rtol=0, atol=1e-9 * np.abs(w).sum())
+
+
+def test_q4k_row_permutation_and_scaling():
+    blob = synth.q4k_weights(synth.rng(70, 1), 33, 512)
+    xq = oracle.quantize_q8_1(synth.activation(synth.rng(70, 0), 512))
+    y, _ = oracle.gemv_q4k_q8_int(blob, xq)
+    perm = np.random.default_rng(1).permutation(33)
+    yp, _ = oracle.gemv_q4k_q8_int(blob[perm], xq)
+    assert np.array_equal(yp, y[perm])
+    x2 = oracle.Q8Blocks(xq.d * np.float32(2), xq.s * np.float32(2), xq.q)
+    y2, _ = oracle.gemv_q4k_q8_int(blob, x2)
+    assert np.array_equal(y2, 2 * y)
+
+
+def test_q4k_isum_brute_force_tiny():
+    """Sub-block sums against a scalar loop over the bytes of one row."""
+    blob = synth.q4k_weights(synth.rng(80, 1), 2, 256)
+    xq = oracle.quantize_q8_1(synth.activation(synth.rng(80, 0), 256))
+    _, _, isum = oracle.gemv_q4k_q8_int(blob, xq, return_isum=True)
+    for r in range(2):
+        qs = blob[r, 0, 16:144]
+        for j in range(8):
+            acc = 0
+            for l in range(32):
+                byte = int(qs[32 * (j // 2) + l])
+                nib = byte & 0xF if j % 2 == 0 else byte >> 4
+                acc += nib * int(xq.q[j, l])
+            assert isum[r, 0, j] == acc
+
+
+# ----------------------------------------------------------------- Q4_0
+def _q4_0_fixture():
+    fx = load("q4_0_block.txt")
+    blob = np.frombuffer(hexbytes(fx["block_hex"]), np.uint8).reshape(1, 1, 18).copy()
+    return fx, blob
+
+
+def test_q4_0_hand_worked_block():
+    fx, blob = _q4_0_fixture()
+    w = oracle.dequantize_q4_0(blob)[0]
+    for idx, val in pairs(fx["w_at"]):
+        assert w[idx] == val
+    for k, key in ((0, "y_onehot0"), (16, "y_onehot16")):
+        x = np.zeros(32, np.float32)
+        x[k] = 1.0
+        assert oracle.gemv_q4_0_f32(blob, x)[0][0] == float(fx[key])
+        assert oracle.gemv_q4_0_q8_int(blob, _onehot_q8(1, k))[0][0] == float(fx[key])
+
+
+@pytest.mark.parametrize("qn,d", [(0, 0.5), (15, 0.0078125), (8, 1.0), (3, 2.0)])
+def test_q4_0_closed_form(qn, d):
+    nb = 5
+    blob = np.frombuffer((_f16le(d) + bytes([qn | (qn << 4)] * 16)) * nb, np.uint8).reshape(1, nb, 18).copy()
+    x = synth.activation(np.random.default_rng(qn), nb * 32)
+    y, _ = oracle.gemv_q4_0_f32(blob, x)
+    assert y[0] == pytest.approx(d * (qn - 8) * x.astype(np.float64).sum(), rel=1e-12, abs=1e-12)
+
+
+@pytest.mark.parametrize("rows,in_dim,seed", [(7, 64, 0), (130, 1024, 1)])
+def test_q4_0_q8_variant_matches_fp32_on_dequantized_activation(rows, in_dim, seed):
+    """Q4_0 x Q8_1 (integer form) equals dequantized weights times d*q."""
+    blob = synth.q4_0_weights(synth.rng(90 + seed, 1), rows, in_dim)
+    xq = oracle.quantize_q8_1(synth.activation(synth.rng(90 + seed, 0), in_dim))
+    y8, t8 = oracle.gemv_q4_0_q8_int(blob, xq)
+    w = oracle.dequantize_q4_0(blob)
+    xh = oracle.dequantize_q8_1(xq)          # exact in float64
+    assert np.all(np.abs(y8 - w @ xh) <= 1e-12 * t8)
+
+
+def test_q4_0_padding_invariance():
+    rows, n, in_dim = 16, 896, 1024
+    blob = synth.q4_0_weights(synth.rng(3, 1), rows, in_dim)
+    x = np.zeros(in_dim, np.float32)
+    x[:n] = synth.activation(synth.rng(3, 0), n)
+    y, _ = oracle.gemv_q4_0_f32(blob, x)
+    b2 = blob.copy()
+    # re-randomise the nibbles of the four padded blocks (their fp16 scales stay
+    # finite: a padded weight is an ordinary finite weight meeting a zero value)
+    b2[:, 28:, 2:18] = np.random.default_rng(5).integers(0, 256, (rows, 4, 16), dtype=np.uint8)
+    y2, _ = oracle.gemv_q4_0_f32(b2, x)
+    assert np.array_equal(y, y2)
+
+
+# ----------------------------------------------------------------- SwiGLU
+def test_silu_textbook_values():
+    # silu(1) = sigma(1) = 1/(1+e^-1); silu(0) = 0; silu(x) -> x for large x, -> 0 for very negative x
+    assert oracle.silu(1.0) == pytest.approx(0.7310585786300049, rel=1e-15)
+    assert oracle.silu(0.0) == 0.0
+    assert oracle.silu(50.0) == pytest.approx(50.0, rel=1e-15)
+    assert abs(oracle.silu(-800.0)) == 0.0
+    g = np.linspace(-20, 20, 81)
+    assert np.allclose(oracle.silu(-g), oracle.silu(g) - g, rtol=0, atol=1e-12)
+
+
+def test_silu_grad_by_finite_difference():
+    g = np.linspace(-12, 12, 97)
+    h = 1e-6
+    fd = (oracle.silu(g + h) - oracle.silu(g - h)) / (2 * h)
+    assert np.allclose(oracle.silu_grad(g), fd, rtol=0, atol=1e-8)
+    from oracle.swiglu import SILU_CURV_MAX, SILU_GRAD_MAX
+    dense = np.linspace(-30, 30, 60001)
+    assert np.max(np.abs(oracle.silu_grad(dense))) <= SILU_GRAD_MAX
+    curv = np.gradient(oracle.silu_grad(dense), dense)
+    assert np.max(np.abs(curv)) <= SILU_CURV_MAX + 1e-6
+
+
+def test_ffn_chain_zero_up_gives_zero():
+    """u = 0 (all up scales zero) gives h = 0, all-zero Q8_1 blocks and y = 0."""
+    hidden, inter = 256, 512
+    wg = synth.q4k_weights(synth.rng(2, 1), inter, hidden)
+    wu = synth.q4k_weights(synth.rng(2, 2), inter, hidden, d_fixed=0.0, dmin_fixed=0.0)
+    wd = synth.q4k_weights(synth.rng(2, 3), hidden, inter)
+    xq = oracle.quantize_q8_1(synth.activation(synth.rng(2, 0), hidden))
+    st = oracle.ffn_swiglu_q4k(wg, wu, wd, xq)
+    assert np.all(st["u"] == 0) and np.all(st["h"] == 0)
+    assert np.all(st["h_q8"].d == 0) and np.all(st["h_q8"].q == 0) and np.all(st["h_q8"].s == 0)
+    assert np.all(st["y"] == 0)
+
+
+def test_ffn_chain_stages_compose():
+    hidden, inter = 256, 512
+    wg = synth.q4k_weights(synth.rng(2, 1), inter, hidden)
+    wu = synth.q4k_weights(synth.rng(2, 2), inter, hidden)
+    wd = synth.q4k_weights(synth.rng(2, 3), hidden, inter)
+    xq = oracle.quantize_q8_1(synth.activation(synth.rng(2, 0), hidden))
+    st = oracle.ffn_swiglu_q4k(wg, wu, wd, xq)
+    assert np.array_equal(st["h"], oracle.silu(st["g"]) * st["u"])
+    # the down projection of the fp64 h (no requantization) agrees with y to the
+    # Q8_1 quantization error sum_k |w_k| * d_k / 2
+    w = oracle.dequantize_q4k(wd)
+    d_blocks = np.repeat(st["h_q8"].d.astype(np.float64), 32)
+    assert np.all(np.abs(st["y"] - w @ st["h"]) <= np.abs(w) @ (d_blocks / 2) * (1 + 1e-6) + 1e-9)
+
+
+def test_h_tolerance_covers_perturbations():
+    g = np.random.default_rng(0).normal(0, 40, 4096)
+    u = np.random.default_rng(1).normal(0, 40, 4096)
+    tg = np.full_like(g, 0.01)
+    tu = np.full_like(u, 0.01)
+    h = oracle.swiglu(g, u)
+    tol = oracle.h_tolerance(g, u, tg, tu, h)
+    for sg, su in ((1, 1), (1, -1), (-1, 1), (-1, -1)):
+        hp = oracle.swiglu(g + sg * tg, u + su * tu)
+        assert np.all(np.abs(hp - h) <= tol)
