@@ -1,0 +1,218 @@
+"""Benchmark of the Q4_K x Q8_1 decode GEMV at 4096 -> 14336, batch 1.
+
+One step = the whole hot path for one token: quantize the fp32 activation to
+Q8_1 (rz_q8_1_quantize), then y = W x (rz_q4k_q8_gemv) with W a 14336 x 4096
+Q4_K matrix (33,030,144 bytes).  Every step reads the next of R weight copies
+(R * 33 MB >= 1 GiB), so no step finds its weights in the 256 MB Infinity
+Cache or an L2; inputs are resident in HBM before the timed region.
+
+Printed (one JSON line): the whole-step weight-stream rate in GB/s (`value`),
+the GEMV kernel's own rate against the 8 TB/s HBM peak (`roofline`, from HIP
+events around each GEMV launch on the launch stream), and the CPU oracle
+timed on the host (`cpu_baseline`).
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Q4_K×Q8_1 GEMV weight-stream GB/s and % HBM peak at 4096→14336, batch 1"
+HBM_PEAK_GBS = 8000.0
+OUT_DIM, IN_DIM = 14336, 4096
+W_BYTES = OUT_DIM * (IN_DIM // 256) * 144            # 33,030,144
+XQ_BYTES = (IN_DIM // 32) * 40                        # 5,120
+Y_BYTES = OUT_DIM * 4                                 # 57,344
+GEMV_ALGO_BYTES = W_BYTES + XQ_BYTES + Y_BYTES        # 33,092,608 per launch
+ROTATE_BYTES = 1 << 30
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "q4k_gemv_4096x14336_traffic.txt")
+KERNEL_SOURCES = ["q4k_gemv.h", "q4k_gemv.hip", "rz_device.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "q4_q8_integer_quantize_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per GEMV launch from the committed rocprofv3 counter summary,
+    or None when that summary was taken on different kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    fields = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(target_seconds: float):
+    """The oracle as it stands: Q8_1 quantize of the activation plus the integer
+    form of the GEMV over all 14336 rows, repeated until target_seconds of wall
+    time; rate = weight bytes per second.  Threads used = CPU time / wall time."""
+    import numpy as np
+    import oracle
+    import synth
+    w = synth.q4k_weights(synth.rng(2, synth.T_W0), OUT_DIM, IN_DIM)
+    x = synth.activation(synth.rng(2, synth.T_ACT), IN_DIM)
+    reps, wall, cpu = 0, 0.0, 0.0
+    while wall < target_seconds or reps < 1:
+        c0, t0 = time.process_time(), time.perf_counter()
+        xq = oracle.quantize_q8_1(x)
+        oracle.gemv_q4k_q8_int(w, xq)
+        wall += time.perf_counter() - t0
+        cpu += time.process_time() - c0
+        reps += 1
+    rate = reps * W_BYTES / wall / 1e9
+    return {"value": round(rate, 4), "unit": "GB/s", "cores": max(1, round(cpu / wall)),
+            "kind": "oracle",
+            "sample": "%d full passes (quantize 4096 + integer-form GEMV 14336x4096, numpy), "
+                      "%.1f s wall; host has %d cores" % (reps, wall, len(os.sched_getaffinity(0)))}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--hold-cycles", type=float, default=2e8,
+                    help="spin-kernel cycles that hold the stream while launches are enqueued")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this path runs on one GPU; --gpus %d is not supported "
+              "(rows shard without communication; see the design notes)" % args.gpus,
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    import synth
+    import q4_q8_integer_quantize_amd as rz
+
+    rz.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    w0 = synth.q4k_weights(synth.rng(2, synth.T_W0), OUT_DIM, IN_DIM)
+    w0_dev = torch.from_numpy(w0.reshape(-1).copy()).to(dev)
+    n_copies = -(-ROTATE_BYTES // W_BYTES)
+    copies = [w0_dev] + [w0_dev.clone() for _ in range(n_copies - 1)]
+    x = torch.from_numpy(synth.activation(synth.rng(2, synth.T_ACT), IN_DIM)).to(dev)
+    xq = torch.empty(XQ_BYTES, dtype=torch.uint8, device=dev)
+    y = torch.empty(OUT_DIM, dtype=torch.float32, device=dev)
+    s = stream.cuda_stream
+
+    lib = rz.load_library()
+    x_p, xq_p, y_p = x.data_ptr(), xq.data_ptr(), y.data_ptr()
+    w_p = [c.data_ptr() for c in copies]
+
+    def step(i, strm):
+        # direct C calls: the binding's checks were made once above
+        rc = lib.rz_q8_1_quantize(x_p, IN_DIM, IN_DIM, 1, xq_p, strm)
+        rc |= lib.rz_q4k_q8_gemv(w_p[i % n_copies], xq_p, y_p, OUT_DIM, IN_DIM, 1, strm)
+        if rc:
+            raise RuntimeError(rz.rz_last_error())
+
+    rz.rz_q8_1_quantize(x, IN_DIM, IN_DIM, 1, xq, s)                 # checked once
+    rz.rz_q4k_q8_gemv(copies[0], xq, y, OUT_DIM, IN_DIM, 1, s)
+    for i in range(args.warmup):
+        step(i, s)
+    torch.cuda.synchronize()
+
+    # ---- whole-step throughput: K steps captured once in a HIP graph, replayed
+    K = args.steps
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cs = torch.cuda.current_stream().cuda_stream
+        for i in range(K):
+            step(args.warmup + i, cs)
+    graph.replay()                      # untimed replay: graph upload and warm caches
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    graph.replay()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / K
+
+    # ---- GEMV kernel duration: HIP events around every GEMV launch on the
+    # launch stream; the stream is held by a spin kernel while the host enqueues,
+    # so no host gap falls between an event pair
+    ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(args.hold_cycles))
+    for i in range(K):
+        lib.rz_q8_1_quantize(x_p, IN_DIM, IN_DIM, 1, xq_p, s)
+        ev_s[i].record(stream)
+        lib.rz_q4k_q8_gemv(w_p[(args.warmup + i) % n_copies], xq_p, y_p, OUT_DIM, IN_DIM, 1, s)
+        ev_e[i].record(stream)
+    torch.cuda.synchronize()
+    gemv_ms = np.array([a.elapsed_time(b) for a, b in zip(ev_s, ev_e)])
+    gemv_avg_s = float(gemv_ms.mean()) * 1e-3
+    achieved = GEMV_ALGO_BYTES / gemv_avg_s / 1e9
+    traffic = measured_traffic()
+
+    value = W_BYTES / (ms_step * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {
+            "workload": "Q8_1 quantize + Q4_K x Q8_1 GEMV, 4096 -> 14336, batch 1",
+            "out_dim": OUT_DIM, "in_dim": IN_DIM, "n_tokens": 1,
+            "weight_bytes": W_BYTES, "weight_copies_rotated": n_copies,
+            "pct_hbm_peak_step": round(100 * value / HBM_PEAK_GBS, 2),
+        },
+        "gemv_us_avg": round(gemv_avg_s * 1e6, 3),
+        "gemv_us_p10_p50_p90": [round(float(v) * 1e3, 3) for v in np.percentile(gemv_ms, [10, 50, 90])],
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,133 @@
+/*
+ * rz.h -- C ABI of librz.so: integer-quantized GEMV for MI355X (gfx950).
+ *
+ * The operations are the quantized decode-time matrix-vector products of the
+ * realizar source pages (docs.rs, realizar 0.8.4 / 0.8.5):
+ *
+ *   - src/cuda/executor/cached.rs, transformer_layer_gpu_true_dp4a: the fp32
+ *     activation is quantized to Q8_1 once (step 2) and multiplied by Q4_K
+ *     weight matrices with integer dot products (steps 3 and 6); the FFN runs
+ *     on the same integer path (step 9);
+ *   - src/gpu/adapters/using.rs, GpuModelQ4::forward step 5: the LM head is a
+ *     Q4_0 GEMV over the fp32 normed hidden state;
+ *   - src/cuda/executor/layers/forward_utils.rs, pad_and_upload_input: the
+ *     activation is zero-padded to a multiple of the 256-value super-block.
+ *
+ * Formats (GGML layouts; little endian):
+ *   Q8_1 block, 40 bytes : float d; float s; int8 q[32];   x ~= d * q, s = d * sum(q)
+ *   Q4_K super-block, 144: fp16 d; fp16 dmin; u8 scales[12]; u8 qs[128]  (256 values)
+ *   Q4_0 block, 18 bytes : fp16 d; u8 qs[16]                            (32 values)
+ * Weight matrices are row-major: row r is out_dim-major, its blocks follow
+ * each other along in_dim.  Arguments are ordered (out_dim, in_dim) as in the
+ * pages' q4k_q8_gemv_async / q4_0_gemv_into calls.
+ *
+ * Conventions shared by every entry point:
+ *   - every pointer argument except `stream` is a DEVICE pointer owned by the
+ *     caller; the library allocates, frees and synchronises nothing and keeps
+ *     no state but a thread-local error message;
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream); the
+ *     work is enqueued asynchronously on it;
+ *   - arguments are validated on the host before any HIP call; the return
+ *     value is RZ_OK or a negative RZ_E* code, and rz_last_error() then holds a
+ *     message.  A device-side fault surfaces at the caller's next sync.
+ *   - in_dim is always the PADDED length (the caller zero-pads activations;
+ *     rz_q8_1_quantize does it while quantizing).
+ */
+#ifndef RZ_H
+#define RZ_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RZ_OK 0
+#define RZ_EINVAL (-1)  /* null pointer, bad n_tokens or format flag          */
+#define RZ_EDIM (-2)    /* dimension not a positive multiple of the block size */
+#define RZ_EALIGN (-3)  /* pointer alignment below the stated requirement      */
+#define RZ_ELAUNCH (-4) /* the HIP runtime rejected a kernel launch            */
+
+#define RZ_Q8_1_BLOCK_BYTES 40
+#define RZ_Q4K_BLOCK_BYTES 144
+#define RZ_Q4_0_BLOCK_BYTES 18
+#define RZ_MAX_TOKENS 8
+#define RZ_MAX_DIM (1 << 24)
+
+/* rz_q8_1_quantize -- fp32 activations to Q8_1 blocks.
+ * Passage: realizar 0.8.5 src/cuda/executor/cached.rs,
+ * transformer_layer_gpu_true_dp4a, steps 2 and 5 (quantize once, share).
+ * Per block of 32: amax = max|x|, d = amax / 127 (IEEE fp32 division),
+ * q = round-half-even(x / d) (fp32 division), s = d * sum(q); amax == 0 gives
+ * an all-zero block.
+ *   x        fp32 [n_tokens][n] (token rows of n values, contiguous), 4-byte aligned
+ *   n        logical length, 1 <= n <= n_padded
+ *   n_padded multiple of 32; values n..n_padded-1 are taken as +0.0
+ *   n_tokens 1 <= n_tokens <= RZ_MAX_TOKENS
+ *   x_q8     out: [n_tokens][n_padded/32] blocks, 8-byte aligned
+ * Errors: RZ_EINVAL (null pointer, n_tokens out of range), RZ_EDIM,
+ * RZ_EALIGN, RZ_ELAUNCH.  The output is bit-exact (a unique result). */
+int rz_q8_1_quantize(const float* x, int n, int n_padded, int n_tokens,
+                     void* x_q8, void* stream);
+
+/* rz_q4k_q8_gemv -- y = W x with W Q4_K and x Q8_1, for 1..8 tokens.
+ * Passage: realizar 0.8.5 src/cuda/executor/cached.rs,
+ * transformer_layer_gpu_true_dp4a, steps 3 and 6 (Q4K x Q8 integer dot
+ * product; weights streamed once per call, whatever the token count).
+ * Per 32-value sub-block j of super-block b: isum = sum(q4 * q8) in int32,
+ * y += d * sc_j * d_x * isum - dmin * m_j * s_x.
+ *   w_q4k    [out_dim][in_dim/256] super-blocks, 16-byte aligned
+ *   x_q8     [n_tokens][in_dim/32] Q8_1 blocks, 8-byte aligned
+ *   y        out: fp32 [n_tokens][out_dim] (token-major), 4-byte aligned
+ *   out_dim  >= 1; in_dim multiple of 256 (padded); both <= RZ_MAX_DIM
+ *   n_tokens 1..RZ_MAX_TOKENS
+ * Errors: RZ_EINVAL, RZ_EDIM, RZ_EALIGN, RZ_ELAUNCH. */
+int rz_q4k_q8_gemv(const void* w_q4k, const void* x_q8, float* y,
+                   int out_dim, int in_dim, int n_tokens, void* stream);
+
+/* rz_q4_0_gemv -- y = W x with W Q4_0 and x fp32 or Q8_1 (the LM head).
+ * Passage: realizar 0.8.4 src/gpu/adapters/using.rs, GpuModelQ4::forward
+ * step 5 (q4_0_gemv_into(lm_head, normed, logits, vocab, hidden)).
+ * Weight value = (q - 8) * d.
+ *   w_q4_0   [out_dim][in_dim/32] blocks of 18 bytes, 4-byte aligned
+ *   x        x_format 0: fp32 [in_dim], 16-byte aligned;
+ *            x_format 1: Q8_1 [in_dim/32] blocks, 8-byte aligned
+ *   y        out: fp32 [out_dim], 4-byte aligned
+ *   in_dim   multiple of 64 (pairs of blocks keep every load 4-byte aligned)
+ * Errors: RZ_EINVAL (also unknown x_format), RZ_EDIM, RZ_EALIGN, RZ_ELAUNCH. */
+int rz_q4_0_gemv(const void* w_q4_0, const void* x, int x_format, float* y,
+                 int out_dim, int in_dim, void* stream);
+
+/* rz_swiglu_ffn_q4k -- the SwiGLU FFN on the integer path.
+ * Passages: realizar 0.8.5 src/cuda/executor/cached.rs,
+ * transformer_layer_gpu_true_dp4a step 9 (fused_ffn_swiglu_gpu_true_dp4a);
+ * realizar 0.8.4 src/gguf/cuda/clone_layer_weights.rs, cuda_swiglu_ffn
+ * (silu on gate, times up, then down).
+ *   g = W_gate x, u = W_up x            (Q4_K x Q8_1, inter_dim rows)
+ *   h = silu(g) * u = g / (1 + exp(-g)) * u      (fp32)
+ *   h_q8 = Q8_1(h)                      (same rule as rz_q8_1_quantize)
+ *   y = W_down h_q8                     (Q4_K x Q8_1, hidden_dim rows)
+ *   w_gate, w_up  [inter_dim][hidden_dim/256] super-blocks, 16-byte aligned
+ *   w_down        [hidden_dim][inter_dim/256] super-blocks, 16-byte aligned
+ *   x_q8          [hidden_dim/32] Q8_1 blocks, 8-byte aligned
+ *   h             out: fp32 [inter_dim]
+ *   h_q8          out: [inter_dim/32] Q8_1 blocks, 8-byte aligned
+ *   y             out: fp32 [hidden_dim]
+ *   gu            optional out (NULL to skip): fp32 [2][inter_dim], g then u
+ *   hidden_dim, inter_dim  multiples of 256; hidden_dim <= 16384 (the fused
+ *                 gate/up kernel keeps a row's activation in registers)
+ * Two kernels run in order on `stream`; h and h_q8 are written by the first
+ * and read by the second.  Errors: RZ_EINVAL, RZ_EDIM, RZ_EALIGN, RZ_ELAUNCH. */
+int rz_swiglu_ffn_q4k(const void* w_gate, const void* w_up, const void* w_down,
+                      const void* x_q8, float* h, void* h_q8, float* y,
+                      float* gu, int hidden_dim, int inter_dim, void* stream);
+
+/* Message for the most recent non-zero return on the calling thread. */
+const char* rz_last_error(void);
+
+/* ABI version (major * 100 + minor). */
+int rz_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RZ_H */

@@ -1,0 +1,162 @@
+"""Python binding of librz.so -- Q4_K / Q4_0 x Q8_1 integer GEMV for MI355X.
+
+The functions carry the names of the C entry points (include/rz.h) and do
+argument marshalling only: tensors become device pointers, the stream defaults
+to PyTorch's current stream, and a negative return code becomes a
+``RuntimeError`` carrying ``rz_last_error()``.  Every step of the computation
+runs in the HIP kernels of librz.so; there is no fallback.  If the library has
+not been built (``python -m q4_q8_integer_quantize_amd.build``) every call
+raises.
+
+PyTorch is used for device memory and streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "RZ_OK", "RZ_EINVAL", "RZ_EDIM", "RZ_EALIGN", "RZ_ELAUNCH",
+    "Q8_1_BLOCK_BYTES", "Q4K_BLOCK_BYTES", "Q4_0_BLOCK_BYTES", "MAX_TOKENS",
+    "library_path", "load_library", "rz_last_error", "rz_abi_version",
+    "rz_q8_1_quantize", "rz_q4k_q8_gemv", "rz_q4_0_gemv", "rz_swiglu_ffn_q4k",
+    "q8_1_nbytes", "RzError",
+]
+
+RZ_OK, RZ_EINVAL, RZ_EDIM, RZ_EALIGN, RZ_ELAUNCH = 0, -1, -2, -3, -4
+Q8_1_BLOCK_BYTES = 40
+Q4K_BLOCK_BYTES = 144
+Q4_0_BLOCK_BYTES = 18
+MAX_TOKENS = 8
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+class RzError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__("%s (rz code %d)" % (msg, code))
+        self.code = code
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "librz.so")
+
+
+def load_library() -> ctypes.CDLL:
+    """Load librz.so (built in-tree).  Raises if it is missing."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError("librz.so is not built (%s); run "
+                           "`python -m q4_q8_integer_quantize_amd.build`" % path)
+    lib = ctypes.CDLL(path)
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    lib.rz_q8_1_quantize.argtypes = [vp, i, i, i, vp, vp]
+    lib.rz_q4k_q8_gemv.argtypes = [vp, vp, vp, i, i, i, vp]
+    lib.rz_q4_0_gemv.argtypes = [vp, vp, i, vp, i, i, vp]
+    lib.rz_swiglu_ffn_q4k.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, vp]
+    for fn in ("rz_q8_1_quantize", "rz_q4k_q8_gemv", "rz_q4_0_gemv", "rz_swiglu_ffn_q4k",
+               "rz_abi_version"):
+        getattr(lib, fn).restype = i
+    lib.rz_last_error.argtypes = []
+    lib.rz_last_error.restype = ctypes.c_char_p
+    lib.rz_abi_version.argtypes = []
+    _LIB = lib
+    return lib
+
+
+def rz_last_error() -> str:
+    return load_library().rz_last_error().decode()
+
+
+def rz_abi_version() -> int:
+    return load_library().rz_abi_version()
+
+
+def q8_1_nbytes(n_padded: int, n_tokens: int = 1) -> int:
+    return n_tokens * (n_padded // 32) * Q8_1_BLOCK_BYTES
+
+
+def _ptr(t):
+    """Device pointer of a tensor (or pass an int / None through)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("librz takes device tensors (got a %s tensor)" % t.device)
+    if not t.is_contiguous():
+        raise ValueError("librz takes contiguous tensors")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(rc: int):
+    if rc != RZ_OK:
+        raise RzError(rc, rz_last_error())
+
+
+def _need(t, nbytes: int, name: str):
+    if t is None or isinstance(t, int):
+        return
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError("%s holds %d bytes, needs %d" % (name, have, nbytes))
+
+
+def rz_q8_1_quantize(x, n: int, n_padded: int, n_tokens: int, x_q8, stream=None) -> None:
+    """x fp32 [n_tokens, n] -> x_q8 uint8 [n_tokens * n_padded/32 * 40]."""
+    _need(x, 4 * n * n_tokens, "x")
+    _need(x_q8, q8_1_nbytes(n_padded, n_tokens) if n_padded > 0 else 0, "x_q8")
+    _check(load_library().rz_q8_1_quantize(_ptr(x), n, n_padded, n_tokens, _ptr(x_q8),
+                                           _stream(stream)))
+
+
+def rz_q4k_q8_gemv(w_q4k, x_q8, y, out_dim: int, in_dim: int, n_tokens: int = 1,
+                   stream=None) -> None:
+    """y fp32 [n_tokens, out_dim] = W (Q4_K [out_dim, in_dim/256, 144]) x (Q8_1)."""
+    if in_dim > 0 and in_dim % 256 == 0 and out_dim > 0:
+        _need(w_q4k, out_dim * (in_dim // 256) * Q4K_BLOCK_BYTES, "w_q4k")
+        _need(x_q8, q8_1_nbytes(in_dim, n_tokens), "x_q8")
+        _need(y, 4 * out_dim * n_tokens, "y")
+    _check(load_library().rz_q4k_q8_gemv(_ptr(w_q4k), _ptr(x_q8), _ptr(y), out_dim, in_dim,
+                                         n_tokens, _stream(stream)))
+
+
+def rz_q4_0_gemv(w_q4_0, x, x_format: int, y, out_dim: int, in_dim: int, stream=None) -> None:
+    """y fp32 [out_dim] = W (Q4_0 [out_dim, in_dim/32, 18]) x; x_format 0 = fp32, 1 = Q8_1."""
+    if in_dim > 0 and in_dim % 64 == 0 and out_dim > 0:
+        _need(w_q4_0, out_dim * (in_dim // 32) * Q4_0_BLOCK_BYTES, "w_q4_0")
+        _need(x, 4 * in_dim if x_format == 0 else q8_1_nbytes(in_dim), "x")
+        _need(y, 4 * out_dim, "y")
+    _check(load_library().rz_q4_0_gemv(_ptr(w_q4_0), _ptr(x), x_format, _ptr(y), out_dim,
+                                       in_dim, _stream(stream)))
+
+
+def rz_swiglu_ffn_q4k(w_gate, w_up, w_down, x_q8, h, h_q8, y, gu, hidden_dim: int,
+                      inter_dim: int, stream=None) -> None:
+    """SwiGLU FFN: h = silu(W_gate x) * (W_up x), h_q8 = Q8_1(h), y = W_down h_q8."""
+    if hidden_dim > 0 and inter_dim > 0 and hidden_dim % 256 == 0 and inter_dim % 256 == 0:
+        nw = inter_dim * (hidden_dim // 256) * Q4K_BLOCK_BYTES
+        _need(w_gate, nw, "w_gate")
+        _need(w_up, nw, "w_up")
+        _need(w_down, nw, "w_down")
+        _need(x_q8, q8_1_nbytes(hidden_dim), "x_q8")
+        _need(h, 4 * inter_dim, "h")
+        _need(h_q8, q8_1_nbytes(inter_dim), "h_q8")
+        _need(y, 4 * hidden_dim, "y")
+        _need(gu, 8 * inter_dim, "gu")
+    _check(load_library().rz_swiglu_ffn_q4k(_ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(x_q8),
+                                            _ptr(h), _ptr(h_q8), _ptr(y), _ptr(gu), hidden_dim,
+                                            inter_dim, _stream(stream)))

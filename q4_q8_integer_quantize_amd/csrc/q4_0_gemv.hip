@@ -1,0 +1,256 @@
+// q4_0_gemv.hip -- y = W x with W Q4_0 (the LM head) and x fp32 or Q8_1.
+//
+// realizar 0.8.4 src/gpu/adapters/using.rs, GpuModelQ4::forward step 5
+// (q4_0_gemv_into(lm_head, normed, logits, vocab_size, hidden_dim) over the
+// fp32 output of the final RMSNorm).  Weight value (q - 8) * d, value l < 16
+// in the low nibble of qs[l], value 16 + l in its high nibble.
+//
+// A lane owns a pair of 18-byte blocks (36 bytes, 4-byte aligned when in_dim
+// is a multiple of 64): block A = d | qs at bytes 0..17, block B at 18..35.
+// LPR lanes share a row (RW = 64/LPR rows side by side); S pair slots per
+// lane keep that lane's activation values in registers for the wave's life.
+//   fp32 x : sum_l q_l x_l per block, then d * (sum - 8 * sum_l x_l)
+//   Q8_1 x : isum = sum_l q_l q8_l - 8 * sum_l q8_l (exact), then d * d_x * isum
+#include "rz_device.h"
+#include "rz_launch.h"
+
+namespace rz {
+
+struct Q40Args {
+  const uint8_t* w;
+  const void* x;
+  float* y;
+  int out_dim;
+  int npairs_row;   // block pairs per full row
+  int p0;           // first pair of this column chunk
+  int npairs;       // pairs in this chunk
+  int accumulate;
+};
+
+template <int S, bool Q8>
+struct X40;
+
+template <int S>
+struct X40<S, false> {
+  float v[S][64];
+  float sum[S][2];
+};
+
+template <int S>
+struct X40<S, true> {
+  int q[S][16];
+  float dx[S][2];
+  int qsum[S][2];
+};
+
+template <int LPR, int S, bool Q8>
+__device__ __forceinline__ void load_x40(X40<S, Q8>& xs, const Q40Args& a, int ps) {
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int p = s * LPR + ps;
+    const bool on = p < a.npairs;
+    const long gp = (long)a.p0 + p;
+    if constexpr (!Q8) {
+      if (on) {
+        const float4* xp = (const float4*)((const float*)a.x + gp * 64);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const float4 f = xp[k];
+          xs.v[s][4 * k] = f.x; xs.v[s][4 * k + 1] = f.y;
+          xs.v[s][4 * k + 2] = f.z; xs.v[s][4 * k + 3] = f.w;
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 64; ++k) xs.v[s][k] = 0.0f;
+      }
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        float t = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 32; ++k) t += xs.v[s][32 * b + k];
+        xs.sum[s][b] = t;
+      }
+    } else {
+      if (on) {
+        const uint8_t* xb = (const uint8_t*)a.x + gp * 2 * kQ8Bytes;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const uint8_t* blk = xb + b * kQ8Bytes;
+          xs.dx[s][b] = ((const float*)blk)[0];
+          const uint2* qp = (const uint2*)(blk + 8);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const uint2 u = qp[k];
+            xs.q[s][8 * b + 2 * k] = (int)u.x;
+            xs.q[s][8 * b + 2 * k + 1] = (int)u.y;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) xs.q[s][k] = 0;
+        xs.dx[s][0] = xs.dx[s][1] = 0.0f;
+      }
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        int t = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) t = dot4(xs.q[s][8 * b + k], 0x01010101, t);
+        xs.qsum[s][b] = t;
+      }
+    }
+  }
+}
+
+// sum_l q_l * x_l over one block; qs dwords hold values 4k..4k+3 (low
+// nibbles) and 16+4k..16+4k+3 (high nibbles).
+__device__ __forceinline__ float block_dot_f32(const uint32_t qs[4], const float* x) {
+  float acc = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t lo = qs[k] & 0x0F0F0F0Fu;
+    const uint32_t hi = (qs[k] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      acc = fmaf((float)((lo >> (8 * b)) & 0xffu), x[4 * k + b], acc);
+      acc = fmaf((float)((hi >> (8 * b)) & 0xffu), x[16 + 4 * k + b], acc);
+    }
+  }
+  return acc;
+}
+
+__device__ __forceinline__ int block_dot_q8(const uint32_t qs[4], const int* q8) {
+  int acc = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    acc = dot4((int)(qs[k] & 0x0F0F0F0Fu), q8[k], acc);
+    acc = dot4((int)((qs[k] >> 4) & 0x0F0F0F0Fu), q8[4 + k], acc);
+  }
+  return acc;
+}
+
+template <int LPR, int S, int R, bool Q8>
+__global__ __launch_bounds__(256) void q4_0_gemv_kernel(Q40Args a) {
+  constexpr int RW = kWave / LPR;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int rs = lane / LPR, ps = lane % LPR;
+  const long wave = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const long row_base = wave * (RW * R);
+  if (row_base >= a.out_dim) return;   // wave-uniform
+  X40<S, Q8> xs;
+  load_x40<LPR, S, Q8>(xs, a, ps);
+
+  const size_t row_bytes = (size_t)a.npairs_row * 36;
+  u32x4_a4 v0[R][S], v1[R][S];
+  uint32_t v8[R][S];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    long row = row_base + (long)r * RW + rs;
+    if (row >= a.out_dim) row = a.out_dim - 1;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      int p = s * LPR + ps;
+      if (p >= a.npairs) p = a.npairs - 1;   // inactive slot: zero activation
+      const uint8_t* ptr = a.w + (size_t)row * row_bytes + ((size_t)a.p0 + p) * 36;
+      v0[r][s] = *(const u32x4_a4*)ptr;
+      v1[r][s] = *(const u32x4_a4*)(ptr + 16);
+      v8[r][s] = *(const uint32_t*)(ptr + 32);
+    }
+  }
+
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float ar = 0.0f;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const u32x4_a4 A = v0[r][s], B = v1[r][s];
+      const float dA = f16_lo(A.x), dB = f16_hi(B.x);
+      const uint32_t qa[4] = {__builtin_amdgcn_alignbyte(A.y, A.x, 2),
+                              __builtin_amdgcn_alignbyte(A.z, A.y, 2),
+                              __builtin_amdgcn_alignbyte(A.w, A.z, 2),
+                              __builtin_amdgcn_alignbyte(B.x, A.w, 2)};
+      const uint32_t qb[4] = {B.y, B.z, B.w, v8[r][s]};
+      if constexpr (!Q8) {
+        const float sa = block_dot_f32(qa, &xs.v[s][0]);
+        const float sb = block_dot_f32(qb, &xs.v[s][32]);
+        ar = fmaf(dA, fmaf(-8.0f, xs.sum[s][0], sa), ar);
+        ar = fmaf(dB, fmaf(-8.0f, xs.sum[s][1], sb), ar);
+      } else {
+        const int ia = block_dot_q8(qa, &xs.q[s][0]) - 8 * xs.qsum[s][0];
+        const int ib = block_dot_q8(qb, &xs.q[s][8]) - 8 * xs.qsum[s][1];
+        ar = fmaf(dA * xs.dx[s][0], (float)ia, ar);
+        ar = fmaf(dB * xs.dx[s][1], (float)ib, ar);
+      }
+    }
+    acc[r] = group_sum<LPR>(ar);
+  }
+
+  if (ps == 0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const long row = row_base + (long)r * RW + rs;
+      if (row < a.out_dim) a.y[row] = a.accumulate ? a.y[row] + acc[r] : acc[r];
+    }
+  }
+}
+
+template <bool Q8>
+constexpr int pair_slots_max() { return Q8 ? 4 : 2; }
+
+template <int LPR, int S, bool Q8>
+static hipError_t run_q40(const Q40Args& a, hipStream_t st) {
+  constexpr int R = S >= 4 ? 1 : 4 / S;
+  constexpr int RW = kWave / LPR;
+  const long rows_per_wave = (long)RW * R;
+  const long waves = (a.out_dim + rows_per_wave - 1) / rows_per_wave;
+  const unsigned grid = (unsigned)((waves + 3) / 4);
+  hipLaunchKernelGGL((q4_0_gemv_kernel<LPR, S, R, Q8>), dim3(grid), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <bool Q8>
+static hipError_t run_q40_chunk(const Q40Args& a, hipStream_t st) {
+  const int np = a.npairs;
+  if (np <= 1) return run_q40<1, 1, Q8>(a, st);
+  if (np <= 2) return run_q40<2, 1, Q8>(a, st);
+  if (np <= 4) return run_q40<4, 1, Q8>(a, st);
+  if (np <= 8) return run_q40<8, 1, Q8>(a, st);
+  if (np <= 16) return run_q40<16, 1, Q8>(a, st);
+  if (np <= 32) return run_q40<32, 1, Q8>(a, st);
+  switch ((np + 63) / 64) {
+    case 1: return run_q40<64, 1, Q8>(a, st);
+    case 2: return run_q40<64, 2, Q8>(a, st);
+    case 3: if constexpr (Q8) return run_q40<64, 3, Q8>(a, st); else return hipErrorInvalidValue;
+    case 4: if constexpr (Q8) return run_q40<64, 4, Q8>(a, st); else return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <bool Q8>
+static hipError_t run_q40_all(Q40Args a, hipStream_t st) {
+  const int chunk = 64 * pair_slots_max<Q8>();
+  for (int p0 = 0; p0 < a.npairs_row; p0 += chunk) {
+    a.p0 = p0;
+    a.npairs = a.npairs_row - p0 < chunk ? a.npairs_row - p0 : chunk;
+    a.accumulate = p0 > 0;
+    const hipError_t e = run_q40_chunk<Q8>(a, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_q4_0_gemv(const uint8_t* w, const void* x, int x_format, float* y,
+                            int out_dim, int in_dim, hipStream_t stream) {
+  Q40Args a;
+  a.w = w;
+  a.x = x;
+  a.y = y;
+  a.out_dim = out_dim;
+  a.npairs_row = in_dim / 64;
+  a.p0 = 0;
+  a.npairs = a.npairs_row;
+  a.accumulate = 0;
+  return x_format == 0 ? run_q40_all<false>(a, stream) : run_q40_all<true>(a, stream);
+}
+
+}  // namespace rz

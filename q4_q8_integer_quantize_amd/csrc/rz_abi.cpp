@@ -1,0 +1,129 @@
+// rz_abi.cpp -- the extern "C" boundary of librz.so (declared in include/rz.h).
+//
+// Every entry point validates its arguments on the host first and returns a
+// negative code with a message before touching the HIP runtime, so the checks
+// run on machines without a GPU.  Kernels are only enqueued on the caller's
+// stream; nothing here allocates, frees or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "rz.h"
+#include "rz_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int launch_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return RZ_OK;
+  return fail(RZ_ELAUNCH, "%s: kernel launch failed: %s", what, hipGetErrorString(e));
+}
+
+int check_dim(const char* what, const char* name, int v, int multiple) {
+  if (v <= 0 || v > RZ_MAX_DIM || v % multiple != 0)
+    return fail(RZ_EDIM, "%s: %s=%d must be a positive multiple of %d and <= %d", what, name, v,
+                multiple, RZ_MAX_DIM);
+  return RZ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* rz_last_error(void) { return g_err; }
+
+int rz_abi_version(void) { return 100; }
+
+int rz_q8_1_quantize(const float* x, int n, int n_padded, int n_tokens, void* x_q8,
+                     void* stream) {
+  const char* what = "rz_q8_1_quantize";
+  if (!x || !x_q8) return fail(RZ_EINVAL, "%s: null pointer", what);
+  if (n_tokens < 1 || n_tokens > RZ_MAX_TOKENS)
+    return fail(RZ_EINVAL, "%s: n_tokens=%d outside 1..%d", what, n_tokens, RZ_MAX_TOKENS);
+  if (int rc = check_dim(what, "n_padded", n_padded, 32)) return rc;
+  if (n <= 0 || n > n_padded)
+    return fail(RZ_EDIM, "%s: n=%d must satisfy 1 <= n <= n_padded=%d", what, n, n_padded);
+  if (!aligned(x, 4)) return fail(RZ_EALIGN, "%s: x must be 4-byte aligned", what);
+  if (!aligned(x_q8, 8)) return fail(RZ_EALIGN, "%s: x_q8 must be 8-byte aligned", what);
+  return launch_status(rz::launch_q8_1_quantize(x, n, n_padded, n_tokens,
+                                                static_cast<uint8_t*>(x_q8),
+                                                static_cast<hipStream_t>(stream)),
+                       what);
+}
+
+int rz_q4k_q8_gemv(const void* w_q4k, const void* x_q8, float* y, int out_dim, int in_dim,
+                   int n_tokens, void* stream) {
+  const char* what = "rz_q4k_q8_gemv";
+  if (!w_q4k || !x_q8 || !y) return fail(RZ_EINVAL, "%s: null pointer", what);
+  if (n_tokens < 1 || n_tokens > RZ_MAX_TOKENS)
+    return fail(RZ_EINVAL, "%s: n_tokens=%d outside 1..%d", what, n_tokens, RZ_MAX_TOKENS);
+  if (int rc = check_dim(what, "out_dim", out_dim, 1)) return rc;
+  if (int rc = check_dim(what, "in_dim", in_dim, 256)) return rc;
+  if (!aligned(w_q4k, 16)) return fail(RZ_EALIGN, "%s: w_q4k must be 16-byte aligned", what);
+  if (!aligned(x_q8, 8)) return fail(RZ_EALIGN, "%s: x_q8 must be 8-byte aligned", what);
+  if (!aligned(y, 4)) return fail(RZ_EALIGN, "%s: y must be 4-byte aligned", what);
+  return launch_status(rz::launch_q4k_q8_gemv(static_cast<const uint8_t*>(w_q4k),
+                                               static_cast<const uint8_t*>(x_q8), y, out_dim,
+                                               in_dim, n_tokens,
+                                               static_cast<hipStream_t>(stream)),
+                       what);
+}
+
+int rz_q4_0_gemv(const void* w_q4_0, const void* x, int x_format, float* y, int out_dim,
+                 int in_dim, void* stream) {
+  const char* what = "rz_q4_0_gemv";
+  if (!w_q4_0 || !x || !y) return fail(RZ_EINVAL, "%s: null pointer", what);
+  if (x_format != 0 && x_format != 1)
+    return fail(RZ_EINVAL, "%s: x_format=%d (0 = fp32, 1 = Q8_1)", what, x_format);
+  if (int rc = check_dim(what, "out_dim", out_dim, 1)) return rc;
+  if (int rc = check_dim(what, "in_dim", in_dim, 64)) return rc;
+  if (!aligned(w_q4_0, 4)) return fail(RZ_EALIGN, "%s: w_q4_0 must be 4-byte aligned", what);
+  if (!aligned(x, x_format == 0 ? 16 : 8))
+    return fail(RZ_EALIGN, "%s: x must be %d-byte aligned", what, x_format == 0 ? 16 : 8);
+  if (!aligned(y, 4)) return fail(RZ_EALIGN, "%s: y must be 4-byte aligned", what);
+  return launch_status(rz::launch_q4_0_gemv(static_cast<const uint8_t*>(w_q4_0), x, x_format, y,
+                                            out_dim, in_dim, static_cast<hipStream_t>(stream)),
+                       what);
+}
+
+int rz_swiglu_ffn_q4k(const void* w_gate, const void* w_up, const void* w_down,
+                      const void* x_q8, float* h, void* h_q8, float* y, float* gu,
+                      int hidden_dim, int inter_dim, void* stream) {
+  const char* what = "rz_swiglu_ffn_q4k";
+  if (!w_gate || !w_up || !w_down || !x_q8 || !h || !h_q8 || !y)
+    return fail(RZ_EINVAL, "%s: null pointer", what);
+  if (int rc = check_dim(what, "hidden_dim", hidden_dim, 256)) return rc;
+  if (int rc = check_dim(what, "inter_dim", inter_dim, 256)) return rc;
+  if (hidden_dim > 16384)
+    return fail(RZ_EDIM, "%s: hidden_dim=%d above the fused gate/up limit 16384", what,
+                hidden_dim);
+  if (!aligned(w_gate, 16) || !aligned(w_up, 16) || !aligned(w_down, 16))
+    return fail(RZ_EALIGN, "%s: weight blobs must be 16-byte aligned", what);
+  if (!aligned(x_q8, 8) || !aligned(h_q8, 8))
+    return fail(RZ_EALIGN, "%s: Q8_1 buffers must be 8-byte aligned", what);
+  if (!aligned(h, 4) || !aligned(y, 4) || (gu && !aligned(gu, 4)))
+    return fail(RZ_EALIGN, "%s: fp32 buffers must be 4-byte aligned", what);
+  return launch_status(
+      rz::launch_swiglu_ffn_q4k(static_cast<const uint8_t*>(w_gate),
+                                static_cast<const uint8_t*>(w_up),
+                                static_cast<const uint8_t*>(w_down),
+                                static_cast<const uint8_t*>(x_q8), h,
+                                static_cast<uint8_t*>(h_q8), y, gu, hidden_dim, inter_dim,
+                                static_cast<hipStream_t>(stream)),
+      what);
+}
+
+}  // extern "C"

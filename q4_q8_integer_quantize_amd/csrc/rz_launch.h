@@ -1,0 +1,26 @@
+// rz_launch.h -- host-side launchers of the librz kernels (internal).
+// Arguments are validated by the C ABI (rz_abi.cpp) before these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rz {
+
+hipError_t launch_q8_1_quantize(const float* x, int n, int n_padded, int n_tokens,
+                                uint8_t* out, hipStream_t stream);
+
+// Q4_K x Q8_1 GEMV over super-blocks [sb0, sb0 + nsb) of every row; when
+// `accumulate` is set the result is added to y instead of stored.
+hipError_t launch_q4k_q8_gemv(const uint8_t* w, const uint8_t* xq, float* y, int out_dim,
+                              int in_dim, int n_tokens, hipStream_t stream);
+
+hipError_t launch_q4_0_gemv(const uint8_t* w, const void* x, int x_format, float* y,
+                            int out_dim, int in_dim, hipStream_t stream);
+
+hipError_t launch_swiglu_ffn_q4k(const uint8_t* w_gate, const uint8_t* w_up,
+                                 const uint8_t* w_down, const uint8_t* xq, float* h,
+                                 uint8_t* h_q8, float* y, float* gu, int hidden_dim,
+                                 int inter_dim, hipStream_t stream);
+
+}  // namespace rz

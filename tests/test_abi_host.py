@@ -1,0 +1,162 @@
+"""Host-only checks of the C ABI: librz.so loads, exports every function that
+include/rz.h declares, and rejects bad arguments before any HIP call.
+
+The rejection calls pass made-up device addresses, so they run in a child
+process that sees no GPU (ROCR_VISIBLE_DEVICES=-1): should a case ever pass
+validation by mistake, its launch fails for want of a device instead of
+touching memory.  Such a case shows up as RZ_ELAUNCH and fails its test."""
+import ctypes
+import json
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+import q4_q8_integer_quantize_amd as rz
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rz.h")
+
+# plausible-looking device addresses; validation never dereferences them
+P = 0x7f0000000000
+P_ODD = P + 2
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\s*\*)\s*(rz_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(rz.library_path()):
+        pytest.skip("librz.so not built")
+    return rz.load_library()
+
+
+def test_header_declares_the_four_operations():
+    syms = declared_symbols()
+    for name in ("rz_q8_1_quantize", "rz_q4k_q8_gemv", "rz_q4_0_gemv", "rz_swiglu_ffn_q4k",
+                 "rz_last_error", "rz_abi_version"):
+        assert name in syms
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(rz.library_path())
+    for name in declared_symbols():
+        assert hasattr(raw, name), name
+
+
+def test_abi_version(lib):
+    assert rz.rz_abi_version() == 100
+
+
+_CHILD = r"""
+import json, sys
+sys.path.insert(0, sys.argv[1])
+import q4_q8_integer_quantize_amd as rz
+lib = rz.load_library()
+out = []
+for fn, args in json.loads(sys.stdin.read()):
+    rc = getattr(lib, fn)(*args)
+    out.append([rc, rz.rz_last_error()])
+print(json.dumps(out))
+"""
+
+
+def run_isolated(calls):
+    """[(fn, args)] -> [(rc, message)], executed in a GPU-less child process."""
+    env = dict(os.environ, ROCR_VISIBLE_DEVICES="-1", HIP_VISIBLE_DEVICES="-1")
+    res = subprocess.run([sys.executable, "-c", _CHILD, ROOT], input=json.dumps(calls),
+                         capture_output=True, text=True, env=env, timeout=120)
+    assert res.returncode == 0, res.stderr
+    return [tuple(x) for x in json.loads(res.stdout.strip().splitlines()[-1])]
+
+
+def _rc(fn, *args):
+    rc, msg = run_isolated([(fn, list(args))])[0]
+    _rc.last = msg
+    return rc
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, 896, 1024, 1, P, None), rz.RZ_EINVAL),          # null x
+    ((P, 896, 1024, 1, None, None), rz.RZ_EINVAL),          # null out
+    ((P, 896, 1024, 0, P, None), rz.RZ_EINVAL),             # n_tokens 0
+    ((P, 896, 1024, 9, P, None), rz.RZ_EINVAL),             # n_tokens 9
+    ((P, 896, 1000, 1, P, None), rz.RZ_EDIM),               # n_padded % 32
+    ((P, 1025, 1024, 1, P, None), rz.RZ_EDIM),              # n > n_padded
+    ((P, 0, 1024, 1, P, None), rz.RZ_EDIM),                 # n == 0
+    ((P, 896, 0, 1, P, None), rz.RZ_EDIM),                  # n_padded == 0
+    ((P_ODD, 896, 1024, 1, P, None), rz.RZ_EALIGN),         # x not 4-aligned
+    ((P, 896, 1024, 1, P + 4, None), rz.RZ_EALIGN),         # x_q8 not 8-aligned
+])
+def test_q8_1_quantize_rejects(lib, args, code):
+    assert _rc("rz_q8_1_quantize", *args) == code
+    assert _rc.last.startswith("rz_q8_1_quantize")
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, P, P, 14336, 4096, 1, None), rz.RZ_EINVAL),
+    ((P, None, P, 14336, 4096, 1, None), rz.RZ_EINVAL),
+    ((P, P, None, 14336, 4096, 1, None), rz.RZ_EINVAL),
+    ((P, P, P, 14336, 4096, 0, None), rz.RZ_EINVAL),
+    ((P, P, P, 14336, 4096, 9, None), rz.RZ_EINVAL),
+    ((P, P, P, 14336, 896, 1, None), rz.RZ_EDIM),           # unpadded in_dim
+    ((P, P, P, 14336, 0, 1, None), rz.RZ_EDIM),
+    ((P, P, P, 0, 4096, 1, None), rz.RZ_EDIM),
+    ((P, P, P, -5, 4096, 1, None), rz.RZ_EDIM),
+    ((P, P, P, 14336, 1 << 25, 1, None), rz.RZ_EDIM),
+    ((P + 8, P, P, 14336, 4096, 1, None), rz.RZ_EALIGN),    # weights need 16
+    ((P, P + 4, P, 14336, 4096, 1, None), rz.RZ_EALIGN),
+    ((P, P, P_ODD, 14336, 4096, 1, None), rz.RZ_EALIGN),
+])
+def test_q4k_q8_gemv_rejects(lib, args, code):
+    assert _rc("rz_q4k_q8_gemv", *args) == code
+    assert "rz_q4k_q8_gemv" in _rc.last
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, P, 0, P, 151936, 1024, None), rz.RZ_EINVAL),
+    ((P, P, 2, P, 151936, 1024, None), rz.RZ_EINVAL),       # unknown format
+    ((P, P, -1, P, 151936, 1024, None), rz.RZ_EINVAL),
+    ((P, P, 0, P, 151936, 800, None), rz.RZ_EDIM),          # 800 % 64 != 0
+    ((P, P, 0, P, 151936, 32, None), rz.RZ_EDIM),
+    ((P, P, 0, P, 0, 1024, None), rz.RZ_EDIM),
+    ((P_ODD, P, 0, P, 151936, 1024, None), rz.RZ_EALIGN),
+    ((P, P + 8, 0, P, 151936, 1024, None), rz.RZ_EALIGN),   # fp32 x needs 16
+    ((P, P + 4, 1, P, 151936, 1024, None), rz.RZ_EALIGN),   # Q8_1 x needs 8
+    ((P, P, 0, P_ODD, 151936, 1024, None), rz.RZ_EALIGN),
+])
+def test_q4_0_gemv_rejects(lib, args, code):
+    assert _rc("rz_q4_0_gemv", *args) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, P, P, P, P, P, P, None, 4096, 14336, None), rz.RZ_EINVAL),
+    ((P, P, P, P, None, P, P, None, 4096, 14336, None), rz.RZ_EINVAL),
+    ((P, P, P, P, P, P, None, None, 4096, 14336, None), rz.RZ_EINVAL),
+    ((P, P, P, P, P, P, P, None, 4000, 14336, None), rz.RZ_EDIM),
+    ((P, P, P, P, P, P, P, None, 4096, 14000, None), rz.RZ_EDIM),
+    ((P, P, P, P, P, P, P, None, 32768, 14336, None), rz.RZ_EDIM),   # hidden above fused limit
+    ((P + 8, P, P, P, P, P, P, None, 4096, 14336, None), rz.RZ_EALIGN),
+    ((P, P, P, P + 4, P, P, P, None, 4096, 14336, None), rz.RZ_EALIGN),
+    ((P, P, P, P, P, P, P, P_ODD, 4096, 14336, None), rz.RZ_EALIGN),
+])
+def test_swiglu_ffn_rejects(lib, args, code):
+    assert _rc("rz_swiglu_ffn_q4k", *args) == code
+
+
+def test_error_message_is_per_call(lib):
+    (rc1, m1), (rc2, m2) = run_isolated([("rz_q4k_q8_gemv", [P, P, P, 10, 100, 1, None]),
+                                         ("rz_q4_0_gemv", [P, P, 7, P, 10, 64, None])])
+    assert rc1 == rz.RZ_EDIM and "in_dim=100" in m1
+    assert rc2 == rz.RZ_EINVAL and "x_format=7" in m2
+
+
+def test_binding_rejects_host_tensors():
+    torch = pytest.importorskip("torch")
+    with pytest.raises(ValueError):
+        rz.rz_q8_1_quantize(torch.zeros(32), 32, 32, 1, torch.zeros(40, dtype=torch.uint8), stream=0)

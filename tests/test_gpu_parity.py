@@ -1,0 +1,500 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars (the oracle decides; see oracle/):
+  * Q8_1 blocks: byte-exact (codes, d, s);
+  * GEMV outputs: |y_gpu - y_oracle| <= 1e-5 * terms + 1e-6 per output, where
+    terms = sum of |summands| of the integer form;
+  * integer-exact inputs (d = dmin = 1, activation scale 1, small codes): every
+    sub-block sum and every partial sum is an integer below 2**24, so y must
+    match bit for bit -- this pins the int32 sub-block sums;
+  * SwiGLU chain: per stage (see test_swiglu_*).
+Inputs are seeded synthetic tensors (synth/); weights are fed to both sides,
+and the GEMV tests give the GPU the oracle's own Q8_1 bytes so that a GEMV
+failure is never a quantize failure in disguise.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import q4_q8_integer_quantize_amd as rz
+from golden_io import floats, hexbytes, ints, load, pairs
+from gpu_util import (banner, dev_bytes, dev_f32, empty_bytes, empty_f32, first_mismatch, host,
+                      q8_host_bytes)
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------------------------ helpers
+def gpu_quantize(x: np.ndarray, n_padded: int):
+    x2 = x if x.ndim == 2 else x[None, :]
+    nt, n = x2.shape
+    xd = dev_f32(x2)
+    out = empty_bytes(rz.q8_1_nbytes(n_padded, nt))
+    rz.rz_q8_1_quantize(xd, n, n_padded, nt, out)
+    return q8_host_bytes(out, nt * n_padded // 32).reshape(nt, n_padded // 32, 40)
+
+
+def gpu_q4k(blob: np.ndarray, xq_bytes: np.ndarray, n_tokens: int = 1):
+    out_dim, nsb, _ = blob.shape
+    y = empty_f32(out_dim * n_tokens)
+    rz.rz_q4k_q8_gemv(dev_bytes(blob), dev_bytes(xq_bytes), y, out_dim, nsb * 256, n_tokens)
+    return host(y).reshape(n_tokens, out_dim)
+
+
+def gpu_q4_0(blob: np.ndarray, x, x_format: int):
+    out_dim, nb, _ = blob.shape
+    y = empty_f32(out_dim)
+    xd = dev_f32(x) if x_format == 0 else dev_bytes(x)
+    rz.rz_q4_0_gemv(dev_bytes(blob), xd, x_format, y, out_dim, nb * 32)
+    return host(y)
+
+
+def assert_within(y_gpu, y_ref, terms, what):
+    tol = oracle.gemv_tolerance(terms)
+    err = np.abs(np.asarray(y_gpu, np.float64) - y_ref)
+    bad = err > tol
+    if bad.any():
+        r = int(np.argmax(bad))
+        raise AssertionError("%s: %d of %d outputs outside 1e-5*terms+1e-6; first row %d: "
+                             "gpu=%r oracle=%r tol=%r terms=%r"
+                             % (what, int(bad.sum()), bad.size, r, float(y_gpu[r]),
+                                float(y_ref[r]), float(tol[r]), float(terms[r])))
+
+
+def oracle_q4k(blob, xq, n_tokens=1):
+    """Oracle y and terms for every token: (n_tokens, out_dim) each."""
+    if n_tokens == 1 and xq.d.ndim == 1:
+        y, t = oracle.gemv_q4k_q8_int(blob, xq)
+        return y[None], t[None]
+    ys, ts = zip(*(oracle.gemv_q4k_q8_int(blob, xq.token(t)) for t in range(n_tokens)))
+    return np.stack(ys), np.stack(ts)
+
+
+# ------------------------------------------------------------------ Q8_1
+def test_q8_1_hand_worked_blocks_gpu():
+    banner("q8_1 hand-worked blocks")
+    fx = load("q8_1_blocks.txt")
+    x = np.zeros(128, np.float32)
+    for b, key in enumerate("ABCD"):
+        vals = floats(fx[key + ".x"])
+        x[32 * b: 32 * b + len(vals)] = vals
+    got = gpu_quantize(x, 128)[0]
+    for b, key in enumerate("ABCD"):
+        blk = got[b]
+        assert blk[0:4].view("<f4")[0] == np.float32(float(fx[key + ".d"]))
+        assert blk[4:8].view("<f4")[0] == np.float32(float(fx[key + ".s"]))
+        q = np.zeros(32, np.int64)
+        qv = ints(fx[key + ".q"])
+        q[:len(qv)] = qv
+        assert np.array_equal(blk[8:40].view(np.int8).astype(np.int64), q), key
+    assert np.array_equal(got, oracle.q8_1_to_bytes(oracle.quantize_q8_1(x, 128)))
+
+
+def _q8_case(kind, n, nt, seed):
+    g = np.random.default_rng(seed)
+    if kind == "normal":
+        return synth.activation(g, n, nt if nt > 1 else None)
+    if kind == "rmsnorm":
+        return synth.rmsnorm_activation(synth.rng(1, 0), synth.rng(1, synth.T_GAMMA), n)
+    if kind == "wide":
+        x = g.standard_normal((nt, n)) * np.exp(g.uniform(-20, 20, (nt, n)))
+        return x.astype(np.float32)[0] if nt == 1 else x.astype(np.float32)
+    if kind == "tiny":
+        return (g.standard_normal((nt, n)) * 1e-30).astype(np.float32).squeeze(0) if nt == 1 else \
+            (g.standard_normal((nt, n)) * 1e-30).astype(np.float32)
+    if kind == "huge":
+        return (g.standard_normal((nt, n)) * 1e30).astype(np.float32).squeeze(0) if nt == 1 else \
+            (g.standard_normal((nt, n)) * 1e30).astype(np.float32)
+    if kind == "ties":
+        # halves at d = 1: every code is a round-half-to-even decision
+        x = (g.integers(-254, 255, (nt, n)) / 2.0).astype(np.float32)
+        x[:, ::32] = 127.0
+        return x[0] if nt == 1 else x
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("kind,n,n_padded,nt", [
+    ("normal", 896, 1024, 1),      # padded activation of the 896-wide workloads
+    ("rmsnorm", 4096, 4096, 1),    # attention-projection input
+    ("normal", 4096, 4096, 8),     # 8-token batch
+    ("normal", 14336, 14336, 1),   # requantized FFN width
+    ("normal", 1000, 1024, 1),     # ragged tail inside a block
+    ("normal", 33, 64, 3),
+    ("normal", 1, 32, 1),
+    ("normal", 100, 128, 5),
+    ("wide", 2048, 2048, 2),
+    ("tiny", 512, 512, 1),
+    ("huge", 512, 512, 2),
+    ("ties", 1024, 1024, 4),
+])
+def test_q8_1_matches_oracle(kind, n, n_padded, nt):
+    banner("q8_1", kind, n, n_padded, nt)
+    x = _q8_case(kind, n, nt, seed=n + nt)
+    got = gpu_quantize(x, n_padded)
+    want = oracle.q8_1_to_bytes(oracle.quantize_q8_1(x, n_padded)).reshape(got.shape)
+    mm = first_mismatch(got, want)
+    assert mm is None, "first differing byte %s gpu=%d oracle=%d (%d bytes differ)" % mm
+
+
+def test_q8_1_zero_input_gives_zero_blocks():
+    banner("q8_1 zeros")
+    got = gpu_quantize(np.zeros(256, np.float32), 256)
+    assert not got.any()
+
+
+# ------------------------------------------------------------------ Q4_K pins
+def test_q4k_hand_worked_superblock_gpu():
+    banner("q4k hand-worked super-block")
+    fx = load("q4k_superblock.txt")
+    sb = hexbytes(fx["header_hex"]) + hexbytes(fx["qs_fill_hex"]) * 128
+    blob = np.frombuffer(sb * 3, np.uint8).reshape(3, 1, 144).copy()   # three identical rows
+    ones = np.zeros((8, 40), np.uint8)
+    ones[:, 0:4] = np.frombuffer(np.float32(1).tobytes(), np.uint8)
+    ones[:, 4:8] = np.frombuffer(np.float32(32).tobytes(), np.uint8)
+    ones[:, 8:40] = 1
+    y = gpu_q4k(blob, ones)[0]
+    assert np.all(y == float(fx["y_ones"])), y
+
+
+def test_q4k_nibble_order_gpu():
+    banner("q4k nibble order")
+    fx = load("q4k_nibble_order.txt")
+    raw = bytearray(hexbytes(fx["header_hex"]) + bytes(128))
+    for k, v in pairs(fx["qs_set"], int, lambda s: int(s, 16)):
+        raw[16 + k] = v
+    blob = np.frombuffer(bytes(raw), np.uint8).reshape(1, 1, 144).copy()
+    x = np.zeros((8, 40), np.uint8)
+    x[1, 0:4] = np.frombuffer(np.float32(1).tobytes(), np.uint8)
+    x[1, 4:8] = np.frombuffer(np.float32(1).tobytes(), np.uint8)
+    x[1, 8] = 1
+    assert gpu_q4k(blob, x)[0][0] == float(fx["y_onehot32"])
+
+
+def _integer_q8(nblocks, seed, qmax=8):
+    g = np.random.default_rng(seed)
+    q = g.integers(-qmax, qmax + 1, size=(nblocks, 32)).astype(np.int8)
+    xq = oracle.Q8Blocks(np.ones(nblocks, np.float32), q.sum(axis=1).astype(np.float32), q)
+    return xq
+
+
+@pytest.mark.parametrize("out_dim,in_dim", [(5, 256), (64, 512), (300, 1024), (37, 2048),
+                                            (19, 1280)])
+def test_q4k_integer_exact_inputs_bit_exact(out_dim, in_dim):
+    """d = dmin = 1, activation d = 1, codes in [-8, 8]: y is an integer below
+    2**24 computed exactly by any summation order, so the GPU must match the
+    oracle bit for bit; any wrong int32 sub-block sum shows up as a difference."""
+    banner("q4k integer-exact", out_dim, in_dim)
+    blob = synth.q4k_weights(synth.rng(60, out_dim), out_dim, in_dim, d_fixed=1.0, dmin_fixed=1.0)
+    xq = _integer_q8(in_dim // 32, seed=in_dim)
+    y_ref, _ = oracle.gemv_q4k_q8_int(blob, xq)
+    y = gpu_q4k(blob, oracle.q8_1_to_bytes(xq))[0]
+    assert np.all(np.abs(y_ref) < 2 ** 24)
+    mm = first_mismatch(y.astype(np.float64), y_ref)
+    assert mm is None, "row %s gpu=%r oracle=%r (%d rows differ)" % mm
+
+
+# ------------------------------------------------------------------ Q4_K parity
+@pytest.mark.parametrize("out_dim,in_dim", [
+    (1, 256), (3, 256), (64, 256), (65, 256), (257, 256),
+    (1, 512), (3, 512), (64, 512), (65, 512), (257, 512),
+    (896, 1024),          # the 896-wide workload, in_dim padded to 1024
+    (100, 768), (129, 1280), (70, 3072), (33, 14336),
+    (40, 20480),          # longer than one register window: two column chunks
+])
+def test_q4k_matches_oracle(out_dim, in_dim):
+    banner("q4k", out_dim, in_dim)
+    blob = synth.q4k_weights(synth.rng(10, out_dim * 7 + in_dim), out_dim, in_dim)
+    xq = oracle.quantize_q8_1(synth.activation(synth.rng(10, in_dim), in_dim))
+    y_ref, terms = oracle.gemv_q4k_q8_int(blob, xq)
+    y = gpu_q4k(blob, oracle.q8_1_to_bytes(xq))[0]
+    assert_within(y, y_ref, terms, "q4k %dx%d" % (out_dim, in_dim))
+
+
+def test_q4k_padding_invariance_gpu():
+    """in_dim 896 zero-padded to 1024: re-randomising the padded half of the last
+    super-block (nibbles and 6-bit fields of sub-blocks 4..7) leaves y bit-identical,
+    and y agrees with the oracle restricted to the first 896 values."""
+    banner("q4k padding invariance 896->1024")
+    n, in_dim, rows = 896, 1024, 896
+    blob = synth.q4k_weights(synth.rng(0, synth.T_W0), rows, in_dim)
+    x = synth.activation(synth.rng(0, synth.T_ACT), n)
+    xq = oracle.quantize_q8_1(x, in_dim)
+    xb = oracle.q8_1_to_bytes(xq)
+    y1 = gpu_q4k(blob, xb)[0]
+    g = np.random.default_rng(1234)
+    b2 = blob.copy()
+    b2[:, -1, 16 + 64:144] = g.integers(0, 256, (rows, 64), dtype=np.uint8)
+    r = g.integers(0, 256, (rows, 12), dtype=np.uint8)
+    b2[:, -1, 4:12] = (blob[:, -1, 4:12] & 63) | (r[:, 0:8] & 0xC0)
+    b2[:, -1, 12:16] = r[:, 8:12]
+    y2 = gpu_q4k(b2, xb)[0]
+    assert np.array_equal(y1, y2)
+    w = oracle.dequantize_q4k(blob)[:, :n]
+    xh = oracle.dequantize_q8_1(xq)[:n]
+    assert_within(y1, w @ xh, np.abs(w) @ np.abs(xh) + oracle.gemv_q4k_q8_int(blob, xq)[1],
+                  "q4k padded")
+
+
+def test_q4k_scaling_and_row_permutation_gpu():
+    """Doubling every activation d and s doubles y exactly; permuting weight rows
+    permutes y exactly."""
+    banner("q4k scaling/permutation")
+    out_dim, in_dim = 333, 4096
+    blob = synth.q4k_weights(synth.rng(11, 1), out_dim, in_dim)
+    xq = oracle.quantize_q8_1(synth.activation(synth.rng(11, 0), in_dim))
+    y = gpu_q4k(blob, oracle.q8_1_to_bytes(xq))[0]
+    x2 = oracle.Q8Blocks(xq.d * np.float32(2), xq.s * np.float32(2), xq.q)
+    y2 = gpu_q4k(blob, oracle.q8_1_to_bytes(x2))[0]
+    assert np.array_equal(y2, 2 * y)
+    perm = np.random.default_rng(3).permutation(out_dim)
+    yp = gpu_q4k(blob[perm].copy(), oracle.q8_1_to_bytes(xq))[0]
+    assert np.array_equal(yp, y[perm])
+
+
+@pytest.mark.parametrize("n_tokens", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_q4k_token_batch(n_tokens):
+    """Each token against the oracle, and the batched result equal bit for bit
+    to one-token launches (tokens share the weight pass, not arithmetic)."""
+    banner("q4k batch", n_tokens)
+    out_dim, in_dim = 515, 4096
+    blob = synth.q4k_weights(synth.rng(4, 1), out_dim, in_dim)
+    X = synth.activation(synth.rng(4, 0), in_dim, n_tokens=n_tokens)
+    xq = oracle.quantize_q8_1(X)
+    xb = oracle.q8_1_to_bytes(xq)
+    Y = gpu_q4k(blob, xb, n_tokens)
+    y_ref, terms = oracle_q4k(blob, xq, n_tokens)
+    for t in range(n_tokens):
+        assert_within(Y[t], y_ref[t], terms[t], "token %d" % t)
+        single = gpu_q4k(blob, xb[t])[0]
+        assert np.array_equal(single, Y[t]), "token %d differs from its single launch" % t
+
+
+# ------------------------------------------------------------------ full-size workloads
+def test_q4k_attention_projections_full():
+    """Q 4096x4096, K/V 1024x4096, O 4096x4096 sharing one RMSNorm'd activation."""
+    w = synth.WORKLOADS["attn_4096"]
+    x = synth.rmsnorm_activation(synth.rng(1, synth.T_ACT), synth.rng(1, synth.T_GAMMA), w["n"])
+    xq = oracle.quantize_q8_1(x, w["in_dim"])
+    got_q8 = gpu_quantize(x, w["in_dim"])[0]
+    assert np.array_equal(got_q8, oracle.q8_1_to_bytes(xq))
+    for k, (name, rows) in enumerate(w["shapes"]):
+        banner("attention", name, rows)
+        blob = synth.q4k_weights(synth.rng(1, synth.T_W0 + k), rows, w["in_dim"])
+        y_ref, terms = oracle.gemv_q4k_q8_int(blob, xq)
+        y = gpu_q4k(blob, got_q8)[0]
+        assert_within(y, y_ref, terms, "attention " + name)
+
+
+def test_q4k_gate_4096_to_14336_full():
+    """The measured GEMV (4096 -> 14336, one token) in the launch configuration
+    the benchmark times: GPU quantize then GPU GEMV, every output checked."""
+    banner("q4k 4096->14336 full")
+    blob = synth.q4k_weights(synth.rng(2, synth.T_W0), 14336, 4096)
+    x = synth.activation(synth.rng(2, synth.T_ACT), 4096)
+    xq = oracle.quantize_q8_1(x)
+    got_q8 = gpu_quantize(x, 4096)[0]
+    assert np.array_equal(got_q8, oracle.q8_1_to_bytes(xq))
+    y_ref, terms = oracle.gemv_q4k_q8_int(blob, xq)
+    assert_within(gpu_q4k(blob, got_q8)[0], y_ref, terms, "gate 4096->14336")
+
+
+def test_q4k_batch8_full_sampled():
+    """8 tokens x 4096 -> 14336: all outputs of tokens 0 and 7, and 512 sampled
+    rows of every token, against the oracle."""
+    banner("q4k batch8 4096->14336")
+    w = synth.WORKLOADS["q4k_batch8"]
+    blob = synth.q4k_weights(synth.rng(4, synth.T_W0), w["out_dim"], w["in_dim"])
+    X = synth.activation(synth.rng(4, synth.T_ACT), w["in_dim"], n_tokens=8)
+    xq = oracle.quantize_q8_1(X)
+    got_q8 = gpu_quantize(X, w["in_dim"])
+    assert np.array_equal(got_q8, oracle.q8_1_to_bytes(xq))
+    Y = gpu_q4k(blob, got_q8, 8)
+    rows = np.sort(np.random.default_rng(8).choice(w["out_dim"], 512, replace=False))
+    for t in range(8):
+        if t in (0, 7):
+            y_ref, terms = oracle.gemv_q4k_q8_int(blob, xq.token(t))
+            assert_within(Y[t], y_ref, terms, "batch8 token %d" % t)
+        else:
+            y_ref, terms = oracle.gemv_q4k_q8_int(blob[rows], xq.token(t))
+            assert_within(Y[t][rows], y_ref, terms, "batch8 token %d (sampled)" % t)
+
+
+# ------------------------------------------------------------------ Q4_0
+def test_q4_0_hand_worked_block_gpu():
+    banner("q4_0 hand-worked block")
+    fx = load("q4_0_block.txt")
+    blk = hexbytes(fx["block_hex"])
+    zero_blk = np.float16(0).tobytes() + bytes(16)
+    blob = np.frombuffer(blk + zero_blk, np.uint8).reshape(1, 2, 18).copy()
+    for k, key in ((0, "y_onehot0"), (16, "y_onehot16")):
+        x = np.zeros(64, np.float32)
+        x[k] = 1.0
+        assert gpu_q4_0(blob, x, 0)[0] == float(fx[key])
+        xq = np.zeros((2, 40), np.uint8)
+        xq[0, 0:4] = np.frombuffer(np.float32(1).tobytes(), np.uint8)
+        xq[0, 4:8] = np.frombuffer(np.float32(1).tobytes(), np.uint8)
+        xq[0, 8 + k] = 1
+        assert gpu_q4_0(blob, xq, 1)[0] == float(fx[key])
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("out_dim,in_dim", [
+    (1, 64), (3, 128), (65, 192), (257, 1024), (130, 4096),
+    (33, 8192),      # fp32: two pair slots per lane
+    (17, 16384),     # fp32: two column chunks
+    (40, 20480),     # both formats chunked
+])
+def test_q4_0_matches_oracle(fmt, out_dim, in_dim):
+    banner("q4_0", "fp32" if fmt == 0 else "q8_1", out_dim, in_dim)
+    blob = synth.q4_0_weights(synth.rng(30, out_dim + in_dim), out_dim, in_dim)
+    x = synth.activation(synth.rng(30, in_dim), in_dim)
+    if fmt == 0:
+        y_ref, terms = oracle.gemv_q4_0_f32(blob, x)
+        y = gpu_q4_0(blob, x, 0)
+    else:
+        xq = oracle.quantize_q8_1(x)
+        y_ref, terms = oracle.gemv_q4_0_q8_int(blob, xq)
+        y = gpu_q4_0(blob, oracle.q8_1_to_bytes(xq), 1)
+    assert_within(y, y_ref, terms, "q4_0 %dx%d fmt %d" % (out_dim, in_dim, fmt))
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_q4_0_lm_head_full(fmt):
+    """LM head 151936 x (896 padded to 1024), every logit checked."""
+    banner("q4_0 lm head full", fmt)
+    w = synth.WORKLOADS["lm_head_q4_0"]
+    blob = synth.q4_0_weights(synth.rng(3, synth.T_W0), w["out_dim"], w["in_dim"])
+    x = np.zeros(w["in_dim"], np.float32)
+    x[:w["n"]] = synth.activation(synth.rng(3, synth.T_ACT), w["n"])
+    if fmt == 0:
+        y_ref, terms = oracle.gemv_q4_0_f32(blob, x)
+        y = gpu_q4_0(blob, x, 0)
+    else:
+        xq = oracle.quantize_q8_1(x[:w["n"]], w["in_dim"])
+        y_ref, terms = oracle.gemv_q4_0_q8_int(blob, xq)
+        y = gpu_q4_0(blob, oracle.q8_1_to_bytes(xq), 1)
+    assert_within(y, y_ref, terms, "lm head fmt %d" % fmt)
+
+
+def test_q4_0_padding_invariance_gpu():
+    banner("q4_0 padding invariance")
+    rows, n, in_dim = 500, 896, 1024
+    blob = synth.q4_0_weights(synth.rng(3, 1), rows, in_dim)
+    x = np.zeros(in_dim, np.float32)
+    x[:n] = synth.activation(synth.rng(3, 0), n)
+    y1 = gpu_q4_0(blob, x, 0)
+    b2 = blob.copy()
+    b2[:, 28:, 2:18] = np.random.default_rng(5).integers(0, 256, (rows, 4, 16), dtype=np.uint8)
+    assert np.array_equal(y1, gpu_q4_0(b2, x, 0))
+
+
+# ------------------------------------------------------------------ SwiGLU chain
+def run_ffn(wg, wu, wd, xq_bytes, hidden, inter, with_gu=True):
+    h = empty_f32(inter)
+    hq = empty_bytes(rz.q8_1_nbytes(inter))
+    y = empty_f32(hidden)
+    gu = empty_f32(2 * inter) if with_gu else None
+    rz.rz_swiglu_ffn_q4k(dev_bytes(wg), dev_bytes(wu), dev_bytes(wd), dev_bytes(xq_bytes), h, hq,
+                         y, gu, hidden, inter)
+    out = dict(h=host(h), hq=q8_host_bytes(hq, inter // 32), y=host(y))
+    if with_gu:
+        g_u = host(gu)
+        out["g"], out["u"] = g_u[:inter], g_u[inter:]
+    return out
+
+
+@pytest.mark.parametrize("hidden,inter", [(256, 512), (512, 768), (1024, 2816), (4096, 14336)])
+def test_swiglu_ffn_chain(hidden, inter):
+    """Stage by stage:
+      (i)   g, u within the GEMV bound of the oracle's g, u;
+      (ii)  h within the bound propagated through silu(g) * u;
+      (iii) h_q8 equals the standalone GPU quantize of the GPU's own h (byte-exact;
+            the standalone quantize is byte-exact against the oracle elsewhere), and
+            against the oracle's h_q8: d within the propagated bound, codes within
+            one step, equal wherever the oracle's h/d is clear of a rounding tie;
+      (iv)  y equals the standalone GPU GEMV over the GPU's h_q8 (bit-exact), the
+            standalone down GEMV over the oracle's h_q8 is within the GEMV bound of
+            the oracle, and the chain's y is within the GEMV bound plus the
+            activation difference |W| . |x_hat_gpu - x_hat_oracle|."""
+    banner("swiglu", hidden, inter)
+    cid = 2 if (hidden, inter) == (4096, 14336) else 20 + hidden // 256
+    wg = synth.q4k_weights(synth.rng(cid, synth.T_W0), inter, hidden)
+    wu = synth.q4k_weights(synth.rng(cid, synth.T_W0 + 1), inter, hidden)
+    wd = synth.q4k_weights(synth.rng(cid, synth.T_W0 + 2), hidden, inter)
+    x = synth.activation(synth.rng(cid, synth.T_ACT), hidden)
+    xq = oracle.quantize_q8_1(x)
+    st = oracle.ffn_swiglu_q4k(wg, wu, wd, xq)
+    got = run_ffn(wg, wu, wd, oracle.q8_1_to_bytes(xq), hidden, inter)
+
+    # (i)
+    assert_within(got["g"], st["g"], st["g_terms"], "gate")
+    assert_within(got["u"], st["u"], st["u_terms"], "up")
+    # (ii)
+    tol_h = oracle.h_tolerance(st["g"], st["u"], st["tol_g"], st["tol_u"], st["h"])
+    err_h = np.abs(got["h"].astype(np.float64) - st["h"])
+    assert np.all(err_h <= tol_h), "h: %d outside, worst ratio %.3g" % (
+        int((err_h > tol_h).sum()), float(np.max(err_h / tol_h)))
+    # (iii) self-consistency with the standalone quantize kernel
+    requant = gpu_quantize(got["h"], inter)[0]
+    assert np.array_equal(got["hq"], requant)
+    # (iii) against the oracle's blocks
+    d_gpu = got["hq"][:, 0:4].copy().view("<f4")[:, 0].astype(np.float64)
+    q_gpu = got["hq"][:, 8:40].copy().view(np.int8).astype(np.int64)
+    d_ref = st["h_q8"].d.astype(np.float64)
+    q_ref = st["h_q8"].q.astype(np.int64)
+    amax_tol = np.max(tol_h.reshape(-1, 32), axis=1)
+    assert np.all(np.abs(d_gpu - d_ref) <= amax_tol / 127 + 4 * 2.0 ** -24 * d_ref)
+    assert np.all(np.abs(q_gpu - q_ref) <= 1)
+    ratio = st["h"].reshape(-1, 32) / np.where(d_ref > 0, d_ref, 1.0)[:, None]
+    frac = np.abs(ratio - np.floor(ratio) - 0.5)
+    margin = (tol_h.reshape(-1, 32) / np.where(d_ref > 0, d_ref, 1.0)[:, None]
+              + np.abs(ratio) * (np.abs(d_gpu - d_ref) / np.where(d_ref > 0, d_ref, 1.0))[:, None]
+              + 1e-4)
+    clear = frac > margin
+    assert np.array_equal(q_gpu[clear], q_ref[clear])
+    # (iv)
+    y_chain = gpu_q4k(wd, got["hq"])[0]
+    assert np.array_equal(y_chain, got["y"])
+    y_std = gpu_q4k(wd, oracle.q8_1_to_bytes(st["h_q8"]))[0]
+    assert_within(y_std, st["y"], st["y_terms"], "down over oracle h_q8")
+    xhat_gpu = (d_gpu[:, None] * q_gpu).reshape(-1)
+    xhat_ref = oracle.dequantize_q8_1(st["h_q8"])
+    w_abs = np.abs(oracle.dequantize_q4k(wd))
+    extra = w_abs @ np.abs(xhat_gpu - xhat_ref)
+    assert_within(got["y"], st["y"], st["y_terms"] + extra / oracle.GEMV_REL, "chain y")
+
+
+def test_swiglu_zero_up_gives_zero_gpu():
+    banner("swiglu zero up")
+    hidden, inter = 512, 1024
+    wg = synth.q4k_weights(synth.rng(5, 1), inter, hidden)
+    wu = synth.q4k_weights(synth.rng(5, 2), inter, hidden, d_fixed=0.0, dmin_fixed=0.0)
+    wd = synth.q4k_weights(synth.rng(5, 3), hidden, inter)
+    xq = oracle.quantize_q8_1(synth.activation(synth.rng(5, 0), hidden))
+    got = run_ffn(wg, wu, wd, oracle.q8_1_to_bytes(xq), hidden, inter)
+    assert np.all(got["u"] == 0) and np.all(got["h"] == 0)
+    assert not got["hq"].any() and np.all(got["y"] == 0)
+
+
+def test_swiglu_optional_gu_pointer():
+    banner("swiglu without gu")
+    hidden, inter = 1024, 2048
+    wg = synth.q4k_weights(synth.rng(6, 1), inter, hidden)
+    wu = synth.q4k_weights(synth.rng(6, 2), inter, hidden)
+    wd = synth.q4k_weights(synth.rng(6, 3), hidden, inter)
+    xb = oracle.q8_1_to_bytes(oracle.quantize_q8_1(synth.activation(synth.rng(6, 0), hidden)))
+    a = run_ffn(wg, wu, wd, xb, hidden, inter, with_gu=True)
+    b = run_ffn(wg, wu, wd, xb, hidden, inter, with_gu=False)
+    assert np.array_equal(a["h"], b["h"]) and np.array_equal(a["hq"], b["hq"])
+    assert np.array_equal(a["y"], b["y"])
+
+
+# ------------------------------------------------------------------ errors on device tensors
+def test_binding_errors_on_gpu():
+    banner("binding errors")
+    t = dev_f32(np.zeros(64, np.float32))
+    with pytest.raises(rz.RzError):
+        rz.rz_q4k_q8_gemv(t, t, t, 1, 100, 1)
+    with pytest.raises(ValueError):
+        rz.rz_q4k_q8_gemv(t, t, t, 1, 256, 1)     # buffers too small for the shape
