@@ -77,7 +77,8 @@ int rz_q8_1_quantize(const float* x, int n, int n_padded, int n_tokens,
  *   w_q4k    [out_dim][in_dim/256] super-blocks, 16-byte aligned
  *   x_q8     [n_tokens][in_dim/32] Q8_1 blocks, 8-byte aligned
  *   y        out: fp32 [n_tokens][out_dim] (token-major), 4-byte aligned
- *   out_dim  >= 1; in_dim multiple of 256 (padded); both <= RZ_MAX_DIM
+ *   out_dim  >= 1; in_dim multiple of 256 (padded); both <= RZ_MAX_DIM;
+ *            the matrix (out_dim * in_dim/256 * 144 bytes) < 2 GiB
  *   n_tokens 1..RZ_MAX_TOKENS
  * Errors: RZ_EINVAL, RZ_EDIM, RZ_EALIGN, RZ_ELAUNCH. */
 int rz_q4k_q8_gemv(const void* w_q4k, const void* x_q8, float* y,
@@ -113,7 +114,8 @@ int rz_q4_0_gemv(const void* w_q4_0, const void* x, int x_format, float* y,
  *   y             out: fp32 [hidden_dim]
  *   gu            optional out (NULL to skip): fp32 [2][inter_dim], g then u
  *   hidden_dim, inter_dim  multiples of 256; hidden_dim <= 16384 (the fused
- *                 gate/up kernel keeps a row's activation in registers)
+ *                 gate/up kernel keeps a row's activation in registers);
+ *                 each matrix < 2 GiB
  * Two kernels run in order on `stream`; h and h_q8 are written by the first
  * and read by the second.  Errors: RZ_EINVAL, RZ_EDIM, RZ_EALIGN, RZ_ELAUNCH. */
 int rz_swiglu_ffn_q4k(const void* w_gate, const void* w_up, const void* w_down,

@@ -4,14 +4,17 @@
 // Integer form of the product (realizar 0.8.5 src/cuda/executor/cached.rs,
 // transformer_layer_gpu_true_dp4a, steps 3 and 6: Q4K x Q8 integer dot
 // product): for every 32-value sub-block j of a super-block,
-//   isum_j = sum_l q4[32 j + l] * q8[32 j + l]         (exact, int32)
-//   y     += d * sc_j * dx_j * isum_j - dmin * m_j * s_j   (fp32)
+//   isum_j = sum_l q4[32 j + l] * q8[32 j + l]                 (exact, int32)
+//   y     += d * (d_x,j * (sc_j * isum_j)) - dmin * (s_j * m_j)    (fp32)
+// sc_j * isum_j is an exact 24-bit integer product (|.| < 2**22).
 //
 // Lane roles inside a wave (lane = 8 * team + i):
 //   i (0..7)   reads the 16-byte slice i of a super-block's qs: chunk c = i/2,
 //              half h = i%2, i.e. 16 low nibbles of sub-block 2c and 16 high
-//              nibbles of sub-block 2c+1, both at positions 16h..16h+15.
-//              After exchanging half sums with lane i^1 it owns sub-block j = i.
+//              nibbles of sub-block 2c+1, both at positions 16h..16h+15.  One
+//              load instruction therefore covers each super-block's 128 qs
+//              bytes contiguously.  After adding the partner's (lane i^1)
+//              half sum the lane owns sub-block j = i.
 //   team (0..7) rs = team / TPR picks one of the RW = 8/TPR rows processed side
 //              by side; tslot = team % TPR takes super-blocks sb = s*TPR + tslot
 //              for slots s < S.  A row is reduced over its 8*TPR lanes.
@@ -34,6 +37,9 @@ struct XSlots {
 struct LaneRole {
   int lane, i, c, h, rs, tslot;
   // sub-block j = i: where its 6-bit scale and min sit in the 12 scale bytes
+  //   j < 4 : sc = scales[j] & 63, m = scales[j+4] & 63
+  //   j >= 4: sc = (scales[j+4] & 15) | (scales[j-4] >> 6) << 4
+  //           m  = (scales[j+4] >> 4) | (scales[j]   >> 6) << 4
   bool hij;
   uint32_t sh_sc, sh_m, len_lo, sh_hi, len_hi;
 };
@@ -50,9 +56,6 @@ __device__ __forceinline__ LaneRole make_role() {
   r.tslot = team % TPR;
   const int jj = r.i & 3;
   r.hij = r.i >= 4;
-  // j < 4 : sc = scales[j] & 63, m = scales[j+4] & 63
-  // j >= 4: sc = (scales[j+4] & 15) | (scales[j-4] >> 6) << 4
-  //         m  = (scales[j+4] >> 4) | (scales[j]   >> 6) << 4
   r.sh_sc = 8u * jj;
   r.sh_m = r.hij ? 8u * jj + 4u : 8u * jj;
   r.len_lo = r.hij ? 4u : 6u;
@@ -95,53 +98,122 @@ __device__ __forceinline__ void load_x_slots(XSlots<S, NT>& xs, const uint8_t* _
   }
 }
 
-// Partial dot products of R*RW rows (RW = 8/TPR side by side, R unrolled):
-// rows row_base + r*RW + rs for r < R.  Rows at or past out_dim are clamped
-// to the last row (their results are discarded by the caller).  On return
-// acc[r][t] holds the full row sum in every lane of the row's lane group.
-template <int TPR, int S, int R, int NT>
-__device__ __forceinline__ void q4k_rows(float (&acc)[R][NT], const uint8_t* __restrict__ w,
-                                         size_t row_bytes, long row_base, int out_dim,
-                                         int nsb, const XSlots<S, NT>& xs, const LaneRole& ro) {
+// Weights of R*RW rows (RW = 8/TPR side by side, R unrolled) for one lane:
+// the 16-byte header and the lane's 16-byte qs slice of each slot.
+template <int S, int R>
+struct WTile {
+  u32x4 hd[R][S];
+  u32x4 qs[R][S];
+};
+
+// A weight matrix read through a raw buffer descriptor: offsets are 32-bit,
+// and a read past `bytes` returns zeros instead of faulting, so rows past
+// out_dim and slots past the row need no clamping (their activation
+// registers are zero, or their results are never stored).
+struct WSrc {
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t row_bytes;
+};
+
+__device__ __forceinline__ WSrc make_wsrc(const uint8_t* w, uint32_t row_bytes, uint32_t bytes) {
+  WSrc src;
+  src.rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)w, (short)0, (int)bytes, kBufferWord3);
+  src.row_bytes = row_bytes;
+  return src;
+}
+
+// Per-lane byte offsets of a lane's header and qs slice for each slot,
+// relative to the start of the lane's row: super-block sb0 + s*TPR + tslot.
+template <int TPR, int S>
+struct LaneOffsets {
+  uint32_t hd[S];
+  uint32_t qs[S];
+};
+
+template <int TPR, int S>
+__device__ __forceinline__ LaneOffsets<TPR, S> lane_offsets(const WSrc& src, int sb0,
+                                                            const LaneRole& ro) {
+  LaneOffsets<TPR, S> o;
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    o.hd[s] = (uint32_t)ro.rs * src.row_bytes + (uint32_t)(sb0 + s * TPR + ro.tslot) * kQ4KBytes;
+    o.qs[s] = o.hd[s] + 16u + 16u * (uint32_t)ro.i;
+  }
+  return o;
+}
+
+// Rows row_base + r*RW + rs for r < R; row_base is wave-uniform.  The whole
+// offset travels in the per-lane VGPR offset, which is the part the hardware
+// range-checks against the descriptor (the scalar offset is not checked).
+template <int TPR, int S, int R>
+__device__ __forceinline__ void load_w_tile(WTile<S, R>& wt, const WSrc& src,
+                                            const LaneOffsets<TPR, S>& lo, uint32_t row_base) {
   constexpr int RW = 8 / TPR;
 #pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[r][t] = 0.0f;
-
-  u32x4 hd[R][S], qs[R][S];
-#pragma unroll
   for (int r = 0; r < R; ++r) {
-    long row = row_base + (long)r * RW + ro.rs;
-    if (row >= out_dim) row = out_dim - 1;
-    const uint8_t* wrow = w + (size_t)row * row_bytes;
+    const uint32_t roff = (row_base + (uint32_t)(r * RW)) * src.row_bytes;
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-      int sb = s * TPR + ro.tslot;
-      if (sb >= nsb) sb = nsb - 1;   // inactive slot: its x registers are zero
-      const uint8_t* p = wrow + (size_t)sb * kQ4KBytes;
-      hd[r][s] = *(const u32x4*)p;
-      qs[r][s] = *(const u32x4*)(p + 16 + 16 * ro.i);
+      wt.hd[r][s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  src.rsrc, lo.hd[s] + roff, 0, 0));
+      wt.qs[r][s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  src.rsrc, lo.qs[s] + roff, 0, 0));
     }
   }
+}
 
+// Integer exchange with lane ^ 1 (DPP quad_perm [1,0,3,2]).
+__device__ __forceinline__ int xor1_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                               CTRL, ROW_MASK, 0xF, false));
+}
+
+// Sum over aligned groups of W lanes (W in 8, 16, 32, 64) with DPP.  The full
+// sum is valid in the LAST lane of each group (for W <= 16 in every lane).
+template <int W>
+__device__ __forceinline__ float group_sum_dpp(float v) {
+  static_assert(W == 8 || W == 16 || W == 32 || W == 64, "group width");
+  v += dpp_f<0xB1, 0xF>(v);    // quad_perm [1,0,3,2]: lane ^ 1
+  v += dpp_f<0x4E, 0xF>(v);    // quad_perm [2,3,0,1]: lane ^ 2
+  v += dpp_f<0x141, 0xF>(v);   // row_half_mirror: quads 0 <-> 1 of each 8
+  if constexpr (W >= 16) v += dpp_f<0x140, 0xF>(v);   // row_mirror: 8-groups of a row
+  if constexpr (W >= 32) v += dpp_f<0x142, 0xA>(v);   // row_bcast:15 into rows 1, 3
+  if constexpr (W >= 64) v += dpp_f<0x143, 0xC>(v);   // row_bcast:31 into rows 2, 3
+  return v;
+}
+
+// Multiply-accumulate one tile into acc[r][t] and reduce each row over its
+// 8*TPR lanes.  On return acc[r][t] is the full row sum in the last lane of
+// the row's lane group.
+template <int TPR, int S, int R, int NT>
+__device__ __forceinline__ void q4k_tile_dot(float (&acc)[R][NT], const WTile<S, R>& wt,
+                                             const XSlots<S, NT>& xs, const LaneRole& ro) {
 #pragma unroll
   for (int r = 0; r < R; ++r) {
 #pragma unroll
+    for (int t = 0; t < NT; ++t) acc[r][t] = 0.0f;
+#pragma unroll
     for (int s = 0; s < S; ++s) {
-      const u32x4 H = hd[r][s];
-      const float d = f16_lo(H.x), dmin = f16_hi(H.x);
+      const u32x4 H = wt.hd[r][s];
+      const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)(H.x & 0xffffu));
+      const _Float16 dmin = __builtin_bit_cast(_Float16, (uint16_t)(H.x >> 16));
       const uint32_t a_sc = ro.hij ? H.w : H.y;
       const uint32_t a_m = ro.hij ? H.w : H.z;
-      const uint32_t sc = bits(a_sc, ro.sh_sc, ro.len_lo) | (bits(H.y, ro.sh_hi, ro.len_hi) << 4);
-      const uint32_t m = bits(a_m, ro.sh_m, ro.len_lo) | (bits(H.z, ro.sh_hi, ro.len_hi) << 4);
-      const float dsc = d * (float)sc;     // exact: 11-bit mantissa times 6 bits
-      const float dmm = dmin * (float)m;   // exact
+      const int sc = (int)((__builtin_amdgcn_ubfe(H.y, ro.sh_hi, ro.len_hi) << 4) |
+                           __builtin_amdgcn_ubfe(a_sc, ro.sh_sc, ro.len_lo));
+      const int m = (int)((__builtin_amdgcn_ubfe(H.z, ro.sh_hi, ro.len_hi) << 4) |
+                          __builtin_amdgcn_ubfe(a_m, ro.sh_m, ro.len_lo));
+      const float fm = (float)m;
       int lo[4], hi[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        lo[k] = (int)(qs[r][s][k] & 0x0F0F0F0Fu);
-        hi[k] = (int)((qs[r][s][k] >> 4) & 0x0F0F0F0Fu);
+        lo[k] = (int)(wt.qs[r][s][k] & 0x0F0F0F0Fu);
+        hi[k] = (int)((wt.qs[r][s][k] >> 4) & 0x0F0F0F0Fu);
       }
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
@@ -155,19 +227,95 @@ __device__ __forceinline__ void q4k_rows(float (&acc)[R][NT], const uint8_t* __r
         // each receives the partner's half sum of the sub-block it keeps
         const int keep = ro.h ? sh : sl;
         const int send = ro.h ? sl : sh;
-        const int isum = keep + __shfl_xor(send, 1);
+        const int isum = keep + xor1_i(send);
+        // the fp16 scales enter the fmas directly (v_fma_mix_f32)
         float a = acc[r][t];
-        a = fmaf(dsc, xs.dx[t][s] * (float)isum, a);
-        a = fmaf(-dmm, xs.sx[t][s], a);
+        a = __builtin_fmaf((float)d, xs.dx[t][s] * (float)__mul24(sc, isum), a);
+        a = __builtin_fmaf((float)dmin, -xs.sx[t][s] * fm, a);
         acc[r][t] = a;
       }
     }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[r][t] = group_sum_dpp<8 * TPR>(acc[r][t]);
   }
+}
 
+// True in the lane that holds a row's reduced sum.
+template <int TPR>
+__device__ __forceinline__ bool row_leader(const LaneRole& ro) {
+  return (ro.lane & (8 * TPR - 1)) == 8 * TPR - 1;
+}
+
+struct Q4KGemvArgs {
+  const uint8_t* w;   // row 0, super-block 0
+  const uint8_t* xq;  // token 0, block 0
+  float* y;
+  int out_dim;
+  int nsb_row;        // super-blocks per full row
+  int sb0;            // first super-block of this column chunk
+  int nsb;            // super-blocks in this chunk
+  int n_tokens;
+};
+
+// Store one tile's row sums (leader lanes only); ACC adds to y instead.
+template <int TPR, int R, int NT, bool ACC>
+__device__ __forceinline__ void store_rows(const Q4KGemvArgs& a, const float (&acc)[R][NT],
+                                           long row_base, const LaneRole& ro) {
+  constexpr int RW = 8 / TPR;
+  if (!row_leader<TPR>(ro)) return;
 #pragma unroll
-  for (int r = 0; r < R; ++r)
+  for (int r = 0; r < R; ++r) {
+    const long row = row_base + (long)r * RW + ro.rs;
+    if (row < a.out_dim) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) acc[r][t] = group_sum<8 * TPR>(acc[r][t]);
+      for (int t = 0; t < NT; ++t) {
+        if (t < a.n_tokens) {
+          float* dst = a.y + (size_t)t * a.out_dim + row;
+          if constexpr (ACC) *dst += acc[r][t];
+          else *dst = acc[r][t];
+        }
+      }
+    }
+  }
+}
+
+// GEMV: wave w of W takes the G row groups w, w+W, ..., w+(G-1)W (a group is
+// RW*R rows).  The G groups are unrolled into straight-line code with P tiles
+// in flight: group k+P is requested before group k is reduced, and because no
+// load sits under a branch the compiler waits for exactly the tile it needs.
+// Groups past the end read zeros through the buffer descriptor and store
+// nothing.
+template <int TPR, int S, int R, int NT, int G, int P, bool ACC>
+__global__ __launch_bounds__(256) void q4k_q8_gemv_kernel(Q4KGemvArgs a) {
+  constexpr int RW = 8 / TPR;
+  constexpr uint32_t kRowsPerGroup = (uint32_t)RW * R;
+  const uint32_t nwaves = gridDim.x * 4u;
+  const uint32_t w0 = __builtin_amdgcn_readfirstlane(blockIdx.x * 4u + (threadIdx.x >> 6));
+  const LaneRole ro = make_role<TPR>();
+  const uint32_t row_bytes = (uint32_t)a.nsb_row * kQ4KBytes;
+  const WSrc src = make_wsrc(a.w, row_bytes, (uint32_t)a.out_dim * row_bytes);
+  const LaneOffsets<TPR, S> off = lane_offsets<TPR, S>(src, a.sb0, ro);
+
+  // activation first: vector loads retire in order, so waiting for x must
+  // not mean waiting for weight tiles issued before it
+  XSlots<S, NT> xs;
+  load_x_slots<TPR, S, NT>(xs, a.xq + (size_t)a.sb0 * 8 * kQ8Bytes,
+                           (size_t)a.nsb_row * 8 * kQ8Bytes, a.nsb, a.n_tokens, ro);
+  WTile<S, R> t[G];
+#pragma unroll
+  for (int k = 0; k < P && k < G; ++k)
+    load_w_tile<TPR, S, R>(t[k], src, off, (w0 + k * nwaves) * kRowsPerGroup);
+  // keep the scheduler from sinking requests below the first wait
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int k = 0; k < G; ++k) {
+    if (k + P < G)
+      load_w_tile<TPR, S, R>(t[k + P], src, off, (w0 + (k + P) * nwaves) * kRowsPerGroup);
+    __builtin_amdgcn_sched_barrier(0);
+    float acc[R][NT];
+    q4k_tile_dot<TPR, S, R, NT>(acc, t[k], xs, ro);
+    store_rows<TPR, R, NT, ACC>(a, acc, (long)(w0 + k * nwaves) * kRowsPerGroup, ro);
+  }
 }
 
 }  // namespace rz

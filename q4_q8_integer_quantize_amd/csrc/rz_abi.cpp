@@ -25,6 +25,9 @@ int fail(int code, const char* fmt, ...) {
   return code;
 }
 
+// Weight matrices are addressed with 32-bit offsets (raw buffer loads).
+constexpr long long kMaxMatrixBytes = (1LL << 31) - 1;
+
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 int launch_status(hipError_t e, const char* what) {
@@ -72,6 +75,8 @@ int rz_q4k_q8_gemv(const void* w_q4k, const void* x_q8, float* y, int out_dim, i
     return fail(RZ_EINVAL, "%s: n_tokens=%d outside 1..%d", what, n_tokens, RZ_MAX_TOKENS);
   if (int rc = check_dim(what, "out_dim", out_dim, 1)) return rc;
   if (int rc = check_dim(what, "in_dim", in_dim, 256)) return rc;
+  if ((long long)out_dim * (in_dim / 256) * RZ_Q4K_BLOCK_BYTES > kMaxMatrixBytes)
+    return fail(RZ_EDIM, "%s: weight matrix larger than %lld bytes", what, kMaxMatrixBytes);
   if (!aligned(w_q4k, 16)) return fail(RZ_EALIGN, "%s: w_q4k must be 16-byte aligned", what);
   if (!aligned(x_q8, 8)) return fail(RZ_EALIGN, "%s: x_q8 must be 8-byte aligned", what);
   if (!aligned(y, 4)) return fail(RZ_EALIGN, "%s: y must be 4-byte aligned", what);
@@ -107,6 +112,8 @@ int rz_swiglu_ffn_q4k(const void* w_gate, const void* w_up, const void* w_down,
     return fail(RZ_EINVAL, "%s: null pointer", what);
   if (int rc = check_dim(what, "hidden_dim", hidden_dim, 256)) return rc;
   if (int rc = check_dim(what, "inter_dim", inter_dim, 256)) return rc;
+  if ((long long)inter_dim * (hidden_dim / 256) * RZ_Q4K_BLOCK_BYTES > kMaxMatrixBytes)
+    return fail(RZ_EDIM, "%s: weight matrix larger than %lld bytes", what, kMaxMatrixBytes);
   if (hidden_dim > 16384)
     return fail(RZ_EDIM, "%s: hidden_dim=%d above the fused gate/up limit 16384", what,
                 hidden_dim);

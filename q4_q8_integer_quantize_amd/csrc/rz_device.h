@@ -18,6 +18,8 @@ constexpr int kQKK = 256;
 constexpr int kQ4KBytes = 144;
 constexpr int kQK40 = 32;
 constexpr int kQ40Bytes = 18;
+// Raw buffer descriptor word 3 (data format 32, no swizzle) for gfx9 parts.
+constexpr int kBufferWord3 = 0x00020000;
 
 // 16-byte vector whose pointer only promises 4-byte alignment; gfx9 global
 // loads accept dword-aligned addresses for multi-dword accesses.

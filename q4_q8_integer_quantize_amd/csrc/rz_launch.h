@@ -10,8 +10,7 @@ namespace rz {
 hipError_t launch_q8_1_quantize(const float* x, int n, int n_padded, int n_tokens,
                                 uint8_t* out, hipStream_t stream);
 
-// Q4_K x Q8_1 GEMV over super-blocks [sb0, sb0 + nsb) of every row; when
-// `accumulate` is set the result is added to y instead of stored.
+// Q4_K x Q8_1 GEMV for 1..8 tokens (token-major y).
 hipError_t launch_q4k_q8_gemv(const uint8_t* w, const uint8_t* xq, float* y, int out_dim,
                               int in_dim, int n_tokens, hipStream_t stream);
 

@@ -31,27 +31,37 @@ struct SwiArgs {
 template <int TPR, int S, int R>
 __global__ __launch_bounds__(256) void swiglu_gate_up_kernel(SwiArgs a) {
   constexpr int RW = 8 / TPR;
-  static_assert(8 % (RW * R) == 0, "a wave's 8 rows split into whole passes");
+  constexpr int kPassRows = RW * R;
+  static_assert(32 % kPassRows == 0, "the 32 rows of a block split into whole passes");
   __shared__ float gs[32], us[32], hs[32];
-  const int wave = threadIdx.x >> 6;
-  const long blk_row0 = (long)blockIdx.x * 32;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t blk_row0 = blockIdx.x * 32u;
   const LaneRole ro = make_role<TPR>();
   XSlots<S, 1> xs;
   load_x_slots<TPR, S, 1>(xs, a.xq, 0, a.nsb, 1, ro);
-  const size_t row_bytes = (size_t)a.nsb * kQ4KBytes;
+  const uint32_t row_bytes = (uint32_t)a.nsb * kQ4KBytes;
+  const uint32_t bytes = (uint32_t)a.inter * row_bytes;
+  const WSrc sg = make_wsrc(a.wg, row_bytes, bytes);
+  const WSrc su = make_wsrc(a.wu, row_bytes, bytes);
+  const LaneOffsets<TPR, S> off = lane_offsets<TPR, S>(sg, 0, ro);
 
+  // passes of RW*R rows, dealt to the 4 waves in turn; gate and up tiles of a
+  // pass are requested together before either is reduced
+  for (uint32_t pass = wave; pass < 32u / kPassRows; pass += 4u) {
+    const uint32_t row_base = blk_row0 + pass * kPassRows;
+    WTile<S, R> tg, tu;
+    load_w_tile<TPR, S, R>(tg, sg, off, row_base);
+    load_w_tile<TPR, S, R>(tu, su, off, row_base);
+    __builtin_amdgcn_sched_barrier(0);
+    float ag[R][1], au[R][1];
+    q4k_tile_dot<TPR, S, R, 1>(ag, tg, xs, ro);
+    q4k_tile_dot<TPR, S, R, 1>(au, tu, xs, ro);
+    if (row_leader<TPR>(ro)) {
 #pragma unroll
-  for (int mat = 0; mat < 2; ++mat) {
-    const uint8_t* w = mat ? a.wu : a.wg;
-    float* dst = mat ? us : gs;
-#pragma unroll
-    for (int r0 = 0; r0 < 8; r0 += RW * R) {
-      float acc[R][1];
-      const long row_base = blk_row0 + 8 * wave + r0;
-      q4k_rows<TPR, S, R, 1>(acc, w, row_bytes, row_base, a.inter, a.nsb, xs, ro);
-      if ((ro.lane & (8 * TPR - 1)) == 0) {
-#pragma unroll
-        for (int r = 0; r < R; ++r) dst[8 * wave + r0 + r * RW + ro.rs] = acc[r][0];
+      for (int r = 0; r < R; ++r) {
+        const int local = pass * kPassRows + r * RW + ro.rs;
+        gs[local] = ag[r][0];
+        us[local] = au[r][0];
       }
     }
   }
@@ -85,9 +95,10 @@ __global__ __launch_bounds__(256) void swiglu_gate_up_kernel(SwiArgs a) {
 template <int TPR, int S>
 static hipError_t run_gate_up(const SwiArgs& a, hipStream_t st) {
   constexpr int RW = 8 / TPR;
-  constexpr int RMAX = 8 / RW;
-  constexpr int RS = S >= 8 ? 1 : 8 / S;
-  constexpr int R = RS < RMAX ? RS : RMAX;
+  // one pass of 8 rows per wave when registers allow (two tiles of R*S slots)
+  constexpr int R_fit = 8 / RW > 0 ? 8 / RW : 1;
+  constexpr int R_reg = S >= 6 ? 1 : (S >= 3 ? 2 : (S >= 2 ? 4 : 8));
+  constexpr int R = R_fit < R_reg ? R_fit : R_reg;
   hipLaunchKernelGGL((swiglu_gate_up_kernel<TPR, S, R>), dim3(a.inter / 32), dim3(256), 0, st, a);
   return hipGetLastError();
 }
