@@ -6,10 +6,11 @@ Q4_K matrix (33,030,144 bytes).  Every step reads the next of R weight copies
 (R * 33 MB >= 1 GiB), so no step finds its weights in the 256 MB Infinity
 Cache or an L2; inputs are resident in HBM before the timed region.
 
-Printed (one JSON line): the whole-step weight-stream rate in GB/s (`value`),
-the GEMV kernel's own rate against the 8 TB/s HBM peak (`roofline`, from HIP
-events around each GEMV launch on the launch stream), and the CPU oracle
-timed on the host (`cpu_baseline`).
+Printed (one JSON line): the whole-step weight-stream rate in GB/s (`value`,
+K steps captured in one HIP graph and replayed between HIP events), the GEMV
+kernel's own rate against the 8 TB/s HBM peak (`roofline`: K back-to-back GEMV
+launches in a graph, timed the same way), and the CPU oracle timed on the host
+(`cpu_baseline`).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
@@ -32,10 +33,12 @@ OUT_DIM, IN_DIM = 14336, 4096
 W_BYTES = OUT_DIM * (IN_DIM // 256) * 144            # 33,030,144
 XQ_BYTES = (IN_DIM // 32) * 40                        # 5,120
 Y_BYTES = OUT_DIM * 4                                 # 57,344
-GEMV_ALGO_BYTES = W_BYTES + XQ_BYTES + Y_BYTES        # 33,092,608 per launch
+X_BYTES = IN_DIM * 4                                  # 16,384
+GEMV_ALGO_BYTES = W_BYTES + XQ_BYTES + Y_BYTES        # 33,092,608 per GEMV launch
+STEP_ALGO_BYTES = W_BYTES + X_BYTES + Y_BYTES         # 33,103,872 per fused launch
 ROTATE_BYTES = 1 << 30
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "q4k_gemv_4096x14336_traffic.txt")
-KERNEL_SOURCES = ["q4k_gemv.h", "q4k_gemv.hip", "rz_device.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "q4k_gemv_f32_4096x14336_traffic.txt")
+KERNEL_SOURCES = ["q4k_gemv.h", "q4k_gemv_f32.hip", "rz_device.h"]
 
 
 def kernel_source_hash() -> str:
@@ -96,8 +99,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--hold-cycles", type=float, default=2e8,
-                    help="spin-kernel cycles that hold the stream while launches are enqueued")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after timing, run 4 plain device copies of MIB MiB (a reference "
+                         "for the HBM byte counters of a profiling run)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this path runs on one GPU; --gpus %d is not supported "
@@ -128,54 +132,65 @@ def main() -> int:
     x_p, xq_p, y_p = x.data_ptr(), xq.data_ptr(), y.data_ptr()
     w_p = [c.data_ptr() for c in copies]
 
-    def step(i, strm):
-        # direct C calls: the binding's checks were made once above
-        rc = lib.rz_q8_1_quantize(x_p, IN_DIM, IN_DIM, 1, xq_p, strm)
-        rc |= lib.rz_q4k_q8_gemv(w_p[i % n_copies], xq_p, y_p, OUT_DIM, IN_DIM, 1, strm)
-        if rc:
+    def fused(i, strm):
+        # the step: Q8_1 quantize + Q4_K x Q8_1 GEMV in one launch
+        if lib.rz_q4k_q8_gemv_f32(w_p[i % n_copies], x_p, IN_DIM, None, y_p, OUT_DIM, IN_DIM, strm):
             raise RuntimeError(rz.rz_last_error())
 
-    rz.rz_q8_1_quantize(x, IN_DIM, IN_DIM, 1, xq, s)                 # checked once
+    def two_launch(i, strm):
+        if (lib.rz_q8_1_quantize(x_p, IN_DIM, IN_DIM, 1, xq_p, strm)
+                or lib.rz_q4k_q8_gemv(w_p[i % n_copies], xq_p, y_p, OUT_DIM, IN_DIM, 1, strm)):
+            raise RuntimeError(rz.rz_last_error())
+
+    def gemv_only(i, strm):
+        if lib.rz_q4k_q8_gemv(w_p[i % n_copies], xq_p, y_p, OUT_DIM, IN_DIM, 1, strm):
+            raise RuntimeError(rz.rz_last_error())
+
+    # argument checks of the binding, once
+    rz.rz_q4k_q8_gemv_f32(copies[0], x, IN_DIM, None, y, OUT_DIM, IN_DIM, s)
+    rz.rz_q8_1_quantize(x, IN_DIM, IN_DIM, 1, xq, s)
     rz.rz_q4k_q8_gemv(copies[0], xq, y, OUT_DIM, IN_DIM, 1, s)
     for i in range(args.warmup):
-        step(i, s)
+        fused(i, s)
     torch.cuda.synchronize()
-
-    # ---- whole-step throughput: K steps captured once in a HIP graph, replayed
     K = args.steps
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        cs = torch.cuda.current_stream().cuda_stream
-        for i in range(K):
-            step(args.warmup + i, cs)
-    graph.replay()                      # untimed replay: graph upload and warm caches
-    torch.cuda.synchronize()
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    graph.replay()
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    ms_step = t_start.elapsed_time(t_end) / K
 
-    # ---- GEMV kernel duration: HIP events around every GEMV launch on the
-    # launch stream; the stream is held by a spin kernel while the host enqueues,
-    # so no host gap falls between an event pair
-    ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    torch.cuda.synchronize()
-    torch.cuda._sleep(int(args.hold_cycles))
-    for i in range(K):
-        lib.rz_q8_1_quantize(x_p, IN_DIM, IN_DIM, 1, xq_p, s)
-        ev_s[i].record(stream)
-        lib.rz_q4k_q8_gemv(w_p[(args.warmup + i) % n_copies], xq_p, y_p, OUT_DIM, IN_DIM, 1, s)
-        ev_e[i].record(stream)
-    torch.cuda.synchronize()
-    gemv_ms = np.array([a.elapsed_time(b) for a, b in zip(ev_s, ev_e)])
-    gemv_avg_s = float(gemv_ms.mean()) * 1e-3
-    achieved = GEMV_ALGO_BYTES / gemv_avg_s / 1e9
+    def graph_time(body):
+        """K calls of body, each on the next weight copy, captured in one HIP
+        graph; mean seconds per call over one replay bracketed by HIP events on
+        the launch stream (after one untimed replay)."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cs = torch.cuda.current_stream().cuda_stream
+            for i in range(K):
+                body(args.warmup + i, cs)
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / K
+
+    step_s = graph_time(fused)            # the timed steps (whole hot path)
+    ms_step = step_s * 1e3
+    two_s = graph_time(two_launch)        # same work as two launches
+    gemv_s = graph_time(gemv_only)        # the GEMV kernel alone
+    achieved = STEP_ALGO_BYTES / step_s / 1e9
     traffic = measured_traffic()
+
+    if args.copy_calibration > 0:
+        nbytes = args.copy_calibration << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     value = W_BYTES / (ms_step * 1e-3) / 1e9
     out = {
@@ -192,13 +207,17 @@ def main() -> int:
         "dtype": "int8",
         "data": "synthetic",
         "config": {
-            "workload": "Q8_1 quantize + Q4_K x Q8_1 GEMV, 4096 -> 14336, batch 1",
+            "workload": "Q8_1 quantize + Q4_K x Q8_1 GEMV, 4096 -> 14336, batch 1 "
+                        "(one launch, rz_q4k_q8_gemv_f32)",
             "out_dim": OUT_DIM, "in_dim": IN_DIM, "n_tokens": 1,
             "weight_bytes": W_BYTES, "weight_copies_rotated": n_copies,
             "pct_hbm_peak_step": round(100 * value / HBM_PEAK_GBS, 2),
         },
-        "gemv_us_avg": round(gemv_avg_s * 1e6, 3),
-        "gemv_us_p10_p50_p90": [round(float(v) * 1e3, 3) for v in np.percentile(gemv_ms, [10, 50, 90])],
+        "us_per_step": round(step_s * 1e6, 3),
+        "two_launch_us_per_step": round(two_s * 1e6, 3),
+        "gemv_kernel_us": round(gemv_s * 1e6, 3),
+        "gemv_kernel_gbs": round(GEMV_ALGO_BYTES / gemv_s / 1e9, 2),
+        "kernel_source_sha256_16": kernel_source_hash(),
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 2),

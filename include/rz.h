@@ -84,6 +84,24 @@ int rz_q8_1_quantize(const float* x, int n, int n_padded, int n_tokens,
 int rz_q4k_q8_gemv(const void* w_q4k, const void* x_q8, float* y,
                    int out_dim, int in_dim, int n_tokens, void* stream);
 
+/* rz_q4k_q8_gemv_f32 -- Q8_1 quantize and Q4_K x Q8_1 GEMV in one launch.
+ * Passage: realizar 0.8.5 src/cuda/executor/cached.rs,
+ * transformer_layer_gpu_true_dp4a, steps 2-3 (quantize the normed
+ * activation to Q8_1, then the Q4K x Q8 integer dot product).
+ * Bit for bit the result of rz_q8_1_quantize(x, n, in_dim, 1, x_q8) followed
+ * by rz_q4k_q8_gemv(w_q4k, x_q8, y, out_dim, in_dim, 1): each workgroup
+ * quantizes the activation into its LDS while its first weight tiles load.
+ *   w_q4k    [out_dim][in_dim/256] super-blocks, 16-byte aligned, < 2 GiB
+ *   x        fp32 [n], 4-byte aligned; values n..in_dim-1 are taken as 0
+ *   n        1 <= n <= in_dim
+ *   x_q8     optional out (NULL to skip): the [in_dim/32] Q8_1 blocks, for
+ *            further projections of the same activation; 8-byte aligned
+ *   y        out: fp32 [out_dim], 4-byte aligned
+ *   in_dim   multiple of 256, <= 16384; one token
+ * Errors: RZ_EINVAL, RZ_EDIM, RZ_EALIGN, RZ_ELAUNCH. */
+int rz_q4k_q8_gemv_f32(const void* w_q4k, const float* x, int n, void* x_q8, float* y,
+                       int out_dim, int in_dim, void* stream);
+
 /* rz_q4_0_gemv -- y = W x with W Q4_0 and x fp32 or Q8_1 (the LM head).
  * Passage: realizar 0.8.4 src/gpu/adapters/using.rs, GpuModelQ4::forward
  * step 5 (q4_0_gemv_into(lm_head, normed, logits, vocab, hidden)).

@@ -19,7 +19,8 @@ __all__ = [
     "RZ_OK", "RZ_EINVAL", "RZ_EDIM", "RZ_EALIGN", "RZ_ELAUNCH",
     "Q8_1_BLOCK_BYTES", "Q4K_BLOCK_BYTES", "Q4_0_BLOCK_BYTES", "MAX_TOKENS",
     "library_path", "load_library", "rz_last_error", "rz_abi_version",
-    "rz_q8_1_quantize", "rz_q4k_q8_gemv", "rz_q4_0_gemv", "rz_swiglu_ffn_q4k",
+    "rz_q8_1_quantize", "rz_q4k_q8_gemv", "rz_q4k_q8_gemv_f32", "rz_q4_0_gemv",
+    "rz_swiglu_ffn_q4k",
     "q8_1_nbytes", "RzError",
 ]
 
@@ -56,10 +57,11 @@ def load_library() -> ctypes.CDLL:
     vp, i = ctypes.c_void_p, ctypes.c_int
     lib.rz_q8_1_quantize.argtypes = [vp, i, i, i, vp, vp]
     lib.rz_q4k_q8_gemv.argtypes = [vp, vp, vp, i, i, i, vp]
+    lib.rz_q4k_q8_gemv_f32.argtypes = [vp, vp, i, vp, vp, i, i, vp]
     lib.rz_q4_0_gemv.argtypes = [vp, vp, i, vp, i, i, vp]
     lib.rz_swiglu_ffn_q4k.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, vp]
-    for fn in ("rz_q8_1_quantize", "rz_q4k_q8_gemv", "rz_q4_0_gemv", "rz_swiglu_ffn_q4k",
-               "rz_abi_version"):
+    for fn in ("rz_q8_1_quantize", "rz_q4k_q8_gemv", "rz_q4k_q8_gemv_f32", "rz_q4_0_gemv",
+               "rz_swiglu_ffn_q4k", "rz_abi_version"):
         getattr(lib, fn).restype = i
     lib.rz_last_error.argtypes = []
     lib.rz_last_error.restype = ctypes.c_char_p
@@ -132,6 +134,19 @@ def rz_q4k_q8_gemv(w_q4k, x_q8, y, out_dim: int, in_dim: int, n_tokens: int = 1,
         _need(y, 4 * out_dim * n_tokens, "y")
     _check(load_library().rz_q4k_q8_gemv(_ptr(w_q4k), _ptr(x_q8), _ptr(y), out_dim, in_dim,
                                          n_tokens, _stream(stream)))
+
+
+def rz_q4k_q8_gemv_f32(w_q4k, x, n: int, x_q8, y, out_dim: int, in_dim: int,
+                       stream=None) -> None:
+    """Quantize fp32 x [n] to Q8_1 in-kernel (optionally writing the blocks to
+    x_q8, or pass None) and compute y fp32 [out_dim] = W (Q4_K) x, one launch."""
+    if in_dim > 0 and in_dim % 256 == 0 and out_dim > 0:
+        _need(w_q4k, out_dim * (in_dim // 256) * Q4K_BLOCK_BYTES, "w_q4k")
+        _need(x, 4 * n, "x")
+        _need(x_q8, q8_1_nbytes(in_dim), "x_q8")
+        _need(y, 4 * out_dim, "y")
+    _check(load_library().rz_q4k_q8_gemv_f32(_ptr(w_q4k), _ptr(x), n, _ptr(x_q8), _ptr(y),
+                                             out_dim, in_dim, _stream(stream)))
 
 
 def rz_q4_0_gemv(w_q4_0, x, x_format: int, y, out_dim: int, in_dim: int, stream=None) -> None:

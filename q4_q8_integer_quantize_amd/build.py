@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "librz.so")
 
-SOURCES = ["q8_1_quantize.hip", "q4k_gemv.hip", "q4_0_gemv.hip", "swiglu_ffn.hip", "rz_abi.cpp"]
+SOURCES = ["q8_1_quantize.hip", "q4k_gemv.hip", "q4k_gemv_f32.hip", "q4_0_gemv.hip",
+           "swiglu_ffn.hip", "rz_abi.cpp"]
 ARCH = os.environ.get("RZ_OFFLOAD_ARCH", "gfx950")
 
 

@@ -182,10 +182,10 @@ __global__ __launch_bounds__(256) void q4_0_gemv_kernel(Q40Args a) {
         ar = fmaf(dB * xs.dx[s][1], (float)ib, ar);
       }
     }
-    acc[r] = group_sum<LPR>(ar);
+    acc[r] = group_sum_dpp<LPR>(ar);
   }
 
-  if (ps == 0) {
+  if (ps == LPR - 1) {   // the lane that holds the reduced row sum
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const long row = row_base + (long)r * RW + rs;

@@ -163,29 +163,7 @@ __device__ __forceinline__ void load_w_tile(WTile<S, R>& wt, const WSrc& src,
 }
 
 // Integer exchange with lane ^ 1 (DPP quad_perm [1,0,3,2]).
-__device__ __forceinline__ int xor1_i(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
-}
-
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
-                                                               CTRL, ROW_MASK, 0xF, false));
-}
-
-// Sum over aligned groups of W lanes (W in 8, 16, 32, 64) with DPP.  The full
-// sum is valid in the LAST lane of each group (for W <= 16 in every lane).
-template <int W>
-__device__ __forceinline__ float group_sum_dpp(float v) {
-  static_assert(W == 8 || W == 16 || W == 32 || W == 64, "group width");
-  v += dpp_f<0xB1, 0xF>(v);    // quad_perm [1,0,3,2]: lane ^ 1
-  v += dpp_f<0x4E, 0xF>(v);    // quad_perm [2,3,0,1]: lane ^ 2
-  v += dpp_f<0x141, 0xF>(v);   // row_half_mirror: quads 0 <-> 1 of each 8
-  if constexpr (W >= 16) v += dpp_f<0x140, 0xF>(v);   // row_mirror: 8-groups of a row
-  if constexpr (W >= 32) v += dpp_f<0x142, 0xA>(v);   // row_bcast:15 into rows 1, 3
-  if constexpr (W >= 64) v += dpp_f<0x143, 0xC>(v);   // row_bcast:31 into rows 2, 3
-  return v;
-}
+__device__ __forceinline__ int xor1_i(int v) { return dpp_i<0xB1>(v); }
 
 // Multiply-accumulate one tile into acc[r][t] and reduce each row over its
 // 8*TPR lanes.  On return acc[r][t] is the full row sum in the last lane of
@@ -285,12 +263,15 @@ __device__ __forceinline__ void store_rows(const Q4KGemvArgs& a, const float (&a
 // load sits under a branch the compiler waits for exactly the tile it needs.
 // Groups past the end read zeros through the buffer descriptor and store
 // nothing.
-template <int TPR, int S, int R, int NT, int G, int P, bool ACC>
-__global__ __launch_bounds__(256) void q4k_q8_gemv_kernel(Q4KGemvArgs a) {
+template <int TPR, int S, int R, int NT, int G, int P, bool ACC, int WPB = 4, bool STRIDED = true>
+__global__ __launch_bounds__(64 * WPB) void q4k_q8_gemv_kernel(Q4KGemvArgs a) {
   constexpr int RW = 8 / TPR;
   constexpr uint32_t kRowsPerGroup = (uint32_t)RW * R;
-  const uint32_t nwaves = gridDim.x * 4u;
-  const uint32_t w0 = __builtin_amdgcn_readfirstlane(blockIdx.x * 4u + (threadIdx.x >> 6));
+  const uint32_t nwaves = gridDim.x * (uint32_t)WPB;
+  const uint32_t wid = __builtin_amdgcn_readfirstlane(blockIdx.x * (uint32_t)WPB + (threadIdx.x >> 6));
+  // group k of this wave: strided (wid + k*nwaves) or a contiguous band (wid*G + k)
+  const uint32_t g0 = STRIDED ? wid : wid * (uint32_t)G;
+  const uint32_t gstep = STRIDED ? nwaves : 1u;
   const LaneRole ro = make_role<TPR>();
   const uint32_t row_bytes = (uint32_t)a.nsb_row * kQ4KBytes;
   const WSrc src = make_wsrc(a.w, row_bytes, (uint32_t)a.out_dim * row_bytes);
@@ -304,17 +285,17 @@ __global__ __launch_bounds__(256) void q4k_q8_gemv_kernel(Q4KGemvArgs a) {
   WTile<S, R> t[G];
 #pragma unroll
   for (int k = 0; k < P && k < G; ++k)
-    load_w_tile<TPR, S, R>(t[k], src, off, (w0 + k * nwaves) * kRowsPerGroup);
+    load_w_tile<TPR, S, R>(t[k], src, off, (g0 + k * gstep) * kRowsPerGroup);
   // keep the scheduler from sinking requests below the first wait
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int k = 0; k < G; ++k) {
     if (k + P < G)
-      load_w_tile<TPR, S, R>(t[k + P], src, off, (w0 + (k + P) * nwaves) * kRowsPerGroup);
+      load_w_tile<TPR, S, R>(t[k + P], src, off, (g0 + (k + P) * gstep) * kRowsPerGroup);
     __builtin_amdgcn_sched_barrier(0);
     float acc[R][NT];
     q4k_tile_dot<TPR, S, R, NT>(acc, t[k], xs, ro);
-    store_rows<TPR, R, NT, ACC>(a, acc, (long)(w0 + k * nwaves) * kRowsPerGroup, ro);
+    store_rows<TPR, R, NT, ACC>(a, acc, (long)(g0 + k * gstep) * kRowsPerGroup, ro);
   }
 }
 

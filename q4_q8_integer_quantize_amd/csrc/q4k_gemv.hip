@@ -6,29 +6,43 @@
 // for every token (the weights are the only large operand).
 //
 // Work split: a group is RW*R consecutive rows (RW = 8/TPR side by side, R
-// unrolled); each wave takes G groups strided by the wave count and keeps P of
-// them in flight.  Rows longer than the register-resident activation window
+// unrolled); each wave takes G groups strided by the wave count and keeps P
+// more in flight while it reduces one.  Rows longer than the register-resident activation window
 // are processed in column chunks by successive launches that accumulate into y.
 #include "q4k_gemv.h"
 #include "rz_launch.h"
 
 namespace rz {
 
-constexpr int kGroupsPerWave = 4;   // G: row groups per wave, unrolled
-constexpr int kTilesInFlight = 2;   // P: weight tiles requested ahead
+constexpr int kTilesInFlight = 2;   // P: weight tiles requested ahead of the one reduced
+constexpr long kTargetWaves = 1024; // about one wave per SIMD (256 CUs x 4)
 
 // Activation slots a lane holds in registers (10 VGPRs per slot and token).
 template <int NT>
 constexpr int slots_max() { return NT <= 2 ? 8 : (NT == 4 ? 4 : 2); }
 
-// Rows unrolled per group: about 4 super-block slots per lane per group, with
-// the register footprint bounded as tokens multiply the activation state.
+// Rows unrolled per group: two for short rows of one or two tokens, else one.
 template <int S, int NT>
-constexpr int rows_unrolled() {
-  constexpr int per = S * (NT <= 2 ? 1 : NT / 2);
-  return per >= 4 ? 1 : 4 / per;
+constexpr int rows_unrolled() { return (S <= 2 && NT <= 2) ? 2 : 1; }
+
+template <int TPR, int S, int NT, int G>
+static hipError_t launch_g(const Q4KGemvArgs& a, long groups, bool acc, hipStream_t st) {
+  constexpr int R = rows_unrolled<S, NT>();
+  constexpr int P = G > kTilesInFlight ? kTilesInFlight : (G > 1 ? G - 1 : 1);
+  const long waves = (groups + G - 1) / G;
+  const unsigned grid = (unsigned)((waves + 3) / 4);
+  if (acc)
+    hipLaunchKernelGGL((q4k_q8_gemv_kernel<TPR, S, R, NT, G, P, true>), dim3(grid), dim3(256), 0,
+                       st, a);
+  else
+    hipLaunchKernelGGL((q4k_q8_gemv_kernel<TPR, S, R, NT, G, P, false>), dim3(grid), dim3(256), 0,
+                       st, a);
+  return hipGetLastError();
 }
 
+// G (row groups per wave) is the smallest power of two, at most 8, that keeps
+// the grid at about one wave per SIMD; fewer, deeper-pipelined waves stream
+// better than many short ones.
 template <int TPR, int S, int NT>
 static hipError_t run_q4k(const Q4KGemvArgs& a, bool acc, hipStream_t st) {
   if constexpr (S > slots_max<NT>()) {
@@ -36,18 +50,13 @@ static hipError_t run_q4k(const Q4KGemvArgs& a, bool acc, hipStream_t st) {
   } else {
     constexpr int R = rows_unrolled<S, NT>();
     constexpr int RW = 8 / TPR;
-    constexpr int G = kGroupsPerWave, P = kTilesInFlight;
     const long rows_per_group = (long)RW * R;
     const long groups = (a.out_dim + rows_per_group - 1) / rows_per_group;
-    const long waves = (groups + G - 1) / G;
-    const unsigned grid = (unsigned)((waves + 3) / 4);
-    if (acc)
-      hipLaunchKernelGGL((q4k_q8_gemv_kernel<TPR, S, R, NT, G, P, true>), dim3(grid), dim3(256),
-                         0, st, a);
-    else
-      hipLaunchKernelGGL((q4k_q8_gemv_kernel<TPR, S, R, NT, G, P, false>), dim3(grid),
-                         dim3(256), 0, st, a);
-    return hipGetLastError();
+    const long per_wave = (groups + kTargetWaves - 1) / kTargetWaves;
+    if (per_wave <= 1) return launch_g<TPR, S, NT, 1>(a, groups, acc, st);
+    if (per_wave <= 2) return launch_g<TPR, S, NT, 2>(a, groups, acc, st);
+    if (per_wave <= 4) return launch_g<TPR, S, NT, 4>(a, groups, acc, st);
+    return launch_g<TPR, S, NT, 8>(a, groups, acc, st);
   }
 }
 

@@ -21,13 +21,11 @@ __global__ __launch_bounds__(256) void q8_1_quantize_kernel(const float* __restr
   const int nb = n_padded / kQK8;
   const long t = g / nb;
   const int b = (int)(g - t * nb);
-  const float* xt = x + t * (long)n;
+  const uint32_t bytes = (uint32_t)(total_blocks / nb) * (uint32_t)n * 4u;
+  const __amdgpu_buffer_rsrc_t xr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, (int)bytes, kBufferWord3);
   float v[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int idx = b * kQK8 + 4 * i + k;
-    v[k] = idx < n ? xt[idx] : 0.0f;
-  }
+  load_block_quad(v, xr, (uint32_t)t * (uint32_t)n, b * kQK8 + 4 * i, n, true, bytes);
   float d, s;
   const uint32_t packed = q8_1_block_group8(v, d, s);
   uint8_t* blk = out + g * kQ8Bytes;

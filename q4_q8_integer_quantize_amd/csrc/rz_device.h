@@ -46,24 +46,47 @@ __device__ __forceinline__ float f16_hi(uint32_t v) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
 }
 
-// Sum over aligned groups of W lanes (W a power of two <= 64).
+// DPP lane exchange within rows of 16 lanes (control words: quad_perm
+// [1,0,3,2] = 0xB1 is lane^1, [2,3,0,1] = 0x4E is lane^2, row_half_mirror
+// 0x141 swaps the two quads of each group of 8, row_mirror 0x140 the two
+// groups of 8 of a row, row_bcast 0x142 / 0x143 broadcast lane 15 / 31).
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, false);
+}
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, dpp_i<CTRL, ROW_MASK>(__builtin_bit_cast(int, v)));
+}
+
+// Sum over aligned groups of W lanes (W a power of two, 1..64) with DPP.  The
+// full sum is valid in the LAST lane of each group (for W <= 16 in every lane).
 template <int W>
-__device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, W);
+__device__ __forceinline__ float group_sum_dpp(float v) {
+  static_assert(W >= 1 && W <= 64 && (W & (W - 1)) == 0, "group width");
+  if constexpr (W >= 2) v += dpp_f<0xB1>(v);          // lane ^ 1
+  if constexpr (W >= 4) v += dpp_f<0x4E>(v);          // lane ^ 2
+  if constexpr (W >= 8) v += dpp_f<0x141>(v);         // quads of an 8
+  if constexpr (W >= 16) v += dpp_f<0x140>(v);        // 8-groups of a row
+  if constexpr (W >= 32) v += dpp_f<0x142, 0xA>(v);   // row_bcast:15 into rows 1, 3
+  if constexpr (W >= 64) v += dpp_f<0x143, 0xC>(v);   // row_bcast:31 into rows 2, 3
   return v;
 }
-template <int W>
-__device__ __forceinline__ int group_sum_i(int v) {
+
+// Four consecutive activation values x[base + idx .. base + idx + 3], read as
+// single dwords through a raw buffer descriptor that spans exactly x (`bytes`).
+// Values at idx + k >= n, or of an inactive block, take the offset `bytes`,
+// which the hardware range check turns into 0: no branch and no clamping, so
+// the loads of several blocks stay in flight together.
+__device__ __forceinline__ void load_block_quad(float v[4], __amdgpu_buffer_rsrc_t xr,
+                                                uint32_t base, int idx, int n, bool active,
+                                                uint32_t bytes) {
 #pragma unroll
-  for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, W);
-  return v;
-}
-template <int W>
-__device__ __forceinline__ float group_max(float v) {
-#pragma unroll
-  for (int o = W / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, W));
-  return v;
+  for (int k = 0; k < 4; ++k) {
+    const int j = idx + k;
+    const uint32_t off = (active && j < n) ? (base + (uint32_t)j) * 4u : bytes;
+    v[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(xr, off, 0, 0));
+  }
 }
 
 // One Q8_1 block quantized by an aligned group of 8 lanes; lane i (0..7) holds
@@ -71,26 +94,29 @@ __device__ __forceinline__ float group_max(float v) {
 // sets d and s (identical in all 8 lanes).  The rule: amax = max|x| (exact),
 // d = amax / 127 (correctly rounded fp32 division), q = rint(x / d) (fp32
 // division, ties to even), s = d * float(sum q); amax == 0 gives zeros.
+// Branch-free: the 8-lane max and sum run on DPP, and an all-zero block takes
+// its zero codes by a select (its quotients are 0/0).
 __device__ __forceinline__ uint32_t q8_1_block_group8(const float v[4], float& d, float& s) {
   float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-  amax = group_max<8>(amax);
+  amax = fmaxf(amax, dpp_f<0xB1>(amax));
+  amax = fmaxf(amax, dpp_f<0x4E>(amax));
+  amax = fmaxf(amax, dpp_f<0x141>(amax));
   d = amax / 127.0f;
+  const bool zero = amax == 0.0f;
   uint32_t packed = 0;
   int sum = 0;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    int q = 0;
-    if (amax != 0.0f) {
-      float r = rintf(v[k] / d);
-      r = fminf(fmaxf(r, -127.0f), 127.0f);
-      q = (int)r;
-    }
+    float r = rintf(v[k] / d);
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    const int q = zero ? 0 : (int)r;
     sum += q;
     packed |= ((uint32_t)(q & 0xff)) << (8 * k);
   }
-  sum = group_sum_i<8>(sum);
+  sum += dpp_i<0xB1>(sum);
+  sum += dpp_i<0x4E>(sum);
+  sum += dpp_i<0x141>(sum);
   s = d * (float)sum;
-  if (amax == 0.0f) { d = 0.0f; s = 0.0f; }
   return packed;
 }
 

@@ -38,8 +38,8 @@ def lib():
 
 def test_header_declares_the_four_operations():
     syms = declared_symbols()
-    for name in ("rz_q8_1_quantize", "rz_q4k_q8_gemv", "rz_q4_0_gemv", "rz_swiglu_ffn_q4k",
-                 "rz_last_error", "rz_abi_version"):
+    for name in ("rz_q8_1_quantize", "rz_q4k_q8_gemv", "rz_q4k_q8_gemv_f32", "rz_q4_0_gemv",
+                 "rz_swiglu_ffn_q4k", "rz_last_error", "rz_abi_version"):
         assert name in syms
 
 
@@ -116,6 +116,23 @@ def test_q8_1_quantize_rejects(lib, args, code):
 def test_q4k_q8_gemv_rejects(lib, args, code):
     assert _rc("rz_q4k_q8_gemv", *args) == code
     assert "rz_q4k_q8_gemv" in _rc.last
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, P, 4096, P, P, 14336, 4096, None), rz.RZ_EINVAL),
+    ((P, None, 4096, P, P, 14336, 4096, None), rz.RZ_EINVAL),
+    ((P, P, 4096, P, None, 14336, 4096, None), rz.RZ_EINVAL),
+    ((P, P, 4096, P, P, 14336, 4000, None), rz.RZ_EDIM),
+    ((P, P, 4097, P, P, 14336, 4096, None), rz.RZ_EDIM),     # n > in_dim
+    ((P, P, 0, P, P, 14336, 4096, None), rz.RZ_EDIM),
+    ((P, P, 20480, P, P, 14336, 20480, None), rz.RZ_EDIM),   # above the fused limit
+    ((P, P, 4096, P, P, 0, 4096, None), rz.RZ_EDIM),
+    ((P + 8, P, 4096, P, P, 14336, 4096, None), rz.RZ_EALIGN),
+    ((P, P_ODD, 4096, P, P, 14336, 4096, None), rz.RZ_EALIGN),
+    ((P, P, 4096, P + 4, P, 14336, 4096, None), rz.RZ_EALIGN),
+])
+def test_q4k_q8_gemv_f32_rejects(lib, args, code):
+    assert _rc("rz_q4k_q8_gemv_f32", *args) == code
 
 
 @pytest.mark.parametrize("args,code", [

@@ -270,6 +270,48 @@ def test_q4k_token_batch(n_tokens):
         assert np.array_equal(single, Y[t]), "token %d differs from its single launch" % t
 
 
+# ------------------------------------------------------------------ fused quantize + GEMV
+@pytest.mark.parametrize("out_dim,n,in_dim", [
+    (3, 200, 256), (65, 512, 512), (896, 896, 1024), (129, 1280, 1280), (1000, 3000, 3072),
+    (1024, 4096, 4096), (14336, 4096, 4096), (4096, 14336, 14336), (77, 16384, 16384),
+])
+def test_q4k_gemv_f32_matches_two_step_and_oracle(out_dim, n, in_dim):
+    """One launch (quantize in LDS + GEMV) equals rz_q8_1_quantize followed by
+    rz_q4k_q8_gemv bit for bit; its Q8_1 side output equals the oracle's bytes;
+    y is within the GEMV bound of the oracle."""
+    banner("q4k gemv f32", out_dim, n, in_dim)
+    blob = synth.q4k_weights(synth.rng(12, out_dim + in_dim), out_dim, in_dim)
+    x = synth.activation(synth.rng(12, n), n)
+    wd = dev_bytes(blob)
+    xd = dev_f32(x)
+    xq = empty_bytes(rz.q8_1_nbytes(in_dim))
+    y = empty_f32(out_dim)
+    rz.rz_q4k_q8_gemv_f32(wd, xd, n, xq, y, out_dim, in_dim)
+    y_f = host(y)
+    xq_f = q8_host_bytes(xq, in_dim // 32)
+    xq_ref = oracle.quantize_q8_1(x, in_dim)
+    assert np.array_equal(xq_f, oracle.q8_1_to_bytes(xq_ref))
+    xq2 = empty_bytes(rz.q8_1_nbytes(in_dim))
+    rz.rz_q8_1_quantize(xd, n, in_dim, 1, xq2)
+    y2 = empty_f32(out_dim)
+    rz.rz_q4k_q8_gemv(wd, xq2, y2, out_dim, in_dim, 1)
+    assert np.array_equal(y_f, host(y2))
+    y_ref, terms = oracle.gemv_q4k_q8_int(blob, xq_ref)
+    assert_within(y_f, y_ref, terms, "q4k gemv f32 %dx%d" % (out_dim, in_dim))
+
+
+def test_q4k_gemv_f32_without_side_output():
+    banner("q4k gemv f32 no x_q8")
+    out_dim, in_dim = 300, 2048
+    blob = synth.q4k_weights(synth.rng(13, 1), out_dim, in_dim)
+    x = synth.activation(synth.rng(13, 0), in_dim)
+    y1, y2 = empty_f32(out_dim), empty_f32(out_dim)
+    rz.rz_q4k_q8_gemv_f32(dev_bytes(blob), dev_f32(x), in_dim, None, y1, out_dim, in_dim)
+    xq = empty_bytes(rz.q8_1_nbytes(in_dim))
+    rz.rz_q4k_q8_gemv_f32(dev_bytes(blob), dev_f32(x), in_dim, xq, y2, out_dim, in_dim)
+    assert np.array_equal(host(y1), host(y2))
+
+
 # ------------------------------------------------------------------ full-size workloads
 def test_q4k_attention_projections_full():
     """Q 4096x4096, K/V 1024x4096, O 4096x4096 sharing one RMSNorm'd activation."""
