@@ -1,18 +1,23 @@
 """Benchmark of the Q4_K x Q8_1 decode GEMV at 4096 -> 14336, batch 1.
 
 One step = the whole hot path for one token: quantize the fp32 activation to
-Q8_1 (rz_q8_1_quantize), then y = W x (rz_q4k_q8_gemv) with W a 14336 x 4096
-Q4_K matrix (33,030,144 bytes).  Every step reads the next of R weight copies
+Q8_1 and compute y = W x with W a 14336 x 4096 Q4_K matrix (33,030,144
+bytes), as one rz_q4k_q8_gemv_f32 launch (bit-identical to rz_q8_1_quantize
+followed by rz_q4k_q8_gemv, which is also timed).  Every step reads the next of R weight copies
 (R * 33 MB >= 1 GiB), so no step finds its weights in the 256 MB Infinity
 Cache or an L2; inputs are resident in HBM before the timed region.
 
 Printed (one JSON line): the whole-step weight-stream rate in GB/s (`value`,
-K steps captured in one HIP graph and replayed between HIP events), the GEMV
-kernel's own rate against the 8 TB/s HBM peak (`roofline`: K back-to-back GEMV
-launches in a graph, timed the same way), and the CPU oracle timed on the host
-(`cpu_baseline`).
+K steps captured in one HIP graph and replayed between HIP events), the fused
+kernel's rate against the 8 TB/s HBM peak (`roofline`), the CPU oracle timed
+on the host (`cpu_baseline`), and under `rows` every other kernel of the path
+at its own workload, timed the same way with its own weight rotation:
+Q8_1 quantize, the GEMV alone, the four attention projections on one shared
+activation, the SwiGLU chain and its down projection, the Q4_0 LM head (fp32
+and Q8_1 activation), 8 tokens sharing one weight pass, and the small
+896 x 1024 case.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-rows]
 """
 from __future__ import annotations
 
@@ -92,6 +97,147 @@ def cpu_baseline(target_seconds: float):
                       "%.1f s wall; host has %d cores" % (reps, wall, len(os.sched_getaffinity(0)))}
 
 
+def q4k_bytes(out_dim: int, in_dim: int) -> int:
+    return out_dim * (in_dim // 256) * 144
+
+
+def q4_0_bytes(out_dim: int, in_dim: int) -> int:
+    return out_dim * (in_dim // 32) * 18
+
+
+def q8_bytes(n: int) -> int:
+    return (n // 32) * 40
+
+
+def row_entry(seconds: float, algo_bytes: int, weight_bytes: int, launches: str) -> dict:
+    gbs = algo_bytes / seconds / 1e9
+    return {"us": round(seconds * 1e6, 3), "launches": launches, "algo_bytes": algo_bytes,
+            "weight_gbs": round(weight_bytes / seconds / 1e9, 2), "algo_gbs": round(gbs, 2),
+            "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def time_rows(lib, rz, torch, dev, graph_time, copies, x, xq, y) -> dict:
+    """Every kernel of the path at its own workload.  Each row rotates over its
+    own weight copies (>= 1 GiB in all), so every call streams its weights from
+    HBM; times are graph-replay means per call, as for the step."""
+    import synth
+
+    def rotated(blobs):
+        reps = max(1, -(-ROTATE_BYTES // sum(b.size for b in blobs)))
+        first = [torch.from_numpy(b.reshape(-1).copy()).to(dev) for b in blobs]
+        return [first] + [[t.clone() for t in first] for _ in range(reps - 1)]
+
+    def check(rc):
+        if rc:
+            raise RuntimeError(rz.rz_last_error())
+
+    rows = {}
+    x_p, xq_p, y_p = x.data_ptr(), xq.data_ptr(), y.data_ptr()
+    n_copies = len(copies)
+    w_p = [c.data_ptr() for c in copies]
+
+    # a1: Q8_1 quantize of one 4096-value activation (launch-latency bound)
+    rows["q8_1_quantize_4096"] = row_entry(
+        graph_time(lambda i, s: check(lib.rz_q8_1_quantize(x_p, IN_DIM, IN_DIM, 1, xq_p, s))),
+        X_BYTES + XQ_BYTES, 0, "rz_q8_1_quantize")
+    check(lib.rz_q8_1_quantize(x_p, IN_DIM, IN_DIM, 1, xq_p, torch.cuda.current_stream().cuda_stream))
+
+    # a2+a3: the GEMV alone over the shared Q8_1 activation
+    rows["q4k_gemv_4096x14336"] = row_entry(
+        graph_time(lambda i, s: check(lib.rz_q4k_q8_gemv(w_p[i % n_copies], xq_p, y_p, OUT_DIM,
+                                                         IN_DIM, 1, s))),
+        GEMV_ALGO_BYTES, W_BYTES, "rz_q4k_q8_gemv")
+
+    # a8: 8 tokens, one weight pass
+    x8 = torch.from_numpy(synth.activation(synth.rng(4, synth.T_ACT), IN_DIM, 8)).to(dev)
+    xq8 = torch.empty(8 * XQ_BYTES, dtype=torch.uint8, device=dev)
+    y8 = torch.empty(8 * OUT_DIM, dtype=torch.float32, device=dev)
+    check(lib.rz_q8_1_quantize(x8.data_ptr(), IN_DIM, IN_DIM, 8, xq8.data_ptr(),
+                               torch.cuda.current_stream().cuda_stream))
+    rows["q4k_gemv_batch8_4096x14336"] = row_entry(
+        graph_time(lambda i, s: check(lib.rz_q4k_q8_gemv(w_p[i % n_copies], xq8.data_ptr(),
+                                                         y8.data_ptr(), OUT_DIM, IN_DIM, 8, s))),
+        W_BYTES + 8 * XQ_BYTES + 8 * Y_BYTES, W_BYTES, "rz_q4k_q8_gemv n_tokens=8")
+
+    # attention projections of one layer: Q 4096x4096, K and V 1024x4096, O 4096x4096
+    shapes = [(4096, 4096), (1024, 4096), (1024, 4096), (4096, 4096)]
+    attn = rotated([synth.q4k_weights(synth.rng(1, 1 + k), o, i) for k, (o, i) in enumerate(shapes)])
+    ya = torch.empty(4096, dtype=torch.float32, device=dev)
+    attn_p = [[t.data_ptr() for t in c] for c in attn]
+
+    def attn_body(i, s):
+        ws = attn_p[i % len(attn_p)]
+        for w, (o, n) in zip(ws, shapes):
+            check(lib.rz_q4k_q8_gemv(w, xq_p, ya.data_ptr(), o, n, 1, s))
+
+    attn_w = sum(q4k_bytes(o, n) for o, n in shapes)
+    rows["attn_qkvo_4096"] = row_entry(
+        graph_time(attn_body), attn_w + 4 * XQ_BYTES + 4 * (4096 + 1024 + 1024 + 4096), attn_w,
+        "4 x rz_q4k_q8_gemv (Q, K, V, O) on one Q8_1 activation")
+    del attn
+
+    # SwiGLU chain 4096 -> 14336 -> 4096, and its down projection alone
+    INTER = 14336
+    ffn = rotated([synth.q4k_weights(synth.rng(2, 1), INTER, IN_DIM),
+                   synth.q4k_weights(synth.rng(2, 2), INTER, IN_DIM),
+                   synth.q4k_weights(synth.rng(2, 3), IN_DIM, INTER)])
+    ffn_p = [[t.data_ptr() for t in c] for c in ffn]
+    h = torch.empty(INTER, dtype=torch.float32, device=dev)
+    hq = torch.empty(q8_bytes(INTER), dtype=torch.uint8, device=dev)
+    yf = torch.empty(IN_DIM, dtype=torch.float32, device=dev)
+
+    def ffn_body(i, s):
+        wg, wu, wd = ffn_p[i % len(ffn_p)]
+        check(lib.rz_swiglu_ffn_q4k(wg, wu, wd, xq_p, h.data_ptr(), hq.data_ptr(), yf.data_ptr(),
+                                    None, IN_DIM, INTER, s))
+
+    ffn_w = 3 * W_BYTES
+    rows["swiglu_ffn_4096_14336"] = row_entry(
+        graph_time(ffn_body),
+        ffn_w + XQ_BYTES + 4 * INTER + 2 * q8_bytes(INTER) + 4 * IN_DIM, ffn_w,
+        "rz_swiglu_ffn_q4k (gate/up + silu*up + requantize, then down)")
+    rows["q4k_gemv_down_14336x4096"] = row_entry(
+        graph_time(lambda i, s: check(lib.rz_q4k_q8_gemv(ffn_p[i % len(ffn_p)][2], hq.data_ptr(),
+                                                         yf.data_ptr(), IN_DIM, INTER, 1, s))),
+        W_BYTES + q8_bytes(INTER) + 4 * IN_DIM, W_BYTES, "rz_q4k_q8_gemv")
+    del ffn
+
+    # Q4_0 LM head 151936 x (896 -> 1024), fp32 and Q8_1 activation
+    VOCAB, HID, HID_P = 151936, 896, 1024
+    lm = rotated([synth.q4_0_weights(synth.rng(3, 1), VOCAB, HID_P)])
+    lm_p = [c[0].data_ptr() for c in lm]
+    xl = torch.zeros(HID_P, dtype=torch.float32, device=dev)
+    xl[:HID] = torch.from_numpy(synth.activation(synth.rng(3, synth.T_ACT), HID)).to(dev)
+    xlq = torch.empty(q8_bytes(HID_P), dtype=torch.uint8, device=dev)
+    check(lib.rz_q8_1_quantize(xl.data_ptr(), HID, HID_P, 1, xlq.data_ptr(),
+                               torch.cuda.current_stream().cuda_stream))
+    logits = torch.empty(VOCAB, dtype=torch.float32, device=dev)
+    lm_w = q4_0_bytes(VOCAB, HID_P)
+    for fmt, xp, xbytes, name in ((0, xl.data_ptr(), 4 * HID_P, "fp32"),
+                                  (1, xlq.data_ptr(), q8_bytes(HID_P), "q8_1")):
+        rows["q4_0_lm_head_151936x1024_%s" % name] = row_entry(
+            graph_time(lambda i, s: check(lib.rz_q4_0_gemv(lm_p[i % len(lm_p)], xp, fmt,
+                                                           logits.data_ptr(), VOCAB, HID_P, s))),
+            lm_w + xbytes + 4 * VOCAB, lm_w, "rz_q4_0_gemv x_format=%d" % fmt)
+    del lm
+
+    # the small case: 896 x (896 -> 1024), launch-bound
+    small = rotated([synth.q4k_weights(synth.rng(0, 1), 896, 1024)])
+    small_p = [c[0].data_ptr() for c in small]
+    xs = torch.zeros(1024, dtype=torch.float32, device=dev)
+    xs[:896] = torch.from_numpy(synth.activation(synth.rng(0, synth.T_ACT), 896)).to(dev)
+    ys = torch.empty(896, dtype=torch.float32, device=dev)
+    rows["q4k_fused_896x1024"] = row_entry(
+        graph_time(lambda i, s: check(lib.rz_q4k_q8_gemv_f32(small_p[i % len(small_p)],
+                                                             xs.data_ptr(), 896, None,
+                                                             ys.data_ptr(), 896, 1024, s))),
+        q4k_bytes(896, 1024) + 4 * 896 + 4 * 896, q4k_bytes(896, 1024), "rz_q4k_q8_gemv_f32")
+    del small
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rows
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -99,6 +245,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-rows", action="store_true",
+                    help="time only the step, not the other kernels of the path")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after timing, run 4 plain device copies of MIB MiB (a reference "
                          "for the HBM byte counters of a profiling run)")
@@ -176,6 +324,7 @@ def main() -> int:
         return e0.elapsed_time(e1) * 1e-3 / K
 
     step_s = graph_time(fused)            # the timed steps (whole hot path)
+    rows = None if args.no_rows else time_rows(lib, rz, torch, dev, graph_time, copies, x, xq, y)
     ms_step = step_s * 1e3
     two_s = graph_time(two_launch)        # same work as two launches
     gemv_s = graph_time(gemv_only)        # the GEMV kernel alone
@@ -218,6 +367,7 @@ def main() -> int:
         "gemv_kernel_us": round(gemv_s * 1e6, 3),
         "gemv_kernel_gbs": round(GEMV_ALGO_BYTES / gemv_s / 1e9, 2),
         "kernel_source_sha256_16": kernel_source_hash(),
+        "rows": rows,
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 2),

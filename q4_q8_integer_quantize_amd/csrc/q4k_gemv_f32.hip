@@ -11,6 +11,11 @@
 // rz_q4k_q8_gemv, and workgroup 0 can also write the Q8_1 blocks out so that
 // further projections of the same activation (K, V after Q) reuse them.
 //
+// When n is a multiple of 4 (XV) every thread's four values of a pass come in
+// one 16-byte load; otherwise as four dword loads, so a quad that straddles n
+// reads zeros past it.  The activation loads go out first and as few as
+// possible: at kernel start they compete with the first weight tiles.
+//
 // Order inside a workgroup: (1) the lane's share of x is requested, (2) the
 // first weight tiles are requested, (3) x is quantized into LDS as soon as it
 // arrives (vector loads retire in order, so this wait does not include the
@@ -62,7 +67,7 @@ __device__ __forceinline__ void load_x_slots_lds(XSlots<S, 1>& xs, const uint8_t
 // Q8_1 blocks per workgroup pass: 256 threads, 8 lanes per block.
 constexpr int kBlocksPerPass = 32;
 
-template <int TPR, int S, int R, int G, int P>
+template <int TPR, int S, int R, int G, int P, bool XV>
 __global__ __launch_bounds__(256) void q4k_gemv_f32_kernel(Q4KF32Args a) {
   constexpr int RW = 8 / TPR;
   constexpr uint32_t kRowsPerGroup = (uint32_t)RW * R;
@@ -82,7 +87,19 @@ __global__ __launch_bounds__(256) void q4k_gemv_f32_kernel(Q4KF32Args a) {
 #pragma unroll
   for (int p = 0; p < kPasses; ++p) {
     const int b = p * kBlocksPerPass + qb;
-    load_block_quad(xv[p], xr, 0u, b * kQK8 + 4 * qi, a.n, b < nblk, xbytes);
+    if constexpr (XV) {
+      const uint32_t e = (uint32_t)(b * kQK8 + 4 * qi);
+      const uint32_t off = (b < nblk && e < (uint32_t)a.n) ? e * 4u : xbytes;
+      const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
+      // copy the elements out before reinterpreting them
+      const uint32_t v0 = v.x, v1 = v.y, v2 = v.z, v3 = v.w;
+      xv[p][0] = __builtin_bit_cast(float, v0);
+      xv[p][1] = __builtin_bit_cast(float, v1);
+      xv[p][2] = __builtin_bit_cast(float, v2);
+      xv[p][3] = __builtin_bit_cast(float, v3);
+    } else {
+      load_block_quad(xv[p], xr, 0u, b * kQK8 + 4 * qi, a.n, b < nblk, xbytes);
+    }
   }
 
   // (2) the first weight tiles
@@ -153,28 +170,33 @@ __global__ __launch_bounds__(256) void q4k_gemv_f32_kernel(Q4KF32Args a) {
 constexpr int kF32TilesInFlight = 2;
 constexpr long kF32TargetWaves = 1024;
 
-template <int TPR, int S, int G>
+template <int TPR, int S, int G, bool XV>
 static hipError_t launch_f32_g(const Q4KF32Args& a, long groups, hipStream_t st) {
   constexpr int R = S <= 2 ? 2 : 1;
   constexpr int P = G > kF32TilesInFlight ? kF32TilesInFlight : (G > 1 ? G - 1 : 1);
   const long waves = (groups + G - 1) / G;
   const unsigned grid = (unsigned)((waves + 3) / 4);
   const size_t lds = (size_t)a.nsb * 8 * kQ8Bytes;
-  hipLaunchKernelGGL((q4k_gemv_f32_kernel<TPR, S, R, G, P>), dim3(grid), dim3(256), lds, st, a);
+  hipLaunchKernelGGL((q4k_gemv_f32_kernel<TPR, S, R, G, P, XV>), dim3(grid), dim3(256), lds, st, a);
   return hipGetLastError();
 }
 
-template <int TPR, int S>
-static hipError_t run_f32(const Q4KF32Args& a, hipStream_t st) {
+template <int TPR, int S, bool XV>
+static hipError_t run_f32_x(const Q4KF32Args& a, hipStream_t st) {
   constexpr int R = S <= 2 ? 2 : 1;
   constexpr int RW = 8 / TPR;
   const long rows_per_group = (long)RW * R;
   const long groups = (a.out_dim + rows_per_group - 1) / rows_per_group;
   const long per_wave = (groups + kF32TargetWaves - 1) / kF32TargetWaves;
-  if (per_wave <= 1) return launch_f32_g<TPR, S, 1>(a, groups, st);
-  if (per_wave <= 2) return launch_f32_g<TPR, S, 2>(a, groups, st);
-  if (per_wave <= 4) return launch_f32_g<TPR, S, 4>(a, groups, st);
-  return launch_f32_g<TPR, S, 8>(a, groups, st);
+  if (per_wave <= 1) return launch_f32_g<TPR, S, 1, XV>(a, groups, st);
+  if (per_wave <= 2) return launch_f32_g<TPR, S, 2, XV>(a, groups, st);
+  if (per_wave <= 4) return launch_f32_g<TPR, S, 4, XV>(a, groups, st);
+  return launch_f32_g<TPR, S, 8, XV>(a, groups, st);
+}
+
+template <int TPR, int S>
+static hipError_t run_f32(const Q4KF32Args& a, hipStream_t st) {
+  return (a.n & 3) == 0 ? run_f32_x<TPR, S, true>(a, st) : run_f32_x<TPR, S, false>(a, st);
 }
 
 hipError_t launch_q4k_q8_gemv_f32(const uint8_t* w, const float* x, int n, uint8_t* xq_out,
