@@ -20,8 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "librz.so")
 
-SOURCES = ["q8_1_quantize.hip", "q4k_gemv.hip", "q4k_gemv_f32.hip", "q4_0_gemv.hip",
-           "swiglu_ffn.hip", "rz_abi.cpp"]
+SOURCES = ["q8_1_quantize.hip", "q4k_gemv.hip", "q4k_gemv_f32.hip", "q4k_gemm_mfma.hip",
+           "q4_0_gemv.hip", "swiglu_ffn.hip", "rz_abi.cpp"]
 ARCH = os.environ.get("RZ_OFFLOAD_ARCH", "gfx950")
 
 
@@ -35,6 +35,8 @@ def common_flags() -> list[str]:
         f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-fast-math",
+        # MFMA results in VGPRs (read by the rescale right away) instead of AGPRs
+        "-mllvm", "-amdgpu-mfma-vgpr-form=1",
         "-I", INCLUDE, "-I", CSRC,
     ]
 

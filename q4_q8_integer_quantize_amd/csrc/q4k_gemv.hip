@@ -5,6 +5,9 @@
 // The token batch streams the weights once and reuses each loaded super-block
 // for every token (the weights are the only large operand).
 //
+// From kMfmaMinTokens tokens on, the batch runs on the matrix cores
+// (q4k_gemm_mfma.hip).
+//
 // Work split: a group is RW*R consecutive rows (RW = 8/TPR side by side, R
 // unrolled); each wave takes G groups strided by the wave count and keeps P
 // more in flight while it reduces one.  Rows longer than the register-resident activation window
@@ -102,6 +105,8 @@ hipError_t launch_q4k_q8_gemv(const uint8_t* w, const uint8_t* xq, float* y, int
   a.sb0 = 0;
   a.nsb = a.nsb_row;
   a.n_tokens = n_tokens;
+  if (n_tokens >= kMfmaMinTokens)
+    return launch_q4k_q8_gemm_mfma(w, xq, y, out_dim, in_dim, n_tokens, stream);
   if (n_tokens == 1) return run_q4k_all<1>(a, stream);
   if (n_tokens == 2) return run_q4k_all<2>(a, stream);
   if (n_tokens <= 4) return run_q4k_all<4>(a, stream);

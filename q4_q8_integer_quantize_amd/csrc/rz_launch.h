@@ -14,6 +14,12 @@ hipError_t launch_q8_1_quantize(const float* x, int n, int n_padded, int n_token
 hipError_t launch_q4k_q8_gemv(const uint8_t* w, const uint8_t* xq, float* y, int out_dim,
                               int in_dim, int n_tokens, hipStream_t stream);
 
+// The same for a batch of tokens on the matrix cores (used by
+// launch_q4k_q8_gemv from kMfmaMinTokens tokens on).
+hipError_t launch_q4k_q8_gemm_mfma(const uint8_t* w, const uint8_t* xq, float* y, int out_dim,
+                                   int in_dim, int n_tokens, hipStream_t stream);
+constexpr int kMfmaMinTokens = 3;
+
 // Q8_1 quantize of an fp32 activation fused into the Q4_K GEMV (1 token).
 hipError_t launch_q4k_q8_gemv_f32(const uint8_t* w, const float* x, int n, uint8_t* xq_out,
                                   float* y, int out_dim, int in_dim, hipStream_t stream);

@@ -254,8 +254,8 @@ def test_q4k_scaling_and_row_permutation_gpu():
 
 @pytest.mark.parametrize("n_tokens", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_q4k_token_batch(n_tokens):
-    """Each token against the oracle, and the batched result equal bit for bit
-    to one-token launches (tokens share the weight pass, not arithmetic)."""
+    """Each token against the oracle; the tokens of a batch do not interact:
+    reversing their order reverses the outputs bit for bit."""
     banner("q4k batch", n_tokens)
     out_dim, in_dim = 515, 4096
     blob = synth.q4k_weights(synth.rng(4, 1), out_dim, in_dim)
@@ -266,8 +266,29 @@ def test_q4k_token_batch(n_tokens):
     y_ref, terms = oracle_q4k(blob, xq, n_tokens)
     for t in range(n_tokens):
         assert_within(Y[t], y_ref[t], terms[t], "token %d" % t)
-        single = gpu_q4k(blob, xb[t])[0]
-        assert np.array_equal(single, Y[t]), "token %d differs from its single launch" % t
+    Yr = gpu_q4k(blob, np.ascontiguousarray(xb.reshape(n_tokens, -1)[::-1]), n_tokens)
+    assert np.array_equal(Yr, Y[::-1]), "token order changes the results"
+
+
+@pytest.mark.parametrize("n_tokens,out_dim,in_dim", [
+    (8, 515, 4096), (3, 64, 1024), (5, 100, 2048), (8, 33, 14336), (7, 17, 3072), (4, 16, 256),
+])
+def test_q4k_batch_integer_exact_bit_exact(n_tokens, out_dim, in_dim):
+    """d = dmin = 1, activation d = 1, codes in [-8, 8] for every token: each
+    output is an integer below 2**24 that any summation order reaches exactly,
+    so the batched GPU result must equal the oracle bit for bit; a wrong int32
+    sub-block sum, or a token or sub-block mixed into another, shows up here."""
+    banner("q4k batch integer-exact", n_tokens, out_dim, in_dim)
+    blob = synth.q4k_weights(synth.rng(61, out_dim), out_dim, in_dim, d_fixed=1.0, dmin_fixed=1.0)
+    nb = in_dim // 32
+    toks = [_integer_q8(nb, seed=1000 * t + in_dim) for t in range(n_tokens)]
+    xb = np.concatenate([oracle.q8_1_to_bytes(q) for q in toks])
+    Y = gpu_q4k(blob, xb, n_tokens)
+    for t, q in enumerate(toks):
+        y_ref, _ = oracle.gemv_q4k_q8_int(blob, q)
+        assert np.all(np.abs(y_ref) < 2 ** 24)
+        mm = first_mismatch(Y[t].astype(np.float64), y_ref)
+        assert mm is None, "token %d: row %s gpu=%r oracle=%r (%d rows differ)" % ((t,) + mm)
 
 
 # ------------------------------------------------------------------ fused quantize + GEMV
