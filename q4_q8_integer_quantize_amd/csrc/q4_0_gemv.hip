@@ -8,7 +8,8 @@
 // A lane owns a pair of 18-byte blocks (36 bytes, 4-byte aligned when in_dim
 // is a multiple of 64): block A = d | qs at bytes 0..17, block B at 18..35.
 // LPR lanes share a row (RW = 64/LPR rows side by side); S pair slots per
-// lane keep that lane's activation values in registers for the wave's life.
+// lane keep that lane's activation values in registers for the wave's life,
+// and each wave streams G row groups with P of them requested ahead.
 //   fp32 x : sum_l q_l x_l per block, then d * (sum - 8 * sum_l x_l)
 //   Q8_1 x : isum = sum_l q_l q8_l - 8 * sum_l q8_l (exact), then d * d_x * isum
 #include "rz_device.h"
@@ -102,46 +103,50 @@ __device__ __forceinline__ void load_x40(X40<S, Q8>& xs, const Q40Args& a, int p
 }
 
 // sum_l q_l * x_l over one block; qs dwords hold values 4k..4k+3 (low
-// nibbles) and 16+4k..16+4k+3 (high nibbles).
+// nibbles) and 16+4k..16+4k+3 (high nibbles).  Eight independent partial sums
+// (one per byte position and nibble) keep the fma chains short; they are added
+// pairwise at the end.
 __device__ __forceinline__ float block_dot_f32(const uint32_t qs[4], const float* x) {
-  float acc = 0.0f;
+  float acc[8];
+#pragma unroll
+  for (int b = 0; b < 8; ++b) acc[b] = 0.0f;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const uint32_t lo = qs[k] & 0x0F0F0F0Fu;
     const uint32_t hi = (qs[k] >> 4) & 0x0F0F0F0Fu;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      acc = fmaf((float)((lo >> (8 * b)) & 0xffu), x[4 * k + b], acc);
-      acc = fmaf((float)((hi >> (8 * b)) & 0xffu), x[16 + 4 * k + b], acc);
+      acc[b] = fmaf((float)((lo >> (8 * b)) & 0xffu), x[4 * k + b], acc[b]);
+      acc[4 + b] = fmaf((float)((hi >> (8 * b)) & 0xffu), x[16 + 4 * k + b], acc[4 + b]);
     }
   }
-  return acc;
+  return ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
 }
 
 __device__ __forceinline__ int block_dot_q8(const uint32_t qs[4], const int* q8) {
-  int acc = 0;
+  int lo = 0, hi = 0;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    acc = dot4((int)(qs[k] & 0x0F0F0F0Fu), q8[k], acc);
-    acc = dot4((int)((qs[k] >> 4) & 0x0F0F0F0Fu), q8[4 + k], acc);
+    lo = dot4((int)(qs[k] & 0x0F0F0F0Fu), q8[k], lo);
+    hi = dot4((int)((qs[k] >> 4) & 0x0F0F0F0Fu), q8[4 + k], hi);
   }
-  return acc;
+  return lo + hi;
 }
 
-template <int LPR, int S, int R, bool Q8>
-__global__ __launch_bounds__(256) void q4_0_gemv_kernel(Q40Args a) {
-  constexpr int RW = kWave / LPR;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int rs = lane / LPR, ps = lane % LPR;
-  const long wave = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const long row_base = wave * (RW * R);
-  if (row_base >= a.out_dim) return;   // wave-uniform
-  X40<S, Q8> xs;
-  load_x40<LPR, S, Q8>(xs, a, ps);
-
-  const size_t row_bytes = (size_t)a.npairs_row * 36;
+// Weights of R rows x S pair slots for one lane: the two 18-byte blocks of a
+// pair as 16 + 16 + 4 bytes.  Rows past out_dim and slots past the chunk read
+// row out_dim - 1 / the chunk's last pair (their results are not stored, and
+// idle slots have zero activations).
+template <int S, int R>
+struct Q40Tile {
   u32x4_a4 v0[R][S], v1[R][S];
   uint32_t v8[R][S];
+};
+
+template <int LPR, int S, int R>
+__device__ __forceinline__ void load_q40_tile(Q40Tile<S, R>& t, const Q40Args& a, long row_base,
+                                              int rs, int ps, size_t row_bytes) {
+  constexpr int RW = kWave / LPR;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     long row = row_base + (long)r * RW + rs;
@@ -149,47 +154,71 @@ __global__ __launch_bounds__(256) void q4_0_gemv_kernel(Q40Args a) {
 #pragma unroll
     for (int s = 0; s < S; ++s) {
       int p = s * LPR + ps;
-      if (p >= a.npairs) p = a.npairs - 1;   // inactive slot: zero activation
+      if (p >= a.npairs) p = a.npairs - 1;
       const uint8_t* ptr = a.w + (size_t)row * row_bytes + ((size_t)a.p0 + p) * 36;
-      v0[r][s] = *(const u32x4_a4*)ptr;
-      v1[r][s] = *(const u32x4_a4*)(ptr + 16);
-      v8[r][s] = *(const uint32_t*)(ptr + 32);
+      t.v0[r][s] = *(const u32x4_a4*)ptr;
+      t.v1[r][s] = *(const u32x4_a4*)(ptr + 16);
+      t.v8[r][s] = *(const uint32_t*)(ptr + 32);
     }
   }
+}
 
-  float acc[R];
+// Wave w of W takes the G row groups w, w+W, ... (a group is RW*R rows),
+// unrolled with P groups requested ahead, as in q4k_q8_gemv_kernel.
+template <int LPR, int S, int R, int G, int P, bool Q8, bool ACC>
+__global__ __launch_bounds__(256) void q4_0_gemv_kernel(Q40Args a) {
+  constexpr int RW = kWave / LPR;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int rs = lane / LPR, ps = lane % LPR;
+  const long nwaves = (long)gridDim.x * 4;
+  const long wid = __builtin_amdgcn_readfirstlane(blockIdx.x * 4u + (threadIdx.x >> 6));
+  const size_t row_bytes = (size_t)a.npairs_row * 36;
+  X40<S, Q8> xs;
+  load_x40<LPR, S, Q8>(xs, a, ps);
+  Q40Tile<S, R> t[G];
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    float ar = 0.0f;
+  for (int k = 0; k < P && k < G; ++k)
+    load_q40_tile<LPR, S, R>(t[k], a, (wid + k * nwaves) * (RW * R), rs, ps, row_bytes);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const u32x4_a4 A = v0[r][s], B = v1[r][s];
-      const float dA = f16_lo(A.x), dB = f16_hi(B.x);
-      const uint32_t qa[4] = {__builtin_amdgcn_alignbyte(A.y, A.x, 2),
-                              __builtin_amdgcn_alignbyte(A.z, A.y, 2),
-                              __builtin_amdgcn_alignbyte(A.w, A.z, 2),
-                              __builtin_amdgcn_alignbyte(B.x, A.w, 2)};
-      const uint32_t qb[4] = {B.y, B.z, B.w, v8[r][s]};
-      if constexpr (!Q8) {
-        const float sa = block_dot_f32(qa, &xs.v[s][0]);
-        const float sb = block_dot_f32(qb, &xs.v[s][32]);
-        ar = fmaf(dA, fmaf(-8.0f, xs.sum[s][0], sa), ar);
-        ar = fmaf(dB, fmaf(-8.0f, xs.sum[s][1], sb), ar);
-      } else {
-        const int ia = block_dot_q8(qa, &xs.q[s][0]) - 8 * xs.qsum[s][0];
-        const int ib = block_dot_q8(qb, &xs.q[s][8]) - 8 * xs.qsum[s][1];
-        ar = fmaf(dA * xs.dx[s][0], (float)ia, ar);
-        ar = fmaf(dB * xs.dx[s][1], (float)ib, ar);
-      }
-    }
-    acc[r] = group_sum_dpp<LPR>(ar);
-  }
-
-  if (ps == LPR - 1) {   // the lane that holds the reduced row sum
+  for (int k = 0; k < G; ++k) {
+    if (k + P < G)
+      load_q40_tile<LPR, S, R>(t[k + P], a, (wid + (k + P) * nwaves) * (RW * R), rs, ps, row_bytes);
+    __builtin_amdgcn_sched_barrier(0);
+    const long row_base = (wid + k * nwaves) * (RW * R);
+    float acc[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const long row = row_base + (long)r * RW + rs;
-      if (row < a.out_dim) a.y[row] = a.accumulate ? a.y[row] + acc[r] : acc[r];
+      float ar = 0.0f;
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const u32x4_a4 A = t[k].v0[r][s], B = t[k].v1[r][s];
+        const float dA = f16_lo(A.x), dB = f16_hi(B.x);
+        const uint32_t qa[4] = {__builtin_amdgcn_alignbyte(A.y, A.x, 2),
+                                __builtin_amdgcn_alignbyte(A.z, A.y, 2),
+                                __builtin_amdgcn_alignbyte(A.w, A.z, 2),
+                                __builtin_amdgcn_alignbyte(B.x, A.w, 2)};
+        const uint32_t qb[4] = {B.y, B.z, B.w, t[k].v8[r][s]};
+        if constexpr (!Q8) {
+          const float sa = block_dot_f32(qa, &xs.v[s][0]);
+          const float sb = block_dot_f32(qb, &xs.v[s][32]);
+          ar = fmaf(dA, fmaf(-8.0f, xs.sum[s][0], sa), ar);
+          ar = fmaf(dB, fmaf(-8.0f, xs.sum[s][1], sb), ar);
+        } else {
+          const int ia = block_dot_q8(qa, &xs.q[s][0]) - 8 * xs.qsum[s][0];
+          const int ib = block_dot_q8(qb, &xs.q[s][8]) - 8 * xs.qsum[s][1];
+          ar = fmaf(dA * xs.dx[s][0], (float)ia, ar);
+          ar = fmaf(dB * xs.dx[s][1], (float)ib, ar);
+        }
+      }
+      acc[r] = group_sum_dpp<LPR>(ar);
+    }
+    if (ps == LPR - 1) {   // the lane that holds the reduced row sum
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const long row = row_base + (long)r * RW + rs;
+        if (row < a.out_dim) a.y[row] = ACC ? a.y[row] + acc[r] : acc[r];
+      }
     }
   }
 }
@@ -197,15 +226,30 @@ __global__ __launch_bounds__(256) void q4_0_gemv_kernel(Q40Args a) {
 template <bool Q8>
 constexpr int pair_slots_max() { return Q8 ? 4 : 2; }
 
+template <int LPR, int S, int R, int G, bool Q8>
+static hipError_t launch_q40_g(const Q40Args& a, long groups, hipStream_t st) {
+  constexpr int P = G > 2 ? 2 : (G > 1 ? G - 1 : 1);
+  const long waves = (groups + G - 1) / G;
+  const unsigned grid = (unsigned)((waves + 3) / 4);
+  if (a.accumulate)
+    hipLaunchKernelGGL((q4_0_gemv_kernel<LPR, S, R, G, P, Q8, true>), dim3(grid), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((q4_0_gemv_kernel<LPR, S, R, G, P, Q8, false>), dim3(grid), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+// Groups per wave: the Q8_1 form streams best with many one-group waves
+// (latency hidden by occupancy); the fp32 form, whose arithmetic is heavier,
+// with two groups per wave once there are enough rows (measured on the
+// 151936 x 1024 LM head: 16.6 us and 23.9 us).
 template <int LPR, int S, bool Q8>
 static hipError_t run_q40(const Q40Args& a, hipStream_t st) {
   constexpr int R = S >= 4 ? 1 : 4 / S;
   constexpr int RW = kWave / LPR;
-  const long rows_per_wave = (long)RW * R;
-  const long waves = (a.out_dim + rows_per_wave - 1) / rows_per_wave;
-  const unsigned grid = (unsigned)((waves + 3) / 4);
-  hipLaunchKernelGGL((q4_0_gemv_kernel<LPR, S, R, Q8>), dim3(grid), dim3(256), 0, st, a);
-  return hipGetLastError();
+  const long rows_per_group = (long)RW * R;
+  const long groups = (a.out_dim + rows_per_group - 1) / rows_per_group;
+  if (!Q8 && groups >= 2048) return launch_q40_g<LPR, S, R, 2, Q8>(a, groups, st);
+  return launch_q40_g<LPR, S, R, 1, Q8>(a, groups, st);
 }
 
 template <bool Q8>

@@ -28,41 +28,48 @@ struct SwiArgs {
   int nsb;        // hidden / 256
 };
 
-template <int TPR, int S, int R>
+// Wave w owns rows 8w .. 8w+7 of the block.  Its work is G = 2 * (8 / (RW*R))
+// row groups -- gate and up alternating -- unrolled into straight-line code
+// with P groups requested ahead, as in q4k_q8_gemv_kernel: no load sits under
+// a branch, so each wait is for exactly the tile about to be reduced.
+template <int TPR, int S, int R, int P>
 __global__ __launch_bounds__(256) void swiglu_gate_up_kernel(SwiArgs a) {
   constexpr int RW = 8 / TPR;
-  constexpr int kPassRows = RW * R;
-  static_assert(32 % kPassRows == 0, "the 32 rows of a block split into whole passes");
+  constexpr int kGroupRows = RW * R;                 // rows of one matrix per group
+  static_assert(8 % kGroupRows == 0, "a wave's 8 rows split into whole groups");
+  constexpr int G = 2 * (8 / kGroupRows);            // gate, up, gate, up, ...
   __shared__ float gs[32], us[32], hs[32];
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t blk_row0 = blockIdx.x * 32u;
+  const uint32_t row0 = blk_row0 + wave * 8u;
   const LaneRole ro = make_role<TPR>();
-  XSlots<S, 1> xs;
-  load_x_slots<TPR, S, 1>(xs, a.xq, 0, a.nsb, 1, ro);
   const uint32_t row_bytes = (uint32_t)a.nsb * kQ4KBytes;
   const uint32_t bytes = (uint32_t)a.inter * row_bytes;
   const WSrc sg = make_wsrc(a.wg, row_bytes, bytes);
   const WSrc su = make_wsrc(a.wu, row_bytes, bytes);
   const LaneOffsets<TPR, S> off = lane_offsets<TPR, S>(sg, 0, ro);
 
-  // passes of RW*R rows, dealt to the 4 waves in turn; gate and up tiles of a
-  // pass are requested together before either is reduced
-  for (uint32_t pass = wave; pass < 32u / kPassRows; pass += 4u) {
-    const uint32_t row_base = blk_row0 + pass * kPassRows;
-    WTile<S, R> tg, tu;
-    load_w_tile<TPR, S, R>(tg, sg, off, row_base);
-    load_w_tile<TPR, S, R>(tu, su, off, row_base);
-    __builtin_amdgcn_sched_barrier(0);
-    float ag[R][1], au[R][1];
-    q4k_tile_dot<TPR, S, R, 1>(ag, tg, xs, ro);
-    q4k_tile_dot<TPR, S, R, 1>(au, tu, xs, ro);
-    if (row_leader<TPR>(ro)) {
+  // activation first: vector loads retire in order
+  XSlots<S, 1> xs;
+  load_x_slots<TPR, S, 1>(xs, a.xq, 0, a.nsb, 1, ro);
+  WTile<S, R> t[G];
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int local = pass * kPassRows + r * RW + ro.rs;
-        gs[local] = ag[r][0];
-        us[local] = au[r][0];
-      }
+  for (int k = 0; k < P && k < G; ++k)
+    load_w_tile<TPR, S, R>(t[k], (k & 1) ? su : sg, off, row0 + (uint32_t)(k >> 1) * kGroupRows);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int k = 0; k < G; ++k) {
+    if (k + P < G)
+      load_w_tile<TPR, S, R>(t[k + P], ((k + P) & 1) ? su : sg, off,
+                             row0 + (uint32_t)((k + P) >> 1) * kGroupRows);
+    __builtin_amdgcn_sched_barrier(0);
+    float acc[R][1];
+    q4k_tile_dot<TPR, S, R, 1>(acc, t[k], xs, ro);
+    if (row_leader<TPR>(ro)) {
+      float* dst = (k & 1) ? us : gs;
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        dst[wave * 8u + (uint32_t)(k >> 1) * kGroupRows + r * RW + ro.rs] = acc[r][0];
     }
   }
   __syncthreads();
@@ -95,11 +102,11 @@ __global__ __launch_bounds__(256) void swiglu_gate_up_kernel(SwiArgs a) {
 template <int TPR, int S>
 static hipError_t run_gate_up(const SwiArgs& a, hipStream_t st) {
   constexpr int RW = 8 / TPR;
-  // one pass of 8 rows per wave when registers allow (two tiles of R*S slots)
-  constexpr int R_fit = 8 / RW > 0 ? 8 / RW : 1;
-  constexpr int R_reg = S >= 6 ? 1 : (S >= 3 ? 2 : (S >= 2 ? 4 : 8));
-  constexpr int R = R_fit < R_reg ? R_fit : R_reg;
-  hipLaunchKernelGGL((swiglu_gate_up_kernel<TPR, S, R>), dim3(a.inter / 32), dim3(256), 0, st, a);
+  constexpr int R_reg = S <= 2 ? 2 : 1;               // rows unrolled per group
+  constexpr int R = RW * R_reg <= 8 ? R_reg : 1;
+  constexpr int G = 2 * (8 / (RW * R));
+  constexpr int P = G > 2 ? 2 : G - 1 > 0 ? G - 1 : 1;
+  hipLaunchKernelGGL((swiglu_gate_up_kernel<TPR, S, R, P>), dim3(a.inter / 32), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
