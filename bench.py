@@ -13,7 +13,7 @@ kernel's rate against the 8 TB/s HBM peak (`roofline`), the CPU oracle timed
 on the host (`cpu_baseline`), and under `rows` every other kernel of the path
 at its own workload, timed the same way with its own weight rotation:
 Q8_1 quantize, the GEMV alone, the four attention projections on one shared
-activation, the SwiGLU chain and its down projection, the Q4_0 LM head (fp32
+activation (one multi-matrix launch, and four launches), the SwiGLU chain and its down projection, the Q4_0 LM head (fp32
 and Q8_1 activation), 8 tokens sharing one weight pass, and the small
 896 x 1024 case.
 
@@ -170,8 +170,21 @@ def time_rows(lib, rz, torch, dev, graph_time, copies, x, xq, y) -> dict:
         for w, (o, n) in zip(ws, shapes):
             check(lib.rz_q4k_q8_gemv(w, xq_p, ya.data_ptr(), o, n, 1, s))
 
+    import ctypes
+    outs = [torch.empty(o, dtype=torch.float32, device=dev) for o, _ in shapes]
+    ods = (ctypes.c_int * 4)(*[o for o, _ in shapes])
+    yarr = (ctypes.c_void_p * 4)(*[t.data_ptr() for t in outs])
+    warrs = [(ctypes.c_void_p * 4)(*c) for c in attn_p]
+
+    def attn_multi(i, s):
+        check(lib.rz_q4k_q8_gemv_multi(4, warrs[i % len(warrs)], yarr, ods, xq_p, 4096, 1, s))
+
     attn_w = sum(q4k_bytes(o, n) for o, n in shapes)
+    attn_bytes = attn_w + XQ_BYTES + 4 * (4096 + 1024 + 1024 + 4096)
     rows["attn_qkvo_4096"] = row_entry(
+        graph_time(attn_multi), attn_bytes, attn_w,
+        "rz_q4k_q8_gemv_multi: Q, K, V, O in one launch on one Q8_1 activation")
+    rows["attn_qkvo_4096_separate"] = row_entry(
         graph_time(attn_body), attn_w + 4 * XQ_BYTES + 4 * (4096 + 1024 + 1024 + 4096), attn_w,
         "4 x rz_q4k_q8_gemv (Q, K, V, O) on one Q8_1 activation")
     del attn

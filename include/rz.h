@@ -50,6 +50,7 @@ extern "C" {
 #define RZ_Q4K_BLOCK_BYTES 144
 #define RZ_Q4_0_BLOCK_BYTES 18
 #define RZ_MAX_TOKENS 8
+#define RZ_MAX_MATS 8
 #define RZ_MAX_DIM (1 << 24)
 
 /* rz_q8_1_quantize -- fp32 activations to Q8_1 blocks.
@@ -83,6 +84,29 @@ int rz_q8_1_quantize(const float* x, int n, int n_padded, int n_tokens,
  * Errors: RZ_EINVAL, RZ_EDIM, RZ_EALIGN, RZ_ELAUNCH. */
 int rz_q4k_q8_gemv(const void* w_q4k, const void* x_q8, float* y,
                    int out_dim, int in_dim, int n_tokens, void* stream);
+
+/* rz_q4k_q8_gemv_multi -- several Q4_K matrices times one Q8_1 activation.
+ * Passage: realizar 0.8.5 src/cuda/executor/cached.rs,
+ * transformer_layer_gpu_true_dp4a, steps 2-3 (the activation is quantized
+ * once and the Q, K and V projections all read it).
+ * One launch covers the row groups of every matrix (small matrices such as a
+ * GQA layer's K and V would otherwise pay a launch each); each y[m] equals
+ * rz_q4k_q8_gemv(w_q4k[m], x_q8, y[m], out_dims[m], in_dim, n_tokens) bit for
+ * bit.  With more than 2 tokens or in_dim above 16384 the matrices are
+ * processed by one rz_q4k_q8_gemv call each.
+ *   n_mats    1..RZ_MAX_MATS
+ *   w_q4k     HOST array of n_mats device pointers; matrix m is
+ *             [out_dims[m]][in_dim/256] super-blocks, 16-byte aligned, < 2 GiB
+ *   y         HOST array of n_mats device pointers, out: fp32
+ *             [n_tokens][out_dims[m]], 4-byte aligned, not overlapping
+ *   out_dims  HOST array of n_mats row counts, each >= 1 and <= RZ_MAX_DIM
+ *   x_q8, in_dim, n_tokens: as for rz_q4k_q8_gemv
+ * The three host arrays are read during the call only.
+ * Errors: RZ_EINVAL (null pointer or array entry, n_mats or n_tokens out of
+ * range), RZ_EDIM, RZ_EALIGN, RZ_ELAUNCH. */
+int rz_q4k_q8_gemv_multi(int n_mats, const void* const* w_q4k, float* const* y,
+                         const int* out_dims, const void* x_q8, int in_dim, int n_tokens,
+                         void* stream);
 
 /* rz_q4k_q8_gemv_f32 -- Q8_1 quantize and Q4_K x Q8_1 GEMV in one launch.
  * Passage: realizar 0.8.5 src/cuda/executor/cached.rs,

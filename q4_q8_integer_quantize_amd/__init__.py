@@ -58,10 +58,11 @@ def load_library() -> ctypes.CDLL:
     lib.rz_q8_1_quantize.argtypes = [vp, i, i, i, vp, vp]
     lib.rz_q4k_q8_gemv.argtypes = [vp, vp, vp, i, i, i, vp]
     lib.rz_q4k_q8_gemv_f32.argtypes = [vp, vp, i, vp, vp, i, i, vp]
+    lib.rz_q4k_q8_gemv_multi.argtypes = [i, vp, vp, vp, vp, i, i, vp]
     lib.rz_q4_0_gemv.argtypes = [vp, vp, i, vp, i, i, vp]
     lib.rz_swiglu_ffn_q4k.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, vp]
-    for fn in ("rz_q8_1_quantize", "rz_q4k_q8_gemv", "rz_q4k_q8_gemv_f32", "rz_q4_0_gemv",
-               "rz_swiglu_ffn_q4k", "rz_abi_version"):
+    for fn in ("rz_q8_1_quantize", "rz_q4k_q8_gemv", "rz_q4k_q8_gemv_f32", "rz_q4k_q8_gemv_multi",
+               "rz_q4_0_gemv", "rz_swiglu_ffn_q4k", "rz_abi_version"):
         getattr(lib, fn).restype = i
     lib.rz_last_error.argtypes = []
     lib.rz_last_error.restype = ctypes.c_char_p
@@ -134,6 +135,26 @@ def rz_q4k_q8_gemv(w_q4k, x_q8, y, out_dim: int, in_dim: int, n_tokens: int = 1,
         _need(y, 4 * out_dim * n_tokens, "y")
     _check(load_library().rz_q4k_q8_gemv(_ptr(w_q4k), _ptr(x_q8), _ptr(y), out_dim, in_dim,
                                          n_tokens, _stream(stream)))
+
+
+def rz_q4k_q8_gemv_multi(ws, x_q8, ys, out_dims, in_dim: int, n_tokens: int = 1,
+                         stream=None) -> None:
+    """ys[m] fp32 [n_tokens, out_dims[m]] = ws[m] (Q4_K) x (Q8_1) for every m,
+    in one launch (see rz_q4k_q8_gemv_multi in include/rz.h)."""
+    n = len(ws)
+    if len(ys) != n or len(out_dims) != n:
+        raise ValueError("ws, ys and out_dims must have the same length")
+    if in_dim > 0 and in_dim % 256 == 0:
+        _need(x_q8, q8_1_nbytes(in_dim, n_tokens), "x_q8")
+        for w, y, od in zip(ws, ys, out_dims):
+            if od > 0:
+                _need(w, od * (in_dim // 256) * Q4K_BLOCK_BYTES, "w_q4k")
+                _need(y, 4 * od * n_tokens, "y")
+    wa = (ctypes.c_void_p * max(n, 1))(*[_ptr(w) for w in ws])
+    ya = (ctypes.c_void_p * max(n, 1))(*[_ptr(y) for y in ys])
+    da = (ctypes.c_int * max(n, 1))(*[int(d) for d in out_dims])
+    _check(load_library().rz_q4k_q8_gemv_multi(n, wa, ya, da, _ptr(x_q8), in_dim, n_tokens,
+                                               _stream(stream)))
 
 
 def rz_q4k_q8_gemv_f32(w_q4k, x, n: int, x_q8, y, out_dim: int, in_dim: int,

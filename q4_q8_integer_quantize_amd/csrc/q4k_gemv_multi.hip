@@ -1,0 +1,184 @@
+// q4k_gemv_multi.hip -- several Q4_K matrices times one Q8_1 activation in
+// one launch.
+//
+// realizar 0.8.5 src/cuda/executor/cached.rs, transformer_layer_gpu_true_dp4a,
+// steps 2-3: the activation is quantized to Q8_1 once and the Q, K and V
+// projections all read it.  Launched one by one, the small K and V matrices
+// (1024 x 4096 in a 7B-class GQA layer, 2.4 MB) cost more in launch and ramp
+// than in streaming.  Here the row groups of all matrices form one grid: wave
+// w takes groups w, w+W, ..., and finds each group's matrix in a prefix table
+// (a scalar loop over at most 8 entries).  The per-row arithmetic is exactly
+// that of q4k_q8_gemv_kernel with the same template parameters, so every y[m]
+// equals a separate rz_q4k_q8_gemv call bit for bit.
+#include "q4k_gemv.h"
+#include "rz_launch.h"
+
+namespace rz {
+
+struct Q4KMultiArgs {
+  const uint8_t* xq;
+  int nsb;                          // super-blocks per row (all matrices)
+  int n_tokens;
+  int n_mats;
+  const uint8_t* w[kMaxMats];
+  float* y[kMaxMats];
+  int out_dim[kMaxMats];
+  uint32_t group0[kMaxMats + 1];    // first row group of each matrix; [n_mats] = total
+};
+
+template <int TPR, int S, int R, int NT, int G, int P>
+__global__ __launch_bounds__(256) void q4k_q8_gemv_multi_kernel(Q4KMultiArgs a) {
+  constexpr int RW = 8 / TPR;
+  constexpr uint32_t kRowsPerGroup = (uint32_t)RW * R;
+  const uint32_t nwaves = gridDim.x * 4u;
+  const uint32_t wid = __builtin_amdgcn_readfirstlane(blockIdx.x * 4u + (threadIdx.x >> 6));
+  const LaneRole ro = make_role<TPR>();
+  const uint32_t row_bytes = (uint32_t)a.nsb * kQ4KBytes;
+
+  // group k of this wave: matrix m[k] (wave-uniform), first row rb[k]; groups
+  // past the end use matrix 0 at a row past its end (reads zeros, stores nothing)
+  int m[G];
+  uint32_t rb[G];
+#pragma unroll
+  for (int k = 0; k < G; ++k) {
+    const uint32_t gidx = wid + (uint32_t)k * nwaves;
+    int mm = 0;
+    uint32_t first = 0;
+#pragma unroll
+    for (int j = 1; j < kMaxMats; ++j) {
+      const bool in = j < a.n_mats && gidx >= a.group0[j];
+      mm = in ? j : mm;
+      first = in ? a.group0[j] : first;
+    }
+    uint32_t total = a.group0[0];
+#pragma unroll
+    for (int j = 1; j <= kMaxMats; ++j) total = j == a.n_mats ? a.group0[j] : total;
+    const bool past = gidx >= total;
+    m[k] = past ? 0 : mm;
+    rb[k] = past ? (uint32_t)a.out_dim[0] : (gidx - first) * kRowsPerGroup;
+  }
+  // the matrix's fields by select chains (a dynamic index into the kernel
+  // argument block would go through scratch memory)
+  auto w_of = [&](int mm) {
+    const uint8_t* p = a.w[0];
+#pragma unroll
+    for (int j = 1; j < kMaxMats; ++j) p = mm == j ? a.w[j] : p;
+    return p;
+  };
+  auto y_of = [&](int mm) {
+    float* p = a.y[0];
+#pragma unroll
+    for (int j = 1; j < kMaxMats; ++j) p = mm == j ? a.y[j] : p;
+    return p;
+  };
+  auto rows_of = [&](int mm) {
+    int r = a.out_dim[0];
+#pragma unroll
+    for (int j = 1; j < kMaxMats; ++j) r = mm == j ? a.out_dim[j] : r;
+    return r;
+  };
+  auto src_of = [&](int k) {
+    return make_wsrc(w_of(m[k]), row_bytes, (uint32_t)rows_of(m[k]) * row_bytes);
+  };
+  const LaneOffsets<TPR, S> off = lane_offsets<TPR, S>(src_of(0), 0, ro);
+
+  XSlots<S, NT> xs;
+  load_x_slots<TPR, S, NT>(xs, a.xq, (size_t)a.nsb * 8 * kQ8Bytes, a.nsb, a.n_tokens, ro);
+  WTile<S, R> t[G];
+#pragma unroll
+  for (int k = 0; k < P && k < G; ++k) load_w_tile<TPR, S, R>(t[k], src_of(k), off, rb[k]);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int k = 0; k < G; ++k) {
+    if (k + P < G) load_w_tile<TPR, S, R>(t[k + P], src_of(k + P), off, rb[k + P]);
+    __builtin_amdgcn_sched_barrier(0);
+    float acc[R][NT];
+    q4k_tile_dot<TPR, S, R, NT>(acc, t[k], xs, ro);
+    Q4KGemvArgs ga;
+    ga.w = w_of(m[k]);
+    ga.xq = a.xq;
+    ga.y = y_of(m[k]);
+    ga.out_dim = rows_of(m[k]);
+    ga.nsb_row = a.nsb;
+    ga.sb0 = 0;
+    ga.nsb = a.nsb;
+    ga.n_tokens = a.n_tokens;
+    store_rows<TPR, R, NT, false>(ga, acc, (long)rb[k], ro);
+  }
+}
+
+template <int TPR, int S, int NT, int G>
+static hipError_t launch_multi_g(const Q4KMultiArgs& a, hipStream_t st) {
+  constexpr int R = (S <= 2 && NT <= 2) ? 2 : 1;
+  constexpr int P = G > 2 ? 2 : (G > 1 ? G - 1 : 1);
+  const long waves = ((long)a.group0[a.n_mats] + G - 1) / G;
+  const unsigned grid = (unsigned)((waves + 3) / 4);
+  hipLaunchKernelGGL((q4k_q8_gemv_multi_kernel<TPR, S, R, NT, G, P>), dim3(grid), dim3(256), 0,
+                     st, a);
+  return hipGetLastError();
+}
+
+// Groups per wave: the largest power of two (at most 8) that still leaves
+// about one wave per SIMD (1024).
+template <int TPR, int S, int NT>
+static hipError_t run_multi(Q4KMultiArgs a, hipStream_t st) {
+  constexpr int R = (S <= 2 && NT <= 2) ? 2 : 1;
+  constexpr uint32_t rows_per_group = (uint32_t)(8 / TPR) * R;
+  a.group0[0] = 0;
+  for (int j = 0; j < kMaxMats; ++j)
+    a.group0[j + 1] = a.group0[j] + (j < a.n_mats ? ((uint32_t)a.out_dim[j] + rows_per_group - 1) /
+                                                       rows_per_group
+                                                 : 0u);
+  const long groups = a.group0[a.n_mats];
+  if (groups >= 8 * 1024) return launch_multi_g<TPR, S, NT, 8>(a, st);
+  if (groups >= 4 * 1024) return launch_multi_g<TPR, S, NT, 4>(a, st);
+  if (groups >= 2 * 1024) return launch_multi_g<TPR, S, NT, 2>(a, st);
+  return launch_multi_g<TPR, S, NT, 1>(a, st);
+}
+
+template <int NT>
+static hipError_t run_multi_nt(const Q4KMultiArgs& a, hipStream_t st) {
+  const int nsb = a.nsb;
+  if (nsb == 1) return run_multi<1, 1, NT>(a, st);
+  if (nsb == 2) return run_multi<2, 1, NT>(a, st);
+  if (nsb <= 4) return run_multi<4, 1, NT>(a, st);
+  switch ((nsb + 7) / 8) {
+    case 1: return run_multi<8, 1, NT>(a, st);
+    case 2: return run_multi<8, 2, NT>(a, st);
+    case 3: return run_multi<8, 3, NT>(a, st);
+    case 4: return run_multi<8, 4, NT>(a, st);
+    case 5: return run_multi<8, 5, NT>(a, st);
+    case 6: return run_multi<8, 6, NT>(a, st);
+    case 7: return run_multi<8, 7, NT>(a, st);
+    case 8: return run_multi<8, 8, NT>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_q4k_q8_gemv_multi(int n_mats, const uint8_t* const* w, float* const* y,
+                                    const int* out_dims, const uint8_t* xq, int in_dim,
+                                    int n_tokens, hipStream_t stream) {
+  // one launch while the activation fits the register window of one or two
+  // tokens (the single-matrix path takes the same route); otherwise one call
+  // per matrix
+  if (n_tokens > 2 || in_dim > kMultiMaxInDim) {
+    for (int j = 0; j < n_mats; ++j) {
+      const hipError_t e = launch_q4k_q8_gemv(w[j], xq, y[j], out_dims[j], in_dim, n_tokens, stream);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  Q4KMultiArgs a;
+  a.xq = xq;
+  a.nsb = in_dim / kQKK;
+  a.n_tokens = n_tokens;
+  a.n_mats = n_mats;
+  for (int j = 0; j < kMaxMats; ++j) {
+    a.w[j] = j < n_mats ? w[j] : w[0];
+    a.y[j] = j < n_mats ? y[j] : y[0];
+    a.out_dim[j] = j < n_mats ? out_dims[j] : out_dims[0];
+  }
+  return n_tokens == 1 ? run_multi_nt<1>(a, stream) : run_multi_nt<2>(a, stream);
+}
+
+}  // namespace rz

@@ -87,6 +87,38 @@ int rz_q4k_q8_gemv(const void* w_q4k, const void* x_q8, float* y, int out_dim, i
                        what);
 }
 
+int rz_q4k_q8_gemv_multi(int n_mats, const void* const* w_q4k, float* const* y,
+                         const int* out_dims, const void* x_q8, int in_dim, int n_tokens,
+                         void* stream) {
+  const char* what = "rz_q4k_q8_gemv_multi";
+  if (!w_q4k || !y || !out_dims || !x_q8) return fail(RZ_EINVAL, "%s: null pointer", what);
+  if (n_mats < 1 || n_mats > RZ_MAX_MATS)
+    return fail(RZ_EINVAL, "%s: n_mats=%d outside 1..%d", what, n_mats, RZ_MAX_MATS);
+  if (n_tokens < 1 || n_tokens > RZ_MAX_TOKENS)
+    return fail(RZ_EINVAL, "%s: n_tokens=%d outside 1..%d", what, n_tokens, RZ_MAX_TOKENS);
+  if (int rc = check_dim(what, "in_dim", in_dim, 256)) return rc;
+  if (!aligned(x_q8, 8)) return fail(RZ_EALIGN, "%s: x_q8 must be 8-byte aligned", what);
+  const uint8_t* w[RZ_MAX_MATS];
+  float* yy[RZ_MAX_MATS];
+  int od[RZ_MAX_MATS];
+  for (int m = 0; m < n_mats; ++m) {
+    if (!w_q4k[m] || !y[m]) return fail(RZ_EINVAL, "%s: null pointer in matrix %d", what, m);
+    if (int rc = check_dim(what, "out_dims[m]", out_dims[m], 1)) return rc;
+    if ((long long)out_dims[m] * (in_dim / 256) * RZ_Q4K_BLOCK_BYTES > kMaxMatrixBytes)
+      return fail(RZ_EDIM, "%s: matrix %d larger than %lld bytes", what, m, kMaxMatrixBytes);
+    if (!aligned(w_q4k[m], 16))
+      return fail(RZ_EALIGN, "%s: w_q4k[%d] must be 16-byte aligned", what, m);
+    if (!aligned(y[m], 4)) return fail(RZ_EALIGN, "%s: y[%d] must be 4-byte aligned", what, m);
+    w[m] = static_cast<const uint8_t*>(w_q4k[m]);
+    yy[m] = y[m];
+    od[m] = out_dims[m];
+  }
+  return launch_status(rz::launch_q4k_q8_gemv_multi(n_mats, w, yy, od,
+                                                     static_cast<const uint8_t*>(x_q8), in_dim,
+                                                     n_tokens, static_cast<hipStream_t>(stream)),
+                       what);
+}
+
 int rz_q4k_q8_gemv_f32(const void* w_q4k, const float* x, int n, void* x_q8, float* y,
                        int out_dim, int in_dim, void* stream) {
   const char* what = "rz_q4k_q8_gemv_f32";

@@ -20,6 +20,14 @@ hipError_t launch_q4k_q8_gemm_mfma(const uint8_t* w, const uint8_t* xq, float* y
                                    int in_dim, int n_tokens, hipStream_t stream);
 constexpr int kMfmaMinTokens = 3;
 
+// Several Q4_K matrices (at most kMaxMats) times one Q8_1 activation; one
+// launch for 1..2 tokens and in_dim <= kMultiMaxInDim, else one call per matrix.
+constexpr int kMaxMats = 8;
+constexpr int kMultiMaxInDim = 16384;
+hipError_t launch_q4k_q8_gemv_multi(int n_mats, const uint8_t* const* w, float* const* y,
+                                    const int* out_dims, const uint8_t* xq, int in_dim,
+                                    int n_tokens, hipStream_t stream);
+
 // Q8_1 quantize of an fp32 activation fused into the Q4_K GEMV (1 token).
 hipError_t launch_q4k_q8_gemv_f32(const uint8_t* w, const float* x, int n, uint8_t* xq_out,
                                   float* y, int out_dim, int in_dim, hipStream_t stream);

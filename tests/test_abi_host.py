@@ -39,7 +39,8 @@ def lib():
 def test_header_declares_the_four_operations():
     syms = declared_symbols()
     for name in ("rz_q8_1_quantize", "rz_q4k_q8_gemv", "rz_q4k_q8_gemv_f32", "rz_q4_0_gemv",
-                 "rz_swiglu_ffn_q4k", "rz_last_error", "rz_abi_version"):
+                 "rz_swiglu_ffn_q4k", "rz_q4k_q8_gemv_multi", "rz_last_error",
+                 "rz_abi_version"):
         assert name in syms
 
 
@@ -59,8 +60,16 @@ sys.path.insert(0, sys.argv[1])
 import q4_q8_integer_quantize_amd as rz
 lib = rz.load_library()
 out = []
+import ctypes
+def conv(a):
+    # {"p": [...]} -> a host array of pointers, {"i": [...]} -> a host int array
+    if isinstance(a, dict) and "p" in a:
+        return (ctypes.c_void_p * max(1, len(a["p"])))(*a["p"])
+    if isinstance(a, dict) and "i" in a:
+        return (ctypes.c_int * max(1, len(a["i"])))(*a["i"])
+    return a
 for fn, args in json.loads(sys.stdin.read()):
-    rc = getattr(lib, fn)(*args)
+    rc = getattr(lib, fn)(*[conv(a) for a in args])
     out.append([rc, rz.rz_last_error()])
 print(json.dumps(out))
 """
@@ -116,6 +125,29 @@ def test_q8_1_quantize_rejects(lib, args, code):
 def test_q4k_q8_gemv_rejects(lib, args, code):
     assert _rc("rz_q4k_q8_gemv", *args) == code
     assert "rz_q4k_q8_gemv" in _rc.last
+
+
+def _m(ws, ys, ods):
+    return {"p": ws}, {"p": ys}, {"i": ods}
+
+
+@pytest.mark.parametrize("args,code", [
+    ((3,) + _m([P, P, P], [P, P, P], [4096, 1024, 1024]) + (P, 4096, 9, None), rz.RZ_EINVAL),
+    ((0,) + _m([P], [P], [4096]) + (P, 4096, 1, None), rz.RZ_EINVAL),          # n_mats 0
+    ((9,) + _m([P] * 9, [P] * 9, [16] * 9) + (P, 4096, 1, None), rz.RZ_EINVAL),  # n_mats 9
+    ((2,) + _m([P, 0], [P, P], [16, 16]) + (P, 4096, 1, None), rz.RZ_EINVAL),  # null entry
+    ((2,) + _m([P, P], [P, 0], [16, 16]) + (P, 4096, 1, None), rz.RZ_EINVAL),
+    ((2,) + _m([P, P], [P, P], [16, 16]) + (None, 4096, 1, None), rz.RZ_EINVAL),
+    ((2,) + _m([P, P], [P, P], [16, 0]) + (P, 4096, 1, None), rz.RZ_EDIM),     # empty matrix
+    ((2,) + _m([P, P], [P, P], [16, 16]) + (P, 4000, 1, None), rz.RZ_EDIM),
+    ((2,) + _m([P, P + 8], [P, P], [16, 16]) + (P, 4096, 1, None), rz.RZ_EALIGN),
+    ((2,) + _m([P, P], [P, P_ODD], [16, 16]) + (P, 4096, 1, None), rz.RZ_EALIGN),
+    ((2,) + _m([P, P], [P, P], [16, 16]) + (P + 4, 4096, 1, None), rz.RZ_EALIGN),
+    ((1,) + _m([P], [P], [1 << 20]) + (P, 1 << 14, 1, None), rz.RZ_EDIM),      # > 2 GiB
+])
+def test_q4k_q8_gemv_multi_rejects(lib, args, code):
+    assert _rc("rz_q4k_q8_gemv_multi", *args) == code
+    assert _rc.last.startswith("rz_q4k_q8_gemv_multi")
 
 
 @pytest.mark.parametrize("args,code", [

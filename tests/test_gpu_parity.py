@@ -349,6 +349,55 @@ def test_q4k_attention_projections_full():
         assert_within(y, y_ref, terms, "attention " + name)
 
 
+def test_q4k_multi_attention_one_launch():
+    """The four attention projections in one rz_q4k_q8_gemv_multi launch: each
+    output equals its own rz_q4k_q8_gemv call bit for bit and the oracle within
+    the GEMV bound."""
+    w = synth.WORKLOADS["attn_4096"]
+    x = synth.rmsnorm_activation(synth.rng(1, synth.T_ACT), synth.rng(1, synth.T_GAMMA), w["n"])
+    xq = oracle.quantize_q8_1(x, w["in_dim"])
+    xb = dev_bytes(oracle.q8_1_to_bytes(xq))
+    blobs = [synth.q4k_weights(synth.rng(1, synth.T_W0 + k), rows, w["in_dim"])
+             for k, (_, rows) in enumerate(w["shapes"])]
+    dws = [dev_bytes(b) for b in blobs]
+    ys = [empty_f32(rows) for _, rows in w["shapes"]]
+    banner("multi attention", len(ys))
+    rz.rz_q4k_q8_gemv_multi(dws, xb, ys, [rows for _, rows in w["shapes"]], w["in_dim"])
+    for k, (name, rows) in enumerate(w["shapes"]):
+        single = empty_f32(rows)
+        rz.rz_q4k_q8_gemv(dws[k], xb, single, rows, w["in_dim"], 1)
+        assert np.array_equal(host(ys[k]), host(single)), name
+        y_ref, terms = oracle.gemv_q4k_q8_int(blobs[k], xq)
+        assert_within(host(ys[k]), y_ref, terms, "multi " + name)
+
+
+@pytest.mark.parametrize("n_tokens,out_dims,in_dim", [
+    (1, [1, 65, 257], 512), (2, [3, 64], 1024), (1, [896, 100, 7, 33, 1, 2, 3, 129], 1280),
+    (5, [33, 64], 4096), (2, [17, 40], 20480),
+])
+def test_q4k_multi_matches_single_calls(n_tokens, out_dims, in_dim):
+    """Ragged matrices, up to 8 of them, one and two tokens in one launch, and
+    the per-matrix fallbacks (more tokens, longer rows): every output equals
+    its own single-matrix call bit for bit; the first matrix is also checked
+    against the oracle."""
+    banner("multi", n_tokens, out_dims, in_dim)
+    blobs = [synth.q4k_weights(synth.rng(70, 10 * k + o), o, in_dim) for k, o in enumerate(out_dims)]
+    X = synth.activation(synth.rng(70, in_dim), in_dim, n_tokens=n_tokens)
+    xq = oracle.quantize_q8_1(X)
+    xb = dev_bytes(oracle.q8_1_to_bytes(xq))
+    dws = [dev_bytes(b) for b in blobs]
+    ys = [empty_f32(o * n_tokens) for o in out_dims]
+    rz.rz_q4k_q8_gemv_multi(dws, xb, ys, out_dims, in_dim, n_tokens)
+    for k, o in enumerate(out_dims):
+        single = empty_f32(o * n_tokens)
+        rz.rz_q4k_q8_gemv(dws[k], xb, single, o, in_dim, n_tokens)
+        assert np.array_equal(host(ys[k]), host(single)), "matrix %d" % k
+    y_ref, terms = oracle_q4k(blobs[0], xq, n_tokens)
+    Y = host(ys[0]).reshape(n_tokens, out_dims[0])
+    for t in range(n_tokens):
+        assert_within(Y[t], y_ref[t], terms[t], "multi token %d" % t)
+
+
 def test_q4k_gate_4096_to_14336_full():
     """The measured GEMV (4096 -> 14336, one token) in the launch configuration
     the benchmark times: GPU quantize then GPU GEMV, every output checked."""
