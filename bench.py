@@ -251,6 +251,53 @@ def time_rows(lib, rz, torch, dev, graph_time, copies, x, xq, y) -> dict:
     return rows
 
 
+ONLY = {
+    "step": "rz_q4k_q8_gemv_f32 4096 -> 14336",
+    "gemv": "rz_q4k_q8_gemv 4096 -> 14336, 1 token",
+    "batch8": "rz_q4k_q8_gemv 4096 -> 14336, 8 tokens",
+    "lm_head_fp32": "rz_q4_0_gemv 151936 x 1024, fp32 x",
+    "lm_head_q8": "rz_q4_0_gemv 151936 x 1024, Q8_1 x",
+}
+
+
+def run_only(name: str, launches: int) -> int:
+    """Run one kernel `launches` times over 4 weight copies, untimed."""
+    import numpy as np
+    import torch
+    import synth
+    import q4_q8_integer_quantize_amd as rz
+    dev = torch.device("cuda:0")
+    if name.startswith("lm_head"):
+        V, H = 151936, 1024
+        blob = synth.q4_0_weights(synth.rng(3, 1), V, H)
+        x = np.zeros(H, np.float32)
+        x[:896] = synth.activation(synth.rng(3, synth.T_ACT), 896)
+        xd = torch.from_numpy(x).to(dev)
+        xq = torch.empty((H // 32) * 40, dtype=torch.uint8, device=dev)
+        rz.rz_q8_1_quantize(xd, 896, H, 1, xq)
+        y = torch.empty(V, dtype=torch.float32, device=dev)
+        ws = [torch.from_numpy(blob.reshape(-1).copy()).to(dev) for _ in range(4)]
+        fmt = 0 if name == "lm_head_fp32" else 1
+        for i in range(launches):
+            rz.rz_q4_0_gemv(ws[i % 4], xd if fmt == 0 else xq, fmt, y, V, H)
+    else:
+        nt = 8 if name == "batch8" else 1
+        blob = synth.q4k_weights(synth.rng(2, synth.T_W0), OUT_DIM, IN_DIM)
+        ws = [torch.from_numpy(blob.reshape(-1).copy()).to(dev) for _ in range(4)]
+        x = torch.from_numpy(synth.activation(synth.rng(4, synth.T_ACT), IN_DIM, nt)).to(dev)
+        xq = torch.empty(nt * XQ_BYTES, dtype=torch.uint8, device=dev)
+        rz.rz_q8_1_quantize(x, IN_DIM, IN_DIM, nt, xq)
+        y = torch.empty(nt * OUT_DIM, dtype=torch.float32, device=dev)
+        for i in range(launches):
+            if name == "step":
+                rz.rz_q4k_q8_gemv_f32(ws[i % 4], x, IN_DIM, None, y, OUT_DIM, IN_DIM)
+            else:
+                rz.rz_q4k_q8_gemv(ws[i % 4], xq, y, OUT_DIM, IN_DIM, nt)
+    torch.cuda.synchronize()
+    print("ran %s x %d" % (ONLY[name], launches), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -258,6 +305,10 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--only", choices=sorted(ONLY), default=None,
+                    help="run one kernel of the path --launches times, untimed (for counter "
+                         "collection under rocprofv3), then exit")
+    ap.add_argument("--launches", type=int, default=12)
     ap.add_argument("--no-rows", action="store_true",
                     help="time only the step, not the other kernels of the path")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -269,6 +320,9 @@ def main() -> int:
               "(rows shard without communication; see the design notes)" % args.gpus,
               file=sys.stderr)
         return 2
+
+    if args.only:
+        return run_only(args.only, args.launches)
 
     import numpy as np
     import torch
