@@ -15,6 +15,9 @@ source pages (docs.rs, realizar 0.8.4/0.8.5):
   the gate output, then multiplied elementwise by the up output.
 * ``src/cuda/executor/layers/forward_utils.rs``, ``pad_and_upload_input``: the
   activation is zero-padded to a multiple of the 256-value super-block.
+* ``src/gpu/adapters/using.rs``, ``rms_norm_inplace``, and ``cached.rs`` steps 1, 7,
+  8 and 10: the RMSNorm before the quantize and the residual adds after the O
+  projection and the FFN.
 
 The block formats are not printed on the pages; the GGML layouts the pages name
 (Q4_K super-blocks of 256 values, type id 12; Q4_0; Q8_1) are read as written in
@@ -35,6 +38,7 @@ from .q4_0 import (q4_0_fields, dequantize_q4_0, gemv_q4_0_f32,
                    gemv_q4_0_q8_int)
 from .swiglu import silu, silu_grad, swiglu, ffn_swiglu_q4k, h_tolerance
 from .tolerance import gemv_tolerance, GEMV_REL, GEMV_ABS
+from .norm import rmsnorm, rmsnorm_tolerance, residual_add
 
 __all__ = [
     "QK8_1", "Q8_1_BLOCK_BYTES", "quantize_q8_1", "q8_1_to_bytes", "q8_1_from_bytes",
@@ -44,4 +48,5 @@ __all__ = [
     "q4_0_fields", "dequantize_q4_0", "gemv_q4_0_f32", "gemv_q4_0_q8_int",
     "silu", "silu_grad", "swiglu", "ffn_swiglu_q4k", "h_tolerance",
     "gemv_tolerance", "GEMV_REL", "GEMV_ABS",
+    "rmsnorm", "rmsnorm_tolerance", "residual_add",
 ]

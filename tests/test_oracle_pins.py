@@ -379,3 +379,71 @@ def test_h_tolerance_covers_perturbations():
     for sg, su in ((1, 1), (1, -1), (-1, 1), (-1, -1)):
         hp = oracle.swiglu(g + sg * tg, u + su * tu)
         assert np.all(np.abs(hp - h) <= tol)
+
+
+# ------------------------------------------------------------------ RMSNorm, residual
+# using.rs rms_norm_inplace: RMS = sqrt(mean(x^2) + eps); x * (1 / RMS) * weight.
+
+def test_rmsnorm_hand_worked():
+    # [3, 4]: mean of squares 12.5 (a sum of 25 would give [0.6, 0.8]; no root, [0.24, 0.32])
+    y = oracle.rmsnorm(np.array([3.0, 4.0]), np.ones(2), 0.0)
+    assert np.allclose(y, [3 / np.sqrt(12.5), 4 / np.sqrt(12.5)], rtol=0, atol=1e-15)
+    assert abs(y[0] - 0.848528137423857) < 1e-14 and abs(y[1] - 1.131370849898476) < 1e-14
+
+
+def test_rmsnorm_eps_inside_the_root():
+    # mean 1, eps 3: RMS = sqrt(4) = 2 (eps added after the root would give 4)
+    assert np.array_equal(oracle.rmsnorm(np.ones(4), np.ones(4), 3.0), np.full(4, 0.5))
+    # all-zero input: the eps keeps it finite, and the output is zero
+    assert np.array_equal(oracle.rmsnorm(np.zeros(8), np.ones(8), 1e-5), np.zeros(8))
+
+
+def test_rmsnorm_weight_is_per_element():
+    assert np.array_equal(oracle.rmsnorm(np.array([2.0, 2.0]), np.array([1.0, 3.0]), 0.0),
+                          np.array([1.0, 3.0]))
+    g = np.random.default_rng(5)
+    x, w = g.normal(size=64), g.normal(1, 0.1, 64)
+    assert np.array_equal(oracle.rmsnorm(x, 2 * w, 1e-5), 2 * oracle.rmsnorm(x, w, 1e-5))
+
+
+def test_rmsnorm_unit_rms_and_scale_invariance():
+    g = np.random.default_rng(6)
+    x = g.normal(size=4096)
+    y = oracle.rmsnorm(x, np.ones(4096), 0.0)
+    assert abs(np.mean(y * y) - 1.0) < 1e-12
+    for k in (0.25, 8.0, 2.0 ** -20):   # powers of two: exact with eps = 0
+        assert np.array_equal(oracle.rmsnorm(k * x, np.ones(4096), 0.0), y)
+
+
+def test_rmsnorm_rows_are_independent():
+    g = np.random.default_rng(7)
+    X = g.normal(size=(3, 96)) * np.array([[1.0], [100.0], [1e-3]])
+    w = g.normal(1, 0.1, 96)
+    Y = oracle.rmsnorm(X, w, 1e-5)
+    for t in range(3):
+        assert np.array_equal(Y[t], oracle.rmsnorm(X[t], w, 1e-5))
+
+
+@pytest.mark.parametrize("n", [32, 896, 4096, 16384])
+def test_rmsnorm_tolerance_covers_fp32_evaluations(n):
+    """fp32 evaluations of the same formula -- a sequential sum as the pages
+    write it, and numpy's blocked pairwise sum -- stay within the bound for
+    their summation chains."""
+    g = np.random.default_rng(n)
+    x = g.normal(size=n).astype(np.float32)
+    w = g.normal(1, 0.1, n).astype(np.float32)
+    ref = oracle.rmsnorm(x, w, 1e-5)
+    f = np.float32
+    seq = f(0)
+    for v in x:
+        seq = f(seq + f(v * v))
+    pair = np.sum(x * x, dtype=np.float32)
+    for ss, chain in ((seq, n), (pair, 128 + int(np.ceil(np.log2(max(n / 128, 1)))) + 1)):
+        scale = f(f(1) / f(np.sqrt(f(f(ss / f(n)) + f(1e-5)))))
+        y32 = (x * scale) * w
+        assert np.all(np.abs(y32.astype(np.float64) - ref) <= oracle.rmsnorm_tolerance(ref, chain))
+
+
+def test_residual_add():
+    r = np.array([1.0, -2.0, 0.5])
+    assert np.array_equal(oracle.residual_add(r, np.array([0.25, 2.0, -0.5])), [1.25, 0.0, 0.0])
