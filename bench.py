@@ -142,6 +142,14 @@ def time_rows(lib, rz, torch, dev, graph_time, copies, x, xq, y) -> dict:
         X_BYTES + XQ_BYTES, 0, "rz_q8_1_quantize")
     check(lib.rz_q8_1_quantize(x_p, IN_DIM, IN_DIM, 1, xq_p, torch.cuda.current_stream().cuda_stream))
 
+    # RMSNorm fused with the Q8_1 quantize (the attention and FFN inputs)
+    gam = torch.from_numpy(synth.norm_weights(synth.rng(1, synth.T_GAMMA), IN_DIM)).to(dev)
+    xq_n = torch.empty(XQ_BYTES, dtype=torch.uint8, device=dev)
+    rows["rmsnorm_q8_1_4096"] = row_entry(
+        graph_time(lambda i, s: check(lib.rz_rmsnorm_q8_1(x_p, gam.data_ptr(), 1e-5, IN_DIM,
+                                                          IN_DIM, 1, None, xq_n.data_ptr(), s))),
+        2 * X_BYTES + XQ_BYTES, 0, "rz_rmsnorm_q8_1")
+
     # a2+a3: the GEMV alone over the shared Q8_1 activation
     rows["q4k_gemv_4096x14336"] = row_entry(
         graph_time(lambda i, s: check(lib.rz_q4k_q8_gemv(w_p[i % n_copies], xq_p, y_p, OUT_DIM,
@@ -187,6 +195,19 @@ def time_rows(lib, rz, torch, dev, graph_time, copies, x, xq, y) -> dict:
     rows["attn_qkvo_4096_separate"] = row_entry(
         graph_time(attn_body), attn_w + 4 * XQ_BYTES + 4 * (4096 + 1024 + 1024 + 4096), attn_w,
         "4 x rz_q4k_q8_gemv (Q, K, V, O) on one Q8_1 activation")
+
+    # the O projection alone, and with the residual add in its store (in place)
+    o_w = q4k_bytes(4096, 4096)
+    hid = torch.zeros(4096, dtype=torch.float32, device=dev)
+    rows["o_proj_4096"] = row_entry(
+        graph_time(lambda i, s: check(lib.rz_q4k_q8_gemv(attn_p[i % len(attn_p)][3], xq_p,
+                                                         ya.data_ptr(), 4096, 4096, 1, s))),
+        o_w + XQ_BYTES + 4 * 4096, o_w, "rz_q4k_q8_gemv")
+    rows["o_proj_add_4096"] = row_entry(
+        graph_time(lambda i, s: check(lib.rz_q4k_q8_gemv_add(attn_p[i % len(attn_p)][3], xq_p,
+                                                             hid.data_ptr(), hid.data_ptr(),
+                                                             4096, 4096, 1, s))),
+        o_w + XQ_BYTES + 8 * 4096, o_w, "rz_q4k_q8_gemv_add (hidden += O x, in place)")
     del attn
 
     # SwiGLU chain 4096 -> 14336 -> 4096, and its down projection alone
@@ -209,6 +230,18 @@ def time_rows(lib, rz, torch, dev, graph_time, copies, x, xq, y) -> dict:
         graph_time(ffn_body),
         ffn_w + XQ_BYTES + 4 * INTER + 2 * q8_bytes(INTER) + 4 * IN_DIM, ffn_w,
         "rz_swiglu_ffn_q4k (gate/up + silu*up + requantize, then down)")
+    hid_f = torch.zeros(IN_DIM, dtype=torch.float32, device=dev)
+
+    def ffn_add_body(i, s):
+        wg, wu, wd = ffn_p[i % len(ffn_p)]
+        check(lib.rz_swiglu_ffn_q4k_add(wg, wu, wd, xq_p, h.data_ptr(), hq.data_ptr(),
+                                        hid_f.data_ptr(), hid_f.data_ptr(), None, IN_DIM, INTER,
+                                        s))
+
+    rows["swiglu_ffn_add_4096_14336"] = row_entry(
+        graph_time(ffn_add_body),
+        ffn_w + XQ_BYTES + 4 * INTER + 2 * q8_bytes(INTER) + 8 * IN_DIM, ffn_w,
+        "rz_swiglu_ffn_q4k_add (the chain, then hidden += y in the down store)")
     rows["q4k_gemv_down_14336x4096"] = row_entry(
         graph_time(lambda i, s: check(lib.rz_q4k_q8_gemv(ffn_p[i % len(ffn_p)][2], hq.data_ptr(),
                                                          yf.data_ptr(), IN_DIM, INTER, 1, s))),
@@ -257,6 +290,7 @@ ONLY = {
     "batch8": "rz_q4k_q8_gemv 4096 -> 14336, 8 tokens",
     "lm_head_fp32": "rz_q4_0_gemv 151936 x 1024, fp32 x",
     "lm_head_q8": "rz_q4_0_gemv 151936 x 1024, Q8_1 x",
+    "rmsnorm": "rz_rmsnorm_q8_1 4096, 1 token",
 }
 
 
@@ -267,7 +301,13 @@ def run_only(name: str, launches: int) -> int:
     import synth
     import q4_q8_integer_quantize_amd as rz
     dev = torch.device("cuda:0")
-    if name.startswith("lm_head"):
+    if name == "rmsnorm":
+        x = torch.from_numpy(synth.activation(synth.rng(1, synth.T_ACT), IN_DIM)).to(dev)
+        gam = torch.from_numpy(synth.norm_weights(synth.rng(1, synth.T_GAMMA), IN_DIM)).to(dev)
+        xq = torch.empty(XQ_BYTES, dtype=torch.uint8, device=dev)
+        for i in range(launches):
+            rz.rz_rmsnorm_q8_1(x, gam, 1e-5, IN_DIM, IN_DIM, 1, None, xq)
+    elif name.startswith("lm_head"):
         V, H = 151936, 1024
         blob = synth.q4_0_weights(synth.rng(3, 1), V, H)
         x = np.zeros(H, np.float32)

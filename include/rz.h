@@ -69,6 +69,34 @@ extern "C" {
 int rz_q8_1_quantize(const float* x, int n, int n_padded, int n_tokens,
                      void* x_q8, void* stream);
 
+/* rz_rmsnorm_q8_1 -- RMSNorm of fp32 activations, quantized to Q8_1, in one
+ * launch.
+ * Passages: realizar 0.8.4 src/gpu/adapters/using.rs, rms_norm_inplace (the
+ * root of mean(x^2) + eps is the RMS; each value is multiplied by 1/RMS and
+ * by its weight); realizar 0.8.5 src/cuda/executor/cached.rs,
+ * transformer_layer_gpu_true_dp4a, steps 1-2 and 8 (the normed activation
+ * is quantized once for the projections that follow).
+ * Per token: ss = sum(x^2) in fp32, scale = 1 / sqrt(ss / n + eps) (IEEE
+ * division and square root), v = (x * scale) * gamma; the Q8_1 blocks of v
+ * then follow the rule of rz_q8_1_quantize and equal
+ * rz_q8_1_quantize(v) byte for byte.  ss is summed in a fixed order (per
+ * thread over 4 of every 1024 values, then an 8-level tree; rows longer than
+ * 16384 values: 4 of every 4096, then 10 levels), so v differs from the exact
+ * value by rounding only, the same on every run.
+ *   x        fp32 [n_tokens][n], 4-byte aligned
+ *   gamma    fp32 [n] weights, 4-byte aligned
+ *   eps      > 0 and finite
+ *   n        1 <= n <= n_padded; n_padded multiple of 32 (values n..n_padded-1
+ *            are +0.0, as for rz_q8_1_quantize)
+ *   n_tokens 1..RZ_MAX_TOKENS
+ *   normed   optional out (NULL to skip): fp32 [n_tokens][n], the values v
+ *   x_q8     out: [n_tokens][n_padded/32] blocks, 8-byte aligned
+ * Inputs whose sum of squares overflows fp32 are outside the contract.
+ * Errors: RZ_EINVAL (null pointer, n_tokens or eps), RZ_EDIM, RZ_EALIGN,
+ * RZ_ELAUNCH. */
+int rz_rmsnorm_q8_1(const float* x, const float* gamma, float eps, int n, int n_padded,
+                    int n_tokens, float* normed, void* x_q8, void* stream);
+
 /* rz_q4k_q8_gemv -- y = W x with W Q4_K and x Q8_1, for 1..8 tokens.
  * Passage: realizar 0.8.5 src/cuda/executor/cached.rs,
  * transformer_layer_gpu_true_dp4a, steps 3 and 6 (Q4K x Q8 integer dot
@@ -84,6 +112,23 @@ int rz_q8_1_quantize(const float* x, int n, int n_padded, int n_tokens,
  * Errors: RZ_EINVAL, RZ_EDIM, RZ_EALIGN, RZ_ELAUNCH. */
 int rz_q4k_q8_gemv(const void* w_q4k, const void* x_q8, float* y,
                    int out_dim, int in_dim, int n_tokens, void* stream);
+
+/* rz_q4k_q8_gemv_add -- y = W x + r: the GEMV with the residual add in its
+ * store.
+ * Passage: realizar 0.8.5 src/cuda/executor/cached.rs,
+ * transformer_layer_gpu_true_dp4a, steps 6-7 and 10 (the output projection
+ * and the FFN output are each added to the layer's running hidden state).
+ * Same operation as rz_q4k_q8_gemv, plus r.  When one pass covers the row
+ * (in_dim <= 16384 for 1-2 tokens, <= 4096 for 3-8 tokens) y is
+ * fl32(rz_q4k_q8_gemv result + r) bit for bit; longer rows run in column
+ * passes, and r is added to the first pass's partial sum.
+ *   r        fp32 [n_tokens][out_dim] (token-major, like y), 4-byte aligned;
+ *            may be y itself (in place) but must not overlap it otherwise
+ *   w_q4k, x_q8, y, out_dim, in_dim, n_tokens: as for rz_q4k_q8_gemv
+ * Errors: RZ_EINVAL (also a partial overlap of r and y), RZ_EDIM, RZ_EALIGN,
+ * RZ_ELAUNCH. */
+int rz_q4k_q8_gemv_add(const void* w_q4k, const void* x_q8, const float* r, float* y,
+                       int out_dim, int in_dim, int n_tokens, void* stream);
 
 /* rz_q4k_q8_gemv_multi -- several Q4_K matrices times one Q8_1 activation.
  * Passage: realizar 0.8.5 src/cuda/executor/cached.rs,
@@ -163,6 +208,19 @@ int rz_q4_0_gemv(const void* w_q4_0, const void* x, int x_format, float* y,
 int rz_swiglu_ffn_q4k(const void* w_gate, const void* w_up, const void* w_down,
                       const void* x_q8, float* h, void* h_q8, float* y,
                       float* gu, int hidden_dim, int inter_dim, void* stream);
+
+/* rz_swiglu_ffn_q4k_add -- the SwiGLU FFN with the residual add:
+ * y = W_down h_q8 + r.
+ * Passage: realizar 0.8.5 src/cuda/executor/cached.rs,
+ * transformer_layer_gpu_true_dp4a, steps 9-10 (the FFN output is added to
+ * the hidden state).  Everything as rz_swiglu_ffn_q4k; the down projection
+ * stores fl32(W_down h_q8 + r) as rz_q4k_q8_gemv_add does for one token.
+ *   r        fp32 [hidden_dim], 4-byte aligned; may be y itself but must not
+ *            overlap it otherwise, nor h, h_q8 or gu
+ * Errors: RZ_EINVAL (also overlaps), RZ_EDIM, RZ_EALIGN, RZ_ELAUNCH. */
+int rz_swiglu_ffn_q4k_add(const void* w_gate, const void* w_up, const void* w_down,
+                          const void* x_q8, float* h, void* h_q8, const float* r, float* y,
+                          float* gu, int hidden_dim, int inter_dim, void* stream);
 
 /* Message for the most recent non-zero return on the calling thread. */
 const char* rz_last_error(void);

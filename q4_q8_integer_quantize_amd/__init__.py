@@ -19,8 +19,9 @@ __all__ = [
     "RZ_OK", "RZ_EINVAL", "RZ_EDIM", "RZ_EALIGN", "RZ_ELAUNCH",
     "Q8_1_BLOCK_BYTES", "Q4K_BLOCK_BYTES", "Q4_0_BLOCK_BYTES", "MAX_TOKENS",
     "library_path", "load_library", "rz_last_error", "rz_abi_version",
-    "rz_q8_1_quantize", "rz_q4k_q8_gemv", "rz_q4k_q8_gemv_f32", "rz_q4_0_gemv",
-    "rz_swiglu_ffn_q4k",
+    "rz_q8_1_quantize", "rz_rmsnorm_q8_1", "rz_q4k_q8_gemv", "rz_q4k_q8_gemv_add",
+    "rz_q4k_q8_gemv_multi", "rz_q4k_q8_gemv_f32", "rz_q4_0_gemv", "rz_swiglu_ffn_q4k",
+    "rz_swiglu_ffn_q4k_add",
     "q8_1_nbytes", "RzError",
 ]
 
@@ -56,13 +57,17 @@ def load_library() -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     vp, i = ctypes.c_void_p, ctypes.c_int
     lib.rz_q8_1_quantize.argtypes = [vp, i, i, i, vp, vp]
+    lib.rz_rmsnorm_q8_1.argtypes = [vp, vp, ctypes.c_float, i, i, i, vp, vp, vp]
     lib.rz_q4k_q8_gemv.argtypes = [vp, vp, vp, i, i, i, vp]
+    lib.rz_q4k_q8_gemv_add.argtypes = [vp, vp, vp, vp, i, i, i, vp]
     lib.rz_q4k_q8_gemv_f32.argtypes = [vp, vp, i, vp, vp, i, i, vp]
     lib.rz_q4k_q8_gemv_multi.argtypes = [i, vp, vp, vp, vp, i, i, vp]
     lib.rz_q4_0_gemv.argtypes = [vp, vp, i, vp, i, i, vp]
     lib.rz_swiglu_ffn_q4k.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, vp]
-    for fn in ("rz_q8_1_quantize", "rz_q4k_q8_gemv", "rz_q4k_q8_gemv_f32", "rz_q4k_q8_gemv_multi",
-               "rz_q4_0_gemv", "rz_swiglu_ffn_q4k", "rz_abi_version"):
+    lib.rz_swiglu_ffn_q4k_add.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, vp]
+    for fn in ("rz_q8_1_quantize", "rz_rmsnorm_q8_1", "rz_q4k_q8_gemv", "rz_q4k_q8_gemv_add",
+               "rz_q4k_q8_gemv_f32", "rz_q4k_q8_gemv_multi", "rz_q4_0_gemv", "rz_swiglu_ffn_q4k",
+               "rz_swiglu_ffn_q4k_add", "rz_abi_version"):
         getattr(lib, fn).restype = i
     lib.rz_last_error.argtypes = []
     lib.rz_last_error.restype = ctypes.c_char_p
@@ -126,6 +131,19 @@ def rz_q8_1_quantize(x, n: int, n_padded: int, n_tokens: int, x_q8, stream=None)
                                            _stream(stream)))
 
 
+def rz_rmsnorm_q8_1(x, gamma, eps: float, n: int, n_padded: int, n_tokens: int, normed, x_q8,
+                    stream=None) -> None:
+    """RMSNorm of x fp32 [n_tokens, n] with weights gamma [n], quantized to
+    x_q8 uint8 [n_tokens * n_padded/32 * 40]; normed fp32 [n_tokens, n] is
+    written too unless None."""
+    _need(x, 4 * n * n_tokens, "x")
+    _need(gamma, 4 * n, "gamma")
+    _need(normed, 4 * n * n_tokens, "normed")
+    _need(x_q8, q8_1_nbytes(n_padded, n_tokens) if n_padded > 0 else 0, "x_q8")
+    _check(load_library().rz_rmsnorm_q8_1(_ptr(x), _ptr(gamma), float(eps), n, n_padded,
+                                          n_tokens, _ptr(normed), _ptr(x_q8), _stream(stream)))
+
+
 def rz_q4k_q8_gemv(w_q4k, x_q8, y, out_dim: int, in_dim: int, n_tokens: int = 1,
                    stream=None) -> None:
     """y fp32 [n_tokens, out_dim] = W (Q4_K [out_dim, in_dim/256, 144]) x (Q8_1)."""
@@ -135,6 +153,18 @@ def rz_q4k_q8_gemv(w_q4k, x_q8, y, out_dim: int, in_dim: int, n_tokens: int = 1,
         _need(y, 4 * out_dim * n_tokens, "y")
     _check(load_library().rz_q4k_q8_gemv(_ptr(w_q4k), _ptr(x_q8), _ptr(y), out_dim, in_dim,
                                          n_tokens, _stream(stream)))
+
+
+def rz_q4k_q8_gemv_add(w_q4k, x_q8, r, y, out_dim: int, in_dim: int, n_tokens: int = 1,
+                       stream=None) -> None:
+    """y fp32 [n_tokens, out_dim] = W (Q4_K) x (Q8_1) + r; r may be y itself."""
+    if in_dim > 0 and in_dim % 256 == 0 and out_dim > 0:
+        _need(w_q4k, out_dim * (in_dim // 256) * Q4K_BLOCK_BYTES, "w_q4k")
+        _need(x_q8, q8_1_nbytes(in_dim, n_tokens), "x_q8")
+        _need(r, 4 * out_dim * n_tokens, "r")
+        _need(y, 4 * out_dim * n_tokens, "y")
+    _check(load_library().rz_q4k_q8_gemv_add(_ptr(w_q4k), _ptr(x_q8), _ptr(r), _ptr(y), out_dim,
+                                             in_dim, n_tokens, _stream(stream)))
 
 
 def rz_q4k_q8_gemv_multi(ws, x_q8, ys, out_dims, in_dim: int, n_tokens: int = 1,
@@ -196,3 +226,22 @@ def rz_swiglu_ffn_q4k(w_gate, w_up, w_down, x_q8, h, h_q8, y, gu, hidden_dim: in
     _check(load_library().rz_swiglu_ffn_q4k(_ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(x_q8),
                                             _ptr(h), _ptr(h_q8), _ptr(y), _ptr(gu), hidden_dim,
                                             inter_dim, _stream(stream)))
+
+
+def rz_swiglu_ffn_q4k_add(w_gate, w_up, w_down, x_q8, h, h_q8, r, y, gu, hidden_dim: int,
+                          inter_dim: int, stream=None) -> None:
+    """rz_swiglu_ffn_q4k with the residual: y = W_down h_q8 + r (r may be y)."""
+    if hidden_dim > 0 and inter_dim > 0 and hidden_dim % 256 == 0 and inter_dim % 256 == 0:
+        nw = inter_dim * (hidden_dim // 256) * Q4K_BLOCK_BYTES
+        _need(w_gate, nw, "w_gate")
+        _need(w_up, nw, "w_up")
+        _need(w_down, nw, "w_down")
+        _need(x_q8, q8_1_nbytes(hidden_dim), "x_q8")
+        _need(h, 4 * inter_dim, "h")
+        _need(h_q8, q8_1_nbytes(inter_dim), "h_q8")
+        _need(r, 4 * hidden_dim, "r")
+        _need(y, 4 * hidden_dim, "y")
+        _need(gu, 8 * inter_dim, "gu")
+    _check(load_library().rz_swiglu_ffn_q4k_add(_ptr(w_gate), _ptr(w_up), _ptr(w_down),
+                                                _ptr(x_q8), _ptr(h), _ptr(h_q8), _ptr(r), _ptr(y),
+                                                _ptr(gu), hidden_dim, inter_dim, _stream(stream)))

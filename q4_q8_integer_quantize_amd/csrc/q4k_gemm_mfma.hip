@@ -206,16 +206,19 @@ __global__ __launch_bounds__(256) void q4k_q8_gemm_mfma_kernel(Q4KGemvArgs a) {
       y1 += q.y;
     }
   }
+  // a storing chunk adds the residual (if any): y = fl(partial + r)
   const uint32_t row = rb * kMfmaRows + n;
   if (row < (uint32_t)a.out_dim) {
     const uint32_t t0 = 2u * g, t1 = 2u * g + 1u;
     if (t0 < (uint32_t)a.n_tokens) {
-      float* q = a.y + (size_t)t0 * a.out_dim + row;
-      *q = ACC ? *q + y0 : y0;
+      const size_t i0 = (size_t)t0 * a.out_dim + row;
+      float* q = a.y + i0;
+      *q = ACC ? *q + y0 : (a.r ? y0 + a.r[i0] : y0);
     }
     if (t1 < (uint32_t)a.n_tokens) {
-      float* q = a.y + (size_t)t1 * a.out_dim + row;
-      *q = ACC ? *q + y1 : y1;
+      const size_t i1 = (size_t)t1 * a.out_dim + row;
+      float* q = a.y + i1;
+      *q = ACC ? *q + y1 : (a.r ? y1 + a.r[i1] : y1);
     }
   }
 }
@@ -239,8 +242,9 @@ hipError_t launch_mfma_chunk(const Q4KGemvArgs& a, bool acc, hipStream_t st) {
 // instruction touches 16 rows -- keeps the vector L1 busy (its tag lookups
 // stall the address unit), which is what bounds this kernel today.
 hipError_t launch_q4k_q8_gemm_mfma(const uint8_t* w, const uint8_t* xq, float* y, int out_dim,
-                                   int in_dim, int n_tokens, hipStream_t stream) {
+                                   int in_dim, int n_tokens, hipStream_t stream, const float* r) {
   Q4KGemvArgs a;
+  a.r = r;
   a.w = w;
   a.xq = xq;
   a.y = y;

@@ -233,6 +233,7 @@ struct Q4KGemvArgs {
   int sb0;            // first super-block of this column chunk
   int nsb;            // super-blocks in this chunk
   int n_tokens;
+  const float* r;     // residual [n_tokens][out_dim] added by the RES store, else unused
 };
 
 // Store one tile's row sums (leader lanes only); ACC adds to y instead.
@@ -257,14 +258,54 @@ __device__ __forceinline__ void store_rows(const Q4KGemvArgs& a, const float (&a
   }
 }
 
+// The residual values of one tile's rows, [R][NT], through a buffer
+// descriptor over r: rows past out_dim and tokens past n_tokens read 0.  All
+// lanes of a row load the same address; only the leader uses the value.
+template <int TPR, int R, int NT>
+__device__ __forceinline__ void load_residual(float (&rv)[R][NT], __amdgpu_buffer_rsrc_t rr,
+                                              const Q4KGemvArgs& a, long row_base,
+                                              const LaneRole& ro) {
+  constexpr int RW = 8 / TPR;
+  const uint32_t bytes = (uint32_t)a.n_tokens * (uint32_t)a.out_dim * 4u;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const long row = row_base + (long)r * RW + ro.rs;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const uint32_t off = (row < a.out_dim && t < a.n_tokens)
+                               ? ((uint32_t)t * (uint32_t)a.out_dim + (uint32_t)row) * 4u
+                               : bytes;
+      rv[r][t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rr, off, 0, 0));
+    }
+  }
+}
+
+// Store row sums plus their residual: y = fl(acc + r), one rounding.
+template <int TPR, int R, int NT>
+__device__ __forceinline__ void store_rows_residual(const Q4KGemvArgs& a,
+                                                    const float (&acc)[R][NT],
+                                                    const float (&rv)[R][NT], long row_base,
+                                                    const LaneRole& ro) {
+  float sum[R][NT];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) sum[r][t] = acc[r][t] + rv[r][t];
+  store_rows<TPR, R, NT, false>(a, sum, row_base, ro);
+}
+
 // GEMV: wave w of W takes the G row groups w, w+W, ..., w+(G-1)W (a group is
 // RW*R rows).  The G groups are unrolled into straight-line code with P tiles
 // in flight: group k+P is requested before group k is reduced, and because no
 // load sits under a branch the compiler waits for exactly the tile it needs.
 // Groups past the end read zeros through the buffer descriptor and store
-// nothing.
-template <int TPR, int S, int R, int NT, int G, int P, bool ACC, int WPB = 4, bool STRIDED = true>
+// nothing.  RES (with ACC false) adds the residual a.r in the store; a group's
+// residual values are requested right after its weight tile, so waiting for
+// them never waits for a tile issued later.
+template <int TPR, int S, int R, int NT, int G, int P, bool ACC, int WPB = 4, bool STRIDED = true,
+          bool RES = false>
 __global__ __launch_bounds__(64 * WPB) void q4k_q8_gemv_kernel(Q4KGemvArgs a) {
+  static_assert(!(RES && ACC), "the residual is added by a storing pass");
   constexpr int RW = 8 / TPR;
   constexpr uint32_t kRowsPerGroup = (uint32_t)RW * R;
   const uint32_t nwaves = gridDim.x * (uint32_t)WPB;
@@ -283,19 +324,35 @@ __global__ __launch_bounds__(64 * WPB) void q4k_q8_gemv_kernel(Q4KGemvArgs a) {
   load_x_slots<TPR, S, NT>(xs, a.xq + (size_t)a.sb0 * 8 * kQ8Bytes,
                            (size_t)a.nsb_row * 8 * kQ8Bytes, a.nsb, a.n_tokens, ro);
   WTile<S, R> t[G];
+  float rv[G][R][NT];
+  __amdgpu_buffer_rsrc_t rr;
+  if constexpr (RES)
+    rr = __builtin_amdgcn_make_buffer_rsrc((void*)a.r, (short)0,
+                                           (int)((uint32_t)a.n_tokens * (uint32_t)a.out_dim * 4u),
+                                           kBufferWord3);
 #pragma unroll
-  for (int k = 0; k < P && k < G; ++k)
+  for (int k = 0; k < P && k < G; ++k) {
     load_w_tile<TPR, S, R>(t[k], src, off, (g0 + k * gstep) * kRowsPerGroup);
+    if constexpr (RES)
+      load_residual<TPR, R, NT>(rv[k], rr, a, (long)(g0 + k * gstep) * kRowsPerGroup, ro);
+  }
   // keep the scheduler from sinking requests below the first wait
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int k = 0; k < G; ++k) {
-    if (k + P < G)
+    if (k + P < G) {
       load_w_tile<TPR, S, R>(t[k + P], src, off, (g0 + (k + P) * gstep) * kRowsPerGroup);
+      if constexpr (RES)
+        load_residual<TPR, R, NT>(rv[k + P], rr, a, (long)(g0 + (k + P) * gstep) * kRowsPerGroup,
+                                  ro);
+    }
     __builtin_amdgcn_sched_barrier(0);
     float acc[R][NT];
     q4k_tile_dot<TPR, S, R, NT>(acc, t[k], xs, ro);
-    store_rows<TPR, R, NT, ACC>(a, acc, (long)(g0 + k * gstep) * kRowsPerGroup, ro);
+    if constexpr (RES)
+      store_rows_residual<TPR, R, NT>(a, acc, rv[k], (long)(g0 + k * gstep) * kRowsPerGroup, ro);
+    else
+      store_rows<TPR, R, NT, ACC>(a, acc, (long)(g0 + k * gstep) * kRowsPerGroup, ro);
   }
 }
 

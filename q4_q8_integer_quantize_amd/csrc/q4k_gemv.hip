@@ -8,6 +8,10 @@
 // From kMfmaMinTokens tokens on, the batch runs on the matrix cores
 // (q4k_gemm_mfma.hip).
 //
+// With a residual r, the first column chunk stores fl(partial + r) and later
+// chunks accumulate as without it; for one chunk y = fl(W x + r) exactly.
+// r may be y itself: each element is read and written by the same lane.
+//
 // Work split: a group is RW*R consecutive rows (RW = 8/TPR side by side, R
 // unrolled); each wave takes G groups strided by the wave count and keeps P
 // more in flight while it reduces one.  Rows longer than the register-resident activation window
@@ -28,15 +32,21 @@ constexpr int slots_max() { return NT <= 2 ? 8 : (NT == 4 ? 4 : 2); }
 template <int S, int NT>
 constexpr int rows_unrolled() { return (S <= 2 && NT <= 2) ? 2 : 1; }
 
+// How a column chunk's launch writes y.
+enum class Epi { kStore, kAccumulate, kResidual };
+
 template <int TPR, int S, int NT, int G>
-static hipError_t launch_g(const Q4KGemvArgs& a, long groups, bool acc, hipStream_t st) {
+static hipError_t launch_g(const Q4KGemvArgs& a, long groups, Epi epi, hipStream_t st) {
   constexpr int R = rows_unrolled<S, NT>();
   constexpr int P = G > kTilesInFlight ? kTilesInFlight : (G > 1 ? G - 1 : 1);
   const long waves = (groups + G - 1) / G;
   const unsigned grid = (unsigned)((waves + 3) / 4);
-  if (acc)
+  if (epi == Epi::kAccumulate)
     hipLaunchKernelGGL((q4k_q8_gemv_kernel<TPR, S, R, NT, G, P, true>), dim3(grid), dim3(256), 0,
                        st, a);
+  else if (epi == Epi::kResidual)
+    hipLaunchKernelGGL((q4k_q8_gemv_kernel<TPR, S, R, NT, G, P, false, 4, true, true>), dim3(grid),
+                       dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL((q4k_q8_gemv_kernel<TPR, S, R, NT, G, P, false>), dim3(grid), dim3(256), 0,
                        st, a);
@@ -47,7 +57,7 @@ static hipError_t launch_g(const Q4KGemvArgs& a, long groups, bool acc, hipStrea
 // the grid at about one wave per SIMD; fewer, deeper-pipelined waves stream
 // better than many short ones.
 template <int TPR, int S, int NT>
-static hipError_t run_q4k(const Q4KGemvArgs& a, bool acc, hipStream_t st) {
+static hipError_t run_q4k(const Q4KGemvArgs& a, Epi epi, hipStream_t st) {
   if constexpr (S > slots_max<NT>()) {
     return hipErrorInvalidValue;
   } else {
@@ -56,28 +66,28 @@ static hipError_t run_q4k(const Q4KGemvArgs& a, bool acc, hipStream_t st) {
     const long rows_per_group = (long)RW * R;
     const long groups = (a.out_dim + rows_per_group - 1) / rows_per_group;
     const long per_wave = (groups + kTargetWaves - 1) / kTargetWaves;
-    if (per_wave <= 1) return launch_g<TPR, S, NT, 1>(a, groups, acc, st);
-    if (per_wave <= 2) return launch_g<TPR, S, NT, 2>(a, groups, acc, st);
-    if (per_wave <= 4) return launch_g<TPR, S, NT, 4>(a, groups, acc, st);
-    return launch_g<TPR, S, NT, 8>(a, groups, acc, st);
+    if (per_wave <= 1) return launch_g<TPR, S, NT, 1>(a, groups, epi, st);
+    if (per_wave <= 2) return launch_g<TPR, S, NT, 2>(a, groups, epi, st);
+    if (per_wave <= 4) return launch_g<TPR, S, NT, 4>(a, groups, epi, st);
+    return launch_g<TPR, S, NT, 8>(a, groups, epi, st);
   }
 }
 
 template <int NT>
-static hipError_t run_q4k_chunk(const Q4KGemvArgs& a, bool acc, hipStream_t st) {
+static hipError_t run_q4k_chunk(const Q4KGemvArgs& a, Epi epi, hipStream_t st) {
   const int nsb = a.nsb;
-  if (nsb == 1) return run_q4k<1, 1, NT>(a, acc, st);
-  if (nsb == 2) return run_q4k<2, 1, NT>(a, acc, st);
-  if (nsb <= 4) return run_q4k<4, 1, NT>(a, acc, st);
+  if (nsb == 1) return run_q4k<1, 1, NT>(a, epi, st);
+  if (nsb == 2) return run_q4k<2, 1, NT>(a, epi, st);
+  if (nsb <= 4) return run_q4k<4, 1, NT>(a, epi, st);
   switch ((nsb + 7) / 8) {
-    case 1: return run_q4k<8, 1, NT>(a, acc, st);
-    case 2: return run_q4k<8, 2, NT>(a, acc, st);
-    case 3: return run_q4k<8, 3, NT>(a, acc, st);
-    case 4: return run_q4k<8, 4, NT>(a, acc, st);
-    case 5: return run_q4k<8, 5, NT>(a, acc, st);
-    case 6: return run_q4k<8, 6, NT>(a, acc, st);
-    case 7: return run_q4k<8, 7, NT>(a, acc, st);
-    case 8: return run_q4k<8, 8, NT>(a, acc, st);
+    case 1: return run_q4k<8, 1, NT>(a, epi, st);
+    case 2: return run_q4k<8, 2, NT>(a, epi, st);
+    case 3: return run_q4k<8, 3, NT>(a, epi, st);
+    case 4: return run_q4k<8, 4, NT>(a, epi, st);
+    case 5: return run_q4k<8, 5, NT>(a, epi, st);
+    case 6: return run_q4k<8, 6, NT>(a, epi, st);
+    case 7: return run_q4k<8, 7, NT>(a, epi, st);
+    case 8: return run_q4k<8, 8, NT>(a, epi, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -88,15 +98,17 @@ static hipError_t run_q4k_all(Q4KGemvArgs a, hipStream_t st) {
   for (int sb0 = 0; sb0 < a.nsb_row; sb0 += chunk) {
     a.sb0 = sb0;
     a.nsb = a.nsb_row - sb0 < chunk ? a.nsb_row - sb0 : chunk;
-    const hipError_t e = run_q4k_chunk<NT>(a, sb0 > 0, st);
+    const Epi epi = sb0 > 0 ? Epi::kAccumulate : (a.r ? Epi::kResidual : Epi::kStore);
+    const hipError_t e = run_q4k_chunk<NT>(a, epi, st);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
 hipError_t launch_q4k_q8_gemv(const uint8_t* w, const uint8_t* xq, float* y, int out_dim,
-                              int in_dim, int n_tokens, hipStream_t stream) {
+                              int in_dim, int n_tokens, hipStream_t stream, const float* r) {
   Q4KGemvArgs a;
+  a.r = r;
   a.w = w;
   a.xq = xq;
   a.y = y;
@@ -106,7 +118,7 @@ hipError_t launch_q4k_q8_gemv(const uint8_t* w, const uint8_t* xq, float* y, int
   a.nsb = a.nsb_row;
   a.n_tokens = n_tokens;
   if (n_tokens >= kMfmaMinTokens)
-    return launch_q4k_q8_gemm_mfma(w, xq, y, out_dim, in_dim, n_tokens, stream);
+    return launch_q4k_q8_gemm_mfma(w, xq, y, out_dim, in_dim, n_tokens, stream, r);
   if (n_tokens == 1) return run_q4k_all<1>(a, stream);
   if (n_tokens == 2) return run_q4k_all<2>(a, stream);
   if (n_tokens <= 4) return run_q4k_all<4>(a, stream);

@@ -148,6 +148,7 @@ __global__ __launch_bounds__(256) void q4k_gemv_f32_kernel(Q4KF32Args a) {
   XSlots<S, 1> xs;
   load_x_slots_lds<TPR, S>(xs, xq_lds, a.nsb, ro);
   Q4KGemvArgs ga;
+  ga.r = nullptr;
   ga.w = a.w;
   ga.xq = nullptr;
   ga.y = a.y;

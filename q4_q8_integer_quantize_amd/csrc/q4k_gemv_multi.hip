@@ -95,6 +95,7 @@ __global__ __launch_bounds__(256) void q4k_q8_gemv_multi_kernel(Q4KMultiArgs a) 
     float acc[R][NT];
     q4k_tile_dot<TPR, S, R, NT>(acc, t[k], xs, ro);
     Q4KGemvArgs ga;
+    ga.r = nullptr;
     ga.w = w_of(m[k]);
     ga.xq = a.xq;
     ga.y = y_of(m[k]);

@@ -35,6 +35,17 @@ int launch_status(hipError_t e, const char* what) {
   return fail(RZ_ELAUNCH, "%s: kernel launch failed: %s", what, hipGetErrorString(e));
 }
 
+// Byte ranges [a, a + na) and [b, b + nb) do not overlap.
+bool disjoint(const void* a, long long na, const void* b, long long nb) {
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+  return pa + static_cast<uintptr_t>(na) <= pb || pb + static_cast<uintptr_t>(nb) <= pa;
+}
+
+// Two fp32 arrays of `count` values either coincide or do not overlap.
+bool same_or_disjoint(const float* a, const float* b, long long count) {
+  return a == b || disjoint(a, count * 4, b, count * 4);
+}
+
 int check_dim(const char* what, const char* name, int v, int multiple) {
   if (v <= 0 || v > RZ_MAX_DIM || v % multiple != 0)
     return fail(RZ_EDIM, "%s: %s=%d must be a positive multiple of %d and <= %d", what, name, v,
@@ -67,6 +78,26 @@ int rz_q8_1_quantize(const float* x, int n, int n_padded, int n_tokens, void* x_
                        what);
 }
 
+int rz_rmsnorm_q8_1(const float* x, const float* gamma, float eps, int n, int n_padded,
+                    int n_tokens, float* normed, void* x_q8, void* stream) {
+  const char* what = "rz_rmsnorm_q8_1";
+  if (!x || !gamma || !x_q8) return fail(RZ_EINVAL, "%s: null pointer", what);
+  if (n_tokens < 1 || n_tokens > RZ_MAX_TOKENS)
+    return fail(RZ_EINVAL, "%s: n_tokens=%d outside 1..%d", what, n_tokens, RZ_MAX_TOKENS);
+  if (!(eps > 0.0f) || !(eps <= 3.0e38f))
+    return fail(RZ_EINVAL, "%s: eps=%g must be positive and finite", what, (double)eps);
+  if (int rc = check_dim(what, "n_padded", n_padded, 32)) return rc;
+  if (n <= 0 || n > n_padded)
+    return fail(RZ_EDIM, "%s: n=%d must satisfy 1 <= n <= n_padded=%d", what, n, n_padded);
+  if (!aligned(x, 4) || !aligned(gamma, 4) || (normed && !aligned(normed, 4)))
+    return fail(RZ_EALIGN, "%s: fp32 buffers must be 4-byte aligned", what);
+  if (!aligned(x_q8, 8)) return fail(RZ_EALIGN, "%s: x_q8 must be 8-byte aligned", what);
+  return launch_status(rz::launch_rmsnorm_q8_1(x, gamma, eps, n, n_padded, n_tokens, normed,
+                                               static_cast<uint8_t*>(x_q8),
+                                               static_cast<hipStream_t>(stream)),
+                       what);
+}
+
 int rz_q4k_q8_gemv(const void* w_q4k, const void* x_q8, float* y, int out_dim, int in_dim,
                    int n_tokens, void* stream) {
   const char* what = "rz_q4k_q8_gemv";
@@ -84,6 +115,29 @@ int rz_q4k_q8_gemv(const void* w_q4k, const void* x_q8, float* y, int out_dim, i
                                                static_cast<const uint8_t*>(x_q8), y, out_dim,
                                                in_dim, n_tokens,
                                                static_cast<hipStream_t>(stream)),
+                       what);
+}
+
+int rz_q4k_q8_gemv_add(const void* w_q4k, const void* x_q8, const float* r, float* y,
+                       int out_dim, int in_dim, int n_tokens, void* stream) {
+  const char* what = "rz_q4k_q8_gemv_add";
+  if (!w_q4k || !x_q8 || !r || !y) return fail(RZ_EINVAL, "%s: null pointer", what);
+  if (n_tokens < 1 || n_tokens > RZ_MAX_TOKENS)
+    return fail(RZ_EINVAL, "%s: n_tokens=%d outside 1..%d", what, n_tokens, RZ_MAX_TOKENS);
+  if (int rc = check_dim(what, "out_dim", out_dim, 1)) return rc;
+  if (int rc = check_dim(what, "in_dim", in_dim, 256)) return rc;
+  if ((long long)out_dim * (in_dim / 256) * RZ_Q4K_BLOCK_BYTES > kMaxMatrixBytes)
+    return fail(RZ_EDIM, "%s: weight matrix larger than %lld bytes", what, kMaxMatrixBytes);
+  if (!aligned(w_q4k, 16)) return fail(RZ_EALIGN, "%s: w_q4k must be 16-byte aligned", what);
+  if (!aligned(x_q8, 8)) return fail(RZ_EALIGN, "%s: x_q8 must be 8-byte aligned", what);
+  if (!aligned(r, 4) || !aligned(y, 4))
+    return fail(RZ_EALIGN, "%s: r and y must be 4-byte aligned", what);
+  if (!same_or_disjoint(r, y, (long long)n_tokens * out_dim))
+    return fail(RZ_EINVAL, "%s: r must be y itself or not overlap it", what);
+  return launch_status(rz::launch_q4k_q8_gemv(static_cast<const uint8_t*>(w_q4k),
+                                               static_cast<const uint8_t*>(x_q8), y, out_dim,
+                                               in_dim, n_tokens,
+                                               static_cast<hipStream_t>(stream), r),
                        what);
 }
 
@@ -158,10 +212,13 @@ int rz_q4_0_gemv(const void* w_q4_0, const void* x, int x_format, float* y, int 
                        what);
 }
 
-int rz_swiglu_ffn_q4k(const void* w_gate, const void* w_up, const void* w_down,
-                      const void* x_q8, float* h, void* h_q8, float* y, float* gu,
-                      int hidden_dim, int inter_dim, void* stream) {
-  const char* what = "rz_swiglu_ffn_q4k";
+}  // extern "C"
+
+namespace {
+
+int swiglu_ffn(const char* what, const void* w_gate, const void* w_up, const void* w_down,
+               const void* x_q8, float* h, void* h_q8, const float* r, float* y, float* gu,
+               int hidden_dim, int inter_dim, void* stream) {
   if (!w_gate || !w_up || !w_down || !x_q8 || !h || !h_q8 || !y)
     return fail(RZ_EINVAL, "%s: null pointer", what);
   if (int rc = check_dim(what, "hidden_dim", hidden_dim, 256)) return rc;
@@ -175,16 +232,42 @@ int rz_swiglu_ffn_q4k(const void* w_gate, const void* w_up, const void* w_down,
     return fail(RZ_EALIGN, "%s: weight blobs must be 16-byte aligned", what);
   if (!aligned(x_q8, 8) || !aligned(h_q8, 8))
     return fail(RZ_EALIGN, "%s: Q8_1 buffers must be 8-byte aligned", what);
-  if (!aligned(h, 4) || !aligned(y, 4) || (gu && !aligned(gu, 4)))
+  if (!aligned(h, 4) || !aligned(y, 4) || (gu && !aligned(gu, 4)) || (r && !aligned(r, 4)))
     return fail(RZ_EALIGN, "%s: fp32 buffers must be 4-byte aligned", what);
+  if (r && !same_or_disjoint(r, y, hidden_dim))
+    return fail(RZ_EINVAL, "%s: r must be y itself or not overlap it", what);
+  // the first kernel writes h, h_q8 and gu before the second reads r
+  if (r && (!disjoint(r, 4LL * hidden_dim, h, 4LL * inter_dim) ||
+            !disjoint(r, 4LL * hidden_dim, h_q8, (long long)inter_dim / 32 * RZ_Q8_1_BLOCK_BYTES) ||
+            (gu && !disjoint(r, 4LL * hidden_dim, gu, 8LL * inter_dim))))
+    return fail(RZ_EINVAL, "%s: r must not overlap h, h_q8 or gu", what);
   return launch_status(
       rz::launch_swiglu_ffn_q4k(static_cast<const uint8_t*>(w_gate),
                                 static_cast<const uint8_t*>(w_up),
                                 static_cast<const uint8_t*>(w_down),
                                 static_cast<const uint8_t*>(x_q8), h,
                                 static_cast<uint8_t*>(h_q8), y, gu, hidden_dim, inter_dim,
-                                static_cast<hipStream_t>(stream)),
+                                static_cast<hipStream_t>(stream), r),
       what);
+}
+
+}  // namespace
+
+extern "C" {
+
+int rz_swiglu_ffn_q4k(const void* w_gate, const void* w_up, const void* w_down,
+                      const void* x_q8, float* h, void* h_q8, float* y, float* gu,
+                      int hidden_dim, int inter_dim, void* stream) {
+  return swiglu_ffn("rz_swiglu_ffn_q4k", w_gate, w_up, w_down, x_q8, h, h_q8, nullptr, y, gu,
+                    hidden_dim, inter_dim, stream);
+}
+
+int rz_swiglu_ffn_q4k_add(const void* w_gate, const void* w_up, const void* w_down,
+                          const void* x_q8, float* h, void* h_q8, const float* r, float* y,
+                          float* gu, int hidden_dim, int inter_dim, void* stream) {
+  if (!r) return fail(RZ_EINVAL, "rz_swiglu_ffn_q4k_add: null pointer");
+  return swiglu_ffn("rz_swiglu_ffn_q4k_add", w_gate, w_up, w_down, x_q8, h, h_q8, r, y, gu,
+                    hidden_dim, inter_dim, stream);
 }
 
 }  // extern "C"

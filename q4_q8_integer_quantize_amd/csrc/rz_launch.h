@@ -10,14 +10,23 @@ namespace rz {
 hipError_t launch_q8_1_quantize(const float* x, int n, int n_padded, int n_tokens,
                                 uint8_t* out, hipStream_t stream);
 
-// Q4_K x Q8_1 GEMV for 1..8 tokens (token-major y).
+// RMSNorm of [n_tokens][n] fp32 values with weights gamma[n], quantized to
+// Q8_1 ([n_tokens][n_padded/32] blocks); normed ([n_tokens][n]) is optional.
+hipError_t launch_rmsnorm_q8_1(const float* x, const float* gamma, float eps, int n,
+                               int n_padded, int n_tokens, float* normed, uint8_t* x_q8,
+                               hipStream_t stream);
+
+// Q4_K x Q8_1 GEMV for 1..8 tokens (token-major y).  With r (token-major,
+// like y; may be y) the result is W x + r.
 hipError_t launch_q4k_q8_gemv(const uint8_t* w, const uint8_t* xq, float* y, int out_dim,
-                              int in_dim, int n_tokens, hipStream_t stream);
+                              int in_dim, int n_tokens, hipStream_t stream,
+                              const float* r = nullptr);
 
 // The same for a batch of tokens on the matrix cores (used by
 // launch_q4k_q8_gemv from kMfmaMinTokens tokens on).
 hipError_t launch_q4k_q8_gemm_mfma(const uint8_t* w, const uint8_t* xq, float* y, int out_dim,
-                                   int in_dim, int n_tokens, hipStream_t stream);
+                                   int in_dim, int n_tokens, hipStream_t stream,
+                                   const float* r = nullptr);
 constexpr int kMfmaMinTokens = 3;
 
 // Several Q4_K matrices (at most kMaxMats) times one Q8_1 activation; one
@@ -35,9 +44,10 @@ hipError_t launch_q4k_q8_gemv_f32(const uint8_t* w, const float* x, int n, uint8
 hipError_t launch_q4_0_gemv(const uint8_t* w, const void* x, int x_format, float* y,
                             int out_dim, int in_dim, hipStream_t stream);
 
+// SwiGLU FFN chain; with r the down projection's output is y = W_down h + r.
 hipError_t launch_swiglu_ffn_q4k(const uint8_t* w_gate, const uint8_t* w_up,
                                  const uint8_t* w_down, const uint8_t* xq, float* h,
                                  uint8_t* h_q8, float* y, float* gu, int hidden_dim,
-                                 int inter_dim, hipStream_t stream);
+                                 int inter_dim, hipStream_t stream, const float* r = nullptr);
 
 }  // namespace rz

@@ -113,7 +113,7 @@ static hipError_t run_gate_up(const SwiArgs& a, hipStream_t st) {
 hipError_t launch_swiglu_ffn_q4k(const uint8_t* w_gate, const uint8_t* w_up,
                                  const uint8_t* w_down, const uint8_t* xq, float* h,
                                  uint8_t* h_q8, float* y, float* gu, int hidden_dim,
-                                 int inter_dim, hipStream_t stream) {
+                                 int inter_dim, hipStream_t stream, const float* r) {
   SwiArgs a;
   a.wg = w_gate;
   a.wu = w_up;
@@ -142,7 +142,7 @@ hipError_t launch_swiglu_ffn_q4k(const uint8_t* w_gate, const uint8_t* w_up,
     }
   }
   if (e != hipSuccess) return e;
-  return launch_q4k_q8_gemv(w_down, h_q8, y, hidden_dim, inter_dim, 1, stream);
+  return launch_q4k_q8_gemv(w_down, h_q8, y, hidden_dim, inter_dim, 1, stream, r);
 }
 
 }  // namespace rz

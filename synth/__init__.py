@@ -15,9 +15,10 @@ Workload recipe (all synthetic; the pages print no data):
   in 0..63.  Uniform qs bytes give uniform nibbles in 0..15.
 * Q4_0 block (32 weights, 18 bytes): fp16 ``d`` uniform in [1e-3, 1e-2] and 16
   bytes of uniform nibbles.
-* Activations: fp32 cast of float64 N(0, 1) draws, optionally passed through an
-  RMSNorm (gamma ~ N(1, 0.1), eps 1e-5, computed in float64) as the attention
-  projection workload does.
+* Activations: fp32 cast of float64 N(0, 1) draws.  The attention-projection
+  workload normalises such a draw with RMSNorm weights (``norm_weights``: fp32
+  cast of N(1, 0.1) draws, eps 1e-5) before quantizing it; the norm itself is
+  computed by the caller (the oracle on the CPU side, the library on the GPU).
 """
 from __future__ import annotations
 
@@ -89,18 +90,9 @@ def activation(g: np.random.Generator, n: int, n_tokens: int | None = None) -> n
     return g.standard_normal(shape).astype(np.float32)
 
 
-def rmsnorm_activation(g_x: np.random.Generator, g_gamma: np.random.Generator,
-                       n: int, eps: float = 1e-5) -> np.ndarray:
-    """fp32 activation after an RMSNorm with gamma ~ N(1, 0.1), eps inside the root.
-
-    The norm is the input recipe of the attention-projection workload (the layer
-    normalises the hidden state before quantizing it once for Q, K and V); it is
-    computed in float64 and the result is rounded once to fp32.
-    """
-    x = g_x.standard_normal(n)
-    gamma = 1.0 + 0.1 * g_gamma.standard_normal(n)
-    rms = np.sqrt(np.mean(x * x) + eps)
-    return (x / rms * gamma).astype(np.float32)
+def norm_weights(g: np.random.Generator, n: int) -> np.ndarray:
+    """RMSNorm weights: fp32 cast of N(1, 0.1) draws."""
+    return (1.0 + 0.1 * g.standard_normal(n)).astype(np.float32)
 
 
 def weight_copies(make, count: int):

@@ -39,7 +39,8 @@ def lib():
 def test_header_declares_the_four_operations():
     syms = declared_symbols()
     for name in ("rz_q8_1_quantize", "rz_q4k_q8_gemv", "rz_q4k_q8_gemv_f32", "rz_q4_0_gemv",
-                 "rz_swiglu_ffn_q4k", "rz_q4k_q8_gemv_multi", "rz_last_error",
+                 "rz_swiglu_ffn_q4k", "rz_q4k_q8_gemv_multi", "rz_rmsnorm_q8_1",
+                 "rz_q4k_q8_gemv_add", "rz_swiglu_ffn_q4k_add", "rz_last_error",
                  "rz_abi_version"):
         assert name in syms
 
@@ -196,6 +197,76 @@ def test_q4_0_gemv_rejects(lib, args, code):
 ])
 def test_swiglu_ffn_rejects(lib, args, code):
     assert _rc("rz_swiglu_ffn_q4k", *args) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, P, 1e-5, 4096, 4096, 1, None, P, None), rz.RZ_EINVAL),       # null x
+    ((P, None, 1e-5, 4096, 4096, 1, None, P, None), rz.RZ_EINVAL),       # null gamma
+    ((P, P, 1e-5, 4096, 4096, 1, None, None, None), rz.RZ_EINVAL),       # null x_q8
+    ((P, P, 1e-5, 4096, 4096, 0, None, P, None), rz.RZ_EINVAL),          # n_tokens 0
+    ((P, P, 1e-5, 4096, 4096, 9, None, P, None), rz.RZ_EINVAL),          # n_tokens 9
+    ((P, P, 0.0, 4096, 4096, 1, None, P, None), rz.RZ_EINVAL),           # eps 0
+    ((P, P, -1e-5, 4096, 4096, 1, None, P, None), rz.RZ_EINVAL),         # eps < 0
+    ((P, P, float("inf"), 4096, 4096, 1, None, P, None), rz.RZ_EINVAL),  # eps inf
+    ((P, P, float("nan"), 4096, 4096, 1, None, P, None), rz.RZ_EINVAL),  # eps NaN
+    ((P, P, 1e-5, 896, 1000, 1, None, P, None), rz.RZ_EDIM),             # n_padded % 32
+    ((P, P, 1e-5, 1025, 1024, 1, None, P, None), rz.RZ_EDIM),            # n > n_padded
+    ((P, P, 1e-5, 0, 1024, 1, None, P, None), rz.RZ_EDIM),               # n == 0
+    ((P_ODD, P, 1e-5, 896, 1024, 1, None, P, None), rz.RZ_EALIGN),       # x
+    ((P, P_ODD, 1e-5, 896, 1024, 1, None, P, None), rz.RZ_EALIGN),       # gamma
+    ((P, P, 1e-5, 896, 1024, 1, P_ODD, P, None), rz.RZ_EALIGN),          # normed
+    ((P, P, 1e-5, 896, 1024, 1, None, P + 4, None), rz.RZ_EALIGN),       # x_q8
+])
+def test_rmsnorm_q8_1_rejects(lib, args, code):
+    assert _rc("rz_rmsnorm_q8_1", *args) == code
+    assert _rc.last.startswith("rz_rmsnorm_q8_1")
+
+
+Y = P + (1 << 30)   # a y buffer far from P
+@pytest.mark.parametrize("args,code", [
+    ((None, P, P, Y, 4096, 4096, 1, None), rz.RZ_EINVAL),
+    ((P, None, P, Y, 4096, 4096, 1, None), rz.RZ_EINVAL),
+    ((P, P, None, Y, 4096, 4096, 1, None), rz.RZ_EINVAL),          # null r
+    ((P, P, P, None, 4096, 4096, 1, None), rz.RZ_EINVAL),
+    ((P, P, P, Y, 4096, 4096, 0, None), rz.RZ_EINVAL),
+    ((P, P, P, Y, 4096, 4096, 9, None), rz.RZ_EINVAL),
+    ((P, P, Y + 4, Y, 4096, 4096, 1, None), rz.RZ_EINVAL),         # r overlaps y, not equal
+    ((P, P, Y - 4 * 4095, Y, 4096, 4096, 1, None), rz.RZ_EINVAL),  # overlap by one value
+    ((P, P, Y, Y + 4 * 4096 * 2, 4096, 4096, 3, None), rz.RZ_EINVAL),  # 3 tokens: overlaps
+    ((P, P, P, Y, 4096, 896, 1, None), rz.RZ_EDIM),
+    ((P, P, P, Y, 0, 4096, 1, None), rz.RZ_EDIM),
+    ((P + 8, P, P, Y, 4096, 4096, 1, None), rz.RZ_EALIGN),
+    ((P, P + 4, P, Y, 4096, 4096, 1, None), rz.RZ_EALIGN),
+    ((P, P, P_ODD, Y, 4096, 4096, 1, None), rz.RZ_EALIGN),
+    ((P, P, P, Y + 2, 4096, 4096, 1, None), rz.RZ_EALIGN),
+])
+def test_q4k_q8_gemv_add_rejects(lib, args, code):
+    assert _rc("rz_q4k_q8_gemv_add", *args) == code
+    assert _rc.last.startswith("rz_q4k_q8_gemv_add")
+
+
+def test_q4k_q8_gemv_add_accepts_in_place_and_adjacent(lib):
+    # r == y and r right after y pass validation; with no device visible the
+    # launch itself then fails
+    res = run_isolated([("rz_q4k_q8_gemv_add", [P, P, Y, Y, 4096, 4096, 2, None]),
+                        ("rz_q4k_q8_gemv_add", [P, P, Y + 4 * 4096 * 2, Y, 4096, 4096, 2, None])])
+    assert [rc for rc, _ in res] == [rz.RZ_ELAUNCH, rz.RZ_ELAUNCH]
+
+
+H = P + (2 << 30)
+@pytest.mark.parametrize("args,code", [
+    ((P, P, P, P, H, P, None, Y, None, 4096, 14336, None), rz.RZ_EINVAL),        # null r
+    ((P, P, P, P, H, P, Y + 4, Y, None, 4096, 14336, None), rz.RZ_EINVAL),       # r overlaps y
+    ((P, P, P, P, H, P, H + 64, Y, None, 4096, 14336, None), rz.RZ_EINVAL),      # r inside h
+    ((P, P, P, P, H, Y + 65536, Y + 65536 - 400, Y, None, 4096, 14336, None),
+     rz.RZ_EINVAL),                                                              # r meets h_q8
+    ((P, P, P, P, H, P, H + 4 * 14336, Y, H, 4096, 14336, None), rz.RZ_EINVAL),  # r inside gu
+    ((P, P, P, P, H, P, P_ODD, Y, None, 4096, 14336, None), rz.RZ_EALIGN),
+    ((P, P, P, P, H, P, Y, Y, None, 4000, 14336, None), rz.RZ_EDIM),
+])
+def test_swiglu_ffn_add_rejects(lib, args, code):
+    assert _rc("rz_swiglu_ffn_q4k_add", *args) == code
+    assert _rc.last.startswith("rz_swiglu_ffn_q4k_add")
 
 
 def test_error_message_is_per_call(lib):

@@ -62,6 +62,14 @@ def assert_within(y_gpu, y_ref, terms, what):
                                 float(y_ref[r]), float(tol[r]), float(terms[r])))
 
 
+def normed_activation(cid, n):
+    """The attention workload's input: an fp32 N(0,1) hidden state through the
+    oracle's RMSNorm (gamma ~ N(1, 0.1), eps 1e-5), rounded once to fp32."""
+    x = synth.activation(synth.rng(cid, synth.T_ACT), n)
+    gamma = synth.norm_weights(synth.rng(cid, synth.T_GAMMA), n)
+    return oracle.rmsnorm(x, gamma, 1e-5).astype(np.float32)
+
+
 def oracle_q4k(blob, xq, n_tokens=1):
     """Oracle y and terms for every token: (n_tokens, out_dim) each."""
     if n_tokens == 1 and xq.d.ndim == 1:
@@ -96,7 +104,7 @@ def _q8_case(kind, n, nt, seed):
     if kind == "normal":
         return synth.activation(g, n, nt if nt > 1 else None)
     if kind == "rmsnorm":
-        return synth.rmsnorm_activation(synth.rng(1, 0), synth.rng(1, synth.T_GAMMA), n)
+        return normed_activation(1, n)
     if kind == "wide":
         x = g.standard_normal((nt, n)) * np.exp(g.uniform(-20, 20, (nt, n)))
         return x.astype(np.float32)[0] if nt == 1 else x.astype(np.float32)
@@ -337,7 +345,7 @@ def test_q4k_gemv_f32_without_side_output():
 def test_q4k_attention_projections_full():
     """Q 4096x4096, K/V 1024x4096, O 4096x4096 sharing one RMSNorm'd activation."""
     w = synth.WORKLOADS["attn_4096"]
-    x = synth.rmsnorm_activation(synth.rng(1, synth.T_ACT), synth.rng(1, synth.T_GAMMA), w["n"])
+    x = normed_activation(1, w["n"])
     xq = oracle.quantize_q8_1(x, w["in_dim"])
     got_q8 = gpu_quantize(x, w["in_dim"])[0]
     assert np.array_equal(got_q8, oracle.q8_1_to_bytes(xq))
@@ -354,7 +362,7 @@ def test_q4k_multi_attention_one_launch():
     output equals its own rz_q4k_q8_gemv call bit for bit and the oracle within
     the GEMV bound."""
     w = synth.WORKLOADS["attn_4096"]
-    x = synth.rmsnorm_activation(synth.rng(1, synth.T_ACT), synth.rng(1, synth.T_GAMMA), w["n"])
+    x = normed_activation(1, w["n"])
     xq = oracle.quantize_q8_1(x, w["in_dim"])
     xb = dev_bytes(oracle.q8_1_to_bytes(xq))
     blobs = [synth.q4k_weights(synth.rng(1, synth.T_W0 + k), rows, w["in_dim"])
@@ -600,6 +608,177 @@ def test_swiglu_optional_gu_pointer():
     b = run_ffn(wg, wu, wd, xb, hidden, inter, with_gu=False)
     assert np.array_equal(a["h"], b["h"]) and np.array_equal(a["hq"], b["hq"])
     assert np.array_equal(a["y"], b["y"])
+
+
+# ------------------------------------------------------------------ RMSNorm -> Q8_1
+def gpu_rmsnorm_q8(x, gamma, eps, n_padded, with_normed=True):
+    x2 = x if x.ndim == 2 else x[None, :]
+    nt, n = x2.shape
+    normed = empty_f32(nt * n) if with_normed else None
+    xq = empty_bytes(rz.q8_1_nbytes(n_padded, nt))
+    rz.rz_rmsnorm_q8_1(dev_f32(x2), dev_f32(gamma), eps, n, n_padded, nt, normed, xq)
+    q = q8_host_bytes(xq, nt * n_padded // 32).reshape(nt, n_padded // 32, 40)
+    return (host(normed).reshape(nt, n) if with_normed else None), q
+
+
+def _norm_chain(n_padded):
+    """Longest chain of dependent fp32 additions in the kernel's sum of squares.
+    Rows of up to 16384 values: 4 values per 1024-value pass in each of 256
+    threads, then 6 DPP levels inside a wave and 2 over the 4 wave sums; longer
+    rows: 4 values per 4096-value pass in each of 1024 threads, 6 + 4 levels."""
+    if n_padded <= 16384:
+        return 4 * -(-n_padded // 1024) + 8
+    return 4 * -(-n_padded // 4096) + 10
+
+
+@pytest.mark.parametrize("n,n_padded,nt,scale", [
+    (4096, 4096, 1, 1.0),       # the attention-projection input
+    (896, 1024, 1, 1.0),        # 896-wide hidden state, padded
+    (4096, 4096, 8, 1.0),       # 8 tokens
+    (14336, 14336, 1, 1.0),
+    (1000, 1024, 3, 1.0),       # ragged tail inside a block
+    (1, 32, 1, 1.0),
+    (33, 64, 2, 1.0),
+    (20000, 20480, 1, 1.0),     # several 32-block passes
+    (4096, 4096, 2, 1e-4),      # eps comparable to the mean square
+    (4096, 4096, 1, 1e15),      # large values: the sum of squares near 1e34
+])
+def test_rmsnorm_q8_1_matches_oracle(n, n_padded, nt, scale):
+    """Stage by stage: the normed values within the fp32 rounding bound of the
+    float64 definition; the Q8_1 blocks byte-equal to the standalone quantize of
+    the GPU's own normed values (and those bytes are pinned elsewhere); against
+    the oracle's blocks of its own normed values, d within the propagated bound
+    and every code within one step."""
+    banner("rmsnorm_q8_1", n, n_padded, nt, scale)
+    g = np.random.default_rng(n * 7 + nt)
+    x = (synth.activation(g, n, nt) * np.float32(scale)).astype(np.float32)
+    gamma = synth.norm_weights(np.random.default_rng(n + 1), n)
+    eps = 1e-5
+    normed, q = gpu_rmsnorm_q8(x, gamma, eps, n_padded)
+    ref = oracle.rmsnorm(x, gamma, eps)
+    tol = oracle.rmsnorm_tolerance(ref, _norm_chain(n_padded))
+    err = np.abs(normed.astype(np.float64) - ref)
+    assert np.all(err <= tol), "normed: %d outside, worst ratio %.3g" % (
+        int((err > tol).sum()), float(np.max(err / tol)))
+    assert np.array_equal(q, gpu_quantize(normed, n_padded))
+    # against the oracle's quantize of its own (float64 -> fp32) normed values
+    want = oracle.quantize_q8_1(ref.astype(np.float32), n_padded)
+    d_gpu = q[..., 0:4].copy().view("<f4")[..., 0].astype(np.float64).reshape(-1)
+    q_gpu = q[..., 8:40].copy().view(np.int8).astype(np.int64).reshape(-1, 32)
+    d_ref = want.d.astype(np.float64).reshape(-1)
+    q_ref = want.q.astype(np.int64).reshape(-1, 32)
+    tol_pad = np.zeros((nt, n_padded))
+    tol_pad[:, :n] = tol + np.abs(ref) * 2.0 ** -24
+    amax_tol = np.max(tol_pad.reshape(-1, 32), axis=1)
+    assert np.all(np.abs(d_gpu - d_ref) <= amax_tol / 127 + 2 * 2.0 ** -24 * d_ref)
+    assert np.all(np.abs(q_gpu - q_ref) <= 1)
+
+
+def test_rmsnorm_q8_1_tokens_independent_and_optional_output():
+    """Each token is normalised on its own (a batch equals its tokens one at a
+    time, bit for bit), and skipping the normed output changes nothing."""
+    banner("rmsnorm tokens")
+    n = 4096
+    x = synth.activation(np.random.default_rng(11), n, 5)
+    gamma = synth.norm_weights(np.random.default_rng(12), n)
+    normed, q = gpu_rmsnorm_q8(x, gamma, 1e-5, n)
+    _, q_skip = gpu_rmsnorm_q8(x, gamma, 1e-5, n, with_normed=False)
+    assert np.array_equal(q, q_skip)
+    for t in (4, 0, 2):
+        nt_, qt = gpu_rmsnorm_q8(x[t], gamma, 1e-5, n)
+        assert np.array_equal(nt_[0], normed[t]) and np.array_equal(qt[0], q[t])
+
+
+def test_rmsnorm_q8_1_degenerate_inputs():
+    """All-zero tokens give zero values and all-zero blocks; a zero weight zeroes
+    its value; a constant token of c gives c / sqrt(c^2 + eps) * gamma."""
+    banner("rmsnorm degenerate")
+    n = 512
+    x = np.zeros((3, n), np.float32)
+    x[1] = 3.0
+    x[2] = synth.activation(np.random.default_rng(13), n)
+    gamma = synth.norm_weights(np.random.default_rng(14), n)
+    gamma[::7] = 0.0
+    normed, q = gpu_rmsnorm_q8(x, gamma, 1e-5, n)
+    assert np.all(normed[0] == 0) and not q[0].any()
+    assert np.all(normed[1:, ::7] == 0)
+    ref = oracle.rmsnorm(x[1], gamma, 1e-5)
+    closed = 3.0 / np.sqrt(9.0 + 1e-5) * gamma.astype(np.float64)
+    assert np.allclose(ref, closed, rtol=1e-15, atol=0)
+    assert np.all(np.abs(normed[1] - closed) <= oracle.rmsnorm_tolerance(closed, _norm_chain(n)))
+
+
+# ------------------------------------------------------------------ residual-add epilogue
+def _one_pass(n_tokens, in_dim):
+    """The row fits one pass of the kernel (so y = fl32(W x + r) exactly)."""
+    return in_dim <= (16384 if n_tokens <= 2 else 4096)
+
+
+def gpu_q4k_add(blob, xq_bytes, r, n_tokens, in_place=False):
+    out_dim = blob.shape[0]
+    rd = dev_f32(r.reshape(-1))
+    y = rd if in_place else empty_f32(out_dim * n_tokens)
+    rz.rz_q4k_q8_gemv_add(dev_bytes(blob), dev_bytes(xq_bytes), rd, y, out_dim,
+                          blob.shape[1] * 256, n_tokens)
+    return host(y).reshape(n_tokens, out_dim)
+
+
+@pytest.mark.parametrize("out_dim,in_dim,nt", [
+    (4096, 4096, 1),      # O projection of the attention workload
+    (4096, 14336, 1),     # FFN down projection
+    (300, 1024, 1),
+    (37, 2048, 2),
+    (100, 20480, 1),      # two column passes
+    (513, 4096, 3),       # matrix cores, one pass
+    (14336, 4096, 8),
+    (1000, 14336, 8),     # matrix cores, four passes
+])
+def test_q4k_gemv_add(out_dim, in_dim, nt):
+    """y = W x + r: bit-equal to fl32(rz_q4k_q8_gemv + r) when one pass covers
+    the row, the same in place (r is y), and within the GEMV bound of the
+    oracle with the residual counted as one more term."""
+    banner("gemv_add", out_dim, in_dim, nt)
+    cid = 40 + nt
+    blob = synth.q4k_weights(synth.rng(cid, synth.T_W0), out_dim, in_dim)
+    x = synth.activation(synth.rng(cid, synth.T_ACT), in_dim, nt)
+    xq = oracle.quantize_q8_1(x, in_dim)
+    xb = oracle.q8_1_to_bytes(xq)
+    r = (synth.activation(synth.rng(cid, 7), out_dim, nt) * np.float32(3.0)).astype(np.float32)
+    y = gpu_q4k_add(blob, xb, r, nt)
+    y_in_place = gpu_q4k_add(blob, xb, r, nt, in_place=True)
+    assert np.array_equal(y, y_in_place)
+    if _one_pass(nt, in_dim):
+        plain = gpu_q4k(blob, xb, nt)
+        assert np.array_equal(y, (plain + r).astype(np.float32))
+    y_ref, terms = oracle_q4k(blob, xq, nt)
+    for t in range(nt):
+        assert_within(y[t], oracle.residual_add(r[t], y_ref[t]), terms[t] + np.abs(r[t]),
+                      "gemv_add token %d" % t)
+
+
+def test_swiglu_ffn_add():
+    """The FFN with the residual: h and h_q8 as without it, y bit-equal to
+    fl32(y + r) of the plain chain (one pass: inter 14336), and in place."""
+    hidden, inter = 4096, 14336
+    banner("swiglu_add", hidden, inter)
+    cid = 2
+    wg = synth.q4k_weights(synth.rng(cid, synth.T_W0), inter, hidden)
+    wu = synth.q4k_weights(synth.rng(cid, synth.T_W0 + 1), inter, hidden)
+    wd = synth.q4k_weights(synth.rng(cid, synth.T_W0 + 2), hidden, inter)
+    xb = oracle.q8_1_to_bytes(oracle.quantize_q8_1(synth.activation(synth.rng(cid, synth.T_ACT),
+                                                                    hidden)))
+    r = synth.activation(synth.rng(cid, 7), hidden)
+    plain = run_ffn(wg, wu, wd, xb, hidden, inter, with_gu=False)
+    dw = [dev_bytes(a) for a in (wg, wu, wd, xb)]
+    for in_place in (False, True):
+        h = empty_f32(inter)
+        hq = empty_bytes(rz.q8_1_nbytes(inter))
+        rd = dev_f32(r)
+        y = rd if in_place else empty_f32(hidden)
+        rz.rz_swiglu_ffn_q4k_add(*dw, h, hq, rd, y, None, hidden, inter)
+        assert np.array_equal(host(h), plain["h"])
+        assert np.array_equal(q8_host_bytes(hq, inter // 32), plain["hq"])
+        assert np.array_equal(host(y), (plain["y"] + r).astype(np.float32))
 
 
 # ------------------------------------------------------------------ errors on device tensors

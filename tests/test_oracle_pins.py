@@ -444,6 +444,28 @@ def test_rmsnorm_tolerance_covers_fp32_evaluations(n):
         assert np.all(np.abs(y32.astype(np.float64) - ref) <= oracle.rmsnorm_tolerance(ref, chain))
 
 
+def test_rmsnorm_tolerance_rejects_planted_mistakes():
+    """At the chain length of a tree-shaped sum over 4096 values (24 dependent
+    additions), the bound is tight enough to reject a dropped eps, a mean over
+    n - 1 values and eps added after the root (each evaluated exactly, so only
+    the mistake separates it from the definition)."""
+    g = np.random.default_rng(9)
+    n = 4096
+    x = g.normal(size=n)
+    w = g.normal(1, 0.1, n)
+    eps = 1e-5
+    ref = oracle.rmsnorm(x, w, eps)
+    tol = oracle.rmsnorm_tolerance(ref, 24)
+    ms = np.mean(x * x)
+    planted = {
+        "eps dropped": x / np.sqrt(ms) * w,
+        "mean over n-1": x / np.sqrt(np.sum(x * x) / (n - 1) + eps) * w,
+        "eps after the root": x / (np.sqrt(ms) + eps) * w,
+    }
+    for name, y in planted.items():
+        assert np.all(np.abs(y - ref) > tol), name
+
+
 def test_residual_add():
     r = np.array([1.0, -2.0, 0.5])
     assert np.array_equal(oracle.residual_add(r, np.array([0.25, 2.0, -0.5])), [1.25, 0.0, 0.0])
