@@ -15,6 +15,9 @@ source pages (docs.rs, realizar 0.8.4/0.8.5):
   the gate output, then multiplied elementwise by the up output.
 * ``src/cuda/executor/layers/forward_utils.rs``, ``pad_and_upload_input``: the
   activation is zero-padded to a multiple of the 256-value super-block.
+* ``cached.rs``, ``transformer_layer_gpu_cached`` steps 2, 4 and 7: the same
+  projections and FFN with the fp32 normed activation, not quantized
+  (``q4k_gemv_cached_async``, ``fused_ffn_swiglu_gpu``).
 * ``src/gpu/adapters/using.rs``, ``rms_norm_inplace``, and ``cached.rs`` steps 1, 7,
   8 and 10: the RMSNorm before the quantize and the residual adds after the O
   projection and the FFN.
@@ -33,10 +36,11 @@ dequantize-then-dot identity.
 from .q8_1 import (QK8_1, Q8_1_BLOCK_BYTES, quantize_q8_1, q8_1_to_bytes,
                    q8_1_from_bytes, dequantize_q8_1, Q8Blocks)
 from .q4k import (q4k_fields, q4k_unpack_scales, dequantize_q4k,
-                  gemv_q4k_q8_def, gemv_q4k_q8_int)
+                  gemv_q4k_q8_def, gemv_q4k_q8_int, gemv_q4k_f32)
 from .q4_0 import (q4_0_fields, dequantize_q4_0, gemv_q4_0_f32,
                    gemv_q4_0_q8_int)
-from .swiglu import silu, silu_grad, swiglu, ffn_swiglu_q4k, h_tolerance
+from .swiglu import (silu, silu_grad, swiglu, ffn_swiglu_q4k, ffn_swiglu_q4k_f32,
+                     h_tolerance)
 from .tolerance import gemv_tolerance, GEMV_REL, GEMV_ABS
 from .norm import rmsnorm, rmsnorm_tolerance, residual_add
 
@@ -44,9 +48,9 @@ __all__ = [
     "QK8_1", "Q8_1_BLOCK_BYTES", "quantize_q8_1", "q8_1_to_bytes", "q8_1_from_bytes",
     "dequantize_q8_1", "Q8Blocks",
     "q4k_fields", "q4k_unpack_scales", "dequantize_q4k", "gemv_q4k_q8_def",
-    "gemv_q4k_q8_int",
+    "gemv_q4k_q8_int", "gemv_q4k_f32",
     "q4_0_fields", "dequantize_q4_0", "gemv_q4_0_f32", "gemv_q4_0_q8_int",
-    "silu", "silu_grad", "swiglu", "ffn_swiglu_q4k", "h_tolerance",
+    "silu", "silu_grad", "swiglu", "ffn_swiglu_q4k", "ffn_swiglu_q4k_f32", "h_tolerance",
     "gemv_tolerance", "GEMV_REL", "GEMV_ABS",
     "rmsnorm", "rmsnorm_tolerance", "residual_add",
 ]

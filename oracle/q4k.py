@@ -28,7 +28,8 @@ Two statements of the product, both in float64:
 * integer form: ``isum_j = sum_l q4 * q8`` exactly (int64), then
   ``y[r] = sum_{b, j} d * sc_j * d_x * isum_j - dmin * m_j * s_j``.
 
-They differ only by the fp32 rounding of ``s_j``.  ``terms`` is
+They differ only by the fp32 rounding of ``s_j``.  ``gemv_q4k_f32`` states the
+product with an fp32 activation (no Q8_1), the definition again.  ``terms`` is
 ``sum |d sc d_x isum| + |dmin m s|``, the summands an fp32 kernel rounds; the
 pass bound of an fp32 result is ``1e-5 * terms + 1e-6``.
 """
@@ -101,6 +102,37 @@ def gemv_q4k_q8_def(blob: np.ndarray, x: Q8Blocks) -> np.ndarray:
     for r0 in range(0, blob.shape[0], ROW_CHUNK):
         y[r0:r0 + ROW_CHUNK] = dequantize_q4k(blob[r0:r0 + ROW_CHUNK]) @ xh
     return y
+
+
+def gemv_q4k_f32(blob: np.ndarray, x: np.ndarray):
+    """fp32 activation (realizar 0.8.5 ``src/cuda/executor/cached.rs``,
+    ``transformer_layer_gpu_cached`` steps 2 and 4: ``q4k_gemv_cached_async`` /
+    ``tiled_q4k_gemv_cached_async`` over the fp32 normed activation, no Q8_1).
+
+    Returns (y, terms) float64 (rows,).  ``y`` is the definition
+    ``sum_k w[r, k] * x[k]``.  ``terms`` counts the summands of the factored
+    form a kernel evaluates per sub-block, ``d * sc_j * sum_l q_l x_l -
+    dmin * m_j * sum_l x_l``: ``sum_{b,j} d sc_j sum_l |q_l x_l| + dmin m_j
+    sum_l |x_l|``.  It is never below ``sum_k |w[r, k] x[k]|``, so a direct
+    evaluation of the definition meets the same bound."""
+    x = np.asarray(x, np.float32).astype(np.float64)
+    nsb = blob.shape[1]
+    if x.shape[0] != nsb * QK_K:
+        raise ValueError("activation length must equal the padded in_dim")
+    assert np.all(np.isfinite(x))
+    rows = blob.shape[0]
+    y = np.empty(rows, np.float64)
+    terms = np.empty(rows, np.float64)
+    ax = np.abs(x).reshape(nsb, 8, QK8_1)
+    ax_sum = ax.sum(axis=2)                                     # (nsb, 8)
+    for r0 in range(0, rows, ROW_CHUNK):
+        part = blob[r0:r0 + ROW_CHUNK]
+        y[r0:r0 + ROW_CHUNK] = dequantize_q4k(part) @ x
+        d, dmin, sc, m, q = q4k_fields(part)
+        qx = np.einsum('rbjl,bjl->rbj', q, ax)                  # sum_l |q_l x_l| (q >= 0)
+        t = d[..., None] * sc * qx + dmin[..., None] * m * ax_sum[None]
+        terms[r0:r0 + ROW_CHUNK] = t.sum(axis=(1, 2))
+    return y, terms
 
 
 def gemv_q4k_q8_int(blob: np.ndarray, x: Q8Blocks, return_isum: bool = False):

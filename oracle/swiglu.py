@@ -23,7 +23,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .q4k import gemv_q4k_q8_int
+from .q4k import gemv_q4k_f32, gemv_q4k_q8_int
 from .q8_1 import quantize_q8_1
 from .tolerance import gemv_tolerance
 
@@ -79,4 +79,21 @@ def ffn_swiglu_q4k(w_gate, w_up, w_down, x_q8):
     y, ty = gemv_q4k_q8_int(w_down, h_q8)
     return dict(g=g, g_terms=tg, u=u, u_terms=tu, h=h, h32=h32, h_q8=h_q8,
                 y=y, y_terms=ty,
+                tol_g=gemv_tolerance(tg), tol_u=gemv_tolerance(tu))
+
+
+def ffn_swiglu_q4k_f32(w_gate, w_up, w_down, x):
+    """The chain on the fp32-activation path (realizar 0.8.5
+    ``src/cuda/executor/cached.rs``, ``transformer_layer_gpu_cached`` step 7,
+    ``fused_ffn_swiglu_gpu``; realizar 0.8.4 ``src/gpu/adapters/using.rs``,
+    ``ffn_swiglu_gpu``: gate and up GEMVs of the fp32 input, the fused SwiGLU,
+    then the down GEMV of its fp32 output).  No Q8_1 anywhere: h is rounded to
+    fp32 (its storage type) and is the down projection's activation.
+    Returns g, u (+ terms), h (float64), h32 (fp32), y (+ terms)."""
+    g, tg = gemv_q4k_f32(w_gate, x)
+    u, tu = gemv_q4k_f32(w_up, x)
+    h = swiglu(g, u)
+    h32 = h.astype(np.float32)
+    y, ty = gemv_q4k_f32(w_down, h32)
+    return dict(g=g, g_terms=tg, u=u, u_terms=tu, h=h, h32=h32, y=y, y_terms=ty,
                 tol_g=gemv_tolerance(tg), tol_u=gemv_tolerance(tu))

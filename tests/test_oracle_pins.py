@@ -164,6 +164,79 @@ def test_q4k_hand_worked_nibble_order():
     assert oracle.gemv_q4k_q8_def(blob, x)[0] == float(fx["y_onehot32"])
 
 
+def test_q4k_f32_hand_worked_superblock():
+    """fp32 activation of all ones: y and the factored-form terms as worked by hand."""
+    fx, blob = _fixture_superblock()
+    y, terms = oracle.gemv_q4k_f32(blob, np.ones(256, np.float32))
+    assert y[0] == float(fx["y_ones"])
+    assert terms[0] == float(fx["terms_f32_ones"])
+
+
+def test_q4k_f32_unit_vectors_pick_the_fixture_elements():
+    """x = e_k returns weight k of the super-block: the element order of the fp32
+    path against the hand-worked positions (an interleaved nibble order or an
+    off-by-one chunk fails here)."""
+    fx = load("q4k_nibble_order.txt")
+    raw = bytearray(hexbytes(fx["header_hex"]) + bytes(128))
+    for k, v in pairs(fx["qs_set"], int, lambda s: int(s, 16)):
+        raw[16 + k] = v
+    blob = np.frombuffer(bytes(raw), np.uint8).reshape(1, 1, 144).copy()
+    for idx, val in pairs(fx["w_at"]):
+        x = np.zeros(256, np.float32)
+        x[idx] = 1.0
+        assert oracle.gemv_q4k_f32(blob, x)[0][0] == val, idx
+    x = np.zeros(256, np.float32)
+    x[32] = 1.0
+    assert oracle.gemv_q4k_f32(blob, x)[0][0] == float(fx["y_onehot32"])
+
+
+@pytest.mark.parametrize("qn,S,M,v", [(3, 5, 9, 0.75), (15, 63, 63, -2.5), (0, 40, 17, 1.0),
+                                      (9, 18, 0, -0.125)])
+def test_q4k_f32_closed_form(qn, S, M, v):
+    """All nibbles qn, scales S, mins M, every activation value v:
+    y = in_dim * v * (d*S*qn - dmin*M) and terms = in_dim * |v| * (d*S*qn + dmin*M)."""
+    d, dmin, nsb = 0.0078125, 0.001953125, 3
+    sb = _f16le(d) + _f16le(dmin) + _pack_uniform_scales(S, M) + bytes([qn | (qn << 4)] * 128)
+    blob = np.frombuffer(sb * nsb, np.uint8).reshape(1, nsb, 144).copy()
+    y, terms = oracle.gemv_q4k_f32(blob, np.full(nsb * 256, v, np.float32))
+    n = nsb * 256
+    assert y[0] == pytest.approx(n * v * (d * S * qn - dmin * M), rel=1e-13, abs=1e-12)
+    assert terms[0] == pytest.approx(n * abs(v) * (d * S * qn + dmin * M), rel=1e-13)
+
+
+@pytest.mark.parametrize("out_dim,in_dim,seed", [(1, 256, 0), (7, 512, 1), (65, 1024, 2),
+                                                 (40, 4096, 3)])
+def test_q4k_f32_equals_integer_form_on_exact_activations(out_dim, in_dim, seed):
+    """x = D * q with D a power of two and int8 codes q is exact in fp32 and is
+    its own Q8_1 dequantization (d = D, s = D * sum q exactly): the fp32 path and
+    the integer form (exact int64 sums, separate code) must agree to float64
+    rounding.  Also terms >= sum |w x| >= |y|."""
+    g = np.random.default_rng(70 + seed)
+    blob = synth.q4k_weights(synth.rng(70 + seed, 1), out_dim, in_dim)
+    D = 2.0 ** -5
+    q = g.integers(-127, 128, (in_dim // 32, 32)).astype(np.int8)
+    x = (D * q.astype(np.float64)).astype(np.float32).reshape(-1)
+    xq = oracle.Q8Blocks(np.full(in_dim // 32, D, np.float32),
+                         (D * q.astype(np.int64).sum(axis=1)).astype(np.float32), q)
+    y, terms = oracle.gemv_q4k_f32(blob, x)
+    y_int, _ = oracle.gemv_q4k_q8_int(blob, xq)
+    assert np.all(np.abs(y - y_int) <= 1e-12 * terms)
+    direct = np.abs(oracle.dequantize_q4k(blob)) @ np.abs(x.astype(np.float64))
+    assert np.all(terms >= direct * (1 - 1e-12)) and np.all(direct >= np.abs(y) * (1 - 1e-12))
+
+
+def test_q4k_f32_padding_invariance():
+    """Zero activation values make their weights irrelevant, whatever the bytes."""
+    blob = synth.q4k_weights(synth.rng(75, 1), 33, 1024)
+    x = np.zeros(1024, np.float32)
+    x[:896] = synth.activation(synth.rng(75, 0), 896)
+    y1, t1 = oracle.gemv_q4k_f32(blob, x)
+    b2 = blob.copy()
+    b2[:, 3, 16 + 64:] = np.random.default_rng(3).integers(0, 256, (33, 64), dtype=np.uint8)
+    y2, t2 = oracle.gemv_q4k_f32(b2, x)
+    assert np.array_equal(y1, y2)
+
+
 @pytest.mark.parametrize("qn,S,M,Q,D", [(3, 5, 9, 7, 0.25), (15, 63, 63, -127, 0.5),
                                         (0, 40, 17, 100, 2.0), (9, 18, 0, -3, 1.0)])
 def test_q4k_closed_form(qn, S, M, Q, D):
@@ -339,6 +412,32 @@ def test_silu_grad_by_finite_difference():
     assert np.max(np.abs(oracle.silu_grad(dense))) <= SILU_GRAD_MAX
     curv = np.gradient(oracle.silu_grad(dense), dense)
     assert np.max(np.abs(curv)) <= SILU_CURV_MAX + 1e-6
+
+
+def _uniform_q4k(nsb, rows, qn, S, M, d=0.0078125, dmin=0.001953125):
+    sb = _f16le(d) + _f16le(dmin) + _pack_uniform_scales(S, M) + bytes([qn | (qn << 4)] * 128)
+    return np.frombuffer(sb * (nsb * rows), np.uint8).reshape(rows, nsb, 144).copy()
+
+
+def test_ffn_chain_f32_closed_form():
+    """Uniform gate, up and down matrices and a constant activation v: every g is
+    gw*H*v, every u is uw*H*v (gw, uw the uniform weights), h = silu(g)*u in
+    every row, and y = dw*I*fp32(h).  Gate and up differ, so swapping them (silu
+    on the up projection) changes h."""
+    H, I = 512, 768
+    wg = _uniform_q4k(H // 256, I, 11, 30, 7)
+    wu = _uniform_q4k(H // 256, I, 4, 9, 50)
+    wd = _uniform_q4k(I // 256, H, 6, 20, 12)
+    v = 2.0 ** -8                                            # g, u of order 1
+    d, dmin = 0.0078125, 0.001953125
+    gw, uw, dw = d * 30 * 11 - dmin * 7, d * 9 * 4 - dmin * 50, d * 20 * 6 - dmin * 12
+    g, u = gw * H * v, uw * H * v
+    h = g / (1.0 + np.exp(-g)) * u
+    assert abs(h - u / (1.0 + np.exp(-u)) * g) > 0.1          # the swap is visible
+    st = oracle.ffn_swiglu_q4k_f32(wg, wu, wd, np.full(H, v, np.float32))
+    assert np.allclose(st["g"], g, rtol=1e-13) and np.allclose(st["u"], u, rtol=1e-13)
+    assert np.allclose(st["h"], h, rtol=1e-13)
+    assert np.allclose(st["y"], dw * I * float(np.float32(h)), rtol=1e-13)
 
 
 def test_ffn_chain_zero_up_gives_zero():
