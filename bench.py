@@ -156,6 +156,12 @@ def time_rows(lib, rz, torch, dev, graph_time, copies, x, xq, y) -> dict:
                                                          IN_DIM, 1, s))),
         GEMV_ALGO_BYTES, W_BYTES, "rz_q4k_q8_gemv")
 
+    # the same GEMV on the fp32 activation, no Q8_1 (the non-quantized path)
+    rows["q4k_gemv_xf32_4096x14336"] = row_entry(
+        graph_time(lambda i, s: check(lib.rz_q4k_gemv(w_p[i % n_copies], x_p, IN_DIM, y_p,
+                                                      OUT_DIM, IN_DIM, s))),
+        W_BYTES + X_BYTES + Y_BYTES, W_BYTES, "rz_q4k_gemv (fp32 x)")
+
     # a8: 8 tokens, one weight pass
     x8 = torch.from_numpy(synth.activation(synth.rng(4, synth.T_ACT), IN_DIM, 8)).to(dev)
     xq8 = torch.empty(8 * XQ_BYTES, dtype=torch.uint8, device=dev)
@@ -242,6 +248,20 @@ def time_rows(lib, rz, torch, dev, graph_time, copies, x, xq, y) -> dict:
         graph_time(ffn_add_body),
         ffn_w + XQ_BYTES + 4 * INTER + 2 * q8_bytes(INTER) + 8 * IN_DIM, ffn_w,
         "rz_swiglu_ffn_q4k_add (the chain, then hidden += y in the down store)")
+    xf = torch.from_numpy(synth.activation(synth.rng(2, synth.T_ACT), IN_DIM)).to(dev)
+
+    def ffn_f32_body(i, s):
+        wg, wu, wd = ffn_p[i % len(ffn_p)]
+        check(lib.rz_swiglu_ffn_q4k_f32(wg, wu, wd, xf.data_ptr(), h.data_ptr(), yf.data_ptr(),
+                                        None, IN_DIM, INTER, s))
+
+    rows["swiglu_ffn_f32_4096_14336"] = row_entry(
+        graph_time(ffn_f32_body), ffn_w + 4 * IN_DIM + 2 * 4 * INTER + 4 * IN_DIM, ffn_w,
+        "rz_swiglu_ffn_q4k_f32 (fp32 x and h, no Q8_1)")
+    rows["q4k_gemv_xf32_down_14336x4096"] = row_entry(
+        graph_time(lambda i, s: check(lib.rz_q4k_gemv(ffn_p[i % len(ffn_p)][2], h.data_ptr(),
+                                                      INTER, yf.data_ptr(), IN_DIM, INTER, s))),
+        W_BYTES + 4 * INTER + 4 * IN_DIM, W_BYTES, "rz_q4k_gemv (fp32 x, in_dim 14336)")
     rows["q4k_gemv_down_14336x4096"] = row_entry(
         graph_time(lambda i, s: check(lib.rz_q4k_q8_gemv(ffn_p[i % len(ffn_p)][2], hq.data_ptr(),
                                                          yf.data_ptr(), IN_DIM, INTER, 1, s))),

@@ -171,6 +171,45 @@ int rz_q4k_q8_gemv_multi(int n_mats, const void* const* w_q4k, float* const* y,
 int rz_q4k_q8_gemv_f32(const void* w_q4k, const float* x, int n, void* x_q8, float* y,
                        int out_dim, int in_dim, void* stream);
 
+/* rz_q4k_gemv -- y = W x with W Q4_K and x fp32, no Q8_1 (one token).
+ * Passage: realizar 0.8.5 src/cuda/executor/cached.rs,
+ * transformer_layer_gpu_cached, steps 2 and 4 (q4k_gemv_cached_async and
+ * tiled_q4k_gemv_cached_async over the fp32 normed activation).
+ * Per 32-value sub-block j of super-block b, in fp32:
+ * y += d * (sc_j * sum(q * x)) - dmin * (m_j * sum(x)).
+ *   w_q4k    [out_dim][in_dim/256] super-blocks, 16-byte aligned, < 2 GiB
+ *   x        fp32 [n], 4-byte aligned; values n..in_dim-1 are taken as 0;
+ *            must not overlap y
+ *   n        1 <= n <= in_dim
+ *   y        out: fp32 [out_dim], 4-byte aligned
+ *   out_dim  >= 1; in_dim multiple of 256; both <= RZ_MAX_DIM (any in_dim:
+ *            rows longer than 4096 values are walked in column chunks inside
+ *            the one launch)
+ * Errors: RZ_EINVAL (also overlap), RZ_EDIM, RZ_EALIGN, RZ_ELAUNCH. */
+int rz_q4k_gemv(const void* w_q4k, const float* x, int n, float* y, int out_dim, int in_dim,
+                void* stream);
+
+/* rz_swiglu_ffn_q4k_f32 -- the SwiGLU FFN on fp32 activations, no Q8_1.
+ * Passages: realizar 0.8.5 src/cuda/executor/cached.rs,
+ * transformer_layer_gpu_cached step 7 (fused_ffn_swiglu_gpu); realizar 0.8.4
+ * src/gpu/adapters/using.rs, ffn_swiglu_gpu (gate and up GEMVs, the fused
+ * SwiGLU, the down GEMV of its output).
+ *   g = W_gate x, u = W_up x            (rz_q4k_gemv arithmetic)
+ *   h = silu(g) * u = g / (1 + exp(-g)) * u      (fp32)
+ *   y = W_down h                        (rz_q4k_gemv arithmetic, in_dim inter)
+ *   w_gate, w_up  [inter_dim][hidden_dim/256] super-blocks, 16-byte aligned
+ *   w_down        [hidden_dim][inter_dim/256] super-blocks, 16-byte aligned
+ *   x             fp32 [hidden_dim]
+ *   h             out: fp32 [inter_dim]
+ *   y             out: fp32 [hidden_dim] (may be x itself)
+ *   gu            optional out (NULL to skip): fp32 [2][inter_dim], g then u
+ *   hidden_dim, inter_dim  multiples of 256; each matrix < 2 GiB
+ * Two kernels run in order on `stream`.  x, h and gu must not overlap each
+ * other, nor h and y.  Errors: RZ_EINVAL, RZ_EDIM, RZ_EALIGN, RZ_ELAUNCH. */
+int rz_swiglu_ffn_q4k_f32(const void* w_gate, const void* w_up, const void* w_down,
+                          const float* x, float* h, float* y, float* gu, int hidden_dim,
+                          int inter_dim, void* stream);
+
 /* rz_q4_0_gemv -- y = W x with W Q4_0 and x fp32 or Q8_1 (the LM head).
  * Passage: realizar 0.8.4 src/gpu/adapters/using.rs, GpuModelQ4::forward
  * step 5 (q4_0_gemv_into(lm_head, normed, logits, vocab, hidden)).

@@ -21,7 +21,7 @@ __all__ = [
     "library_path", "load_library", "rz_last_error", "rz_abi_version",
     "rz_q8_1_quantize", "rz_rmsnorm_q8_1", "rz_q4k_q8_gemv", "rz_q4k_q8_gemv_add",
     "rz_q4k_q8_gemv_multi", "rz_q4k_q8_gemv_f32", "rz_q4_0_gemv", "rz_swiglu_ffn_q4k",
-    "rz_swiglu_ffn_q4k_add",
+    "rz_swiglu_ffn_q4k_add", "rz_q4k_gemv", "rz_swiglu_ffn_q4k_f32",
     "q8_1_nbytes", "RzError",
 ]
 
@@ -65,9 +65,12 @@ def load_library() -> ctypes.CDLL:
     lib.rz_q4_0_gemv.argtypes = [vp, vp, i, vp, i, i, vp]
     lib.rz_swiglu_ffn_q4k.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, vp]
     lib.rz_swiglu_ffn_q4k_add.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, vp]
+    lib.rz_q4k_gemv.argtypes = [vp, vp, i, vp, i, i, vp]
+    lib.rz_swiglu_ffn_q4k_f32.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, vp]
     for fn in ("rz_q8_1_quantize", "rz_rmsnorm_q8_1", "rz_q4k_q8_gemv", "rz_q4k_q8_gemv_add",
                "rz_q4k_q8_gemv_f32", "rz_q4k_q8_gemv_multi", "rz_q4_0_gemv", "rz_swiglu_ffn_q4k",
-               "rz_swiglu_ffn_q4k_add", "rz_abi_version"):
+               "rz_swiglu_ffn_q4k_add", "rz_q4k_gemv", "rz_swiglu_ffn_q4k_f32",
+               "rz_abi_version"):
         getattr(lib, fn).restype = i
     lib.rz_last_error.argtypes = []
     lib.rz_last_error.restype = ctypes.c_char_p
@@ -245,3 +248,30 @@ def rz_swiglu_ffn_q4k_add(w_gate, w_up, w_down, x_q8, h, h_q8, r, y, gu, hidden_
     _check(load_library().rz_swiglu_ffn_q4k_add(_ptr(w_gate), _ptr(w_up), _ptr(w_down),
                                                 _ptr(x_q8), _ptr(h), _ptr(h_q8), _ptr(r), _ptr(y),
                                                 _ptr(gu), hidden_dim, inter_dim, _stream(stream)))
+
+
+def rz_q4k_gemv(w_q4k, x, n: int, y, out_dim: int, in_dim: int, stream=None) -> None:
+    """y fp32 [out_dim] = W (Q4_K) x with x fp32 [n] (zero past n), no Q8_1."""
+    if in_dim > 0 and in_dim % 256 == 0 and out_dim > 0:
+        _need(w_q4k, out_dim * (in_dim // 256) * Q4K_BLOCK_BYTES, "w_q4k")
+        _need(x, 4 * n, "x")
+        _need(y, 4 * out_dim, "y")
+    _check(load_library().rz_q4k_gemv(_ptr(w_q4k), _ptr(x), n, _ptr(y), out_dim, in_dim,
+                                      _stream(stream)))
+
+
+def rz_swiglu_ffn_q4k_f32(w_gate, w_up, w_down, x, h, y, gu, hidden_dim: int, inter_dim: int,
+                          stream=None) -> None:
+    """SwiGLU FFN on fp32 activations: h = silu(W_gate x) * (W_up x), y = W_down h."""
+    if hidden_dim > 0 and inter_dim > 0 and hidden_dim % 256 == 0 and inter_dim % 256 == 0:
+        nw = inter_dim * (hidden_dim // 256) * Q4K_BLOCK_BYTES
+        _need(w_gate, nw, "w_gate")
+        _need(w_up, nw, "w_up")
+        _need(w_down, nw, "w_down")
+        _need(x, 4 * hidden_dim, "x")
+        _need(h, 4 * inter_dim, "h")
+        _need(y, 4 * hidden_dim, "y")
+        _need(gu, 8 * inter_dim, "gu")
+    _check(load_library().rz_swiglu_ffn_q4k_f32(_ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(x),
+                                                _ptr(h), _ptr(y), _ptr(gu), hidden_dim,
+                                                inter_dim, _stream(stream)))

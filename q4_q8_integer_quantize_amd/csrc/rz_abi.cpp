@@ -195,6 +195,54 @@ int rz_q4k_q8_gemv_f32(const void* w_q4k, const float* x, int n, void* x_q8, flo
                        what);
 }
 
+int rz_q4k_gemv(const void* w_q4k, const float* x, int n, float* y, int out_dim, int in_dim,
+                void* stream) {
+  const char* what = "rz_q4k_gemv";
+  if (!w_q4k || !x || !y) return fail(RZ_EINVAL, "%s: null pointer", what);
+  if (int rc = check_dim(what, "out_dim", out_dim, 1)) return rc;
+  if (int rc = check_dim(what, "in_dim", in_dim, 256)) return rc;
+  if (n <= 0 || n > in_dim)
+    return fail(RZ_EDIM, "%s: n=%d must satisfy 1 <= n <= in_dim=%d", what, n, in_dim);
+  if ((long long)out_dim * (in_dim / 256) * RZ_Q4K_BLOCK_BYTES > kMaxMatrixBytes)
+    return fail(RZ_EDIM, "%s: weight matrix larger than %lld bytes", what, kMaxMatrixBytes);
+  if (!aligned(w_q4k, 16)) return fail(RZ_EALIGN, "%s: w_q4k must be 16-byte aligned", what);
+  if (!aligned(x, 4) || !aligned(y, 4))
+    return fail(RZ_EALIGN, "%s: x and y must be 4-byte aligned", what);
+  if (!disjoint(x, 4LL * n, y, 4LL * out_dim))
+    return fail(RZ_EINVAL, "%s: x and y must not overlap", what);
+  return launch_status(rz::launch_q4k_gemv_xf32(static_cast<const uint8_t*>(w_q4k), x, n, y,
+                                                out_dim, in_dim, static_cast<hipStream_t>(stream)),
+                       what);
+}
+
+int rz_swiglu_ffn_q4k_f32(const void* w_gate, const void* w_up, const void* w_down,
+                          const float* x, float* h, float* y, float* gu, int hidden_dim,
+                          int inter_dim, void* stream) {
+  const char* what = "rz_swiglu_ffn_q4k_f32";
+  if (!w_gate || !w_up || !w_down || !x || !h || !y)
+    return fail(RZ_EINVAL, "%s: null pointer", what);
+  if (int rc = check_dim(what, "hidden_dim", hidden_dim, 256)) return rc;
+  if (int rc = check_dim(what, "inter_dim", inter_dim, 256)) return rc;
+  if ((long long)inter_dim * (hidden_dim / 256) * RZ_Q4K_BLOCK_BYTES > kMaxMatrixBytes)
+    return fail(RZ_EDIM, "%s: weight matrix larger than %lld bytes", what, kMaxMatrixBytes);
+  if (!aligned(w_gate, 16) || !aligned(w_up, 16) || !aligned(w_down, 16))
+    return fail(RZ_EALIGN, "%s: weight blobs must be 16-byte aligned", what);
+  if (!aligned(x, 4) || !aligned(h, 4) || !aligned(y, 4) || (gu && !aligned(gu, 4)))
+    return fail(RZ_EALIGN, "%s: fp32 buffers must be 4-byte aligned", what);
+  // x is read by the first kernel while it writes h and gu; h by the second while it writes y
+  if (!disjoint(x, 4LL * hidden_dim, h, 4LL * inter_dim) ||
+      (gu && (!disjoint(x, 4LL * hidden_dim, gu, 8LL * inter_dim) ||
+              !disjoint(h, 4LL * inter_dim, gu, 8LL * inter_dim))) ||
+      !disjoint(h, 4LL * inter_dim, y, 4LL * hidden_dim))
+    return fail(RZ_EINVAL, "%s: x, h, gu and y must not overlap (x and y may)", what);
+  return launch_status(
+      rz::launch_swiglu_ffn_q4k_xf32(static_cast<const uint8_t*>(w_gate),
+                                     static_cast<const uint8_t*>(w_up),
+                                     static_cast<const uint8_t*>(w_down), x, h, y, gu, hidden_dim,
+                                     inter_dim, static_cast<hipStream_t>(stream)),
+      what);
+}
+
 int rz_q4_0_gemv(const void* w_q4_0, const void* x, int x_format, float* y, int out_dim,
                  int in_dim, void* stream) {
   const char* what = "rz_q4_0_gemv";

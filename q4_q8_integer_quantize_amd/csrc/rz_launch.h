@@ -41,6 +41,15 @@ hipError_t launch_q4k_q8_gemv_multi(int n_mats, const uint8_t* const* w, float* 
 hipError_t launch_q4k_q8_gemv_f32(const uint8_t* w, const float* x, int n, uint8_t* xq_out,
                                   float* y, int out_dim, int in_dim, hipStream_t stream);
 
+// Q4_K times an fp32 activation without Q8_1 (1 token), and the SwiGLU FFN on
+// that path (gate/up with silu*up into h, then the down GEMV over fp32 h).
+hipError_t launch_q4k_gemv_xf32(const uint8_t* w, const float* x, int n, float* y, int out_dim,
+                                int in_dim, hipStream_t stream);
+hipError_t launch_swiglu_ffn_q4k_xf32(const uint8_t* w_gate, const uint8_t* w_up,
+                                      const uint8_t* w_down, const float* x, float* h, float* y,
+                                      float* gu, int hidden_dim, int inter_dim,
+                                      hipStream_t stream);
+
 hipError_t launch_q4_0_gemv(const uint8_t* w, const void* x, int x_format, float* y,
                             int out_dim, int in_dim, hipStream_t stream);
 

@@ -40,7 +40,8 @@ def test_header_declares_the_four_operations():
     syms = declared_symbols()
     for name in ("rz_q8_1_quantize", "rz_q4k_q8_gemv", "rz_q4k_q8_gemv_f32", "rz_q4_0_gemv",
                  "rz_swiglu_ffn_q4k", "rz_q4k_q8_gemv_multi", "rz_rmsnorm_q8_1",
-                 "rz_q4k_q8_gemv_add", "rz_swiglu_ffn_q4k_add", "rz_last_error",
+                 "rz_q4k_q8_gemv_add", "rz_swiglu_ffn_q4k_add", "rz_q4k_gemv",
+                 "rz_swiglu_ffn_q4k_f32", "rz_last_error",
                  "rz_abi_version"):
         assert name in syms
 
@@ -267,6 +268,49 @@ H = P + (2 << 30)
 def test_swiglu_ffn_add_rejects(lib, args, code):
     assert _rc("rz_swiglu_ffn_q4k_add", *args) == code
     assert _rc.last.startswith("rz_swiglu_ffn_q4k_add")
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, P, 4096, Y, 14336, 4096, None), rz.RZ_EINVAL),
+    ((P, None, 4096, Y, 14336, 4096, None), rz.RZ_EINVAL),
+    ((P, P, 4096, None, 14336, 4096, None), rz.RZ_EINVAL),
+    ((P, Y + 4, 4096, Y, 14336, 4096, None), rz.RZ_EINVAL),     # x overlaps y
+    ((P, P, 4097, Y, 14336, 4096, None), rz.RZ_EDIM),           # n > in_dim
+    ((P, P, 0, Y, 14336, 4096, None), rz.RZ_EDIM),
+    ((P, P, 896, Y, 14336, 896, None), rz.RZ_EDIM),             # unpadded in_dim
+    ((P, P, 4096, Y, 0, 4096, None), rz.RZ_EDIM),
+    ((P, P, 4096, Y, 1 << 20, 16384, None), rz.RZ_EDIM),        # matrix >= 2 GiB
+    ((P + 8, P, 4096, Y, 14336, 4096, None), rz.RZ_EALIGN),
+    ((P, P_ODD, 4096, Y, 14336, 4096, None), rz.RZ_EALIGN),
+    ((P, P, 4096, Y + 2, 14336, 4096, None), rz.RZ_EALIGN),
+])
+def test_q4k_gemv_rejects(lib, args, code):
+    assert _rc("rz_q4k_gemv", *args) == code
+    assert _rc.last.startswith("rz_q4k_gemv")
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, P, P, P, H, Y, None, 4096, 14336, None), rz.RZ_EINVAL),
+    ((P, P, P, None, H, Y, None, 4096, 14336, None), rz.RZ_EINVAL),
+    ((P, P, P, P, None, Y, None, 4096, 14336, None), rz.RZ_EINVAL),
+    ((P, P, P, H + 64, H, Y, None, 4096, 14336, None), rz.RZ_EINVAL),    # x overlaps h
+    ((P, P, P, P, H, H + 64, None, 4096, 14336, None), rz.RZ_EINVAL),    # y overlaps h
+    ((P, P, P, P, H, Y, H + 64, 4096, 14336, None), rz.RZ_EINVAL),       # gu overlaps h
+    ((P, P, P, P, H, Y, None, 4000, 14336, None), rz.RZ_EDIM),
+    ((P, P, P, P, H, Y, None, 4096, 14000, None), rz.RZ_EDIM),
+    ((P + 8, P, P, P, H, Y, None, 4096, 14336, None), rz.RZ_EALIGN),
+    ((P, P, P, P_ODD, H, Y, None, 4096, 14336, None), rz.RZ_EALIGN),
+    ((P, P, P, P, H, Y, P_ODD, 4096, 14336, None), rz.RZ_EALIGN),
+])
+def test_swiglu_ffn_f32_rejects(lib, args, code):
+    assert _rc("rz_swiglu_ffn_q4k_f32", *args) == code
+    assert _rc.last.startswith("rz_swiglu_ffn_q4k_f32")
+
+
+def test_swiglu_ffn_f32_accepts_y_on_x(lib):
+    (rc, _), = run_isolated([("rz_swiglu_ffn_q4k_f32", [P, P, P, Y, H, Y, None, 4096, 14336,
+                                                        None])])
+    assert rc == rz.RZ_ELAUNCH
 
 
 def test_error_message_is_per_call(lib):

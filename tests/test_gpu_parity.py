@@ -781,6 +781,144 @@ def test_swiglu_ffn_add():
         assert np.array_equal(host(y), (plain["y"] + r).astype(np.float32))
 
 
+# ------------------------------------------------------------------ Q4_K x fp32 activation
+def gpu_q4k_xf32(blob, x, n=None):
+    out_dim, nsb, _ = blob.shape
+    n = x.shape[0] if n is None else n
+    y = empty_f32(out_dim)
+    rz.rz_q4k_gemv(dev_bytes(blob), dev_f32(x[:n]), n, y, out_dim, nsb * 256)
+    return host(y)
+
+
+def _padded(x, in_dim):
+    xp = np.zeros(in_dim, np.float32)
+    xp[:x.shape[0]] = x
+    return xp
+
+
+@pytest.mark.parametrize("out_dim,n,in_dim", [
+    (1, 256, 256), (3, 200, 256), (64, 512, 512), (257, 1024, 1024), (300, 896, 1024),
+    (37, 2048, 2048), (100, 4096, 4096), (65, 5000, 5120), (33, 14335, 14336),
+    (8, 20480, 20480), (14336, 4096, 4096), (4096, 14336, 14336),
+])
+def test_q4k_gemv_xf32_matches_oracle(out_dim, n, in_dim):
+    """rz_q4k_gemv within 1e-5 * terms + 1e-6 of the float64 definition, terms
+    being the factored form's summands; one to five column chunks, ragged n
+    (16-byte and dword activation loads), the full gate and down shapes."""
+    banner("q4k_gemv_xf32", out_dim, n, in_dim)
+    cid = 80 + in_dim // 256
+    blob = synth.q4k_weights(synth.rng(cid, synth.T_W0), out_dim, in_dim)
+    x = synth.activation(synth.rng(cid, synth.T_ACT), n)
+    y = gpu_q4k_xf32(blob, x)
+    y_ref, terms = oracle.gemv_q4k_f32(blob, _padded(x, in_dim))
+    assert_within(y, y_ref, terms, "q4k_gemv fp32 x")
+
+
+@pytest.mark.parametrize("out_dim,in_dim", [(5, 256), (64, 1024), (300, 4096), (40, 14336)])
+def test_q4k_gemv_xf32_integer_exact_bit_exact(out_dim, in_dim):
+    """d = dmin = 1 and small integer activations: every product and partial sum
+    is an integer below 2**24, so the fp32 path must match the oracle exactly;
+    this pins the element order of the fp32 activation on the GPU."""
+    banner("q4k_gemv_xf32 integer", out_dim, in_dim)
+    blob = synth.q4k_weights(synth.rng(90, 1), out_dim, in_dim, d_fixed=1.0, dmin_fixed=1.0)
+    x = np.random.default_rng(91).integers(-8, 9, in_dim).astype(np.float32)
+    y = gpu_q4k_xf32(blob, x)
+    y_ref, _ = oracle.gemv_q4k_f32(blob, x)
+    assert np.all(np.abs(y_ref) < 2 ** 24)
+    mm = first_mismatch(y.astype(np.float64), y_ref)
+    assert mm is None, "row %s gpu=%r oracle=%r (%d rows differ)" % mm
+
+
+def test_q4k_gemv_xf32_padding_invariance():
+    """Values past n read as zero: the same y as an explicitly zero-padded x,
+    whatever the weight bytes in the padding hold."""
+    banner("q4k_gemv_xf32 padding")
+    blob = synth.q4k_weights(synth.rng(92, 1), 129, 1024)
+    x = synth.activation(synth.rng(92, 0), 896)
+    y1 = gpu_q4k_xf32(blob, x)
+    y2 = gpu_q4k_xf32(blob, _padded(x, 1024))
+    b2 = blob.copy()
+    b2[:, 3, 16 + 64:] = np.random.default_rng(7).integers(0, 256, (129, 64), dtype=np.uint8)
+    y3 = gpu_q4k_xf32(b2, x)
+    assert np.array_equal(y1, y2) and np.array_equal(y1, y3)
+
+
+def test_q4k_gemv_xf32_is_more_accurate_than_q8_1():
+    """The comparison the fp32 path exists for, at 4096 -> 14336 against the
+    float64 definition on the unquantized activation: the fp32 path is within
+    its rounding bound, the Q8_1 path carries the activation's quantization
+    error, which is far larger."""
+    banner("fp32 vs Q8_1 accuracy")
+    blob = synth.q4k_weights(synth.rng(2, synth.T_W0), 14336, 4096)
+    x = synth.activation(synth.rng(2, synth.T_ACT), 4096)
+    y_def, terms = oracle.gemv_q4k_f32(blob, x)
+    y32 = gpu_q4k_xf32(blob, x)
+    y8 = gpu_q4k(blob, gpu_quantize(x, 4096)[0])[0]
+    e32 = np.abs(y32 - y_def) / terms
+    e8 = np.abs(y8 - y_def) / terms
+    print("[accuracy] max |y - y_def| / terms: fp32 x %.3g, Q8_1 x %.3g; median %.3g / %.3g"
+          % (e32.max(), e8.max(), np.median(e32), np.median(e8)), flush=True)
+    assert e32.max() <= 1e-5 and e8.max() > 10 * e32.max()
+
+
+def run_ffn_f32(wg, wu, wd, x, hidden, inter, with_gu=True):
+    h = empty_f32(inter)
+    y = empty_f32(hidden)
+    gu = empty_f32(2 * inter) if with_gu else None
+    rz.rz_swiglu_ffn_q4k_f32(dev_bytes(wg), dev_bytes(wu), dev_bytes(wd), dev_f32(x), h, y, gu,
+                             hidden, inter)
+    out = dict(h=host(h), y=host(y))
+    if with_gu:
+        g_u = host(gu)
+        out["g"], out["u"] = g_u[:inter], g_u[inter:]
+    return out
+
+
+@pytest.mark.parametrize("hidden,inter", [(256, 512), (512, 768), (1024, 2816), (4096, 14336)])
+def test_swiglu_ffn_f32_chain(hidden, inter):
+    """Stage by stage, as for the Q8_1 chain: g and u within the GEMV bound; h
+    within the bound propagated through silu(g) * u; y bit-equal to rz_q4k_gemv
+    over the GPU's own h, the standalone down GEMV over the oracle's h within
+    the GEMV bound, and the chain's y within that bound plus |W| . |h_gpu - h|."""
+    banner("swiglu fp32", hidden, inter)
+    cid = 2 if (hidden, inter) == (4096, 14336) else 30 + hidden // 256
+    wg = synth.q4k_weights(synth.rng(cid, synth.T_W0), inter, hidden)
+    wu = synth.q4k_weights(synth.rng(cid, synth.T_W0 + 1), inter, hidden)
+    wd = synth.q4k_weights(synth.rng(cid, synth.T_W0 + 2), hidden, inter)
+    x = synth.activation(synth.rng(cid, synth.T_ACT), hidden)
+    st = oracle.ffn_swiglu_q4k_f32(wg, wu, wd, x)
+    got = run_ffn_f32(wg, wu, wd, x, hidden, inter)
+    assert_within(got["g"], st["g"], st["g_terms"], "gate")
+    assert_within(got["u"], st["u"], st["u_terms"], "up")
+    tol_h = oracle.h_tolerance(st["g"], st["u"], st["tol_g"], st["tol_u"], st["h"])
+    err_h = np.abs(got["h"].astype(np.float64) - st["h"])
+    assert np.all(err_h <= tol_h), "h: %d outside, worst ratio %.3g" % (
+        int((err_h > tol_h).sum()), float(np.max(err_h / tol_h)))
+    assert np.array_equal(got["y"], gpu_q4k_xf32(wd, got["h"]))
+    assert_within(gpu_q4k_xf32(wd, st["h32"]), st["y"], st["y_terms"], "down over oracle h")
+    w_abs = np.abs(oracle.dequantize_q4k(wd))
+    extra = w_abs @ np.abs(got["h"].astype(np.float64) - st["h32"].astype(np.float64))
+    assert_within(got["y"], st["y"], st["y_terms"] + extra / oracle.GEMV_REL, "chain y")
+
+
+def test_swiglu_ffn_f32_optional_gu_and_y_on_x():
+    """Skipping gu changes nothing, and y may overwrite x."""
+    banner("swiglu fp32 options")
+    hidden, inter = 1024, 2048
+    wg = synth.q4k_weights(synth.rng(33, 1), inter, hidden)
+    wu = synth.q4k_weights(synth.rng(33, 2), inter, hidden)
+    wd = synth.q4k_weights(synth.rng(33, 3), hidden, inter)
+    x = synth.activation(synth.rng(33, 0), hidden)
+    a = run_ffn_f32(wg, wu, wd, x, hidden, inter, with_gu=True)
+    b = run_ffn_f32(wg, wu, wd, x, hidden, inter, with_gu=False)
+    assert np.array_equal(a["h"], b["h"]) and np.array_equal(a["y"], b["y"])
+    xd = dev_f32(x)
+    h = empty_f32(inter)
+    rz.rz_swiglu_ffn_q4k_f32(dev_bytes(wg), dev_bytes(wu), dev_bytes(wd), xd, h, xd, None,
+                             hidden, inter)
+    assert np.array_equal(host(xd), a["y"])
+
+
 # ------------------------------------------------------------------ errors on device tensors
 def test_binding_errors_on_gpu():
     banner("binding errors")
