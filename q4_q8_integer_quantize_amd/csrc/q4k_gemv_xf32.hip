@@ -90,6 +90,16 @@ __device__ __forceinline__ void request_x(XF32Slots<S>& xs, __amdgpu_buffer_rsrc
 
 __device__ __forceinline__ float xor1_f(float v) { return dpp_f<0xB1>(v); }
 
+// v & m, opaque to the compiler's known-bits analysis.  With the nibble mask
+// visible, the byte conversions below fold into a 4-bit extract followed by a
+// byte-0 conversion (two instructions per weight); behind this AND each byte
+// converts with one v_cvt_f32_ubyte{0..3}.
+__device__ __forceinline__ uint32_t opaque_and(uint32_t v, uint32_t m) {
+  uint32_t r;
+  asm("v_and_b32 %0, %1, %2" : "=v"(r) : "v"(v), "v"(m));
+  return r;
+}
+
 // Sum of 16 values as a fixed tree.
 __device__ __forceinline__ float sum16(const float (&v)[16]) {
   float a[8];
@@ -130,20 +140,20 @@ __device__ __forceinline__ void tile_dot_xf32(float (&part)[R], const WTile<S, R
                            __builtin_amdgcn_ubfe(a_sc, ro.sh_sc, ro.len_lo));
       const int m = (int)((__builtin_amdgcn_ubfe(H.z, ro.sh_hi, ro.len_hi) << 4) |
                           __builtin_amdgcn_ubfe(a_m, ro.sh_m, ro.len_lo));
-      // four partial sums per half keep the fma chains short
-      float pl[4] = {0.0f, 0.0f, 0.0f, 0.0f}, ph[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      // two partial sums per half (even and odd bytes)
+      float pl[2] = {0.0f, 0.0f}, ph[2] = {0.0f, 0.0f};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const uint32_t lo = wt.qs[r][s][k] & 0x0F0F0F0Fu;
-        const uint32_t hi = (wt.qs[r][s][k] >> 4) & 0x0F0F0F0Fu;
+        const uint32_t lo = opaque_and(wt.qs[r][s][k], 0x0F0F0F0Fu);
+        const uint32_t hi = opaque_and(wt.qs[r][s][k] >> 4, 0x0F0F0F0Fu);
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-          pl[b] = fmaf((float)((lo >> (8 * b)) & 0xffu), xs.lo[s][4 * k + b], pl[b]);
-          ph[b] = fmaf((float)((hi >> (8 * b)) & 0xffu), xs.hi[s][4 * k + b], ph[b]);
+          pl[b & 1] = fmaf((float)((lo >> (8 * b)) & 0xffu), xs.lo[s][4 * k + b], pl[b & 1]);
+          ph[b & 1] = fmaf((float)((hi >> (8 * b)) & 0xffu), xs.hi[s][4 * k + b], ph[b & 1]);
         }
       }
-      const float sl = (pl[0] + pl[1]) + (pl[2] + pl[3]);
-      const float sh = (ph[0] + ph[1]) + (ph[2] + ph[3]);
+      const float sl = pl[0] + pl[1];
+      const float sh = ph[0] + ph[1];
       const float keep = ro.h ? sh : sl;
       const float send = ro.h ? sl : sh;
       const float qx = keep + xor1_f(send);
@@ -256,10 +266,12 @@ static hipError_t launch_xf32_g(const XF32Args& a, long groups, hipStream_t st) 
 }
 
 // Steps per wave: the smallest power of two (at most 8) that keeps the grid at
-// about one wave per SIMD.
+// about one wave per SIMD.  Rows per group: two for the one-slot window, one
+// for the two-slot window (measured at 4096 -> 14336: 9.9 us against 11.0 for
+// two rows, whose extra tile registers cost occupancy).
 template <int TPR, int S, bool SWI>
 static hipError_t run_xf32(const XF32Args& a, hipStream_t st) {
-  constexpr int R = S <= 2 ? 2 : 1;
+  constexpr int R = S == 1 ? 2 : 1;
   constexpr long rows_per_group = (long)(8 / TPR) * R;
   const long groups = (a.out_dim + rows_per_group - 1) / rows_per_group;
   const long steps = SWI ? 2 * groups : groups;
