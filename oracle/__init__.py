@@ -22,6 +22,10 @@ source pages (docs.rs, realizar 0.8.4/0.8.5):
   8 and 10: the RMSNorm before the quantize and the residual adds after the O
   projection and the FFN.
 
+* ``cached.rs``, ``preload_lm_head_bias`` and ``dispatch_lm_head_and_download``:
+  the LM head's output bias and the logits it produces (the greedy token is the
+  index of the largest logit).
+
 The block formats are not printed on the pages; the GGML layouts the pages name
 (Q4_K super-blocks of 256 values, type id 12; Q4_0; Q8_1) are read as written in
 each module's docstring.
@@ -43,6 +47,7 @@ from .swiglu import (silu, silu_grad, swiglu, ffn_swiglu_q4k, ffn_swiglu_q4k_f32
                      h_tolerance)
 from .tolerance import gemv_tolerance, GEMV_REL, GEMV_ABS
 from .norm import rmsnorm, rmsnorm_tolerance, residual_add
+from .lm_head import lm_head_q4_0, argmax_first
 
 __all__ = [
     "QK8_1", "Q8_1_BLOCK_BYTES", "quantize_q8_1", "q8_1_to_bytes", "q8_1_from_bytes",
@@ -53,4 +58,5 @@ __all__ = [
     "silu", "silu_grad", "swiglu", "ffn_swiglu_q4k", "ffn_swiglu_q4k_f32", "h_tolerance",
     "gemv_tolerance", "GEMV_REL", "GEMV_ABS",
     "rmsnorm", "rmsnorm_tolerance", "residual_add",
+    "lm_head_q4_0", "argmax_first",
 ]

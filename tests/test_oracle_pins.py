@@ -568,3 +568,37 @@ def test_rmsnorm_tolerance_rejects_planted_mistakes():
 def test_residual_add():
     r = np.array([1.0, -2.0, 0.5])
     assert np.array_equal(oracle.residual_add(r, np.array([0.25, 2.0, -0.5])), [1.25, 0.0, 0.0])
+
+
+# ----------------------------------------------------------------- LM head
+def test_argmax_first_tie_rule_and_special_cases():
+    assert oracle.argmax_first([1.0]) == 0
+    assert oracle.argmax_first([3.0, 7.0, 7.0, -1.0]) == 1          # first of equal maxima
+    assert oracle.argmax_first([-5.0, -2.0, -3.0]) == 1              # all negative
+    assert oracle.argmax_first([0.0, -0.0, 0.0]) == 0                # signed zeros are equal
+    assert oracle.argmax_first([-0.0, 0.0]) == 0
+    assert oracle.argmax_first(np.full(17, 2.5)) == 0
+    assert oracle.argmax_first([1.0, 2.0, 3.0, 3.0000002]) == 3
+
+
+def test_argmax_first_matches_numpy_on_random_ties():
+    g = np.random.default_rng(1)
+    for _ in range(50):
+        v = g.integers(-3, 4, g.integers(1, 40)).astype(np.float32)   # many ties
+        assert oracle.argmax_first(v) == int(np.argmax(v))
+
+
+def test_lm_head_bias_closed_form():
+    """Uniform Q4_0 weights w and activation v give v*in_dim*w in every row; the
+    bias shifts each row by its own value, and it moves the greedy token."""
+    d, qn, in_dim, rows = 0.0078125, 11, 128, 5
+    blk = np.array([d], np.float16).tobytes() + bytes([qn | (qn << 4)] * 16)
+    blob = np.frombuffer(blk * (rows * in_dim // 32), np.uint8).reshape(rows, in_dim // 32, 18).copy()
+    x = np.full(in_dim, 0.5, np.float32)
+    base = 0.5 * in_dim * (qn - 8) * d
+    bias = np.array([0.0, 1.0, -1.0, 2.0, 1.5], np.float32)
+    y, terms = oracle.lm_head_q4_0(blob, x, bias)
+    assert np.allclose(y, base + bias.astype(np.float64), rtol=0, atol=1e-12)
+    y0, t0 = oracle.lm_head_q4_0(blob, x)
+    assert np.allclose(terms - t0, np.abs(bias.astype(np.float64)), rtol=0, atol=1e-12)
+    assert oracle.argmax_first(y0) == 0 and oracle.argmax_first(y) == 3
