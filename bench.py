@@ -285,6 +285,21 @@ def time_rows(lib, rz, torch, dev, graph_time, copies, x, xq, y) -> dict:
             graph_time(lambda i, s: check(lib.rz_q4_0_gemv(lm_p[i % len(lm_p)], xp, fmt,
                                                            logits.data_ptr(), VOCAB, HID_P, s))),
             lm_w + xbytes + 4 * VOCAB, lm_w, "rz_q4_0_gemv x_format=%d" % fmt)
+    # the same with the output bias and the greedy token (two kernels: the GEMV
+    # with its epilogue, then the merge of the per-workgroup pairs)
+    lm_bias = torch.from_numpy(synth.activation(synth.rng(3, 8), VOCAB)).to(dev)
+    am_idx = torch.zeros(1, dtype=torch.int32, device=dev)
+    am_val = torch.zeros(1, dtype=torch.float32, device=dev)
+    for fmt, xp, xbytes, name in ((0, xl.data_ptr(), 4 * HID_P, "fp32"),
+                                  (1, xlq.data_ptr(), q8_bytes(HID_P), "q8_1")):
+        ws_bytes = lib.rz_lm_head_q4_0_workspace_bytes(VOCAB, HID_P, fmt)
+        ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
+        rows["q4_0_lm_head_bias_argmax_151936x1024_%s" % name] = row_entry(
+            graph_time(lambda i, s: check(lib.rz_lm_head_q4_0(
+                lm_p[i % len(lm_p)], xp, fmt, lm_bias.data_ptr(), logits.data_ptr(), VOCAB,
+                HID_P, am_idx.data_ptr(), am_val.data_ptr(), ws.data_ptr(), ws_bytes, s))),
+            lm_w + xbytes + 8 * VOCAB, lm_w,
+            "rz_lm_head_q4_0 x_format=%d (bias + argmax epilogue, merge kernel)" % fmt)
     del lm
 
     # the small case: 896 x (896 -> 1024), launch-bound

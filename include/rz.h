@@ -36,6 +36,8 @@
 #ifndef RZ_H
 #define RZ_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -222,6 +224,38 @@ int rz_swiglu_ffn_q4k_f32(const void* w_gate, const void* w_up, const void* w_do
  * Errors: RZ_EINVAL (also unknown x_format), RZ_EDIM, RZ_EALIGN, RZ_ELAUNCH. */
 int rz_q4_0_gemv(const void* w_q4_0, const void* x, int x_format, float* y,
                  int out_dim, int in_dim, void* stream);
+
+/* rz_lm_head_q4_0 -- the LM head: Q4_0 GEMV, output bias, greedy token.
+ * Passages: realizar 0.8.4 src/gpu/adapters/using.rs, GpuModelQ4::forward
+ * step 5 (the Q4_0 LM-head GEMV); realizar 0.8.5 src/cuda/executor/cached.rs,
+ * preload_lm_head_bias (an output bias of vocab values added to the logits
+ * after the GEMV) and dispatch_lm_head_and_download (the logits go to the
+ * host, where the next token is chosen).
+ *   logits = fl32(W x + bias), W x as rz_q4_0_gemv computes it (bit for bit
+ *   when bias is NULL).  With argmax_idx and/or argmax_val, the index of the
+ *   largest logit (the smallest index among equal largest values) and that
+ *   logit: each workgroup reduces its rows in the GEMV's epilogue and one
+ *   small kernel merges the pairs, so a greedy step reads back 4 bytes
+ *   instead of 4 * out_dim.
+ *   w_q4_0, x, x_format, out_dim, in_dim: as for rz_q4_0_gemv
+ *   bias        optional [out_dim] fp32 (NULL: none), 4-byte aligned; may be
+ *               logits itself, must not overlap it otherwise
+ *   logits      out: fp32 [out_dim], 4-byte aligned
+ *   argmax_idx  optional out: int32 [1]; argmax_val optional out: fp32 [1]
+ *   workspace   with an argmax output: device memory of at least
+ *               rz_lm_head_q4_0_workspace_bytes(out_dim, in_dim, x_format)
+ *               bytes, 4-byte aligned, not overlapping logits, bias or the
+ *               argmax outputs; its contents on entry do not matter
+ * Finite logits are assumed (a NaN never ranks as the largest).
+ * Errors: RZ_EINVAL (also a short workspace or overlaps), RZ_EDIM,
+ * RZ_EALIGN, RZ_ELAUNCH. */
+int rz_lm_head_q4_0(const void* w_q4_0, const void* x, int x_format, const float* bias,
+                    float* logits, int out_dim, int in_dim, int* argmax_idx, float* argmax_val,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace rz_lm_head_q4_0 needs for its argmax (0 for arguments it
+ * would reject). */
+size_t rz_lm_head_q4_0_workspace_bytes(int out_dim, int in_dim, int x_format);
 
 /* rz_swiglu_ffn_q4k -- the SwiGLU FFN on the integer path.
  * Passages: realizar 0.8.5 src/cuda/executor/cached.rs,

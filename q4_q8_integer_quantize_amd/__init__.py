@@ -22,6 +22,7 @@ __all__ = [
     "rz_q8_1_quantize", "rz_rmsnorm_q8_1", "rz_q4k_q8_gemv", "rz_q4k_q8_gemv_add",
     "rz_q4k_q8_gemv_multi", "rz_q4k_q8_gemv_f32", "rz_q4_0_gemv", "rz_swiglu_ffn_q4k",
     "rz_swiglu_ffn_q4k_add", "rz_q4k_gemv", "rz_swiglu_ffn_q4k_f32",
+    "rz_lm_head_q4_0", "rz_lm_head_q4_0_workspace_bytes",
     "q8_1_nbytes", "RzError",
 ]
 
@@ -67,10 +68,13 @@ def load_library() -> ctypes.CDLL:
     lib.rz_swiglu_ffn_q4k_add.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, vp]
     lib.rz_q4k_gemv.argtypes = [vp, vp, i, vp, i, i, vp]
     lib.rz_swiglu_ffn_q4k_f32.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, vp]
+    lib.rz_lm_head_q4_0.argtypes = [vp, vp, i, vp, vp, i, i, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.rz_lm_head_q4_0_workspace_bytes.argtypes = [i, i, i]
+    lib.rz_lm_head_q4_0_workspace_bytes.restype = ctypes.c_size_t
     for fn in ("rz_q8_1_quantize", "rz_rmsnorm_q8_1", "rz_q4k_q8_gemv", "rz_q4k_q8_gemv_add",
                "rz_q4k_q8_gemv_f32", "rz_q4k_q8_gemv_multi", "rz_q4_0_gemv", "rz_swiglu_ffn_q4k",
                "rz_swiglu_ffn_q4k_add", "rz_q4k_gemv", "rz_swiglu_ffn_q4k_f32",
-               "rz_abi_version"):
+               "rz_lm_head_q4_0", "rz_abi_version"):
         getattr(lib, fn).restype = i
     lib.rz_last_error.argtypes = []
     lib.rz_last_error.restype = ctypes.c_char_p
@@ -275,3 +279,30 @@ def rz_swiglu_ffn_q4k_f32(w_gate, w_up, w_down, x, h, y, gu, hidden_dim: int, in
     _check(load_library().rz_swiglu_ffn_q4k_f32(_ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(x),
                                                 _ptr(h), _ptr(y), _ptr(gu), hidden_dim,
                                                 inter_dim, _stream(stream)))
+
+
+def rz_lm_head_q4_0_workspace_bytes(out_dim: int, in_dim: int, x_format: int) -> int:
+    """Workspace bytes rz_lm_head_q4_0 needs for its argmax (0 for bad arguments)."""
+    return int(load_library().rz_lm_head_q4_0_workspace_bytes(out_dim, in_dim, x_format))
+
+
+def rz_lm_head_q4_0(w_q4_0, x, x_format: int, bias, logits, out_dim: int, in_dim: int,
+                    argmax_idx=None, argmax_val=None, workspace=None, stream=None) -> None:
+    """logits fp32 [out_dim] = W (Q4_0) x + bias (bias may be None); with
+    argmax_idx (int32 [1]) and/or argmax_val (fp32 [1]) also the index and value
+    of the largest logit (smallest index on ties), using `workspace` (device
+    bytes, rz_lm_head_q4_0_workspace_bytes of them)."""
+    if in_dim > 0 and in_dim % 64 == 0 and out_dim > 0 and x_format in (0, 1):
+        _need(w_q4_0, out_dim * (in_dim // 32) * Q4_0_BLOCK_BYTES, "w_q4_0")
+        _need(x, 4 * in_dim if x_format == 0 else q8_1_nbytes(in_dim), "x")
+        _need(bias, 4 * out_dim, "bias")
+        _need(logits, 4 * out_dim, "logits")
+        _need(argmax_idx, 4, "argmax_idx")
+        _need(argmax_val, 4, "argmax_val")
+    ws_bytes = 0
+    if workspace is not None and not isinstance(workspace, int):
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load_library().rz_lm_head_q4_0(_ptr(w_q4_0), _ptr(x), x_format, _ptr(bias),
+                                          _ptr(logits), out_dim, in_dim, _ptr(argmax_idx),
+                                          _ptr(argmax_val), _ptr(workspace), ws_bytes,
+                                          _stream(stream)))

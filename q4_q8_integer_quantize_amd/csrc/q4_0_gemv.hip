@@ -12,6 +12,15 @@
 // and each wave streams G row groups with P of them requested ahead.
 //   fp32 x : sum_l q_l x_l per block, then d * (sum - 8 * sum_l x_l)
 //   Q8_1 x : isum = sum_l q_l q8_l - 8 * sum_l q8_l (exact), then d * d_x * isum
+//
+// LM-head epilogue (EPI, the launch that completes the rows): the output bias
+// is added in the store, logits = fl32(W x + bias) (realizar 0.8.5
+// src/cuda/executor/cached.rs, preload_lm_head_bias: the bias is added to the
+// logits after the LM-head GEMV), and each workgroup reduces its rows to one
+// (value, index) pair, the largest logit with the smallest index on ties.
+// argmax_merge_kernel then reduces the pairs, so a greedy step downloads one
+// index instead of vocab logits (dispatch_lm_head_and_download brings all of
+// them to the host).
 #include "rz_device.h"
 #include "rz_launch.h"
 
@@ -26,6 +35,10 @@ struct Q40Args {
   int p0;           // first pair of this column chunk
   int npairs;       // pairs in this chunk
   int accumulate;
+  const float* bias;  // EPI: optional [out_dim] output bias
+  float* part_val;    // EPI: optional [grid] per-workgroup best logit
+  int* part_idx;      //      and its row
+  long part_count;    // EPI with pairs: the grid the pairs were sized for
 };
 
 template <int S, bool Q8>
@@ -163,9 +176,30 @@ __device__ __forceinline__ void load_q40_tile(Q40Tile<S, R>& t, const Q40Args& a
   }
 }
 
+// (v, i) ranks above (bv, bi): a larger value, or an equal value at a smaller
+// index.  Every pair compares, so the reduction's result is unique.
+__device__ __forceinline__ bool ranks_above(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+// Best pair over the wave, in every lane.
+__device__ __forceinline__ void wave_best(float& bv, int& bi) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float ov = __shfl_xor(bv, off);
+    const int oi = __shfl_xor(bi, off);
+    if (ranks_above(ov, oi, bv, bi)) {
+      bv = ov;
+      bi = oi;
+    }
+  }
+}
+
+constexpr int kNoRow = 0x7fffffff;
+
 // Wave w of W takes the G row groups w, w+W, ... (a group is RW*R rows),
 // unrolled with P groups requested ahead, as in q4k_q8_gemv_kernel.
-template <int LPR, int S, int R, int G, int P, bool Q8, bool ACC>
+template <int LPR, int S, int R, int G, int P, bool Q8, bool ACC, bool EPI>
 __global__ __launch_bounds__(256) void q4_0_gemv_kernel(Q40Args a) {
   constexpr int RW = kWave / LPR;
   const int lane = threadIdx.x & (kWave - 1);
@@ -175,15 +209,38 @@ __global__ __launch_bounds__(256) void q4_0_gemv_kernel(Q40Args a) {
   const size_t row_bytes = (size_t)a.npairs_row * 36;
   X40<S, Q8> xs;
   load_x40<LPR, S, Q8>(xs, a, ps);
+  // EPI: the bias of a group's rows is requested right after its weight tile
+  // (a null bias reads as an empty buffer and is not added)
+  const bool has_bias = EPI && a.bias != nullptr;
+  const uint32_t bias_bytes = has_bias ? (uint32_t)a.out_dim * 4u : 0u;
+  const __amdgpu_buffer_rsrc_t br =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.bias, (short)0, (int)bias_bytes, kBufferWord3);
+  float bv[G][R];
+  auto load_bias = [&](int k) {
+    if constexpr (EPI) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const long row = (wid + k * nwaves) * (RW * R) + (long)r * RW + rs;
+        const uint32_t off = row < a.out_dim ? (uint32_t)row * 4u : bias_bytes;
+        bv[k][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(br, off, 0, 0));
+      }
+    }
+  };
+  float best_v = -__builtin_inff();
+  int best_i = kNoRow;
   Q40Tile<S, R> t[G];
 #pragma unroll
-  for (int k = 0; k < P && k < G; ++k)
+  for (int k = 0; k < P && k < G; ++k) {
     load_q40_tile<LPR, S, R>(t[k], a, (wid + k * nwaves) * (RW * R), rs, ps, row_bytes);
+    load_bias(k);
+  }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int k = 0; k < G; ++k) {
-    if (k + P < G)
+    if (k + P < G) {
       load_q40_tile<LPR, S, R>(t[k + P], a, (wid + (k + P) * nwaves) * (RW * R), rs, ps, row_bytes);
+      load_bias(k + P);
+    }
     __builtin_amdgcn_sched_barrier(0);
     const long row_base = (wid + k * nwaves) * (RW * R);
     float acc[R];
@@ -217,9 +274,78 @@ __global__ __launch_bounds__(256) void q4_0_gemv_kernel(Q40Args a) {
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const long row = row_base + (long)r * RW + rs;
-        if (row < a.out_dim) a.y[row] = ACC ? a.y[row] + acc[r] : acc[r];
+        if (row < a.out_dim) {
+          float v = ACC ? a.y[row] + acc[r] : acc[r];
+          if constexpr (EPI) {
+            if (has_bias) v = v + bv[k][r];
+            if (ranks_above(v, (int)row, best_v, best_i)) {
+              best_v = v;
+              best_i = (int)row;
+            }
+          }
+          a.y[row] = v;
+        }
       }
     }
+  }
+  if constexpr (EPI) {
+    if (a.part_val != nullptr) {
+      __shared__ float wv[4];
+      __shared__ int wi[4];
+      wave_best(best_v, best_i);
+      const int wave = threadIdx.x >> 6;
+      if (lane == 0) {
+        wv[wave] = best_v;
+        wi[wave] = best_i;
+      }
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        float v = wv[0];
+        int i = wi[0];
+#pragma unroll
+        for (int w = 1; w < 4; ++w)
+          if (ranks_above(wv[w], wi[w], v, i)) {
+            v = wv[w];
+            i = wi[w];
+          }
+        a.part_val[blockIdx.x] = v;
+        a.part_idx[blockIdx.x] = i;
+      }
+    }
+  }
+}
+
+// The best of `count` (value, index) pairs; one workgroup of 1024 threads.
+__global__ __launch_bounds__(1024) void argmax_merge_kernel(const float* __restrict__ pv,
+                                                            const int* __restrict__ pi, int count,
+                                                            int* __restrict__ out_idx,
+                                                            float* __restrict__ out_val) {
+  __shared__ float wv[16];
+  __shared__ int wi[16];
+  float bv = -__builtin_inff();
+  int bi = kNoRow;
+  for (int j = (int)threadIdx.x; j < count; j += 1024)
+    if (ranks_above(pv[j], pi[j], bv, bi)) {
+      bv = pv[j];
+      bi = pi[j];
+    }
+  wave_best(bv, bi);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    wv[wave] = bv;
+    wi[wave] = bi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float v = wv[0];
+    int i = wi[0];
+    for (int w = 1; w < 16; ++w)
+      if (ranks_above(wv[w], wi[w], v, i)) {
+        v = wv[w];
+        i = wi[w];
+      }
+    if (out_idx) *out_idx = i;
+    if (out_val) *out_val = v;
   }
 }
 
@@ -227,14 +353,21 @@ template <bool Q8>
 constexpr int pair_slots_max() { return Q8 ? 4 : 2; }
 
 template <int LPR, int S, int R, int G, bool Q8>
-static hipError_t launch_q40_g(const Q40Args& a, long groups, hipStream_t st) {
+static hipError_t launch_q40_g(const Q40Args& a, long groups, bool epi, hipStream_t st) {
   constexpr int P = G > 2 ? 2 : (G > 1 ? G - 1 : 1);
   const long waves = (groups + G - 1) / G;
   const unsigned grid = (unsigned)((waves + 3) / 4);
-  if (a.accumulate)
-    hipLaunchKernelGGL((q4_0_gemv_kernel<LPR, S, R, G, P, Q8, true>), dim3(grid), dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL((q4_0_gemv_kernel<LPR, S, R, G, P, Q8, false>), dim3(grid), dim3(256), 0, st, a);
+  if (epi && a.part_val != nullptr && (long)grid != a.part_count) return hipErrorInvalidValue;
+  if (epi) {
+    if (a.accumulate)
+      hipLaunchKernelGGL((q4_0_gemv_kernel<LPR, S, R, G, P, Q8, true, true>), dim3(grid), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((q4_0_gemv_kernel<LPR, S, R, G, P, Q8, false, true>), dim3(grid), dim3(256), 0, st, a);
+  } else if (a.accumulate) {
+    hipLaunchKernelGGL((q4_0_gemv_kernel<LPR, S, R, G, P, Q8, true, false>), dim3(grid), dim3(256), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((q4_0_gemv_kernel<LPR, S, R, G, P, Q8, false, false>), dim3(grid), dim3(256), 0, st, a);
+  }
   return hipGetLastError();
 }
 
@@ -242,49 +375,71 @@ static hipError_t launch_q40_g(const Q40Args& a, long groups, hipStream_t st) {
 // (latency hidden by occupancy); the fp32 form, whose arithmetic is heavier,
 // with two groups per wave once there are enough rows (measured on the
 // 151936 x 1024 LM head: 16.6 us and 23.9 us).
+// Rows per group and groups per wave of a chunk of np pairs (the launch shape
+// that run_q40 takes; q40_grid uses it to size the per-workgroup pairs).
+struct Q40Shape {
+  int lpr, s, r, g;
+};
+
+static Q40Shape q40_shape(int np, long out_dim, bool q8) {
+  Q40Shape sh;
+  if (np <= 32) {
+    sh.lpr = np <= 1 ? 1 : np <= 2 ? 2 : np <= 4 ? 4 : np <= 8 ? 8 : np <= 16 ? 16 : 32;
+    sh.s = 1;
+  } else {
+    sh.lpr = 64;
+    sh.s = (np + 63) / 64;
+  }
+  sh.r = sh.s >= 4 ? 1 : 4 / sh.s;
+  const long groups = (out_dim + (long)(kWave / sh.lpr) * sh.r - 1) / ((long)(kWave / sh.lpr) * sh.r);
+  sh.g = (!q8 && groups >= 2048) ? 2 : 1;
+  return sh;
+}
+
 template <int LPR, int S, bool Q8>
-static hipError_t run_q40(const Q40Args& a, hipStream_t st) {
+static hipError_t run_q40(const Q40Args& a, bool epi, hipStream_t st) {
   constexpr int R = S >= 4 ? 1 : 4 / S;
   constexpr int RW = kWave / LPR;
   const long rows_per_group = (long)RW * R;
   const long groups = (a.out_dim + rows_per_group - 1) / rows_per_group;
-  if (!Q8 && groups >= 2048) return launch_q40_g<LPR, S, R, 2, Q8>(a, groups, st);
-  return launch_q40_g<LPR, S, R, 1, Q8>(a, groups, st);
+  // Groups per wave as in q40_shape.
+  if (!Q8 && groups >= 2048) return launch_q40_g<LPR, S, R, 2, Q8>(a, groups, epi, st);
+  return launch_q40_g<LPR, S, R, 1, Q8>(a, groups, epi, st);
 }
 
 template <bool Q8>
-static hipError_t run_q40_chunk(const Q40Args& a, hipStream_t st) {
+static hipError_t run_q40_chunk(const Q40Args& a, bool epi, hipStream_t st) {
   const int np = a.npairs;
-  if (np <= 1) return run_q40<1, 1, Q8>(a, st);
-  if (np <= 2) return run_q40<2, 1, Q8>(a, st);
-  if (np <= 4) return run_q40<4, 1, Q8>(a, st);
-  if (np <= 8) return run_q40<8, 1, Q8>(a, st);
-  if (np <= 16) return run_q40<16, 1, Q8>(a, st);
-  if (np <= 32) return run_q40<32, 1, Q8>(a, st);
+  if (np <= 1) return run_q40<1, 1, Q8>(a, epi, st);
+  if (np <= 2) return run_q40<2, 1, Q8>(a, epi, st);
+  if (np <= 4) return run_q40<4, 1, Q8>(a, epi, st);
+  if (np <= 8) return run_q40<8, 1, Q8>(a, epi, st);
+  if (np <= 16) return run_q40<16, 1, Q8>(a, epi, st);
+  if (np <= 32) return run_q40<32, 1, Q8>(a, epi, st);
   switch ((np + 63) / 64) {
-    case 1: return run_q40<64, 1, Q8>(a, st);
-    case 2: return run_q40<64, 2, Q8>(a, st);
-    case 3: if constexpr (Q8) return run_q40<64, 3, Q8>(a, st); else return hipErrorInvalidValue;
-    case 4: if constexpr (Q8) return run_q40<64, 4, Q8>(a, st); else return hipErrorInvalidValue;
+    case 1: return run_q40<64, 1, Q8>(a, epi, st);
+    case 2: return run_q40<64, 2, Q8>(a, epi, st);
+    case 3: if constexpr (Q8) return run_q40<64, 3, Q8>(a, epi, st); else return hipErrorInvalidValue;
+    case 4: if constexpr (Q8) return run_q40<64, 4, Q8>(a, epi, st); else return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }
 
+// Column chunks; the last one runs the epilogue when `epi`.
 template <bool Q8>
-static hipError_t run_q40_all(Q40Args a, hipStream_t st) {
+static hipError_t run_q40_all(Q40Args a, bool epi, hipStream_t st) {
   const int chunk = 64 * pair_slots_max<Q8>();
   for (int p0 = 0; p0 < a.npairs_row; p0 += chunk) {
     a.p0 = p0;
     a.npairs = a.npairs_row - p0 < chunk ? a.npairs_row - p0 : chunk;
     a.accumulate = p0 > 0;
-    const hipError_t e = run_q40_chunk<Q8>(a, st);
+    const hipError_t e = run_q40_chunk<Q8>(a, epi && p0 + chunk >= a.npairs_row, st);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
-hipError_t launch_q4_0_gemv(const uint8_t* w, const void* x, int x_format, float* y,
-                            int out_dim, int in_dim, hipStream_t stream) {
+static Q40Args q40_args(const uint8_t* w, const void* x, float* y, int out_dim, int in_dim) {
   Q40Args a;
   a.w = w;
   a.x = x;
@@ -294,7 +449,50 @@ hipError_t launch_q4_0_gemv(const uint8_t* w, const void* x, int x_format, float
   a.p0 = 0;
   a.npairs = a.npairs_row;
   a.accumulate = 0;
-  return x_format == 0 ? run_q40_all<false>(a, stream) : run_q40_all<true>(a, stream);
+  a.bias = nullptr;
+  a.part_val = nullptr;
+  a.part_idx = nullptr;
+  a.part_count = 0;
+  return a;
+}
+
+hipError_t launch_q4_0_gemv(const uint8_t* w, const void* x, int x_format, float* y,
+                            int out_dim, int in_dim, hipStream_t stream) {
+  const Q40Args a = q40_args(w, x, y, out_dim, in_dim);
+  return x_format == 0 ? run_q40_all<false>(a, false, stream) : run_q40_all<true>(a, false, stream);
+}
+
+long q4_0_lm_head_partials(int out_dim, int in_dim, int x_format) {
+  const bool q8 = x_format == 1;
+  const int npairs_row = in_dim / 64;
+  const int chunk = 64 * (q8 ? pair_slots_max<true>() : pair_slots_max<false>());
+  const int last = npairs_row - ((npairs_row - 1) / chunk) * chunk;   // pairs of the last chunk
+  const Q40Shape sh = q40_shape(last, out_dim, q8);
+  const long rows_per_group = (long)(kWave / sh.lpr) * sh.r;
+  const long groups = (out_dim + rows_per_group - 1) / rows_per_group;
+  const long waves = (groups + sh.g - 1) / sh.g;
+  return (waves + 3) / 4;
+}
+
+hipError_t launch_q4_0_lm_head(const uint8_t* w, const void* x, int x_format, const float* bias,
+                               float* logits, int out_dim, int in_dim, int* argmax_idx,
+                               float* argmax_val, float* part_val, int* part_idx,
+                               hipStream_t stream) {
+  Q40Args a = q40_args(w, x, logits, out_dim, in_dim);
+  a.bias = bias;
+  const bool argmax = argmax_idx != nullptr || argmax_val != nullptr;
+  if (argmax) {
+    a.part_val = part_val;
+    a.part_idx = part_idx;
+    a.part_count = q4_0_lm_head_partials(out_dim, in_dim, x_format);
+  }
+  const hipError_t e = x_format == 0 ? run_q40_all<false>(a, true, stream)
+                                     : run_q40_all<true>(a, true, stream);
+  if (e != hipSuccess || !argmax) return e;
+  const int count = (int)q4_0_lm_head_partials(out_dim, in_dim, x_format);
+  hipLaunchKernelGGL(argmax_merge_kernel, dim3(1), dim3(1024), 0, stream, part_val, part_idx,
+                     count, argmax_idx, argmax_val);
+  return hipGetLastError();
 }
 
 }  // namespace rz

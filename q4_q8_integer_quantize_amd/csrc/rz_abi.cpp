@@ -303,6 +303,55 @@ int swiglu_ffn(const char* what, const void* w_gate, const void* w_up, const voi
 
 extern "C" {
 
+size_t rz_lm_head_q4_0_workspace_bytes(int out_dim, int in_dim, int x_format) {
+  if (out_dim <= 0 || out_dim > RZ_MAX_DIM || in_dim <= 0 || in_dim > RZ_MAX_DIM ||
+      in_dim % 64 != 0 || (x_format != 0 && x_format != 1))
+    return 0;
+  return (size_t)rz::q4_0_lm_head_partials(out_dim, in_dim, x_format) * 8u;
+}
+
+int rz_lm_head_q4_0(const void* w_q4_0, const void* x, int x_format, const float* bias,
+                    float* logits, int out_dim, int in_dim, int* argmax_idx, float* argmax_val,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  const char* what = "rz_lm_head_q4_0";
+  if (!w_q4_0 || !x || !logits) return fail(RZ_EINVAL, "%s: null pointer", what);
+  if (x_format != 0 && x_format != 1)
+    return fail(RZ_EINVAL, "%s: x_format=%d (0 = fp32, 1 = Q8_1)", what, x_format);
+  if (int rc = check_dim(what, "out_dim", out_dim, 1)) return rc;
+  if (int rc = check_dim(what, "in_dim", in_dim, 64)) return rc;
+  if (!aligned(w_q4_0, 4)) return fail(RZ_EALIGN, "%s: w_q4_0 must be 4-byte aligned", what);
+  if (!aligned(x, x_format == 0 ? 16 : 8))
+    return fail(RZ_EALIGN, "%s: x must be %d-byte aligned", what, x_format == 0 ? 16 : 8);
+  if (!aligned(logits, 4) || (bias && !aligned(bias, 4)) || (argmax_idx && !aligned(argmax_idx, 4)) ||
+      (argmax_val && !aligned(argmax_val, 4)))
+    return fail(RZ_EALIGN, "%s: logits, bias and the argmax outputs must be 4-byte aligned", what);
+  if (bias && !same_or_disjoint(bias, logits, out_dim))
+    return fail(RZ_EINVAL, "%s: bias must be logits itself or not overlap it", what);
+  const bool argmax = argmax_idx || argmax_val;
+  float* part_val = nullptr;
+  int* part_idx = nullptr;
+  if (argmax) {
+    const size_t need = rz_lm_head_q4_0_workspace_bytes(out_dim, in_dim, x_format);
+    if (!workspace) return fail(RZ_EINVAL, "%s: the argmax needs a workspace", what);
+    if (!aligned(workspace, 4)) return fail(RZ_EALIGN, "%s: workspace must be 4-byte aligned", what);
+    if (workspace_bytes < need)
+      return fail(RZ_EINVAL, "%s: workspace of %zu bytes, %zu needed", what, workspace_bytes, need);
+    if (!disjoint(workspace, (long long)need, logits, 4LL * out_dim) ||
+        (bias && !disjoint(workspace, (long long)need, bias, 4LL * out_dim)))
+      return fail(RZ_EINVAL, "%s: workspace must not overlap logits or bias", what);
+    if ((argmax_idx && !disjoint(argmax_idx, 4, workspace, (long long)need)) ||
+        (argmax_val && !disjoint(argmax_val, 4, workspace, (long long)need)))
+      return fail(RZ_EINVAL, "%s: the argmax outputs must not overlap the workspace", what);
+    part_val = static_cast<float*>(workspace);
+    part_idx = reinterpret_cast<int*>(static_cast<char*>(workspace) + need / 2);
+  }
+  return launch_status(rz::launch_q4_0_lm_head(static_cast<const uint8_t*>(w_q4_0), x, x_format,
+                                               bias, logits, out_dim, in_dim, argmax_idx,
+                                               argmax_val, part_val, part_idx,
+                                               static_cast<hipStream_t>(stream)),
+                       what);
+}
+
 int rz_swiglu_ffn_q4k(const void* w_gate, const void* w_up, const void* w_down,
                       const void* x_q8, float* h, void* h_q8, float* y, float* gu,
                       int hidden_dim, int inter_dim, void* stream) {

@@ -53,6 +53,15 @@ hipError_t launch_swiglu_ffn_q4k_xf32(const uint8_t* w_gate, const uint8_t* w_up
 hipError_t launch_q4_0_gemv(const uint8_t* w, const void* x, int x_format, float* y,
                             int out_dim, int in_dim, hipStream_t stream);
 
+// The LM head: Q4_0 GEMV with the output bias added in the store and,
+// when argmax_idx or argmax_val is given, the greedy token (per-workgroup
+// pairs in part_val/part_idx, q4_0_lm_head_partials of each, then one merge).
+long q4_0_lm_head_partials(int out_dim, int in_dim, int x_format);
+hipError_t launch_q4_0_lm_head(const uint8_t* w, const void* x, int x_format, const float* bias,
+                               float* logits, int out_dim, int in_dim, int* argmax_idx,
+                               float* argmax_val, float* part_val, int* part_idx,
+                               hipStream_t stream);
+
 // SwiGLU FFN chain; with r the down projection's output is y = W_down h + r.
 hipError_t launch_swiglu_ffn_q4k(const uint8_t* w_gate, const uint8_t* w_up,
                                  const uint8_t* w_down, const uint8_t* xq, float* h,

@@ -26,7 +26,8 @@ P_ODD = P + 2
 
 def declared_symbols():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:int|const char\s*\*)\s*(rz_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\s*\*)\s*(rz_\w+)\s*\(", text,
+                                 re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -41,7 +42,8 @@ def test_header_declares_the_four_operations():
     for name in ("rz_q8_1_quantize", "rz_q4k_q8_gemv", "rz_q4k_q8_gemv_f32", "rz_q4_0_gemv",
                  "rz_swiglu_ffn_q4k", "rz_q4k_q8_gemv_multi", "rz_rmsnorm_q8_1",
                  "rz_q4k_q8_gemv_add", "rz_swiglu_ffn_q4k_add", "rz_q4k_gemv",
-                 "rz_swiglu_ffn_q4k_f32", "rz_last_error",
+                 "rz_swiglu_ffn_q4k_f32", "rz_lm_head_q4_0", "rz_lm_head_q4_0_workspace_bytes",
+                 "rz_last_error",
                  "rz_abi_version"):
         assert name in syms
 
@@ -311,6 +313,49 @@ def test_swiglu_ffn_f32_accepts_y_on_x(lib):
     (rc, _), = run_isolated([("rz_swiglu_ffn_q4k_f32", [P, P, P, Y, H, Y, None, 4096, 14336,
                                                         None])])
     assert rc == rz.RZ_ELAUNCH
+
+
+def test_lm_head_workspace_bytes(lib):
+    # 151936 x 1024: 16 pairs a row -> 16 lanes a row, 4 rows side by side, 4 unrolled,
+    # 9496 row groups; fp32 x takes 2 groups a wave (1187 workgroups), Q8_1 x one (2374)
+    assert rz.rz_lm_head_q4_0_workspace_bytes(151936, 1024, 0) == 1187 * 8
+    assert rz.rz_lm_head_q4_0_workspace_bytes(151936, 1024, 1) == 2374 * 8
+    assert rz.rz_lm_head_q4_0_workspace_bytes(1, 64, 0) == 8
+    for bad in ((0, 1024, 0), (151936, 1000, 0), (151936, 1024, 2), (151936, 0, 1)):
+        assert rz.rz_lm_head_q4_0_workspace_bytes(*bad) == 0
+
+
+WS = P + (3 << 30)
+IDX = P + (4 << 30)
+@pytest.mark.parametrize("args,code", [
+    ((None, P, 0, None, Y, 151936, 1024, None, None, None, 0, None), rz.RZ_EINVAL),
+    ((P, None, 0, None, Y, 151936, 1024, None, None, None, 0, None), rz.RZ_EINVAL),
+    ((P, P, 0, None, None, 151936, 1024, None, None, None, 0, None), rz.RZ_EINVAL),
+    ((P, P, 2, None, Y, 151936, 1024, None, None, None, 0, None), rz.RZ_EINVAL),
+    ((P, P, 0, None, Y, 151936, 1000, None, None, None, 0, None), rz.RZ_EDIM),
+    ((P, P, 0, None, Y, 0, 1024, None, None, None, 0, None), rz.RZ_EDIM),
+    ((P, P, 0, None, Y, 151936, 1024, IDX, None, None, 0, None), rz.RZ_EINVAL),     # no workspace
+    ((P, P, 0, None, Y, 151936, 1024, IDX, None, WS, 9495, None), rz.RZ_EINVAL),    # short
+    ((P, P, 1, None, Y, 151936, 1024, None, IDX, WS, 9496, None), rz.RZ_EINVAL),    # short (Q8_1)
+    ((P, P, 0, Y + 4, Y, 151936, 1024, None, None, None, 0, None), rz.RZ_EINVAL),   # bias overlaps
+    ((P, P, 0, None, Y, 151936, 1024, IDX, None, Y + 64, 9496, None), rz.RZ_EINVAL),  # ws on logits
+    ((P, P, 0, None, Y, 151936, 1024, WS + 8, None, WS, 9496, None), rz.RZ_EINVAL),   # idx in ws
+    ((P, P, 0, None, Y, 151936, 1024, IDX, None, WS + 2, 9496, None), rz.RZ_EALIGN),
+    ((P, P + 8, 0, None, Y, 151936, 1024, None, None, None, 0, None), rz.RZ_EALIGN),
+    ((P, P, 0, P_ODD, Y, 151936, 1024, None, None, None, 0, None), rz.RZ_EALIGN),
+    ((P, P, 0, None, Y, 151936, 1024, IDX + 2, None, WS, 9496, None), rz.RZ_EALIGN),
+])
+def test_lm_head_rejects(lib, args, code):
+    assert _rc("rz_lm_head_q4_0", *args) == code
+    assert _rc.last.startswith("rz_lm_head_q4_0")
+
+
+def test_lm_head_accepts_bias_in_place_and_exact_workspace(lib):
+    res = run_isolated([("rz_lm_head_q4_0", [P, P, 0, Y, Y, 151936, 1024, None, None, None, 0,
+                                             None]),
+                        ("rz_lm_head_q4_0", [P, P, 0, None, Y, 151936, 1024, IDX, IDX + 4, WS,
+                                             9496, None])])
+    assert [rc for rc, _ in res] == [rz.RZ_ELAUNCH, rz.RZ_ELAUNCH]
 
 
 def test_error_message_is_per_call(lib):

@@ -919,6 +919,121 @@ def test_swiglu_ffn_f32_optional_gu_and_y_on_x():
     assert np.array_equal(host(xd), a["y"])
 
 
+# ------------------------------------------------------------------ LM head epilogue
+def gpu_lm_head(blob, x, x_format, bias, argmax=True):
+    """(logits, idx, val) from rz_lm_head_q4_0; idx/val None without argmax."""
+    torch = __import__("torch")
+    out_dim, nb, _ = blob.shape
+    in_dim = nb * 32
+    logits = empty_f32(out_dim)
+    xd = dev_f32(x) if x_format == 0 else dev_bytes(x)
+    bd = dev_f32(bias) if bias is not None else None
+    idx = torch.full((1,), -7, dtype=torch.int32, device="cuda") if argmax else None
+    val = empty_f32(1) if argmax else None
+    ws = None
+    if argmax:
+        ws = empty_bytes(rz.rz_lm_head_q4_0_workspace_bytes(out_dim, in_dim, x_format))
+    rz.rz_lm_head_q4_0(dev_bytes(blob), xd, x_format, bd, logits, out_dim, in_dim, idx, val, ws)
+    lg = host(logits)
+    if not argmax:
+        return lg, None, None
+    return lg, int(host(idx)[0]), host(val)[0]
+
+
+def _check_lm_head(blob, x, x_format, bias, x_oracle):
+    lg, idx, val = gpu_lm_head(blob, x, x_format, bias)
+    # logits: fl32(plain GEMV + bias), and the oracle bound with |bias| as a term
+    plain = gpu_q4_0(blob, x, x_format)
+    want = plain if bias is None else (plain + bias).astype(np.float32)
+    mm = first_mismatch(lg, want)
+    assert mm is None, "logit %s fused=%r plain+bias=%r (%d differ)" % mm
+    y_ref, terms = oracle.lm_head_q4_0(blob, x_oracle, bias, x_format)
+    assert_within(lg, y_ref, terms, "lm head logits")
+    # the greedy token: unique on the GPU's own logits (same fp32 values, same tie rule)
+    assert idx == oracle.argmax_first(lg)
+    assert np.float32(val).tobytes() == np.float32(lg[idx]).tobytes()
+    # and a valid choice against the exact logits: within both tolerances of the true maximum
+    tol = oracle.gemv_tolerance(terms)
+    best = oracle.argmax_first(y_ref)
+    assert y_ref[idx] >= y_ref[best] - tol[idx] - tol[best]
+    return lg, idx
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_lm_head_full_with_bias(fmt):
+    """151936 x 1024 with an N(0, 1) output bias."""
+    banner("lm head full", fmt)
+    w = synth.WORKLOADS["lm_head_q4_0"]
+    blob = synth.q4_0_weights(synth.rng(3, synth.T_W0), w["out_dim"], w["in_dim"])
+    x = _padded(synth.activation(synth.rng(3, synth.T_ACT), w["n"]), w["in_dim"])
+    bias = synth.activation(synth.rng(3, 8), w["out_dim"])
+    if fmt == 0:
+        _check_lm_head(blob, x, 0, bias, x)
+    else:
+        xq = oracle.quantize_q8_1(x)
+        _check_lm_head(blob, oracle.q8_1_to_bytes(xq), 1, bias, xq)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("out_dim,in_dim", [(1, 64), (17, 64), (1000, 1024), (4097, 2048),
+                                            (3000, 16384), (50, 32768)])
+def test_lm_head_shapes(fmt, out_dim, in_dim):
+    """Ragged row counts, one and several column passes (the epilogue runs in
+    the last), with and without bias."""
+    banner("lm head", fmt, out_dim, in_dim)
+    g = np.random.default_rng(out_dim + in_dim)
+    blob = synth.q4_0_weights(synth.rng(60, 1), out_dim, in_dim)
+    x = synth.activation(g, in_dim)
+    bias = None if out_dim % 2 else synth.activation(g, out_dim)
+    if fmt == 0:
+        _check_lm_head(blob, x, 0, bias, x)
+    else:
+        xq = oracle.quantize_q8_1(x)
+        _check_lm_head(blob, oracle.q8_1_to_bytes(xq), 1, bias, xq)
+
+
+def test_lm_head_ties_and_negative_logits():
+    """Zero weights make the logits equal to the bias exactly: equal largest
+    values at rows 5000 and 100000 give 5000; an all-equal bias gives 0; all
+    negative logits still give the largest."""
+    banner("lm head ties")
+    rows, in_dim = 151936, 1024
+    blob = synth.q4_0_weights(synth.rng(61, 1), rows, in_dim, d_fixed=0.0)
+    x = synth.activation(synth.rng(61, 0), in_dim)
+    bias = -np.abs(synth.activation(synth.rng(61, 2), rows)) - 1.0
+    bias[100000] = bias[5000] = -0.25
+    lg, idx, val = gpu_lm_head(blob, x, 0, bias)
+    assert np.array_equal(lg, bias) and idx == 5000 and val == np.float32(-0.25)
+    lg, idx, val = gpu_lm_head(blob, x, 0, np.full(rows, 3.5, np.float32))
+    assert idx == 0 and val == np.float32(3.5)
+    lg, idx, val = gpu_lm_head(blob, x, 0, None)
+    assert idx == 0 and np.all(lg == 0)
+
+
+def test_lm_head_optional_outputs_and_workspace_reuse():
+    """Only the index, only the value, no argmax at all, and one workspace used
+    by two calls of different sizes in a row (it holds no state)."""
+    banner("lm head options")
+    torch = __import__("torch")
+    blob = synth.q4_0_weights(synth.rng(62, 1), 20000, 1024)
+    x = synth.activation(synth.rng(62, 0), 1024)
+    lg_full, idx_full, val_full = gpu_lm_head(blob, x, 0, None)
+    ws = empty_bytes(rz.rz_lm_head_q4_0_workspace_bytes(20000, 1024, 0))
+    xd, wd = dev_f32(x), dev_bytes(blob)
+    logits = empty_f32(20000)
+    idx = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    val = empty_f32(1)
+    rz.rz_lm_head_q4_0(wd, xd, 0, None, logits, 20000, 1024, idx, None, ws)
+    assert int(host(idx)[0]) == idx_full
+    rz.rz_lm_head_q4_0(wd, xd, 0, None, logits, 20000, 1024, None, val, ws)
+    assert host(val)[0] == val_full
+    small = blob[:777]
+    rz.rz_lm_head_q4_0(dev_bytes(small), xd, 0, None, logits, 777, 1024, idx, val, ws)
+    assert int(host(idx)[0]) == oracle.argmax_first(host(logits)[:777])
+    rz.rz_lm_head_q4_0(wd, xd, 0, None, logits, 20000, 1024, None, None, None)
+    assert np.array_equal(host(logits), lg_full)
+
+
 # ------------------------------------------------------------------ errors on device tensors
 def test_binding_errors_on_gpu():
     banner("binding errors")
