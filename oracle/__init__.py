@@ -26,6 +26,9 @@ source pages (docs.rs, realizar 0.8.4/0.8.5):
   the LM head's output bias and the logits it produces (the greedy token is the
   index of the largest logit).
 
+* using.rs ``ffn_standard_gpu`` and clone_layer_weights.rs ``cuda_gelu_ffn``: the
+  GELU FFN (up projection, optional bias, GELU, down projection, optional bias).
+
 The block formats are not printed on the pages; the GGML layouts the pages name
 (Q4_K super-blocks of 256 values, type id 12; Q4_0; Q8_1) are read as written in
 each module's docstring.
@@ -48,6 +51,7 @@ from .swiglu import (silu, silu_grad, swiglu, ffn_swiglu_q4k, ffn_swiglu_q4k_f32
 from .tolerance import gemv_tolerance, GEMV_REL, GEMV_ABS
 from .norm import rmsnorm, rmsnorm_tolerance, residual_add
 from .lm_head import lm_head_q4_0, argmax_first
+from .gelu import gelu, gelu_grad, gelu_h_tolerance, ffn_gelu_q4_0
 
 __all__ = [
     "QK8_1", "Q8_1_BLOCK_BYTES", "quantize_q8_1", "q8_1_to_bytes", "q8_1_from_bytes",
@@ -59,4 +63,5 @@ __all__ = [
     "gemv_tolerance", "GEMV_REL", "GEMV_ABS",
     "rmsnorm", "rmsnorm_tolerance", "residual_add",
     "lm_head_q4_0", "argmax_first",
+    "gelu", "gelu_grad", "gelu_h_tolerance", "ffn_gelu_q4_0",
 ]

@@ -602,3 +602,70 @@ def test_lm_head_bias_closed_form():
     y0, t0 = oracle.lm_head_q4_0(blob, x)
     assert np.allclose(terms - t0, np.abs(bias.astype(np.float64)), rtol=0, atol=1e-12)
     assert oracle.argmax_first(y0) == 0 and oracle.argmax_first(y) == 3
+
+
+# ----------------------------------------------------------------- GELU FFN
+def test_gelu_against_the_erf_definition():
+    """The tanh form stays within 5e-4 of x * Phi(x) (scipy's erf, an independent
+    routine); a wrong constant or a missing sqrt(2/pi) moves it much further."""
+    from scipy.special import erf
+    u = np.linspace(-10, 10, 200001)
+    exact = 0.5 * u * (1.0 + erf(u / np.sqrt(2.0)))
+    assert np.max(np.abs(oracle.gelu(u) - exact)) < 5e-4
+    wrong_c = 0.5 * u * (1.0 + np.tanh(np.sqrt(2 / np.pi) * (u + 0.44715 * u ** 3)))
+    wrong_k = 0.5 * u * (1.0 + np.tanh(u + 0.044715 * u ** 3))
+    assert np.max(np.abs(wrong_c - exact)) > 1e-2 and np.max(np.abs(wrong_k - exact)) > 1e-2
+
+
+def test_gelu_identities_and_limits():
+    u = np.linspace(-30, 30, 6001)
+    # gelu(u) - gelu(-u) = u, and the sigmoid form used on the device is the same function
+    assert np.allclose(oracle.gelu(u) - oracle.gelu(-u), u, rtol=0, atol=1e-12)
+    z = np.sqrt(2 / np.pi) * (u + 0.044715 * u ** 3)
+    with np.errstate(over="ignore"):
+        sig_form = u / (1.0 + np.exp(-2.0 * z))
+    # the tanh form cancels for negative u (1 + tanh z), so compare with an
+    # allowance of a few float64 ulps of |u|
+    assert np.all(np.abs(sig_form - oracle.gelu(u)) <= 1e-13 * np.abs(sig_form) + 1e-15 * np.abs(u))
+    assert oracle.gelu(0.0) == 0.0
+    assert oracle.gelu(10.0) == pytest.approx(10.0, rel=1e-15)
+    assert abs(oracle.gelu(-10.0)) < 1e-40
+
+
+def test_gelu_grad_by_finite_difference_and_bounds():
+    from oracle.gelu import GELU_CURV_MAX, GELU_GRAD_MAX
+    u = np.linspace(-8, 8, 1601)
+    h = 1e-6
+    fd = (oracle.gelu(u + h) - oracle.gelu(u - h)) / (2 * h)
+    assert np.allclose(oracle.gelu_grad(u), fd, rtol=0, atol=1e-8)
+    dense = np.linspace(-12, 12, 1200001)
+    g = oracle.gelu_grad(dense)
+    assert np.max(np.abs(g)) <= GELU_GRAD_MAX
+    assert np.max(np.abs(np.gradient(g, dense))) <= GELU_CURV_MAX
+
+
+def _uniform_q4_0(rows, in_dim, qn, d):
+    blk = np.array([d], np.float16).tobytes() + bytes([qn | (qn << 4)] * 16)
+    return np.frombuffer(blk * (rows * in_dim // 32), np.uint8).reshape(rows, in_dim // 32, 18).copy()
+
+
+def test_ffn_gelu_chain_closed_form():
+    """Zero up weights make u the up bias exactly; uniform down weights w make
+    every y equal w * sum(fp32(gelu(b))) + down bias.  Biases on both sides are
+    exercised, and the order (bias before GELU) is visible."""
+    H, I = 128, 192
+    wu = _uniform_q4_0(I, H, 5, 0.0)
+    d, qn = 0.0078125, 13
+    wd = _uniform_q4_0(H, I, qn, d)
+    g = np.random.default_rng(2)
+    x = g.standard_normal(H).astype(np.float32)
+    ub = g.standard_normal(I).astype(np.float32)
+    db = g.standard_normal(H).astype(np.float32)
+    st = oracle.ffn_gelu_q4_0(wu, wd, x, ub, db)
+    assert np.array_equal(st["u"], ub.astype(np.float64))
+    h32 = oracle.gelu(ub.astype(np.float64)).astype(np.float32)
+    assert np.array_equal(st["h32"], h32)
+    w = (qn - 8) * d
+    assert np.allclose(st["y"], w * h32.astype(np.float64).sum() + db, rtol=1e-13, atol=1e-12)
+    # GELU of (0 + bias) differs from GELU(0) + bias
+    assert not np.allclose(oracle.gelu(ub), ub)
