@@ -302,6 +302,28 @@ def time_rows(lib, rz, torch, dev, graph_time, copies, x, xq, y) -> dict:
             "rz_lm_head_q4_0 x_format=%d (bias + argmax epilogue, merge kernel)" % fmt)
     del lm
 
+    # GELU FFN of a phi-2-sized layer on Q4_0 weights, 2560 -> 10240 -> 2560, with biases
+    GH, GI = 2560, 10240
+    gelu_w = rotated([synth.q4_0_weights(synth.rng(5, 1), GI, GH),
+                      synth.q4_0_weights(synth.rng(5, 2), GH, GI)])
+    gelu_p = [[t.data_ptr() for t in c] for c in gelu_w]
+    gx = torch.from_numpy(synth.activation(synth.rng(5, synth.T_ACT), GH)).to(dev)
+    gub = torch.from_numpy(synth.activation(synth.rng(5, 7), GI)).to(dev)
+    gdb = torch.from_numpy(synth.activation(synth.rng(5, 8), GH)).to(dev)
+    gh = torch.empty(GI, dtype=torch.float32, device=dev)
+    gy = torch.empty(GH, dtype=torch.float32, device=dev)
+
+    def gelu_body(i, s):
+        wu, wd = gelu_p[i % len(gelu_p)]
+        check(lib.rz_gelu_ffn_q4_0(wu, wd, gx.data_ptr(), gub.data_ptr(), gdb.data_ptr(),
+                                   gh.data_ptr(), gy.data_ptr(), GH, GI, s))
+
+    gelu_wb = 2 * q4_0_bytes(GI, GH)
+    rows["gelu_ffn_q4_0_2560_10240"] = row_entry(
+        graph_time(gelu_body), gelu_wb + 4 * GH + 4 * GI + 2 * 4 * GI + 4 * GH + 4 * GH, gelu_wb,
+        "rz_gelu_ffn_q4_0 (up + bias + GELU, then down + bias)")
+    del gelu_w
+
     # the small case: 896 x (896 -> 1024), launch-bound
     small = rotated([synth.q4k_weights(synth.rng(0, 1), 896, 1024)])
     small_p = [c[0].data_ptr() for c in small]

@@ -257,6 +257,29 @@ int rz_lm_head_q4_0(const void* w_q4_0, const void* x, int x_format, const float
  * would reject). */
 size_t rz_lm_head_q4_0_workspace_bytes(int out_dim, int in_dim, int x_format);
 
+/* rz_gelu_ffn_q4_0 -- the GELU FFN on Q4_0 weights and fp32 activations.
+ * Passages: realizar 0.8.4 src/gpu/adapters/using.rs, ffn_standard_gpu (up
+ * projection, GELU in place, down projection, all Q4_0 GEMVs on fp32
+ * activations); realizar 0.8.4 src/gguf/cuda/clone_layer_weights.rs,
+ * cuda_gelu_ffn (the phi-2-style path, with optional biases).
+ *   h = gelu(W_up x + up_bias)        gelu(u) = 0.5 u (1 + tanh(sqrt(2/pi)
+ *                                      (u + 0.044715 u^3))), evaluated as
+ *                                      u / (1 + exp(-2 sqrt(2/pi) (u + 0.044715 u^3)))
+ *   y = W_down h + down_bias          (fp32 h, rz_q4_0_gemv arithmetic)
+ *   w_up      [inter_dim][hidden_dim/32] Q4_0 blocks; w_down [hidden_dim][inter_dim/32];
+ *             4-byte aligned
+ *   x         fp32 [hidden_dim], 16-byte aligned
+ *   up_bias   optional fp32 [inter_dim]; down_bias optional fp32 [hidden_dim]
+ *   h         out: fp32 [inter_dim], 16-byte aligned (the down projection's input)
+ *   y         out: fp32 [hidden_dim], 4-byte aligned
+ *   hidden_dim, inter_dim  multiples of 64
+ * Two GEMV launches run in order on `stream`.  x and h, h and y must not
+ * overlap; a bias may be its output itself but must not overlap it otherwise.
+ * Errors: RZ_EINVAL, RZ_EDIM, RZ_EALIGN, RZ_ELAUNCH. */
+int rz_gelu_ffn_q4_0(const void* w_up, const void* w_down, const float* x, const float* up_bias,
+                     const float* down_bias, float* h, float* y, int hidden_dim, int inter_dim,
+                     void* stream);
+
 /* rz_swiglu_ffn_q4k -- the SwiGLU FFN on the integer path.
  * Passages: realizar 0.8.5 src/cuda/executor/cached.rs,
  * transformer_layer_gpu_true_dp4a step 9 (fused_ffn_swiglu_gpu_true_dp4a);

@@ -22,7 +22,7 @@ __all__ = [
     "rz_q8_1_quantize", "rz_rmsnorm_q8_1", "rz_q4k_q8_gemv", "rz_q4k_q8_gemv_add",
     "rz_q4k_q8_gemv_multi", "rz_q4k_q8_gemv_f32", "rz_q4_0_gemv", "rz_swiglu_ffn_q4k",
     "rz_swiglu_ffn_q4k_add", "rz_q4k_gemv", "rz_swiglu_ffn_q4k_f32",
-    "rz_lm_head_q4_0", "rz_lm_head_q4_0_workspace_bytes",
+    "rz_lm_head_q4_0", "rz_lm_head_q4_0_workspace_bytes", "rz_gelu_ffn_q4_0",
     "q8_1_nbytes", "RzError",
 ]
 
@@ -69,12 +69,13 @@ def load_library() -> ctypes.CDLL:
     lib.rz_q4k_gemv.argtypes = [vp, vp, i, vp, i, i, vp]
     lib.rz_swiglu_ffn_q4k_f32.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, vp]
     lib.rz_lm_head_q4_0.argtypes = [vp, vp, i, vp, vp, i, i, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.rz_gelu_ffn_q4_0.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, vp]
     lib.rz_lm_head_q4_0_workspace_bytes.argtypes = [i, i, i]
     lib.rz_lm_head_q4_0_workspace_bytes.restype = ctypes.c_size_t
     for fn in ("rz_q8_1_quantize", "rz_rmsnorm_q8_1", "rz_q4k_q8_gemv", "rz_q4k_q8_gemv_add",
                "rz_q4k_q8_gemv_f32", "rz_q4k_q8_gemv_multi", "rz_q4_0_gemv", "rz_swiglu_ffn_q4k",
                "rz_swiglu_ffn_q4k_add", "rz_q4k_gemv", "rz_swiglu_ffn_q4k_f32",
-               "rz_lm_head_q4_0", "rz_abi_version"):
+               "rz_lm_head_q4_0", "rz_gelu_ffn_q4_0", "rz_abi_version"):
         getattr(lib, fn).restype = i
     lib.rz_last_error.argtypes = []
     lib.rz_last_error.restype = ctypes.c_char_p
@@ -306,3 +307,21 @@ def rz_lm_head_q4_0(w_q4_0, x, x_format: int, bias, logits, out_dim: int, in_dim
                                           _ptr(logits), out_dim, in_dim, _ptr(argmax_idx),
                                           _ptr(argmax_val), _ptr(workspace), ws_bytes,
                                           _stream(stream)))
+
+
+def rz_gelu_ffn_q4_0(w_up, w_down, x, up_bias, down_bias, h, y, hidden_dim: int, inter_dim: int,
+                     stream=None) -> None:
+    """GELU FFN on Q4_0 weights: h = gelu(W_up x + up_bias), y = W_down h + down_bias
+    (either bias may be None)."""
+    if hidden_dim > 0 and inter_dim > 0 and hidden_dim % 64 == 0 and inter_dim % 64 == 0:
+        nw = inter_dim * (hidden_dim // 32) * Q4_0_BLOCK_BYTES
+        _need(w_up, nw, "w_up")
+        _need(w_down, nw, "w_down")
+        _need(x, 4 * hidden_dim, "x")
+        _need(up_bias, 4 * inter_dim, "up_bias")
+        _need(down_bias, 4 * hidden_dim, "down_bias")
+        _need(h, 4 * inter_dim, "h")
+        _need(y, 4 * hidden_dim, "y")
+    _check(load_library().rz_gelu_ffn_q4_0(_ptr(w_up), _ptr(w_down), _ptr(x), _ptr(up_bias),
+                                           _ptr(down_bias), _ptr(h), _ptr(y), hidden_dim,
+                                           inter_dim, _stream(stream)))

@@ -39,6 +39,7 @@ struct Q40Args {
   float* part_val;    // EPI: optional [grid] per-workgroup best logit
   int* part_idx;      //      and its row
   long part_count;    // EPI with pairs: the grid the pairs were sized for
+  int act;            // EPI: 1 = GELU after the bias (the GELU FFN's up projection)
 };
 
 template <int S, bool Q8>
@@ -176,6 +177,15 @@ __device__ __forceinline__ void load_q40_tile(Q40Tile<S, R>& t, const Q40Args& a
   }
 }
 
+// GELU, tanh form (realizar 0.8.4 src/gguf/cuda/clone_layer_weights.rs,
+// cuda_gelu_ffn, for phi-2-style models), evaluated as its equal
+// u * sigmoid(2 z), z = sqrt(2/pi) (u + 0.044715 u^3): for negative u this
+// avoids the cancellation in 1 + tanh(z).
+__device__ __forceinline__ float gelu_tanh(float u) {
+  const float z2 = -1.5957691216057308f * (u + 0.044715f * (u * u * u));   // -2 z
+  return u / (1.0f + expf(z2));
+}
+
 // (v, i) ranks above (bv, bi): a larger value, or an equal value at a smaller
 // index.  Every pair compares, so the reduction's result is unique.
 __device__ __forceinline__ bool ranks_above(float v, int i, float bv, int bi) {
@@ -278,6 +288,7 @@ __global__ __launch_bounds__(256) void q4_0_gemv_kernel(Q40Args a) {
           float v = ACC ? a.y[row] + acc[r] : acc[r];
           if constexpr (EPI) {
             if (has_bias) v = v + bv[k][r];
+            if (a.act) v = gelu_tanh(v);
             if (ranks_above(v, (int)row, best_v, best_i)) {
               best_v = v;
               best_i = (int)row;
@@ -453,6 +464,7 @@ static Q40Args q40_args(const uint8_t* w, const void* x, float* y, int out_dim, 
   a.part_val = nullptr;
   a.part_idx = nullptr;
   a.part_count = 0;
+  a.act = 0;
   return a;
 }
 
@@ -493,6 +505,23 @@ hipError_t launch_q4_0_lm_head(const uint8_t* w, const void* x, int x_format, co
   hipLaunchKernelGGL(argmax_merge_kernel, dim3(1), dim3(1024), 0, stream, part_val, part_idx,
                      count, argmax_idx, argmax_val);
   return hipGetLastError();
+}
+
+// GELU FFN (realizar 0.8.4 src/gpu/adapters/using.rs, ffn_standard_gpu;
+// clone_layer_weights.rs, cuda_gelu_ffn): h = gelu(W_up x + up_bias) in the
+// up projection's epilogue, then y = W_down h + down_bias, both on fp32
+// activations.
+hipError_t launch_gelu_ffn_q4_0(const uint8_t* w_up, const uint8_t* w_down, const float* x,
+                                const float* up_bias, const float* down_bias, float* h, float* y,
+                                int hidden_dim, int inter_dim, hipStream_t stream) {
+  Q40Args up = q40_args(w_up, x, h, inter_dim, hidden_dim);
+  up.bias = up_bias;
+  up.act = 1;
+  hipError_t e = run_q40_all<false>(up, true, stream);
+  if (e != hipSuccess) return e;
+  Q40Args down = q40_args(w_down, h, y, hidden_dim, inter_dim);
+  down.bias = down_bias;
+  return run_q40_all<false>(down, true, stream);
 }
 
 }  // namespace rz

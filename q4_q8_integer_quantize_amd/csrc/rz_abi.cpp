@@ -352,6 +352,33 @@ int rz_lm_head_q4_0(const void* w_q4_0, const void* x, int x_format, const float
                        what);
 }
 
+int rz_gelu_ffn_q4_0(const void* w_up, const void* w_down, const float* x, const float* up_bias,
+                     const float* down_bias, float* h, float* y, int hidden_dim, int inter_dim,
+                     void* stream) {
+  const char* what = "rz_gelu_ffn_q4_0";
+  if (!w_up || !w_down || !x || !h || !y) return fail(RZ_EINVAL, "%s: null pointer", what);
+  if (int rc = check_dim(what, "hidden_dim", hidden_dim, 64)) return rc;
+  if (int rc = check_dim(what, "inter_dim", inter_dim, 64)) return rc;
+  if (!aligned(w_up, 4) || !aligned(w_down, 4))
+    return fail(RZ_EALIGN, "%s: weight blobs must be 4-byte aligned", what);
+  if (!aligned(x, 16) || !aligned(h, 16))
+    return fail(RZ_EALIGN, "%s: x and h must be 16-byte aligned", what);
+  if (!aligned(y, 4) || (up_bias && !aligned(up_bias, 4)) || (down_bias && !aligned(down_bias, 4)))
+    return fail(RZ_EALIGN, "%s: y and the biases must be 4-byte aligned", what);
+  // the up projection reads x and up_bias while it writes h; the down
+  // projection reads h and down_bias while it writes y
+  if (!disjoint(x, 4LL * hidden_dim, h, 4LL * inter_dim) ||
+      (up_bias && !same_or_disjoint(up_bias, h, inter_dim)) ||
+      !disjoint(h, 4LL * inter_dim, y, 4LL * hidden_dim) ||
+      (down_bias && !same_or_disjoint(down_bias, y, hidden_dim)))
+    return fail(RZ_EINVAL, "%s: overlapping buffers (x, h; h, y; a bias and its output)", what);
+  return launch_status(rz::launch_gelu_ffn_q4_0(static_cast<const uint8_t*>(w_up),
+                                                static_cast<const uint8_t*>(w_down), x, up_bias,
+                                                down_bias, h, y, hidden_dim, inter_dim,
+                                                static_cast<hipStream_t>(stream)),
+                       what);
+}
+
 int rz_swiglu_ffn_q4k(const void* w_gate, const void* w_up, const void* w_down,
                       const void* x_q8, float* h, void* h_q8, float* y, float* gu,
                       int hidden_dim, int inter_dim, void* stream) {

@@ -57,6 +57,11 @@ hipError_t launch_q4_0_gemv(const uint8_t* w, const void* x, int x_format, float
 // when argmax_idx or argmax_val is given, the greedy token (per-workgroup
 // pairs in part_val/part_idx, q4_0_lm_head_partials of each, then one merge).
 long q4_0_lm_head_partials(int out_dim, int in_dim, int x_format);
+
+// GELU FFN on Q4_0 weights and fp32 activations, optional biases.
+hipError_t launch_gelu_ffn_q4_0(const uint8_t* w_up, const uint8_t* w_down, const float* x,
+                                const float* up_bias, const float* down_bias, float* h, float* y,
+                                int hidden_dim, int inter_dim, hipStream_t stream);
 hipError_t launch_q4_0_lm_head(const uint8_t* w, const void* x, int x_format, const float* bias,
                                float* logits, int out_dim, int in_dim, int* argmax_idx,
                                float* argmax_val, float* part_val, int* part_idx,

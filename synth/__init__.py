@@ -115,4 +115,7 @@ WORKLOADS = {
     "lm_head_q4_0": dict(config_id=3, out_dim=151936, n=896, in_dim=1024),
     # 8-token Q4_K GEMM 4096 -> 14336
     "q4k_batch8": dict(config_id=4, out_dim=14336, in_dim=4096, n_tokens=8),
+    # GELU FFN of a phi-2-sized layer on Q4_0 weights: 2560 -> 10240 -> 2560,
+    # with up and down biases
+    "gelu_ffn_2560_10240": dict(config_id=5, hidden=2560, inter=10240),
 }

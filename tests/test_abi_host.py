@@ -43,6 +43,7 @@ def test_header_declares_the_four_operations():
                  "rz_swiglu_ffn_q4k", "rz_q4k_q8_gemv_multi", "rz_rmsnorm_q8_1",
                  "rz_q4k_q8_gemv_add", "rz_swiglu_ffn_q4k_add", "rz_q4k_gemv",
                  "rz_swiglu_ffn_q4k_f32", "rz_lm_head_q4_0", "rz_lm_head_q4_0_workspace_bytes",
+                 "rz_gelu_ffn_q4_0",
                  "rz_last_error",
                  "rz_abi_version"):
         assert name in syms
@@ -356,6 +357,27 @@ def test_lm_head_accepts_bias_in_place_and_exact_workspace(lib):
                         ("rz_lm_head_q4_0", [P, P, 0, None, Y, 151936, 1024, IDX, IDX + 4, WS,
                                              9496, None])])
     assert [rc for rc, _ in res] == [rz.RZ_ELAUNCH, rz.RZ_ELAUNCH]
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, P, P, None, None, H, Y, 2560, 10240, None), rz.RZ_EINVAL),
+    ((P, P, None, None, None, H, Y, 2560, 10240, None), rz.RZ_EINVAL),
+    ((P, P, P, None, None, None, Y, 2560, 10240, None), rz.RZ_EINVAL),
+    ((P, P, P, None, None, H, None, 2560, 10240, None), rz.RZ_EINVAL),
+    ((P, P, H + 64, None, None, H, Y, 2560, 10240, None), rz.RZ_EINVAL),       # x overlaps h
+    ((P, P, P, None, None, H, H + 64, 2560, 10240, None), rz.RZ_EINVAL),       # y overlaps h
+    ((P, P, P, H + 4, None, H, Y, 2560, 10240, None), rz.RZ_EINVAL),          # up_bias shifted on h
+    ((P, P, P, None, Y + 4, H, Y, 2560, 10240, None), rz.RZ_EINVAL),          # down_bias shifted on y
+    ((P, P, P, None, None, H, Y, 2500, 10240, None), rz.RZ_EDIM),
+    ((P, P, P, None, None, H, Y, 2560, 10000, None), rz.RZ_EDIM),
+    ((P + 2, P, P, None, None, H, Y, 2560, 10240, None), rz.RZ_EALIGN),
+    ((P, P, P + 8, None, None, H, Y, 2560, 10240, None), rz.RZ_EALIGN),         # x needs 16
+    ((P, P, P, None, None, H + 8, Y, 2560, 10240, None), rz.RZ_EALIGN),         # h needs 16
+    ((P, P, P, P_ODD, None, H, Y, 2560, 10240, None), rz.RZ_EALIGN),
+])
+def test_gelu_ffn_rejects(lib, args, code):
+    assert _rc("rz_gelu_ffn_q4_0", *args) == code
+    assert _rc.last.startswith("rz_gelu_ffn_q4_0")
 
 
 def test_error_message_is_per_call(lib):

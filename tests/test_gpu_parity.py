@@ -1034,6 +1034,72 @@ def test_lm_head_optional_outputs_and_workspace_reuse():
     assert np.array_equal(host(logits), lg_full)
 
 
+# ------------------------------------------------------------------ GELU FFN (Q4_0)
+def gpu_q4_0_bias(blob, x, bias):
+    """W x + bias through rz_lm_head_q4_0 (no argmax): the GEMV and bias stage
+    the GELU FFN runs, for the staged checks."""
+    out_dim, nb, _ = blob.shape
+    y = empty_f32(out_dim)
+    rz.rz_lm_head_q4_0(dev_bytes(blob), dev_f32(x), 0, dev_f32(bias) if bias is not None else None,
+                       y, out_dim, nb * 32)
+    return host(y)
+
+
+@pytest.mark.parametrize("hidden,inter,biases", [(64, 64, True), (256, 512, False),
+                                                 (1024, 4096, True), (512, 16384, True),
+                                                 (2560, 10240, True)])
+def test_gelu_ffn_chain(hidden, inter, biases):
+    """Stage by stage: h within the bound propagated through GELU from the up
+    projection's GEMV bound; y bit-equal to the same GEMV + bias over the GPU's
+    own h; that GEMV over the oracle's h within the bound; the chain's y within
+    the bound plus |W| . |h_gpu - h|."""
+    banner("gelu ffn", hidden, inter, biases)
+    cid = 5 if (hidden, inter) == (2560, 10240) else 40 + hidden // 64
+    wu = synth.q4_0_weights(synth.rng(cid, synth.T_W0), inter, hidden)
+    wd = synth.q4_0_weights(synth.rng(cid, synth.T_W0 + 1), hidden, inter)
+    x = synth.activation(synth.rng(cid, synth.T_ACT), hidden)
+    ub = synth.activation(synth.rng(cid, 7), inter) if biases else None
+    db = synth.activation(synth.rng(cid, 8), hidden) if biases else None
+    st = oracle.ffn_gelu_q4_0(wu, wd, x, ub, db)
+    h = empty_f32(inter)
+    y = empty_f32(hidden)
+    rz.rz_gelu_ffn_q4_0(dev_bytes(wu), dev_bytes(wd), dev_f32(x),
+                        dev_f32(ub) if biases else None, dev_f32(db) if biases else None,
+                        h, y, hidden, inter)
+    h_gpu, y_gpu = host(h), host(y)
+    assert_within(gpu_q4_0_bias(wu, x, ub), st["u"], st["u_terms"], "up + bias")
+    tol_h = oracle.gelu_h_tolerance(st["u"], st["tol_u"], st["h"])
+    err_h = np.abs(h_gpu.astype(np.float64) - st["h"])
+    assert np.all(err_h <= tol_h), "h: %d outside, worst ratio %.3g" % (
+        int((err_h > tol_h).sum()), float(np.max(err_h / tol_h)))
+    assert np.array_equal(y_gpu, gpu_q4_0_bias(wd, h_gpu, db))
+    assert_within(gpu_q4_0_bias(wd, st["h32"], db), st["y"], st["y_terms"], "down over oracle h")
+    extra = np.abs(oracle.dequantize_q4_0(wd)) @ np.abs(h_gpu.astype(np.float64) -
+                                                       st["h32"].astype(np.float64))
+    assert_within(y_gpu, st["y"], st["y_terms"] + extra / oracle.GEMV_REL, "chain y")
+
+
+def test_gelu_ffn_zero_up_weights():
+    """Zero up weights: h = gelu(up_bias) exactly as the oracle rounds it, up to
+    the device exp; with no up bias h is exactly 0 and y is the down bias."""
+    banner("gelu ffn zero up")
+    hidden, inter = 256, 1024
+    wu = synth.q4_0_weights(synth.rng(45, 1), inter, hidden, d_fixed=0.0)
+    wd = synth.q4_0_weights(synth.rng(45, 2), hidden, inter)
+    x = synth.activation(synth.rng(45, 0), hidden)
+    db = synth.activation(synth.rng(45, 3), hidden)
+    h = empty_f32(inter)
+    y = empty_f32(hidden)
+    rz.rz_gelu_ffn_q4_0(dev_bytes(wu), dev_bytes(wd), dev_f32(x), None, dev_f32(db), h, y,
+                        hidden, inter)
+    assert np.all(host(h) == 0) and np.array_equal(host(y), db)
+    ub = (4.0 * synth.activation(synth.rng(45, 4), inter)).astype(np.float32)
+    rz.rz_gelu_ffn_q4_0(dev_bytes(wu), dev_bytes(wd), dev_f32(x), dev_f32(ub), dev_f32(db), h, y,
+                        hidden, inter)
+    ref = oracle.gelu(ub.astype(np.float64))
+    assert np.all(np.abs(host(h) - ref) <= 8 * 2.0 ** -24 * np.abs(ref) + 1e-6)
+
+
 # ------------------------------------------------------------------ errors on device tensors
 def test_binding_errors_on_gpu():
     banner("binding errors")
