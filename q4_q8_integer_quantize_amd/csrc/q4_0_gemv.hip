@@ -116,25 +116,33 @@ __device__ __forceinline__ void load_x40(X40<S, Q8>& xs, const Q40Args& a, int p
   }
 }
 
+// v & m, opaque to the compiler's known-bits analysis: with the nibble mask
+// visible it folds each byte conversion below into a 4-bit extract plus a
+// byte-0 conversion (two instructions per weight); behind this AND every byte
+// converts with one v_cvt_f32_ubyte{0..3}.
+__device__ __forceinline__ uint32_t opaque_and(uint32_t v, uint32_t m) {
+  uint32_t r;
+  asm("v_and_b32 %0, %1, %2" : "=v"(r) : "v"(v), "v"(m));
+  return r;
+}
+
 // sum_l q_l * x_l over one block; qs dwords hold values 4k..4k+3 (low
-// nibbles) and 16+4k..16+4k+3 (high nibbles).  Eight independent partial sums
-// (one per byte position and nibble) keep the fma chains short; they are added
-// pairwise at the end.
+// nibbles) and 16+4k..16+4k+3 (high nibbles).  Four independent partial sums
+// (one per byte position) keep the fma chains short; they are added pairwise
+// at the end.
 __device__ __forceinline__ float block_dot_f32(const uint32_t qs[4], const float* x) {
-  float acc[8];
-#pragma unroll
-  for (int b = 0; b < 8; ++b) acc[b] = 0.0f;
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const uint32_t lo = qs[k] & 0x0F0F0F0Fu;
-    const uint32_t hi = (qs[k] >> 4) & 0x0F0F0F0Fu;
+    const uint32_t lo = opaque_and(qs[k], 0x0F0F0F0Fu);
+    const uint32_t hi = opaque_and(qs[k] >> 4, 0x0F0F0F0Fu);
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       acc[b] = fmaf((float)((lo >> (8 * b)) & 0xffu), x[4 * k + b], acc[b]);
-      acc[4 + b] = fmaf((float)((hi >> (8 * b)) & 0xffu), x[16 + 4 * k + b], acc[4 + b]);
+      acc[b] = fmaf((float)((hi >> (8 * b)) & 0xffu), x[16 + 4 * k + b], acc[b]);
     }
   }
-  return ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
 }
 
 __device__ __forceinline__ int block_dot_q8(const uint32_t qs[4], const int* q8) {
