@@ -7,9 +7,10 @@
 //
 // A lane owns a pair of 18-byte blocks (36 bytes, 4-byte aligned when in_dim
 // is a multiple of 64): block A = d | qs at bytes 0..17, block B at 18..35.
-// LPR lanes share a row (RW = 64/LPR rows side by side); S pair slots per
-// lane keep that lane's activation values in registers for the wave's life,
-// and each wave streams G row groups with P of them requested ahead.
+// LPR lanes share a row (RW = 64/LPR rows side by side) and a lane takes S
+// pairs of it; each wave streams G row groups with P of them requested ahead.
+// A Q8_1 activation stays in the lane's registers for the wave's life; an
+// fp32 activation (64 values a pair) is staged once per workgroup in LDS.
 //   fp32 x : sum_l q_l x_l per block, then d * (sum - 8 * sum_l x_l)
 //   Q8_1 x : isum = sum_l q_l q8_l - 8 * sum_l q8_l (exact), then d * d_x * isum
 //
@@ -42,76 +43,47 @@ struct Q40Args {
   int act;            // EPI: 1 = GELU after the bias (the GELU FFN's up projection)
 };
 
-template <int S, bool Q8>
-struct X40;
-
+// Q8_1 activation slots of one lane: the codes of its S pairs (two blocks
+// each), the blocks' d, and each block's code sum (for the -8 offset).
 template <int S>
-struct X40<S, false> {
-  float v[S][64];
-  float sum[S][2];
-};
-
-template <int S>
-struct X40<S, true> {
+struct X40Q8 {
   int q[S][16];
   float dx[S][2];
   int qsum[S][2];
 };
 
-template <int LPR, int S, bool Q8>
-__device__ __forceinline__ void load_x40(X40<S, Q8>& xs, const Q40Args& a, int ps) {
+template <int LPR, int S>
+__device__ __forceinline__ void load_x40_q8(X40Q8<S>& xs, const Q40Args& a, int ps) {
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     const int p = s * LPR + ps;
     const bool on = p < a.npairs;
     const long gp = (long)a.p0 + p;
-    if constexpr (!Q8) {
-      if (on) {
-        const float4* xp = (const float4*)((const float*)a.x + gp * 64);
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-          const float4 f = xp[k];
-          xs.v[s][4 * k] = f.x; xs.v[s][4 * k + 1] = f.y;
-          xs.v[s][4 * k + 2] = f.z; xs.v[s][4 * k + 3] = f.w;
-        }
-      } else {
-#pragma unroll
-        for (int k = 0; k < 64; ++k) xs.v[s][k] = 0.0f;
-      }
+    if (on) {
+      const uint8_t* xb = (const uint8_t*)a.x + gp * 2 * kQ8Bytes;
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
-        float t = 0.0f;
+        const uint8_t* blk = xb + b * kQ8Bytes;
+        xs.dx[s][b] = ((const float*)blk)[0];
+        const uint2* qp = (const uint2*)(blk + 8);
 #pragma unroll
-        for (int k = 0; k < 32; ++k) t += xs.v[s][32 * b + k];
-        xs.sum[s][b] = t;
+        for (int k = 0; k < 4; ++k) {
+          const uint2 u = qp[k];
+          xs.q[s][8 * b + 2 * k] = (int)u.x;
+          xs.q[s][8 * b + 2 * k + 1] = (int)u.y;
+        }
       }
     } else {
-      if (on) {
-        const uint8_t* xb = (const uint8_t*)a.x + gp * 2 * kQ8Bytes;
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          const uint8_t* blk = xb + b * kQ8Bytes;
-          xs.dx[s][b] = ((const float*)blk)[0];
-          const uint2* qp = (const uint2*)(blk + 8);
+      for (int k = 0; k < 16; ++k) xs.q[s][k] = 0;
+      xs.dx[s][0] = xs.dx[s][1] = 0.0f;
+    }
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const uint2 u = qp[k];
-            xs.q[s][8 * b + 2 * k] = (int)u.x;
-            xs.q[s][8 * b + 2 * k + 1] = (int)u.y;
-          }
-        }
-      } else {
+    for (int b = 0; b < 2; ++b) {
+      int t = 0;
 #pragma unroll
-        for (int k = 0; k < 16; ++k) xs.q[s][k] = 0;
-        xs.dx[s][0] = xs.dx[s][1] = 0.0f;
-      }
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        int t = 0;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) t = dot4(xs.q[s][8 * b + k], 0x01010101, t);
-        xs.qsum[s][b] = t;
-      }
+      for (int k = 0; k < 8; ++k) t = dot4(xs.q[s][8 * b + k], 0x01010101, t);
+      xs.qsum[s][b] = t;
     }
   }
 }
@@ -215,18 +187,51 @@ __device__ __forceinline__ void wave_best(float& bv, int& bi) {
 
 constexpr int kNoRow = 0x7fffffff;
 
+// fp32 activation staged in LDS: pair p of the launch at byte
+// p * kPairStride -- its 64 values, then the sums of its two blocks.  The 16
+// bytes of padding per pair put the pairs of neighbouring lanes in different
+// LDS banks.
+constexpr int kPairStride = 272;
+constexpr int kXlMaxPairs = 256;   // 16384 values a launch, 69,632 bytes of LDS
+
+template <int S, int LPR>
+constexpr size_t xl_lds_bytes() { return (size_t)S * LPR * kPairStride; }
+
 // Wave w of W takes the G row groups w, w+W, ... (a group is RW*R rows),
 // unrolled with P groups requested ahead, as in q4k_q8_gemv_kernel.
+// Q8_1 x: each lane keeps the codes of its pairs in registers.  fp32 x: the
+// workgroup first copies the launch's activation pairs (S*LPR of them, zeros
+// past npairs) into LDS with their block sums and the lanes read them from
+// there, so a lane may take many pairs of a row (64 fp32 values a pair would
+// not fit in registers).
 template <int LPR, int S, int R, int G, int P, bool Q8, bool ACC, bool EPI>
 __global__ __launch_bounds__(256) void q4_0_gemv_kernel(Q40Args a) {
+  constexpr bool XL = !Q8;
   constexpr int RW = kWave / LPR;
   const int lane = threadIdx.x & (kWave - 1);
   const int rs = lane / LPR, ps = lane % LPR;
   const long nwaves = (long)gridDim.x * 4;
   const long wid = __builtin_amdgcn_readfirstlane(blockIdx.x * 4u + (threadIdx.x >> 6));
   const size_t row_bytes = (size_t)a.npairs_row * 36;
-  X40<S, Q8> xs;
-  load_x40<LPR, S, Q8>(xs, a, ps);
+  extern __shared__ __attribute__((aligned(16))) uint8_t xl[];
+  constexpr int kChunks = S * LPR * 16;                  // 16-byte chunks staged
+  constexpr int kIters = (kChunks + 255) / 256;
+  u32x4 xin[XL ? kIters : 1];
+  X40Q8<Q8 ? S : 1> xs;
+  if constexpr (XL) {
+    // (1) request the activation: chunk g = pair g/16, values 4(g%16) .. +3
+    const uint32_t xbytes = (uint32_t)a.npairs * 256u;
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const float*)a.x + (size_t)a.p0 * 64), (short)0, (int)xbytes, kBufferWord3);
+#pragma unroll
+    for (int j = 0; j < kIters; ++j) {
+      const uint32_t g = (uint32_t)(j * 256) + threadIdx.x;
+      const uint32_t off = g * 16u < xbytes ? g * 16u : xbytes;
+      xin[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
+    }
+  } else {
+    load_x40_q8<LPR, S>(xs, a, ps);
+  }
   // EPI: the bias of a group's rows is requested right after its weight tile
   // (a null bias reads as an empty buffer and is not added)
   const bool has_bias = EPI && a.bias != nullptr;
@@ -253,6 +258,28 @@ __global__ __launch_bounds__(256) void q4_0_gemv_kernel(Q40Args a) {
     load_bias(k);
   }
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (XL) {
+    // (3) stage into LDS; eight consecutive threads hold one block and sum it
+    // (vector loads retire in order: this waits for the activation only)
+#pragma unroll
+    for (int j = 0; j < kIters; ++j) {
+      const int g = j * 256 + (int)threadIdx.x;
+      const u32x4 v = xin[j];
+      const uint32_t v0 = v.x, v1 = v.y, v2 = v.z, v3 = v.w;
+      const float part = (__builtin_bit_cast(float, v0) + __builtin_bit_cast(float, v1)) +
+                         (__builtin_bit_cast(float, v2) + __builtin_bit_cast(float, v3));
+      const float bsum = group_sum_dpp<8>(part);
+      if (g < kChunks) {
+        uint8_t* pair = xl + (g >> 4) * kPairStride;
+        *(u32x4*)(pair + 16 * (g & 15)) = v;
+        if ((g & 7) == 7) *(float*)(pair + 256 + 4 * ((g & 15) >> 3)) = bsum;
+      }
+    }
+    // LDS-only release/acquire: the weight loads stay in flight
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  }
 #pragma unroll
   for (int k = 0; k < G; ++k) {
     if (k + P < G) {
@@ -261,12 +288,26 @@ __global__ __launch_bounds__(256) void q4_0_gemv_kernel(Q40Args a) {
     }
     __builtin_amdgcn_sched_barrier(0);
     const long row_base = (wid + k * nwaves) * (RW * R);
-    float acc[R];
+    float ar[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      float ar = 0.0f;
+    for (int r = 0; r < R; ++r) ar[r] = 0.0f;
 #pragma unroll
-      for (int s = 0; s < S; ++s) {
+    for (int s = 0; s < S; ++s) {
+      // fp32 x: this slot's pair from LDS, shared by the R rows
+      float xv[XL ? 64 : 1], xsum[2];
+      if constexpr (XL) {
+        const uint8_t* pair = xl + (s * LPR + ps) * kPairStride;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+          const float4 f = *(const float4*)(pair + 16 * c);
+          xv[4 * c] = f.x; xv[4 * c + 1] = f.y; xv[4 * c + 2] = f.z; xv[4 * c + 3] = f.w;
+        }
+        const float2 sm = *(const float2*)(pair + 256);
+        xsum[0] = sm.x;
+        xsum[1] = sm.y;
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
         const u32x4_a4 A = t[k].v0[r][s], B = t[k].v1[r][s];
         const float dA = f16_lo(A.x), dB = f16_hi(B.x);
         const uint32_t qa[4] = {__builtin_amdgcn_alignbyte(A.y, A.x, 2),
@@ -274,20 +315,22 @@ __global__ __launch_bounds__(256) void q4_0_gemv_kernel(Q40Args a) {
                                 __builtin_amdgcn_alignbyte(A.w, A.z, 2),
                                 __builtin_amdgcn_alignbyte(B.x, A.w, 2)};
         const uint32_t qb[4] = {B.y, B.z, B.w, t[k].v8[r][s]};
-        if constexpr (!Q8) {
-          const float sa = block_dot_f32(qa, &xs.v[s][0]);
-          const float sb = block_dot_f32(qb, &xs.v[s][32]);
-          ar = fmaf(dA, fmaf(-8.0f, xs.sum[s][0], sa), ar);
-          ar = fmaf(dB, fmaf(-8.0f, xs.sum[s][1], sb), ar);
+        if constexpr (XL) {
+          const float sa = block_dot_f32(qa, &xv[0]);
+          const float sb = block_dot_f32(qb, &xv[32]);
+          ar[r] = fmaf(dA, fmaf(-8.0f, xsum[0], sa), ar[r]);
+          ar[r] = fmaf(dB, fmaf(-8.0f, xsum[1], sb), ar[r]);
         } else {
           const int ia = block_dot_q8(qa, &xs.q[s][0]) - 8 * xs.qsum[s][0];
           const int ib = block_dot_q8(qb, &xs.q[s][8]) - 8 * xs.qsum[s][1];
-          ar = fmaf(dA * xs.dx[s][0], (float)ia, ar);
-          ar = fmaf(dB * xs.dx[s][1], (float)ib, ar);
+          ar[r] = fmaf(dA * xs.dx[s][0], (float)ia, ar[r]);
+          ar[r] = fmaf(dB * xs.dx[s][1], (float)ib, ar[r]);
         }
       }
-      acc[r] = group_sum_dpp<LPR>(ar);
     }
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = group_sum_dpp<LPR>(ar[r]);
     if (ps == LPR - 1) {   // the lane that holds the reduced row sum
 #pragma unroll
       for (int r = 0; r < R; ++r) {
@@ -368,78 +411,133 @@ __global__ __launch_bounds__(1024) void argmax_merge_kernel(const float* __restr
   }
 }
 
-template <bool Q8>
-constexpr int pair_slots_max() { return Q8 ? 4 : 2; }
-
 template <int LPR, int S, int R, int G, bool Q8>
 static hipError_t launch_q40_g(const Q40Args& a, long groups, bool epi, hipStream_t st) {
   constexpr int P = G > 2 ? 2 : (G > 1 ? G - 1 : 1);
   const long waves = (groups + G - 1) / G;
   const unsigned grid = (unsigned)((waves + 3) / 4);
+  const size_t lds = Q8 ? 0 : xl_lds_bytes<S, LPR>();
   if (epi && a.part_val != nullptr && (long)grid != a.part_count) return hipErrorInvalidValue;
   if (epi) {
     if (a.accumulate)
-      hipLaunchKernelGGL((q4_0_gemv_kernel<LPR, S, R, G, P, Q8, true, true>), dim3(grid), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((q4_0_gemv_kernel<LPR, S, R, G, P, Q8, true, true>), dim3(grid), dim3(256), lds, st, a);
     else
-      hipLaunchKernelGGL((q4_0_gemv_kernel<LPR, S, R, G, P, Q8, false, true>), dim3(grid), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((q4_0_gemv_kernel<LPR, S, R, G, P, Q8, false, true>), dim3(grid), dim3(256), lds, st, a);
   } else if (a.accumulate) {
-    hipLaunchKernelGGL((q4_0_gemv_kernel<LPR, S, R, G, P, Q8, true, false>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((q4_0_gemv_kernel<LPR, S, R, G, P, Q8, true, false>), dim3(grid), dim3(256), lds, st, a);
   } else {
-    hipLaunchKernelGGL((q4_0_gemv_kernel<LPR, S, R, G, P, Q8, false, false>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((q4_0_gemv_kernel<LPR, S, R, G, P, Q8, false, false>), dim3(grid), dim3(256), lds, st, a);
   }
   return hipGetLastError();
 }
 
-// Groups per wave: the Q8_1 form streams best with many one-group waves
-// (latency hidden by occupancy); the fp32 form, whose arithmetic is heavier,
-// with two groups per wave once there are enough rows (measured on the
-// 151936 x 1024 LM head: 16.6 us and 23.9 us).
-// Rows per group and groups per wave of a chunk of np pairs (the launch shape
-// that run_q40 takes; q40_grid uses it to size the per-workgroup pairs).
+// Pairs a launch covers: Q8_1 x keeps up to 4 pairs a lane in registers (64
+// lanes a row); fp32 x is staged in LDS, at most kXlChunkPairs pairs (60,928
+// bytes, within a workgroup's 64 KiB).
+constexpr int kQ8ChunkPairs = 256;
+constexpr int kXlChunkPairs = 224;
+
+// Launch shape of a column chunk of np pairs (run_q40_chunk and run_xl_chunk
+// take exactly these; q4_0_lm_head_partials uses them to size the
+// per-workgroup pairs).
+//   Q8_1 x: LPR lanes a row up to 32 (one pair a lane), else 64 lanes and
+//           ceil(np/64) pairs a lane; R = 4 / pairs rows unrolled (at least 1).
+//   fp32 x: up to 16 pairs, one pair a lane and 4 rows unrolled; longer rows
+//           8, 16 or 32 lanes a row (8 rows side by side at 8) and up to 8
+//           pairs a lane, one row a group -- every lane busy for 40-pair and
+//           160-pair rows.
+// Groups per wave: Q8_1 x streams best with many one-group waves; fp32 x
+// takes two once there are 2048 groups (measured on the 151936 x 1024 LM head).
 struct Q40Shape {
   int lpr, s, r, g;
 };
 
+static int pow2_at_least(int v) {
+  int p = 1;
+  while (p < v) p *= 2;
+  return p;
+}
+
 static Q40Shape q40_shape(int np, long out_dim, bool q8) {
   Q40Shape sh;
-  if (np <= 32) {
-    sh.lpr = np <= 1 ? 1 : np <= 2 ? 2 : np <= 4 ? 4 : np <= 8 ? 8 : np <= 16 ? 16 : 32;
+  if (q8) {
+    sh.lpr = np <= 32 ? pow2_at_least(np) : 64;
+    sh.s = np <= 32 ? 1 : (np + 63) / 64;
+    sh.r = sh.s >= 4 ? 1 : 4 / sh.s;
+  } else if (np <= 16) {
+    sh.lpr = pow2_at_least(np);
     sh.s = 1;
+    sh.r = 4;
   } else {
-    sh.lpr = 64;
-    sh.s = (np + 63) / 64;
+    sh.lpr = np <= 64 ? 8 : np <= 128 ? 16 : 32;
+    sh.s = (np + sh.lpr - 1) / sh.lpr;
+    sh.r = 1;
   }
-  sh.r = sh.s >= 4 ? 1 : 4 / sh.s;
-  const long groups = (out_dim + (long)(kWave / sh.lpr) * sh.r - 1) / ((long)(kWave / sh.lpr) * sh.r);
+  const long rows_per_group = (long)(kWave / sh.lpr) * sh.r;
+  const long groups = (out_dim + rows_per_group - 1) / rows_per_group;
   sh.g = (!q8 && groups >= 2048) ? 2 : 1;
   return sh;
 }
 
-template <int LPR, int S, bool Q8>
+template <int LPR, int S, int R, bool Q8>
 static hipError_t run_q40(const Q40Args& a, bool epi, hipStream_t st) {
-  constexpr int R = S >= 4 ? 1 : 4 / S;
   constexpr int RW = kWave / LPR;
   const long rows_per_group = (long)RW * R;
   const long groups = (a.out_dim + rows_per_group - 1) / rows_per_group;
-  // Groups per wave as in q40_shape.
   if (!Q8 && groups >= 2048) return launch_q40_g<LPR, S, R, 2, Q8>(a, groups, epi, st);
   return launch_q40_g<LPR, S, R, 1, Q8>(a, groups, epi, st);
 }
 
-template <bool Q8>
-static hipError_t run_q40_chunk(const Q40Args& a, bool epi, hipStream_t st) {
+// Q8_1 activation.
+static hipError_t run_q8_chunk(const Q40Args& a, bool epi, hipStream_t st) {
   const int np = a.npairs;
-  if (np <= 1) return run_q40<1, 1, Q8>(a, epi, st);
-  if (np <= 2) return run_q40<2, 1, Q8>(a, epi, st);
-  if (np <= 4) return run_q40<4, 1, Q8>(a, epi, st);
-  if (np <= 8) return run_q40<8, 1, Q8>(a, epi, st);
-  if (np <= 16) return run_q40<16, 1, Q8>(a, epi, st);
-  if (np <= 32) return run_q40<32, 1, Q8>(a, epi, st);
+  if (np <= 1) return run_q40<1, 1, 4, true>(a, epi, st);
+  if (np <= 2) return run_q40<2, 1, 4, true>(a, epi, st);
+  if (np <= 4) return run_q40<4, 1, 4, true>(a, epi, st);
+  if (np <= 8) return run_q40<8, 1, 4, true>(a, epi, st);
+  if (np <= 16) return run_q40<16, 1, 4, true>(a, epi, st);
+  if (np <= 32) return run_q40<32, 1, 4, true>(a, epi, st);
   switch ((np + 63) / 64) {
-    case 1: return run_q40<64, 1, Q8>(a, epi, st);
-    case 2: return run_q40<64, 2, Q8>(a, epi, st);
-    case 3: if constexpr (Q8) return run_q40<64, 3, Q8>(a, epi, st); else return hipErrorInvalidValue;
-    case 4: if constexpr (Q8) return run_q40<64, 4, Q8>(a, epi, st); else return hipErrorInvalidValue;
+    case 1: return run_q40<64, 1, 4, true>(a, epi, st);
+    case 2: return run_q40<64, 2, 2, true>(a, epi, st);
+    case 3: return run_q40<64, 3, 1, true>(a, epi, st);
+    case 4: return run_q40<64, 4, 1, true>(a, epi, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// fp32 activation, staged in LDS.
+static hipError_t run_xl_chunk(const Q40Args& a, bool epi, hipStream_t st) {
+  const int np = a.npairs;
+  if (np <= 1) return run_q40<1, 1, 4, false>(a, epi, st);
+  if (np <= 2) return run_q40<2, 1, 4, false>(a, epi, st);
+  if (np <= 4) return run_q40<4, 1, 4, false>(a, epi, st);
+  if (np <= 8) return run_q40<8, 1, 4, false>(a, epi, st);
+  if (np <= 16) return run_q40<16, 1, 4, false>(a, epi, st);
+  if (np <= 64) {
+    switch ((np + 7) / 8) {
+      case 3: return run_q40<8, 3, 1, false>(a, epi, st);
+      case 4: return run_q40<8, 4, 1, false>(a, epi, st);
+      case 5: return run_q40<8, 5, 1, false>(a, epi, st);
+      case 6: return run_q40<8, 6, 1, false>(a, epi, st);
+      case 7: return run_q40<8, 7, 1, false>(a, epi, st);
+      case 8: return run_q40<8, 8, 1, false>(a, epi, st);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (np <= 128) {
+    switch ((np + 15) / 16) {
+      case 5: return run_q40<16, 5, 1, false>(a, epi, st);
+      case 6: return run_q40<16, 6, 1, false>(a, epi, st);
+      case 7: return run_q40<16, 7, 1, false>(a, epi, st);
+      case 8: return run_q40<16, 8, 1, false>(a, epi, st);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  switch ((np + 31) / 32) {
+    case 5: return run_q40<32, 5, 1, false>(a, epi, st);
+    case 6: return run_q40<32, 6, 1, false>(a, epi, st);
+    case 7: return run_q40<32, 7, 1, false>(a, epi, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -447,12 +545,13 @@ static hipError_t run_q40_chunk(const Q40Args& a, bool epi, hipStream_t st) {
 // Column chunks; the last one runs the epilogue when `epi`.
 template <bool Q8>
 static hipError_t run_q40_all(Q40Args a, bool epi, hipStream_t st) {
-  const int chunk = 64 * pair_slots_max<Q8>();
+  const int chunk = Q8 ? kQ8ChunkPairs : kXlChunkPairs;
   for (int p0 = 0; p0 < a.npairs_row; p0 += chunk) {
     a.p0 = p0;
     a.npairs = a.npairs_row - p0 < chunk ? a.npairs_row - p0 : chunk;
     a.accumulate = p0 > 0;
-    const hipError_t e = run_q40_chunk<Q8>(a, epi && p0 + chunk >= a.npairs_row, st);
+    const bool last = p0 + chunk >= a.npairs_row;
+    const hipError_t e = Q8 ? run_q8_chunk(a, epi && last, st) : run_xl_chunk(a, epi && last, st);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -485,7 +584,7 @@ hipError_t launch_q4_0_gemv(const uint8_t* w, const void* x, int x_format, float
 long q4_0_lm_head_partials(int out_dim, int in_dim, int x_format) {
   const bool q8 = x_format == 1;
   const int npairs_row = in_dim / 64;
-  const int chunk = 64 * (q8 ? pair_slots_max<true>() : pair_slots_max<false>());
+  const int chunk = q8 ? kQ8ChunkPairs : kXlChunkPairs;
   const int last = npairs_row - ((npairs_row - 1) / chunk) * chunk;   // pairs of the last chunk
   const Q40Shape sh = q40_shape(last, out_dim, q8);
   const long rows_per_group = (long)(kWave / sh.lpr) * sh.r;
