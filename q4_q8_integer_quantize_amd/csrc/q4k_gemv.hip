@@ -24,9 +24,9 @@ namespace rz {
 constexpr int kTilesInFlight = 2;   // P: weight tiles requested ahead of the one reduced
 constexpr long kTargetWaves = 1024; // about one wave per SIMD (256 CUs x 4)
 
-// Activation slots a lane holds in registers (10 VGPRs per slot and token).
-template <int NT>
-constexpr int slots_max() { return NT <= 2 ? 8 : (NT == 4 ? 4 : 2); }
+// Activation slots a lane holds in registers (10 VGPRs per slot and token);
+// this kernel runs 1 or 2 tokens (more go to the matrix cores).
+constexpr int kSlotsMax = 8;
 
 // Rows unrolled per group: two for short rows of one or two tokens, else one.
 template <int S, int NT>
@@ -58,19 +58,15 @@ static hipError_t launch_g(const Q4KGemvArgs& a, long groups, Epi epi, hipStream
 // better than many short ones.
 template <int TPR, int S, int NT>
 static hipError_t run_q4k(const Q4KGemvArgs& a, Epi epi, hipStream_t st) {
-  if constexpr (S > slots_max<NT>()) {
-    return hipErrorInvalidValue;
-  } else {
-    constexpr int R = rows_unrolled<S, NT>();
-    constexpr int RW = 8 / TPR;
-    const long rows_per_group = (long)RW * R;
-    const long groups = (a.out_dim + rows_per_group - 1) / rows_per_group;
-    const long per_wave = (groups + kTargetWaves - 1) / kTargetWaves;
-    if (per_wave <= 1) return launch_g<TPR, S, NT, 1>(a, groups, epi, st);
-    if (per_wave <= 2) return launch_g<TPR, S, NT, 2>(a, groups, epi, st);
-    if (per_wave <= 4) return launch_g<TPR, S, NT, 4>(a, groups, epi, st);
-    return launch_g<TPR, S, NT, 8>(a, groups, epi, st);
-  }
+  constexpr int R = rows_unrolled<S, NT>();
+  constexpr int RW = 8 / TPR;
+  const long rows_per_group = (long)RW * R;
+  const long groups = (a.out_dim + rows_per_group - 1) / rows_per_group;
+  const long per_wave = (groups + kTargetWaves - 1) / kTargetWaves;
+  if (per_wave <= 1) return launch_g<TPR, S, NT, 1>(a, groups, epi, st);
+  if (per_wave <= 2) return launch_g<TPR, S, NT, 2>(a, groups, epi, st);
+  if (per_wave <= 4) return launch_g<TPR, S, NT, 4>(a, groups, epi, st);
+  return launch_g<TPR, S, NT, 8>(a, groups, epi, st);
 }
 
 template <int NT>
@@ -94,7 +90,7 @@ static hipError_t run_q4k_chunk(const Q4KGemvArgs& a, Epi epi, hipStream_t st) {
 
 template <int NT>
 static hipError_t run_q4k_all(Q4KGemvArgs a, hipStream_t st) {
-  const int chunk = 8 * slots_max<NT>();
+  const int chunk = 8 * kSlotsMax;
   for (int sb0 = 0; sb0 < a.nsb_row; sb0 += chunk) {
     a.sb0 = sb0;
     a.nsb = a.nsb_row - sb0 < chunk ? a.nsb_row - sb0 : chunk;
@@ -120,9 +116,7 @@ hipError_t launch_q4k_q8_gemv(const uint8_t* w, const uint8_t* xq, float* y, int
   if (n_tokens >= kMfmaMinTokens)
     return launch_q4k_q8_gemm_mfma(w, xq, y, out_dim, in_dim, n_tokens, stream, r);
   if (n_tokens == 1) return run_q4k_all<1>(a, stream);
-  if (n_tokens == 2) return run_q4k_all<2>(a, stream);
-  if (n_tokens <= 4) return run_q4k_all<4>(a, stream);
-  return run_q4k_all<8>(a, stream);
+  return run_q4k_all<2>(a, stream);
 }
 
 }  // namespace rz
