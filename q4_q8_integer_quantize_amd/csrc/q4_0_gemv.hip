@@ -192,7 +192,6 @@ constexpr int kNoRow = 0x7fffffff;
 // bytes of padding per pair put the pairs of neighbouring lanes in different
 // LDS banks.
 constexpr int kPairStride = 272;
-constexpr int kXlMaxPairs = 256;   // 16384 values a launch, 69,632 bytes of LDS
 
 template <int S, int LPR>
 constexpr size_t xl_lds_bytes() { return (size_t)S * LPR * kPairStride; }
@@ -414,6 +413,7 @@ __global__ __launch_bounds__(1024) void argmax_merge_kernel(const float* __restr
 template <int LPR, int S, int R, int G, bool Q8>
 static hipError_t launch_q40_g(const Q40Args& a, long groups, bool epi, hipStream_t st) {
   constexpr int P = G > 2 ? 2 : (G > 1 ? G - 1 : 1);
+  static_assert(Q8 || xl_lds_bytes<S, LPR>() <= 65536, "staged activation within 64 KiB of LDS");
   const long waves = (groups + G - 1) / G;
   const unsigned grid = (unsigned)((waves + 3) / 4);
   const size_t lds = Q8 ? 0 : xl_lds_bytes<S, LPR>();
@@ -436,6 +436,7 @@ static hipError_t launch_q40_g(const Q40Args& a, long groups, bool epi, hipStrea
 // bytes, within a workgroup's 64 KiB).
 constexpr int kQ8ChunkPairs = 256;
 constexpr int kXlChunkPairs = 224;
+constexpr long kXlTwoGroups = 8192;
 
 // Launch shape of a column chunk of np pairs (run_q40_chunk and run_xl_chunk
 // take exactly these; q4_0_lm_head_partials uses them to size the
@@ -443,11 +444,17 @@ constexpr int kXlChunkPairs = 224;
 //   Q8_1 x: LPR lanes a row up to 32 (one pair a lane), else 64 lanes and
 //           ceil(np/64) pairs a lane; R = 4 / pairs rows unrolled (at least 1).
 //   fp32 x: up to 16 pairs, one pair a lane and 4 rows unrolled; longer rows
-//           8, 16 or 32 lanes a row (8 rows side by side at 8) and up to 8
-//           pairs a lane, one row a group -- every lane busy for 40-pair and
-//           160-pair rows.
+//           one row a group, with 8 lanes a row up to 32 pairs, 16 up to 64,
+//           32 up to 128 and 64 up to 192 (3 or 4 pairs a lane; at most a
+//           third of the slots idle), and 32 lanes of 7 pairs up to 224 (64
+//           lanes of 4 would need more than 64 KiB of LDS).  Measured: twice
+//           the waves with a few idle slots beat every lane busy (40 pairs:
+//           16 lanes x 3 at 6.4 us against 8 x 5 at 7.4 us; 160 pairs: 64 x 3
+//           at 7.9 us against 32 x 5 at 8.8 us; 128 pairs: 32 x 4 at 7.1 us
+//           against 16 x 8 at 8.3 us).
 // Groups per wave: Q8_1 x streams best with many one-group waves; fp32 x
-// takes two once there are 2048 groups (measured on the 151936 x 1024 LM head).
+// takes two once there are 8192 groups (the 151936 x 1024 LM head; at 2560
+// and 3584 groups one group a wave was faster).
 struct Q40Shape {
   int lpr, s, r, g;
 };
@@ -469,13 +476,13 @@ static Q40Shape q40_shape(int np, long out_dim, bool q8) {
     sh.s = 1;
     sh.r = 4;
   } else {
-    sh.lpr = np <= 64 ? 8 : np <= 128 ? 16 : 32;
+    sh.lpr = np <= 32 ? 8 : np <= 64 ? 16 : np <= 128 ? 32 : np <= 192 ? 64 : 32;
     sh.s = (np + sh.lpr - 1) / sh.lpr;
     sh.r = 1;
   }
   const long rows_per_group = (long)(kWave / sh.lpr) * sh.r;
   const long groups = (out_dim + rows_per_group - 1) / rows_per_group;
-  sh.g = (!q8 && groups >= 2048) ? 2 : 1;
+  sh.g = (!q8 && groups >= kXlTwoGroups) ? 2 : 1;
   return sh;
 }
 
@@ -484,7 +491,7 @@ static hipError_t run_q40(const Q40Args& a, bool epi, hipStream_t st) {
   constexpr int RW = kWave / LPR;
   const long rows_per_group = (long)RW * R;
   const long groups = (a.out_dim + rows_per_group - 1) / rows_per_group;
-  if (!Q8 && groups >= 2048) return launch_q40_g<LPR, S, R, 2, Q8>(a, groups, epi, st);
+  if (!Q8 && groups >= kXlTwoGroups) return launch_q40_g<LPR, S, R, 2, Q8>(a, groups, epi, st);
   return launch_q40_g<LPR, S, R, 1, Q8>(a, groups, epi, st);
 }
 
@@ -514,32 +521,15 @@ static hipError_t run_xl_chunk(const Q40Args& a, bool epi, hipStream_t st) {
   if (np <= 4) return run_q40<4, 1, 4, false>(a, epi, st);
   if (np <= 8) return run_q40<8, 1, 4, false>(a, epi, st);
   if (np <= 16) return run_q40<16, 1, 4, false>(a, epi, st);
-  if (np <= 64) {
-    switch ((np + 7) / 8) {
-      case 3: return run_q40<8, 3, 1, false>(a, epi, st);
-      case 4: return run_q40<8, 4, 1, false>(a, epi, st);
-      case 5: return run_q40<8, 5, 1, false>(a, epi, st);
-      case 6: return run_q40<8, 6, 1, false>(a, epi, st);
-      case 7: return run_q40<8, 7, 1, false>(a, epi, st);
-      case 8: return run_q40<8, 8, 1, false>(a, epi, st);
-      default: return hipErrorInvalidValue;
-    }
-  }
-  if (np <= 128) {
-    switch ((np + 15) / 16) {
-      case 5: return run_q40<16, 5, 1, false>(a, epi, st);
-      case 6: return run_q40<16, 6, 1, false>(a, epi, st);
-      case 7: return run_q40<16, 7, 1, false>(a, epi, st);
-      case 8: return run_q40<16, 8, 1, false>(a, epi, st);
-      default: return hipErrorInvalidValue;
-    }
-  }
-  switch ((np + 31) / 32) {
-    case 5: return run_q40<32, 5, 1, false>(a, epi, st);
-    case 6: return run_q40<32, 6, 1, false>(a, epi, st);
-    case 7: return run_q40<32, 7, 1, false>(a, epi, st);
-    default: return hipErrorInvalidValue;
-  }
+  if (np <= 24) return run_q40<8, 3, 1, false>(a, epi, st);
+  if (np <= 32) return run_q40<8, 4, 1, false>(a, epi, st);
+  if (np <= 48) return run_q40<16, 3, 1, false>(a, epi, st);
+  if (np <= 64) return run_q40<16, 4, 1, false>(a, epi, st);
+  if (np <= 96) return run_q40<32, 3, 1, false>(a, epi, st);
+  if (np <= 128) return run_q40<32, 4, 1, false>(a, epi, st);
+  if (np <= 192) return run_q40<64, 3, 1, false>(a, epi, st);
+  if (np <= kXlChunkPairs) return run_q40<32, 7, 1, false>(a, epi, st);
+  return hipErrorInvalidValue;
 }
 
 // Column chunks; the last one runs the epilogue when `epi`.

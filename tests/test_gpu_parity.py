@@ -461,7 +461,12 @@ def test_q4_0_hand_worked_block_gpu():
 @pytest.mark.parametrize("fmt", [0, 1])
 @pytest.mark.parametrize("out_dim,in_dim", [
     (1, 64), (3, 128), (65, 192), (257, 1024), (130, 4096),
-    (33, 8192),      # fp32: two pair slots per lane
+    (70, 1536),      # fp32: 8 lanes x 3 pairs a row
+    (129, 2560),     # fp32: 16 lanes x 3 pairs, 8 of 48 slots idle
+    (66, 6144),      # fp32: 32 lanes x 3 pairs
+    (33, 8192),      # fp32: 32 lanes x 4 pairs
+    (9, 10240),      # fp32: 64 lanes x 3 pairs, 32 of 192 slots idle
+    (5, 12288),      # fp32: 64 lanes x 3 pairs, all busy
     (17, 16384),     # fp32: two column chunks
     (40, 20480),     # both formats chunked
 ])
