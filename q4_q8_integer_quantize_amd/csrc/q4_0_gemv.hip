@@ -377,6 +377,11 @@ __global__ __launch_bounds__(256) void q4_0_gemv_kernel(Q40Args a) {
 }
 
 // The best of `count` (value, index) pairs; one workgroup of 1024 threads.
+// Each thread requests up to kMergePer pairs before comparing any, so a
+// head's pairs (a few thousand) arrive in one round trip; the ranking is a
+// total order, so the order of the comparisons does not change the result.
+constexpr int kMergePer = 4;
+
 __global__ __launch_bounds__(1024) void argmax_merge_kernel(const float* __restrict__ pv,
                                                             const int* __restrict__ pi, int count,
                                                             int* __restrict__ out_idx,
@@ -385,11 +390,22 @@ __global__ __launch_bounds__(1024) void argmax_merge_kernel(const float* __restr
   __shared__ int wi[16];
   float bv = -__builtin_inff();
   int bi = kNoRow;
-  for (int j = (int)threadIdx.x; j < count; j += 1024)
-    if (ranks_above(pv[j], pi[j], bv, bi)) {
-      bv = pv[j];
-      bi = pi[j];
+  for (int base = 0; base < count; base += 1024 * kMergePer) {
+    float v[kMergePer];
+    int ix[kMergePer];
+#pragma unroll
+    for (int k = 0; k < kMergePer; ++k) {
+      const int j = base + k * 1024 + (int)threadIdx.x;
+      v[k] = j < count ? pv[j] : -__builtin_inff();
+      ix[k] = j < count ? pi[j] : kNoRow;
     }
+#pragma unroll
+    for (int k = 0; k < kMergePer; ++k)
+      if (ranks_above(v[k], ix[k], bv, bi)) {
+        bv = v[k];
+        bi = ix[k];
+      }
+  }
   wave_best(bv, bi);
   const int wave = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) {
