@@ -9,7 +9,8 @@ Cache or an L2; inputs are resident in HBM before the timed region.
 
 Printed (one JSON line): the whole-step weight-stream rate in GB/s (`value`,
 K steps captured in one HIP graph and replayed between HIP events), the fused
-kernel's rate against the 8 TB/s HBM peak (`roofline`), the CPU oracle timed
+kernel's rate against the 8 TB/s HBM peak (`roofline`), a plain streaming read
+of the same bytes as the practical ceiling (`read_ceiling`), the CPU oracle timed
 on the host (`cpu_baseline`), and under `rows` every other kernel of the path
 at its own workload, timed the same way with its own weight rotation:
 Q8_1 quantize, the GEMV alone, the four attention projections on one shared
@@ -341,6 +342,31 @@ def time_rows(lib, rz, torch, dev, graph_time, copies, x, xq, y) -> dict:
     return rows
 
 
+def read_ceiling(torch, dev, graph_time, w_p, n_copies) -> dict:
+    """A plain streaming read of the same 33 MB weight copies, rotated the same
+    way (librz_stream_read.so, not part of the path): what a kernel that only
+    reads these bytes reaches on this part.  The best of a few grid sizes."""
+    import ctypes
+    path = os.path.join(ROOT, "q4_q8_integer_quantize_amd", "librz_stream_read.so")
+    rd = ctypes.CDLL(path)
+    rd.rz_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                  ctypes.c_void_p]
+    rd.rz_stream_read.restype = ctypes.c_int
+    sink = torch.zeros(256, dtype=torch.int32, device=dev)
+    best = None
+    for grid in (256, 512, 1024, 2048, 4096):
+        def body(i, strm, grid=grid):
+            if rd.rz_stream_read(w_p[i % n_copies], W_BYTES, sink.data_ptr(), grid, strm):
+                raise RuntimeError("rz_stream_read failed")
+        sec = graph_time(body)
+        if best is None or sec < best[0]:
+            best = (sec, grid)
+    return {"what": "plain non-temporal read of the step's weight bytes, same rotation",
+            "bytes": W_BYTES, "us": round(best[0] * 1e6, 3),
+            "gbs": round(W_BYTES / best[0] / 1e9, 2), "grid": best[1],
+            "frac": round(W_BYTES / best[0] / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 ONLY = {
     "step": "rz_q4k_q8_gemv_f32 4096 -> 14336",
     "gemv": "rz_q4k_q8_gemv 4096 -> 14336, 1 token",
@@ -351,8 +377,15 @@ ONLY = {
 }
 
 
+def rotated_copies(torch, dev, blob):
+    """Device copies of a weight blob, >= 1 GiB in all, so that consecutive
+    launches find none of their weights in a cache."""
+    first = torch.from_numpy(blob.reshape(-1).copy()).to(dev)
+    return [first] + [first.clone() for _ in range(-(-ROTATE_BYTES // blob.size) - 1)]
+
+
 def run_only(name: str, launches: int) -> int:
-    """Run one kernel `launches` times over 4 weight copies, untimed."""
+    """Run one kernel `launches` times over >= 1 GiB of weight copies, untimed."""
     import numpy as np
     import torch
     import synth
@@ -373,23 +406,23 @@ def run_only(name: str, launches: int) -> int:
         xq = torch.empty((H // 32) * 40, dtype=torch.uint8, device=dev)
         rz.rz_q8_1_quantize(xd, 896, H, 1, xq)
         y = torch.empty(V, dtype=torch.float32, device=dev)
-        ws = [torch.from_numpy(blob.reshape(-1).copy()).to(dev) for _ in range(4)]
+        ws = rotated_copies(torch, dev, blob)
         fmt = 0 if name == "lm_head_fp32" else 1
         for i in range(launches):
-            rz.rz_q4_0_gemv(ws[i % 4], xd if fmt == 0 else xq, fmt, y, V, H)
+            rz.rz_q4_0_gemv(ws[i % len(ws)], xd if fmt == 0 else xq, fmt, y, V, H)
     else:
         nt = 8 if name == "batch8" else 1
         blob = synth.q4k_weights(synth.rng(2, synth.T_W0), OUT_DIM, IN_DIM)
-        ws = [torch.from_numpy(blob.reshape(-1).copy()).to(dev) for _ in range(4)]
+        ws = rotated_copies(torch, dev, blob)
         x = torch.from_numpy(synth.activation(synth.rng(4, synth.T_ACT), IN_DIM, nt)).to(dev)
         xq = torch.empty(nt * XQ_BYTES, dtype=torch.uint8, device=dev)
         rz.rz_q8_1_quantize(x, IN_DIM, IN_DIM, nt, xq)
         y = torch.empty(nt * OUT_DIM, dtype=torch.float32, device=dev)
         for i in range(launches):
             if name == "step":
-                rz.rz_q4k_q8_gemv_f32(ws[i % 4], x, IN_DIM, None, y, OUT_DIM, IN_DIM)
+                rz.rz_q4k_q8_gemv_f32(ws[i % len(ws)], x, IN_DIM, None, y, OUT_DIM, IN_DIM)
             else:
-                rz.rz_q4k_q8_gemv(ws[i % 4], xq, y, OUT_DIM, IN_DIM, nt)
+                rz.rz_q4k_q8_gemv(ws[i % len(ws)], xq, y, OUT_DIM, IN_DIM, nt)
     torch.cuda.synchronize()
     print("ran %s x %d" % (ONLY[name], launches), flush=True)
     return 0
@@ -489,6 +522,7 @@ def main() -> int:
 
     step_s = graph_time(fused)            # the timed steps (whole hot path)
     rows = None if args.no_rows else time_rows(lib, rz, torch, dev, graph_time, copies, x, xq, y)
+    ceiling = read_ceiling(torch, dev, graph_time, w_p, n_copies)
     ms_step = step_s * 1e3
     two_s = graph_time(two_launch)        # same work as two launches
     gemv_s = graph_time(gemv_only)        # the GEMV kernel alone
@@ -532,6 +566,7 @@ def main() -> int:
         "gemv_kernel_gbs": round(GEMV_ALGO_BYTES / gemv_s / 1e9, 2),
         "kernel_source_sha256_16": kernel_source_hash(),
         "rows": rows,
+        "read_ceiling": dict(ceiling, step_frac_of_ceiling=round(achieved / ceiling["gbs"], 4)),
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 2),

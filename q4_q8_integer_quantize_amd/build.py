@@ -1,4 +1,5 @@
-"""Build librz.so (the HIP kernels and the C ABI) in-tree for gfx950.
+"""Build librz.so (the HIP kernels and the C ABI) in-tree for gfx950, and the
+benchmark's streaming-read helper librz_stream_read.so.
 
     python -m q4_q8_integer_quantize_amd.build
 
@@ -19,6 +20,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "librz.so")
+# measurement helper for bench.py (a plain streaming read), outside librz.so
+READ_SRC = "stream_read.hip"
+READ_LIB = os.path.join(PKG, "librz_stream_read.so")
 
 SOURCES = ["q8_1_quantize.hip", "q4k_gemv.hip", "q4k_gemv_f32.hip", "q4k_gemm_mfma.hip",
            "q4k_gemv_multi.hip", "q4_0_gemv.hip", "swiglu_ffn.hip", "rmsnorm_q8_1.hip",
@@ -56,15 +60,20 @@ def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
         objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+    _link(objs, LIB)
+    _link([_compile(READ_SRC)], READ_LIB)
+    if verbose:
+        print("built", LIB, "and", READ_LIB)
+    return LIB
+
+
+def _link(objs: list[str], lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), res.stderr))
-    os.replace(tmp, LIB)
-    if verbose:
-        print("built", LIB)
-    return LIB
+    os.replace(tmp, lib)
 
 
 if __name__ == "__main__":

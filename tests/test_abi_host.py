@@ -391,3 +391,30 @@ def test_binding_rejects_host_tensors():
     torch = pytest.importorskip("torch")
     with pytest.raises(ValueError):
         rz.rz_q8_1_quantize(torch.zeros(32), 32, 32, 1, torch.zeros(40, dtype=torch.uint8), stream=0)
+
+
+_READ_CHILD = r"""
+import ctypes, json, sys
+lib = ctypes.CDLL(sys.argv[1])
+f = lib.rz_stream_read
+f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+f.restype = ctypes.c_int
+print(json.dumps([f(*a) for a in json.loads(sys.stdin.read())]))
+"""
+
+
+def test_stream_read_helper_rejects_bad_arguments():
+    """The benchmark's streaming-read helper (librz_stream_read.so, not part of
+    librz.so) exports rz_stream_read and refuses null, unaligned or ragged
+    buffers and grids out of range before any launch."""
+    path = os.path.join(ROOT, "q4_q8_integer_quantize_amd", "librz_stream_read.so")
+    if not os.path.exists(path):
+        pytest.skip("librz_stream_read.so not built")
+    calls = [[None, 1024, P, 256, None], [P, 1024, None, 256, None], [P + 8, 1024, P, 256, None],
+             [P, 1000, P, 256, None], [P, 0, P, 256, None], [P, 1024, P, 0, None],
+             [P, 1024, P, 65537, None]]
+    env = dict(os.environ, ROCR_VISIBLE_DEVICES="-1", HIP_VISIBLE_DEVICES="-1")
+    res = subprocess.run([sys.executable, "-c", _READ_CHILD, path], input=json.dumps(calls),
+                         capture_output=True, text=True, env=env, timeout=120)
+    assert res.returncode == 0, res.stderr
+    assert json.loads(res.stdout) == [-1] * len(calls)
