@@ -203,18 +203,19 @@ constexpr size_t xl_lds_bytes() { return (size_t)S * LPR * kPairStride; }
 // past npairs) into LDS with their block sums and the lanes read them from
 // there, so a lane may take many pairs of a row (64 fp32 values a pair would
 // not fit in registers).
-template <int LPR, int S, int R, int G, int P, bool Q8, bool ACC, bool EPI>
-__global__ __launch_bounds__(256) void q4_0_gemv_kernel(Q40Args a) {
+template <int LPR, int S, int R, int G, int P, bool Q8, bool ACC, bool EPI, int WPB = 4>
+__global__ __launch_bounds__(64 * WPB) void q4_0_gemv_kernel(Q40Args a) {
   constexpr bool XL = !Q8;
   constexpr int RW = kWave / LPR;
+  constexpr int NT = 64 * WPB;                           // threads a workgroup
   const int lane = threadIdx.x & (kWave - 1);
   const int rs = lane / LPR, ps = lane % LPR;
-  const long nwaves = (long)gridDim.x * 4;
-  const long wid = __builtin_amdgcn_readfirstlane(blockIdx.x * 4u + (threadIdx.x >> 6));
+  const long nwaves = (long)gridDim.x * WPB;
+  const long wid = __builtin_amdgcn_readfirstlane(blockIdx.x * (uint32_t)WPB + (threadIdx.x >> 6));
   const size_t row_bytes = (size_t)a.npairs_row * 36;
   extern __shared__ __attribute__((aligned(16))) uint8_t xl[];
   constexpr int kChunks = S * LPR * 16;                  // 16-byte chunks staged
-  constexpr int kIters = (kChunks + 255) / 256;
+  constexpr int kIters = (kChunks + NT - 1) / NT;
   u32x4 xin[XL ? kIters : 1];
   X40Q8<Q8 ? S : 1> xs;
   if constexpr (XL) {
@@ -224,7 +225,7 @@ __global__ __launch_bounds__(256) void q4_0_gemv_kernel(Q40Args a) {
         (void*)((const float*)a.x + (size_t)a.p0 * 64), (short)0, (int)xbytes, kBufferWord3);
 #pragma unroll
     for (int j = 0; j < kIters; ++j) {
-      const uint32_t g = (uint32_t)(j * 256) + threadIdx.x;
+      const uint32_t g = (uint32_t)(j * NT) + threadIdx.x;
       const uint32_t off = g * 16u < xbytes ? g * 16u : xbytes;
       xin[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
     }
@@ -262,7 +263,7 @@ __global__ __launch_bounds__(256) void q4_0_gemv_kernel(Q40Args a) {
     // (vector loads retire in order: this waits for the activation only)
 #pragma unroll
     for (int j = 0; j < kIters; ++j) {
-      const int g = j * 256 + (int)threadIdx.x;
+      const int g = j * NT + (int)threadIdx.x;
       const u32x4 v = xin[j];
       const uint32_t v0 = v.x, v1 = v.y, v2 = v.z, v3 = v.w;
       const float part = (__builtin_bit_cast(float, v0) + __builtin_bit_cast(float, v1)) +
@@ -351,8 +352,8 @@ __global__ __launch_bounds__(256) void q4_0_gemv_kernel(Q40Args a) {
   }
   if constexpr (EPI) {
     if (a.part_val != nullptr) {
-      __shared__ float wv[4];
-      __shared__ int wi[4];
+      __shared__ float wv[WPB];
+      __shared__ int wi[WPB];
       wave_best(best_v, best_i);
       const int wave = threadIdx.x >> 6;
       if (lane == 0) {
@@ -364,7 +365,7 @@ __global__ __launch_bounds__(256) void q4_0_gemv_kernel(Q40Args a) {
         float v = wv[0];
         int i = wi[0];
 #pragma unroll
-        for (int w = 1; w < 4; ++w)
+        for (int w = 1; w < WPB; ++w)
           if (ranks_above(wv[w], wi[w], v, i)) {
             v = wv[w];
             i = wi[w];
@@ -426,23 +427,32 @@ __global__ __launch_bounds__(1024) void argmax_merge_kernel(const float* __restr
   }
 }
 
+// Waves a workgroup: eight when the staged activation is 128 pairs or more
+// (every workgroup copies it into LDS, so larger workgroups copy it less
+// often; 160-pair rows: 7.7 against 8.1 us), else four (48 pairs: 6.5 against
+// 7.4 us with eight).
+template <int LPR, int S, bool Q8>
+constexpr int q40_wpb() { return (!Q8 && S * LPR >= 128) ? 8 : 4; }
+
 template <int LPR, int S, int R, int G, bool Q8>
 static hipError_t launch_q40_g(const Q40Args& a, long groups, bool epi, hipStream_t st) {
   constexpr int P = G > 2 ? 2 : (G > 1 ? G - 1 : 1);
+  constexpr int WPB = q40_wpb<LPR, S, Q8>();
   static_assert(Q8 || xl_lds_bytes<S, LPR>() <= 65536, "staged activation within 64 KiB of LDS");
   const long waves = (groups + G - 1) / G;
-  const unsigned grid = (unsigned)((waves + 3) / 4);
+  const unsigned grid = (unsigned)((waves + WPB - 1) / WPB);
+  const dim3 block(64 * WPB);
   const size_t lds = Q8 ? 0 : xl_lds_bytes<S, LPR>();
   if (epi && a.part_val != nullptr && (long)grid != a.part_count) return hipErrorInvalidValue;
   if (epi) {
     if (a.accumulate)
-      hipLaunchKernelGGL((q4_0_gemv_kernel<LPR, S, R, G, P, Q8, true, true>), dim3(grid), dim3(256), lds, st, a);
+      hipLaunchKernelGGL((q4_0_gemv_kernel<LPR, S, R, G, P, Q8, true, true, WPB>), dim3(grid), block, lds, st, a);
     else
-      hipLaunchKernelGGL((q4_0_gemv_kernel<LPR, S, R, G, P, Q8, false, true>), dim3(grid), dim3(256), lds, st, a);
+      hipLaunchKernelGGL((q4_0_gemv_kernel<LPR, S, R, G, P, Q8, false, true, WPB>), dim3(grid), block, lds, st, a);
   } else if (a.accumulate) {
-    hipLaunchKernelGGL((q4_0_gemv_kernel<LPR, S, R, G, P, Q8, true, false>), dim3(grid), dim3(256), lds, st, a);
+    hipLaunchKernelGGL((q4_0_gemv_kernel<LPR, S, R, G, P, Q8, true, false, WPB>), dim3(grid), block, lds, st, a);
   } else {
-    hipLaunchKernelGGL((q4_0_gemv_kernel<LPR, S, R, G, P, Q8, false, false>), dim3(grid), dim3(256), lds, st, a);
+    hipLaunchKernelGGL((q4_0_gemv_kernel<LPR, S, R, G, P, Q8, false, false, WPB>), dim3(grid), block, lds, st, a);
   }
   return hipGetLastError();
 }
@@ -472,7 +482,7 @@ constexpr long kXlTwoGroups = 8192;
 // takes two once there are 8192 groups (the 151936 x 1024 LM head; at 2560
 // and 3584 groups one group a wave was faster).
 struct Q40Shape {
-  int lpr, s, r, g;
+  int lpr, s, r, g, wpb;
 };
 
 static int pow2_at_least(int v) {
@@ -499,6 +509,7 @@ static Q40Shape q40_shape(int np, long out_dim, bool q8) {
   const long rows_per_group = (long)(kWave / sh.lpr) * sh.r;
   const long groups = (out_dim + rows_per_group - 1) / rows_per_group;
   sh.g = (!q8 && groups >= kXlTwoGroups) ? 2 : 1;
+  sh.wpb = (!q8 && sh.s * sh.lpr >= 128) ? 8 : 4;   // q40_wpb
   return sh;
 }
 
@@ -596,7 +607,7 @@ long q4_0_lm_head_partials(int out_dim, int in_dim, int x_format) {
   const long rows_per_group = (long)(kWave / sh.lpr) * sh.r;
   const long groups = (out_dim + rows_per_group - 1) / rows_per_group;
   const long waves = (groups + sh.g - 1) / sh.g;
-  return (waves + 3) / 4;
+  return (waves + sh.wpb - 1) / sh.wpb;
 }
 
 hipError_t launch_q4_0_lm_head(const uint8_t* w, const void* x, int x_format, const float* bias,

@@ -981,6 +981,7 @@ def test_lm_head_full_with_bias(fmt):
 
 @pytest.mark.parametrize("fmt", [0, 1])
 @pytest.mark.parametrize("out_dim,in_dim", [(1, 64), (17, 64), (1000, 1024), (4097, 2048),
+                                            (77, 8192), (300, 10240),   # fp32: 8-wave workgroups
                                             (3000, 16384), (50, 32768)])
 def test_lm_head_shapes(fmt, out_dim, in_dim):
     """Ragged row counts, one and several column passes (the epilogue runs in
