@@ -31,7 +31,9 @@
  *     value is RZ_OK or a negative RZ_E* code, and rz_last_error() then holds a
  *     message.  A device-side fault surfaces at the caller's next sync.
  *   - in_dim is always the PADDED length (the caller zero-pads activations;
- *     rz_q8_1_quantize does it while quantizing).
+ *     rz_q8_1_quantize does it while quantizing);
+ *   - empty work is an error, not a no-op: a zero dimension gives RZ_EDIM and
+ *     zero tokens or matrices RZ_EINVAL, before anything is enqueued.
  */
 #ifndef RZ_H
 #define RZ_H
