@@ -92,8 +92,17 @@ def cpu_baseline(target_seconds: float):
         cpu += time.process_time() - c0
         reps += 1
     rate = reps * W_BYTES / wall / 1e9
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": round(rate, 4), "unit": "GB/s", "cores": max(1, round(cpu / wall)),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model,
             "sample": "%d full passes (quantize 4096 + integer-form GEMV 14336x4096, numpy), "
                       "%.1f s wall; host has %d cores" % (reps, wall, len(os.sched_getaffinity(0)))}
 
