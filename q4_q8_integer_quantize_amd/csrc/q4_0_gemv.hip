@@ -88,16 +88,6 @@ __device__ __forceinline__ void load_x40_q8(X40Q8<S>& xs, const Q40Args& a, int 
   }
 }
 
-// v & m, opaque to the compiler's known-bits analysis: with the nibble mask
-// visible it folds each byte conversion below into a 4-bit extract plus a
-// byte-0 conversion (two instructions per weight); behind this AND every byte
-// converts with one v_cvt_f32_ubyte{0..3}.
-__device__ __forceinline__ uint32_t opaque_and(uint32_t v, uint32_t m) {
-  uint32_t r;
-  asm("v_and_b32 %0, %1, %2" : "=v"(r) : "v"(v), "v"(m));
-  return r;
-}
-
 // sum_l q_l * x_l over one block; qs dwords hold values 4k..4k+3 (low
 // nibbles) and 16+4k..16+4k+3 (high nibbles).  Four independent partial sums
 // (one per byte position) keep the fma chains short; they are added pairwise

@@ -90,16 +90,6 @@ __device__ __forceinline__ void request_x(XF32Slots<S>& xs, __amdgpu_buffer_rsrc
 
 __device__ __forceinline__ float xor1_f(float v) { return dpp_f<0xB1>(v); }
 
-// v & m, opaque to the compiler's known-bits analysis.  With the nibble mask
-// visible, the byte conversions below fold into a 4-bit extract followed by a
-// byte-0 conversion (two instructions per weight); behind this AND each byte
-// converts with one v_cvt_f32_ubyte{0..3}.
-__device__ __forceinline__ uint32_t opaque_and(uint32_t v, uint32_t m) {
-  uint32_t r;
-  asm("v_and_b32 %0, %1, %2" : "=v"(r) : "v"(v), "v"(m));
-  return r;
-}
-
 // Sum of 16 values as a fixed tree.
 __device__ __forceinline__ float sum16(const float (&v)[16]) {
   float a[8];

@@ -46,6 +46,16 @@ __device__ __forceinline__ float f16_hi(uint32_t v) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
 }
 
+// v & m, opaque to the compiler's known-bits analysis.  With a nibble mask
+// visible, a byte conversion of the result folds into a 4-bit extract plus a
+// byte-0 conversion (two instructions per weight); behind this AND each byte
+// converts with one v_cvt_f32_ubyte{0..3}.  Used by the fp32-activation dots.
+__device__ __forceinline__ uint32_t opaque_and(uint32_t v, uint32_t m) {
+  uint32_t r;
+  asm("v_and_b32 %0, %1, %2" : "=v"(r) : "v"(v), "v"(m));
+  return r;
+}
+
 // DPP lane exchange within rows of 16 lanes (control words: quad_perm
 // [1,0,3,2] = 0xB1 is lane^1, [2,3,0,1] = 0x4E is lane^2, row_half_mirror
 // 0x141 swaps the two quads of each group of 8, row_mirror 0x140 the two
