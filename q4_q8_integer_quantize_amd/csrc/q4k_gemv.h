@@ -98,6 +98,39 @@ __device__ __forceinline__ void load_x_slots(XSlots<S, NT>& xs, const uint8_t* _
   }
 }
 
+// The same slots from a workgroup's LDS copy of the chunk's Q8_1 blocks:
+// token t's blocks start at xl + t * tok_bytes.
+template <int TPR, int S, int NT>
+__device__ __forceinline__ void load_x_slots_from_lds(XSlots<S, NT>& xs, const uint8_t* xl,
+                                                      uint32_t tok_bytes, int nsb, int n_tokens,
+                                                      const LaneRole& ro) {
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const int sb = s * TPR + ro.tslot;
+      if (t < n_tokens && sb < nsb) {
+        const uint8_t* xb = xl + t * tok_bytes + sb * 8 * kQ8Bytes;
+        const uint2* plo = (const uint2*)(xb + (2 * ro.c) * kQ8Bytes + 8 + 16 * ro.h);
+        const uint2* phi = (const uint2*)(xb + (2 * ro.c + 1) * kQ8Bytes + 8 + 16 * ro.h);
+        const uint2 a0 = plo[0], a1 = plo[1], b0 = phi[0], b1 = phi[1];
+        xs.lo[t][s][0] = (int)a0.x; xs.lo[t][s][1] = (int)a0.y;
+        xs.lo[t][s][2] = (int)a1.x; xs.lo[t][s][3] = (int)a1.y;
+        xs.hi[t][s][0] = (int)b0.x; xs.hi[t][s][1] = (int)b0.y;
+        xs.hi[t][s][2] = (int)b1.x; xs.hi[t][s][3] = (int)b1.y;
+        const float2 own = *(const float2*)(xb + ro.i * kQ8Bytes);
+        xs.dx[t][s] = own.x;
+        xs.sx[t][s] = own.y;
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) { xs.lo[t][s][k] = 0; xs.hi[t][s][k] = 0; }
+        xs.dx[t][s] = 0.0f;
+        xs.sx[t][s] = 0.0f;
+      }
+    }
+  }
+}
+
 // Weights of R*RW rows (RW = 8/TPR side by side, R unrolled) for one lane:
 // the 16-byte header and the lane's 16-byte qs slice of each slot.
 template <int S, int R>
@@ -303,7 +336,7 @@ __device__ __forceinline__ void store_rows_residual(const Q4KGemvArgs& a,
 // residual values are requested right after its weight tile, so waiting for
 // them never waits for a tile issued later.
 template <int TPR, int S, int R, int NT, int G, int P, bool ACC, int WPB = 4, bool STRIDED = true,
-          bool RES = false>
+          bool RES = false, bool XL = false>
 __global__ __launch_bounds__(64 * WPB) void q4k_q8_gemv_kernel(Q4KGemvArgs a) {
   static_assert(!(RES && ACC), "the residual is added by a storing pass");
   constexpr int RW = 8 / TPR;
@@ -319,10 +352,34 @@ __global__ __launch_bounds__(64 * WPB) void q4k_q8_gemv_kernel(Q4KGemvArgs a) {
   const LaneOffsets<TPR, S> off = lane_offsets<TPR, S>(src, a.sb0, ro);
 
   // activation first: vector loads retire in order, so waiting for x must
-  // not mean waiting for weight tiles issued before it
+  // not mean waiting for weight tiles issued before it.  XL: the workgroup
+  // copies the chunk's blocks into LDS once (16 bytes a thread per step) and
+  // the lanes read their slots from there, instead of every wave reading
+  // them from L2.
   XSlots<S, NT> xs;
-  load_x_slots<TPR, S, NT>(xs, a.xq + (size_t)a.sb0 * 8 * kQ8Bytes,
-                           (size_t)a.nsb_row * 8 * kQ8Bytes, a.nsb, a.n_tokens, ro);
+  constexpr uint32_t kTokBytes = (uint32_t)(S * TPR * 8 * kQ8Bytes);   // LDS bytes a token
+  constexpr int kXChunks = NT * (int)(kTokBytes / 16);
+  constexpr int kXIters = XL ? (kXChunks + 64 * WPB - 1) / (64 * WPB) : 1;
+  extern __shared__ __attribute__((aligned(16))) uint8_t xl_lds[];
+  u32x4 xin[kXIters];
+  if constexpr (XL) {
+    const uint32_t tok_stride = (uint32_t)a.nsb_row * 8u * kQ8Bytes;
+    const uint32_t chunk_bytes = (uint32_t)a.nsb * 8u * kQ8Bytes;
+    const uint32_t xbytes = (uint32_t)a.n_tokens * tok_stride;
+    const __amdgpu_buffer_rsrc_t xr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)a.xq, (short)0, (int)xbytes, kBufferWord3);
+#pragma unroll
+    for (int j = 0; j < kXIters; ++j) {
+      const uint32_t gidx = (uint32_t)(j * 64 * WPB) + threadIdx.x;
+      const uint32_t tk = gidx / (kTokBytes / 16u), c16 = 16u * (gidx % (kTokBytes / 16u));
+      const bool on = gidx < (uint32_t)kXChunks && tk < (uint32_t)a.n_tokens && c16 < chunk_bytes;
+      const uint32_t off = on ? tk * tok_stride + (uint32_t)a.sb0 * 8u * kQ8Bytes + c16 : xbytes;
+      xin[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
+    }
+  } else {
+    load_x_slots<TPR, S, NT>(xs, a.xq + (size_t)a.sb0 * 8 * kQ8Bytes,
+                             (size_t)a.nsb_row * 8 * kQ8Bytes, a.nsb, a.n_tokens, ro);
+  }
   WTile<S, R> t[G];
   float rv[G][R][NT];
   __amdgpu_buffer_rsrc_t rr;
@@ -338,6 +395,19 @@ __global__ __launch_bounds__(64 * WPB) void q4k_q8_gemv_kernel(Q4KGemvArgs a) {
   }
   // keep the scheduler from sinking requests below the first wait
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (XL) {
+    // stage x (this waits for the activation loads only), then an LDS-only
+    // release/acquire around the barrier, so the weight loads stay in flight
+#pragma unroll
+    for (int j = 0; j < kXIters; ++j) {
+      const uint32_t gidx = (uint32_t)(j * 64 * WPB) + threadIdx.x;
+      if (gidx < (uint32_t)kXChunks) *(u32x4*)(xl_lds + 16u * gidx) = xin[j];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    load_x_slots_from_lds<TPR, S, NT>(xs, xl_lds, kTokBytes, a.nsb, a.n_tokens, ro);
+  }
 #pragma unroll
   for (int k = 0; k < G; ++k) {
     if (k + P < G) {
