@@ -33,7 +33,11 @@
  *   - in_dim is always the PADDED length (the caller zero-pads activations;
  *     rz_q8_1_quantize does it while quantizing);
  *   - empty work is an error, not a no-op: a zero dimension gives RZ_EDIM and
- *     zero tokens or matrices RZ_EINVAL, before anything is enqueued.
+ *     zero tokens or matrices RZ_EINVAL, before anything is enqueued;
+ *   - an output must not overlap the call's weights, its activations or its
+ *     other outputs, except where an entry point allows it (a residual may be
+ *     the output it is added to, a bias may be its output, a chain's final
+ *     output may be its input); an overlap gives RZ_EINVAL.
  */
 #ifndef RZ_H
 #define RZ_H

@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <initializer_list>
 
 #include "rz.h"
 #include "rz_launch.h"
@@ -46,6 +47,24 @@ bool same_or_disjoint(const float* a, const float* b, long long count) {
   return a == b || disjoint(a, count * 4, b, count * 4);
 }
 
+// A buffer and its byte length, for the overlap checks below.
+struct Span {
+  const void* p;
+  long long n;
+};
+
+// An output span overlaps none of `others` (null pointers are skipped).
+bool clear_of(Span out, std::initializer_list<Span> others) {
+  if (!out.p) return true;
+  for (const Span& o : others)
+    if (o.p && !disjoint(out.p, out.n, o.p, o.n)) return false;
+  return true;
+}
+
+long long q4k_bytes(int out_dim, int in_dim) { return (long long)out_dim * (in_dim / 256) * RZ_Q4K_BLOCK_BYTES; }
+long long q4_0_bytes(int out_dim, int in_dim) { return (long long)out_dim * (in_dim / 32) * RZ_Q4_0_BLOCK_BYTES; }
+long long q8_bytes(int n_tokens, int n_padded) { return (long long)n_tokens * (n_padded / 32) * RZ_Q8_1_BLOCK_BYTES; }
+
 int check_dim(const char* what, const char* name, int v, int multiple) {
   if (v <= 0 || v > RZ_MAX_DIM || v % multiple != 0)
     return fail(RZ_EDIM, "%s: %s=%d must be a positive multiple of %d and <= %d", what, name, v,
@@ -72,6 +91,8 @@ int rz_q8_1_quantize(const float* x, int n, int n_padded, int n_tokens, void* x_
     return fail(RZ_EDIM, "%s: n=%d must satisfy 1 <= n <= n_padded=%d", what, n, n_padded);
   if (!aligned(x, 4)) return fail(RZ_EALIGN, "%s: x must be 4-byte aligned", what);
   if (!aligned(x_q8, 8)) return fail(RZ_EALIGN, "%s: x_q8 must be 8-byte aligned", what);
+  if (!clear_of({x_q8, q8_bytes(n_tokens, n_padded)}, {{x, 4LL * n_tokens * n}}))
+    return fail(RZ_EINVAL, "%s: x_q8 must not overlap x", what);
   return launch_status(rz::launch_q8_1_quantize(x, n, n_padded, n_tokens,
                                                 static_cast<uint8_t*>(x_q8),
                                                 static_cast<hipStream_t>(stream)),
@@ -92,6 +113,10 @@ int rz_rmsnorm_q8_1(const float* x, const float* gamma, float eps, int n, int n_
   if (!aligned(x, 4) || !aligned(gamma, 4) || (normed && !aligned(normed, 4)))
     return fail(RZ_EALIGN, "%s: fp32 buffers must be 4-byte aligned", what);
   if (!aligned(x_q8, 8)) return fail(RZ_EALIGN, "%s: x_q8 must be 8-byte aligned", what);
+  // every workgroup reads the whole row while others write their slices
+  const Span xs{x, 4LL * n_tokens * n}, gs{gamma, 4LL * n}, qs{x_q8, q8_bytes(n_tokens, n_padded)};
+  if (!clear_of(qs, {xs, gs}) || !clear_of({normed, 4LL * n_tokens * n}, {xs, gs, qs}))
+    return fail(RZ_EINVAL, "%s: normed and x_q8 must not overlap x, gamma or each other", what);
   return launch_status(rz::launch_rmsnorm_q8_1(x, gamma, eps, n, n_padded, n_tokens, normed,
                                                static_cast<uint8_t*>(x_q8),
                                                static_cast<hipStream_t>(stream)),
@@ -111,6 +136,9 @@ int rz_q4k_q8_gemv(const void* w_q4k, const void* x_q8, float* y, int out_dim, i
   if (!aligned(w_q4k, 16)) return fail(RZ_EALIGN, "%s: w_q4k must be 16-byte aligned", what);
   if (!aligned(x_q8, 8)) return fail(RZ_EALIGN, "%s: x_q8 must be 8-byte aligned", what);
   if (!aligned(y, 4)) return fail(RZ_EALIGN, "%s: y must be 4-byte aligned", what);
+  if (!clear_of({y, 4LL * n_tokens * out_dim},
+                {{w_q4k, q4k_bytes(out_dim, in_dim)}, {x_q8, q8_bytes(n_tokens, in_dim)}}))
+    return fail(RZ_EINVAL, "%s: y must not overlap w_q4k or x_q8", what);
   return launch_status(rz::launch_q4k_q8_gemv(static_cast<const uint8_t*>(w_q4k),
                                                static_cast<const uint8_t*>(x_q8), y, out_dim,
                                                in_dim, n_tokens,
@@ -134,6 +162,9 @@ int rz_q4k_q8_gemv_add(const void* w_q4k, const void* x_q8, const float* r, floa
     return fail(RZ_EALIGN, "%s: r and y must be 4-byte aligned", what);
   if (!same_or_disjoint(r, y, (long long)n_tokens * out_dim))
     return fail(RZ_EINVAL, "%s: r must be y itself or not overlap it", what);
+  if (!clear_of({y, 4LL * n_tokens * out_dim},
+                {{w_q4k, q4k_bytes(out_dim, in_dim)}, {x_q8, q8_bytes(n_tokens, in_dim)}}))
+    return fail(RZ_EINVAL, "%s: y must not overlap w_q4k or x_q8", what);
   return launch_status(rz::launch_q4k_q8_gemv(static_cast<const uint8_t*>(w_q4k),
                                                static_cast<const uint8_t*>(x_q8), y, out_dim,
                                                in_dim, n_tokens,
@@ -167,6 +198,17 @@ int rz_q4k_q8_gemv_multi(int n_mats, const void* const* w_q4k, float* const* y,
     yy[m] = y[m];
     od[m] = out_dims[m];
   }
+  // each output clear of the activation, every weight blob and the other outputs
+  for (int m = 0; m < n_mats; ++m) {
+    const Span ym{yy[m], 4LL * n_tokens * od[m]};
+    if (!clear_of(ym, {{x_q8, q8_bytes(n_tokens, in_dim)}}))
+      return fail(RZ_EINVAL, "%s: y[%d] must not overlap x_q8", what, m);
+    for (int k = 0; k < n_mats; ++k) {
+      if (!clear_of(ym, {{w[k], q4k_bytes(od[k], in_dim)}}) ||
+          (k != m && !clear_of(ym, {{yy[k], 4LL * n_tokens * od[k]}})))
+        return fail(RZ_EINVAL, "%s: y[%d] overlaps a weight blob or another output", what, m);
+    }
+  }
   return launch_status(rz::launch_q4k_q8_gemv_multi(n_mats, w, yy, od,
                                                      static_cast<const uint8_t*>(x_q8), in_dim,
                                                      n_tokens, static_cast<hipStream_t>(stream)),
@@ -189,6 +231,11 @@ int rz_q4k_q8_gemv_f32(const void* w_q4k, const float* x, int n, void* x_q8, flo
   if (!aligned(x, 4) || !aligned(y, 4))
     return fail(RZ_EALIGN, "%s: x and y must be 4-byte aligned", what);
   if (x_q8 && !aligned(x_q8, 8)) return fail(RZ_EALIGN, "%s: x_q8 must be 8-byte aligned", what);
+  {
+    const Span ws{w_q4k, q4k_bytes(out_dim, in_dim)}, xs{x, 4LL * n}, qs{x_q8, q8_bytes(1, in_dim)};
+    if (!clear_of({y, 4LL * out_dim}, {ws, xs, qs}) || !clear_of(qs, {ws, xs}))
+      return fail(RZ_EINVAL, "%s: y and x_q8 must not overlap w_q4k, x or each other", what);
+  }
   return launch_status(rz::launch_q4k_q8_gemv_f32(static_cast<const uint8_t*>(w_q4k), x, n,
                                                    static_cast<uint8_t*>(x_q8), y, out_dim,
                                                    in_dim, static_cast<hipStream_t>(stream)),
@@ -208,8 +255,8 @@ int rz_q4k_gemv(const void* w_q4k, const float* x, int n, float* y, int out_dim,
   if (!aligned(w_q4k, 16)) return fail(RZ_EALIGN, "%s: w_q4k must be 16-byte aligned", what);
   if (!aligned(x, 4) || !aligned(y, 4))
     return fail(RZ_EALIGN, "%s: x and y must be 4-byte aligned", what);
-  if (!disjoint(x, 4LL * n, y, 4LL * out_dim))
-    return fail(RZ_EINVAL, "%s: x and y must not overlap", what);
+  if (!clear_of({y, 4LL * out_dim}, {{x, 4LL * n}, {w_q4k, q4k_bytes(out_dim, in_dim)}}))
+    return fail(RZ_EINVAL, "%s: y must not overlap x or w_q4k", what);
   return launch_status(rz::launch_q4k_gemv_xf32(static_cast<const uint8_t*>(w_q4k), x, n, y,
                                                 out_dim, in_dim, static_cast<hipStream_t>(stream)),
                        what);
@@ -235,6 +282,12 @@ int rz_swiglu_ffn_q4k_f32(const void* w_gate, const void* w_up, const void* w_do
               !disjoint(h, 4LL * inter_dim, gu, 8LL * inter_dim))) ||
       !disjoint(h, 4LL * inter_dim, y, 4LL * hidden_dim))
     return fail(RZ_EINVAL, "%s: x, h, gu and y must not overlap (x and y may)", what);
+  {
+    const long long wb = q4k_bytes(inter_dim, hidden_dim), db = q4k_bytes(hidden_dim, inter_dim);
+    for (Span o : {Span{h, 4LL * inter_dim}, Span{y, 4LL * hidden_dim}, Span{gu, 8LL * inter_dim}})
+      if (!clear_of(o, {{w_gate, wb}, {w_up, wb}, {w_down, db}}))
+        return fail(RZ_EINVAL, "%s: h, y and gu must not overlap the weight blobs", what);
+  }
   return launch_status(
       rz::launch_swiglu_ffn_q4k_xf32(static_cast<const uint8_t*>(w_gate),
                                      static_cast<const uint8_t*>(w_up),
@@ -255,6 +308,9 @@ int rz_q4_0_gemv(const void* w_q4_0, const void* x, int x_format, float* y, int 
   if (!aligned(x, x_format == 0 ? 16 : 8))
     return fail(RZ_EALIGN, "%s: x must be %d-byte aligned", what, x_format == 0 ? 16 : 8);
   if (!aligned(y, 4)) return fail(RZ_EALIGN, "%s: y must be 4-byte aligned", what);
+  if (!clear_of({y, 4LL * out_dim}, {{w_q4_0, q4_0_bytes(out_dim, in_dim)},
+                                     {x, x_format == 0 ? 4LL * in_dim : q8_bytes(1, in_dim)}}))
+    return fail(RZ_EINVAL, "%s: y must not overlap w_q4_0 or x", what);
   return launch_status(rz::launch_q4_0_gemv(static_cast<const uint8_t*>(w_q4_0), x, x_format, y,
                                             out_dim, in_dim, static_cast<hipStream_t>(stream)),
                        what);
@@ -284,6 +340,18 @@ int swiglu_ffn(const char* what, const void* w_gate, const void* w_up, const voi
     return fail(RZ_EALIGN, "%s: fp32 buffers must be 4-byte aligned", what);
   if (r && !same_or_disjoint(r, y, hidden_dim))
     return fail(RZ_EINVAL, "%s: r must be y itself or not overlap it", what);
+  {
+    // the first kernel reads x_q8 and the gate/up weights while it writes h,
+    // h_q8 and gu; the second reads h_q8 and the down weights while it writes y
+    const long long wb = q4k_bytes(inter_dim, hidden_dim), db = q4k_bytes(hidden_dim, inter_dim);
+    const Span xs{x_q8, q8_bytes(1, hidden_dim)}, hs{h, 4LL * inter_dim},
+        hq{h_q8, q8_bytes(1, inter_dim)}, gs{gu, 8LL * inter_dim}, ys{y, 4LL * hidden_dim},
+        wg{w_gate, wb}, wu{w_up, wb}, wd{w_down, db};
+    if (!clear_of(hs, {xs, hq, gs, wg, wu, wd}) || !clear_of(hq, {xs, gs, ys, wg, wu, wd}) ||
+        !clear_of(gs, {xs, wg, wu, wd}) || !clear_of(ys, {wd, wg, wu}))
+      return fail(RZ_EINVAL, "%s: h, h_q8, gu and y must not overlap x_q8, the weights or each "
+                  "other (y may overlap x_q8)", what);
+  }
   // the first kernel writes h, h_q8 and gu before the second reads r
   if (r && (!disjoint(r, 4LL * hidden_dim, h, 4LL * inter_dim) ||
             !disjoint(r, 4LL * hidden_dim, h_q8, (long long)inter_dim / 32 * RZ_Q8_1_BLOCK_BYTES) ||
@@ -327,6 +395,14 @@ int rz_lm_head_q4_0(const void* w_q4_0, const void* x, int x_format, const float
     return fail(RZ_EALIGN, "%s: logits, bias and the argmax outputs must be 4-byte aligned", what);
   if (bias && !same_or_disjoint(bias, logits, out_dim))
     return fail(RZ_EINVAL, "%s: bias must be logits itself or not overlap it", what);
+  const Span wspan{w_q4_0, q4_0_bytes(out_dim, in_dim)},
+      xspan{x, x_format == 0 ? 4LL * in_dim : q8_bytes(1, in_dim)};
+  if (!clear_of({logits, 4LL * out_dim}, {wspan, xspan}))
+    return fail(RZ_EINVAL, "%s: logits must not overlap w_q4_0 or x", what);
+  if (!clear_of({argmax_idx, 4}, {wspan, xspan, {logits, 4LL * out_dim}, {argmax_val, 4}}) ||
+      !clear_of({argmax_val, 4}, {wspan, xspan, {logits, 4LL * out_dim}}))
+    return fail(RZ_EINVAL, "%s: the argmax outputs must not overlap w_q4_0, x, logits or "
+                "each other", what);
   const bool argmax = argmax_idx || argmax_val;
   float* part_val = nullptr;
   int* part_idx = nullptr;
@@ -336,9 +412,9 @@ int rz_lm_head_q4_0(const void* w_q4_0, const void* x, int x_format, const float
     if (!aligned(workspace, 4)) return fail(RZ_EALIGN, "%s: workspace must be 4-byte aligned", what);
     if (workspace_bytes < need)
       return fail(RZ_EINVAL, "%s: workspace of %zu bytes, %zu needed", what, workspace_bytes, need);
-    if (!disjoint(workspace, (long long)need, logits, 4LL * out_dim) ||
-        (bias && !disjoint(workspace, (long long)need, bias, 4LL * out_dim)))
-      return fail(RZ_EINVAL, "%s: workspace must not overlap logits or bias", what);
+    if (!clear_of({workspace, (long long)need}, {{logits, 4LL * out_dim}, {bias, 4LL * out_dim},
+                                                  wspan, xspan}))
+      return fail(RZ_EINVAL, "%s: workspace must not overlap logits, bias, w_q4_0 or x", what);
     if ((argmax_idx && !disjoint(argmax_idx, 4, workspace, (long long)need)) ||
         (argmax_val && !disjoint(argmax_val, 4, workspace, (long long)need)))
       return fail(RZ_EINVAL, "%s: the argmax outputs must not overlap the workspace", what);
@@ -372,6 +448,12 @@ int rz_gelu_ffn_q4_0(const void* w_up, const void* w_down, const float* x, const
       !disjoint(h, 4LL * inter_dim, y, 4LL * hidden_dim) ||
       (down_bias && !same_or_disjoint(down_bias, y, hidden_dim)))
     return fail(RZ_EINVAL, "%s: overlapping buffers (x, h; h, y; a bias and its output)", what);
+  {
+    const long long ub = q4_0_bytes(inter_dim, hidden_dim), db = q4_0_bytes(hidden_dim, inter_dim);
+    if (!clear_of({h, 4LL * inter_dim}, {{w_up, ub}, {w_down, db}}) ||
+        !clear_of({y, 4LL * hidden_dim}, {{w_up, ub}, {w_down, db}}))
+      return fail(RZ_EINVAL, "%s: h and y must not overlap the weight blobs", what);
+  }
   return launch_status(rz::launch_gelu_ffn_q4_0(static_cast<const uint8_t*>(w_up),
                                                 static_cast<const uint8_t*>(w_down), x, up_bias,
                                                 down_bias, h, y, hidden_dim, inter_dim,

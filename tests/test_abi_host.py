@@ -418,3 +418,57 @@ def test_stream_read_helper_rejects_bad_arguments():
                          capture_output=True, text=True, env=env, timeout=120)
     assert res.returncode == 0, res.stderr
     assert json.loads(res.stdout) == [-1] * len(calls)
+
+
+# Buffers 4 GiB apart never overlap; an output placed on an input does.
+def _b(k):
+    return P + (k << 32)
+
+
+_OVERLAP_CASES = [
+    # (entry, args with separate buffers, index of an output, index of an input it is moved onto)
+    ("rz_q8_1_quantize", [_b(0), 896, 1024, 2, _b(1), None], 4, 0),
+    ("rz_rmsnorm_q8_1", [_b(0), _b(1), 1e-5, 4096, 4096, 1, _b(2), _b(3), None], 6, 0),
+    ("rz_rmsnorm_q8_1", [_b(0), _b(1), 1e-5, 4096, 4096, 1, _b(2), _b(3), None], 7, 1),
+    ("rz_q4k_q8_gemv", [_b(0), _b(1), _b(2), 4096, 4096, 1, None], 2, 1),
+    ("rz_q4k_q8_gemv", [_b(0), _b(1), _b(2), 4096, 4096, 1, None], 2, 0),
+    ("rz_q4k_q8_gemv_add", [_b(0), _b(1), _b(3), _b(2), 4096, 4096, 1, None], 3, 1),
+    ("rz_q4k_q8_gemv_f32", [_b(0), _b(1), 4096, _b(2), _b(3), 4096, 4096, None], 3, 1),
+    ("rz_q4k_q8_gemv_f32", [_b(0), _b(1), 4096, _b(2), _b(3), 4096, 4096, None], 4, 3),
+    ("rz_q4k_q8_gemv_f32", [_b(0), _b(1), 4096, _b(2), _b(3), 4096, 4096, None], 4, 0),
+    ("rz_q4k_gemv", [_b(0), _b(1), 4096, _b(2), 4096, 4096, None], 3, 0),
+    ("rz_q4_0_gemv", [_b(0), _b(1), 0, _b(2), 4096, 1024, None], 3, 1),
+    ("rz_q4_0_gemv", [_b(0), _b(1), 1, _b(2), 4096, 1024, None], 3, 0),
+    ("rz_swiglu_ffn_q4k", [_b(0), _b(1), _b(2), _b(3), _b(4), _b(5), _b(6), None, 4096, 14336, None], 4, 3),
+    ("rz_swiglu_ffn_q4k", [_b(0), _b(1), _b(2), _b(3), _b(4), _b(5), _b(6), None, 4096, 14336, None], 6, 5),
+    ("rz_swiglu_ffn_q4k", [_b(0), _b(1), _b(2), _b(3), _b(4), _b(5), _b(6), None, 4096, 14336, None], 5, 1),
+    ("rz_swiglu_ffn_q4k_f32", [_b(0), _b(1), _b(2), _b(3), _b(4), _b(5), None, 4096, 14336, None], 5, 2),
+    ("rz_gelu_ffn_q4_0", [_b(0), _b(1), _b(2), None, None, _b(3), _b(4), 2560, 10240, None], 5, 0),
+    ("rz_gelu_ffn_q4_0", [_b(0), _b(1), _b(2), None, None, _b(3), _b(4), 2560, 10240, None], 6, 1),
+]
+
+
+@pytest.mark.parametrize("fn,args,out_i,in_i", _OVERLAP_CASES)
+def test_outputs_must_not_overlap_inputs(lib, fn, args, out_i, in_i):
+    """With every buffer apart the call passes validation (and, with no device
+    visible, fails at the launch); with the output moved onto one of the
+    call's inputs it is rejected before any HIP call."""
+    bad = list(args)
+    bad[out_i] = args[in_i]
+    (rc_ok, _), (rc_bad, msg) = run_isolated([(fn, args), (fn, bad)])
+    assert rc_ok == rz.RZ_ELAUNCH
+    assert rc_bad == rz.RZ_EINVAL and "overlap" in msg, msg
+
+
+def test_lm_head_outputs_must_not_overlap_inputs(lib):
+    need = 1187 * 8     # fp32 x, 151936 x 1024
+    base = [_b(0), _b(1), 0, None, _b(2), 151936, 1024, _b(3), _b(4), _b(5), need, None]
+    cases = [list(base)]
+    for out_i, in_i in [(4, 0), (4, 1), (7, 1), (9, 0), (8, 7)]:
+        c = list(base)
+        c[out_i] = base[in_i]
+        cases.append(c)
+    res = run_isolated([("rz_lm_head_q4_0", c) for c in cases])
+    assert res[0][0] == rz.RZ_ELAUNCH
+    for rc, msg in res[1:]:
+        assert rc == rz.RZ_EINVAL and "overlap" in msg, msg
