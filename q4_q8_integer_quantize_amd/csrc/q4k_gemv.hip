@@ -62,15 +62,24 @@ static hipError_t launch_g(const Q4KGemvArgs& a, long groups, Epi epi, hipStream
 }
 
 // G (row groups per wave) is the smallest power of two, at most 8, that keeps
-// the grid at about one wave per SIMD; fewer, deeper-pipelined waves stream
-// better than many short ones.
+// the grid within a target wave count.  With the activation staged in LDS
+// (two or more slots) a wave's start is cheap, and many waves in flight
+// stream best: two-slot rows take one group a wave (4096 -> 14336: 7.2
+// against 7.5 us at 8 groups; two tokens 9.3-9.9 against 9.8-10.2 us); rows
+// of three or more slots, whose waves hold many more registers, aim at 2048
+// waves (14336 -> 4096: 7.7-7.9 us at 2 groups, 8.2 at 4, 8.1-8.4 at 1).
+// One-slot rows read x directly and aim at about one wave per SIMD.
+template <int S>
+constexpr long target_waves() { return S >= 3 ? 2048 : kTargetWaves; }
+
 template <int TPR, int S, int NT>
 static hipError_t run_q4k(const Q4KGemvArgs& a, Epi epi, hipStream_t st) {
   constexpr int R = rows_unrolled<S, NT>();
   constexpr int RW = 8 / TPR;
   const long rows_per_group = (long)RW * R;
   const long groups = (a.out_dim + rows_per_group - 1) / rows_per_group;
-  const long per_wave = (groups + kTargetWaves - 1) / kTargetWaves;
+  const long target = S == 2 ? groups : target_waves<S>();
+  const long per_wave = (groups + target - 1) / target;
   if (per_wave <= 1) return launch_g<TPR, S, NT, 1>(a, groups, epi, st);
   if (per_wave <= 2) return launch_g<TPR, S, NT, 2>(a, groups, epi, st);
   if (per_wave <= 4) return launch_g<TPR, S, NT, 4>(a, groups, epi, st);
