@@ -28,20 +28,24 @@ struct SwiArgs {
   int nsb;        // hidden / 256
 };
 
-// Wave w owns rows 8w .. 8w+7 of the block.  Its work is G = 2 * (8 / (RW*R))
-// row groups -- gate and up alternating -- unrolled into straight-line code
-// with P groups requested ahead, as in q4k_q8_gemv_kernel: no load sits under
-// a branch, so each wait is for exactly the tile about to be reduced.
-template <int TPR, int S, int R, int P>
-__global__ __launch_bounds__(256) void swiglu_gate_up_kernel(SwiArgs a) {
+// Wave w of WPB owns rows RPW*w .. RPW*w + RPW-1 of the block (RPW = 32 /
+// WPB).  Its work is G = 2 * (RPW / (RW*R)) row groups -- gate and up
+// alternating -- unrolled into straight-line code with P groups requested
+// ahead, as in q4k_q8_gemv_kernel: no load sits under a branch, so each wait
+// is for exactly the tile about to be reduced.  XL: the workgroup copies x
+// into LDS once and the lanes read their slots from there.
+template <int TPR, int S, int R, int P, int WPB = 4, bool XL = false>
+__global__ __launch_bounds__(64 * WPB) void swiglu_gate_up_kernel(SwiArgs a) {
   constexpr int RW = 8 / TPR;
   constexpr int kGroupRows = RW * R;                 // rows of one matrix per group
-  static_assert(8 % kGroupRows == 0, "a wave's 8 rows split into whole groups");
-  constexpr int G = 2 * (8 / kGroupRows);            // gate, up, gate, up, ...
+  constexpr int RPW = 32 / WPB;                      // rows of the block a wave owns
+  static_assert(32 % WPB == 0 && RPW % kGroupRows == 0, "a wave's rows split into whole groups");
+  constexpr int G = 2 * (RPW / kGroupRows);          // gate, up, gate, up, ...
+  constexpr int NT = 64 * WPB;
   __shared__ float gs[32], us[32], hs[32];
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t blk_row0 = blockIdx.x * 32u;
-  const uint32_t row0 = blk_row0 + wave * 8u;
+  const uint32_t row0 = blk_row0 + wave * (uint32_t)RPW;
   const LaneRole ro = make_role<TPR>();
   const uint32_t row_bytes = (uint32_t)a.nsb * kQ4KBytes;
   const uint32_t bytes = (uint32_t)a.inter * row_bytes;
@@ -51,12 +55,40 @@ __global__ __launch_bounds__(256) void swiglu_gate_up_kernel(SwiArgs a) {
 
   // activation first: vector loads retire in order
   XSlots<S, 1> xs;
-  load_x_slots<TPR, S, 1>(xs, a.xq, 0, a.nsb, 1, ro);
+  constexpr uint32_t kXBytes = (uint32_t)(S * TPR * 8 * kQ8Bytes);
+  constexpr int kXChunks = (int)(kXBytes / 16);
+  constexpr int kXIters = XL ? (kXChunks + NT - 1) / NT : 1;
+  __shared__ __attribute__((aligned(16))) uint8_t x_lds[XL ? kXBytes : 16];
+  u32x4 xin[kXIters];
+  if constexpr (XL) {
+    const uint32_t xbytes = (uint32_t)a.nsb * 8u * kQ8Bytes;
+    const __amdgpu_buffer_rsrc_t xr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)a.xq, (short)0, (int)xbytes, kBufferWord3);
+#pragma unroll
+    for (int j = 0; j < kXIters; ++j) {
+      const uint32_t c = (uint32_t)(j * NT) + threadIdx.x;
+      xin[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             xr, 16u * c < xbytes ? 16u * c : xbytes, 0, 0));
+    }
+  } else {
+    load_x_slots<TPR, S, 1>(xs, a.xq, 0, a.nsb, 1, ro);
+  }
   WTile<S, R> t[G];
 #pragma unroll
   for (int k = 0; k < P && k < G; ++k)
     load_w_tile<TPR, S, R>(t[k], (k & 1) ? su : sg, off, row0 + (uint32_t)(k >> 1) * kGroupRows);
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (XL) {
+#pragma unroll
+    for (int j = 0; j < kXIters; ++j) {
+      const uint32_t c = (uint32_t)(j * NT) + threadIdx.x;
+      if (c < (uint32_t)kXChunks) *(u32x4*)(x_lds + 16u * c) = xin[j];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    load_x_slots_from_lds<TPR, S, 1>(xs, x_lds, kXBytes, a.nsb, 1, ro);
+  }
 #pragma unroll
   for (int k = 0; k < G; ++k) {
     if (k + P < G)
@@ -69,7 +101,7 @@ __global__ __launch_bounds__(256) void swiglu_gate_up_kernel(SwiArgs a) {
       float* dst = (k & 1) ? us : gs;
 #pragma unroll
       for (int r = 0; r < R; ++r)
-        dst[wave * 8u + (uint32_t)(k >> 1) * kGroupRows + r * RW + ro.rs] = acc[r][0];
+        dst[wave * (uint32_t)RPW + (uint32_t)(k >> 1) * kGroupRows + r * RW + ro.rs] = acc[r][0];
     }
   }
   __syncthreads();
@@ -106,7 +138,12 @@ static hipError_t run_gate_up(const SwiArgs& a, hipStream_t st) {
   constexpr int R = RW * R_reg <= 8 ? R_reg : 1;
   constexpr int G = 2 * (8 / (RW * R));
   constexpr int P = G > 2 ? 2 : G - 1 > 0 ? G - 1 : 1;
-  hipLaunchKernelGGL((swiglu_gate_up_kernel<TPR, S, R, P>), dim3(a.inter / 32), dim3(256), 0, st, a);
+  // x staged in LDS for rows of two or more slots, as in the GEMV (4096 ->
+  // 2 x 14336: 13.0-13.2 against 13.2-13.4 us); more waves a workgroup
+  // (8 or 16, fewer rows each) measured slower (14.3-14.8 us)
+  constexpr bool XL = S >= 2;
+  hipLaunchKernelGGL((swiglu_gate_up_kernel<TPR, S, R, P, 4, XL>), dim3(a.inter / 32), dim3(256), 0,
+                     st, a);
   return hipGetLastError();
 }
 
