@@ -131,6 +131,58 @@ __device__ __forceinline__ void load_x_slots_from_lds(XSlots<S, NT>& xs, const u
   }
 }
 
+// A workgroup's copy of the activation chunk in LDS: the chunk's Q8_1 blocks
+// of every token (token t at byte t * kTokBytes), brought in 16 bytes a thread
+// per step.  x_stage_request issues the loads (before the first weight
+// tiles: vector loads retire in order, so waiting for them later never waits
+// for a tile); x_stage_commit writes them to LDS, passes an LDS-only barrier
+// (weight loads stay in flight) and fills the lane's slots from LDS.
+template <int TPR, int S, int NT, int WPB>
+struct XStage {
+  static constexpr uint32_t kTokBytes = (uint32_t)(S * TPR * 8 * kQ8Bytes);
+  static constexpr int kChunks = NT * (int)(kTokBytes / 16);
+  static constexpr int kIters = (kChunks + 64 * WPB - 1) / (64 * WPB);
+  static constexpr size_t kLdsBytes = (size_t)NT * kTokBytes;
+  u32x4 v[kIters];
+};
+
+// xq: token 0, block 0 of the full activation; the chunk starts at super-block
+// sb0 and holds nsb super-blocks; token t starts tok_stride bytes after t-1.
+template <int TPR, int S, int NT, int WPB>
+__device__ __forceinline__ void x_stage_request(XStage<TPR, S, NT, WPB>& st, const uint8_t* xq,
+                                                uint32_t tok_stride, int sb0, int nsb,
+                                                int n_tokens) {
+  using X = XStage<TPR, S, NT, WPB>;
+  const uint32_t chunk_bytes = (uint32_t)nsb * 8u * kQ8Bytes;
+  const uint32_t xbytes = (uint32_t)n_tokens * tok_stride;
+  const __amdgpu_buffer_rsrc_t xr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)xq, (short)0, (int)xbytes, kBufferWord3);
+#pragma unroll
+  for (int j = 0; j < X::kIters; ++j) {
+    const uint32_t gidx = (uint32_t)(j * 64 * WPB) + threadIdx.x;
+    const uint32_t tk = gidx / (X::kTokBytes / 16u), c16 = 16u * (gidx % (X::kTokBytes / 16u));
+    const bool on = gidx < (uint32_t)X::kChunks && tk < (uint32_t)n_tokens && c16 < chunk_bytes;
+    const uint32_t off = on ? tk * tok_stride + (uint32_t)sb0 * 8u * kQ8Bytes + c16 : xbytes;
+    st.v[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
+  }
+}
+
+template <int TPR, int S, int NT, int WPB>
+__device__ __forceinline__ void x_stage_commit(const XStage<TPR, S, NT, WPB>& st, uint8_t* lds,
+                                               XSlots<S, NT>& xs, int nsb, int n_tokens,
+                                               const LaneRole& ro) {
+  using X = XStage<TPR, S, NT, WPB>;
+#pragma unroll
+  for (int j = 0; j < X::kIters; ++j) {
+    const uint32_t gidx = (uint32_t)(j * 64 * WPB) + threadIdx.x;
+    if (gidx < (uint32_t)X::kChunks) *(u32x4*)(lds + 16u * gidx) = st.v[j];
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  load_x_slots_from_lds<TPR, S, NT>(xs, lds, X::kTokBytes, nsb, n_tokens, ro);
+}
+
 // Weights of R*RW rows (RW = 8/TPR side by side, R unrolled) for one lane:
 // the 16-byte header and the lane's 16-byte qs slice of each slot.
 template <int S, int R>
@@ -357,29 +409,13 @@ __global__ __launch_bounds__(64 * WPB) void q4k_q8_gemv_kernel(Q4KGemvArgs a) {
   // the lanes read their slots from there, instead of every wave reading
   // them from L2.
   XSlots<S, NT> xs;
-  constexpr uint32_t kTokBytes = (uint32_t)(S * TPR * 8 * kQ8Bytes);   // LDS bytes a token
-  constexpr int kXChunks = NT * (int)(kTokBytes / 16);
-  constexpr int kXIters = XL ? (kXChunks + 64 * WPB - 1) / (64 * WPB) : 1;
+  XStage<TPR, S, NT, WPB> xst;
   extern __shared__ __attribute__((aligned(16))) uint8_t xl_lds[];
-  u32x4 xin[kXIters];
-  if constexpr (XL) {
-    const uint32_t tok_stride = (uint32_t)a.nsb_row * 8u * kQ8Bytes;
-    const uint32_t chunk_bytes = (uint32_t)a.nsb * 8u * kQ8Bytes;
-    const uint32_t xbytes = (uint32_t)a.n_tokens * tok_stride;
-    const __amdgpu_buffer_rsrc_t xr =
-        __builtin_amdgcn_make_buffer_rsrc((void*)a.xq, (short)0, (int)xbytes, kBufferWord3);
-#pragma unroll
-    for (int j = 0; j < kXIters; ++j) {
-      const uint32_t gidx = (uint32_t)(j * 64 * WPB) + threadIdx.x;
-      const uint32_t tk = gidx / (kTokBytes / 16u), c16 = 16u * (gidx % (kTokBytes / 16u));
-      const bool on = gidx < (uint32_t)kXChunks && tk < (uint32_t)a.n_tokens && c16 < chunk_bytes;
-      const uint32_t off = on ? tk * tok_stride + (uint32_t)a.sb0 * 8u * kQ8Bytes + c16 : xbytes;
-      xin[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
-    }
-  } else {
+  if constexpr (XL)
+    x_stage_request(xst, a.xq, (uint32_t)a.nsb_row * 8u * kQ8Bytes, a.sb0, a.nsb, a.n_tokens);
+  else
     load_x_slots<TPR, S, NT>(xs, a.xq + (size_t)a.sb0 * 8 * kQ8Bytes,
                              (size_t)a.nsb_row * 8 * kQ8Bytes, a.nsb, a.n_tokens, ro);
-  }
   WTile<S, R> t[G];
   float rv[G][R][NT];
   __amdgpu_buffer_rsrc_t rr;
@@ -395,19 +431,7 @@ __global__ __launch_bounds__(64 * WPB) void q4k_q8_gemv_kernel(Q4KGemvArgs a) {
   }
   // keep the scheduler from sinking requests below the first wait
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (XL) {
-    // stage x (this waits for the activation loads only), then an LDS-only
-    // release/acquire around the barrier, so the weight loads stay in flight
-#pragma unroll
-    for (int j = 0; j < kXIters; ++j) {
-      const uint32_t gidx = (uint32_t)(j * 64 * WPB) + threadIdx.x;
-      if (gidx < (uint32_t)kXChunks) *(u32x4*)(xl_lds + 16u * gidx) = xin[j];
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-    load_x_slots_from_lds<TPR, S, NT>(xs, xl_lds, kTokBytes, a.nsb, a.n_tokens, ro);
-  }
+  if constexpr (XL) x_stage_commit(xst, xl_lds, xs, a.nsb, a.n_tokens, ro);
 #pragma unroll
   for (int k = 0; k < G; ++k) {
     if (k + P < G) {

@@ -46,7 +46,7 @@ static hipError_t launch_g(const Q4KGemvArgs& a, long groups, Epi epi, hipStream
   constexpr int R = rows_unrolled<S, NT>();
   constexpr int P = G > kTilesInFlight ? kTilesInFlight : (G > 1 ? G - 1 : 1);
   constexpr bool XL = x_in_lds<S>();
-  const size_t lds = XL ? (size_t)NT * S * TPR * 8 * kQ8Bytes : 0;
+  const size_t lds = XL ? XStage<TPR, S, NT, 4>::kLdsBytes : 0;
   const long waves = (groups + G - 1) / G;
   const unsigned grid = (unsigned)((waves + 3) / 4);
   if (epi == Epi::kAccumulate)

@@ -26,7 +26,7 @@ struct Q4KMultiArgs {
   uint32_t group0[kMaxMats + 1];    // first row group of each matrix; [n_mats] = total
 };
 
-template <int TPR, int S, int R, int NT, int G, int P>
+template <int TPR, int S, int R, int NT, int G, int P, bool XL = false>
 __global__ __launch_bounds__(256) void q4k_q8_gemv_multi_kernel(Q4KMultiArgs a) {
   constexpr int RW = 8 / TPR;
   constexpr uint32_t kRowsPerGroup = (uint32_t)RW * R;
@@ -82,12 +82,19 @@ __global__ __launch_bounds__(256) void q4k_q8_gemv_multi_kernel(Q4KMultiArgs a) 
   };
   const LaneOffsets<TPR, S> off = lane_offsets<TPR, S>(src_of(0), 0, ro);
 
+  // activation first (XL: staged in LDS once per workgroup, as in the GEMV)
   XSlots<S, NT> xs;
-  load_x_slots<TPR, S, NT>(xs, a.xq, (size_t)a.nsb * 8 * kQ8Bytes, a.nsb, a.n_tokens, ro);
+  XStage<TPR, S, NT, 4> xst;
+  extern __shared__ __attribute__((aligned(16))) uint8_t xl_lds[];
+  if constexpr (XL)
+    x_stage_request(xst, a.xq, (uint32_t)a.nsb * 8u * kQ8Bytes, 0, a.nsb, a.n_tokens);
+  else
+    load_x_slots<TPR, S, NT>(xs, a.xq, (size_t)a.nsb * 8 * kQ8Bytes, a.nsb, a.n_tokens, ro);
   WTile<S, R> t[G];
 #pragma unroll
   for (int k = 0; k < P && k < G; ++k) load_w_tile<TPR, S, R>(t[k], src_of(k), off, rb[k]);
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (XL) x_stage_commit(xst, xl_lds, xs, a.nsb, a.n_tokens, ro);
 #pragma unroll
   for (int k = 0; k < G; ++k) {
     if (k + P < G) load_w_tile<TPR, S, R>(t[k + P], src_of(k + P), off, rb[k + P]);
@@ -112,17 +119,22 @@ template <int TPR, int S, int NT, int G>
 static hipError_t launch_multi_g(const Q4KMultiArgs& a, hipStream_t st) {
   constexpr int R = (S <= 2 && NT <= 2) ? 2 : 1;
   constexpr int P = G > 2 ? 2 : (G > 1 ? G - 1 : 1);
+  constexpr bool XL = S >= 2;
+  const size_t lds = XL ? XStage<TPR, S, NT, 4>::kLdsBytes : 0;
   const long waves = ((long)a.group0[a.n_mats] + G - 1) / G;
   const unsigned grid = (unsigned)((waves + 3) / 4);
-  hipLaunchKernelGGL((q4k_q8_gemv_multi_kernel<TPR, S, R, NT, G, P>), dim3(grid), dim3(256), 0,
-                     st, a);
+  hipLaunchKernelGGL((q4k_q8_gemv_multi_kernel<TPR, S, R, NT, G, P, XL>), dim3(grid), dim3(256),
+                     lds, st, a);
   return hipGetLastError();
 }
 
-// Groups per wave: ceil(groups / 1024), at most 8, so that the grid is at most
-// 256 workgroups, one per CU.  A grid a little over 256 leaves some CUs two
-// workgroups and the launch waits for them: measured on the attention set
-// (5120 groups), 4 groups a wave (320 workgroups) 8.7 us, 5 (256) 7.1 us.
+// Groups per wave.  Rows of two or more slots stage x in LDS and follow the
+// single-matrix rule (q4k_gemv.hip): one group a wave for two slots, about
+// 2048 waves beyond (the attention set, 5120 groups: 6.4 us at one group a
+// wave against 7.0-7.3 us at five without the staging).  One-slot rows read x
+// directly and take ceil(groups / 1024), at most 8, so that the grid is at
+// most 256 workgroups, one per CU: a grid a little over 256 leaves some CUs
+// two workgroups and the launch waits for them.
 template <int TPR, int S, int NT>
 static hipError_t run_multi(Q4KMultiArgs a, hipStream_t st) {
   constexpr int R = (S <= 2 && NT <= 2) ? 2 : 1;
@@ -133,7 +145,8 @@ static hipError_t run_multi(Q4KMultiArgs a, hipStream_t st) {
                                                        rows_per_group
                                                  : 0u);
   const long groups = a.group0[a.n_mats];
-  switch ((groups + 1023) / 1024) {
+  const long target = S == 2 ? groups : (S >= 3 ? 2048 : 1024);
+  switch ((groups + target - 1) / target) {
     case 0:
     case 1: return launch_multi_g<TPR, S, NT, 1>(a, st);
     case 2: return launch_multi_g<TPR, S, NT, 2>(a, st);

@@ -41,7 +41,6 @@ __global__ __launch_bounds__(64 * WPB) void swiglu_gate_up_kernel(SwiArgs a) {
   constexpr int RPW = 32 / WPB;                      // rows of the block a wave owns
   static_assert(32 % WPB == 0 && RPW % kGroupRows == 0, "a wave's rows split into whole groups");
   constexpr int G = 2 * (RPW / kGroupRows);          // gate, up, gate, up, ...
-  constexpr int NT = 64 * WPB;
   __shared__ float gs[32], us[32], hs[32];
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t blk_row0 = blockIdx.x * 32u;
@@ -55,40 +54,18 @@ __global__ __launch_bounds__(64 * WPB) void swiglu_gate_up_kernel(SwiArgs a) {
 
   // activation first: vector loads retire in order
   XSlots<S, 1> xs;
-  constexpr uint32_t kXBytes = (uint32_t)(S * TPR * 8 * kQ8Bytes);
-  constexpr int kXChunks = (int)(kXBytes / 16);
-  constexpr int kXIters = XL ? (kXChunks + NT - 1) / NT : 1;
-  __shared__ __attribute__((aligned(16))) uint8_t x_lds[XL ? kXBytes : 16];
-  u32x4 xin[kXIters];
-  if constexpr (XL) {
-    const uint32_t xbytes = (uint32_t)a.nsb * 8u * kQ8Bytes;
-    const __amdgpu_buffer_rsrc_t xr =
-        __builtin_amdgcn_make_buffer_rsrc((void*)a.xq, (short)0, (int)xbytes, kBufferWord3);
-#pragma unroll
-    for (int j = 0; j < kXIters; ++j) {
-      const uint32_t c = (uint32_t)(j * NT) + threadIdx.x;
-      xin[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                             xr, 16u * c < xbytes ? 16u * c : xbytes, 0, 0));
-    }
-  } else {
+  XStage<TPR, S, 1, WPB> xst;
+  __shared__ __attribute__((aligned(16))) uint8_t x_lds[XL ? XStage<TPR, S, 1, WPB>::kLdsBytes : 16];
+  if constexpr (XL)
+    x_stage_request(xst, a.xq, (uint32_t)a.nsb * 8u * kQ8Bytes, 0, a.nsb, 1);
+  else
     load_x_slots<TPR, S, 1>(xs, a.xq, 0, a.nsb, 1, ro);
-  }
   WTile<S, R> t[G];
 #pragma unroll
   for (int k = 0; k < P && k < G; ++k)
     load_w_tile<TPR, S, R>(t[k], (k & 1) ? su : sg, off, row0 + (uint32_t)(k >> 1) * kGroupRows);
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (XL) {
-#pragma unroll
-    for (int j = 0; j < kXIters; ++j) {
-      const uint32_t c = (uint32_t)(j * NT) + threadIdx.x;
-      if (c < (uint32_t)kXChunks) *(u32x4*)(x_lds + 16u * c) = xin[j];
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-    load_x_slots_from_lds<TPR, S, 1>(xs, x_lds, kXBytes, a.nsb, 1, ro);
-  }
+  if constexpr (XL) x_stage_commit(xst, x_lds, xs, a.nsb, 1, ro);
 #pragma unroll
   for (int k = 0; k < G; ++k) {
     if (k + P < G)
