@@ -452,7 +452,6 @@ static hipError_t launch_q40_g(const Q40Args& a, long groups, bool epi, hipStrea
 // bytes, within a workgroup's 64 KiB).
 constexpr int kQ8ChunkPairs = 256;
 constexpr int kXlChunkPairs = 224;
-constexpr long kXlTwoGroups = 8192;
 
 // Launch shape of a column chunk of np pairs (run_q40_chunk and run_xl_chunk
 // take exactly these; q4_0_lm_head_partials uses them to size the
@@ -468,9 +467,9 @@ constexpr long kXlTwoGroups = 8192;
 //           16 lanes x 3 at 6.4 us against 8 x 5 at 7.4 us; 160 pairs: 64 x 3
 //           at 7.9 us against 32 x 5 at 8.8 us; 128 pairs: 32 x 4 at 7.1 us
 //           against 16 x 8 at 8.3 us).
-// Groups per wave: Q8_1 x streams best with many one-group waves; fp32 x
-// takes two once there are 8192 groups (the 151936 x 1024 LM head; at 2560
-// and 3584 groups one group a wave was faster).
+// Groups per wave: one, for both activation formats -- many one-group waves
+// stream best (the 151936 x 1024 LM head with fp32 x, launches of the two
+// shapes interleaved: 18.1 us against 20.2 us at two groups a wave).
 struct Q40Shape {
   int lpr, s, r, g, wpb;
 };
@@ -481,7 +480,7 @@ static int pow2_at_least(int v) {
   return p;
 }
 
-static Q40Shape q40_shape(int np, long out_dim, bool q8) {
+static Q40Shape q40_shape(int np, bool q8) {
   Q40Shape sh;
   if (q8) {
     sh.lpr = np <= 32 ? pow2_at_least(np) : 64;
@@ -496,9 +495,7 @@ static Q40Shape q40_shape(int np, long out_dim, bool q8) {
     sh.s = (np + sh.lpr - 1) / sh.lpr;
     sh.r = 1;
   }
-  const long rows_per_group = (long)(kWave / sh.lpr) * sh.r;
-  const long groups = (out_dim + rows_per_group - 1) / rows_per_group;
-  sh.g = (!q8 && groups >= kXlTwoGroups) ? 2 : 1;
+  sh.g = 1;
   sh.wpb = (!q8 && sh.s * sh.lpr >= 128) ? 8 : 4;   // q40_wpb
   return sh;
 }
@@ -508,7 +505,6 @@ static hipError_t run_q40(const Q40Args& a, bool epi, hipStream_t st) {
   constexpr int RW = kWave / LPR;
   const long rows_per_group = (long)RW * R;
   const long groups = (a.out_dim + rows_per_group - 1) / rows_per_group;
-  if (!Q8 && groups >= kXlTwoGroups) return launch_q40_g<LPR, S, R, 2, Q8>(a, groups, epi, st);
   return launch_q40_g<LPR, S, R, 1, Q8>(a, groups, epi, st);
 }
 
@@ -593,7 +589,7 @@ long q4_0_lm_head_partials(int out_dim, int in_dim, int x_format) {
   const int npairs_row = in_dim / 64;
   const int chunk = q8 ? kQ8ChunkPairs : kXlChunkPairs;
   const int last = npairs_row - ((npairs_row - 1) / chunk) * chunk;   // pairs of the last chunk
-  const Q40Shape sh = q40_shape(last, out_dim, q8);
+  const Q40Shape sh = q40_shape(last, q8);
   const long rows_per_group = (long)(kWave / sh.lpr) * sh.r;
   const long groups = (out_dim + rows_per_group - 1) / rows_per_group;
   const long waves = (groups + sh.g - 1) / sh.g;

@@ -318,8 +318,8 @@ def test_swiglu_ffn_f32_accepts_y_on_x(lib):
 
 def test_lm_head_workspace_bytes(lib):
     # 151936 x 1024: 16 pairs a row -> 16 lanes a row, 4 rows side by side, 4 unrolled,
-    # 9496 row groups; fp32 x takes 2 groups a wave (1187 workgroups), Q8_1 x one (2374)
-    assert rz.rz_lm_head_q4_0_workspace_bytes(151936, 1024, 0) == 1187 * 8
+    # 9496 row groups of 16 rows, one a wave, four waves a workgroup: 2374 workgroups
+    assert rz.rz_lm_head_q4_0_workspace_bytes(151936, 1024, 0) == 2374 * 8
     assert rz.rz_lm_head_q4_0_workspace_bytes(151936, 1024, 1) == 2374 * 8
     assert rz.rz_lm_head_q4_0_workspace_bytes(1, 64, 0) == 8
     for bad in ((0, 1024, 0), (151936, 1000, 0), (151936, 1024, 2), (151936, 0, 1)):
@@ -336,15 +336,15 @@ IDX = P + (4 << 30)
     ((P, P, 0, None, Y, 151936, 1000, None, None, None, 0, None), rz.RZ_EDIM),
     ((P, P, 0, None, Y, 0, 1024, None, None, None, 0, None), rz.RZ_EDIM),
     ((P, P, 0, None, Y, 151936, 1024, IDX, None, None, 0, None), rz.RZ_EINVAL),     # no workspace
-    ((P, P, 0, None, Y, 151936, 1024, IDX, None, WS, 9495, None), rz.RZ_EINVAL),    # short
-    ((P, P, 1, None, Y, 151936, 1024, None, IDX, WS, 9496, None), rz.RZ_EINVAL),    # short (Q8_1)
+    ((P, P, 0, None, Y, 151936, 1024, IDX, None, WS, 18991, None), rz.RZ_EINVAL),    # short
+    ((P, P, 1, None, Y, 151936, 1024, None, IDX, WS, 18991, None), rz.RZ_EINVAL),    # short (Q8_1)
     ((P, P, 0, Y + 4, Y, 151936, 1024, None, None, None, 0, None), rz.RZ_EINVAL),   # bias overlaps
-    ((P, P, 0, None, Y, 151936, 1024, IDX, None, Y + 64, 9496, None), rz.RZ_EINVAL),  # ws on logits
-    ((P, P, 0, None, Y, 151936, 1024, WS + 8, None, WS, 9496, None), rz.RZ_EINVAL),   # idx in ws
-    ((P, P, 0, None, Y, 151936, 1024, IDX, None, WS + 2, 9496, None), rz.RZ_EALIGN),
+    ((P, P, 0, None, Y, 151936, 1024, IDX, None, Y + 64, 18992, None), rz.RZ_EINVAL),  # ws on logits
+    ((P, P, 0, None, Y, 151936, 1024, WS + 8, None, WS, 18992, None), rz.RZ_EINVAL),   # idx in ws
+    ((P, P, 0, None, Y, 151936, 1024, IDX, None, WS + 2, 18992, None), rz.RZ_EALIGN),
     ((P, P + 8, 0, None, Y, 151936, 1024, None, None, None, 0, None), rz.RZ_EALIGN),
     ((P, P, 0, P_ODD, Y, 151936, 1024, None, None, None, 0, None), rz.RZ_EALIGN),
-    ((P, P, 0, None, Y, 151936, 1024, IDX + 2, None, WS, 9496, None), rz.RZ_EALIGN),
+    ((P, P, 0, None, Y, 151936, 1024, IDX + 2, None, WS, 18992, None), rz.RZ_EALIGN),
 ])
 def test_lm_head_rejects(lib, args, code):
     assert _rc("rz_lm_head_q4_0", *args) == code
@@ -355,7 +355,7 @@ def test_lm_head_accepts_bias_in_place_and_exact_workspace(lib):
     res = run_isolated([("rz_lm_head_q4_0", [P, P, 0, Y, Y, 151936, 1024, None, None, None, 0,
                                              None]),
                         ("rz_lm_head_q4_0", [P, P, 0, None, Y, 151936, 1024, IDX, IDX + 4, WS,
-                                             9496, None])])
+                                             2374 * 8, None])])
     assert [rc for rc, _ in res] == [rz.RZ_ELAUNCH, rz.RZ_ELAUNCH]
 
 
@@ -461,7 +461,7 @@ def test_outputs_must_not_overlap_inputs(lib, fn, args, out_i, in_i):
 
 
 def test_lm_head_outputs_must_not_overlap_inputs(lib):
-    need = 1187 * 8     # fp32 x, 151936 x 1024
+    need = 2374 * 8     # fp32 x, 151936 x 1024
     base = [_b(0), _b(1), 0, None, _b(2), 151936, 1024, _b(3), _b(4), _b(5), need, None]
     cases = [list(base)]
     for out_i, in_i in [(4, 0), (4, 1), (7, 1), (9, 0), (8, 7)]:
