@@ -71,7 +71,7 @@ extern "C" {
  *   n        logical length, 1 <= n <= n_padded
  *   n_padded multiple of 32; values n..n_padded-1 are taken as +0.0
  *   n_tokens 1 <= n_tokens <= RZ_MAX_TOKENS
- *   x_q8     out: [n_tokens][n_padded/32] blocks, 8-byte aligned
+ *   x_q8     out: [n_tokens][n_padded/32] blocks, 16-byte aligned
  * Errors: RZ_EINVAL (null pointer, n_tokens out of range), RZ_EDIM,
  * RZ_EALIGN, RZ_ELAUNCH.  The output is bit-exact (a unique result). */
 int rz_q8_1_quantize(const float* x, int n, int n_padded, int n_tokens,
@@ -98,7 +98,7 @@ int rz_q8_1_quantize(const float* x, int n, int n_padded, int n_tokens,
  *            are +0.0, as for rz_q8_1_quantize)
  *   n_tokens 1..RZ_MAX_TOKENS
  *   normed   optional out (NULL to skip): fp32 [n_tokens][n], the values v
- *   x_q8     out: [n_tokens][n_padded/32] blocks, 8-byte aligned
+ *   x_q8     out: [n_tokens][n_padded/32] blocks, 16-byte aligned
  * Inputs whose sum of squares overflows fp32 are outside the contract.
  * Errors: RZ_EINVAL (null pointer, n_tokens or eps), RZ_EDIM, RZ_EALIGN,
  * RZ_ELAUNCH. */
@@ -112,7 +112,7 @@ int rz_rmsnorm_q8_1(const float* x, const float* gamma, float eps, int n, int n_
  * Per 32-value sub-block j of super-block b: isum = sum(q4 * q8) in int32,
  * y += d * sc_j * d_x * isum - dmin * m_j * s_x.
  *   w_q4k    [out_dim][in_dim/256] super-blocks, 16-byte aligned
- *   x_q8     [n_tokens][in_dim/32] Q8_1 blocks, 8-byte aligned
+ *   x_q8     [n_tokens][in_dim/32] Q8_1 blocks, 16-byte aligned
  *   y        out: fp32 [n_tokens][out_dim] (token-major), 4-byte aligned
  *   out_dim  >= 1; in_dim multiple of 256 (padded); both <= RZ_MAX_DIM;
  *            the matrix (out_dim * in_dim/256 * 144 bytes) < 2 GiB
@@ -172,7 +172,7 @@ int rz_q4k_q8_gemv_multi(int n_mats, const void* const* w_q4k, float* const* y,
  *   x        fp32 [n], 4-byte aligned; values n..in_dim-1 are taken as 0
  *   n        1 <= n <= in_dim
  *   x_q8     optional out (NULL to skip): the [in_dim/32] Q8_1 blocks, for
- *            further projections of the same activation; 8-byte aligned
+ *            further projections of the same activation; 16-byte aligned
  *   y        out: fp32 [out_dim], 4-byte aligned
  *   in_dim   multiple of 256, <= 16384; one token
  * Errors: RZ_EINVAL, RZ_EDIM, RZ_EALIGN, RZ_ELAUNCH. */
@@ -224,7 +224,7 @@ int rz_swiglu_ffn_q4k_f32(const void* w_gate, const void* w_up, const void* w_do
  * Weight value = (q - 8) * d.
  *   w_q4_0   [out_dim][in_dim/32] blocks of 18 bytes, 4-byte aligned
  *   x        x_format 0: fp32 [in_dim], 16-byte aligned;
- *            x_format 1: Q8_1 [in_dim/32] blocks, 8-byte aligned
+ *            x_format 1: Q8_1 [in_dim/32] blocks, 16-byte aligned
  *   y        out: fp32 [out_dim], 4-byte aligned
  *   in_dim   multiple of 64 (pairs of blocks keep every load 4-byte aligned)
  * Errors: RZ_EINVAL (also unknown x_format), RZ_EDIM, RZ_EALIGN, RZ_ELAUNCH. */
@@ -297,9 +297,9 @@ int rz_gelu_ffn_q4_0(const void* w_up, const void* w_down, const float* x, const
  *   y = W_down h_q8                     (Q4_K x Q8_1, hidden_dim rows)
  *   w_gate, w_up  [inter_dim][hidden_dim/256] super-blocks, 16-byte aligned
  *   w_down        [hidden_dim][inter_dim/256] super-blocks, 16-byte aligned
- *   x_q8          [hidden_dim/32] Q8_1 blocks, 8-byte aligned
+ *   x_q8          [hidden_dim/32] Q8_1 blocks, 16-byte aligned
  *   h             out: fp32 [inter_dim]
- *   h_q8          out: [inter_dim/32] Q8_1 blocks, 8-byte aligned
+ *   h_q8          out: [inter_dim/32] Q8_1 blocks, 16-byte aligned
  *   y             out: fp32 [hidden_dim]
  *   gu            optional out (NULL to skip): fp32 [2][inter_dim], g then u
  *   hidden_dim, inter_dim  multiples of 256; hidden_dim <= 16384 (the fused

@@ -90,7 +90,7 @@ int rz_q8_1_quantize(const float* x, int n, int n_padded, int n_tokens, void* x_
   if (n <= 0 || n > n_padded)
     return fail(RZ_EDIM, "%s: n=%d must satisfy 1 <= n <= n_padded=%d", what, n, n_padded);
   if (!aligned(x, 4)) return fail(RZ_EALIGN, "%s: x must be 4-byte aligned", what);
-  if (!aligned(x_q8, 8)) return fail(RZ_EALIGN, "%s: x_q8 must be 8-byte aligned", what);
+  if (!aligned(x_q8, 16)) return fail(RZ_EALIGN, "%s: x_q8 must be 16-byte aligned", what);
   if (!clear_of({x_q8, q8_bytes(n_tokens, n_padded)}, {{x, 4LL * n_tokens * n}}))
     return fail(RZ_EINVAL, "%s: x_q8 must not overlap x", what);
   return launch_status(rz::launch_q8_1_quantize(x, n, n_padded, n_tokens,
@@ -112,7 +112,7 @@ int rz_rmsnorm_q8_1(const float* x, const float* gamma, float eps, int n, int n_
     return fail(RZ_EDIM, "%s: n=%d must satisfy 1 <= n <= n_padded=%d", what, n, n_padded);
   if (!aligned(x, 4) || !aligned(gamma, 4) || (normed && !aligned(normed, 4)))
     return fail(RZ_EALIGN, "%s: fp32 buffers must be 4-byte aligned", what);
-  if (!aligned(x_q8, 8)) return fail(RZ_EALIGN, "%s: x_q8 must be 8-byte aligned", what);
+  if (!aligned(x_q8, 16)) return fail(RZ_EALIGN, "%s: x_q8 must be 16-byte aligned", what);
   // every workgroup reads the whole row while others write their slices
   const Span xs{x, 4LL * n_tokens * n}, gs{gamma, 4LL * n}, qs{x_q8, q8_bytes(n_tokens, n_padded)};
   if (!clear_of(qs, {xs, gs}) || !clear_of({normed, 4LL * n_tokens * n}, {xs, gs, qs}))
@@ -134,7 +134,7 @@ int rz_q4k_q8_gemv(const void* w_q4k, const void* x_q8, float* y, int out_dim, i
   if ((long long)out_dim * (in_dim / 256) * RZ_Q4K_BLOCK_BYTES > kMaxMatrixBytes)
     return fail(RZ_EDIM, "%s: weight matrix larger than %lld bytes", what, kMaxMatrixBytes);
   if (!aligned(w_q4k, 16)) return fail(RZ_EALIGN, "%s: w_q4k must be 16-byte aligned", what);
-  if (!aligned(x_q8, 8)) return fail(RZ_EALIGN, "%s: x_q8 must be 8-byte aligned", what);
+  if (!aligned(x_q8, 16)) return fail(RZ_EALIGN, "%s: x_q8 must be 16-byte aligned", what);
   if (!aligned(y, 4)) return fail(RZ_EALIGN, "%s: y must be 4-byte aligned", what);
   if (!clear_of({y, 4LL * n_tokens * out_dim},
                 {{w_q4k, q4k_bytes(out_dim, in_dim)}, {x_q8, q8_bytes(n_tokens, in_dim)}}))
@@ -157,7 +157,7 @@ int rz_q4k_q8_gemv_add(const void* w_q4k, const void* x_q8, const float* r, floa
   if ((long long)out_dim * (in_dim / 256) * RZ_Q4K_BLOCK_BYTES > kMaxMatrixBytes)
     return fail(RZ_EDIM, "%s: weight matrix larger than %lld bytes", what, kMaxMatrixBytes);
   if (!aligned(w_q4k, 16)) return fail(RZ_EALIGN, "%s: w_q4k must be 16-byte aligned", what);
-  if (!aligned(x_q8, 8)) return fail(RZ_EALIGN, "%s: x_q8 must be 8-byte aligned", what);
+  if (!aligned(x_q8, 16)) return fail(RZ_EALIGN, "%s: x_q8 must be 16-byte aligned", what);
   if (!aligned(r, 4) || !aligned(y, 4))
     return fail(RZ_EALIGN, "%s: r and y must be 4-byte aligned", what);
   if (!same_or_disjoint(r, y, (long long)n_tokens * out_dim))
@@ -182,7 +182,7 @@ int rz_q4k_q8_gemv_multi(int n_mats, const void* const* w_q4k, float* const* y,
   if (n_tokens < 1 || n_tokens > RZ_MAX_TOKENS)
     return fail(RZ_EINVAL, "%s: n_tokens=%d outside 1..%d", what, n_tokens, RZ_MAX_TOKENS);
   if (int rc = check_dim(what, "in_dim", in_dim, 256)) return rc;
-  if (!aligned(x_q8, 8)) return fail(RZ_EALIGN, "%s: x_q8 must be 8-byte aligned", what);
+  if (!aligned(x_q8, 16)) return fail(RZ_EALIGN, "%s: x_q8 must be 16-byte aligned", what);
   const uint8_t* w[RZ_MAX_MATS];
   float* yy[RZ_MAX_MATS];
   int od[RZ_MAX_MATS];
@@ -230,7 +230,7 @@ int rz_q4k_q8_gemv_f32(const void* w_q4k, const float* x, int n, void* x_q8, flo
   if (!aligned(w_q4k, 16)) return fail(RZ_EALIGN, "%s: w_q4k must be 16-byte aligned", what);
   if (!aligned(x, 4) || !aligned(y, 4))
     return fail(RZ_EALIGN, "%s: x and y must be 4-byte aligned", what);
-  if (x_q8 && !aligned(x_q8, 8)) return fail(RZ_EALIGN, "%s: x_q8 must be 8-byte aligned", what);
+  if (x_q8 && !aligned(x_q8, 16)) return fail(RZ_EALIGN, "%s: x_q8 must be 16-byte aligned", what);
   {
     const Span ws{w_q4k, q4k_bytes(out_dim, in_dim)}, xs{x, 4LL * n}, qs{x_q8, q8_bytes(1, in_dim)};
     if (!clear_of({y, 4LL * out_dim}, {ws, xs, qs}) || !clear_of(qs, {ws, xs}))
@@ -305,8 +305,7 @@ int rz_q4_0_gemv(const void* w_q4_0, const void* x, int x_format, float* y, int 
   if (int rc = check_dim(what, "out_dim", out_dim, 1)) return rc;
   if (int rc = check_dim(what, "in_dim", in_dim, 64)) return rc;
   if (!aligned(w_q4_0, 4)) return fail(RZ_EALIGN, "%s: w_q4_0 must be 4-byte aligned", what);
-  if (!aligned(x, x_format == 0 ? 16 : 8))
-    return fail(RZ_EALIGN, "%s: x must be %d-byte aligned", what, x_format == 0 ? 16 : 8);
+  if (!aligned(x, 16)) return fail(RZ_EALIGN, "%s: x must be 16-byte aligned", what);
   if (!aligned(y, 4)) return fail(RZ_EALIGN, "%s: y must be 4-byte aligned", what);
   if (!clear_of({y, 4LL * out_dim}, {{w_q4_0, q4_0_bytes(out_dim, in_dim)},
                                      {x, x_format == 0 ? 4LL * in_dim : q8_bytes(1, in_dim)}}))
@@ -334,8 +333,8 @@ int swiglu_ffn(const char* what, const void* w_gate, const void* w_up, const voi
                 hidden_dim);
   if (!aligned(w_gate, 16) || !aligned(w_up, 16) || !aligned(w_down, 16))
     return fail(RZ_EALIGN, "%s: weight blobs must be 16-byte aligned", what);
-  if (!aligned(x_q8, 8) || !aligned(h_q8, 8))
-    return fail(RZ_EALIGN, "%s: Q8_1 buffers must be 8-byte aligned", what);
+  if (!aligned(x_q8, 16) || !aligned(h_q8, 16))
+    return fail(RZ_EALIGN, "%s: Q8_1 buffers must be 16-byte aligned", what);
   if (!aligned(h, 4) || !aligned(y, 4) || (gu && !aligned(gu, 4)) || (r && !aligned(r, 4)))
     return fail(RZ_EALIGN, "%s: fp32 buffers must be 4-byte aligned", what);
   if (r && !same_or_disjoint(r, y, hidden_dim))
@@ -388,8 +387,7 @@ int rz_lm_head_q4_0(const void* w_q4_0, const void* x, int x_format, const float
   if (int rc = check_dim(what, "out_dim", out_dim, 1)) return rc;
   if (int rc = check_dim(what, "in_dim", in_dim, 64)) return rc;
   if (!aligned(w_q4_0, 4)) return fail(RZ_EALIGN, "%s: w_q4_0 must be 4-byte aligned", what);
-  if (!aligned(x, x_format == 0 ? 16 : 8))
-    return fail(RZ_EALIGN, "%s: x must be %d-byte aligned", what, x_format == 0 ? 16 : 8);
+  if (!aligned(x, 16)) return fail(RZ_EALIGN, "%s: x must be 16-byte aligned", what);
   if (!aligned(logits, 4) || (bias && !aligned(bias, 4)) || (argmax_idx && !aligned(argmax_idx, 4)) ||
       (argmax_val && !aligned(argmax_val, 4)))
     return fail(RZ_EALIGN, "%s: logits, bias and the argmax outputs must be 4-byte aligned", what);

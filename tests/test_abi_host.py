@@ -105,7 +105,8 @@ def _rc(fn, *args):
     ((P, 0, 1024, 1, P, None), rz.RZ_EDIM),                 # n == 0
     ((P, 896, 0, 1, P, None), rz.RZ_EDIM),                  # n_padded == 0
     ((P_ODD, 896, 1024, 1, P, None), rz.RZ_EALIGN),         # x not 4-aligned
-    ((P, 896, 1024, 1, P + 4, None), rz.RZ_EALIGN),         # x_q8 not 8-aligned
+    ((P, 896, 1024, 1, P + 4, None), rz.RZ_EALIGN),         # x_q8 not 16-aligned
+    ((P, 896, 1024, 1, P + 8, None), rz.RZ_EALIGN),
 ])
 def test_q8_1_quantize_rejects(lib, args, code):
     assert _rc("rz_q8_1_quantize", *args) == code
@@ -125,6 +126,7 @@ def test_q8_1_quantize_rejects(lib, args, code):
     ((P, P, P, 14336, 1 << 25, 1, None), rz.RZ_EDIM),
     ((P + 8, P, P, 14336, 4096, 1, None), rz.RZ_EALIGN),    # weights need 16
     ((P, P + 4, P, 14336, 4096, 1, None), rz.RZ_EALIGN),
+    ((P, P + 8, P, 14336, 4096, 1, None), rz.RZ_EALIGN),    # Q8_1 activations need 16
     ((P, P, P_ODD, 14336, 4096, 1, None), rz.RZ_EALIGN),
 ])
 def test_q4k_q8_gemv_rejects(lib, args, code):

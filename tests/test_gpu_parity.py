@@ -1114,3 +1114,153 @@ def test_binding_errors_on_gpu():
         rz.rz_q4k_q8_gemv(t, t, t, 1, 100, 1)
     with pytest.raises(ValueError):
         rz.rz_q4k_q8_gemv(t, t, t, 1, 256, 1)     # buffers too small for the shape
+
+
+# ------------------------------------------------------------------ minimum alignments
+def _at(arr_or_n, shift: int, dtype="f32"):
+    """A device buffer whose first byte sits `shift` bytes past a 256-byte
+    boundary: a copy of a numpy array, or (given a size) an output filled
+    with a marker.  Its neighbours inside the backing allocation are never
+    touched by a correct kernel."""
+    import torch
+    if isinstance(arr_or_n, int):
+        n = arr_or_n
+        src = None
+    else:
+        src = np.ascontiguousarray(arr_or_n)
+        n = src.size if dtype == "f32" else src.nbytes
+    esize = 4 if dtype == "f32" else 1
+    nbytes = n * esize
+    raw = torch.full((nbytes + 512,), 0xA5, dtype=torch.uint8, device="cuda")
+    base = (-raw.data_ptr()) % 256
+    view = raw[base + shift: base + shift + nbytes]
+    if dtype == "f32":
+        view = view.view(torch.float32)
+    if src is not None:
+        host_t = torch.from_numpy(src.reshape(-1).view(np.uint8).copy() if dtype != "f32"
+                                  else src.astype(np.float32).reshape(-1).copy())
+        view.copy_(host_t.to("cuda"))
+    else:
+        if dtype == "f32":
+            view.fill_(float("nan"))
+    assert view.data_ptr() % 256 == shift
+    return view
+
+
+def _bits(t):
+    return host(t).view(np.uint8).copy()
+
+
+def _run_both(call, aligned_args, shifted_args, outs_a, outs_s, what):
+    call(*aligned_args)
+    call(*shifted_args)
+    for k, (a, b) in enumerate(zip(outs_a, outs_s)):
+        assert np.array_equal(_bits(a), _bits(b)), "%s: output %d differs at minimum alignment" % (what, k)
+
+
+def test_minimum_alignments_bit_identical():
+    """Every entry point on buffers at exactly the alignments include/rz.h
+    requires (Q4_K and Q8_1 16 bytes, Q4_0 4, fp32 4 -- 16 for the Q4_0 and
+    GELU activations) gives the same bytes as on 256-byte aligned buffers."""
+    banner("minimum alignments")
+    g = synth.rng(70, 1)
+    # Q8_1 quantize and RMSNorm
+    x = synth.activation(synth.rng(70, 0), 4096, 2)
+    gam = synth.norm_weights(synth.rng(70, 2), 4096)
+    qa, qs = _at(2 * 128 * 40, 0, "u8"), _at(2 * 128 * 40, 16, "u8")
+    _run_both(lambda xx, q: rz.rz_q8_1_quantize(xx, 4096, 4096, 2, q),
+              (_at(x, 0), qa), (_at(x, 4), qs), [qa], [qs], "quantize")
+    na, ns = _at(2 * 4096, 0), _at(2 * 4096, 4)
+    qa, qs = _at(2 * 128 * 40, 0, "u8"), _at(2 * 128 * 40, 16, "u8")
+    _run_both(lambda xx, gg, nn, q: rz.rz_rmsnorm_q8_1(xx, gg, 1e-5, 4096, 4096, 2, nn, q),
+              (_at(x, 0), _at(gam, 0), na, qa), (_at(x, 4), _at(gam, 4), ns, qs),
+              [na, qa], [ns, qs], "rmsnorm")
+    # Q4_K x Q8_1 GEMV: two-slot rows, seven-slot rows, two tokens, eight tokens (matrix cores)
+    for out_dim, in_dim, nt in [(1000, 4096, 1), (300, 14336, 1), (129, 4096, 2), (77, 4096, 8)]:
+        w = synth.q4k_weights(synth.rng(71, out_dim), out_dim, in_dim)
+        xq = oracle.q8_1_to_bytes(oracle.quantize_q8_1(synth.activation(synth.rng(71, 0), in_dim, nt), in_dim))
+        ya, ys = _at(nt * out_dim, 0), _at(nt * out_dim, 4)
+        _run_both(lambda ww, q, yy: rz.rz_q4k_q8_gemv(ww, q, yy, out_dim, in_dim, nt),
+                  (_at(w, 0, "u8"), _at(xq, 0, "u8"), ya), (_at(w, 16, "u8"), _at(xq, 16, "u8"), ys),
+                  [ya], [ys], "gemv %dx%d nt %d" % (out_dim, in_dim, nt))
+        r = synth.activation(synth.rng(71, 5), out_dim, nt)
+        ya, ys = _at(nt * out_dim, 0), _at(nt * out_dim, 4)
+        _run_both(lambda ww, q, rr, yy: rz.rz_q4k_q8_gemv_add(ww, q, rr, yy, out_dim, in_dim, nt),
+                  (_at(w, 0, "u8"), _at(xq, 0, "u8"), _at(r, 0), ya),
+                  (_at(w, 16, "u8"), _at(xq, 16, "u8"), _at(r, 4), ys), [ya], [ys], "gemv add")
+    # fused quantize + GEMV (16-byte and dword activation loads) and the fp32-x GEMV
+    w = synth.q4k_weights(synth.rng(72, 1), 500, 4096)
+    xf = synth.activation(synth.rng(72, 0), 4096)
+    for n in (4096, 4093):
+        ya, ys = _at(500, 0), _at(500, 4)
+        qa, qs = _at(128 * 40, 0, "u8"), _at(128 * 40, 16, "u8")
+        _run_both(lambda ww, xx, q, yy: rz.rz_q4k_q8_gemv_f32(ww, xx, n, q, yy, 500, 4096),
+                  (_at(w, 0, "u8"), _at(xf[:n], 0), qa, ya), (_at(w, 16, "u8"), _at(xf[:n], 4), qs, ys),
+                  [ya, qa], [ys, qs], "fused n %d" % n)
+        ya, ys = _at(500, 0), _at(500, 4)
+        _run_both(lambda ww, xx, yy: rz.rz_q4k_gemv(ww, xx, n, yy, 500, 4096),
+                  (_at(w, 0, "u8"), _at(xf[:n], 0), ya), (_at(w, 16, "u8"), _at(xf[:n], 4), ys),
+                  [ya], [ys], "fp32-x gemv n %d" % n)
+    # several matrices in one launch
+    shapes = [(300, 4096), (64, 4096), (129, 4096)]
+    ws = [synth.q4k_weights(synth.rng(73, k), o, i) for k, (o, i) in enumerate(shapes)]
+    xq = oracle.q8_1_to_bytes(oracle.quantize_q8_1(synth.activation(synth.rng(73, 9), 4096), 4096))
+    yas = [_at(o, 0) for o, _ in shapes]
+    yss = [_at(o, 4) for o, _ in shapes]
+    rz.rz_q4k_q8_gemv_multi([_at(w_, 0, "u8") for w_ in ws], _at(xq, 0, "u8"), yas, [o for o, _ in shapes], 4096)
+    rz.rz_q4k_q8_gemv_multi([_at(w_, 16, "u8") for w_ in ws], _at(xq, 16, "u8"), yss, [o for o, _ in shapes], 4096)
+    for a_, b_ in zip(yas, yss):
+        assert np.array_equal(_bits(a_), _bits(b_)), "multi differs at minimum alignment"
+    # SwiGLU chains
+    hid, inter = 1024, 2816
+    wg, wu = (synth.q4k_weights(synth.rng(74, k), inter, hid) for k in (1, 2))
+    wd = synth.q4k_weights(synth.rng(74, 3), hid, inter)
+    xf = synth.activation(synth.rng(74, 0), hid)
+    xq = oracle.q8_1_to_bytes(oracle.quantize_q8_1(xf, hid))
+    outs = {}
+    for sh in (0, 1):
+        h, hq, y = _at(inter, 4 * sh), _at(inter // 32 * 40, 16 * sh, "u8"), _at(hid, 4 * sh)
+        rz.rz_swiglu_ffn_q4k(_at(wg, 16 * sh, "u8"), _at(wu, 16 * sh, "u8"), _at(wd, 16 * sh, "u8"),
+                             _at(xq, 16 * sh, "u8"), h, hq, y, None, hid, inter)
+        h2, y2 = _at(inter, 4 * sh), _at(hid, 4 * sh)
+        rz.rz_swiglu_ffn_q4k_f32(_at(wg, 16 * sh, "u8"), _at(wu, 16 * sh, "u8"), _at(wd, 16 * sh, "u8"),
+                                 _at(xf, 4 * sh), h2, y2, None, hid, inter)
+        outs[sh] = [_bits(t) for t in (h, hq, y, h2, y2)]
+    for k in range(5):
+        assert np.array_equal(outs[0][k], outs[1][k]), "swiglu output %d differs at minimum alignment" % k
+    # Q4_0: GEMV (fp32 and Q8_1 x; 16-pair and 160-pair rows), LM head with argmax, GELU FFN
+    for out_dim, in_dim in [(1000, 1024), (9, 10240)]:
+        w0 = synth.q4_0_weights(synth.rng(75, in_dim), out_dim, in_dim)
+        xf = synth.activation(synth.rng(75, 0), in_dim)
+        xq = oracle.q8_1_to_bytes(oracle.quantize_q8_1(xf, in_dim))
+        for fmt, xx in ((0, xf), (1, xq)):
+            dt = "f32" if fmt == 0 else "u8"
+            ya, ys = _at(out_dim, 0), _at(out_dim, 4)
+            _run_both(lambda ww, x_, yy: rz.rz_q4_0_gemv(ww, x_, fmt, yy, out_dim, in_dim),
+                      (_at(w0, 0, "u8"), _at(xx, 0, dt), ya), (_at(w0, 4, "u8"), _at(xx, 16, dt), ys),
+                      [ya], [ys], "q4_0 %dx%d fmt %d" % (out_dim, in_dim, fmt))
+            need = rz.rz_lm_head_q4_0_workspace_bytes(out_dim, in_dim, fmt)
+            bias = synth.activation(synth.rng(75, 7), out_dim)
+            res = []
+            for sh in (0, 1):
+                lg, idx, val = _at(out_dim, 4 * sh), _at(1, 4 * sh, "u8"), _at(1, 4 * sh)
+                idx = _at(4, 4 * sh, "u8")
+                ws_ = _at(need, 4 * sh, "u8")
+                rz.rz_lm_head_q4_0(_at(w0, 4 * sh, "u8"), _at(xx, 16 * sh, dt), fmt, _at(bias, 4 * sh),
+                                   lg, out_dim, in_dim, idx, val, ws_)
+                res.append([_bits(lg), _bits(idx), _bits(val)])
+            for k in range(3):
+                assert np.array_equal(res[0][k], res[1][k]), "lm head output %d differs" % k
+    hid, inter = 2560, 10240
+    wup = synth.q4_0_weights(synth.rng(76, 1), inter, hid)
+    wdn = synth.q4_0_weights(synth.rng(76, 2), hid, inter)
+    xf = synth.activation(synth.rng(76, 0), hid)
+    ub, db = synth.activation(synth.rng(76, 3), inter), synth.activation(synth.rng(76, 4), hid)
+    res = []
+    for sh in (0, 1):
+        h, y = _at(inter, 16 * sh), _at(hid, 4 * sh)
+        rz.rz_gelu_ffn_q4_0(_at(wup, 4 * sh, "u8"), _at(wdn, 4 * sh, "u8"), _at(xf, 16 * sh),
+                            _at(ub, 4 * sh), _at(db, 4 * sh), h, y, hid, inter)
+        res.append([_bits(h), _bits(y)])
+    for k in range(2):
+        assert np.array_equal(res[0][k], res[1][k]), "gelu output %d differs" % k
