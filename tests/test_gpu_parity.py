@@ -1264,3 +1264,67 @@ def test_minimum_alignments_bit_identical():
         res.append([_bits(h), _bits(y)])
     for k in range(2):
         assert np.array_equal(res[0][k], res[1][k]), "gelu output %d differs" % k
+
+
+# ------------------------------------------------------------------ HIP graph capture
+def test_graph_replays_match_eager():
+    """A decode-layer-shaped sequence -- RMSNorm + Q8_1, the attention
+    projections in one launch, the O projection with its residual, RMSNorm
+    again, the SwiGLU chain with its residual, and the LM head with bias and
+    greedy token -- captured in one HIP graph and replayed three times, with
+    eager work and synchronisations between replays, gives every replay the
+    bytes of the eager run.  Nothing in the library records memsets or
+    allocations, so the graph has kernel nodes only."""
+    import torch
+    banner("graph replays")
+    H, KV, I, V = 4096, 1024, 2816, 5000      # two-slot rows: the LDS-staged activation path
+    g = lambda k: synth.rng(80, k)
+    wq, wk, wv, wo = (dev_bytes(synth.q4k_weights(g(k), o, H)) for k, o in ((1, H), (2, KV), (3, KV), (4, H)))
+    wg, wu = (dev_bytes(synth.q4k_weights(g(k), I, H)) for k in (5, 6))
+    wd = dev_bytes(synth.q4k_weights(g(7), H, I))
+    wl = dev_bytes(synth.q4_0_weights(g(8), V, H))
+    gam1, gam2 = dev_f32(synth.norm_weights(g(9), H)), dev_f32(synth.norm_weights(g(10), H))
+    bias = dev_f32(synth.activation(g(11), V))
+    x0 = dev_f32(synth.activation(g(0), H))
+    hidden = torch.empty(H, dtype=torch.float32, device="cuda")
+    xq = torch.empty(rz.q8_1_nbytes(H), dtype=torch.uint8, device="cuda")
+    q, k_, v = (torch.empty(o, dtype=torch.float32, device="cuda") for o in (H, KV, KV))
+    h = torch.empty(I, dtype=torch.float32, device="cuda")
+    hq = torch.empty(rz.q8_1_nbytes(I), dtype=torch.uint8, device="cuda")
+    logits = torch.empty(V, dtype=torch.float32, device="cuda")
+    idx = torch.empty(1, dtype=torch.int32, device="cuda")
+    val = torch.empty(1, dtype=torch.float32, device="cuda")
+    ws = torch.empty(rz.rz_lm_head_q4_0_workspace_bytes(V, H, 0), dtype=torch.uint8, device="cuda")
+    outs = (hidden, xq, q, k_, v, h, hq, logits, idx, val)
+
+    def layer():
+        hidden.copy_(x0)
+        rz.rz_rmsnorm_q8_1(hidden, gam1, 1e-5, H, H, 1, None, xq)
+        rz.rz_q4k_q8_gemv_multi([wq, wk, wv], xq, [q, k_, v], [H, KV, KV], H)
+        # the attention output stands in as q; quantize it for the O projection
+        rz.rz_q8_1_quantize(q, H, H, 1, xq)
+        rz.rz_q4k_q8_gemv_add(wo, xq, hidden, hidden, H, H, 1)
+        rz.rz_rmsnorm_q8_1(hidden, gam2, 1e-5, H, H, 1, None, xq)
+        rz.rz_swiglu_ffn_q4k_add(wg, wu, wd, xq, h, hq, hidden, hidden, None, H, I)
+        rz.rz_lm_head_q4_0(wl, hidden, 0, bias, logits, V, H, idx, val, ws)
+
+    layer()
+    torch.cuda.synchronize()
+    eager = [_bits(t) for t in outs]
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer()                                   # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        layer()
+    for rep in range(3):
+        for t in outs:                            # eager work between replays
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k, t in enumerate(outs):
+            assert np.array_equal(_bits(t), eager[k]), "replay %d: output %d differs from eager" % (rep, k)
