@@ -224,7 +224,6 @@ def time_rows(lib, rz, torch, dev, graph_time, copies, x, xq, y) -> dict:
                                                              hid.data_ptr(), hid.data_ptr(),
                                                              4096, 4096, 1, s))),
         o_w + XQ_BYTES + 8 * 4096, o_w, "rz_q4k_q8_gemv_add (hidden += O x, in place)")
-    del attn
 
     # SwiGLU chain 4096 -> 14336 -> 4096, and its down projection alone
     INTER = 14336
@@ -276,7 +275,37 @@ def time_rows(lib, rz, torch, dev, graph_time, copies, x, xq, y) -> dict:
         graph_time(lambda i, s: check(lib.rz_q4k_q8_gemv(ffn_p[i % len(ffn_p)][2], hq.data_ptr(),
                                                          yf.data_ptr(), IN_DIM, INTER, 1, s))),
         W_BYTES + q8_bytes(INTER) + 4 * IN_DIM, W_BYTES, "rz_q4k_q8_gemv")
-    del ffn
+
+    # one decode layer's projections in sequence, as a model would chain them:
+    # RMSNorm + Q8_1, Q/K/V in one launch, the attention output (stood in for
+    # by q) quantized for O, O with the residual, RMSNorm + Q8_1, the SwiGLU
+    # chain with the residual; weights of both halves rotated
+    gam_l = torch.from_numpy(synth.norm_weights(synth.rng(1, synth.T_GAMMA), IN_DIM)).to(dev)
+    hid_l = torch.from_numpy(synth.activation(synth.rng(1, synth.T_ACT), IN_DIM)).to(dev)
+    xq_l = torch.empty(XQ_BYTES, dtype=torch.uint8, device=dev)
+    qkv = [torch.empty(o, dtype=torch.float32, device=dev) for o, _ in shapes[:3]]
+    qkv_y = (ctypes.c_void_p * 3)(*[t.data_ptr() for t in qkv])
+    qkv_od = (ctypes.c_int * 3)(*[o for o, _ in shapes[:3]])
+    qkv_w = [(ctypes.c_void_p * 3)(*c[:3]) for c in attn_p]
+
+    def layer_body(i, s):
+        a_w, f_w = attn_p[i % len(attn_p)], ffn_p[i % len(ffn_p)]
+        hp, xp = hid_l.data_ptr(), xq_l.data_ptr()
+        check(lib.rz_rmsnorm_q8_1(hp, gam_l.data_ptr(), 1e-5, IN_DIM, IN_DIM, 1, None, xp, s))
+        check(lib.rz_q4k_q8_gemv_multi(3, qkv_w[i % len(qkv_w)], qkv_y, qkv_od, xp, IN_DIM, 1, s))
+        check(lib.rz_q8_1_quantize(qkv[0].data_ptr(), IN_DIM, IN_DIM, 1, xp, s))
+        check(lib.rz_q4k_q8_gemv_add(a_w[3], xp, hp, hp, IN_DIM, IN_DIM, 1, s))
+        check(lib.rz_rmsnorm_q8_1(hp, gam_l.data_ptr(), 1e-5, IN_DIM, IN_DIM, 1, None, xp, s))
+        check(lib.rz_swiglu_ffn_q4k_add(f_w[0], f_w[1], f_w[2], xp, h.data_ptr(), hq.data_ptr(),
+                                        hp, hp, None, IN_DIM, INTER, s))
+
+    layer_w = attn_w + ffn_w
+    rows["decode_layer_4096_14336"] = row_entry(
+        graph_time(layer_body), layer_w + 8 * XQ_BYTES + 4 * 6 * IN_DIM + 4 * 6144
+        + 4 * INTER + 2 * q8_bytes(INTER), layer_w,
+        "one layer's projections: RMSNorm+Q8_1, Q/K/V (one launch), quantize, O+residual, "
+        "RMSNorm+Q8_1, SwiGLU chain+residual (7 kernels)")
+    del ffn, attn
 
     # Q4_0 LM head 151936 x (896 -> 1024), fp32 and Q8_1 activation
     VOCAB, HID, HID_P = 151936, 896, 1024
