@@ -276,8 +276,9 @@ def time_rows(lib, rz, torch, dev, graph_time, copies, x, xq, y) -> dict:
                                                          yf.data_ptr(), IN_DIM, INTER, 1, s))),
         W_BYTES + q8_bytes(INTER) + 4 * IN_DIM, W_BYTES, "rz_q4k_q8_gemv")
 
+    # RMSNorm + Q8_1 + the Q, K, V projections, in one launch and as two; then
     # one decode layer's projections in sequence, as a model would chain them:
-    # RMSNorm + Q8_1, Q/K/V in one launch, the attention output (stood in for
+    # RMSNorm + Q8_1 + Q/K/V in one launch, the attention output (stood in for
     # by q) quantized for O, O with the residual, RMSNorm + Q8_1, the SwiGLU
     # chain with the residual; weights of both halves rotated
     gam_l = torch.from_numpy(synth.norm_weights(synth.rng(1, synth.T_GAMMA), IN_DIM)).to(dev)
@@ -288,23 +289,65 @@ def time_rows(lib, rz, torch, dev, graph_time, copies, x, xq, y) -> dict:
     qkv_od = (ctypes.c_int * 3)(*[o for o, _ in shapes[:3]])
     qkv_w = [(ctypes.c_void_p * 3)(*c[:3]) for c in attn_p]
 
-    def layer_body(i, s):
-        a_w, f_w = attn_p[i % len(attn_p)], ffn_p[i % len(ffn_p)]
-        hp, xp = hid_l.data_ptr(), xq_l.data_ptr()
+    def qkv_separate(i, s):
+        check(lib.rz_rmsnorm_q8_1(hid_l.data_ptr(), gam_l.data_ptr(), 1e-5, IN_DIM, IN_DIM, 1,
+                                  None, xq_l.data_ptr(), s))
+        check(lib.rz_q4k_q8_gemv_multi(3, qkv_w[i % len(qkv_w)], qkv_y, qkv_od, xq_l.data_ptr(),
+                                       IN_DIM, 1, s))
+
+    def qkv_fused(i, s):
+        check(lib.rz_rmsnorm_q4k_q8_gemv_multi(3, qkv_w[i % len(qkv_w)], qkv_y, qkv_od,
+                                               hid_l.data_ptr(), gam_l.data_ptr(), 1e-5, IN_DIM,
+                                               None, IN_DIM, s))
+
+    qkv_wb = sum(q4k_bytes(o, n) for o, n in shapes[:3])
+    qkv_bytes = qkv_wb + 2 * X_BYTES + 4 * (4096 + 1024 + 1024)
+    rows["rmsnorm_qkv_4096"] = row_entry(
+        graph_time(qkv_fused), qkv_bytes, qkv_wb,
+        "rz_rmsnorm_q4k_q8_gemv_multi: RMSNorm + Q8_1 + Q, K, V in one launch")
+    rows["rmsnorm_qkv_4096_two_launch"] = row_entry(
+        graph_time(qkv_separate), qkv_bytes + 2 * XQ_BYTES, qkv_wb,
+        "rz_rmsnorm_q8_1, then rz_q4k_q8_gemv_multi (Q, K, V)")
+
+    hid_n = torch.from_numpy(synth.activation(synth.rng(2, synth.T_ACT), IN_DIM)).to(dev)
+
+    def ffn_norm_separate(i, s):
+        wg, wu, wd = ffn_p[i % len(ffn_p)]
+        hp, xp = hid_n.data_ptr(), xq_l.data_ptr()
         check(lib.rz_rmsnorm_q8_1(hp, gam_l.data_ptr(), 1e-5, IN_DIM, IN_DIM, 1, None, xp, s))
-        check(lib.rz_q4k_q8_gemv_multi(3, qkv_w[i % len(qkv_w)], qkv_y, qkv_od, xp, IN_DIM, 1, s))
+        check(lib.rz_swiglu_ffn_q4k_add(wg, wu, wd, xp, h.data_ptr(), hq.data_ptr(), hp, hp, None,
+                                        IN_DIM, INTER, s))
+
+    def ffn_norm_fused(i, s, hp=None):
+        wg, wu, wd = ffn_p[i % len(ffn_p)]
+        hp = hp or hid_n.data_ptr()
+        check(lib.rz_rmsnorm_swiglu_ffn_q4k_add(wg, wu, wd, hp, gam_l.data_ptr(), 1e-5,
+                                                h.data_ptr(), hq.data_ptr(), hp, None, IN_DIM,
+                                                INTER, s))
+
+    ffn_norm_bytes = ffn_w + 4 * X_BYTES + 4 * INTER + 2 * q8_bytes(INTER)
+    rows["rmsnorm_swiglu_ffn_add_4096_14336"] = row_entry(
+        graph_time(ffn_norm_fused), ffn_norm_bytes, ffn_w,
+        "rz_rmsnorm_swiglu_ffn_q4k_add: RMSNorm + Q8_1 in every gate/up workgroup, then down "
+        "+ residual (2 kernels)")
+    rows["rmsnorm_swiglu_ffn_add_4096_14336_three_launch"] = row_entry(
+        graph_time(ffn_norm_separate), ffn_norm_bytes + 2 * XQ_BYTES, ffn_w,
+        "rz_rmsnorm_q8_1, then rz_swiglu_ffn_q4k_add")
+
+    def layer_body(i, s):
+        a_w = attn_p[i % len(attn_p)]
+        hp, xp = hid_l.data_ptr(), xq_l.data_ptr()
+        qkv_fused(i, s)
         check(lib.rz_q8_1_quantize(qkv[0].data_ptr(), IN_DIM, IN_DIM, 1, xp, s))
         check(lib.rz_q4k_q8_gemv_add(a_w[3], xp, hp, hp, IN_DIM, IN_DIM, 1, s))
-        check(lib.rz_rmsnorm_q8_1(hp, gam_l.data_ptr(), 1e-5, IN_DIM, IN_DIM, 1, None, xp, s))
-        check(lib.rz_swiglu_ffn_q4k_add(f_w[0], f_w[1], f_w[2], xp, h.data_ptr(), hq.data_ptr(),
-                                        hp, hp, None, IN_DIM, INTER, s))
+        ffn_norm_fused(i, s, hp)
 
     layer_w = attn_w + ffn_w
     rows["decode_layer_4096_14336"] = row_entry(
-        graph_time(layer_body), layer_w + 8 * XQ_BYTES + 4 * 6 * IN_DIM + 4 * 6144
+        graph_time(layer_body), layer_w + 2 * XQ_BYTES + 9 * X_BYTES + 4 * 6144
         + 4 * INTER + 2 * q8_bytes(INTER), layer_w,
-        "one layer's projections: RMSNorm+Q8_1, Q/K/V (one launch), quantize, O+residual, "
-        "RMSNorm+Q8_1, SwiGLU chain+residual (7 kernels)")
+        "one layer's projections: RMSNorm+Q8_1+Q/K/V (one launch), quantize, O+residual, "
+        "RMSNorm+Q8_1+SwiGLU gate/up (one launch), down+residual (5 kernels)")
     del ffn, attn
 
     # Q4_0 LM head 151936 x (896 -> 1024), fp32 and Q8_1 activation

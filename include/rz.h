@@ -161,6 +161,31 @@ int rz_q4k_q8_gemv_multi(int n_mats, const void* const* w_q4k, float* const* y,
                          const int* out_dims, const void* x_q8, int in_dim, int n_tokens,
                          void* stream);
 
+/* rz_rmsnorm_q4k_q8_gemv_multi -- RMSNorm, Q8_1 quantize and several Q4_K
+ * GEMVs in one launch (one token).
+ * Passages: realizar 0.8.5 src/cuda/executor/cached.rs,
+ * transformer_layer_gpu_true_dp4a, steps 1-3 (RMSNorm of the hidden state,
+ * one Q8_1 quantize, the Q, K and V projections); realizar 0.8.4
+ * src/gpu/adapters/using.rs, rms_norm_inplace.
+ * Bit for bit the result of rz_rmsnorm_q8_1(x, gamma, eps, n, in_dim, 1, NULL,
+ * x_q8) followed by rz_q4k_q8_gemv_multi(n_mats, w_q4k, y, out_dims, x_q8,
+ * in_dim, 1): every workgroup normalizes and quantizes the row into its LDS,
+ * summing the squares in the same order as rz_rmsnorm_q8_1.
+ *   n_mats, w_q4k, y, out_dims: as for rz_q4k_q8_gemv_multi (one token)
+ *   x        fp32 [n], the hidden state, 4-byte aligned; values n..in_dim-1
+ *            are taken as 0
+ *   gamma    fp32 [n] RMSNorm weights, 4-byte aligned
+ *   eps      > 0 and finite
+ *   n        1 <= n <= in_dim
+ *   x_q8     optional out (NULL to skip): the [in_dim/32] Q8_1 blocks of the
+ *            normed row, 16-byte aligned
+ *   in_dim   multiple of 256, <= 16384
+ * Errors: RZ_EINVAL (null pointer or array entry, n_mats, eps, overlaps),
+ * RZ_EDIM, RZ_EALIGN, RZ_ELAUNCH. */
+int rz_rmsnorm_q4k_q8_gemv_multi(int n_mats, const void* const* w_q4k, float* const* y,
+                                 const int* out_dims, const float* x, const float* gamma,
+                                 float eps, int n, void* x_q8, int in_dim, void* stream);
+
 /* rz_q4k_q8_gemv_f32 -- Q8_1 quantize and Q4_K x Q8_1 GEMV in one launch.
  * Passage: realizar 0.8.5 src/cuda/executor/cached.rs,
  * transformer_layer_gpu_true_dp4a, steps 2-3 (quantize the normed
@@ -310,6 +335,33 @@ int rz_gelu_ffn_q4_0(const void* w_up, const void* w_down, const float* x, const
 int rz_swiglu_ffn_q4k(const void* w_gate, const void* w_up, const void* w_down,
                       const void* x_q8, float* h, void* h_q8, float* y,
                       float* gu, int hidden_dim, int inter_dim, void* stream);
+
+/* rz_rmsnorm_swiglu_ffn_q4k_add -- the pre-norm FFN block of one token:
+ * y = x + W_down Q8_1(silu(g) * u), with g, u = W_gate, W_up times
+ * Q8_1(RMSNorm(x, gamma, eps)).
+ * Passages: realizar 0.8.5 src/cuda/executor/cached.rs,
+ * transformer_layer_gpu_true_dp4a, steps 8-10 (RMSNorm of the hidden state,
+ * the FFN on its Q8_1 form, the residual add); realizar 0.8.4
+ * src/gpu/adapters/using.rs, rms_norm_inplace and ffn_swiglu_gpu.
+ * Bit for bit the result of rz_rmsnorm_q8_1(x, gamma, eps, hidden_dim,
+ * hidden_dim, 1, NULL, x_q8) followed by rz_swiglu_ffn_q4k_add(w_gate, w_up,
+ * w_down, x_q8, h, h_q8, x, y, gu, hidden_dim, inter_dim): every gate/up
+ * workgroup normalizes and quantizes x into its LDS, summing the squares in
+ * the same order as rz_rmsnorm_q8_1.  Two kernels run in order on `stream`.
+ *   w_gate, w_up, w_down, h, h_q8, gu, hidden_dim, inter_dim: as for
+ *                 rz_swiglu_ffn_q4k (hidden_dim <= 16384)
+ *   x             fp32 [hidden_dim], the hidden state (also the residual),
+ *                 4-byte aligned
+ *   gamma         fp32 [hidden_dim] RMSNorm weights, 4-byte aligned
+ *   eps           > 0 and finite
+ *   y             out: fp32 [hidden_dim], 4-byte aligned; may be x itself
+ * h, h_q8, gu and y must not overlap x, gamma, the weights or each other
+ * (y may be x).  Errors: RZ_EINVAL (also overlaps), RZ_EDIM, RZ_EALIGN,
+ * RZ_ELAUNCH. */
+int rz_rmsnorm_swiglu_ffn_q4k_add(const void* w_gate, const void* w_up, const void* w_down,
+                                  const float* x, const float* gamma, float eps, float* h,
+                                  void* h_q8, float* y, float* gu, int hidden_dim, int inter_dim,
+                                  void* stream);
 
 /* rz_swiglu_ffn_q4k_add -- the SwiGLU FFN with the residual add:
  * y = W_down h_q8 + r.

@@ -20,8 +20,10 @@ __all__ = [
     "Q8_1_BLOCK_BYTES", "Q4K_BLOCK_BYTES", "Q4_0_BLOCK_BYTES", "MAX_TOKENS",
     "library_path", "load_library", "rz_last_error", "rz_abi_version",
     "rz_q8_1_quantize", "rz_rmsnorm_q8_1", "rz_q4k_q8_gemv", "rz_q4k_q8_gemv_add",
-    "rz_q4k_q8_gemv_multi", "rz_q4k_q8_gemv_f32", "rz_q4_0_gemv", "rz_swiglu_ffn_q4k",
-    "rz_swiglu_ffn_q4k_add", "rz_q4k_gemv", "rz_swiglu_ffn_q4k_f32",
+    "rz_q4k_q8_gemv_multi", "rz_rmsnorm_q4k_q8_gemv_multi", "rz_rmsnorm_swiglu_ffn_q4k_add",
+    "rz_q4k_q8_gemv_f32",
+    "rz_q4_0_gemv", "rz_swiglu_ffn_q4k", "rz_swiglu_ffn_q4k_add", "rz_q4k_gemv",
+    "rz_swiglu_ffn_q4k_f32",
     "rz_lm_head_q4_0", "rz_lm_head_q4_0_workspace_bytes", "rz_gelu_ffn_q4_0",
     "q8_1_nbytes", "RzError",
 ]
@@ -63,6 +65,8 @@ def load_library() -> ctypes.CDLL:
     lib.rz_q4k_q8_gemv_add.argtypes = [vp, vp, vp, vp, i, i, i, vp]
     lib.rz_q4k_q8_gemv_f32.argtypes = [vp, vp, i, vp, vp, i, i, vp]
     lib.rz_q4k_q8_gemv_multi.argtypes = [i, vp, vp, vp, vp, i, i, vp]
+    lib.rz_rmsnorm_q4k_q8_gemv_multi.argtypes = [i, vp, vp, vp, vp, vp, ctypes.c_float, i, vp, i, vp]
+    lib.rz_rmsnorm_swiglu_ffn_q4k_add.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, i, i, vp]
     lib.rz_q4_0_gemv.argtypes = [vp, vp, i, vp, i, i, vp]
     lib.rz_swiglu_ffn_q4k.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, vp]
     lib.rz_swiglu_ffn_q4k_add.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, vp]
@@ -73,7 +77,9 @@ def load_library() -> ctypes.CDLL:
     lib.rz_lm_head_q4_0_workspace_bytes.argtypes = [i, i, i]
     lib.rz_lm_head_q4_0_workspace_bytes.restype = ctypes.c_size_t
     for fn in ("rz_q8_1_quantize", "rz_rmsnorm_q8_1", "rz_q4k_q8_gemv", "rz_q4k_q8_gemv_add",
-               "rz_q4k_q8_gemv_f32", "rz_q4k_q8_gemv_multi", "rz_q4_0_gemv", "rz_swiglu_ffn_q4k",
+               "rz_q4k_q8_gemv_f32", "rz_q4k_q8_gemv_multi", "rz_rmsnorm_q4k_q8_gemv_multi",
+               "rz_rmsnorm_swiglu_ffn_q4k_add",
+               "rz_q4_0_gemv", "rz_swiglu_ffn_q4k",
                "rz_swiglu_ffn_q4k_add", "rz_q4k_gemv", "rz_swiglu_ffn_q4k_f32",
                "rz_lm_head_q4_0", "rz_gelu_ffn_q4_0", "rz_abi_version"):
         getattr(lib, fn).restype = i
@@ -193,6 +199,46 @@ def rz_q4k_q8_gemv_multi(ws, x_q8, ys, out_dims, in_dim: int, n_tokens: int = 1,
     da = (ctypes.c_int * max(n, 1))(*[int(d) for d in out_dims])
     _check(load_library().rz_q4k_q8_gemv_multi(n, wa, ya, da, _ptr(x_q8), in_dim, n_tokens,
                                                _stream(stream)))
+
+
+def rz_rmsnorm_q4k_q8_gemv_multi(ws, x, gamma, eps: float, n: int, x_q8, ys, out_dims,
+                                 in_dim: int, stream=None) -> None:
+    """ys[m] fp32 [out_dims[m]] = ws[m] (Q4_K) x Q8_1(RMSNorm(x[:n], gamma, eps)) for
+    every m, in one launch; x_q8 (or None) receives the Q8_1 blocks."""
+    nm = len(ws)
+    if len(ys) != nm or len(out_dims) != nm:
+        raise ValueError("ws, ys and out_dims must have the same length")
+    _need(x, 4 * n, "x")
+    _need(gamma, 4 * n, "gamma")
+    if in_dim > 0 and in_dim % 256 == 0:
+        _need(x_q8, q8_1_nbytes(in_dim), "x_q8")
+        for w, y, od in zip(ws, ys, out_dims):
+            if od > 0:
+                _need(w, od * (in_dim // 256) * Q4K_BLOCK_BYTES, "w_q4k")
+                _need(y, 4 * od, "y")
+    wa = (ctypes.c_void_p * max(nm, 1))(*[_ptr(w) for w in ws])
+    ya = (ctypes.c_void_p * max(nm, 1))(*[_ptr(y) for y in ys])
+    da = (ctypes.c_int * max(nm, 1))(*[int(d) for d in out_dims])
+    _check(load_library().rz_rmsnorm_q4k_q8_gemv_multi(nm, wa, ya, da, _ptr(x), _ptr(gamma),
+                                                       eps, n, _ptr(x_q8), in_dim,
+                                                       _stream(stream)))
+
+
+def rz_rmsnorm_swiglu_ffn_q4k_add(w_gate, w_up, w_down, x, gamma, eps: float, h, h_q8, y, gu,
+                                  hidden_dim: int, inter_dim: int, stream=None) -> None:
+    """The pre-norm FFN block: y = x + SwiGLU chain of Q8_1(RMSNorm(x, gamma, eps));
+    y may be x.  h, h_q8 (and gu unless None) receive the chain's stages."""
+    if hidden_dim > 0 and inter_dim > 0 and hidden_dim % 256 == 0 and inter_dim % 256 == 0:
+        nw = inter_dim * (hidden_dim // 256) * Q4K_BLOCK_BYTES
+        for t_, nm in ((w_gate, "w_gate"), (w_up, "w_up"), (w_down, "w_down")):
+            _need(t_, nw, nm)
+        for t_, nb, nm in ((x, 4 * hidden_dim, "x"), (gamma, 4 * hidden_dim, "gamma"),
+                           (h, 4 * inter_dim, "h"), (h_q8, q8_1_nbytes(inter_dim), "h_q8"),
+                           (y, 4 * hidden_dim, "y"), (gu, 8 * inter_dim, "gu")):
+            _need(t_, nb, nm)
+    _check(load_library().rz_rmsnorm_swiglu_ffn_q4k_add(
+        _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(x), _ptr(gamma), eps, _ptr(h), _ptr(h_q8),
+        _ptr(y), _ptr(gu), hidden_dim, inter_dim, _stream(stream)))
 
 
 def rz_q4k_q8_gemv_f32(w_q4k, x, n: int, x_q8, y, out_dim: int, in_dim: int,

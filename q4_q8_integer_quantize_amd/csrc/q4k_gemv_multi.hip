@@ -12,6 +12,7 @@
 // equals a separate rz_q4k_q8_gemv call bit for bit.
 #include "q4k_gemv.h"
 #include "rz_launch.h"
+#include "xrow_quant.h"
 
 namespace rz {
 
@@ -24,10 +25,20 @@ struct Q4KMultiArgs {
   float* y[kMaxMats];
   int out_dim[kMaxMats];
   uint32_t group0[kMaxMats + 1];    // first row group of each matrix; [n_mats] = total
+  // NORM: the activation is the fp32 row xf[n] with weights gamma[n], RMSNorm'ed
+  // and quantized by every workgroup (xq then unused; WG 0 writes the blocks
+  // to xq_out when it is not null)
+  const float* xf;
+  const float* gamma;
+  float eps;
+  int n;
+  uint8_t* xq_out;
 };
 
-template <int TPR, int S, int R, int NT, int G, int P, bool XL = false>
+template <int TPR, int S, int R, int NT, int G, int P, bool XL = false, bool NORM = false,
+          bool XV = true>
 __global__ __launch_bounds__(256) void q4k_q8_gemv_multi_kernel(Q4KMultiArgs a) {
+  static_assert(!NORM || (NT == 1 && !XL), "the RMSNorm prologue serves one token");
   constexpr int RW = 8 / TPR;
   constexpr uint32_t kRowsPerGroup = (uint32_t)RW * R;
   const uint32_t nwaves = gridDim.x * 4u;
@@ -82,11 +93,16 @@ __global__ __launch_bounds__(256) void q4k_q8_gemv_multi_kernel(Q4KMultiArgs a) 
   };
   const LaneOffsets<TPR, S> off = lane_offsets<TPR, S>(src_of(0), 0, ro);
 
-  // activation first (XL: staged in LDS once per workgroup, as in the GEMV)
+  // activation first (XL: staged in LDS once per workgroup, as in the GEMV;
+  // NORM: the fp32 row, RMSNorm'ed and quantized into LDS by the workgroup)
   XSlots<S, NT> xs;
   XStage<TPR, S, NT, 4> xst;
   extern __shared__ __attribute__((aligned(16))) uint8_t xl_lds[];
-  if constexpr (XL)
+  constexpr int kRowPasses = (S * TPR * 8 + kXrowBlocksPerPass - 1) / kXrowBlocksPerPass;
+  XRow<NORM ? kRowPasses : 1, true> xrow;
+  if constexpr (NORM)
+    xrow_request<kRowPasses, XV, true>(xrow, a.xf, a.gamma, a.n, a.nsb * 8);
+  else if constexpr (XL)
     x_stage_request(xst, a.xq, (uint32_t)a.nsb * 8u * kQ8Bytes, 0, a.nsb, a.n_tokens);
   else
     load_x_slots<TPR, S, NT>(xs, a.xq, (size_t)a.nsb * 8 * kQ8Bytes, a.nsb, a.n_tokens, ro);
@@ -94,7 +110,18 @@ __global__ __launch_bounds__(256) void q4k_q8_gemv_multi_kernel(Q4KMultiArgs a) 
 #pragma unroll
   for (int k = 0; k < P && k < G; ++k) load_w_tile<TPR, S, R>(t[k], src_of(k), off, rb[k]);
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (XL) x_stage_commit(xst, xl_lds, xs, a.nsb, a.n_tokens, ro);
+  if constexpr (NORM) {
+    __shared__ float part[kXrowThreads / kWave];
+    xrow_quantize<kRowPasses, true>(xrow, a.eps, a.n, a.nsb * 8, xl_lds,
+                                    blockIdx.x == 0 ? a.xq_out : nullptr, part);
+    // LDS-only release/acquire: the weight loads stay in flight
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    load_x_slots_from_lds<TPR, S, NT>(xs, xl_lds, 0u, a.nsb, 1, ro);
+  } else if constexpr (XL) {
+    x_stage_commit(xst, xl_lds, xs, a.nsb, a.n_tokens, ro);
+  }
 #pragma unroll
   for (int k = 0; k < G; ++k) {
     if (k + P < G) load_w_tile<TPR, S, R>(t[k + P], src_of(k + P), off, rb[k + P]);
@@ -113,6 +140,44 @@ __global__ __launch_bounds__(256) void q4k_q8_gemv_multi_kernel(Q4KMultiArgs a) 
     ga.n_tokens = a.n_tokens;
     store_rows<TPR, R, NT, false>(ga, acc, (long)rb[k], ro);
   }
+}
+
+// NORM: groups per wave as the fused quantize + GEMV step (about 1024 waves;
+// every workgroup redoes the RMSNorm and the quantize, so fewer, deeper waves
+// pay for it once per CU): the Q, K, V set (3072 groups) at 4 groups a wave
+// 7.6 us, at 1 or 2 7.8-8.0 us, against 8.7 us of kernel time for
+// rz_rmsnorm_q8_1 then the multi-matrix launch, bit-identical outputs.
+template <int TPR, int S, int G, bool XV>
+static hipError_t launch_multi_norm_g(const Q4KMultiArgs& a, hipStream_t st) {
+  constexpr int R = S <= 2 ? 2 : 1;
+  constexpr int P = G > 2 ? 2 : (G > 1 ? G - 1 : 1);
+  const size_t lds = (size_t)a.nsb * 8 * kQ8Bytes;
+  const long waves = ((long)a.group0[a.n_mats] + G - 1) / G;
+  const unsigned grid = (unsigned)((waves + 3) / 4);
+  hipLaunchKernelGGL((q4k_q8_gemv_multi_kernel<TPR, S, R, 1, G, P, false, true, XV>), dim3(grid),
+                     dim3(256), lds, st, a);
+  return hipGetLastError();
+}
+
+template <int TPR, int S, bool XV>
+static hipError_t run_multi_norm(Q4KMultiArgs a, hipStream_t st) {
+  constexpr int R = S <= 2 ? 2 : 1;
+  constexpr uint32_t rows_per_group = (uint32_t)(8 / TPR) * R;
+  a.group0[0] = 0;
+  for (int j = 0; j < kMaxMats; ++j)
+    a.group0[j + 1] = a.group0[j] + (j < a.n_mats ? ((uint32_t)a.out_dim[j] + rows_per_group - 1) /
+                                                       rows_per_group
+                                                 : 0u);
+  const long per_wave = ((long)a.group0[a.n_mats] + 1023) / 1024;
+  if (per_wave <= 1) return launch_multi_norm_g<TPR, S, 1, XV>(a, st);
+  if (per_wave <= 2) return launch_multi_norm_g<TPR, S, 2, XV>(a, st);
+  if (per_wave <= 4) return launch_multi_norm_g<TPR, S, 4, XV>(a, st);
+  return launch_multi_norm_g<TPR, S, 8, XV>(a, st);
+}
+
+template <int TPR, int S>
+static hipError_t run_multi_norm_x(const Q4KMultiArgs& a, hipStream_t st) {
+  return (a.n & 3) == 0 ? run_multi_norm<TPR, S, true>(a, st) : run_multi_norm<TPR, S, false>(a, st);
 }
 
 template <int TPR, int S, int NT, int G>
@@ -202,6 +267,42 @@ hipError_t launch_q4k_q8_gemv_multi(int n_mats, const uint8_t* const* w, float* 
     a.out_dim[j] = j < n_mats ? out_dims[j] : out_dims[0];
   }
   return n_tokens == 1 ? run_multi_nt<1>(a, stream) : run_multi_nt<2>(a, stream);
+}
+
+hipError_t launch_rmsnorm_q4k_q8_gemv_multi(int n_mats, const uint8_t* const* w, float* const* y,
+                                            const int* out_dims, const float* x,
+                                            const float* gamma, float eps, int n,
+                                            uint8_t* xq_out, int in_dim, hipStream_t stream) {
+  Q4KMultiArgs a;
+  a.xq = nullptr;
+  a.nsb = in_dim / kQKK;
+  a.n_tokens = 1;
+  a.n_mats = n_mats;
+  for (int j = 0; j < kMaxMats; ++j) {
+    a.w[j] = j < n_mats ? w[j] : w[0];
+    a.y[j] = j < n_mats ? y[j] : y[0];
+    a.out_dim[j] = j < n_mats ? out_dims[j] : 0;
+  }
+  a.xf = x;
+  a.gamma = gamma;
+  a.eps = eps;
+  a.n = n;
+  a.xq_out = xq_out;
+  const int nsb = a.nsb;
+  if (nsb == 1) return run_multi_norm_x<1, 1>(a, stream);
+  if (nsb == 2) return run_multi_norm_x<2, 1>(a, stream);
+  if (nsb <= 4) return run_multi_norm_x<4, 1>(a, stream);
+  switch ((nsb + 7) / 8) {
+    case 1: return run_multi_norm_x<8, 1>(a, stream);
+    case 2: return run_multi_norm_x<8, 2>(a, stream);
+    case 3: return run_multi_norm_x<8, 3>(a, stream);
+    case 4: return run_multi_norm_x<8, 4>(a, stream);
+    case 5: return run_multi_norm_x<8, 5>(a, stream);
+    case 6: return run_multi_norm_x<8, 6>(a, stream);
+    case 7: return run_multi_norm_x<8, 7>(a, stream);
+    case 8: return run_multi_norm_x<8, 8>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace rz

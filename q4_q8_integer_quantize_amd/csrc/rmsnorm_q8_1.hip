@@ -24,8 +24,8 @@
 // + 10 for longer ones, the same on every run.  The normed values are
 // quantized with the rule of rz_q8_1_quantize, so the Q8_1 blocks equal
 // rz_q8_1_quantize of the normed values bit for bit.
-#include "rz_device.h"
 #include "rz_launch.h"
+#include "xrow_quant.h"
 
 namespace rz {
 
@@ -44,24 +44,6 @@ struct NormArgs {
   float* normed;     // optional
   uint8_t* out;
 };
-
-// Sum of one value per thread over a workgroup of T threads, in a fixed order.
-template <int T>
-__device__ __forceinline__ float workgroup_sum(float v, float* part) {
-  constexpr int NW = T / kWave;
-  v = group_sum_dpp<64>(v);                          // wave sum in lane 63
-  const uint32_t tid = threadIdx.x;
-  if ((tid & 63u) == 63u) part[tid >> 6] = v;
-  __syncthreads();
-  float w[NW];
-#pragma unroll
-  for (int k = 0; k < NW; ++k) w[k] = part[k];
-#pragma unroll
-  for (int step = 1; step < NW; step *= 2)
-#pragma unroll
-    for (int k = 0; k + step < NW; k += 2 * step) w[k] += w[k + step];
-  return w[0];
-}
 
 // Normalize four values (x[i0 .. i0+3] of token t, in xv, with weights gv)
 // and quantize their block b; the thread's 8-lane group holds the block.

@@ -215,6 +215,59 @@ int rz_q4k_q8_gemv_multi(int n_mats, const void* const* w_q4k, float* const* y,
                        what);
 }
 
+int rz_rmsnorm_q4k_q8_gemv_multi(int n_mats, const void* const* w_q4k, float* const* y,
+                                 const int* out_dims, const float* x, const float* gamma,
+                                 float eps, int n, void* x_q8, int in_dim, void* stream) {
+  const char* what = "rz_rmsnorm_q4k_q8_gemv_multi";
+  if (!w_q4k || !y || !out_dims || !x || !gamma) return fail(RZ_EINVAL, "%s: null pointer", what);
+  if (n_mats < 1 || n_mats > RZ_MAX_MATS)
+    return fail(RZ_EINVAL, "%s: n_mats=%d outside 1..%d", what, n_mats, RZ_MAX_MATS);
+  if (!(eps > 0.0f) || !(eps <= 3.0e38f))
+    return fail(RZ_EINVAL, "%s: eps=%g must be positive and finite", what, (double)eps);
+  if (int rc = check_dim(what, "in_dim", in_dim, 256)) return rc;
+  if (in_dim > 16384)
+    return fail(RZ_EDIM, "%s: in_dim=%d above the fused limit 16384", what, in_dim);
+  if (n <= 0 || n > in_dim)
+    return fail(RZ_EDIM, "%s: n=%d must satisfy 1 <= n <= in_dim=%d", what, n, in_dim);
+  if (!aligned(x, 4) || !aligned(gamma, 4))
+    return fail(RZ_EALIGN, "%s: x and gamma must be 4-byte aligned", what);
+  if (x_q8 && !aligned(x_q8, 16)) return fail(RZ_EALIGN, "%s: x_q8 must be 16-byte aligned", what);
+  const uint8_t* w[RZ_MAX_MATS];
+  float* yy[RZ_MAX_MATS];
+  int od[RZ_MAX_MATS];
+  for (int m = 0; m < n_mats; ++m) {
+    if (!w_q4k[m] || !y[m]) return fail(RZ_EINVAL, "%s: null pointer in matrix %d", what, m);
+    if (int rc = check_dim(what, "out_dims[m]", out_dims[m], 1)) return rc;
+    if (q4k_bytes(out_dims[m], in_dim) > kMaxMatrixBytes)
+      return fail(RZ_EDIM, "%s: matrix %d larger than %lld bytes", what, m, kMaxMatrixBytes);
+    if (!aligned(w_q4k[m], 16))
+      return fail(RZ_EALIGN, "%s: w_q4k[%d] must be 16-byte aligned", what, m);
+    if (!aligned(y[m], 4)) return fail(RZ_EALIGN, "%s: y[%d] must be 4-byte aligned", what, m);
+    w[m] = static_cast<const uint8_t*>(w_q4k[m]);
+    yy[m] = y[m];
+    od[m] = out_dims[m];
+  }
+  const Span xs{x, 4LL * n}, gs{gamma, 4LL * n}, qs{x_q8, q8_bytes(1, in_dim)};
+  for (int m = 0; m < n_mats; ++m) {
+    const Span ym{yy[m], 4LL * od[m]};
+    if (!clear_of(ym, {xs, gs, qs}))
+      return fail(RZ_EINVAL, "%s: y[%d] must not overlap x, gamma or x_q8", what, m);
+    for (int k = 0; k < n_mats; ++k)
+      if (!clear_of(ym, {{w[k], q4k_bytes(od[k], in_dim)}}) ||
+          (k != m && !clear_of(ym, {{yy[k], 4LL * od[k]}})))
+        return fail(RZ_EINVAL, "%s: y[%d] overlaps a weight blob or another output", what, m);
+  }
+  if (!clear_of(qs, {xs, gs}))
+    return fail(RZ_EINVAL, "%s: x_q8 must not overlap x or gamma", what);
+  for (int k = 0; k < n_mats; ++k)
+    if (!clear_of(qs, {{w[k], q4k_bytes(od[k], in_dim)}}))
+      return fail(RZ_EINVAL, "%s: x_q8 must not overlap a weight blob", what);
+  return launch_status(rz::launch_rmsnorm_q4k_q8_gemv_multi(n_mats, w, yy, od, x, gamma, eps, n,
+                                                             static_cast<uint8_t*>(x_q8), in_dim,
+                                                             static_cast<hipStream_t>(stream)),
+                       what);
+}
+
 int rz_q4k_q8_gemv_f32(const void* w_q4k, const float* x, int n, void* x_q8, float* y,
                        int out_dim, int in_dim, void* stream) {
   const char* what = "rz_q4k_q8_gemv_f32";
@@ -457,6 +510,49 @@ int rz_gelu_ffn_q4_0(const void* w_up, const void* w_down, const float* x, const
                                                 down_bias, h, y, hidden_dim, inter_dim,
                                                 static_cast<hipStream_t>(stream)),
                        what);
+}
+
+int rz_rmsnorm_swiglu_ffn_q4k_add(const void* w_gate, const void* w_up, const void* w_down,
+                                  const float* x, const float* gamma, float eps, float* h,
+                                  void* h_q8, float* y, float* gu, int hidden_dim, int inter_dim,
+                                  void* stream) {
+  const char* what = "rz_rmsnorm_swiglu_ffn_q4k_add";
+  if (!w_gate || !w_up || !w_down || !x || !gamma || !h || !h_q8 || !y)
+    return fail(RZ_EINVAL, "%s: null pointer", what);
+  if (!(eps > 0.0f) || !(eps <= 3.0e38f))
+    return fail(RZ_EINVAL, "%s: eps=%g must be positive and finite", what, (double)eps);
+  if (int rc = check_dim(what, "hidden_dim", hidden_dim, 256)) return rc;
+  if (int rc = check_dim(what, "inter_dim", inter_dim, 256)) return rc;
+  if (hidden_dim > 16384)
+    return fail(RZ_EDIM, "%s: hidden_dim=%d above the fused gate/up limit 16384", what,
+                hidden_dim);
+  const long long wb = q4k_bytes(inter_dim, hidden_dim), db = q4k_bytes(hidden_dim, inter_dim);
+  if (wb > kMaxMatrixBytes)
+    return fail(RZ_EDIM, "%s: weight matrix larger than %lld bytes", what, kMaxMatrixBytes);
+  if (!aligned(w_gate, 16) || !aligned(w_up, 16) || !aligned(w_down, 16))
+    return fail(RZ_EALIGN, "%s: weight blobs must be 16-byte aligned", what);
+  if (!aligned(h_q8, 16)) return fail(RZ_EALIGN, "%s: h_q8 must be 16-byte aligned", what);
+  if (!aligned(x, 4) || !aligned(gamma, 4) || !aligned(h, 4) || !aligned(y, 4) ||
+      (gu && !aligned(gu, 4)))
+    return fail(RZ_EALIGN, "%s: fp32 buffers must be 4-byte aligned", what);
+  // the first kernel reads x, gamma and the gate/up weights while it writes h,
+  // h_q8 and gu; the second reads h_q8, x (the residual) and the down weights
+  // while it writes y, which may be x itself
+  const Span xs{x, 4LL * hidden_dim}, gs{gamma, 4LL * hidden_dim}, hs{h, 4LL * inter_dim},
+      hq{h_q8, q8_bytes(1, inter_dim)}, us{gu, 8LL * inter_dim}, ys{y, 4LL * hidden_dim},
+      wg{w_gate, wb}, wu{w_up, wb}, wd{w_down, db};
+  if (!clear_of(hs, {xs, gs, hq, us, wg, wu, wd}) || !clear_of(hq, {xs, gs, us, ys, wg, wu, wd}) ||
+      !clear_of(us, {xs, gs, wg, wu, wd}) || !clear_of(ys, {gs, wg, wu, wd}) ||
+      !same_or_disjoint(y, x, hidden_dim))
+    return fail(RZ_EINVAL, "%s: h, h_q8, gu and y must not overlap x, gamma, the weights or each "
+                "other (y may be x itself)", what);
+  return launch_status(
+      rz::launch_rmsnorm_swiglu_ffn_q4k(static_cast<const uint8_t*>(w_gate),
+                                        static_cast<const uint8_t*>(w_up),
+                                        static_cast<const uint8_t*>(w_down), x, gamma, eps, h,
+                                        static_cast<uint8_t*>(h_q8), y, gu, hidden_dim, inter_dim,
+                                        static_cast<hipStream_t>(stream)),
+      what);
 }
 
 int rz_swiglu_ffn_q4k(const void* w_gate, const void* w_up, const void* w_down,

@@ -37,6 +37,15 @@ hipError_t launch_q4k_q8_gemv_multi(int n_mats, const uint8_t* const* w, float* 
                                     const int* out_dims, const uint8_t* xq, int in_dim,
                                     int n_tokens, hipStream_t stream);
 
+// The same for one fp32 token row x[n] (zero-padded to in_dim <= kMultiMaxInDim):
+// every workgroup RMSNorms it with gamma[n] and quantizes it into LDS
+// (bit-identical to launch_rmsnorm_q8_1 followed by launch_q4k_q8_gemv_multi);
+// workgroup 0 writes the Q8_1 blocks to xq_out when it is not null.
+hipError_t launch_rmsnorm_q4k_q8_gemv_multi(int n_mats, const uint8_t* const* w, float* const* y,
+                                            const int* out_dims, const float* x,
+                                            const float* gamma, float eps, int n,
+                                            uint8_t* xq_out, int in_dim, hipStream_t stream);
+
 // Q8_1 quantize of an fp32 activation fused into the Q4_K GEMV (1 token).
 hipError_t launch_q4k_q8_gemv_f32(const uint8_t* w, const float* x, int n, uint8_t* xq_out,
                                   float* y, int out_dim, int in_dim, hipStream_t stream);
@@ -72,5 +81,15 @@ hipError_t launch_swiglu_ffn_q4k(const uint8_t* w_gate, const uint8_t* w_up,
                                  const uint8_t* w_down, const uint8_t* xq, float* h,
                                  uint8_t* h_q8, float* y, float* gu, int hidden_dim,
                                  int inter_dim, hipStream_t stream, const float* r = nullptr);
+
+// The pre-norm FFN block on one token: y = x + SwiGLU chain of
+// Q8_1(RMSNorm(x, gamma, eps)), the RMSNorm and quantize in every gate/up
+// workgroup (bit-identical to launch_rmsnorm_q8_1 followed by
+// launch_swiglu_ffn_q4k with r = x); y may be x.
+hipError_t launch_rmsnorm_swiglu_ffn_q4k(const uint8_t* w_gate, const uint8_t* w_up,
+                                         const uint8_t* w_down, const float* x,
+                                         const float* gamma, float eps, float* h,
+                                         uint8_t* h_q8, float* y, float* gu, int hidden_dim,
+                                         int inter_dim, hipStream_t stream);
 
 }  // namespace rz

@@ -14,6 +14,7 @@
 // GEMV of the down projection over h_q8.
 #include "q4k_gemv.h"
 #include "rz_launch.h"
+#include "xrow_quant.h"
 
 namespace rz {
 
@@ -26,6 +27,11 @@ struct SwiArgs {
   float* gu;      // optional [2][inter]
   int inter;
   int nsb;        // hidden / 256
+  // NORM: x is the fp32 hidden state xf[hidden] with RMSNorm weights gamma,
+  // normed and quantized by every workgroup (xq unused)
+  const float* xf;
+  const float* gamma;
+  float eps;
 };
 
 // Wave w of WPB owns rows RPW*w .. RPW*w + RPW-1 of the block (RPW = 32 /
@@ -34,8 +40,9 @@ struct SwiArgs {
 // ahead, as in q4k_q8_gemv_kernel: no load sits under a branch, so each wait
 // is for exactly the tile about to be reduced.  XL: the workgroup copies x
 // into LDS once and the lanes read their slots from there.
-template <int TPR, int S, int R, int P, int WPB = 4, bool XL = false>
+template <int TPR, int S, int R, int P, int WPB = 4, bool XL = false, bool NORM = false>
 __global__ __launch_bounds__(64 * WPB) void swiglu_gate_up_kernel(SwiArgs a) {
+  static_assert(!NORM || (WPB == 4 && !XL), "the RMSNorm prologue runs on 256 threads");
   constexpr int RW = 8 / TPR;
   constexpr int kGroupRows = RW * R;                 // rows of one matrix per group
   constexpr int RPW = 32 / WPB;                      // rows of the block a wave owns
@@ -55,8 +62,14 @@ __global__ __launch_bounds__(64 * WPB) void swiglu_gate_up_kernel(SwiArgs a) {
   // activation first: vector loads retire in order
   XSlots<S, 1> xs;
   XStage<TPR, S, 1, WPB> xst;
-  __shared__ __attribute__((aligned(16))) uint8_t x_lds[XL ? XStage<TPR, S, 1, WPB>::kLdsBytes : 16];
-  if constexpr (XL)
+  __shared__ __attribute__((aligned(16)))
+  uint8_t x_lds[(XL || NORM) ? XStage<TPR, S, 1, WPB>::kLdsBytes : 16];
+  constexpr int kRowPasses = (S * TPR * 8 + kXrowBlocksPerPass - 1) / kXrowBlocksPerPass;
+  XRow<NORM ? kRowPasses : 1, true> xrow;
+  const int hidden = a.nsb * kQKK;
+  if constexpr (NORM)
+    xrow_request<kRowPasses, true, true>(xrow, a.xf, a.gamma, hidden, a.nsb * 8);
+  else if constexpr (XL)
     x_stage_request(xst, a.xq, (uint32_t)a.nsb * 8u * kQ8Bytes, 0, a.nsb, 1);
   else
     load_x_slots<TPR, S, 1>(xs, a.xq, 0, a.nsb, 1, ro);
@@ -65,7 +78,17 @@ __global__ __launch_bounds__(64 * WPB) void swiglu_gate_up_kernel(SwiArgs a) {
   for (int k = 0; k < P && k < G; ++k)
     load_w_tile<TPR, S, R>(t[k], (k & 1) ? su : sg, off, row0 + (uint32_t)(k >> 1) * kGroupRows);
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (XL) x_stage_commit(xst, x_lds, xs, a.nsb, 1, ro);
+  if constexpr (NORM) {
+    __shared__ float part[kXrowThreads / kWave];
+    xrow_quantize<kRowPasses, true>(xrow, a.eps, hidden, a.nsb * 8, x_lds, nullptr, part);
+    // LDS-only release/acquire: the weight loads stay in flight
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    load_x_slots_from_lds<TPR, S, 1>(xs, x_lds, 0u, a.nsb, 1, ro);
+  } else if constexpr (XL) {
+    x_stage_commit(xst, x_lds, xs, a.nsb, 1, ro);
+  }
 #pragma unroll
   for (int k = 0; k < G; ++k) {
     if (k + P < G)
@@ -108,7 +131,7 @@ __global__ __launch_bounds__(64 * WPB) void swiglu_gate_up_kernel(SwiArgs a) {
   }
 }
 
-template <int TPR, int S>
+template <int TPR, int S, bool NORM>
 static hipError_t run_gate_up(const SwiArgs& a, hipStream_t st) {
   constexpr int RW = 8 / TPR;
   constexpr int R_reg = S <= 2 ? 2 : 1;               // rows unrolled per group
@@ -118,10 +141,29 @@ static hipError_t run_gate_up(const SwiArgs& a, hipStream_t st) {
   // x staged in LDS for rows of two or more slots, as in the GEMV (4096 ->
   // 2 x 14336: 13.0-13.2 against 13.2-13.4 us); more waves a workgroup
   // (8 or 16, fewer rows each) measured slower (14.3-14.8 us)
-  constexpr bool XL = S >= 2;
-  hipLaunchKernelGGL((swiglu_gate_up_kernel<TPR, S, R, P, 4, XL>), dim3(a.inter / 32), dim3(256), 0,
-                     st, a);
+  constexpr bool XL = S >= 2 && !NORM;
+  hipLaunchKernelGGL((swiglu_gate_up_kernel<TPR, S, R, P, 4, XL, NORM>), dim3(a.inter / 32),
+                     dim3(256), 0, st, a);
   return hipGetLastError();
+}
+
+template <bool NORM>
+static hipError_t gate_up(const SwiArgs& a, hipStream_t stream) {
+  const int nsb = a.nsb;
+  if (nsb == 1) return run_gate_up<1, 1, NORM>(a, stream);
+  if (nsb == 2) return run_gate_up<2, 1, NORM>(a, stream);
+  if (nsb <= 4) return run_gate_up<4, 1, NORM>(a, stream);
+  switch ((nsb + 7) / 8) {
+    case 1: return run_gate_up<8, 1, NORM>(a, stream);
+    case 2: return run_gate_up<8, 2, NORM>(a, stream);
+    case 3: return run_gate_up<8, 3, NORM>(a, stream);
+    case 4: return run_gate_up<8, 4, NORM>(a, stream);
+    case 5: return run_gate_up<8, 5, NORM>(a, stream);
+    case 6: return run_gate_up<8, 6, NORM>(a, stream);
+    case 7: return run_gate_up<8, 7, NORM>(a, stream);
+    case 8: return run_gate_up<8, 8, NORM>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_swiglu_ffn_q4k(const uint8_t* w_gate, const uint8_t* w_up,
@@ -137,26 +179,38 @@ hipError_t launch_swiglu_ffn_q4k(const uint8_t* w_gate, const uint8_t* w_up,
   a.gu = gu;
   a.inter = inter_dim;
   a.nsb = hidden_dim / kQKK;
-  hipError_t e;
-  const int nsb = a.nsb;
-  if (nsb == 1) e = run_gate_up<1, 1>(a, stream);
-  else if (nsb == 2) e = run_gate_up<2, 1>(a, stream);
-  else if (nsb <= 4) e = run_gate_up<4, 1>(a, stream);
-  else {
-    switch ((nsb + 7) / 8) {
-      case 1: e = run_gate_up<8, 1>(a, stream); break;
-      case 2: e = run_gate_up<8, 2>(a, stream); break;
-      case 3: e = run_gate_up<8, 3>(a, stream); break;
-      case 4: e = run_gate_up<8, 4>(a, stream); break;
-      case 5: e = run_gate_up<8, 5>(a, stream); break;
-      case 6: e = run_gate_up<8, 6>(a, stream); break;
-      case 7: e = run_gate_up<8, 7>(a, stream); break;
-      case 8: e = run_gate_up<8, 8>(a, stream); break;
-      default: e = hipErrorInvalidValue;
-    }
-  }
+  a.xf = nullptr;
+  a.gamma = nullptr;
+  a.eps = 0.0f;
+  const hipError_t e = gate_up<false>(a, stream);
   if (e != hipSuccess) return e;
   return launch_q4k_q8_gemv(w_down, h_q8, y, hidden_dim, inter_dim, 1, stream, r);
+}
+
+// The pre-norm FFN block: y = x + W_down Q8_1(silu(g) u), g, u = W_gate, W_up
+// times Q8_1(RMSNorm(x)), with the RMSNorm and quantize in every gate/up
+// workgroup (bit-identical to launch_rmsnorm_q8_1 then launch_swiglu_ffn_q4k
+// with r = x).
+hipError_t launch_rmsnorm_swiglu_ffn_q4k(const uint8_t* w_gate, const uint8_t* w_up,
+                                         const uint8_t* w_down, const float* x,
+                                         const float* gamma, float eps, float* h,
+                                         uint8_t* h_q8, float* y, float* gu, int hidden_dim,
+                                         int inter_dim, hipStream_t stream) {
+  SwiArgs a;
+  a.wg = w_gate;
+  a.wu = w_up;
+  a.xq = nullptr;
+  a.h = h;
+  a.hq = h_q8;
+  a.gu = gu;
+  a.inter = inter_dim;
+  a.nsb = hidden_dim / kQKK;
+  a.xf = x;
+  a.gamma = gamma;
+  a.eps = eps;
+  const hipError_t e = gate_up<true>(a, stream);
+  if (e != hipSuccess) return e;
+  return launch_q4k_q8_gemv(w_down, h_q8, y, hidden_dim, inter_dim, 1, stream, x);
 }
 
 }  // namespace rz

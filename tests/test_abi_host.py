@@ -42,6 +42,7 @@ def test_header_declares_the_four_operations():
     for name in ("rz_q8_1_quantize", "rz_q4k_q8_gemv", "rz_q4k_q8_gemv_f32", "rz_q4_0_gemv",
                  "rz_swiglu_ffn_q4k", "rz_q4k_q8_gemv_multi", "rz_rmsnorm_q8_1",
                  "rz_q4k_q8_gemv_add", "rz_swiglu_ffn_q4k_add", "rz_q4k_gemv",
+                 "rz_rmsnorm_q4k_q8_gemv_multi", "rz_rmsnorm_swiglu_ffn_q4k_add",
                  "rz_swiglu_ffn_q4k_f32", "rz_lm_head_q4_0", "rz_lm_head_q4_0_workspace_bytes",
                  "rz_gelu_ffn_q4_0",
                  "rz_last_error",
@@ -474,3 +475,83 @@ def test_lm_head_outputs_must_not_overlap_inputs(lib):
     assert res[0][0] == rz.RZ_ELAUNCH
     for rc, msg in res[1:]:
         assert rc == rz.RZ_EINVAL and "overlap" in msg, msg
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0,) + _m([P], [Y], [4096])[:3] + (P + 16, H, 1e-5, 4096, None, 4096, None), rz.RZ_EINVAL),   # n_mats 0
+    ((1,) + _m([P], [Y], [4096])[:3] + (None, H, 1e-5, 4096, None, 4096, None), rz.RZ_EINVAL),     # null x
+    ((1,) + _m([P], [Y], [4096])[:3] + (H, None, 1e-5, 4096, None, 4096, None), rz.RZ_EINVAL),     # null gamma
+    ((1,) + _m([P], [Y], [4096])[:3] + (H, H + 65536, 0.0, 4096, None, 4096, None), rz.RZ_EINVAL),  # eps 0
+    ((1,) + _m([P], [Y], [4096])[:3] + (H, H + 65536, 1e-5, 4096, None, 20480, None), rz.RZ_EDIM),  # above 16384
+    ((1,) + _m([P], [Y], [4096])[:3] + (H, H + 65536, 1e-5, 4097, None, 4096, None), rz.RZ_EDIM),   # n > in_dim
+    ((1,) + _m([P], [Y], [4096])[:3] + (H, H + 65536, 1e-5, 4096, None, 4000, None), rz.RZ_EDIM),
+    ((1,) + _m([P], [Y], [4096])[:3] + (H + 2, H + 65536, 1e-5, 4096, None, 4096, None), rz.RZ_EALIGN),
+    ((1,) + _m([P], [Y], [4096])[:3] + (H, H + 65536, 1e-5, 4096, WS + 8, 4096, None), rz.RZ_EALIGN),
+    ((1,) + _m([P + 8], [Y], [4096])[:3] + (H, H + 65536, 1e-5, 4096, None, 4096, None), rz.RZ_EALIGN),
+    ((1,) + _m([P], [H], [4096])[:3] + (H, H + 65536, 1e-5, 4096, None, 4096, None), rz.RZ_EINVAL),  # y on x
+    ((1,) + _m([P], [Y], [4096])[:3] + (H, H + 65536, 1e-5, 4096, Y, 4096, None), rz.RZ_EINVAL),    # x_q8 on y
+])
+def test_rmsnorm_q4k_q8_gemv_multi_rejects(lib, args, code):
+    assert _rc("rz_rmsnorm_q4k_q8_gemv_multi", *args) == code
+    assert _rc.last.startswith("rz_rmsnorm_q4k_q8_gemv_multi")
+
+
+def test_rmsnorm_q4k_q8_gemv_multi_accepts(lib):
+    (rc, msg), = run_isolated([("rz_rmsnorm_q4k_q8_gemv_multi",
+                                [2] + list(_m([P, P + (1 << 24)], [Y, Y + 65536], [4096, 1024])) +
+                                [H, H + 65536, 1e-5, 4000, WS, 4096, None])])
+    assert rc == rz.RZ_ELAUNCH, msg
+
+
+# rz_rmsnorm_swiglu_ffn_q4k_add(w_gate, w_up, w_down, x, gamma, eps, h, h_q8, y, gu, hidden, inter, stream)
+_NSW = [_b(0), _b(1), _b(2), _b(3), _b(4), 1e-5, _b(5), _b(6), _b(7), _b(8), 4096, 14336, None]
+
+
+def _nsw(**kw):
+    names = ["wg", "wu", "wd", "x", "gamma", "eps", "h", "hq", "y", "gu", "hidden", "inter", "s"]
+    a = list(_NSW)
+    for k, v in kw.items():
+        a[names.index(k)] = v
+    return a
+
+
+@pytest.mark.parametrize("args,code", [
+    (_nsw(wg=None), rz.RZ_EINVAL),
+    (_nsw(x=None), rz.RZ_EINVAL),
+    (_nsw(gamma=None), rz.RZ_EINVAL),
+    (_nsw(h=None), rz.RZ_EINVAL),
+    (_nsw(hq=None), rz.RZ_EINVAL),
+    (_nsw(y=None), rz.RZ_EINVAL),
+    (_nsw(eps=0.0), rz.RZ_EINVAL),
+    (_nsw(eps=float("nan")), rz.RZ_EINVAL),
+    (_nsw(eps=float("inf")), rz.RZ_EINVAL),
+    (_nsw(hidden=4000), rz.RZ_EDIM),
+    (_nsw(inter=14000), rz.RZ_EDIM),
+    (_nsw(hidden=0), rz.RZ_EDIM),
+    (_nsw(hidden=32768), rz.RZ_EDIM),                  # above the fused gate/up limit
+    (_nsw(wd=_b(2) + 8), rz.RZ_EALIGN),
+    (_nsw(hq=_b(6) + 4), rz.RZ_EALIGN),                # Q8_1 staging is 16-byte
+    (_nsw(x=_b(3) + 2), rz.RZ_EALIGN),
+    (_nsw(gamma=_b(4) + 1), rz.RZ_EALIGN),
+    (_nsw(gu=_b(8) + 2), rz.RZ_EALIGN),
+    (_nsw(y=_b(3) + 4), rz.RZ_EINVAL),                 # y overlaps x without being x
+    (_nsw(y=_b(4)), rz.RZ_EINVAL),                     # y on gamma
+    (_nsw(y=_b(6) + 64), rz.RZ_EINVAL),                # y inside h_q8
+    (_nsw(h=_b(3)), rz.RZ_EINVAL),                     # h on x
+    (_nsw(h=_b(1) + 4096), rz.RZ_EINVAL),              # h inside w_up
+    (_nsw(hq=_b(4) + 16), rz.RZ_EINVAL),               # h_q8 on gamma
+    (_nsw(gu=_b(5) + 4 * 14336 - 4), rz.RZ_EINVAL),    # gu meets h
+])
+def test_rmsnorm_swiglu_ffn_add_rejects(lib, args, code):
+    assert _rc("rz_rmsnorm_swiglu_ffn_q4k_add", *args) == code
+    assert _rc.last.startswith("rz_rmsnorm_swiglu_ffn_q4k_add")
+
+
+def test_rmsnorm_swiglu_ffn_add_accepts(lib):
+    # separate buffers, y written over x in place, and no gu: all pass
+    # validation, and with no device visible the launch fails
+    res = run_isolated([("rz_rmsnorm_swiglu_ffn_q4k_add", _nsw()),
+                        ("rz_rmsnorm_swiglu_ffn_q4k_add", _nsw(y=_b(3))),
+                        ("rz_rmsnorm_swiglu_ffn_q4k_add", _nsw(gu=None)),
+                        ("rz_rmsnorm_swiglu_ffn_q4k_add", _nsw(hidden=16384, inter=256))])
+    assert [rc for rc, _ in res] == [rz.RZ_ELAUNCH] * 4, res

@@ -1328,3 +1328,74 @@ def test_graph_replays_match_eager():
         torch.cuda.synchronize()
         for k, t in enumerate(outs):
             assert np.array_equal(_bits(t), eager[k]), "replay %d: output %d differs from eager" % (rep, k)
+
+
+# ------------------------------------------------------------------ RMSNorm fused into the GEMV
+@pytest.mark.parametrize("in_dim,n,out_dims", [
+    (1024, 1000, [300, 64]),               # four teams a row
+    (2048, 2047, [33, 65, 17]),            # dword activation loads
+    (4096, 4096, [4096, 1024, 1024]),      # the Q, K, V projections
+    (5120, 4999, [700, 128]),              # three slots, ragged n
+    (16384, 16384, [129]),
+])
+def test_rmsnorm_q4k_q8_gemv_multi_bit_identical(in_dim, n, out_dims):
+    """One launch (RMSNorm + Q8_1 in every workgroup, then the GEMVs) equals
+    rz_rmsnorm_q8_1 followed by rz_q4k_q8_gemv_multi bit for bit: the outputs
+    and the Q8_1 side output."""
+    banner("rmsnorm multi", in_dim, n, out_dims)
+    x = synth.activation(synth.rng(81, in_dim), n)
+    gam = synth.norm_weights(synth.rng(81, 1), n)
+    ws = [dev_bytes(synth.q4k_weights(synth.rng(82, k), o, in_dim)) for k, o in enumerate(out_dims)]
+    xd, gd = dev_f32(x), dev_f32(gam)
+    xq_ref = empty_bytes(rz.q8_1_nbytes(in_dim))
+    rz.rz_rmsnorm_q8_1(xd, gd, 1e-5, n, in_dim, 1, None, xq_ref)
+    y_ref = [empty_f32(o) for o in out_dims]
+    rz.rz_q4k_q8_gemv_multi(ws, xq_ref, y_ref, out_dims, in_dim)
+    xq = empty_bytes(rz.q8_1_nbytes(in_dim))
+    y = [empty_f32(o) for o in out_dims]
+    rz.rz_rmsnorm_q4k_q8_gemv_multi(ws, xd, gd, 1e-5, n, xq, y, out_dims, in_dim)
+    assert np.array_equal(host(xq), host(xq_ref)), "Q8_1 side output differs"
+    for m, (a_, b_) in enumerate(zip(y, y_ref)):
+        assert np.array_equal(host(a_).view(np.uint32), host(b_).view(np.uint32)), "matrix %d" % m
+    y2 = [empty_f32(o) for o in out_dims]
+    rz.rz_rmsnorm_q4k_q8_gemv_multi(ws, xd, gd, 1e-5, n, None, y2, out_dims, in_dim)
+    for a_, b_ in zip(y2, y_ref):
+        assert np.array_equal(host(a_).view(np.uint32), host(b_).view(np.uint32))
+
+
+@pytest.mark.parametrize("hidden,inter", [
+    (1024, 2816),
+    (2048, 5632),
+    (4096, 14336),       # the 8B FFN block
+    (16384, 256),        # the widest hidden state, one pass of gate/up rows
+])
+def test_rmsnorm_swiglu_ffn_add_bit_identical(hidden, inter):
+    """The pre-norm FFN block in two launches (RMSNorm + Q8_1 in every gate/up
+    workgroup, then down + residual) equals rz_rmsnorm_q8_1 followed by
+    rz_swiglu_ffn_q4k_add with r = x, bit for bit: h, h_q8, gu and y, also
+    with y written over x."""
+    banner("rmsnorm swiglu add", hidden, inter)
+    x = synth.activation(synth.rng(83, hidden), hidden)
+    gam = synth.norm_weights(synth.rng(83, 1), hidden)
+    ws = [dev_bytes(synth.q4k_weights(synth.rng(84, k), o, i))
+          for k, (o, i) in enumerate(((inter, hidden), (inter, hidden), (hidden, inter)))]
+    xd, gd = dev_f32(x), dev_f32(gam)
+    xq = empty_bytes(rz.q8_1_nbytes(hidden))
+    rz.rz_rmsnorm_q8_1(xd, gd, 1e-5, hidden, hidden, 1, None, xq)
+    h_ref, hq_ref = empty_f32(inter), empty_bytes(rz.q8_1_nbytes(inter))
+    gu_ref, y_ref = empty_f32(2 * inter), empty_f32(hidden)
+    rz.rz_swiglu_ffn_q4k_add(*ws[:3], xq, h_ref, hq_ref, xd, y_ref, gu_ref, hidden, inter)
+    bits = lambda t: host(t).view(np.uint32)
+    for in_place in (False, True):
+        xd2 = dev_f32(x)
+        h, hq = empty_f32(inter), empty_bytes(rz.q8_1_nbytes(inter))
+        gu = empty_f32(2 * inter)
+        y = xd2 if in_place else empty_f32(hidden)
+        rz.rz_rmsnorm_swiglu_ffn_q4k_add(*ws[:3], xd2, gd, 1e-5, h, hq, y, gu, hidden, inter)
+        assert np.array_equal(bits(gu), bits(gu_ref)), "gate/up"
+        assert np.array_equal(bits(h), bits(h_ref)), "h"
+        assert np.array_equal(host(hq), host(hq_ref)), "h_q8"
+        assert np.array_equal(bits(y), bits(y_ref)), "y (in place: %s)" % in_place
+    y2 = empty_f32(hidden)
+    rz.rz_rmsnorm_swiglu_ffn_q4k_add(*ws[:3], xd, gd, 1e-5, h, hq, y2, None, hidden, inter)
+    assert np.array_equal(bits(y2), bits(y_ref)), "without gu"
