@@ -10,8 +10,11 @@ do not print it; the reading used here:
 * ``amax = max |x|`` over the block, ``d = fp32(amax) / fp32(127)`` (one IEEE
   fp32 division, correctly rounded);
 * ``q = round_half_even(fp32(x / d))`` -- again a true fp32 division -- clamped to
-  [-127, 127] (the clamp never binds; it is kept as part of the definition);
-* an all-zero block has ``d = 0``, ``q = 0``, ``s = 0``;
+  [-127, 127] (it binds only where d is a
+  denormal rounded down, e.g. amax = 190 * 2^-149 with d = 2^-149);
+* an all-zero block has ``d = 0``, ``q = 0``, ``s = 0``; so has a block whose
+  ``d`` rounds to 0 (a denormal ``amax`` of at most 63 * 2^-149), where the
+  quotients ``x / d`` have no value and the pages say nothing;
 * ``s = fp32(d * fp32(sum q))`` with the sum taken exactly in integers;
 * stored as 40 bytes: fp32 ``d``, fp32 ``s`` (little endian), then 32 int8 codes.
   Blocks are contiguous; the tokens of a batch follow each other.
@@ -57,9 +60,11 @@ def _quantize_block(xb: np.ndarray):
         a = np.float32(abs(v))
         if a > amax:
             amax = a
-    if amax == np.float32(0.0):
-        return np.float32(0.0), np.float32(0.0), np.zeros(QK8_1, np.int8)
     d = np.float32(amax / _F127)       # fp32 / fp32 -> correctly rounded fp32
+    if d == np.float32(0.0):
+        # amax == 0, or a denormal amax of at most 63 * 2^-149 for which
+        # amax / 127 rounds to 0: x / d has no value, so the block is zeros
+        return np.float32(0.0), np.float32(0.0), np.zeros(QK8_1, np.int8)
     q = np.empty(QK8_1, np.int8)
     total = 0
     for i, v in enumerate(xb):

@@ -102,22 +102,46 @@ __device__ __forceinline__ void load_block_quad(float v[4], __amdgpu_buffer_rsrc
 // One Q8_1 block quantized by an aligned group of 8 lanes; lane i (0..7) holds
 // values 4i..4i+3.  Returns this lane's four codes packed little-endian and
 // sets d and s (identical in all 8 lanes).  The rule: amax = max|x| (exact),
-// d = amax / 127 (correctly rounded fp32 division), q = rint(x / d) (fp32
-// division, ties to even), s = d * float(sum q); amax == 0 gives zeros.
-// Branch-free: the 8-lane max and sum run on DPP, and an all-zero block takes
-// its zero codes by a select (its quotients are 0/0).
+// d = amax / 127 (correctly rounded fp32 division), q = rint(x / d) (the
+// correctly rounded fp32 quotient, ties to even), s = d * float(sum q);
+// d == 0 (amax == 0, or so small that amax / 127 rounds to 0) gives zeros.
+// Branch-free: the 8-lane max and sum run on DPP, and a zero block takes its
+// zero codes by a select (its quotients have no value).
 __device__ __forceinline__ uint32_t q8_1_block_group8(const float v[4], float& d, float& s) {
   float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
   amax = fmaxf(amax, dpp_f<0xB1>(amax));
   amax = fmaxf(amax, dpp_f<0x4E>(amax));
   amax = fmaxf(amax, dpp_f<0x141>(amax));
-  d = amax / 127.0f;
-  const bool zero = amax == 0.0f;
+  // Every quotient here is the correctly rounded one, computed without a
+  // division (Markstein's theorem): with y the correctly rounded reciprocal of
+  // the divisor b, q0 = a*y is within an ulp of a/b, the residual a - q0*b is
+  // exact in one fma, and q0 + residual*y rounds to exactly RN(a/b).
+  // d = RN(amax / 127) this way, with y = RN(1/127) a constant: equal to the
+  // division for every non-negative float, denormals included.
+  constexpr float kInv127 = 1.0f / 127.0f;
+  {
+    const float q0 = amax * kInv127;
+    d = __builtin_fmaf(__builtin_fmaf(-q0, 127.0f, amax), kInv127, q0);
+  }
+  // amax == 0, and amax of at most 63 * 2^-149, where d rounds to 0 and the
+  // quotients have no value: the block of zeros
+  const bool zero = d == 0.0f;
+  // The four v/d: y is the hardware reciprocal (error under one ulp) after one
+  // Newton step, which gives RN(1/d) for every significand; both that and the
+  // quotients hold on this GPU for every float in [2^-102, 2^101) and for
+  // 2^30 sampled quotients.  A block with amax < 2^-60 is scaled by 2^64 first
+  // (exact), so that d, its reciprocal and every residual stay normal.
+  const float sc = amax < 0x1p-60f ? 0x1p64f : 1.0f;
+  const float ds = d * sc;
+  const float y0 = __builtin_amdgcn_rcpf(ds);
+  const float y = __builtin_fmaf(__builtin_fmaf(-ds, y0, 1.0f), y0, y0);
   uint32_t packed = 0;
   int sum = 0;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    float r = rintf(v[k] / d);
+    const float xs = v[k] * sc;
+    const float q0 = xs * y;
+    float r = rintf(__builtin_fmaf(__builtin_fmaf(-q0, ds, xs), y, q0));
     r = fminf(fmaxf(r, -127.0f), 127.0f);
     const int q = zero ? 0 : (int)r;
     sum += q;

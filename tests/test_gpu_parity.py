@@ -114,6 +114,31 @@ def _q8_case(kind, n, nt, seed):
     if kind == "huge":
         return (g.standard_normal((nt, n)) * 1e30).astype(np.float32).squeeze(0) if nt == 1 else \
             (g.standard_normal((nt, n)) * 1e30).astype(np.float32)
+    if kind == "denormal":
+        # per block a scale of 2^-149 .. 2^-118 (denormal and smallest normal
+        # d, and blocks whose d rounds to 0) times integers up to 127
+        e = g.integers(-149, -117, (nt, n // 32 + 1)).repeat(32, axis=1)[:, :n]
+        kmax = g.integers(1, 128, (nt, n // 32 + 1)).repeat(32, axis=1)[:, :n]
+        k = np.rint(g.uniform(-1, 1, (nt, n)) * kmax)
+        x = np.ldexp(k, e).astype(np.float32)
+        return x[0] if nt == 1 else x
+    if kind == "scale_edge":
+        # block maxima on both sides of 2^-60, where the kernel's exact 2^64 scaling starts
+        e = g.uniform(-64, -56, (nt, n // 32 + 1)).repeat(32, axis=1)[:, :n]
+        x = (g.uniform(-1, 1, (nt, n)) * np.exp2(e)).astype(np.float32)
+        return x[0] if nt == 1 else x
+    if kind == "boundary":
+        # values within a few ulps of (k + 1/2) d: every code is a close rounding decision
+        nb = n // 32
+        amax = np.exp2(g.uniform(-30, 30, (nt, nb))).astype(np.float32)
+        d = (amax / np.float32(127)).astype(np.float32)
+        k = g.integers(-127, 127, (nt, nb, 32)) + 0.5
+        x = (k * d[..., None].astype(np.float64)).astype(np.float32)
+        x = (x.view(np.int32) + g.integers(-3, 4, x.shape).astype(np.int32)).view(np.float32)
+        x = np.clip(x, -amax[..., None], amax[..., None])
+        x[..., 0] = amax
+        x = x.reshape(nt, nb * 32)
+        return x[0] if nt == 1 else x
     if kind == "ties":
         # halves at d = 1: every code is a round-half-to-even decision
         x = (g.integers(-254, 255, (nt, n)) / 2.0).astype(np.float32)
@@ -135,6 +160,9 @@ def _q8_case(kind, n, nt, seed):
     ("tiny", 512, 512, 1),
     ("huge", 512, 512, 2),
     ("ties", 1024, 1024, 4),
+    ("denormal", 4096, 4096, 2),
+    ("scale_edge", 4096, 4096, 1),
+    ("boundary", 8192, 8192, 4),
 ])
 def test_q8_1_matches_oracle(kind, n, n_padded, nt):
     banner("q8_1", kind, n, n_padded, nt)

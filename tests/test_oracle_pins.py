@@ -119,6 +119,48 @@ def test_q8_1_sign_and_power_of_two_symmetry(seed):
         assert np.array_equal(sc.s, (a.s * np.float32(2.0 ** k)).astype(np.float32))
 
 
+def _units(vals, e):
+    """float32 values k * 2^e for the integers or halves k (exact, denormals included)."""
+    return np.array([np.ldexp(v, e) for v in vals], np.float64).astype(np.float32)
+
+
+def test_q8_1_denormal_blocks():
+    """Blocks of denormals, worked by hand in units of 2^-149 and 2^-140.
+    amax = 63 units: amax/127 < 2^-150 rounds to 0, and the block is zeros.
+    amax = 64 units: amax/127 = 0.504 units rounds to d = 2^-149, so every code
+    is the value in units.  amax = 190 units: d = 2^-149 again and the clamp
+    binds.  amax = 127 * 2^-140: d = 2^-140 exactly, and halves of d round to
+    even."""
+    x = np.zeros(32, np.float32)
+    x[:3] = _units([63, -5, 1], -149)
+    blk = oracle.quantize_q8_1(x)
+    assert blk.d[0] == 0 and blk.s[0] == 0 and not blk.q.any()
+
+    x = np.zeros(32, np.float32)
+    ks = [64, -63, 1, -1, 0, 32, 7, -40]
+    x[:8] = _units(ks, -149)
+    blk = oracle.quantize_q8_1(x)
+    assert blk.d[0] == np.float32(np.ldexp(1.0, -149))
+    assert list(blk.q[0, :8]) == ks and not blk.q[0, 8:].any()
+    assert blk.s[0] == np.float32(np.ldexp(sum(ks), -149))
+
+    # amax = 190 units: 190/127 = 1.496 rounds down to d = 2^-149, so 190 and
+    # -190 units quotient to +-190 and the clamp to [-127, 127] binds
+    x = np.zeros(32, np.float32)
+    x[:3] = _units([190, 100, -190], -149)
+    blk = oracle.quantize_q8_1(x)
+    assert blk.d[0] == np.float32(np.ldexp(1.0, -149))
+    assert list(blk.q[0, :3]) == [127, 100, -127] and not blk.q[0, 3:].any()
+    assert blk.s[0] == np.float32(np.ldexp(100, -149))
+
+    x = np.zeros(32, np.float32)
+    x[:6] = _units([127, 0.5, 1.5, 2.5, -0.5, -1.5], -140)
+    blk = oracle.quantize_q8_1(x)
+    assert blk.d[0] == np.float32(np.ldexp(1.0, -140))
+    assert list(blk.q[0, :6]) == [127, 0, 2, 2, 0, -2]
+    assert blk.s[0] == np.float32(np.ldexp(129, -140))
+
+
 def test_q8_1_batch_is_per_token():
     X = synth.activation(synth.rng(4, 0), 256, n_tokens=3)
     b = oracle.quantize_q8_1(X)
