@@ -106,12 +106,18 @@ __device__ __forceinline__ void load_block_quad(float v[4], __amdgpu_buffer_rsrc
 // correctly rounded fp32 quotient, ties to even), s = d * float(sum q);
 // d == 0 (amax == 0, or so small that amax / 127 rounds to 0) gives zeros.
 // Branch-free: the 8-lane max and sum run on DPP, and a zero block takes its
-// zero codes by a select (its quotients have no value).
+// zero codes through a zero reciprocal (its quotients have no value).
 __device__ __forceinline__ uint32_t q8_1_block_group8(const float v[4], float& d, float& s) {
   float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-  amax = fmaxf(amax, dpp_f<0xB1>(amax));
-  amax = fmaxf(amax, dpp_f<0x4E>(amax));
-  amax = fmaxf(amax, dpp_f<0x141>(amax));
+  // the 8-lane maximum on bit patterns: non-negative floats order as their
+  // bit patterns do as integers, and an integer max takes the DPP operand
+  {
+    int ai = __builtin_bit_cast(int, amax);
+    ai = max(ai, dpp_i<0xB1>(ai));
+    ai = max(ai, dpp_i<0x4E>(ai));
+    ai = max(ai, dpp_i<0x141>(ai));
+    amax = __builtin_bit_cast(float, ai);
+  }
   // Every quotient here is the correctly rounded one, computed without a
   // division (Markstein's theorem): with y the correctly rounded reciprocal of
   // the divisor b, q0 = a*y is within an ulp of a/b, the residual a - q0*b is
@@ -134,7 +140,8 @@ __device__ __forceinline__ uint32_t q8_1_block_group8(const float v[4], float& d
   const float sc = amax < 0x1p-60f ? 0x1p64f : 1.0f;
   const float ds = d * sc;
   const float y0 = __builtin_amdgcn_rcpf(ds);
-  const float y = __builtin_fmaf(__builtin_fmaf(-ds, y0, 1.0f), y0, y0);
+  // a zero block takes y = 0, so that every quotient is 0
+  const float y = zero ? 0.0f : __builtin_fmaf(__builtin_fmaf(-ds, y0, 1.0f), y0, y0);
   uint32_t packed = 0;
   int sum = 0;
 #pragma unroll
@@ -143,7 +150,7 @@ __device__ __forceinline__ uint32_t q8_1_block_group8(const float v[4], float& d
     const float q0 = xs * y;
     float r = rintf(__builtin_fmaf(__builtin_fmaf(-q0, ds, xs), y, q0));
     r = fminf(fmaxf(r, -127.0f), 127.0f);
-    const int q = zero ? 0 : (int)r;
+    const int q = (int)r;
     sum += q;
     packed |= ((uint32_t)(q & 0xff)) << (8 * k);
   }
