@@ -99,8 +99,10 @@ __device__ __forceinline__ void load_x_slots(XSlots<S, NT>& xs, const uint8_t* _
 }
 
 // The same slots from a workgroup's LDS copy of the chunk's Q8_1 blocks:
-// token t's blocks start at xl + t * tok_bytes.
-template <int TPR, int S, int NT>
+// token t's blocks start at xl + t * tok_bytes.  FILLED: the copy holds every
+// slot of all NT tokens, zero blocks past the chunk and past n_tokens, so the
+// reads need no test (and the registers no zeroing).
+template <int TPR, int S, int NT, bool FILLED = false>
 __device__ __forceinline__ void load_x_slots_from_lds(XSlots<S, NT>& xs, const uint8_t* xl,
                                                       uint32_t tok_bytes, int nsb, int n_tokens,
                                                       const LaneRole& ro) {
@@ -109,7 +111,7 @@ __device__ __forceinline__ void load_x_slots_from_lds(XSlots<S, NT>& xs, const u
 #pragma unroll
     for (int s = 0; s < S; ++s) {
       const int sb = s * TPR + ro.tslot;
-      if (t < n_tokens && sb < nsb) {
+      if (FILLED || (t < n_tokens && sb < nsb)) {
         const uint8_t* xb = xl + t * tok_bytes + sb * 8 * kQ8Bytes;
         const uint2* plo = (const uint2*)(xb + (2 * ro.c) * kQ8Bytes + 8 + 16 * ro.h);
         const uint2* phi = (const uint2*)(xb + (2 * ro.c + 1) * kQ8Bytes + 8 + 16 * ro.h);
@@ -180,7 +182,8 @@ __device__ __forceinline__ void x_stage_commit(const XStage<TPR, S, NT, WPB>& st
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-  load_x_slots_from_lds<TPR, S, NT>(xs, lds, X::kTokBytes, nsb, n_tokens, ro);
+  // every chunk of the copy was written (zeros past the chunk and the tokens)
+  load_x_slots_from_lds<TPR, S, NT, true>(xs, lds, X::kTokBytes, nsb, n_tokens, ro);
 }
 
 // Weights of R*RW rows (RW = 8/TPR side by side, R unrolled) for one lane:

@@ -36,14 +36,16 @@ struct Q4KF32Args {
   int nsb;            // super-blocks per row (in_dim / 256)
 };
 
-// Activation slots from the workgroup's LDS copy of the Q8_1 blocks.
+// Activation slots from the workgroup's LDS copy of the Q8_1 blocks, which
+// holds all S * TPR slots (zero blocks past the row), so no slot is tested.
 template <int TPR, int S>
 __device__ __forceinline__ void load_x_slots_lds(XSlots<S, 1>& xs, const uint8_t* xq, int nsb,
                                                  const LaneRole& ro) {
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     const int sb = s * TPR + ro.tslot;
-    if (sb < nsb) {
+    (void)nsb;   // the LDS copy holds all S * TPR slots, zero blocks past nsb
+    {
       const uint8_t* xb = xq + sb * 8 * kQ8Bytes;
       const uint2* plo = (const uint2*)(xb + (2 * ro.c) * kQ8Bytes + 8 + 16 * ro.h);
       const uint2* phi = (const uint2*)(xb + (2 * ro.c + 1) * kQ8Bytes + 8 + 16 * ro.h);
@@ -55,11 +57,6 @@ __device__ __forceinline__ void load_x_slots_lds(XSlots<S, 1>& xs, const uint8_t
       const float* own = (const float*)(xb + ro.i * kQ8Bytes);
       xs.dx[0][s] = own[0];
       xs.sx[0][s] = own[1];
-    } else {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) { xs.lo[0][s][k] = 0; xs.hi[0][s][k] = 0; }
-      xs.dx[0][s] = 0.0f;
-      xs.sx[0][s] = 0.0f;
     }
   }
 }
@@ -115,11 +112,12 @@ __global__ __launch_bounds__(256) void q4k_gemv_f32_kernel(Q4KF32Args a) {
     load_w_tile<TPR, S, R>(t[k], src, off, (wid + k * nwaves) * kRowsPerGroup);
   __builtin_amdgcn_sched_barrier(0);
 
-  // (3) quantize into LDS (and, in workgroup 0, to global memory)
+  // (3) quantize into LDS (and, in workgroup 0, to global memory); the LDS copy
+  // covers all S * TPR slots, and blocks past nblk quantize zeros into zero blocks
 #pragma unroll
   for (int p = 0; p < kPasses; ++p) {
     const int b = p * kBlocksPerPass + qb;
-    if (b < nblk) {   // whole 8-lane groups take the same branch
+    if (b < S * TPR * 8) {   // whole 8-lane groups take the same branch
       float d, s;
       const uint32_t packed = q8_1_block_group8(xv[p], d, s);
       uint8_t* blk = xq_lds + b * kQ8Bytes;
@@ -128,7 +126,7 @@ __global__ __launch_bounds__(256) void q4k_gemv_f32_kernel(Q4KF32Args a) {
         ((float*)blk)[0] = d;
         ((float*)blk)[1] = s;
       }
-      if (a.xq_out && blockIdx.x == 0) {
+      if (a.xq_out && blockIdx.x == 0 && b < nblk) {
         uint8_t* g = a.xq_out + (size_t)b * kQ8Bytes;
         *(uint32_t*)(g + 8 + 4 * qi) = packed;
         if (qi == 0) {
@@ -177,7 +175,7 @@ static hipError_t launch_f32_g(const Q4KF32Args& a, long groups, hipStream_t st)
   constexpr int P = G > kF32TilesInFlight ? kF32TilesInFlight : (G > 1 ? G - 1 : 1);
   const long waves = (groups + G - 1) / G;
   const unsigned grid = (unsigned)((waves + 3) / 4);
-  const size_t lds = (size_t)a.nsb * 8 * kQ8Bytes;
+  const size_t lds = (size_t)S * TPR * 8 * kQ8Bytes;
   hipLaunchKernelGGL((q4k_gemv_f32_kernel<TPR, S, R, G, P, XV>), dim3(grid), dim3(256), lds, st, a);
   return hipGetLastError();
 }

@@ -112,13 +112,14 @@ __global__ __launch_bounds__(256) void q4k_q8_gemv_multi_kernel(Q4KMultiArgs a) 
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (NORM) {
     __shared__ float part[kXrowThreads / kWave];
-    xrow_quantize<kRowPasses, true>(xrow, a.eps, a.n, a.nsb * 8, xl_lds,
-                                    blockIdx.x == 0 ? a.xq_out : nullptr, part);
+    xrow_quantize<kRowPasses, true, S * TPR * 8>(xrow, a.eps, a.n, a.nsb * 8, xl_lds,
+                                                 blockIdx.x == 0 ? a.xq_out : nullptr, part);
     // LDS-only release/acquire: the weight loads stay in flight
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-    load_x_slots_from_lds<TPR, S, NT>(xs, xl_lds, 0u, a.nsb, 1, ro);
+    static_assert(NT == 1, "the RMSNorm prologue serves one token");
+    load_x_slots_from_lds<TPR, S, NT, true>(xs, xl_lds, 0u, a.nsb, 1, ro);
   } else if constexpr (XL) {
     x_stage_commit(xst, xl_lds, xs, a.nsb, a.n_tokens, ro);
   }
@@ -151,7 +152,7 @@ template <int TPR, int S, int G, bool XV>
 static hipError_t launch_multi_norm_g(const Q4KMultiArgs& a, hipStream_t st) {
   constexpr int R = S <= 2 ? 2 : 1;
   constexpr int P = G > 2 ? 2 : (G > 1 ? G - 1 : 1);
-  const size_t lds = (size_t)a.nsb * 8 * kQ8Bytes;
+  const size_t lds = (size_t)S * TPR * 8 * kQ8Bytes;   // every slot, zero blocks past the row
   const long waves = ((long)a.group0[a.n_mats] + G - 1) / G;
   const unsigned grid = (unsigned)((waves + 3) / 4);
   hipLaunchKernelGGL((q4k_q8_gemv_multi_kernel<TPR, S, R, 1, G, P, false, true, XV>), dim3(grid),

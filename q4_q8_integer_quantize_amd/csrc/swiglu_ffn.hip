@@ -80,12 +80,13 @@ __global__ __launch_bounds__(64 * WPB) void swiglu_gate_up_kernel(SwiArgs a) {
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (NORM) {
     __shared__ float part[kXrowThreads / kWave];
-    xrow_quantize<kRowPasses, true>(xrow, a.eps, hidden, a.nsb * 8, x_lds, nullptr, part);
+    xrow_quantize<kRowPasses, true, S * TPR * 8>(xrow, a.eps, hidden, a.nsb * 8, x_lds, nullptr,
+                                                 part);
     // LDS-only release/acquire: the weight loads stay in flight
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-    load_x_slots_from_lds<TPR, S, 1>(xs, x_lds, 0u, a.nsb, 1, ro);
+    load_x_slots_from_lds<TPR, S, 1, true>(xs, x_lds, 0u, a.nsb, 1, ro);
   } else if constexpr (XL) {
     x_stage_commit(xst, x_lds, xs, a.nsb, 1, ro);
   }

@@ -93,12 +93,14 @@ __device__ __forceinline__ void xrow_request(XRow<NP, NORM>& r, const float* x,
 }
 
 // The row's nblk Q8_1 blocks into LDS at lds + 40 b (and into gout when it is
-// not null); with NORM the values are (x * (1 / sqrt(sum x^2 / n + eps))) *
-// gamma first.  `part` is LDS for 4 floats.  Ends with the block copy written
-// but not yet published: the caller's barrier does that.
-template <int NP, bool NORM>
+// not null), followed in LDS by zero blocks up to CAP (the blocks the copy
+// holds, at most 32 NP); with NORM the values are (x * (1 / sqrt(sum x^2 / n +
+// eps))) * gamma first.  `part` is LDS for 4 floats.  Ends with the block copy
+// written but not yet published: the caller's barrier does that.
+template <int NP, bool NORM, int CAP>
 __device__ __forceinline__ void xrow_quantize(const XRow<NP, NORM>& r, float eps, int n, int nblk,
                                               uint8_t* lds, uint8_t* gout, float* part) {
+  static_assert(CAP <= NP * kXrowBlocksPerPass, "the zero blocks come from the passes");
   float scale = 1.0f;
   if constexpr (NORM) {
     float ss = 0.0f;
@@ -113,7 +115,9 @@ __device__ __forceinline__ void xrow_quantize(const XRow<NP, NORM>& r, float eps
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
     const int b = p * kXrowBlocksPerPass + qb;
-    if (b < nblk) {   // whole 8-lane groups take the same branch
+    // whole 8-lane groups take the same branch; past nblk the values read as
+    // zeros, so the blocks quantize to zero blocks
+    if (b < CAP) {
       float v[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) v[k] = r.x[p][k];
@@ -129,7 +133,7 @@ __device__ __forceinline__ void xrow_quantize(const XRow<NP, NORM>& r, float eps
         ((float*)blk)[0] = d;
         ((float*)blk)[1] = s;
       }
-      if (gout) {
+      if (gout && b < nblk) {
         uint8_t* go = gout + (size_t)b * kQ8Bytes;
         *(uint32_t*)(go + 8 + 4 * qi) = packed;
         if (qi == 0) {
