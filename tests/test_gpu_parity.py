@@ -1295,16 +1295,19 @@ def test_minimum_alignments_bit_identical():
 
 
 # ------------------------------------------------------------------ HIP graph capture
-def test_graph_replays_match_eager():
+@pytest.mark.parametrize("fused", [False, True])
+def test_graph_replays_match_eager(fused):
     """A decode-layer-shaped sequence -- RMSNorm + Q8_1, the attention
     projections in one launch, the O projection with its residual, RMSNorm
     again, the SwiGLU chain with its residual, and the LM head with bias and
     greedy token -- captured in one HIP graph and replayed three times, with
     eager work and synchronisations between replays, gives every replay the
     bytes of the eager run.  Nothing in the library records memsets or
-    allocations, so the graph has kernel nodes only."""
+    allocations, so the graph has kernel nodes only.  `fused`: the RMSNorm runs
+    inside the Q/K/V launch and the gate/up launch; every output but the
+    shared Q8_1 buffer then also equals the unfused sequence's bytes."""
     import torch
-    banner("graph replays")
+    banner("graph replays", "fused" if fused else "separate")
     H, KV, I, V = 4096, 1024, 2816, 5000      # two-slot rows: the LDS-staged activation path
     g = lambda k: synth.rng(80, k)
     wq, wk, wv, wo = (dev_bytes(synth.q4k_weights(g(k), o, H)) for k, o in ((1, H), (2, KV), (3, KV), (4, H)))
@@ -1325,29 +1328,44 @@ def test_graph_replays_match_eager():
     ws = torch.empty(rz.rz_lm_head_q4_0_workspace_bytes(V, H, 0), dtype=torch.uint8, device="cuda")
     outs = (hidden, xq, q, k_, v, h, hq, logits, idx, val)
 
-    def layer():
+    def layer(fused):
         hidden.copy_(x0)
-        rz.rz_rmsnorm_q8_1(hidden, gam1, 1e-5, H, H, 1, None, xq)
-        rz.rz_q4k_q8_gemv_multi([wq, wk, wv], xq, [q, k_, v], [H, KV, KV], H)
+        if fused:
+            rz.rz_rmsnorm_q4k_q8_gemv_multi([wq, wk, wv], hidden, gam1, 1e-5, H, None, [q, k_, v],
+                                            [H, KV, KV], H)
+        else:
+            rz.rz_rmsnorm_q8_1(hidden, gam1, 1e-5, H, H, 1, None, xq)
+            rz.rz_q4k_q8_gemv_multi([wq, wk, wv], xq, [q, k_, v], [H, KV, KV], H)
         # the attention output stands in as q; quantize it for the O projection
         rz.rz_q8_1_quantize(q, H, H, 1, xq)
         rz.rz_q4k_q8_gemv_add(wo, xq, hidden, hidden, H, H, 1)
-        rz.rz_rmsnorm_q8_1(hidden, gam2, 1e-5, H, H, 1, None, xq)
-        rz.rz_swiglu_ffn_q4k_add(wg, wu, wd, xq, h, hq, hidden, hidden, None, H, I)
+        if fused:
+            rz.rz_rmsnorm_swiglu_ffn_q4k_add(wg, wu, wd, hidden, gam2, 1e-5, h, hq, hidden, None,
+                                             H, I)
+        else:
+            rz.rz_rmsnorm_q8_1(hidden, gam2, 1e-5, H, H, 1, None, xq)
+            rz.rz_swiglu_ffn_q4k_add(wg, wu, wd, xq, h, hq, hidden, hidden, None, H, I)
         rz.rz_lm_head_q4_0(wl, hidden, 0, bias, logits, V, H, idx, val, ws)
 
-    layer()
+    layer(False)
     torch.cuda.synchronize()
+    separate = [_bits(t) for t in outs]
+    if fused:
+        layer(True)
+        torch.cuda.synchronize()
     eager = [_bits(t) for t in outs]
+    for k, t in enumerate(outs):
+        if t is not xq:
+            assert np.array_equal(eager[k], separate[k]), "output %d: fused differs from separate" % k
     graph = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        layer()                                   # warm-up on the capture stream
+        layer(fused)                              # warm-up on the capture stream
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     with torch.cuda.graph(graph):
-        layer()
+        layer(fused)
     for rep in range(3):
         for t in outs:                            # eager work between replays
             t.zero_()
