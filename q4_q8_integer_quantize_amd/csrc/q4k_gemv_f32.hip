@@ -61,11 +61,13 @@ __device__ __forceinline__ void load_x_slots_lds(XSlots<S, 1>& xs, const uint8_t
   }
 }
 
-// Q8_1 blocks per workgroup pass: 256 threads, 8 lanes per block.
-constexpr int kBlocksPerPass = 32;
+// Q8_1 blocks per workgroup pass: 8 lanes per block, WPB waves.
+template <int WPB>
+constexpr int blocks_per_pass() { return 8 * WPB; }
 
-template <int TPR, int S, int R, int G, int P, bool XV>
-__global__ __launch_bounds__(256) void q4k_gemv_f32_kernel(Q4KF32Args a) {
+template <int TPR, int S, int R, int G, int P, bool XV, int WPB = 4>
+__global__ __launch_bounds__(64 * WPB) void q4k_gemv_f32_kernel(Q4KF32Args a) {
+  constexpr int kBlocksPerPass = blocks_per_pass<WPB>();
   constexpr int RW = 8 / TPR;
   constexpr uint32_t kRowsPerGroup = (uint32_t)RW * R;
   // the longest activation this instantiation serves: S slots of TPR teams
@@ -100,8 +102,9 @@ __global__ __launch_bounds__(256) void q4k_gemv_f32_kernel(Q4KF32Args a) {
   }
 
   // (2) the first weight tiles
-  const uint32_t nwaves = gridDim.x * 4u;
-  const uint32_t wid = __builtin_amdgcn_readfirstlane(blockIdx.x * 4u + (threadIdx.x >> 6));
+  const uint32_t nwaves = gridDim.x * (uint32_t)WPB;
+  const uint32_t wid =
+      __builtin_amdgcn_readfirstlane(blockIdx.x * (uint32_t)WPB + (threadIdx.x >> 6));
   const LaneRole ro = make_role<TPR>();
   const uint32_t row_bytes = (uint32_t)a.nsb * kQ4KBytes;
   const WSrc src = make_wsrc(a.w, row_bytes, (uint32_t)a.out_dim * row_bytes);
@@ -169,14 +172,15 @@ __global__ __launch_bounds__(256) void q4k_gemv_f32_kernel(Q4KF32Args a) {
 constexpr int kF32TilesInFlight = 2;
 constexpr long kF32TargetWaves = 1024;
 
-template <int TPR, int S, int G, bool XV>
+template <int TPR, int S, int G, bool XV, int WPB = 4>
 static hipError_t launch_f32_g(const Q4KF32Args& a, long groups, hipStream_t st) {
   constexpr int R = S <= 2 ? 2 : 1;
   constexpr int P = G > kF32TilesInFlight ? kF32TilesInFlight : (G > 1 ? G - 1 : 1);
   const long waves = (groups + G - 1) / G;
-  const unsigned grid = (unsigned)((waves + 3) / 4);
+  const unsigned grid = (unsigned)((waves + WPB - 1) / WPB);
   const size_t lds = (size_t)S * TPR * 8 * kQ8Bytes;
-  hipLaunchKernelGGL((q4k_gemv_f32_kernel<TPR, S, R, G, P, XV>), dim3(grid), dim3(256), lds, st, a);
+  hipLaunchKernelGGL((q4k_gemv_f32_kernel<TPR, S, R, G, P, XV, WPB>), dim3(grid), dim3(64 * WPB),
+                     lds, st, a);
   return hipGetLastError();
 }
 
