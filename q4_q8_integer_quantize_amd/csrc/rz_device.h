@@ -132,11 +132,14 @@ __device__ __forceinline__ uint32_t q8_1_block_group8(const float v[4], float& d
   // amax == 0, and amax of at most 63 * 2^-149, where d rounds to 0 and the
   // quotients have no value: the block of zeros
   const bool zero = d == 0.0f;
-  // The four v/d: y is the hardware reciprocal (error under one ulp) after one
-  // Newton step, which gives RN(1/d) for every significand; both that and the
-  // quotients hold on this GPU for every float in [2^-102, 2^101) and for
-  // 2^30 sampled quotients.  A block with amax < 2^-60 is scaled by 2^64 first
-  // (exact), so that d, its reciprocal and every residual stay normal.
+  // The four v/d: y is the hardware reciprocal after one Newton step.  From
+  // any start within an ulp that step lands on RN(1/d), except for the
+  // all-ones significand from its lower neighbour (Markstein's exception); on
+  // this GPU the reciprocal plus the step equals RN(1/d) for every normal d
+  // below 2^126, and d here is at most 2^121.  The quotients equal the
+  // division for 2^30 sampled pairs.  A block with amax < 2^-60 is scaled by
+  // 2^64 first (exact), so that d, its reciprocal and every residual stay
+  // normal.
   const float sc = amax < 0x1p-60f ? 0x1p64f : 1.0f;
   const float ds = d * sc;
   const float y0 = __builtin_amdgcn_rcpf(ds);

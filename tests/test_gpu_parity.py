@@ -139,6 +139,26 @@ def _q8_case(kind, n, nt, seed):
         x[..., 0] = amax
         x = x.reshape(nt, nb * 32)
         return x[0] if nt == 1 else x
+    if kind == "recip_edge":
+        # blocks whose d = RN(amax/127) has an all-ones significand (2 - 2^-23
+        # times a power of two, the one divisor whose reciprocal a Newton step
+        # cannot always correct), with values within ulps of (k + 1/2) d
+        nb = n // 32
+        e = g.integers(-40, 40, (nt, nb))
+        d = np.ldexp(2.0 - 2.0 ** -23, e).astype(np.float32)
+        amax = (d.astype(np.float64) * 127).astype(np.float32)
+        for _ in range(4):   # step amax until amax / 127 rounds to d
+            lo = (amax / np.float32(127)).astype(np.float32) < d
+            hi = (amax / np.float32(127)).astype(np.float32) > d
+            amax = (amax.view(np.int32) + lo.astype(np.int32) - hi.astype(np.int32)).view(np.float32)
+        assert np.array_equal((amax / np.float32(127)).astype(np.float32), d)
+        k = g.integers(-127, 127, (nt, nb, 32)) + 0.5
+        x = (k * d[..., None].astype(np.float64)).astype(np.float32)
+        x = (x.view(np.int32) + g.integers(-2, 3, x.shape).astype(np.int32)).view(np.float32)
+        x = np.clip(x, -amax[..., None], amax[..., None])
+        x[..., 0] = amax
+        x = x.reshape(nt, nb * 32)
+        return x[0] if nt == 1 else x
     if kind == "ties":
         # halves at d = 1: every code is a round-half-to-even decision
         x = (g.integers(-254, 255, (nt, n)) / 2.0).astype(np.float32)
@@ -163,6 +183,7 @@ def _q8_case(kind, n, nt, seed):
     ("denormal", 4096, 4096, 2),
     ("scale_edge", 4096, 4096, 1),
     ("boundary", 8192, 8192, 4),
+    ("recip_edge", 4096, 4096, 2),
 ])
 def test_q8_1_matches_oracle(kind, n, n_padded, nt):
     banner("q8_1", kind, n, n_padded, nt)
