@@ -224,6 +224,26 @@ def time_rows(lib, rz, torch, dev, graph_time, copies, x, xq, y) -> dict:
                                                              hid.data_ptr(), hid.data_ptr(),
                                                              4096, 4096, 1, s))),
         o_w + XQ_BYTES + 8 * 4096, o_w, "rz_q4k_q8_gemv_add (hidden += O x, in place)")
+    # the attention output as fp32: quantize + O + residual in one launch, and as two
+    ao = torch.from_numpy(synth.activation(synth.rng(1, 5), 4096)).to(dev)
+    xq_o = torch.empty(XQ_BYTES, dtype=torch.uint8, device=dev)
+
+    def o_f32_add(i, s, hp=None):
+        hp = hp or hid.data_ptr()
+        check(lib.rz_q4k_q8_gemv_f32_add(attn_p[i % len(attn_p)][3], ao.data_ptr(), 4096, None, hp,
+                                         hp, 4096, 4096, s))
+
+    def o_two_launch(i, s):
+        check(lib.rz_q8_1_quantize(ao.data_ptr(), 4096, 4096, 1, xq_o.data_ptr(), s))
+        check(lib.rz_q4k_q8_gemv_add(attn_p[i % len(attn_p)][3], xq_o.data_ptr(), hid.data_ptr(),
+                                     hid.data_ptr(), 4096, 4096, 1, s))
+
+    rows["o_proj_f32_add_4096"] = row_entry(
+        graph_time(o_f32_add), o_w + 4 * 4096 + 8 * 4096, o_w,
+        "rz_q4k_q8_gemv_f32_add (Q8_1 of the fp32 attention output, O, hidden += in place)")
+    rows["o_proj_f32_add_4096_two_launch"] = row_entry(
+        graph_time(o_two_launch), o_w + 4 * 4096 + 2 * XQ_BYTES + 8 * 4096, o_w,
+        "rz_q8_1_quantize, then rz_q4k_q8_gemv_add")
 
     # SwiGLU chain 4096 -> 14336 -> 4096, and its down projection alone
     INTER = 14336
@@ -279,8 +299,9 @@ def time_rows(lib, rz, torch, dev, graph_time, copies, x, xq, y) -> dict:
     # RMSNorm + Q8_1 + the Q, K, V projections, in one launch and as two; then
     # one decode layer's projections in sequence, as a model would chain them:
     # RMSNorm + Q8_1 + Q/K/V in one launch, the attention output (stood in for
-    # by q) quantized for O, O with the residual, RMSNorm + Q8_1, the SwiGLU
-    # chain with the residual; weights of both halves rotated
+    # by q) quantized for O and O with the residual in one launch, then
+    # RMSNorm + Q8_1 + the SwiGLU chain with the residual; weights of both
+    # halves rotated
     gam_l = torch.from_numpy(synth.norm_weights(synth.rng(1, synth.T_GAMMA), IN_DIM)).to(dev)
     hid_l = torch.from_numpy(synth.activation(synth.rng(1, synth.T_ACT), IN_DIM)).to(dev)
     xq_l = torch.empty(XQ_BYTES, dtype=torch.uint8, device=dev)
@@ -336,18 +357,18 @@ def time_rows(lib, rz, torch, dev, graph_time, copies, x, xq, y) -> dict:
 
     def layer_body(i, s):
         a_w = attn_p[i % len(attn_p)]
-        hp, xp = hid_l.data_ptr(), xq_l.data_ptr()
+        hp = hid_l.data_ptr()
         qkv_fused(i, s)
-        check(lib.rz_q8_1_quantize(qkv[0].data_ptr(), IN_DIM, IN_DIM, 1, xp, s))
-        check(lib.rz_q4k_q8_gemv_add(a_w[3], xp, hp, hp, IN_DIM, IN_DIM, 1, s))
+        check(lib.rz_q4k_q8_gemv_f32_add(a_w[3], qkv[0].data_ptr(), IN_DIM, None, hp, hp, IN_DIM,
+                                         IN_DIM, s))
         ffn_norm_fused(i, s, hp)
 
     layer_w = attn_w + ffn_w
     rows["decode_layer_4096_14336"] = row_entry(
-        graph_time(layer_body), layer_w + 2 * XQ_BYTES + 9 * X_BYTES + 4 * 6144
+        graph_time(layer_body), layer_w + 9 * X_BYTES + 4 * 6144
         + 4 * INTER + 2 * q8_bytes(INTER), layer_w,
-        "one layer's projections: RMSNorm+Q8_1+Q/K/V (one launch), quantize, O+residual, "
-        "RMSNorm+Q8_1+SwiGLU gate/up (one launch), down+residual (5 kernels)")
+        "one layer's projections: RMSNorm+Q8_1+Q/K/V (one launch), Q8_1+O+residual (one launch), "
+        "RMSNorm+Q8_1+SwiGLU gate/up (one launch), down+residual (4 kernels)")
     del ffn, attn
 
     # Q4_0 LM head 151936 x (896 -> 1024), fp32 and Q8_1 activation

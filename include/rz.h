@@ -204,6 +204,22 @@ int rz_rmsnorm_q4k_q8_gemv_multi(int n_mats, const void* const* w_q4k, float* co
 int rz_q4k_q8_gemv_f32(const void* w_q4k, const float* x, int n, void* x_q8, float* y,
                        int out_dim, int in_dim, void* stream);
 
+/* rz_q4k_q8_gemv_f32_add -- Q8_1 quantize, Q4_K x Q8_1 GEMV and a residual
+ * add in one launch: y = W Q8_1(x) + r.
+ * Passage: realizar 0.8.5 src/cuda/executor/cached.rs,
+ * transformer_layer_gpu_true_dp4a, steps 5-7 (the attention output quantized
+ * to Q8_1 for the O projection, whose output is added to the hidden state).
+ * Bit for bit the result of rz_q8_1_quantize(x, n, in_dim, 1, x_q8) followed
+ * by rz_q4k_q8_gemv_add(w_q4k, x_q8, r, y, out_dim, in_dim, 1).
+ *   w_q4k, x, n, x_q8, out_dim, in_dim: as for rz_q4k_q8_gemv_f32
+ *   r        fp32 [out_dim] residual, 4-byte aligned; may be y itself (the
+ *            hidden state updated in place), otherwise must not overlap it
+ *   y        out: fp32 [out_dim], 4-byte aligned
+ * y and x_q8 must not overlap w_q4k, x or each other, nor x_q8 overlap r.
+ * Errors: RZ_EINVAL (also overlaps), RZ_EDIM, RZ_EALIGN, RZ_ELAUNCH. */
+int rz_q4k_q8_gemv_f32_add(const void* w_q4k, const float* x, int n, void* x_q8, const float* r,
+                           float* y, int out_dim, int in_dim, void* stream);
+
 /* rz_q4k_gemv -- y = W x with W Q4_K and x fp32, no Q8_1 (one token).
  * Passage: realizar 0.8.5 src/cuda/executor/cached.rs,
  * transformer_layer_gpu_cached, steps 2 and 4 (q4k_gemv_cached_async and

@@ -21,7 +21,7 @@ __all__ = [
     "library_path", "load_library", "rz_last_error", "rz_abi_version",
     "rz_q8_1_quantize", "rz_rmsnorm_q8_1", "rz_q4k_q8_gemv", "rz_q4k_q8_gemv_add",
     "rz_q4k_q8_gemv_multi", "rz_rmsnorm_q4k_q8_gemv_multi", "rz_rmsnorm_swiglu_ffn_q4k_add",
-    "rz_q4k_q8_gemv_f32",
+    "rz_q4k_q8_gemv_f32", "rz_q4k_q8_gemv_f32_add",
     "rz_q4_0_gemv", "rz_swiglu_ffn_q4k", "rz_swiglu_ffn_q4k_add", "rz_q4k_gemv",
     "rz_swiglu_ffn_q4k_f32",
     "rz_lm_head_q4_0", "rz_lm_head_q4_0_workspace_bytes", "rz_gelu_ffn_q4_0",
@@ -67,6 +67,7 @@ def load_library() -> ctypes.CDLL:
     lib.rz_q4k_q8_gemv_multi.argtypes = [i, vp, vp, vp, vp, i, i, vp]
     lib.rz_rmsnorm_q4k_q8_gemv_multi.argtypes = [i, vp, vp, vp, vp, vp, ctypes.c_float, i, vp, i, vp]
     lib.rz_rmsnorm_swiglu_ffn_q4k_add.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, i, i, vp]
+    lib.rz_q4k_q8_gemv_f32_add.argtypes = [vp, vp, i, vp, vp, vp, i, i, vp]
     lib.rz_q4_0_gemv.argtypes = [vp, vp, i, vp, i, i, vp]
     lib.rz_swiglu_ffn_q4k.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, vp]
     lib.rz_swiglu_ffn_q4k_add.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, vp]
@@ -78,7 +79,7 @@ def load_library() -> ctypes.CDLL:
     lib.rz_lm_head_q4_0_workspace_bytes.restype = ctypes.c_size_t
     for fn in ("rz_q8_1_quantize", "rz_rmsnorm_q8_1", "rz_q4k_q8_gemv", "rz_q4k_q8_gemv_add",
                "rz_q4k_q8_gemv_f32", "rz_q4k_q8_gemv_multi", "rz_rmsnorm_q4k_q8_gemv_multi",
-               "rz_rmsnorm_swiglu_ffn_q4k_add",
+               "rz_rmsnorm_swiglu_ffn_q4k_add", "rz_q4k_q8_gemv_f32_add",
                "rz_q4_0_gemv", "rz_swiglu_ffn_q4k",
                "rz_swiglu_ffn_q4k_add", "rz_q4k_gemv", "rz_swiglu_ffn_q4k_f32",
                "rz_lm_head_q4_0", "rz_gelu_ffn_q4_0", "rz_abi_version"):
@@ -299,6 +300,20 @@ def rz_swiglu_ffn_q4k_add(w_gate, w_up, w_down, x_q8, h, h_q8, r, y, gu, hidden_
     _check(load_library().rz_swiglu_ffn_q4k_add(_ptr(w_gate), _ptr(w_up), _ptr(w_down),
                                                 _ptr(x_q8), _ptr(h), _ptr(h_q8), _ptr(r), _ptr(y),
                                                 _ptr(gu), hidden_dim, inter_dim, _stream(stream)))
+
+
+def rz_q4k_q8_gemv_f32_add(w_q4k, x, n: int, x_q8, r, y, out_dim: int, in_dim: int,
+                           stream=None) -> None:
+    """y fp32 [out_dim] = W (Q4_K) x Q8_1(x[:n]) + r in one launch; r may be y;
+    x_q8 (or None) receives the Q8_1 blocks."""
+    if out_dim > 0 and in_dim > 0 and in_dim % 256 == 0:
+        _need(w_q4k, out_dim * (in_dim // 256) * Q4K_BLOCK_BYTES, "w_q4k")
+        _need(x, 4 * n, "x")
+        _need(x_q8, q8_1_nbytes(in_dim), "x_q8")
+        _need(r, 4 * out_dim, "r")
+        _need(y, 4 * out_dim, "y")
+    _check(load_library().rz_q4k_q8_gemv_f32_add(_ptr(w_q4k), _ptr(x), n, _ptr(x_q8), _ptr(r),
+                                                 _ptr(y), out_dim, in_dim, _stream(stream)))
 
 
 def rz_q4k_gemv(w_q4k, x, n: int, y, out_dim: int, in_dim: int, stream=None) -> None:

@@ -21,6 +21,11 @@
 // arrives (vector loads retire in order, so this wait does not include the
 // weight tiles), (4) an LDS-only barrier, (5) the GEMV pipeline of
 // q4k_q8_gemv_kernel.
+//
+// RES adds a residual in the store, y = W Q8_1(x) + r (cached.rs steps 5-7:
+// the attention output quantized for the O projection, whose result is added
+// to the hidden state), with r's values requested right after each weight tile
+// as in q4k_q8_gemv_kernel; r may be y itself.
 #include "q4k_gemv.h"
 #include "rz_launch.h"
 
@@ -34,6 +39,7 @@ struct Q4KF32Args {
   int n;
   int out_dim;
   int nsb;            // super-blocks per row (in_dim / 256)
+  const float* r;     // RES: residual [out_dim] (may be y), else unused
 };
 
 // Activation slots from the workgroup's LDS copy of the Q8_1 blocks, which
@@ -65,7 +71,7 @@ __device__ __forceinline__ void load_x_slots_lds(XSlots<S, 1>& xs, const uint8_t
 template <int WPB>
 constexpr int blocks_per_pass() { return 8 * WPB; }
 
-template <int TPR, int S, int R, int G, int P, bool XV, int WPB = 4>
+template <int TPR, int S, int R, int G, int P, bool XV, int WPB = 4, bool RES = false>
 __global__ __launch_bounds__(64 * WPB) void q4k_gemv_f32_kernel(Q4KF32Args a) {
   constexpr int kBlocksPerPass = blocks_per_pass<WPB>();
   constexpr int RW = 8 / TPR;
@@ -109,10 +115,28 @@ __global__ __launch_bounds__(64 * WPB) void q4k_gemv_f32_kernel(Q4KF32Args a) {
   const uint32_t row_bytes = (uint32_t)a.nsb * kQ4KBytes;
   const WSrc src = make_wsrc(a.w, row_bytes, (uint32_t)a.out_dim * row_bytes);
   const LaneOffsets<TPR, S> off = lane_offsets<TPR, S>(src, 0, ro);
+  Q4KGemvArgs ga;
+  ga.r = a.r;
+  ga.w = a.w;
+  ga.xq = nullptr;
+  ga.y = a.y;
+  ga.out_dim = a.out_dim;
+  ga.nsb_row = a.nsb;
+  ga.sb0 = 0;
+  ga.nsb = a.nsb;
+  ga.n_tokens = 1;
   WTile<S, R> t[G];
+  float rv[G][R][1];
+  __amdgpu_buffer_rsrc_t rr;
+  if constexpr (RES)
+    rr = __builtin_amdgcn_make_buffer_rsrc((void*)a.r, (short)0, (int)((uint32_t)a.out_dim * 4u),
+                                           kBufferWord3);
 #pragma unroll
-  for (int k = 0; k < P && k < G; ++k)
+  for (int k = 0; k < P && k < G; ++k) {
     load_w_tile<TPR, S, R>(t[k], src, off, (wid + k * nwaves) * kRowsPerGroup);
+    if constexpr (RES)
+      load_residual<TPR, R, 1>(rv[k], rr, ga, (long)(wid + k * nwaves) * kRowsPerGroup, ro);
+  }
   __builtin_amdgcn_sched_barrier(0);
 
   // (3) quantize into LDS (and, in workgroup 0, to global memory); the LDS copy
@@ -148,24 +172,21 @@ __global__ __launch_bounds__(64 * WPB) void q4k_gemv_f32_kernel(Q4KF32Args a) {
   // (5) GEMV over the register-resident slots
   XSlots<S, 1> xs;
   load_x_slots_lds<TPR, S>(xs, xq_lds, a.nsb, ro);
-  Q4KGemvArgs ga;
-  ga.r = nullptr;
-  ga.w = a.w;
-  ga.xq = nullptr;
-  ga.y = a.y;
-  ga.out_dim = a.out_dim;
-  ga.nsb_row = a.nsb;
-  ga.sb0 = 0;
-  ga.nsb = a.nsb;
-  ga.n_tokens = 1;
 #pragma unroll
   for (int k = 0; k < G; ++k) {
-    if (k + P < G)
+    if (k + P < G) {
       load_w_tile<TPR, S, R>(t[k + P], src, off, (wid + (k + P) * nwaves) * kRowsPerGroup);
+      if constexpr (RES)
+        load_residual<TPR, R, 1>(rv[k + P], rr, ga, (long)(wid + (k + P) * nwaves) * kRowsPerGroup,
+                                 ro);
+    }
     __builtin_amdgcn_sched_barrier(0);
     float acc[R][1];
     q4k_tile_dot<TPR, S, R, 1>(acc, t[k], xs, ro);
-    store_rows<TPR, R, 1, false>(ga, acc, (long)(wid + k * nwaves) * kRowsPerGroup, ro);
+    if constexpr (RES)
+      store_rows_residual<TPR, R, 1>(ga, acc, rv[k], (long)(wid + k * nwaves) * kRowsPerGroup, ro);
+    else
+      store_rows<TPR, R, 1, false>(ga, acc, (long)(wid + k * nwaves) * kRowsPerGroup, ro);
   }
 }
 
@@ -179,8 +200,12 @@ static hipError_t launch_f32_g(const Q4KF32Args& a, long groups, hipStream_t st)
   const long waves = (groups + G - 1) / G;
   const unsigned grid = (unsigned)((waves + WPB - 1) / WPB);
   const size_t lds = (size_t)S * TPR * 8 * kQ8Bytes;
-  hipLaunchKernelGGL((q4k_gemv_f32_kernel<TPR, S, R, G, P, XV, WPB>), dim3(grid), dim3(64 * WPB),
-                     lds, st, a);
+  if (a.r)
+    hipLaunchKernelGGL((q4k_gemv_f32_kernel<TPR, S, R, G, P, XV, WPB, true>), dim3(grid),
+                       dim3(64 * WPB), lds, st, a);
+  else
+    hipLaunchKernelGGL((q4k_gemv_f32_kernel<TPR, S, R, G, P, XV, WPB>), dim3(grid), dim3(64 * WPB),
+                       lds, st, a);
   return hipGetLastError();
 }
 
@@ -203,8 +228,10 @@ static hipError_t run_f32(const Q4KF32Args& a, hipStream_t st) {
 }
 
 hipError_t launch_q4k_q8_gemv_f32(const uint8_t* w, const float* x, int n, uint8_t* xq_out,
-                                  float* y, int out_dim, int in_dim, hipStream_t stream) {
+                                  float* y, int out_dim, int in_dim, hipStream_t stream,
+                                  const float* r) {
   Q4KF32Args a;
+  a.r = r;
   a.w = w;
   a.x = x;
   a.xq_out = xq_out;

@@ -295,6 +295,38 @@ int rz_q4k_q8_gemv_f32(const void* w_q4k, const float* x, int n, void* x_q8, flo
                        what);
 }
 
+int rz_q4k_q8_gemv_f32_add(const void* w_q4k, const float* x, int n, void* x_q8, const float* r,
+                           float* y, int out_dim, int in_dim, void* stream) {
+  const char* what = "rz_q4k_q8_gemv_f32_add";
+  if (!w_q4k || !x || !r || !y) return fail(RZ_EINVAL, "%s: null pointer", what);
+  if (int rc = check_dim(what, "out_dim", out_dim, 1)) return rc;
+  if (int rc = check_dim(what, "in_dim", in_dim, 256)) return rc;
+  if (in_dim > 16384)
+    return fail(RZ_EDIM, "%s: in_dim=%d above the fused limit 16384", what, in_dim);
+  if (n <= 0 || n > in_dim)
+    return fail(RZ_EDIM, "%s: n=%d must satisfy 1 <= n <= in_dim=%d", what, n, in_dim);
+  if ((long long)out_dim * (in_dim / 256) * RZ_Q4K_BLOCK_BYTES > kMaxMatrixBytes)
+    return fail(RZ_EDIM, "%s: weight matrix larger than %lld bytes", what, kMaxMatrixBytes);
+  if (!aligned(w_q4k, 16)) return fail(RZ_EALIGN, "%s: w_q4k must be 16-byte aligned", what);
+  if (!aligned(x, 4) || !aligned(r, 4) || !aligned(y, 4))
+    return fail(RZ_EALIGN, "%s: x, r and y must be 4-byte aligned", what);
+  if (x_q8 && !aligned(x_q8, 16)) return fail(RZ_EALIGN, "%s: x_q8 must be 16-byte aligned", what);
+  {
+    // every workgroup reads all of x while others store y; r is read by the
+    // wave that stores the same rows, so r may be y itself
+    const Span ws{w_q4k, q4k_bytes(out_dim, in_dim)}, xs{x, 4LL * n}, qs{x_q8, q8_bytes(1, in_dim)},
+        rs{r, 4LL * out_dim}, ys{y, 4LL * out_dim};
+    if (!clear_of(ys, {ws, xs, qs}) || !clear_of(qs, {ws, xs, rs}) ||
+        !same_or_disjoint(y, r, out_dim))
+      return fail(RZ_EINVAL, "%s: y and x_q8 must not overlap w_q4k, x or each other, x_q8 must "
+                  "not overlap r, and r must be y itself or not overlap it", what);
+  }
+  return launch_status(rz::launch_q4k_q8_gemv_f32(static_cast<const uint8_t*>(w_q4k), x, n,
+                                                   static_cast<uint8_t*>(x_q8), y, out_dim,
+                                                   in_dim, static_cast<hipStream_t>(stream), r),
+                       what);
+}
+
 int rz_q4k_gemv(const void* w_q4k, const float* x, int n, float* y, int out_dim, int in_dim,
                 void* stream) {
   const char* what = "rz_q4k_gemv";

@@ -46,9 +46,11 @@ hipError_t launch_rmsnorm_q4k_q8_gemv_multi(int n_mats, const uint8_t* const* w,
                                             const float* gamma, float eps, int n,
                                             uint8_t* xq_out, int in_dim, hipStream_t stream);
 
-// Q8_1 quantize of an fp32 activation fused into the Q4_K GEMV (1 token).
+// Q8_1 quantize of an fp32 activation fused into the Q4_K GEMV (1 token); with
+// r, y = W Q8_1(x) + r (r may be y).
 hipError_t launch_q4k_q8_gemv_f32(const uint8_t* w, const float* x, int n, uint8_t* xq_out,
-                                  float* y, int out_dim, int in_dim, hipStream_t stream);
+                                  float* y, int out_dim, int in_dim, hipStream_t stream,
+                                  const float* r = nullptr);
 
 // Q4_K times an fp32 activation without Q8_1 (1 token), and the SwiGLU FFN on
 // that path (gate/up with silu*up into h, then the down GEMV over fp32 h).

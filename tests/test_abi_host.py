@@ -43,6 +43,7 @@ def test_header_declares_the_four_operations():
                  "rz_swiglu_ffn_q4k", "rz_q4k_q8_gemv_multi", "rz_rmsnorm_q8_1",
                  "rz_q4k_q8_gemv_add", "rz_swiglu_ffn_q4k_add", "rz_q4k_gemv",
                  "rz_rmsnorm_q4k_q8_gemv_multi", "rz_rmsnorm_swiglu_ffn_q4k_add",
+                 "rz_q4k_q8_gemv_f32_add",
                  "rz_swiglu_ffn_q4k_f32", "rz_lm_head_q4_0", "rz_lm_head_q4_0_workspace_bytes",
                  "rz_gelu_ffn_q4_0",
                  "rz_last_error",
@@ -440,6 +441,10 @@ _OVERLAP_CASES = [
     ("rz_q4k_q8_gemv_f32", [_b(0), _b(1), 4096, _b(2), _b(3), 4096, 4096, None], 4, 3),
     ("rz_q4k_q8_gemv_f32", [_b(0), _b(1), 4096, _b(2), _b(3), 4096, 4096, None], 4, 0),
     ("rz_q4k_gemv", [_b(0), _b(1), 4096, _b(2), 4096, 4096, None], 3, 0),
+    ("rz_q4k_q8_gemv_f32_add", [_b(0), _b(1), 4096, _b(2), _b(3), _b(4), 4096, 4096, None], 5, 1),
+    ("rz_q4k_q8_gemv_f32_add", [_b(0), _b(1), 4096, _b(2), _b(3), _b(4), 4096, 4096, None], 5, 0),
+    ("rz_q4k_q8_gemv_f32_add", [_b(0), _b(1), 4096, _b(2), _b(3), _b(4), 4096, 4096, None], 3, 4),
+    ("rz_q4k_q8_gemv_f32_add", [_b(0), _b(1), 4096, _b(2), _b(3), _b(4), 4096, 4096, None], 5, 3),
     ("rz_q4_0_gemv", [_b(0), _b(1), 0, _b(2), 4096, 1024, None], 3, 1),
     ("rz_q4_0_gemv", [_b(0), _b(1), 1, _b(2), 4096, 1024, None], 3, 0),
     ("rz_swiglu_ffn_q4k", [_b(0), _b(1), _b(2), _b(3), _b(4), _b(5), _b(6), None, 4096, 14336, None], 4, 3),
@@ -555,3 +560,46 @@ def test_rmsnorm_swiglu_ffn_add_accepts(lib):
                         ("rz_rmsnorm_swiglu_ffn_q4k_add", _nsw(gu=None)),
                         ("rz_rmsnorm_swiglu_ffn_q4k_add", _nsw(hidden=16384, inter=256))])
     assert [rc for rc, _ in res] == [rz.RZ_ELAUNCH] * 4, res
+
+
+# rz_q4k_q8_gemv_f32_add(w, x, n, x_q8, r, y, out_dim, in_dim, stream)
+_FA = [_b(0), _b(1), 4096, None, _b(3), _b(4), 14336, 4096, None]
+
+
+def _fa(**kw):
+    names = ["w", "x", "n", "xq", "r", "y", "out", "ind", "s"]
+    a = list(_FA)
+    for k, v in kw.items():
+        a[names.index(k)] = v
+    return a
+
+
+@pytest.mark.parametrize("args,code", [
+    (_fa(w=None), rz.RZ_EINVAL),
+    (_fa(x=None), rz.RZ_EINVAL),
+    (_fa(r=None), rz.RZ_EINVAL),
+    (_fa(y=None), rz.RZ_EINVAL),
+    (_fa(n=0), rz.RZ_EDIM),
+    (_fa(n=4097), rz.RZ_EDIM),
+    (_fa(ind=4000), rz.RZ_EDIM),
+    (_fa(ind=20480, n=20480), rz.RZ_EDIM),            # above the fused limit
+    (_fa(out=0), rz.RZ_EDIM),
+    (_fa(w=_b(0) + 8), rz.RZ_EALIGN),
+    (_fa(x=_b(1) + 2), rz.RZ_EALIGN),
+    (_fa(r=_b(3) + 2), rz.RZ_EALIGN),
+    (_fa(y=_b(4) + 2), rz.RZ_EALIGN),
+    (_fa(xq=_b(2) + 8), rz.RZ_EALIGN),
+    (_fa(y=_b(4), r=_b(4) + 4), rz.RZ_EINVAL),        # r overlaps y without being y
+    (_fa(y=_b(1) + 64), rz.RZ_EINVAL),                # y inside x
+    (_fa(xq=_b(3) + 16), rz.RZ_EINVAL),               # x_q8 on r
+])
+def test_q4k_q8_gemv_f32_add_rejects(lib, args, code):
+    assert _rc("rz_q4k_q8_gemv_f32_add", *args) == code
+    assert _rc.last.startswith("rz_q4k_q8_gemv_f32_add")
+
+
+def test_q4k_q8_gemv_f32_add_accepts_in_place(lib):
+    res = run_isolated([("rz_q4k_q8_gemv_f32_add", _fa()),
+                        ("rz_q4k_q8_gemv_f32_add", _fa(r=_b(4))),                   # r is y
+                        ("rz_q4k_q8_gemv_f32_add", _fa(xq=_b(2), n=4000))])
+    assert [rc for rc, _ in res] == [rz.RZ_ELAUNCH] * 3, res

@@ -1325,8 +1325,9 @@ def test_graph_replays_match_eager(fused):
     eager work and synchronisations between replays, gives every replay the
     bytes of the eager run.  Nothing in the library records memsets or
     allocations, so the graph has kernel nodes only.  `fused`: the RMSNorm runs
-    inside the Q/K/V launch and the gate/up launch; every output but the
-    shared Q8_1 buffer then also equals the unfused sequence's bytes."""
+    inside the Q/K/V launch and the gate/up launch, and the O projection
+    quantizes its input itself; every output but the shared Q8_1 buffer then
+    also equals the unfused sequence's bytes."""
     import torch
     banner("graph replays", "fused" if fused else "separate")
     H, KV, I, V = 4096, 1024, 2816, 5000      # two-slot rows: the LDS-staged activation path
@@ -1352,14 +1353,18 @@ def test_graph_replays_match_eager(fused):
     def layer(fused):
         hidden.copy_(x0)
         if fused:
-            rz.rz_rmsnorm_q4k_q8_gemv_multi([wq, wk, wv], hidden, gam1, 1e-5, H, None, [q, k_, v],
+            # the Q8_1 side output keeps xq an output of the fused sequence too
+            rz.rz_rmsnorm_q4k_q8_gemv_multi([wq, wk, wv], hidden, gam1, 1e-5, H, xq, [q, k_, v],
                                             [H, KV, KV], H)
         else:
             rz.rz_rmsnorm_q8_1(hidden, gam1, 1e-5, H, H, 1, None, xq)
             rz.rz_q4k_q8_gemv_multi([wq, wk, wv], xq, [q, k_, v], [H, KV, KV], H)
         # the attention output stands in as q; quantize it for the O projection
-        rz.rz_q8_1_quantize(q, H, H, 1, xq)
-        rz.rz_q4k_q8_gemv_add(wo, xq, hidden, hidden, H, H, 1)
+        if fused:
+            rz.rz_q4k_q8_gemv_f32_add(wo, q, H, None, hidden, hidden, H, H)
+        else:
+            rz.rz_q8_1_quantize(q, H, H, 1, xq)
+            rz.rz_q4k_q8_gemv_add(wo, xq, hidden, hidden, H, H, 1)
         if fused:
             rz.rz_rmsnorm_swiglu_ffn_q4k_add(wg, wu, wd, hidden, gam2, 1e-5, h, hq, hidden, None,
                                              H, I)
@@ -1466,3 +1471,33 @@ def test_rmsnorm_swiglu_ffn_add_bit_identical(hidden, inter):
     y2 = empty_f32(hidden)
     rz.rz_rmsnorm_swiglu_ffn_q4k_add(*ws[:3], xd, gd, 1e-5, h, hq, y2, None, hidden, inter)
     assert np.array_equal(bits(y2), bits(y_ref)), "without gu"
+
+
+@pytest.mark.parametrize("out_dim,n,in_dim", [
+    (4096, 4096, 4096),      # the O projection of the attention workload
+    (14336, 4096, 4096),
+    (300, 1000, 1024),       # ragged n, ragged rows
+    (65, 16384, 16384),
+])
+def test_q4k_q8_gemv_f32_add_bit_identical(out_dim, n, in_dim):
+    """Quantize + GEMV + residual in one launch equals rz_q8_1_quantize followed
+    by rz_q4k_q8_gemv_add bit for bit: y out of place and in place (r is y),
+    and the Q8_1 side output."""
+    banner("f32 add", out_dim, n, in_dim)
+    x = synth.activation(synth.rng(85, in_dim), n)
+    r = synth.activation(synth.rng(85, 1), out_dim)
+    w = dev_bytes(synth.q4k_weights(synth.rng(86, out_dim), out_dim, in_dim))
+    xd = dev_f32(x)
+    xq_ref = empty_bytes(rz.q8_1_nbytes(in_dim))
+    rz.rz_q8_1_quantize(xd, n, in_dim, 1, xq_ref)
+    y_ref = empty_f32(out_dim)
+    rz.rz_q4k_q8_gemv_add(w, xq_ref, dev_f32(r), y_ref, out_dim, in_dim, 1)
+    bits = lambda t: host(t).view(np.uint32)
+    xq = empty_bytes(rz.q8_1_nbytes(in_dim))
+    y = empty_f32(out_dim)
+    rz.rz_q4k_q8_gemv_f32_add(w, xd, n, xq, dev_f32(r), y, out_dim, in_dim)
+    assert np.array_equal(host(xq), host(xq_ref)), "Q8_1 side output"
+    assert np.array_equal(bits(y), bits(y_ref)), "out of place"
+    yr = dev_f32(r)
+    rz.rz_q4k_q8_gemv_f32_add(w, xd, n, None, yr, yr, out_dim, in_dim)
+    assert np.array_equal(bits(yr), bits(y_ref)), "in place"
