@@ -364,7 +364,8 @@ int rz_swiglu_ffn_q4k_f32(const void* w_gate, const void* w_up, const void* w_do
   // x is read by the first kernel while it writes h and gu; h by the second while it writes y
   if (!disjoint(x, 4LL * hidden_dim, h, 4LL * inter_dim) ||
       (gu && (!disjoint(x, 4LL * hidden_dim, gu, 8LL * inter_dim) ||
-              !disjoint(h, 4LL * inter_dim, gu, 8LL * inter_dim))) ||
+              !disjoint(h, 4LL * inter_dim, gu, 8LL * inter_dim) ||
+              !disjoint(y, 4LL * hidden_dim, gu, 8LL * inter_dim))) ||
       !disjoint(h, 4LL * inter_dim, y, 4LL * hidden_dim))
     return fail(RZ_EINVAL, "%s: x, h, gu and y must not overlap (x and y may)", what);
   {
@@ -431,8 +432,8 @@ int swiglu_ffn(const char* what, const void* w_gate, const void* w_up, const voi
     const Span xs{x_q8, q8_bytes(1, hidden_dim)}, hs{h, 4LL * inter_dim},
         hq{h_q8, q8_bytes(1, inter_dim)}, gs{gu, 8LL * inter_dim}, ys{y, 4LL * hidden_dim},
         wg{w_gate, wb}, wu{w_up, wb}, wd{w_down, db};
-    if (!clear_of(hs, {xs, hq, gs, wg, wu, wd}) || !clear_of(hq, {xs, gs, ys, wg, wu, wd}) ||
-        !clear_of(gs, {xs, wg, wu, wd}) || !clear_of(ys, {wd, wg, wu}))
+    if (!clear_of(hs, {xs, hq, gs, ys, wg, wu, wd}) || !clear_of(hq, {xs, gs, ys, wg, wu, wd}) ||
+        !clear_of(gs, {xs, ys, wg, wu, wd}) || !clear_of(ys, {wd, wg, wu}))
       return fail(RZ_EINVAL, "%s: h, h_q8, gu and y must not overlap x_q8, the weights or each "
                   "other (y may overlap x_q8)", what);
   }
@@ -573,8 +574,9 @@ int rz_rmsnorm_swiglu_ffn_q4k_add(const void* w_gate, const void* w_up, const vo
   const Span xs{x, 4LL * hidden_dim}, gs{gamma, 4LL * hidden_dim}, hs{h, 4LL * inter_dim},
       hq{h_q8, q8_bytes(1, inter_dim)}, us{gu, 8LL * inter_dim}, ys{y, 4LL * hidden_dim},
       wg{w_gate, wb}, wu{w_up, wb}, wd{w_down, db};
-  if (!clear_of(hs, {xs, gs, hq, us, wg, wu, wd}) || !clear_of(hq, {xs, gs, us, ys, wg, wu, wd}) ||
-      !clear_of(us, {xs, gs, wg, wu, wd}) || !clear_of(ys, {gs, wg, wu, wd}) ||
+  if (!clear_of(hs, {xs, gs, hq, us, ys, wg, wu, wd}) ||
+      !clear_of(hq, {xs, gs, us, ys, wg, wu, wd}) || !clear_of(us, {xs, gs, ys, wg, wu, wd}) ||
+      !clear_of(ys, {gs, wg, wu, wd}) ||
       !same_or_disjoint(y, x, hidden_dim))
     return fail(RZ_EINVAL, "%s: h, h_q8, gu and y must not overlap x, gamma, the weights or each "
                 "other (y may be x itself)", what);

@@ -450,7 +450,10 @@ _OVERLAP_CASES = [
     ("rz_swiglu_ffn_q4k", [_b(0), _b(1), _b(2), _b(3), _b(4), _b(5), _b(6), None, 4096, 14336, None], 4, 3),
     ("rz_swiglu_ffn_q4k", [_b(0), _b(1), _b(2), _b(3), _b(4), _b(5), _b(6), None, 4096, 14336, None], 6, 5),
     ("rz_swiglu_ffn_q4k", [_b(0), _b(1), _b(2), _b(3), _b(4), _b(5), _b(6), None, 4096, 14336, None], 5, 1),
+    ("rz_swiglu_ffn_q4k", [_b(0), _b(1), _b(2), _b(3), _b(4), _b(5), _b(6), _b(7), 4096, 14336, None], 6, 4),
+    ("rz_swiglu_ffn_q4k", [_b(0), _b(1), _b(2), _b(3), _b(4), _b(5), _b(6), _b(7), 4096, 14336, None], 6, 7),
     ("rz_swiglu_ffn_q4k_f32", [_b(0), _b(1), _b(2), _b(3), _b(4), _b(5), None, 4096, 14336, None], 5, 2),
+    ("rz_swiglu_ffn_q4k_f32", [_b(0), _b(1), _b(2), _b(3), _b(4), _b(5), _b(6), 4096, 14336, None], 5, 6),
     ("rz_gelu_ffn_q4_0", [_b(0), _b(1), _b(2), None, None, _b(3), _b(4), 2560, 10240, None], 5, 0),
     ("rz_gelu_ffn_q4_0", [_b(0), _b(1), _b(2), None, None, _b(3), _b(4), 2560, 10240, None], 6, 1),
 ]
@@ -546,6 +549,8 @@ def _nsw(**kw):
     (_nsw(h=_b(1) + 4096), rz.RZ_EINVAL),              # h inside w_up
     (_nsw(hq=_b(4) + 16), rz.RZ_EINVAL),               # h_q8 on gamma
     (_nsw(gu=_b(5) + 4 * 14336 - 4), rz.RZ_EINVAL),    # gu meets h
+    (_nsw(y=_b(5) + 64), rz.RZ_EINVAL),                # y inside h
+    (_nsw(y=_b(8) + 4 * 14336), rz.RZ_EINVAL),         # y inside gu's up half
 ])
 def test_rmsnorm_swiglu_ffn_add_rejects(lib, args, code):
     assert _rc("rz_rmsnorm_swiglu_ffn_q4k_add", *args) == code
