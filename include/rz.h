@@ -254,7 +254,8 @@ int rz_q4k_gemv(const void* w_q4k, const float* x, int n, float* y, int out_dim,
  *   gu            optional out (NULL to skip): fp32 [2][inter_dim], g then u
  *   hidden_dim, inter_dim  multiples of 256; each matrix < 2 GiB
  * Two kernels run in order on `stream`.  x, h and gu must not overlap each
- * other, nor h and y.  Errors: RZ_EINVAL, RZ_EDIM, RZ_EALIGN, RZ_ELAUNCH. */
+ * other, nor y h or gu (y may overlap x).  Errors: RZ_EINVAL, RZ_EDIM,
+ * RZ_EALIGN, RZ_ELAUNCH. */
 int rz_swiglu_ffn_q4k_f32(const void* w_gate, const void* w_up, const void* w_down,
                           const float* x, float* h, float* y, float* gu, int hidden_dim,
                           int inter_dim, void* stream);
@@ -347,7 +348,9 @@ int rz_gelu_ffn_q4_0(const void* w_up, const void* w_down, const float* x, const
  *                 gate/up kernel keeps a row's activation in registers);
  *                 each matrix < 2 GiB
  * Two kernels run in order on `stream`; h and h_q8 are written by the first
- * and read by the second.  Errors: RZ_EINVAL, RZ_EDIM, RZ_EALIGN, RZ_ELAUNCH. */
+ * and read by the second.  h, h_q8, gu and y must not overlap x_q8, the
+ * weights or each other (y may overlap x_q8).  Errors: RZ_EINVAL (also
+ * overlaps), RZ_EDIM, RZ_EALIGN, RZ_ELAUNCH. */
 int rz_swiglu_ffn_q4k(const void* w_gate, const void* w_up, const void* w_down,
                       const void* x_q8, float* h, void* h_q8, float* y,
                       float* gu, int hidden_dim, int inter_dim, void* stream);
