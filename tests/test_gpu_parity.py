@@ -1501,3 +1501,50 @@ def test_q4k_q8_gemv_f32_add_bit_identical(out_dim, n, in_dim):
     yr = dev_f32(r)
     rz.rz_q4k_q8_gemv_f32_add(w, xd, n, None, yr, yr, out_dim, in_dim)
     assert np.array_equal(bits(yr), bits(y_ref)), "in place"
+
+
+def test_minimum_alignments_fused_entries():
+    """The RMSNorm-prologue entries and quantize + GEMV + residual on buffers
+    at exactly the alignments include/rz.h requires (Q4_K and Q8_1 16 bytes,
+    fp32 4) give the same bytes as on 256-byte aligned buffers."""
+    banner("minimum alignments, fused entries")
+    H, I = 1024, 2816
+    gam = synth.norm_weights(synth.rng(76, 2), H)
+    shapes = [(300, H), (64, H)]
+    ws = [synth.q4k_weights(synth.rng(76, 10 + k), o, H) for k, (o, _) in enumerate(shapes)]
+    for n in (H, H - 3):           # 16-byte and dword activation loads
+        x = synth.activation(synth.rng(76, n), n)
+        res = []
+        for sh in (0, 1):
+            ys = [_at(o, 4 * sh) for o, _ in shapes]
+            q = _at(H // 32 * 40, 16 * sh, "u8")
+            rz.rz_rmsnorm_q4k_q8_gemv_multi([_at(w_, 16 * sh, "u8") for w_ in ws], _at(x, 4 * sh),
+                                            _at(gam[:n], 4 * sh), 1e-5, n, q, ys,
+                                            [o for o, _ in shapes], H)
+            res.append([_bits(t) for t in ys + [q]])
+        for k, (a_, b_) in enumerate(zip(*res)):
+            assert np.array_equal(a_, b_), "rmsnorm multi n %d output %d" % (n, k)
+    wg, wu = (synth.q4k_weights(synth.rng(77, k), I, H) for k in (1, 2))
+    wd = synth.q4k_weights(synth.rng(77, 3), H, I)
+    x = synth.activation(synth.rng(77, 0), H)
+    res = []
+    for sh in (0, 1):
+        h, hq, y, gu = _at(I, 4 * sh), _at(I // 32 * 40, 16 * sh, "u8"), _at(H, 4 * sh), _at(2 * I, 4 * sh)
+        rz.rz_rmsnorm_swiglu_ffn_q4k_add(_at(wg, 16 * sh, "u8"), _at(wu, 16 * sh, "u8"),
+                                         _at(wd, 16 * sh, "u8"), _at(x, 4 * sh), _at(gam, 4 * sh),
+                                         1e-5, h, hq, y, gu, H, I)
+        res.append([_bits(t) for t in (h, hq, y, gu)])
+    for k, (a_, b_) in enumerate(zip(*res)):
+        assert np.array_equal(a_, b_), "rmsnorm swiglu output %d" % k
+    w = synth.q4k_weights(synth.rng(78, 1), 500, 4096)
+    r = synth.activation(synth.rng(78, 2), 500)
+    for n in (4096, 4093):
+        xf = synth.activation(synth.rng(78, n), n)
+        res = []
+        for sh in (0, 1):
+            y, q = _at(500, 4 * sh), _at(128 * 40, 16 * sh, "u8")
+            rz.rz_q4k_q8_gemv_f32_add(_at(w, 16 * sh, "u8"), _at(xf, 4 * sh), n, q, _at(r, 4 * sh), y,
+                                      500, 4096)
+            res.append([_bits(y), _bits(q)])
+        for k, (a_, b_) in enumerate(zip(*res)):
+            assert np.array_equal(a_, b_), "f32 add n %d output %d" % (n, k)
