@@ -534,7 +534,9 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    # ~20 ms of untimed step launches first, so the clocks have settled when the
+    # (1.6 ms) timed replay starts
+    ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--only", choices=sorted(ONLY), default=None,
