@@ -551,7 +551,8 @@ def main() -> int:
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this path runs on one GPU; --gpus %d is not supported "
-              "(rows shard without communication; see the design notes)" % args.gpus,
+              "(output rows shard across GPUs without communication, so one GPU's share is "
+              "what is measured)" % args.gpus,
               file=sys.stderr)
         return 2
 
