@@ -46,7 +46,7 @@ from .q4k import (q4k_fields, q4k_unpack_scales, dequantize_q4k,
                   gemv_q4k_q8_def, gemv_q4k_q8_int, gemv_q4k_f32)
 from .q4_0 import (q4_0_fields, dequantize_q4_0, gemv_q4_0_f32,
                    gemv_q4_0_q8_int)
-from .swiglu import (silu, silu_grad, swiglu, ffn_swiglu_q4k, ffn_swiglu_q4k_f32,
+from .swiglu import (silu, silu_grad, silu_curv, swiglu, ffn_swiglu_q4k, ffn_swiglu_q4k_f32,
                      h_tolerance)
 from .tolerance import gemv_tolerance, GEMV_REL, GEMV_ABS
 from .norm import rmsnorm, rmsnorm_tolerance, residual_add
@@ -59,7 +59,7 @@ __all__ = [
     "q4k_fields", "q4k_unpack_scales", "dequantize_q4k", "gemv_q4k_q8_def",
     "gemv_q4k_q8_int", "gemv_q4k_f32",
     "q4_0_fields", "dequantize_q4_0", "gemv_q4_0_f32", "gemv_q4_0_q8_int",
-    "silu", "silu_grad", "swiglu", "ffn_swiglu_q4k", "ffn_swiglu_q4k_f32", "h_tolerance",
+    "silu", "silu_grad", "silu_curv", "swiglu", "ffn_swiglu_q4k", "ffn_swiglu_q4k_f32", "h_tolerance",
     "gemv_tolerance", "GEMV_REL", "GEMV_ABS",
     "rmsnorm", "rmsnorm_tolerance", "residual_add",
     "lm_head_q4_0", "argmax_first",

@@ -42,9 +42,34 @@ def silu_grad(g):
     return sig * (1.0 + g * (1.0 - sig))
 
 
-# sup |silu'| and sup |silu''| over the reals (silu'' peaks at g = 0 with 1/2).
+# sup |silu'| and sup |silu''| over the reals (silu'' peaks at g = 0 with 1/2),
+# and the Lipschitz constant of A(g) = 2 - g tanh(g/2), the second factor of
+# silu'' = sigma'(g) A(g) (sup |A'| = 1.19968, near g = -2.4); the pins check
+# them on a dense grid.
 SILU_GRAD_MAX = 1.0999
 SILU_CURV_MAX = 0.5
+SILU_A_LIP = 1.2
+
+
+def _sigma_prime(g):
+    """sigma'(g) = e^-|g| / (1 + e^-|g|)^2, without cancellation for large |g|."""
+    e = np.exp(-np.abs(np.asarray(g, np.float64)))
+    return e / (1.0 + e) ** 2
+
+
+def silu_curv(g):
+    """d^2 silu / d g^2 = sigma'(g) * (2 - g tanh(g/2))  (1 - 2 sigma(g) = -tanh(g/2))."""
+    g = np.asarray(g, np.float64)
+    return _sigma_prime(g) * (2.0 - g * np.tanh(0.5 * g))
+
+
+def silu_curv_bound(g, r):
+    """An upper bound on |silu''| over [g - r, g + r]: log sigma' has slope at
+    most 1 in magnitude and A(g) = 2 - g tanh(g/2) is SILU_A_LIP-Lipschitz, so
+    |silu''(xi)| <= sigma'(g) e^r (|A(g)| + SILU_A_LIP r)."""
+    g = np.asarray(g, np.float64)
+    r = np.asarray(r, np.float64)
+    return _sigma_prime(g) * np.exp(r) * (np.abs(2.0 - g * np.tanh(0.5 * g)) + SILU_A_LIP * r)
 
 
 def swiglu(g, u):
@@ -56,14 +81,20 @@ def h_tolerance(g, u, tol_g, tol_u, h_ref):
     """Bound on |h_kernel - h_ref| when the kernel's g and u are within
     ``tol_g`` / ``tol_u`` of the oracle's and h is formed in fp32.
 
-    First-order propagation through silu(g) * u, the second-order terms of the
-    Taylor remainder, and a fp32 budget of 8 ulp for exp, the division and the
-    two products (device exp is not bit-reproducible on the host).
+    h = silu(g) * u is linear in u, so its change under (dg, du) is exactly
+      silu'(g) u dg + silu(g) du + silu'(g) dg du + silu''(xi) dg^2 (u + du) / 2
+    for some xi within dg of g.  Each term is bounded here, the curvature by
+    ``silu_curv_bound`` over [g - tol_g, g + tol_g], and a fp32 budget of 8 ulp
+    for exp, the division and the two products is added (device exp is not
+    bit-reproducible on the host).
     """
     g = np.asarray(g, np.float64)
     u = np.asarray(u, np.float64)
-    first = np.abs(silu_grad(g) * u) * tol_g + np.abs(silu(g)) * tol_u
-    second = 0.5 * SILU_CURV_MAX * tol_g ** 2 * np.abs(u) + SILU_GRAD_MAX * tol_g * tol_u
+    tol_g = np.asarray(tol_g, np.float64)
+    tol_u = np.asarray(tol_u, np.float64)
+    d1 = np.abs(silu_grad(g))
+    first = d1 * np.abs(u) * tol_g + np.abs(silu(g)) * tol_u
+    second = d1 * tol_g * tol_u + 0.5 * silu_curv_bound(g, tol_g) * tol_g ** 2 * (np.abs(u) + tol_u)
     rounding = 8.0 * 2.0 ** -24 * np.abs(h_ref) + 1e-6
     return first + second + rounding
 

@@ -456,6 +456,34 @@ def test_silu_grad_by_finite_difference():
     assert np.max(np.abs(curv)) <= SILU_CURV_MAX + 1e-6
 
 
+def test_silu_curvature_by_finite_difference_and_bounds():
+    """silu'' against a central difference of silu', at the textbook point
+    silu''(0) = 1/2 and on a grid, also where sigma(g) rounds to 1; its sup and
+    the Lipschitz constant of its second factor hold on a dense grid; and the
+    interval bound used by the h bound is above a brute-force maximum of
+    |silu''| over random intervals (and within a hair of it)."""
+    from oracle.swiglu import SILU_A_LIP, SILU_CURV_MAX, silu_curv_bound
+    assert oracle.silu_curv(0.0) == 0.5
+    g = np.linspace(-40, 40, 161)
+    h = 1e-5
+    fd = (oracle.silu_grad(g + h) - oracle.silu_grad(g - h)) / (2 * h)
+    assert np.allclose(oracle.silu_curv(g), fd, rtol=1e-5, atol=1e-9)
+    dense = np.linspace(-80, 80, 1600001)
+    assert np.max(np.abs(oracle.silu_curv(dense))) <= SILU_CURV_MAX
+    a = 2.0 - dense * np.tanh(0.5 * dense)
+    lip = np.max(np.abs(np.gradient(a, dense)))
+    assert 1.19 < lip <= SILU_A_LIP
+    rng = np.random.default_rng(3)
+    gg = rng.uniform(-60, 60, 4000)
+    r = 10.0 ** rng.uniform(-6, 0.3, 4000)
+    xs = gg[:, None] + r[:, None] * np.linspace(-1, 1, 401)[None, :]
+    sup = np.max(np.abs(oracle.silu_curv(xs)), axis=1)
+    bound = silu_curv_bound(gg, r)
+    assert np.all(sup <= bound * (1 + 1e-12))
+    assert np.median(sup / bound) > 0.5
+
+
+
 def _uniform_q4k(nsb, rows, qn, S, M, d=0.0078125, dmin=0.001953125):
     sb = _f16le(d) + _f16le(dmin) + _pack_uniform_scales(S, M) + bytes([qn | (qn << 4)] * 128)
     return np.frombuffer(sb * (nsb * rows), np.uint8).reshape(rows, nsb, 144).copy()
@@ -520,6 +548,64 @@ def test_h_tolerance_covers_perturbations():
     for sg, su in ((1, 1), (1, -1), (-1, 1), (-1, -1)):
         hp = oracle.swiglu(g + sg * tg, u + su * tu)
         assert np.all(np.abs(hp - h) <= tol)
+
+
+def _swiglu_gpu_scale():
+    """g, u and their GEMV bounds at the scale of the 4096 -> 14336 gate/up
+    projections the GPU test checks (N(0, 1) activation through Q4_K weights
+    drawn as the workload draws them; 512 rows keep this fast)."""
+    import synth
+    wg = synth.q4k_weights(synth.rng(2, synth.T_W0), 512, 4096)
+    wu = synth.q4k_weights(synth.rng(2, synth.T_W0 + 1), 512, 4096)
+    xq = oracle.quantize_q8_1(synth.activation(synth.rng(2, synth.T_ACT), 4096))
+    g, tg = oracle.gemv_q4k_q8_int(wg, xq)
+    u, tu = oracle.gemv_q4k_q8_int(wu, xq)
+    return g, u, oracle.gemv_tolerance(tg), oracle.gemv_tolerance(tu)
+
+
+def test_h_tolerance_rejects_planted_mistakes():
+    """At the GPU test's scales the bound separates the SwiGLU definition from
+    plausible mistakes in it: SiLU on the up projection instead of the gate,
+    the SiLU dropped (h = g * u), SiLU with exp(+g), the up factor dropped.
+    Some rows cannot show a mistake (silu(x) is about x for large positive x
+    and about 0 for large negative x, so with g and u both large and of one
+    sign the swap of g and u changes nothing), but each planted h falls
+    outside the bound on more than a quarter of the rows, so the GPU check
+    (every row within the bound) fails on any of them."""
+    g, u, tg, tu = _swiglu_gpu_scale()
+    h = oracle.swiglu(g, u)
+    tol = oracle.h_tolerance(g, u, tg, tu, h)
+    with np.errstate(over="ignore"):
+        planted = {
+            "silu on up": oracle.silu(u) * g,
+            "no silu": g * u,
+            "silu with exp(+g)": g / (1.0 + np.exp(g)) * u,
+            "up dropped": oracle.silu(g),
+        }
+    for name, hp in planted.items():
+        outside = np.abs(hp - h) > tol
+        assert outside.mean() > 0.25, "%s: only %.3f of rows outside" % (name, outside.mean())
+
+
+def test_h_tolerance_is_not_loose():
+    """The bound stays within a small factor of what it bounds: the largest
+    change of silu(g) * u when g and u move by their GEMV bounds (all four sign
+    combinations) plus the fp32 rounding allowance, also where silu saturates
+    (there the curvature bound decays with sigma'); a bound ten times looser
+    fails this."""
+    g, u, tg, tu = _swiglu_gpu_scale()
+    h = oracle.swiglu(g, u)
+    tol = oracle.h_tolerance(g, u, tg, tu, h)
+    worst = np.zeros_like(h)
+    for sg, su in ((1, 1), (1, -1), (-1, 1), (-1, -1)):
+        worst = np.maximum(worst, np.abs(oracle.swiglu(g + sg * tg, u + su * tu) - h))
+    worst = worst + 8.0 * 2.0 ** -24 * np.abs(h) + 1e-6
+    # where silu is linear the bound equals the change exactly, up to float64 rounding
+    assert np.all(tol >= worst * (1.0 - 1e-9))
+    ratio = tol / worst
+    assert np.median(ratio) < 1.5 and np.percentile(ratio, 99) < 3.0, (np.median(ratio),
+                                                                      np.percentile(ratio, 99))
+    assert np.median(10 * tol / worst) > 3.0       # what a ten-times looser bound would give
 
 
 # ------------------------------------------------------------------ RMSNorm, residual
@@ -711,3 +797,85 @@ def test_ffn_gelu_chain_closed_form():
     assert np.allclose(st["y"], w * h32.astype(np.float64).sum() + db, rtol=1e-13, atol=1e-12)
     # GELU of (0 + bias) differs from GELU(0) + bias
     assert not np.allclose(oracle.gelu(ub), ub)
+
+
+def _gelu_gpu_scale():
+    """The GELU FFN's up projection at the phi-2 size the GPU test checks
+    (2560 -> 10240, Q4_0 weights, N(0, 1) activation and bias; 1024 rows)."""
+    import synth
+    w = synth.q4_0_weights(synth.rng(5, 1), 1024, 2560)
+    x = synth.activation(synth.rng(5, synth.T_ACT), 2560)
+    b = synth.activation(synth.rng(5, 7), 1024).astype(np.float64)
+    u0, tu = oracle.gemv_q4_0_f32(w, x)
+    return u0, b, u0 + b, oracle.gemv_tolerance(tu + np.abs(b))
+
+
+def _gelu_device_form_f32(u):
+    """GELU the way the device evaluates it, in fp32 throughout:
+    u / (1 + exp(-2 sqrt(2/pi) (u + 0.044715 u^3)))."""
+    u = np.asarray(u, np.float32)
+    k2 = np.float32(2.0 * np.sqrt(2.0 / np.pi))
+    c = np.float32(0.044715)
+    with np.errstate(over="ignore"):
+        z = (-k2 * (u + c * u * u * u)).astype(np.float32)
+        return (u / (np.float32(1.0) + np.exp(z).astype(np.float32))).astype(np.float32)
+
+
+def test_gelu_h_tolerance_covers_device_form_and_perturbations():
+    """The bound covers (a) an fp32 evaluation of the device's sigmoid form of
+    GELU on the oracle's exact pre-activations, and (b) GELU of the
+    pre-activation moved by its GEMV bound either way."""
+    _, _, u, tol_u = _gelu_gpu_scale()
+    h = oracle.gelu(u)
+    tol = oracle.gelu_h_tolerance(u, tol_u, h)
+    dev = _gelu_device_form_f32(u.astype(np.float32)).astype(np.float64)
+    # the fp32 cast of u is itself a perturbation well inside tol_u
+    assert np.all(np.abs(u.astype(np.float32).astype(np.float64) - u) <= tol_u)
+    assert np.all(np.abs(dev - h) <= tol)
+    for sgn in (1.0, -1.0):
+        assert np.all(np.abs(oracle.gelu(u + sgn * tol_u) - h) <= tol)
+
+
+def test_gelu_h_tolerance_rejects_planted_mistakes():
+    """At the GPU test's scales the bound rejects plausible mistakes in the GELU
+    stage: the cubic term dropped, its coefficient off by a decimal place, 2/pi
+    for sqrt(2/pi), the bias added after GELU instead of before, and the exact
+    erf form of GELU in place of the tanh form taken here.  Each falls outside
+    the bound on more than a quarter of the rows (near u = 0 and for large |u|
+    the forms agree), so the GPU check (every row within the bound) fails on
+    any of them."""
+    from scipy.special import erf
+    u0, b, u, tol_u = _gelu_gpu_scale()
+    h = oracle.gelu(u)
+    tol = oracle.gelu_h_tolerance(u, tol_u, h)
+    k = np.sqrt(2.0 / np.pi)
+
+    def tanh_gelu(v, kk, cc):
+        return 0.5 * v * (1.0 + np.tanh(kk * (v + cc * v ** 3)))
+    planted = {
+        "cubic term dropped": tanh_gelu(u, k, 0.0),
+        "0.44715 for 0.044715": tanh_gelu(u, k, 0.44715),
+        "2/pi for sqrt(2/pi)": tanh_gelu(u, 2.0 / np.pi, 0.044715),
+        "bias after GELU": oracle.gelu(u0) + b,
+        "erf form": 0.5 * u * (1.0 + erf(u / np.sqrt(2.0))),
+    }
+    for name, hp in planted.items():
+        outside = np.abs(hp - h) > tol
+        assert outside.mean() > 0.25, "%s: only %.3f of rows outside" % (name, outside.mean())
+
+
+def test_gelu_h_tolerance_is_not_loose():
+    """The bound stays within a small factor of the change of GELU over the
+    pre-activation's GEMV bound plus the fp32 rounding allowance (a bound ten
+    times looser fails this), away from the stationary point of GELU near
+    u = -0.75 where its slope vanishes."""
+    _, _, u, tol_u = _gelu_gpu_scale()
+    h = oracle.gelu(u)
+    tol = oracle.gelu_h_tolerance(u, tol_u, h)
+    worst = np.maximum(np.abs(oracle.gelu(u + tol_u) - h), np.abs(oracle.gelu(u - tol_u) - h))
+    worst = worst + 8.0 * 2.0 ** -24 * np.abs(h) + 1e-6
+    assert np.all(tol >= worst * (1.0 - 1e-9))
+    away = np.abs(oracle.gelu_grad(u)) > 0.05
+    ratio = tol[away] / worst[away]
+    assert np.median(ratio) < 1.5 and np.percentile(ratio, 99) < 3.0, (np.median(ratio),
+                                                                      np.percentile(ratio, 99))
