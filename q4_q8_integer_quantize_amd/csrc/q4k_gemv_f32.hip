@@ -191,6 +191,8 @@ __global__ __launch_bounds__(64 * WPB) void q4k_gemv_f32_kernel(Q4KF32Args a) {
 }
 
 constexpr int kF32TilesInFlight = 2;
+// About one wave per SIMD: 256 CUs x 4 SIMDs.  Each workgroup quantizes the
+// whole activation, so the grid stays near one 4-wave workgroup per CU.
 constexpr long kF32TargetWaves = 1024;
 
 template <int TPR, int S, int G, bool XV, int WPB = 4>
@@ -209,6 +211,11 @@ static hipError_t launch_f32_g(const Q4KF32Args& a, long groups, hipStream_t st)
   return hipGetLastError();
 }
 
+// G (row groups a wave) is the smallest count that keeps the grid within the
+// target, not rounded to a power of two: 14336 rows are 7168 groups, so G = 7
+// gives 256 workgroups, one for every CU, where G = 8 left 32 CUs without work
+// (measured on the 4096 -> 14336 step: 7.40 against 7.57 us, kernel trace
+// 7.59 against 7.97 us).
 template <int TPR, int S, bool XV>
 static hipError_t run_f32_x(const Q4KF32Args& a, hipStream_t st) {
   constexpr int R = S <= 2 ? 2 : 1;
@@ -216,10 +223,16 @@ static hipError_t run_f32_x(const Q4KF32Args& a, hipStream_t st) {
   const long rows_per_group = (long)RW * R;
   const long groups = (a.out_dim + rows_per_group - 1) / rows_per_group;
   const long per_wave = (groups + kF32TargetWaves - 1) / kF32TargetWaves;
-  if (per_wave <= 1) return launch_f32_g<TPR, S, 1, XV>(a, groups, st);
-  if (per_wave <= 2) return launch_f32_g<TPR, S, 2, XV>(a, groups, st);
-  if (per_wave <= 4) return launch_f32_g<TPR, S, 4, XV>(a, groups, st);
-  return launch_f32_g<TPR, S, 8, XV>(a, groups, st);
+  switch (per_wave) {
+    case 1: return launch_f32_g<TPR, S, 1, XV>(a, groups, st);
+    case 2: return launch_f32_g<TPR, S, 2, XV>(a, groups, st);
+    case 3: return launch_f32_g<TPR, S, 3, XV>(a, groups, st);
+    case 4: return launch_f32_g<TPR, S, 4, XV>(a, groups, st);
+    case 5: return launch_f32_g<TPR, S, 5, XV>(a, groups, st);
+    case 6: return launch_f32_g<TPR, S, 6, XV>(a, groups, st);
+    case 7: return launch_f32_g<TPR, S, 7, XV>(a, groups, st);
+    default: return launch_f32_g<TPR, S, 8, XV>(a, groups, st);
+  }
 }
 
 template <int TPR, int S>
