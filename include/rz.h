@@ -279,8 +279,12 @@ int rz_q4_0_gemv(const void* w_q4_0, const void* x, int x_format, float* y,
  * preload_lm_head_bias (an output bias of vocab values added to the logits
  * after the GEMV) and dispatch_lm_head_and_download (the logits go to the
  * host, where the next token is chosen).
- *   logits = fl32(W x + bias), W x as rz_q4_0_gemv computes it (bit for bit
- *   when bias is NULL).  With argmax_idx and/or argmax_val, the index of the
+ *   logits = W x + bias, W x as rz_q4_0_gemv computes it (bit for bit when
+ *   bias is NULL).  A row that one pass covers (in_dim <= 14336 for fp32 x,
+ *   <= 16384 for Q8_1 x) gets fl32(W x + bias); a longer row is summed in
+ *   column passes and the bias enters the first pass's partial sum, so a
+ *   bias that is logits itself is read before it is overwritten, at every
+ *   size.  With argmax_idx and/or argmax_val, the index of the
  *   largest logit (the smallest index among equal largest values) and that
  *   logit: each workgroup reduces its rows in the GEMV's epilogue and one
  *   small kernel merges the pairs, so a greedy step reads back 4 bytes
@@ -321,8 +325,10 @@ size_t rz_lm_head_q4_0_workspace_bytes(int out_dim, int in_dim, int x_format);
  *   h         out: fp32 [inter_dim], 16-byte aligned (the down projection's input)
  *   y         out: fp32 [hidden_dim], 4-byte aligned
  *   hidden_dim, inter_dim  multiples of 64
- * Two GEMV launches run in order on `stream`.  x and h, h and y must not
- * overlap; a bias may be its output itself but must not overlap it otherwise.
+ * Two GEMV launches run in order on `stream`.  Each adds its bias as
+ * rz_lm_head_q4_0 does (in the first column pass; GELU after the last).  x
+ * and h, h and y must not overlap; a bias may be its output itself (at any
+ * size) but must not overlap it otherwise.
  * Errors: RZ_EINVAL, RZ_EDIM, RZ_EALIGN, RZ_ELAUNCH. */
 int rz_gelu_ffn_q4_0(const void* w_up, const void* w_down, const float* x, const float* up_bias,
                      const float* down_bias, float* h, float* y, int hidden_dim, int inter_dim,

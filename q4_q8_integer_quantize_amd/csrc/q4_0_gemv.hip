@@ -14,14 +14,18 @@
 //   fp32 x : sum_l q_l x_l per block, then d * (sum - 8 * sum_l x_l)
 //   Q8_1 x : isum = sum_l q_l q8_l - 8 * sum_l q8_l (exact), then d * d_x * isum
 //
-// LM-head epilogue (EPI, the launch that completes the rows): the output bias
-// is added in the store, logits = fl32(W x + bias) (realizar 0.8.5
+// LM-head epilogue (EPI): the output bias is added in a store (realizar 0.8.5
 // src/cuda/executor/cached.rs, preload_lm_head_bias: the bias is added to the
-// logits after the LM-head GEMV), and each workgroup reduces its rows to one
-// (value, index) pair, the largest logit with the smallest index on ties.
-// argmax_merge_kernel then reduces the pairs, so a greedy step downloads one
-// index instead of vocab logits (dispatch_lm_head_and_download brings all of
-// them to the host).
+// logits after the LM-head GEMV), and the launch that completes the rows
+// reduces them, per workgroup, to one (value, index) pair, the largest logit
+// with the smallest index on ties.  argmax_merge_kernel then reduces the
+// pairs, so a greedy step downloads one index instead of vocab logits
+// (dispatch_lm_head_and_download brings all of them to the host).  A row that
+// fits one pass gets logits = fl32(W x + bias); a longer row is summed in
+// column passes, and the bias enters the first pass's store, as the residual
+// does in the Q4_K GEMV: each element of a bias that is also the output is
+// read before it is first written.  GELU (the GELU FFN's up projection) and
+// the greedy token need the finished row and run in the last pass.
 #include "rz_device.h"
 #include "rz_launch.h"
 
@@ -36,11 +40,11 @@ struct Q40Args {
   int p0;           // first pair of this column chunk
   int npairs;       // pairs in this chunk
   int accumulate;
-  const float* bias;  // EPI: optional [out_dim] output bias
-  float* part_val;    // EPI: optional [grid] per-workgroup best logit
+  const float* bias;  // EPI: optional [out_dim] output bias (first pass only)
+  float* part_val;    // EPI: optional [grid] per-workgroup best logit (last pass only)
   int* part_idx;      //      and its row
   long part_count;    // EPI with pairs: the grid the pairs were sized for
-  int act;            // EPI: 1 = GELU after the bias (the GELU FFN's up projection)
+  int act;            // EPI: 1 = GELU after the bias (last pass only; the GELU FFN's up projection)
 };
 
 // Q8_1 activation slots of one lane: the codes of its S pairs (two blocks
@@ -545,16 +549,28 @@ static hipError_t run_xl_chunk(const Q40Args& a, bool epi, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
-// Column chunks; the last one runs the epilogue when `epi`.
+// Column chunks.  With `epi`, the first chunk's store adds the bias and the
+// last chunk's store applies GELU and collects the greedy token (one chunk
+// does all three).
 template <bool Q8>
 static hipError_t run_q40_all(Q40Args a, bool epi, hipStream_t st) {
   const int chunk = Q8 ? kQ8ChunkPairs : kXlChunkPairs;
+  const float* bias = a.bias;
+  float* part_val = a.part_val;
+  int* part_idx = a.part_idx;
+  const int act = a.act;
   for (int p0 = 0; p0 < a.npairs_row; p0 += chunk) {
     a.p0 = p0;
     a.npairs = a.npairs_row - p0 < chunk ? a.npairs_row - p0 : chunk;
     a.accumulate = p0 > 0;
+    const bool first = p0 == 0;
     const bool last = p0 + chunk >= a.npairs_row;
-    const hipError_t e = Q8 ? run_q8_chunk(a, epi && last, st) : run_xl_chunk(a, epi && last, st);
+    a.bias = first ? bias : nullptr;
+    a.act = last ? act : 0;
+    a.part_val = last ? part_val : nullptr;
+    a.part_idx = last ? part_idx : nullptr;
+    const bool e_ = epi && (first || last);
+    const hipError_t e = Q8 ? run_q8_chunk(a, e_, st) : run_xl_chunk(a, e_, st);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
