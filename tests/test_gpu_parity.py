@@ -468,9 +468,9 @@ def test_q4k_gate_4096_to_14336_full():
     assert_within(gpu_q4k(blob, got_q8)[0], y_ref, terms, "gate 4096->14336")
 
 
-def test_q4k_batch8_full_sampled():
-    """8 tokens x 4096 -> 14336: all outputs of tokens 0 and 7, and 512 sampled
-    rows of every token, against the oracle."""
+def test_q4k_batch8_full():
+    """8 tokens x 4096 -> 14336 (the small-batch decode workload): every output
+    of every token against the oracle, each token with its own Q8_1 vector."""
     banner("q4k batch8 4096->14336")
     w = synth.WORKLOADS["q4k_batch8"]
     blob = synth.q4k_weights(synth.rng(4, synth.T_W0), w["out_dim"], w["in_dim"])
@@ -479,14 +479,9 @@ def test_q4k_batch8_full_sampled():
     got_q8 = gpu_quantize(X, w["in_dim"])
     assert np.array_equal(got_q8, oracle.q8_1_to_bytes(xq))
     Y = gpu_q4k(blob, got_q8, 8)
-    rows = np.sort(np.random.default_rng(8).choice(w["out_dim"], 512, replace=False))
     for t in range(8):
-        if t in (0, 7):
-            y_ref, terms = oracle.gemv_q4k_q8_int(blob, xq.token(t))
-            assert_within(Y[t], y_ref, terms, "batch8 token %d" % t)
-        else:
-            y_ref, terms = oracle.gemv_q4k_q8_int(blob[rows], xq.token(t))
-            assert_within(Y[t][rows], y_ref, terms, "batch8 token %d (sampled)" % t)
+        y_ref, terms = oracle.gemv_q4k_q8_int(blob, xq.token(t))
+        assert_within(Y[t], y_ref, terms, "batch8 token %d" % t)
 
 
 # ------------------------------------------------------------------ Q4_0
@@ -583,10 +578,10 @@ def test_swiglu_ffn_chain(hidden, inter):
     """Stage by stage:
       (i)   g, u within the GEMV bound of the oracle's g, u;
       (ii)  h within the bound propagated through silu(g) * u;
-      (iii) h_q8 equals the standalone GPU quantize of the GPU's own h (byte-exact;
-            the standalone quantize is byte-exact against the oracle elsewhere), and
-            against the oracle's h_q8: d within the propagated bound, codes within
-            one step, equal wherever the oracle's h/d is clear of a rounding tie;
+      (iii) h_q8 byte-equal to the oracle's Q8_1 of the GPU's own h; and against
+            the oracle's h_q8 (of the oracle's h): d within the propagated bound,
+            codes within one step, equal wherever the oracle's h/d is clear of a
+            rounding tie;
       (iv)  y equals the standalone GPU GEMV over the GPU's h_q8 (bit-exact), the
             standalone down GEMV over the oracle's h_q8 is within the GEMV bound of
             the oracle, and the chain's y is within the GEMV bound plus the
@@ -609,9 +604,11 @@ def test_swiglu_ffn_chain(hidden, inter):
     err_h = np.abs(got["h"].astype(np.float64) - st["h"])
     assert np.all(err_h <= tol_h), "h: %d outside, worst ratio %.3g" % (
         int((err_h > tol_h).sum()), float(np.max(err_h / tol_h)))
-    # (iii) self-consistency with the standalone quantize kernel
-    requant = gpu_quantize(got["h"], inter)[0]
-    assert np.array_equal(got["hq"], requant)
+    # (iii) byte-exact: the oracle's Q8_1 of the GPU's own h (exactly one block
+    # string is correct for given fp32 values)
+    want_hq = oracle.q8_1_to_bytes(oracle.quantize_q8_1(got["h"], inter))
+    bad = first_mismatch(got["hq"], want_hq)
+    assert bad is None, "h_q8 differs from the oracle's quantize of the GPU's h: %r" % (bad,)
     # (iii) against the oracle's blocks
     d_gpu = got["hq"][:, 0:4].copy().view("<f4")[:, 0].astype(np.float64)
     q_gpu = got["hq"][:, 8:40].copy().view(np.int8).astype(np.int64)
@@ -699,10 +696,9 @@ def _norm_chain(n_padded):
 ])
 def test_rmsnorm_q8_1_matches_oracle(n, n_padded, nt, scale):
     """Stage by stage: the normed values within the fp32 rounding bound of the
-    float64 definition; the Q8_1 blocks byte-equal to the standalone quantize of
-    the GPU's own normed values (and those bytes are pinned elsewhere); against
-    the oracle's blocks of its own normed values, d within the propagated bound
-    and every code within one step."""
+    float64 definition; the Q8_1 blocks byte-equal to the oracle's quantize of
+    the GPU's own normed values; against the oracle's blocks of its own normed
+    values, d within the propagated bound and every code within one step."""
     banner("rmsnorm_q8_1", n, n_padded, nt, scale)
     g = np.random.default_rng(n * 7 + nt)
     x = (synth.activation(g, n, nt) * np.float32(scale)).astype(np.float32)
@@ -714,7 +710,10 @@ def test_rmsnorm_q8_1_matches_oracle(n, n_padded, nt, scale):
     err = np.abs(normed.astype(np.float64) - ref)
     assert np.all(err <= tol), "normed: %d outside, worst ratio %.3g" % (
         int((err > tol).sum()), float(np.max(err / tol)))
-    assert np.array_equal(q, gpu_quantize(normed, n_padded))
+    # byte-exact: the oracle's Q8_1 of the GPU's own normed values
+    want_gpu = oracle.q8_1_to_bytes(oracle.quantize_q8_1(normed, n_padded)).reshape(q.shape)
+    bad = first_mismatch(q, want_gpu)
+    assert bad is None, "Q8_1 differs from the oracle's quantize of the GPU's normed values: %r" % (bad,)
     # against the oracle's quantize of its own (float64 -> fp32) normed values
     want = oracle.quantize_q8_1(ref.astype(np.float32), n_padded)
     d_gpu = q[..., 0:4].copy().view("<f4")[..., 0].astype(np.float64).reshape(-1)
@@ -994,13 +993,21 @@ def gpu_lm_head(blob, x, x_format, bias, argmax=True):
     return lg, int(host(idx)[0]), host(val)[0]
 
 
+def _q4_0_one_pass(in_dim, x_format):
+    """The row fits one column pass of the Q4_0 kernel (224 block pairs for fp32
+    x, 256 for Q8_1 x), so the bias store gives fl32(W x + bias) exactly."""
+    return in_dim <= (16384 if x_format == 1 else 14336)
+
+
 def _check_lm_head(blob, x, x_format, bias, x_oracle):
     lg, idx, val = gpu_lm_head(blob, x, x_format, bias)
-    # logits: fl32(plain GEMV + bias), and the oracle bound with |bias| as a term
+    # logits: fl32(plain GEMV + bias) for one pass (a longer row adds the bias
+    # to its first pass), and the oracle bound with |bias| as a term
     plain = gpu_q4_0(blob, x, x_format)
-    want = plain if bias is None else (plain + bias).astype(np.float32)
-    mm = first_mismatch(lg, want)
-    assert mm is None, "logit %s fused=%r plain+bias=%r (%d differ)" % mm
+    if bias is None or _q4_0_one_pass(blob.shape[1] * 32, x_format):
+        want = plain if bias is None else (plain + bias).astype(np.float32)
+        mm = first_mismatch(lg, want)
+        assert mm is None, "logit %s fused=%r plain+bias=%r (%d differ)" % mm
     y_ref, terms = oracle.lm_head_q4_0(blob, x_oracle, bias, x_format)
     assert_within(lg, y_ref, terms, "lm head logits")
     # the greedy token: unique on the GPU's own logits (same fp32 values, same tie rule)
@@ -1087,6 +1094,53 @@ def test_lm_head_optional_outputs_and_workspace_reuse():
     assert int(host(idx)[0]) == oracle.argmax_first(host(logits)[:777])
     rz.rz_lm_head_q4_0(wd, xd, 0, None, logits, 20000, 1024, None, None, None)
     assert np.array_equal(host(logits), lg_full)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("out_dim,in_dim", [(300, 1024), (50, 32768), (129, 20480)])
+def test_lm_head_bias_is_logits(fmt, out_dim, in_dim):
+    """The bias may be the logits buffer itself: the same logits and greedy
+    token as with a separate bias, bit for bit, with one column pass and with
+    several (the bias enters the first pass, before the buffer is written)."""
+    banner("lm head bias aliased", fmt, out_dim, in_dim)
+    torch = __import__("torch")
+    blob = synth.q4_0_weights(synth.rng(63, in_dim), out_dim, in_dim)
+    x = synth.activation(synth.rng(63, 1), in_dim)
+    xin = x if fmt == 0 else oracle.q8_1_to_bytes(oracle.quantize_q8_1(x))
+    bias = synth.activation(synth.rng(63, 2), out_dim)
+    lg, idx, val = gpu_lm_head(blob, xin, fmt, bias)
+    wd = dev_bytes(blob)
+    xd = dev_f32(xin) if fmt == 0 else dev_bytes(xin)
+    both = dev_f32(bias)
+    i2 = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    v2 = empty_f32(1)
+    ws = empty_bytes(rz.rz_lm_head_q4_0_workspace_bytes(out_dim, in_dim, fmt))
+    rz.rz_lm_head_q4_0(wd, xd, fmt, both, both, out_dim, in_dim, i2, v2, ws)
+    assert np.array_equal(host(both).view(np.uint32), lg.view(np.uint32))
+    assert int(host(i2)[0]) == idx and host(v2)[0] == val
+
+
+@pytest.mark.parametrize("hidden,inter", [(256, 16384), (16384, 256)])
+def test_gelu_ffn_bias_is_output(hidden, inter):
+    """up_bias may be h and down_bias may be y: the same h and y as with
+    separate biases, bit for bit, also where the projection runs in two column
+    passes (inter 16384 for the down projection, hidden 16384 for the up)."""
+    banner("gelu ffn bias aliased", hidden, inter)
+    wu = synth.q4_0_weights(synth.rng(64, 1), inter, hidden)
+    wd = synth.q4_0_weights(synth.rng(64, 2), hidden, inter)
+    x = synth.activation(synth.rng(64, 0), hidden)
+    ub = synth.activation(synth.rng(64, 3), inter)
+    db = synth.activation(synth.rng(64, 4), hidden)
+    dwu, dwd, xd = dev_bytes(wu), dev_bytes(wd), dev_f32(x)
+    h, y = empty_f32(inter), empty_f32(hidden)
+    rz.rz_gelu_ffn_q4_0(dwu, dwd, xd, dev_f32(ub), dev_f32(db), h, y, hidden, inter)
+    h2, y2 = dev_f32(ub), dev_f32(db)
+    rz.rz_gelu_ffn_q4_0(dwu, dwd, xd, h2, y2, h2, y2, hidden, inter)
+    assert np.array_equal(host(h2).view(np.uint32), host(h).view(np.uint32)), "h"
+    assert np.array_equal(host(y2).view(np.uint32), host(y).view(np.uint32)), "y"
+    st = oracle.ffn_gelu_q4_0(wu, wd, x, ub, db)
+    tol_h = oracle.gelu_h_tolerance(st["u"], st["tol_u"], st["h"])
+    assert np.all(np.abs(host(h).astype(np.float64) - st["h"]) <= tol_h)
 
 
 # ------------------------------------------------------------------ GELU FFN (Q4_0)
@@ -1412,15 +1466,19 @@ def test_graph_replays_match_eager(fused):
 ])
 def test_rmsnorm_q4k_q8_gemv_multi_bit_identical(in_dim, n, out_dims):
     """One launch (RMSNorm + Q8_1 in every workgroup, then the GEMVs) equals
-    rz_rmsnorm_q8_1 followed by rz_q4k_q8_gemv_multi bit for bit: the outputs
-    and the Q8_1 side output."""
+    rz_rmsnorm_q8_1 followed by rz_q4k_q8_gemv_multi bit for bit (the outputs
+    and the Q8_1 side output), and against the oracle: the side output is the
+    oracle's Q8_1 of the GPU's normed values, byte for byte, and every output
+    is within the GEMV bound of the oracle's product over those blocks."""
     banner("rmsnorm multi", in_dim, n, out_dims)
     x = synth.activation(synth.rng(81, in_dim), n)
     gam = synth.norm_weights(synth.rng(81, 1), n)
-    ws = [dev_bytes(synth.q4k_weights(synth.rng(82, k), o, in_dim)) for k, o in enumerate(out_dims)]
+    blobs = [synth.q4k_weights(synth.rng(82, k), o, in_dim) for k, o in enumerate(out_dims)]
+    ws = [dev_bytes(b) for b in blobs]
     xd, gd = dev_f32(x), dev_f32(gam)
     xq_ref = empty_bytes(rz.q8_1_nbytes(in_dim))
-    rz.rz_rmsnorm_q8_1(xd, gd, 1e-5, n, in_dim, 1, None, xq_ref)
+    normed = empty_f32(n)
+    rz.rz_rmsnorm_q8_1(xd, gd, 1e-5, n, in_dim, 1, normed, xq_ref)
     y_ref = [empty_f32(o) for o in out_dims]
     rz.rz_q4k_q8_gemv_multi(ws, xq_ref, y_ref, out_dims, in_dim)
     xq = empty_bytes(rz.q8_1_nbytes(in_dim))
@@ -1433,6 +1491,19 @@ def test_rmsnorm_q4k_q8_gemv_multi_bit_identical(in_dim, n, out_dims):
     rz.rz_rmsnorm_q4k_q8_gemv_multi(ws, xd, gd, 1e-5, n, None, y2, out_dims, in_dim)
     for a_, b_ in zip(y2, y_ref):
         assert np.array_equal(host(a_).view(np.uint32), host(b_).view(np.uint32))
+    # against the oracle: the normed values within the fp32 bound of the float64
+    # RMSNorm, the fused launch's Q8_1 side output byte-equal to the oracle's
+    # quantize of those values, every output within the GEMV bound of the
+    # oracle's integer form over those blocks
+    nv = host(normed)
+    ref = oracle.rmsnorm(x, gam, 1e-5)
+    assert np.all(np.abs(nv.astype(np.float64) - ref) <= oracle.rmsnorm_tolerance(ref, _norm_chain(in_dim)))
+    xq_o = oracle.quantize_q8_1(nv, in_dim)
+    bad = first_mismatch(q8_host_bytes(xq, in_dim // 32), oracle.q8_1_to_bytes(xq_o))
+    assert bad is None, "fused Q8_1 side output differs from the oracle: %r" % (bad,)
+    for m, (b_, y_) in enumerate(zip(blobs, y)):
+        y_o, t_o = oracle.gemv_q4k_q8_int(b_, xq_o)
+        assert_within(host(y_), y_o, t_o, "rmsnorm multi matrix %d" % m)
 
 
 @pytest.mark.parametrize("hidden,inter", [
@@ -1449,11 +1520,13 @@ def test_rmsnorm_swiglu_ffn_add_bit_identical(hidden, inter):
     banner("rmsnorm swiglu add", hidden, inter)
     x = synth.activation(synth.rng(83, hidden), hidden)
     gam = synth.norm_weights(synth.rng(83, 1), hidden)
-    ws = [dev_bytes(synth.q4k_weights(synth.rng(84, k), o, i))
-          for k, (o, i) in enumerate(((inter, hidden), (inter, hidden), (hidden, inter)))]
+    blobs = [synth.q4k_weights(synth.rng(84, k), o, i)
+             for k, (o, i) in enumerate(((inter, hidden), (inter, hidden), (hidden, inter)))]
+    ws = [dev_bytes(b) for b in blobs]
     xd, gd = dev_f32(x), dev_f32(gam)
     xq = empty_bytes(rz.q8_1_nbytes(hidden))
-    rz.rz_rmsnorm_q8_1(xd, gd, 1e-5, hidden, hidden, 1, None, xq)
+    normed = empty_f32(hidden)
+    rz.rz_rmsnorm_q8_1(xd, gd, 1e-5, hidden, hidden, 1, normed, xq)
     h_ref, hq_ref = empty_f32(inter), empty_bytes(rz.q8_1_nbytes(inter))
     gu_ref, y_ref = empty_f32(2 * inter), empty_f32(hidden)
     rz.rz_swiglu_ffn_q4k_add(*ws[:3], xq, h_ref, hq_ref, xd, y_ref, gu_ref, hidden, inter)
@@ -1471,6 +1544,31 @@ def test_rmsnorm_swiglu_ffn_add_bit_identical(hidden, inter):
     y2 = empty_f32(hidden)
     rz.rz_rmsnorm_swiglu_ffn_q4k_add(*ws[:3], xd, gd, 1e-5, h, hq, y2, None, hidden, inter)
     assert np.array_equal(bits(y2), bits(y_ref)), "without gu"
+    # against the oracle, stage by stage on the fused launch's outputs (h, h_q8,
+    # gu and y above are those of the fused launch, bit for bit): the activation
+    # blocks are the oracle's Q8_1 of the GPU's normed values; g and u within the
+    # GEMV bound; h within the bound propagated through silu(g) * u; h_q8 the
+    # oracle's Q8_1 of the GPU's h, byte for byte; y within the GEMV bound of the
+    # oracle's down projection over those blocks plus the residual x
+    nv = host(normed)
+    ref = oracle.rmsnorm(x, gam, 1e-5)
+    assert np.all(np.abs(nv.astype(np.float64) - ref) <= oracle.rmsnorm_tolerance(ref, _norm_chain(hidden)))
+    xq_o = oracle.quantize_q8_1(nv, hidden)
+    assert first_mismatch(q8_host_bytes(xq, hidden // 32), oracle.q8_1_to_bytes(xq_o)) is None
+    g_o, tg = oracle.gemv_q4k_q8_int(blobs[0], xq_o)
+    u_o, tu = oracle.gemv_q4k_q8_int(blobs[1], xq_o)
+    gu_h = host(gu)
+    assert_within(gu_h[:inter], g_o, tg, "rmsnorm swiglu gate")
+    assert_within(gu_h[inter:], u_o, tu, "rmsnorm swiglu up")
+    h_o = oracle.swiglu(g_o, u_o)
+    tol_h = oracle.h_tolerance(g_o, u_o, oracle.gemv_tolerance(tg), oracle.gemv_tolerance(tu), h_o)
+    h_h = host(h)
+    assert np.all(np.abs(h_h.astype(np.float64) - h_o) <= tol_h), "rmsnorm swiglu h"
+    hq_o = oracle.quantize_q8_1(h_h, inter)
+    bad = first_mismatch(q8_host_bytes(hq, inter // 32), oracle.q8_1_to_bytes(hq_o))
+    assert bad is None, "h_q8 differs from the oracle's quantize of the GPU's h: %r" % (bad,)
+    y_o, ty = oracle.gemv_q4k_q8_int(blobs[2], hq_o)
+    assert_within(host(y2), oracle.residual_add(x, y_o), ty + np.abs(x), "rmsnorm swiglu y")
 
 
 @pytest.mark.parametrize("out_dim,n,in_dim", [
@@ -1481,12 +1579,14 @@ def test_rmsnorm_swiglu_ffn_add_bit_identical(hidden, inter):
 ])
 def test_q4k_q8_gemv_f32_add_bit_identical(out_dim, n, in_dim):
     """Quantize + GEMV + residual in one launch equals rz_q8_1_quantize followed
-    by rz_q4k_q8_gemv_add bit for bit: y out of place and in place (r is y),
-    and the Q8_1 side output."""
+    by rz_q4k_q8_gemv_add bit for bit (y out of place and in place, r is y, and
+    the Q8_1 side output), the side output is the oracle's Q8_1 of x byte for
+    byte, and y is within the GEMV bound of the oracle plus r."""
     banner("f32 add", out_dim, n, in_dim)
     x = synth.activation(synth.rng(85, in_dim), n)
     r = synth.activation(synth.rng(85, 1), out_dim)
-    w = dev_bytes(synth.q4k_weights(synth.rng(86, out_dim), out_dim, in_dim))
+    blob = synth.q4k_weights(synth.rng(86, out_dim), out_dim, in_dim)
+    w = dev_bytes(blob)
     xd = dev_f32(x)
     xq_ref = empty_bytes(rz.q8_1_nbytes(in_dim))
     rz.rz_q8_1_quantize(xd, n, in_dim, 1, xq_ref)
@@ -1501,6 +1601,13 @@ def test_q4k_q8_gemv_f32_add_bit_identical(out_dim, n, in_dim):
     yr = dev_f32(r)
     rz.rz_q4k_q8_gemv_f32_add(w, xd, n, None, yr, yr, out_dim, in_dim)
     assert np.array_equal(bits(yr), bits(y_ref)), "in place"
+    # against the oracle: the side output is the oracle's Q8_1 of x byte for
+    # byte, and y is within the GEMV bound of the integer form plus r
+    xq_o = oracle.quantize_q8_1(x, in_dim)
+    bad = first_mismatch(q8_host_bytes(xq, in_dim // 32), oracle.q8_1_to_bytes(xq_o))
+    assert bad is None, "Q8_1 side output differs from the oracle: %r" % (bad,)
+    y_o, t_o = oracle.gemv_q4k_q8_int(blob, xq_o)
+    assert_within(host(y), oracle.residual_add(r, y_o), t_o + np.abs(r), "f32 add y")
 
 
 def test_minimum_alignments_fused_entries():
