@@ -8,15 +8,19 @@ followed by rz_q4k_q8_gemv, which is also timed).  Every step reads the next of 
 Cache or an L2; inputs are resident in HBM before the timed region.
 
 Printed (one JSON line): the whole-step weight-stream rate in GB/s (`value`,
-K steps captured in one HIP graph and replayed between HIP events), the fused
-kernel's rate against the 8 TB/s HBM peak (`roofline`), a plain streaming read
-of the same bytes as the practical ceiling (`read_ceiling`), the CPU oracle timed
-on the host (`cpu_baseline`), and under `rows` every other kernel of the path
-at its own workload, timed the same way with its own weight rotation:
-Q8_1 quantize, the GEMV alone, the four attention projections on one shared
-activation (one multi-matrix launch, and four launches), the SwiGLU chain and its down projection, the Q4_0 LM head (fp32
-and Q8_1 activation), 8 tokens sharing one weight pass, and the small
-896 x 1024 case.
+K steps captured in one HIP graph and replayed between HIP events, right after
+W untimed warm-up steps), the fused kernel's rate against the 8 TB/s HBM peak
+(`roofline`), a plain streaming read of the same bytes as the practical
+ceiling (`read_ceiling`), the CPU oracle timed on the host (`cpu_baseline`:
+the step's workload, and every configuration's oracle as the median of 3
+runs), and under `rows` every other kernel of the path at its own workload,
+timed the same way with its own weight rotation (the rows run first, so the
+GPU clocks have settled when the step is timed): Q8_1 quantize, the GEMV
+alone, the four attention projections on one shared activation (one
+multi-matrix launch, and four launches), the SwiGLU chain and its down
+projection, the Q4_0 LM head (fp32 and Q8_1 activation), 8 tokens sharing one
+weight pass, and the small 896 x 1024 case; a row of a measured configuration
+carries that configuration's oracle time.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-rows]
 """
@@ -74,10 +78,55 @@ def measured_traffic():
         return None
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _blas_threads():
+    """BLAS libraries numpy uses and their thread counts (threadpoolctl)."""
+    try:
+        import threadpoolctl
+        return [{"api": d.get("internal_api"), "threads": d.get("num_threads")}
+                for d in threadpoolctl.threadpool_info() if d.get("user_api") == "blas"]
+    except Exception as e:   # threadpoolctl missing or failing: say so
+        return [{"error": type(e).__name__}]
+
+
+def _median_run(fn, runs: int = 3):
+    """Median wall seconds and CPU seconds of `runs` calls of fn."""
+    wall, cpu = [], []
+    for _ in range(runs):
+        c0, t0 = time.process_time(), time.perf_counter()
+        fn()
+        wall.append(time.perf_counter() - t0)
+        cpu.append(time.process_time() - c0)
+    order = sorted(range(runs), key=lambda i: wall[i])
+    mid = order[runs // 2]
+    return wall[mid], cpu[mid]
+
+
 def cpu_baseline(target_seconds: float):
-    """The oracle as it stands: Q8_1 quantize of the activation plus the integer
-    form of the GEMV over all 14336 rows, repeated until target_seconds of wall
-    time; rate = weight bytes per second.  Threads used = CPU time / wall time."""
+    """The oracle as it stands, on the host cores.
+
+    Headline (`value`): Q8_1 quantize of the activation plus the integer form of
+    the 4096 -> 14336 GEMV over all rows, repeated until target_seconds of wall
+    time; rate = weight bytes per second.  `cores` = CPU time / wall time of that
+    loop (the threads it actually kept busy).
+
+    Per configuration (`per_config`), the median of 3 runs of the oracle's whole
+    workload: the 896 x 1024 GEMV; the attention projections Q, K, V, O on one
+    quantized activation; the SwiGLU chain (gate, up, silu * up, requantize,
+    down); the Q4_0 LM head over an fp32 and over a Q8_1 activation; 8 tokens
+    through the 4096 -> 14336 GEMV.  Reported with the weight rate and the
+    threads kept busy (numpy's integer paths run on one core; the fp32 LM head
+    is a BLAS matrix-vector product on the BLAS threads listed)."""
     import numpy as np
     import oracle
     import synth
@@ -92,19 +141,66 @@ def cpu_baseline(target_seconds: float):
         cpu += time.process_time() - c0
         reps += 1
     rate = reps * W_BYTES / wall / 1e9
-    model = "unknown"
-    try:
-        with open("/proc/cpuinfo") as f:
-            for line in f:
-                if line.startswith("model name"):
-                    model = line.split(":", 1)[1].strip()
-                    break
-    except OSError:
-        pass
+
+    per = {}
+
+    def record(name, fn, weight_bytes):
+        sec, cpus = _median_run(fn)
+        per[name] = {"ms": round(sec * 1e3, 2), "weight_gbs": round(weight_bytes / sec / 1e9, 4),
+                     "threads_busy": round(cpus / sec, 2)}
+
+    # config 0: 896 x (896 -> 1024)
+    w0 = synth.q4k_weights(synth.rng(0, 1), 896, 1024)
+    x0 = np.zeros(1024, np.float32)
+    x0[:896] = synth.activation(synth.rng(0, synth.T_ACT), 896)
+    record("q4k_896x1024", lambda: oracle.gemv_q4k_q8_int(w0, oracle.quantize_q8_1(x0)),
+           q4k_bytes(896, 1024))
+    del w0
+    # config 1: attention projections on one activation
+    shapes = [(4096, 4096), (1024, 4096), (1024, 4096), (4096, 4096)]
+    wa = [synth.q4k_weights(synth.rng(1, 1 + k), o, i) for k, (o, i) in enumerate(shapes)]
+    x1 = synth.activation(synth.rng(1, synth.T_ACT), IN_DIM)
+
+    def attn():
+        xq1 = oracle.quantize_q8_1(x1)
+        for wk in wa:
+            oracle.gemv_q4k_q8_int(wk, xq1)
+    record("attn_qkvo_4096", attn, sum(q4k_bytes(o, i) for o, i in shapes))
+    del wa
+    # config 2: the SwiGLU chain
+    INTER = 14336
+    wg = synth.q4k_weights(synth.rng(2, 1), INTER, IN_DIM)
+    wu = synth.q4k_weights(synth.rng(2, 2), INTER, IN_DIM)
+    wd = synth.q4k_weights(synth.rng(2, 3), IN_DIM, INTER)
+    record("swiglu_ffn_4096_14336",
+           lambda: oracle.ffn_swiglu_q4k(wg, wu, wd, oracle.quantize_q8_1(x)), 3 * W_BYTES)
+    del wu, wd
+    # config 4: 8 tokens, one weight matrix
+    x4 = synth.activation(synth.rng(4, synth.T_ACT), IN_DIM, 8)
+
+    def batch8():
+        xq4 = oracle.quantize_q8_1(x4)
+        for t in range(8):
+            oracle.gemv_q4k_q8_int(wg, xq4.token(t))
+    record("q4k_batch8_4096x14336", batch8, W_BYTES)
+    del wg
+    # config 3: the Q4_0 LM head, fp32 and Q8_1 activation
+    VOCAB, HID, HID_P = 151936, 896, 1024
+    wl = synth.q4_0_weights(synth.rng(3, 1), VOCAB, HID_P)
+    xl = np.zeros(HID_P, np.float32)
+    xl[:HID] = synth.activation(synth.rng(3, synth.T_ACT), HID)
+    record("q4_0_lm_head_151936x1024_fp32", lambda: oracle.gemv_q4_0_f32(wl, xl),
+           q4_0_bytes(VOCAB, HID_P))
+    record("q4_0_lm_head_151936x1024_q8_1",
+           lambda: oracle.gemv_q4_0_q8_int(wl, oracle.quantize_q8_1(xl)), q4_0_bytes(VOCAB, HID_P))
+    del wl
     return {"value": round(rate, 4), "unit": "GB/s", "cores": max(1, round(cpu / wall)),
-            "kind": "oracle", "cpu_model": model,
+            "kind": "oracle", "cpu_model": _cpu_model(),
+            "host_cores": len(os.sched_getaffinity(0)), "blas": _blas_threads(),
             "sample": "%d full passes (quantize 4096 + integer-form GEMV 14336x4096, numpy), "
-                      "%.1f s wall; host has %d cores" % (reps, wall, len(os.sched_getaffinity(0)))}
+                      "%.1f s wall; per_config: median of 3 runs of each workload's oracle"
+                      % (reps, wall),
+            "per_config": per}
 
 
 def q4k_bytes(out_dim: int, in_dim: int) -> int:
@@ -534,9 +630,7 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    # ~20 ms of untimed step launches first, so the clocks have settled when the
-    # (1.6 ms) timed replay starts
-    ap.add_argument("--warmup", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--only", choices=sorted(ONLY), default=None,
@@ -600,33 +694,44 @@ def main() -> int:
     rz.rz_q4k_q8_gemv_f32(copies[0], x, IN_DIM, None, y, OUT_DIM, IN_DIM, s)
     rz.rz_q8_1_quantize(x, IN_DIM, IN_DIM, 1, xq, s)
     rz.rz_q4k_q8_gemv(copies[0], xq, y, OUT_DIM, IN_DIM, 1, s)
-    for i in range(args.warmup):
-        fused(i, s)
     torch.cuda.synchronize()
     K = args.steps
+    W = max(1, args.warmup)
 
-    def graph_time(body):
-        """K calls of body, each on the next weight copy, captured in one HIP
-        graph; mean seconds per call over one replay bracketed by HIP events on
-        the launch stream (after one untimed replay)."""
+    def capture(body, first, count):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             cs = torch.cuda.current_stream().cuda_stream
-            for i in range(K):
-                body(args.warmup + i, cs)
+            for i in range(count):
+                body(first + i, cs)
+        return g
+
+    def graph_time(body):
+        """K calls of body, each on the next weight copy, captured in one HIP
+        graph; the mean seconds per call over one replay bracketed by HIP events
+        on the launch stream.  First both graphs run once untimed and the GPU is
+        synchronized; then W untimed warm-up calls (the W copies before the
+        timed ones, so the rotation runs on) are replayed back to back with
+        the timed replay: the GPU is busy while the timed replay is queued, so
+        the events bracket the K calls and not the host's graph launch."""
+        g = capture(body, W, K)
+        wg = capture(body, 0, W)
+        wg.replay()
         g.replay()
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
+        wg.replay()
         e0.record(stream)
         g.replay()
         e1.record(stream)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e-3 / K
 
-    step_s = graph_time(fused)            # the timed steps (whole hot path)
+    # every other kernel first: seconds of back-to-back kernels bring the GPU
+    # clocks to their sustained state before the step is timed
     rows = None if args.no_rows else time_rows(lib, rz, torch, dev, graph_time, copies, x, xq, y)
+    step_s = graph_time(fused)            # the timed steps (whole hot path)
     ceiling = read_ceiling(torch, dev, graph_time, w_p, n_copies)
     ms_step = step_s * 1e3
     two_s = graph_time(two_launch)        # same work as two launches
@@ -683,6 +788,18 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+        # each configuration's oracle time next to its GPU row
+        if rows:
+            for cfg, row in (("q4k_896x1024", "q4k_fused_896x1024"),
+                             ("attn_qkvo_4096", "attn_qkvo_4096"),
+                             ("swiglu_ffn_4096_14336", "swiglu_ffn_4096_14336"),
+                             ("q4k_batch8_4096x14336", "q4k_gemv_batch8_4096x14336"),
+                             ("q4_0_lm_head_151936x1024_fp32", "q4_0_lm_head_151936x1024_fp32"),
+                             ("q4_0_lm_head_151936x1024_q8_1", "q4_0_lm_head_151936x1024_q8_1")):
+                per = out["cpu_baseline"]["per_config"].get(cfg)
+                if per and row in rows:
+                    rows[row]["oracle_ms"] = per["ms"]
+                    rows[row]["oracle_over_gpu"] = round(per["ms"] * 1e3 / rows[row]["us"], 1)
     print(json.dumps(out), flush=True)
     return 0
 
