@@ -309,6 +309,32 @@ int rz_lm_head_q4_0(const void* w_q4_0, const void* x, int x_format, const float
  * would reject). */
 size_t rz_lm_head_q4_0_workspace_bytes(int out_dim, int in_dim, int x_format);
 
+/* rz_lm_head_q4_0_noalloc -- rz_lm_head_q4_0 without the workspace argument,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.
+ *   The arguments, checks, outputs and errors are those of rz_lm_head_q4_0
+ *   (logits and the greedy token bit for bit), except that the argmax's
+ *   per-workgroup (value, row) pairs live in a fixed array of the library:
+ *   RZ_NOALLOC_ARGMAX_PAIRS pairs (256 KiB) on every GPU the library runs on,
+ *   held until the process ends.  Nothing is allocated, freed or
+ *   synchronised.  A shape whose argmax needs more pairs than that
+ *   (rz_lm_head_q4_0_workspace_bytes / 8 > RZ_NOALLOC_ARGMAX_PAIRS; 151936 x
+ *   1024 needs 2374, 262144 x 4096 needs 16384) gives RZ_EINVAL.  Without
+ *   argmax_idx and argmax_val the array is not used.
+ *   `stream` must belong to the current device (else RZ_EINVAL); the array of
+ *   the current device is used.  Every call on a GPU shares that GPU's array
+ *   and its last contents; the kernels write every pair a call reads before
+ *   reading it, so nothing needs clearing.  Calls on one GPU whose kernels
+ *   may overlap (different streams without ordering) race on the array and
+ *   may return a wrong greedy token; calls in one stream, or ordered by
+ *   events, do not.
+ * Errors: those of rz_lm_head_q4_0, plus RZ_EINVAL for a shape beyond the
+ * array or a stream of another device. */
+#define RZ_NOALLOC_ARGMAX_PAIRS 32768
+int rz_lm_head_q4_0_noalloc(const void* w_q4_0, const void* x, int x_format, const float* bias,
+                            float* logits, int out_dim, int in_dim, int* argmax_idx,
+                            float* argmax_val, void* stream);
+
 /* rz_gelu_ffn_q4_0 -- the GELU FFN on Q4_0 weights and fp32 activations.
  * Passages: realizar 0.8.4 src/gpu/adapters/using.rs, ffn_standard_gpu (up
  * projection, GELU in place, down projection, all Q4_0 GEMVs on fp32

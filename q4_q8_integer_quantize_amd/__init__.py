@@ -24,8 +24,8 @@ __all__ = [
     "rz_q4k_q8_gemv_f32", "rz_q4k_q8_gemv_f32_add",
     "rz_q4_0_gemv", "rz_swiglu_ffn_q4k", "rz_swiglu_ffn_q4k_add", "rz_q4k_gemv",
     "rz_swiglu_ffn_q4k_f32",
-    "rz_lm_head_q4_0", "rz_lm_head_q4_0_workspace_bytes", "rz_gelu_ffn_q4_0",
-    "q8_1_nbytes", "RzError",
+    "rz_lm_head_q4_0", "rz_lm_head_q4_0_workspace_bytes", "rz_lm_head_q4_0_noalloc",
+    "rz_gelu_ffn_q4_0", "q8_1_nbytes", "RzError", "NOALLOC_ARGMAX_PAIRS",
 ]
 
 RZ_OK, RZ_EINVAL, RZ_EDIM, RZ_EALIGN, RZ_ELAUNCH = 0, -1, -2, -3, -4
@@ -33,6 +33,7 @@ Q8_1_BLOCK_BYTES = 40
 Q4K_BLOCK_BYTES = 144
 Q4_0_BLOCK_BYTES = 18
 MAX_TOKENS = 8
+NOALLOC_ARGMAX_PAIRS = 32768
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -74,6 +75,7 @@ def load_library() -> ctypes.CDLL:
     lib.rz_q4k_gemv.argtypes = [vp, vp, i, vp, i, i, vp]
     lib.rz_swiglu_ffn_q4k_f32.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, vp]
     lib.rz_lm_head_q4_0.argtypes = [vp, vp, i, vp, vp, i, i, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.rz_lm_head_q4_0_noalloc.argtypes = [vp, vp, i, vp, vp, i, i, vp, vp, vp]
     lib.rz_gelu_ffn_q4_0.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, vp]
     lib.rz_lm_head_q4_0_workspace_bytes.argtypes = [i, i, i]
     lib.rz_lm_head_q4_0_workspace_bytes.restype = ctypes.c_size_t
@@ -82,7 +84,8 @@ def load_library() -> ctypes.CDLL:
                "rz_rmsnorm_swiglu_ffn_q4k_add", "rz_q4k_q8_gemv_f32_add",
                "rz_q4_0_gemv", "rz_swiglu_ffn_q4k",
                "rz_swiglu_ffn_q4k_add", "rz_q4k_gemv", "rz_swiglu_ffn_q4k_f32",
-               "rz_lm_head_q4_0", "rz_gelu_ffn_q4_0", "rz_abi_version"):
+               "rz_lm_head_q4_0", "rz_lm_head_q4_0_noalloc", "rz_gelu_ffn_q4_0",
+               "rz_abi_version"):
         getattr(lib, fn).restype = i
     lib.rz_last_error.argtypes = []
     lib.rz_last_error.restype = ctypes.c_char_p
@@ -368,6 +371,23 @@ def rz_lm_head_q4_0(w_q4_0, x, x_format: int, bias, logits, out_dim: int, in_dim
                                           _ptr(logits), out_dim, in_dim, _ptr(argmax_idx),
                                           _ptr(argmax_val), _ptr(workspace), ws_bytes,
                                           _stream(stream)))
+
+
+def rz_lm_head_q4_0_noalloc(w_q4_0, x, x_format: int, bias, logits, out_dim: int, in_dim: int,
+                            argmax_idx=None, argmax_val=None, stream=None) -> None:
+    """rz_lm_head_q4_0 without a workspace: the argmax pairs live in the
+    library's fixed per-GPU array (at most NOALLOC_ARGMAX_PAIRS of them).
+    Calls on one GPU that may overlap race on that array."""
+    if in_dim > 0 and in_dim % 64 == 0 and out_dim > 0 and x_format in (0, 1):
+        _need(w_q4_0, out_dim * (in_dim // 32) * Q4_0_BLOCK_BYTES, "w_q4_0")
+        _need(x, 4 * in_dim if x_format == 0 else q8_1_nbytes(in_dim), "x")
+        _need(bias, 4 * out_dim, "bias")
+        _need(logits, 4 * out_dim, "logits")
+        _need(argmax_idx, 4, "argmax_idx")
+        _need(argmax_val, 4, "argmax_val")
+    _check(load_library().rz_lm_head_q4_0_noalloc(_ptr(w_q4_0), _ptr(x), x_format, _ptr(bias),
+                                                  _ptr(logits), out_dim, in_dim, _ptr(argmax_idx),
+                                                  _ptr(argmax_val), _stream(stream)))
 
 
 def rz_gelu_ffn_q4_0(w_up, w_down, x, up_bias, down_bias, h, y, hidden_dim: int, inter_dim: int,

@@ -10,6 +10,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <initializer_list>
+#include <mutex>
 
 #include "rz.h"
 #include "rz_launch.h"
@@ -452,21 +453,11 @@ int swiglu_ffn(const char* what, const void* w_gate, const void* w_up, const voi
       what);
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t rz_lm_head_q4_0_workspace_bytes(int out_dim, int in_dim, int x_format) {
-  if (out_dim <= 0 || out_dim > RZ_MAX_DIM || in_dim <= 0 || in_dim > RZ_MAX_DIM ||
-      in_dim % 64 != 0 || (x_format != 0 && x_format != 1))
-    return 0;
-  return (size_t)rz::q4_0_lm_head_partials(out_dim, in_dim, x_format) * 8u;
-}
-
-int rz_lm_head_q4_0(const void* w_q4_0, const void* x, int x_format, const float* bias,
-                    float* logits, int out_dim, int in_dim, int* argmax_idx, float* argmax_val,
-                    void* workspace, size_t workspace_bytes, void* stream) {
-  const char* what = "rz_lm_head_q4_0";
+// Argument checks shared by the two LM-head entry points (everything but the
+// argmax workspace).
+int lm_head_check(const char* what, const void* w_q4_0, const void* x, int x_format,
+                  const float* bias, const float* logits, int out_dim, int in_dim,
+                  const int* argmax_idx, const float* argmax_val) {
   if (!w_q4_0 || !x || !logits) return fail(RZ_EINVAL, "%s: null pointer", what);
   if (x_format != 0 && x_format != 1)
     return fail(RZ_EINVAL, "%s: x_format=%d (0 = fp32, 1 = Q8_1)", what, x_format);
@@ -487,6 +478,79 @@ int rz_lm_head_q4_0(const void* w_q4_0, const void* x, int x_format, const float
       !clear_of({argmax_val, 4}, {wspan, xspan, {logits, 4LL * out_dim}}))
     return fail(RZ_EINVAL, "%s: the argmax outputs must not overlap w_q4_0, x, logits or "
                 "each other", what);
+  return RZ_OK;
+}
+
+}  // namespace
+
+// ----------------------------------------------------------------- no-alloc LM head
+// The argmax pairs of rz_lm_head_q4_0_noalloc: (value, row) for at most
+// kNoAllocPairs workgroups, values first, rows after them (256 KiB).  Every
+// GPU the library runs on holds its own copy for the life of the process.  In
+// host code the array's name is a host-side stand-in, not a device address:
+// kernels only ever get the address hipGetSymbolAddress returns for the
+// current device (kept in g_scratch_ptr).
+constexpr size_t kNoAllocPairs = RZ_NOALLOC_ARGMAX_PAIRS;
+static __device__ __align__(256) unsigned char scratch[kNoAllocPairs * 8];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // per device, taken once with that device current
+
+// The current device's copy of `scratch` (looked up on the first call on the
+// device), after checking that `stream` belongs to that device.
+int scratch_for_current_device(const char* what, hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess)
+    return fail(RZ_ELAUNCH, "%s: hipGetDevice failed: %s", what, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(RZ_EINVAL, "%s: device %d, this library tracks devices 0..%d", what, dev,
+                kMaxDevices - 1);
+  if (stream) {
+    int sdev = -1;
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess)
+      return fail(RZ_ELAUNCH, "%s: hipStreamGetDevice failed: %s", what, hipGetErrorString(e));
+    if (sdev != dev)
+      return fail(RZ_EINVAL, "%s: the stream belongs to device %d, the current device is %d", what,
+                  sdev, dev);
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(RZ_ELAUNCH, "%s: hipGetSymbolAddress of the scratch array failed: %s", what,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return RZ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t rz_lm_head_q4_0_workspace_bytes(int out_dim, int in_dim, int x_format) {
+  if (out_dim <= 0 || out_dim > RZ_MAX_DIM || in_dim <= 0 || in_dim > RZ_MAX_DIM ||
+      in_dim % 64 != 0 || (x_format != 0 && x_format != 1))
+    return 0;
+  return (size_t)rz::q4_0_lm_head_partials(out_dim, in_dim, x_format) * 8u;
+}
+
+int rz_lm_head_q4_0(const void* w_q4_0, const void* x, int x_format, const float* bias,
+                    float* logits, int out_dim, int in_dim, int* argmax_idx, float* argmax_val,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  const char* what = "rz_lm_head_q4_0";
+  if (int rc = lm_head_check(what, w_q4_0, x, x_format, bias, logits, out_dim, in_dim, argmax_idx,
+                             argmax_val))
+    return rc;
+  const Span wspan{w_q4_0, q4_0_bytes(out_dim, in_dim)},
+      xspan{x, x_format == 0 ? 4LL * in_dim : q8_bytes(1, in_dim)};
   const bool argmax = argmax_idx || argmax_val;
   float* part_val = nullptr;
   int* part_idx = nullptr;
@@ -504,6 +568,34 @@ int rz_lm_head_q4_0(const void* w_q4_0, const void* x, int x_format, const float
       return fail(RZ_EINVAL, "%s: the argmax outputs must not overlap the workspace", what);
     part_val = static_cast<float*>(workspace);
     part_idx = reinterpret_cast<int*>(static_cast<char*>(workspace) + need / 2);
+  }
+  return launch_status(rz::launch_q4_0_lm_head(static_cast<const uint8_t*>(w_q4_0), x, x_format,
+                                               bias, logits, out_dim, in_dim, argmax_idx,
+                                               argmax_val, part_val, part_idx,
+                                               static_cast<hipStream_t>(stream)),
+                       what);
+}
+
+int rz_lm_head_q4_0_noalloc(const void* w_q4_0, const void* x, int x_format, const float* bias,
+                            float* logits, int out_dim, int in_dim, int* argmax_idx,
+                            float* argmax_val, void* stream) {
+  const char* what = "rz_lm_head_q4_0_noalloc";
+  if (int rc = lm_head_check(what, w_q4_0, x, x_format, bias, logits, out_dim, in_dim, argmax_idx,
+                             argmax_val))
+    return rc;
+  float* part_val = nullptr;
+  int* part_idx = nullptr;
+  if (argmax_idx || argmax_val) {
+    const long pairs = rz::q4_0_lm_head_partials(out_dim, in_dim, x_format);
+    if (pairs > (long)kNoAllocPairs)
+      return fail(RZ_EINVAL,
+                  "%s: the argmax needs %ld (value, row) pairs, the fixed scratch holds %zu "
+                  "(%zu bytes); use rz_lm_head_q4_0 with a workspace",
+                  what, pairs, kNoAllocPairs, kNoAllocPairs * 8);
+    void* sp = nullptr;
+    if (int rc = scratch_for_current_device(what, static_cast<hipStream_t>(stream), &sp)) return rc;
+    part_val = static_cast<float*>(sp);
+    part_idx = reinterpret_cast<int*>(static_cast<char*>(sp) + kNoAllocPairs * 4);
   }
   return launch_status(rz::launch_q4_0_lm_head(static_cast<const uint8_t*>(w_q4_0), x, x_format,
                                                bias, logits, out_dim, in_dim, argmax_idx,

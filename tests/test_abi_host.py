@@ -45,7 +45,7 @@ def test_header_declares_the_four_operations():
                  "rz_rmsnorm_q4k_q8_gemv_multi", "rz_rmsnorm_swiglu_ffn_q4k_add",
                  "rz_q4k_q8_gemv_f32_add",
                  "rz_swiglu_ffn_q4k_f32", "rz_lm_head_q4_0", "rz_lm_head_q4_0_workspace_bytes",
-                 "rz_gelu_ffn_q4_0",
+                 "rz_lm_head_q4_0_noalloc", "rz_gelu_ffn_q4_0",
                  "rz_last_error",
                  "rz_abi_version"):
         assert name in syms
@@ -361,6 +361,44 @@ def test_lm_head_accepts_bias_in_place_and_exact_workspace(lib):
                         ("rz_lm_head_q4_0", [P, P, 0, None, Y, 151936, 1024, IDX, IDX + 4, WS,
                                              2374 * 8, None])])
     assert [rc for rc, _ in res] == [rz.RZ_ELAUNCH, rz.RZ_ELAUNCH]
+
+
+W_FAR = P + (8 << 30)   # a weight matrix of over a gigabyte, clear of Y, IDX and WS
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, P, 0, None, Y, 151936, 1024, None, None, None), rz.RZ_EINVAL),
+    ((P, P, 2, None, Y, 151936, 1024, None, None, None), rz.RZ_EINVAL),
+    ((P, P, 0, None, Y, 151936, 1000, None, None, None), rz.RZ_EDIM),
+    ((P, P + 8, 0, None, Y, 151936, 1024, None, None, None), rz.RZ_EALIGN),
+    ((P, P, 0, Y + 4, Y, 151936, 1024, None, None, None), rz.RZ_EINVAL),        # bias overlaps
+    ((P, P, 0, None, Y, 151936, 1024, Y + 8, None, None), rz.RZ_EINVAL),        # idx in logits
+    # 600000 x 4096 with an argmax needs 37500 pairs: beyond the fixed array
+    ((W_FAR, P, 0, None, Y, 600000, 4096, IDX, None, None), rz.RZ_EINVAL),
+    ((W_FAR, P, 1, None, Y, 600000, 4096, None, IDX, None), rz.RZ_EINVAL),
+])
+def test_lm_head_noalloc_rejects(lib, args, code):
+    """The checks of rz_lm_head_q4_0, and a shape whose argmax needs more pairs
+    than the fixed array holds."""
+    assert _rc("rz_lm_head_q4_0_noalloc", *args) == code
+    assert _rc.last.startswith("rz_lm_head_q4_0_noalloc")
+
+
+def test_lm_head_noalloc_size_limit_message_and_accepts(lib):
+    """Beyond the fixed array the call says how many pairs it needs and what the
+    array holds; the largest shape within it, and any shape without an argmax,
+    pass validation (and then fail at launch for want of a device)."""
+    res = run_isolated([("rz_lm_head_q4_0_noalloc", [W_FAR, P, 0, None, Y, 600000, 4096, IDX,
+                                                     None, None]),
+                        # 524288 x 4096: 32768 pairs, exactly the array
+                        ("rz_lm_head_q4_0_noalloc", [W_FAR, P, 0, None, Y, 524288, 4096, IDX,
+                                                     None, None]),
+                        ("rz_lm_head_q4_0_noalloc", [W_FAR, P, 0, None, Y, 600000, 4096, None,
+                                                     None, None])])
+    assert res[0][0] == rz.RZ_EINVAL and "37500" in res[0][1] and "32768" in res[0][1]
+    assert res[1][0] == rz.RZ_ELAUNCH and res[2][0] == rz.RZ_ELAUNCH
+    assert rz.rz_lm_head_q4_0_workspace_bytes(524288, 4096, 0) == 32768 * 8
+    assert rz.NOALLOC_ARGMAX_PAIRS == 32768
 
 
 @pytest.mark.parametrize("args,code", [
