@@ -20,7 +20,8 @@ alone, the four attention projections on one shared activation (one
 multi-matrix launch, and four launches), the SwiGLU chain and its down
 projection, the Q4_0 LM head (fp32 and Q8_1 activation), 8 tokens sharing one
 weight pass, and the small 896 x 1024 case; a row of a measured configuration
-carries that configuration's oracle time.
+carries that configuration's oracle time, and every row the time of a plain
+streaming read of its own byte count (`read_ceiling_us`, `frac_of_ceiling`).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-rows]
 """
@@ -540,16 +541,21 @@ def time_rows(lib, rz, torch, dev, graph_time, copies, x, xq, y) -> dict:
     return rows
 
 
-def read_ceiling(torch, dev, graph_time, w_p, n_copies) -> dict:
-    """A plain streaming read of the same 33 MB weight copies, rotated the same
-    way (librz_stream_read.so, not part of the path): what a kernel that only
-    reads these bytes reaches on this part.  The best of a few grid sizes."""
+def _stream_read_lib():
     import ctypes
     path = os.path.join(ROOT, "q4_q8_integer_quantize_amd", "librz_stream_read.so")
     rd = ctypes.CDLL(path)
     rd.rz_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
                                   ctypes.c_void_p]
     rd.rz_stream_read.restype = ctypes.c_int
+    return rd
+
+
+def read_ceiling(torch, dev, graph_time, w_p, n_copies) -> dict:
+    """A plain streaming read of the same 33 MB weight copies, rotated the same
+    way (librz_stream_read.so, not part of the path): what a kernel that only
+    reads these bytes reaches on this part.  The best of a few grid sizes."""
+    rd = _stream_read_lib()
     sink = torch.zeros(256, dtype=torch.int32, device=dev)
     best = None
     for grid in (256, 512, 1024, 2048, 4096):
@@ -563,6 +569,38 @@ def read_ceiling(torch, dev, graph_time, w_p, n_copies) -> dict:
             "bytes": W_BYTES, "us": round(best[0] * 1e6, 3),
             "gbs": round(W_BYTES / best[0] / 1e9, 2), "grid": best[1],
             "frac": round(W_BYTES / best[0] / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def add_row_ceilings(rows: dict, torch, dev, graph_time) -> None:
+    """Next to every row, a plain streaming read of the row's algorithmic bytes
+    (rotated through 1 GiB, so every call reads from HBM, the best of four grid
+    sizes): a launch that moves a few MB pays the same fixed launch and ramp
+    cost as this read, and `frac_of_ceiling` says how close the row comes to
+    the read of its own size."""
+    rd = _stream_read_lib()
+    buf = torch.zeros(ROTATE_BYTES + (128 << 20), dtype=torch.uint8, device=dev)
+    sink = torch.zeros(256, dtype=torch.int32, device=dev)
+    base = buf.data_ptr()
+    cache = {}
+    for row in rows.values():
+        nb = -(-row["algo_bytes"] // 256) * 256
+        if nb > (128 << 20):
+            continue
+        if nb not in cache:
+            span = max(1, ROTATE_BYTES // nb)
+            best = None
+            for grid in (512, 1024, 2048, 4096):
+                def body(i, strm, grid=grid, nb=nb, span=span):
+                    if rd.rz_stream_read(base + (i % span) * nb, nb, sink.data_ptr(), grid, strm):
+                        raise RuntimeError("rz_stream_read failed")
+                sec = graph_time(body)
+                best = sec if best is None else min(best, sec)
+            cache[nb] = best
+        row["read_ceiling_us"] = round(cache[nb] * 1e6, 3)
+        row["frac_of_ceiling"] = round(cache[nb] * 1e6 / row["us"], 4)
+    del buf
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
 
 
 ONLY = {
@@ -731,6 +769,8 @@ def main() -> int:
     # every other kernel first: seconds of back-to-back kernels bring the GPU
     # clocks to their sustained state before the step is timed
     rows = None if args.no_rows else time_rows(lib, rz, torch, dev, graph_time, copies, x, xq, y)
+    if rows:
+        add_row_ceilings(rows, torch, dev, graph_time)
     step_s = graph_time(fused)            # the timed steps (whole hot path)
     ceiling = read_ceiling(torch, dev, graph_time, w_p, n_copies)
     ms_step = step_s * 1e3
