@@ -545,36 +545,52 @@ def _stream_read_lib():
     import ctypes
     path = os.path.join(ROOT, "q4_q8_integer_quantize_amd", "librz_stream_read.so")
     rd = ctypes.CDLL(path)
-    rd.rz_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
-                                  ctypes.c_void_p]
-    rd.rz_stream_read.restype = ctypes.c_int
+    for fn in (rd.rz_stream_read, rd.rz_stream_read_once):
+        fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                       ctypes.c_void_p]
+        fn.restype = ctypes.c_int
     return rd
+
+
+# read shapes tried for a ceiling: ("stride", grid) = grid-stride loop over `grid`
+# workgroups; ("once", u) = one-shot grid, u 16-byte chunks a thread
+READ_SHAPES = (("stride", 256), ("stride", 512), ("stride", 1024), ("stride", 2048),
+               ("stride", 4096), ("once", 1), ("once", 2), ("once", 4))
+
+
+def _read_call(rd, shape, ptr, nbytes, sink, strm) -> int:
+    kind, k = shape
+    if kind == "stride":
+        return rd.rz_stream_read(ptr, nbytes, sink, k, strm)
+    return rd.rz_stream_read_once(ptr, nbytes, sink, k, strm)
 
 
 def read_ceiling(torch, dev, graph_time, w_p, n_copies) -> dict:
     """A plain streaming read of the same 33 MB weight copies, rotated the same
     way (librz_stream_read.so, not part of the path): what a kernel that only
-    reads these bytes reaches on this part.  The best of a few grid sizes."""
+    reads these bytes reaches on this part.  The best of several read shapes."""
     rd = _stream_read_lib()
     sink = torch.zeros(256, dtype=torch.int32, device=dev)
     best = None
-    for grid in (256, 512, 1024, 2048, 4096):
-        def body(i, strm, grid=grid):
-            if rd.rz_stream_read(w_p[i % n_copies], W_BYTES, sink.data_ptr(), grid, strm):
+    for shape in READ_SHAPES:
+        def body(i, strm, shape=shape):
+            if _read_call(rd, shape, w_p[i % n_copies], W_BYTES, sink.data_ptr(), strm):
                 raise RuntimeError("rz_stream_read failed")
         sec = graph_time(body)
         if best is None or sec < best[0]:
-            best = (sec, grid)
-    return {"what": "plain non-temporal read of the step's weight bytes, same rotation",
+            best = (sec, shape)
+    return {"what": "plain non-temporal read of the step's weight bytes, same rotation, "
+                    "best of grid-stride and one-shot shapes",
             "bytes": W_BYTES, "us": round(best[0] * 1e6, 3),
-            "gbs": round(W_BYTES / best[0] / 1e9, 2), "grid": best[1],
+            "gbs": round(W_BYTES / best[0] / 1e9, 2),
+            "shape": "%s %d" % best[1],
             "frac": round(W_BYTES / best[0] / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def add_row_ceilings(rows: dict, torch, dev, graph_time) -> None:
     """Next to every row, a plain streaming read of the row's algorithmic bytes
-    (rotated through 1 GiB, so every call reads from HBM, the best of four grid
-    sizes): a launch that moves a few MB pays the same fixed launch and ramp
+    (rotated through 1 GiB, so every call reads from HBM, the best of four read
+    shapes): a launch that moves a few MB pays the same fixed launch and ramp
     cost as this read, and `frac_of_ceiling` says how close the row comes to
     the read of its own size."""
     rd = _stream_read_lib()
@@ -589,9 +605,9 @@ def add_row_ceilings(rows: dict, torch, dev, graph_time) -> None:
         if nb not in cache:
             span = max(1, ROTATE_BYTES // nb)
             best = None
-            for grid in (512, 1024, 2048, 4096):
-                def body(i, strm, grid=grid, nb=nb, span=span):
-                    if rd.rz_stream_read(base + (i % span) * nb, nb, sink.data_ptr(), grid, strm):
+            for shape in (("stride", 1024), ("stride", 2048), ("once", 1), ("once", 2)):
+                def body(i, strm, shape=shape, nb=nb, span=span):
+                    if _read_call(rd, shape, base + (i % span) * nb, nb, sink.data_ptr(), strm):
                         raise RuntimeError("rz_stream_read failed")
                 sec = graph_time(body)
                 best = sec if best is None else min(best, sec)
