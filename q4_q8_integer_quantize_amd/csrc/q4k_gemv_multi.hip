@@ -35,10 +35,14 @@ struct Q4KMultiArgs {
   uint8_t* xq_out;
 };
 
+// LATE (NORM only): request the weight tiles only once the row of x and gamma
+// has arrived, so the row's loads do not queue behind the whole launch's
+// weight stream.
 template <int TPR, int S, int R, int NT, int G, int P, bool XL = false, bool NORM = false,
-          bool XV = true>
+          bool XV = true, bool LATE = false>
 __global__ __launch_bounds__(256) void q4k_q8_gemv_multi_kernel(Q4KMultiArgs a) {
   static_assert(!NORM || (NT == 1 && !XL), "the RMSNorm prologue serves one token");
+  static_assert(!LATE || NORM, "LATE orders the RMSNorm prologue's loads");
   constexpr int RW = 8 / TPR;
   constexpr uint32_t kRowsPerGroup = (uint32_t)RW * R;
   const uint32_t nwaves = gridDim.x * 4u;
@@ -107,6 +111,8 @@ __global__ __launch_bounds__(256) void q4k_q8_gemv_multi_kernel(Q4KMultiArgs a) 
   else
     load_x_slots<TPR, S, NT>(xs, a.xq, (size_t)a.nsb * 8 * kQ8Bytes, a.nsb, a.n_tokens, ro);
   WTile<S, R> t[G];
+  // only the row's loads are outstanding here
+  if constexpr (LATE) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
   for (int k = 0; k < P && k < G; ++k) load_w_tile<TPR, S, R>(t[k], src_of(k), off, rb[k]);
   __builtin_amdgcn_sched_barrier(0);
@@ -143,20 +149,22 @@ __global__ __launch_bounds__(256) void q4k_q8_gemv_multi_kernel(Q4KMultiArgs a) 
   }
 }
 
-// NORM: groups per wave as the fused quantize + GEMV step (about 1024 waves;
-// every workgroup redoes the RMSNorm and the quantize, so fewer, deeper waves
-// pay for it once per CU): the Q, K, V set (3072 groups) at 4 groups a wave
-// 7.6 us, at 1 or 2 7.8-8.0 us, against 8.7 us of kernel time for
-// rz_rmsnorm_q8_1 then the multi-matrix launch, bit-identical outputs.
+// NORM: every workgroup redoes the RMSNorm and the quantize.  Up to 4096 row
+// groups take one group a wave, with the weights requested after the row (the
+// Q, K, V set, 3072 groups: 6.72 us, against 6.92-6.93 us at one or two groups
+// a wave with the weights requested first and 7.07-7.10 us at four; the
+// unfused pair of launches takes 8.1 us; outputs bit-identical).  Larger sets
+// take 8 groups a wave, so that fewer, deeper waves pay for the prologue.
 template <int TPR, int S, int G, bool XV>
 static hipError_t launch_multi_norm_g(const Q4KMultiArgs& a, hipStream_t st) {
   constexpr int R = S <= 2 ? 2 : 1;
   constexpr int P = G > 2 ? 2 : (G > 1 ? G - 1 : 1);
+  constexpr bool LATE = G == 1;
   const size_t lds = (size_t)S * TPR * 8 * kQ8Bytes;   // every slot, zero blocks past the row
   const long waves = ((long)a.group0[a.n_mats] + G - 1) / G;
   const unsigned grid = (unsigned)((waves + 3) / 4);
-  hipLaunchKernelGGL((q4k_q8_gemv_multi_kernel<TPR, S, R, 1, G, P, false, true, XV>), dim3(grid),
-                     dim3(256), lds, st, a);
+  hipLaunchKernelGGL((q4k_q8_gemv_multi_kernel<TPR, S, R, 1, G, P, false, true, XV, LATE>),
+                     dim3(grid), dim3(256), lds, st, a);
   return hipGetLastError();
 }
 
@@ -169,10 +177,7 @@ static hipError_t run_multi_norm(Q4KMultiArgs a, hipStream_t st) {
     a.group0[j + 1] = a.group0[j] + (j < a.n_mats ? ((uint32_t)a.out_dim[j] + rows_per_group - 1) /
                                                        rows_per_group
                                                  : 0u);
-  const long per_wave = ((long)a.group0[a.n_mats] + 1023) / 1024;
-  if (per_wave <= 1) return launch_multi_norm_g<TPR, S, 1, XV>(a, st);
-  if (per_wave <= 2) return launch_multi_norm_g<TPR, S, 2, XV>(a, st);
-  if (per_wave <= 4) return launch_multi_norm_g<TPR, S, 4, XV>(a, st);
+  if (a.group0[a.n_mats] <= 4096) return launch_multi_norm_g<TPR, S, 1, XV>(a, st);
   return launch_multi_norm_g<TPR, S, 8, XV>(a, st);
 }
 

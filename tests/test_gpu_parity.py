@@ -1463,6 +1463,7 @@ def test_graph_replays_match_eager(fused):
     (4096, 4096, [4096, 1024, 1024]),      # the Q, K, V projections
     (5120, 4999, [700, 128]),              # three slots, ragged n
     (16384, 16384, [129]),
+    (1024, 1024, [8200, 100]),             # over 4096 row groups: 8 groups a wave
 ])
 def test_rmsnorm_q4k_q8_gemv_multi_bit_identical(in_dim, n, out_dims):
     """One launch (RMSNorm + Q8_1 in every workgroup, then the GEMVs) equals
