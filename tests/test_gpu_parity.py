@@ -484,6 +484,86 @@ def test_q4k_batch8_full():
         assert_within(Y[t], y_ref, terms, "batch8 token %d" % t)
 
 
+def test_q4k_largest_matrix_sampled():
+    """The largest matrix the ABI accepts (just under 2 GiB, whose last bytes
+    sit 8 KB below 2**31, where a signed 32-bit offset would overflow): rows
+    at both ends and sampled rows in between, for one token, 8 tokens (the
+    matrix-core path in four column passes), the fused quantize + GEMV entry
+    and the fp32-activation GEMV, each against the oracle."""
+    in_dim = 16384
+    row_bytes = in_dim // 256 * 144
+    out_dim = (2 ** 31 - 1) // row_bytes              # 233016 rows, 2,147,475,456 bytes
+    banner("q4k largest matrix %d x %d" % (out_dim, in_dim))
+    blob = synth.q4k_weights(synth.rng(11, 1), out_dim, in_dim)
+    assert blob.nbytes < 2 ** 31 and blob.nbytes > 2 ** 31 - 2 * row_bytes
+    g = np.random.default_rng(11)
+    rows = np.unique(np.concatenate([np.arange(64), out_dim - 64 + np.arange(64),
+                                     g.choice(out_dim, 128, replace=False)]))
+    X = synth.activation(synth.rng(11, synth.T_ACT), in_dim, n_tokens=8)
+    xq = oracle.quantize_q8_1(X)
+    xq_bytes = oracle.q8_1_to_bytes(xq)
+    wd = dev_bytes(blob)
+    sub = blob[rows]
+    # 1 and 8 tokens on the GEMV entry
+    for nt in (1, 8):
+        y = empty_f32(out_dim * nt)
+        rz.rz_q4k_q8_gemv(wd, dev_bytes(xq_bytes[:nt]), y, out_dim, in_dim, nt)
+        Y = host(y).reshape(nt, out_dim)
+        for t in range(nt):
+            y_ref, terms = oracle.gemv_q4k_q8_int(sub, xq.token(t))
+            assert_within(Y[t, rows], y_ref, terms, "largest matrix, %d tokens, token %d" % (nt, t))
+    # the fused entry: quantize token 0 in the kernel, then the GEMV
+    y = empty_f32(out_dim)
+    rz.rz_q4k_q8_gemv_f32(wd, dev_f32(X[0]), in_dim, None, y, out_dim, in_dim)
+    y_ref, terms = oracle.gemv_q4k_q8_int(sub, xq.token(0))
+    assert_within(host(y)[rows], y_ref, terms, "largest matrix, fused quantize + GEMV")
+    # the fp32-activation GEMV
+    y = empty_f32(out_dim)
+    rz.rz_q4k_gemv(wd, dev_f32(X[0]), in_dim, y, out_dim, in_dim)
+    y_ref, terms = oracle.gemv_q4k_f32(sub, X[0])
+    assert_within(host(y)[rows], y_ref, terms, "largest matrix, fp32 activation")
+
+
+def test_q4_0_largest_matrix_sampled():
+    """The largest Q4_0 matrix the ABI accepts at the LM head's row length
+    (3,728,270 x 1024, less than one row below 2 GiB): rows at both ends and
+    sampled rows, fp32 and Q8_1 activations, against the oracle; with a bias
+    and the greedy token, the logits are the plain GEMV plus the bias bit for
+    bit and the chosen row is the first maximum of them."""
+    in_dim = 1024
+    row_bytes = in_dim // 32 * 18
+    out_dim = (2 ** 31 - 1) // row_bytes
+    banner("q4_0 largest matrix %d x %d" % (out_dim, in_dim))
+    blob = synth.q4_0_weights(synth.rng(12, 1), out_dim, in_dim)
+    assert 2 ** 31 - 2 * row_bytes < blob.nbytes < 2 ** 31
+    g = np.random.default_rng(12)
+    rows = np.unique(np.concatenate([np.arange(64), out_dim - 64 + np.arange(64),
+                                     g.choice(out_dim, 128, replace=False)]))
+    sub = blob[rows]
+    x = synth.activation(synth.rng(12, synth.T_ACT), in_dim)
+    xq = oracle.quantize_q8_1(x)
+    wd = dev_bytes(blob)
+    for fmt in (0, 1):
+        y = empty_f32(out_dim)
+        xd = dev_f32(x) if fmt == 0 else dev_bytes(oracle.q8_1_to_bytes(xq))
+        rz.rz_q4_0_gemv(wd, xd, fmt, y, out_dim, in_dim)
+        if fmt == 0:
+            y_ref, terms = oracle.gemv_q4_0_f32(sub, x)
+        else:
+            y_ref, terms = oracle.gemv_q4_0_q8_int(sub, xq)
+        assert_within(host(y)[rows], y_ref, terms, "largest Q4_0 matrix, x_format %d" % fmt)
+        bias = synth.activation(synth.rng(12, 2), out_dim)
+        logits = empty_f32(out_dim)
+        idx = __import__("torch").full((1,), -7, dtype=__import__("torch").int32, device="cuda")
+        ws = empty_bytes(rz.rz_lm_head_q4_0_workspace_bytes(out_dim, in_dim, fmt))
+        rz.rz_lm_head_q4_0(wd, xd, fmt, dev_f32(bias), logits, out_dim, in_dim, idx, None, ws)
+        lg = host(logits)
+        # one column pass at 1024 values: logits are fl32(W x + bias) bit for bit
+        mm = first_mismatch(lg, (host(y) + bias).astype(np.float32))
+        assert mm is None, "logit %s fused=%r plain+bias=%r (%d differ)" % mm
+        assert int(host(idx)[0]) == oracle.argmax_first(lg)
+
+
 # ------------------------------------------------------------------ Q4_0
 def test_q4_0_hand_worked_block_gpu():
     banner("q4_0 hand-worked block")
