@@ -50,7 +50,7 @@ from .swiglu import (silu, silu_grad, silu_curv, swiglu, ffn_swiglu_q4k, ffn_swi
                      h_tolerance)
 from .tolerance import gemv_tolerance, GEMV_REL, GEMV_ABS
 from .norm import rmsnorm, rmsnorm_tolerance, residual_add
-from .lm_head import lm_head_q4_0, argmax_first
+from .lm_head import lm_head_q4_0, argmax_first, topk_first
 from .gelu import gelu, gelu_grad, gelu_h_tolerance, ffn_gelu_q4_0
 
 __all__ = [
@@ -62,6 +62,6 @@ __all__ = [
     "silu", "silu_grad", "silu_curv", "swiglu", "ffn_swiglu_q4k", "ffn_swiglu_q4k_f32", "h_tolerance",
     "gemv_tolerance", "GEMV_REL", "GEMV_ABS",
     "rmsnorm", "rmsnorm_tolerance", "residual_add",
-    "lm_head_q4_0", "argmax_first",
+    "lm_head_q4_0", "argmax_first", "topk_first",
     "gelu", "gelu_grad", "gelu_h_tolerance", "ffn_gelu_q4_0",
 ]

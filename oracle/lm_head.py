@@ -12,7 +12,9 @@ Sources:
 
 The pages stop at the downloaded logits.  The greedy choice made from them is
 read here as the index of the largest logit, the smallest such index when
-several are equal, so that the choice is unique.
+several are equal, so that the choice is unique.  The top-k selection (the k
+candidates a sampler draws from) is read the same way: the k largest logits
+in descending order, equal values ordered by index, so that it is unique too.
 """
 from __future__ import annotations
 
@@ -47,3 +49,15 @@ def argmax_first(values) -> int:
         if v[i] > v[best]:
             best = i
     return best
+
+
+def topk_first(values, k: int):
+    """The k largest values and their indices, largest first; among equal
+    values the smaller index first.  -0.0 and +0.0 are equal.  Returns
+    (indices int64 [k], values [k]).  Written as a sort on the key
+    (-value, index), which is that order exactly."""
+    v = np.asarray(values)
+    assert v.ndim == 1 and 1 <= k <= v.size and np.all(np.isfinite(v))
+    order = sorted(range(v.size), key=lambda i: (-float(v[i]), i))[:k]
+    idx = np.asarray(order, np.int64)
+    return idx, v[idx]

@@ -716,6 +716,52 @@ def test_argmax_first_matches_numpy_on_random_ties():
         assert oracle.argmax_first(v) == int(np.argmax(v))
 
 
+def test_topk_first_hand_worked():
+    # [3, 1, 3, -0.0, +0.0, 2]: the two 3s in index order, then 2, 1, then the
+    # signed zeros (equal) in index order
+    v = np.array([3.0, 1.0, 3.0, -0.0, 0.0, 2.0], np.float32)
+    idx, val = oracle.topk_first(v, 4)
+    assert idx.tolist() == [0, 2, 5, 1] and val.tolist() == [3.0, 3.0, 2.0, 1.0]
+    idx, _ = oracle.topk_first(v, 6)
+    assert idx.tolist() == [0, 2, 5, 1, 3, 4]
+    idx, _ = oracle.topk_first(np.full(9, -1.5, np.float32), 3)
+    assert idx.tolist() == [0, 1, 2]
+
+
+def test_topk_first_by_repeated_argmax():
+    """Against an independent definition: the first of the top k is the greedy
+    token; remove it and the next is the greedy token of the rest; and so on.
+    Random small arrays with many ties (integers, both signed zeros)."""
+    g = np.random.default_rng(7)
+    for _ in range(60):
+        n = int(g.integers(1, 40))
+        v = g.integers(-3, 4, n).astype(np.float32)
+        v[g.random(n) < 0.2] = -0.0
+        k = int(g.integers(1, n + 1))
+        idx, val = oracle.topk_first(v, k)
+        rest = list(range(n))
+        want = []
+        for _ in range(k):
+            j = rest[oracle.argmax_first(v[rest])]
+            want.append(j)
+            rest.remove(j)
+        assert idx.tolist() == want
+        assert np.array_equal(val, v[want])
+
+
+def test_topk_first_k1_and_full_order():
+    g = np.random.default_rng(8)
+    v = g.standard_normal(1000).astype(np.float32)
+    v[::7] = v[3]                                   # ties
+    idx, _ = oracle.topk_first(v, 1)
+    assert idx.tolist() == [oracle.argmax_first(v)]
+    idx, val = oracle.topk_first(v, v.size)
+    assert sorted(idx.tolist()) == list(range(v.size))             # a permutation
+    assert np.all(val[:-1] >= val[1:])                            # descending
+    eq = val[:-1] == val[1:]
+    assert np.all(idx[:-1][eq] < idx[1:][eq])                     # ties by index
+
+
 def test_lm_head_bias_closed_form():
     """Uniform Q4_0 weights w and activation v give v*in_dim*w in every row; the
     bias shifts each row by its own value, and it moves the greedy token."""
