@@ -500,6 +500,26 @@ def time_rows(lib, rz, torch, dev, graph_time, copies, x, xq, y) -> dict:
                 HID_P, am_idx.data_ptr(), am_val.data_ptr(), ws.data_ptr(), ws_bytes, s))),
             lm_w + xbytes + 8 * VOCAB, lm_w,
             "rz_lm_head_q4_0 x_format=%d (bias + argmax epilogue, merge kernel)" % fmt)
+    # the same with the top 40 instead of the greedy token (GEMV + bias, then
+    # the slice and merge kernels of the selection)
+    tk_idx = torch.zeros(128, dtype=torch.int32, device=dev)
+    tk_val = torch.zeros(128, dtype=torch.float32, device=dev)
+    tk_ws = torch.zeros(lib.rz_topk_f32_workspace_bytes(VOCAB, 128), dtype=torch.uint8,
+                        device=dev)
+    rows["q4_0_lm_head_bias_topk40_151936x1024_fp32"] = row_entry(
+        graph_time(lambda i, s: check(lib.rz_lm_head_q4_0_topk(
+            lm_p[i % len(lm_p)], xl.data_ptr(), 0, lm_bias.data_ptr(), logits.data_ptr(), VOCAB,
+            HID_P, 40, tk_idx.data_ptr(), tk_val.data_ptr(), tk_ws.data_ptr(),
+            lib.rz_topk_f32_workspace_bytes(VOCAB, 40), s))),
+        lm_w + 4 * HID_P + 8 * VOCAB + 8 * 40, lm_w,
+        "rz_lm_head_q4_0_topk x_format=0, k=40 (GEMV + bias, top-k slice and merge kernels)")
+    # the selection alone over the 151936 logits
+    for k in (1, 40, 128):
+        rows["topk%d_151936" % k] = row_entry(
+            graph_time(lambda i, s, k=k: check(lib.rz_topk_f32(
+                logits.data_ptr(), VOCAB, k, tk_idx.data_ptr(), tk_val.data_ptr(),
+                tk_ws.data_ptr(), lib.rz_topk_f32_workspace_bytes(VOCAB, k), s))),
+            4 * VOCAB + 8 * k, 0, "rz_topk_f32 k=%d (slice kernel, merge kernel)" % k)
     del lm
 
     # GELU FFN of a phi-2-sized layer on Q4_0 weights, 2560 -> 10240 -> 2560, with biases

@@ -60,6 +60,7 @@ extern "C" {
 #define RZ_MAX_TOKENS 8
 #define RZ_MAX_MATS 8
 #define RZ_MAX_DIM (1 << 24)
+#define RZ_TOPK_MAX 128
 
 /* rz_q8_1_quantize -- fp32 activations to Q8_1 blocks.
  * Passage: realizar 0.8.5 src/cuda/executor/cached.rs,
@@ -334,6 +335,48 @@ size_t rz_lm_head_q4_0_workspace_bytes(int out_dim, int in_dim, int x_format);
 int rz_lm_head_q4_0_noalloc(const void* w_q4_0, const void* x, int x_format, const float* bias,
                             float* logits, int out_dim, int in_dim, int* argmax_idx,
                             float* argmax_val, void* stream);
+
+/* rz_topk_f32 -- the k largest of n fp32 values, on the device: the
+ * candidates a top-k sampler draws the next token from.
+ * Passage: realizar 0.8.5 src/cuda/executor/cached.rs,
+ * dispatch_lm_head_and_download (the logits go to the host, where the next
+ * token is chosen); selecting the k candidates here reads back 8 k bytes
+ * instead of 4 n.  The pages print no sampler: the k largest values in
+ * descending order, equal values in index order (-0 and +0 equal), which makes
+ * the selection unique; k = 1 is the greedy token of rz_lm_head_q4_0.
+ *   values    fp32 [n], 4-byte aligned; finite values assumed
+ *   n         1 .. RZ_MAX_DIM, at least k
+ *   k         1 .. RZ_TOPK_MAX; n and k must also satisfy
+ *             rz_topk_f32_workspace_bytes(n, k) > 0 (the candidates, n/2048
+ *             rounded up times k, must not exceed 16384: n <= 262144 at k = 128,
+ *             n <= 524288 at k <= 64, any n at k <= 2)
+ *   topk_idx  optional out: int32 [k], the values' indices, largest first
+ *   topk_val  optional out: fp32 [k], those values (at least one of the two)
+ *   workspace device memory of rz_topk_f32_workspace_bytes(n, k) bytes,
+ *             4-byte aligned; its contents on entry do not matter
+ * Two kernels run in order on `stream`.  The outputs and the workspace must
+ * not overlap the values or each other.
+ * Errors: RZ_EINVAL (also k out of range, too many candidates, a short
+ * workspace, overlaps), RZ_EDIM (n), RZ_EALIGN, RZ_ELAUNCH. */
+int rz_topk_f32(const float* values, int n, int k, int* topk_idx, float* topk_val, void* workspace,
+                size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace rz_topk_f32 needs (0 for arguments it would reject). */
+size_t rz_topk_f32_workspace_bytes(int n, int k);
+
+/* rz_lm_head_q4_0_topk -- the LM head with its top-k: rz_lm_head_q4_0's
+ * logits (with the bias, without the greedy token), then rz_topk_f32 over
+ * them, in one call (three kernels in order on `stream`).
+ * Passages: those of rz_lm_head_q4_0 and rz_topk_f32.
+ *   w_q4_0, x, x_format, bias, logits, out_dim, in_dim: as for rz_lm_head_q4_0
+ *   k, topk_idx, topk_val: as for rz_topk_f32 with n = out_dim
+ *   workspace rz_topk_f32_workspace_bytes(out_dim, k) bytes, 4-byte aligned
+ * The top-k outputs and the workspace must not overlap the weights, x, the
+ * bias, the logits or each other.
+ * Errors: those of rz_lm_head_q4_0 and rz_topk_f32. */
+int rz_lm_head_q4_0_topk(const void* w_q4_0, const void* x, int x_format, const float* bias,
+                         float* logits, int out_dim, int in_dim, int k, int* topk_idx,
+                         float* topk_val, void* workspace, size_t workspace_bytes, void* stream);
 
 /* rz_gelu_ffn_q4_0 -- the GELU FFN on Q4_0 weights and fp32 activations.
  * Passages: realizar 0.8.4 src/gpu/adapters/using.rs, ffn_standard_gpu (up

@@ -25,7 +25,8 @@ __all__ = [
     "rz_q4_0_gemv", "rz_swiglu_ffn_q4k", "rz_swiglu_ffn_q4k_add", "rz_q4k_gemv",
     "rz_swiglu_ffn_q4k_f32",
     "rz_lm_head_q4_0", "rz_lm_head_q4_0_workspace_bytes", "rz_lm_head_q4_0_noalloc",
-    "rz_gelu_ffn_q4_0", "q8_1_nbytes", "RzError", "NOALLOC_ARGMAX_PAIRS",
+    "rz_gelu_ffn_q4_0", "rz_topk_f32", "rz_topk_f32_workspace_bytes", "rz_lm_head_q4_0_topk",
+    "TOPK_MAX", "q8_1_nbytes", "RzError", "NOALLOC_ARGMAX_PAIRS",
 ]
 
 RZ_OK, RZ_EINVAL, RZ_EDIM, RZ_EALIGN, RZ_ELAUNCH = 0, -1, -2, -3, -4
@@ -34,6 +35,7 @@ Q4K_BLOCK_BYTES = 144
 Q4_0_BLOCK_BYTES = 18
 MAX_TOKENS = 8
 NOALLOC_ARGMAX_PAIRS = 32768
+TOPK_MAX = 128
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -79,13 +81,17 @@ def load_library() -> ctypes.CDLL:
     lib.rz_gelu_ffn_q4_0.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, vp]
     lib.rz_lm_head_q4_0_workspace_bytes.argtypes = [i, i, i]
     lib.rz_lm_head_q4_0_workspace_bytes.restype = ctypes.c_size_t
+    lib.rz_topk_f32.argtypes = [vp, i, i, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.rz_topk_f32_workspace_bytes.argtypes = [i, i]
+    lib.rz_topk_f32_workspace_bytes.restype = ctypes.c_size_t
+    lib.rz_lm_head_q4_0_topk.argtypes = [vp, vp, i, vp, vp, i, i, i, vp, vp, vp, ctypes.c_size_t, vp]
     for fn in ("rz_q8_1_quantize", "rz_rmsnorm_q8_1", "rz_q4k_q8_gemv", "rz_q4k_q8_gemv_add",
                "rz_q4k_q8_gemv_f32", "rz_q4k_q8_gemv_multi", "rz_rmsnorm_q4k_q8_gemv_multi",
                "rz_rmsnorm_swiglu_ffn_q4k_add", "rz_q4k_q8_gemv_f32_add",
                "rz_q4_0_gemv", "rz_swiglu_ffn_q4k",
                "rz_swiglu_ffn_q4k_add", "rz_q4k_gemv", "rz_swiglu_ffn_q4k_f32",
                "rz_lm_head_q4_0", "rz_lm_head_q4_0_noalloc", "rz_gelu_ffn_q4_0",
-               "rz_abi_version"):
+               "rz_topk_f32", "rz_lm_head_q4_0_topk", "rz_abi_version"):
         getattr(lib, fn).restype = i
     lib.rz_last_error.argtypes = []
     lib.rz_last_error.restype = ctypes.c_char_p
@@ -388,6 +394,47 @@ def rz_lm_head_q4_0_noalloc(w_q4_0, x, x_format: int, bias, logits, out_dim: int
     _check(load_library().rz_lm_head_q4_0_noalloc(_ptr(w_q4_0), _ptr(x), x_format, _ptr(bias),
                                                   _ptr(logits), out_dim, in_dim, _ptr(argmax_idx),
                                                   _ptr(argmax_val), _stream(stream)))
+
+
+def _nbytes(t) -> int:
+    return 0 if t is None or isinstance(t, int) else t.numel() * t.element_size()
+
+
+def rz_topk_f32_workspace_bytes(n: int, k: int) -> int:
+    """Workspace bytes rz_topk_f32 needs (0 for arguments it would reject)."""
+    return int(load_library().rz_topk_f32_workspace_bytes(n, k))
+
+
+def rz_topk_f32(values, n: int, k: int, topk_idx=None, topk_val=None, workspace=None,
+                stream=None) -> None:
+    """The k largest of values fp32 [n], largest first, equal values by index:
+    their indices into topk_idx (int32 [k]) and/or the values into topk_val
+    (fp32 [k]), using `workspace` (rz_topk_f32_workspace_bytes of them)."""
+    if n > 0 and 0 < k <= n:
+        _need(values, 4 * n, "values")
+        _need(topk_idx, 4 * k, "topk_idx")
+        _need(topk_val, 4 * k, "topk_val")
+    _check(load_library().rz_topk_f32(_ptr(values), n, k, _ptr(topk_idx), _ptr(topk_val),
+                                      _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def rz_lm_head_q4_0_topk(w_q4_0, x, x_format: int, bias, logits, out_dim: int, in_dim: int,
+                         k: int, topk_idx=None, topk_val=None, workspace=None,
+                         stream=None) -> None:
+    """rz_lm_head_q4_0's logits (bias may be None), then the top k of them as
+    rz_topk_f32 selects them, in one call."""
+    if in_dim > 0 and in_dim % 64 == 0 and out_dim > 0 and x_format in (0, 1):
+        _need(w_q4_0, out_dim * (in_dim // 32) * Q4_0_BLOCK_BYTES, "w_q4_0")
+        _need(x, 4 * in_dim if x_format == 0 else q8_1_nbytes(in_dim), "x")
+        _need(bias, 4 * out_dim, "bias")
+        _need(logits, 4 * out_dim, "logits")
+        if 0 < k <= out_dim:
+            _need(topk_idx, 4 * k, "topk_idx")
+            _need(topk_val, 4 * k, "topk_val")
+    _check(load_library().rz_lm_head_q4_0_topk(_ptr(w_q4_0), _ptr(x), x_format, _ptr(bias),
+                                               _ptr(logits), out_dim, in_dim, k, _ptr(topk_idx),
+                                               _ptr(topk_val), _ptr(workspace),
+                                               _nbytes(workspace), _stream(stream)))
 
 
 def rz_gelu_ffn_q4_0(w_up, w_down, x, up_bias, down_bias, h, y, hidden_dim: int, inter_dim: int,

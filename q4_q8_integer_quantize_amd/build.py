@@ -26,7 +26,7 @@ READ_LIB = os.path.join(PKG, "librz_stream_read.so")
 
 SOURCES = ["q8_1_quantize.hip", "q4k_gemv.hip", "q4k_gemv_f32.hip", "q4k_gemm_mfma.hip",
            "q4k_gemv_multi.hip", "q4_0_gemv.hip", "swiglu_ffn.hip", "rmsnorm_q8_1.hip",
-           "q4k_gemv_xf32.hip", "rz_abi.cpp"]
+           "q4k_gemv_xf32.hip", "topk.hip", "rz_abi.cpp"]
 ARCH = os.environ.get("RZ_OFFLOAD_ARCH", "gfx950")
 
 

@@ -604,6 +604,102 @@ int rz_lm_head_q4_0_noalloc(const void* w_q4_0, const void* x, int x_format, con
                        what);
 }
 
+// ----------------------------------------------------------------- top-k
+namespace {
+
+static_assert(rz::kTopkMaxK == RZ_TOPK_MAX, "top-k limit");
+
+// Candidates the top-k of n values keeps (slices x k), or -1 for arguments
+// rz_topk_f32 rejects.
+long topk_candidates(int n, int k) {
+  if (n <= 0 || n > RZ_MAX_DIM || k < 1 || k > RZ_TOPK_MAX || k > n) return -1;
+  const long m = rz::topk_slices(n) * k;
+  return m <= rz::kTopkMerge ? m : -1;
+}
+
+// The checks shared by rz_topk_f32 and rz_lm_head_q4_0_topk for the selection
+// over values[n] (`others` are the call's other buffers, which the top-k
+// outputs and the workspace must not overlap).
+int topk_check(const char* what, const float* values, int n, int k, const int* topk_idx,
+               const float* topk_val, const void* workspace, size_t workspace_bytes,
+               std::initializer_list<Span> others) {
+  if (!values || !workspace) return fail(RZ_EINVAL, "%s: null pointer", what);
+  if (!topk_idx && !topk_val)
+    return fail(RZ_EINVAL, "%s: neither topk_idx nor topk_val is given", what);
+  if (k < 1 || k > RZ_TOPK_MAX)
+    return fail(RZ_EINVAL, "%s: k=%d must be in 1..%d", what, k, RZ_TOPK_MAX);
+  if (k > n) return fail(RZ_EINVAL, "%s: k=%d is more than the %d values", what, k, n);
+  const long m = topk_candidates(n, k);
+  if (m < 0)
+    return fail(RZ_EINVAL, "%s: %d values in %ld slices of %d keep %ld candidates for k=%d, more "
+                "than the %d one workgroup merges",
+                what, n, rz::topk_slices(n), rz::kTopkSlice, rz::topk_slices(n) * k, k,
+                rz::kTopkMerge);
+  if (!aligned(values, 4) || !aligned(workspace, 4) || (topk_idx && !aligned(topk_idx, 4)) ||
+      (topk_val && !aligned(topk_val, 4)))
+    return fail(RZ_EALIGN, "%s: values, workspace and the top-k outputs must be 4-byte aligned",
+                what);
+  const size_t need = (size_t)m * 8u;
+  if (workspace_bytes < need)
+    return fail(RZ_EINVAL, "%s: workspace of %zu bytes, %zu needed", what, workspace_bytes, need);
+  const Span vspan{values, 4LL * n}, wsp{workspace, (long long)need}, ispan{topk_idx, 4LL * k},
+      fspan{topk_val, 4LL * k};
+  if (!clear_of(wsp, {vspan}) || !clear_of(wsp, others))
+    return fail(RZ_EINVAL, "%s: workspace must not overlap the values or the call's other buffers",
+                what);
+  if (!clear_of(ispan, {vspan, wsp, fspan}) || !clear_of(fspan, {vspan, wsp}) ||
+      !clear_of(ispan, others) || !clear_of(fspan, others))
+    return fail(RZ_EINVAL, "%s: the top-k outputs must not overlap the values, the workspace, "
+                "each other or the call's other buffers", what);
+  return RZ_OK;
+}
+
+}  // namespace
+
+size_t rz_topk_f32_workspace_bytes(int n, int k) {
+  const long m = topk_candidates(n, k);
+  return m < 0 ? 0 : (size_t)m * 8u;
+}
+
+int rz_topk_f32(const float* values, int n, int k, int* topk_idx, float* topk_val, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  const char* what = "rz_topk_f32";
+  if (int rc = check_dim(what, "n", n, 1)) return rc;
+  if (int rc = topk_check(what, values, n, k, topk_idx, topk_val, workspace, workspace_bytes, {}))
+    return rc;
+  const long m = topk_candidates(n, k);
+  unsigned* cand_key = static_cast<unsigned*>(workspace);
+  int* cand_idx = reinterpret_cast<int*>(static_cast<char*>(workspace) + (size_t)m * 4u);
+  return launch_status(rz::launch_topk_f32(values, n, k, topk_idx, topk_val, cand_key, cand_idx,
+                                           static_cast<hipStream_t>(stream)),
+                       what);
+}
+
+int rz_lm_head_q4_0_topk(const void* w_q4_0, const void* x, int x_format, const float* bias,
+                         float* logits, int out_dim, int in_dim, int k, int* topk_idx,
+                         float* topk_val, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* what = "rz_lm_head_q4_0_topk";
+  if (int rc = lm_head_check(what, w_q4_0, x, x_format, bias, logits, out_dim, in_dim, nullptr,
+                             nullptr))
+    return rc;
+  const Span wspan{w_q4_0, q4_0_bytes(out_dim, in_dim)},
+      xspan{x, x_format == 0 ? 4LL * in_dim : q8_bytes(1, in_dim)}, bspan{bias, 4LL * out_dim};
+  if (int rc = topk_check(what, logits, out_dim, k, topk_idx, topk_val, workspace, workspace_bytes,
+                          {wspan, xspan, bspan}))
+    return rc;
+  const long m = topk_candidates(out_dim, k);
+  unsigned* cand_key = static_cast<unsigned*>(workspace);
+  int* cand_idx = reinterpret_cast<int*>(static_cast<char*>(workspace) + (size_t)m * 4u);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const hipError_t e = rz::launch_q4_0_lm_head(static_cast<const uint8_t*>(w_q4_0), x, x_format,
+                                               bias, logits, out_dim, in_dim, nullptr, nullptr,
+                                               nullptr, nullptr, st);
+  if (e != hipSuccess) return launch_status(e, what);
+  return launch_status(rz::launch_topk_f32(logits, out_dim, k, topk_idx, topk_val, cand_key,
+                                           cand_idx, st),
+                       what);
+}
+
 int rz_gelu_ffn_q4_0(const void* w_up, const void* w_down, const float* x, const float* up_bias,
                      const float* down_bias, float* h, float* y, int hidden_dim, int inter_dim,
                      void* stream) {

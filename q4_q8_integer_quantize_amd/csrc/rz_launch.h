@@ -46,6 +46,16 @@ hipError_t launch_rmsnorm_q4k_q8_gemv_multi(int n_mats, const uint8_t* const* w,
                                             const float* gamma, float eps, int n,
                                             uint8_t* xq_out, int in_dim, hipStream_t stream);
 
+// The k largest of v[n] (largest first, equal values by index) into out_i /
+// out_v (either may be null), through cand_key / cand_idx of topk_slices(n) * k
+// entries each, at most kTopkMerge; 1 <= k <= min(n, kTopkMaxK).
+constexpr int kTopkSlice = 2048;    // values one slice workgroup selects from
+constexpr int kTopkMerge = 16384;   // candidates the merge workgroup selects from
+constexpr int kTopkMaxK = 128;
+long topk_slices(int n);
+hipError_t launch_topk_f32(const float* v, int n, int k, int* out_i, float* out_v,
+                           unsigned* cand_key, int* cand_idx, hipStream_t stream);
+
 // Q8_1 quantize of an fp32 activation fused into the Q4_K GEMV (1 token); with
 // r, y = W Q8_1(x) + r (r may be y).
 hipError_t launch_q4k_q8_gemv_f32(const uint8_t* w, const float* x, int n, uint8_t* xq_out,

@@ -46,6 +46,7 @@ def test_header_declares_the_four_operations():
                  "rz_q4k_q8_gemv_f32_add",
                  "rz_swiglu_ffn_q4k_f32", "rz_lm_head_q4_0", "rz_lm_head_q4_0_workspace_bytes",
                  "rz_lm_head_q4_0_noalloc", "rz_gelu_ffn_q4_0",
+                 "rz_topk_f32", "rz_topk_f32_workspace_bytes", "rz_lm_head_q4_0_topk",
                  "rz_last_error",
                  "rz_abi_version"):
         assert name in syms
@@ -521,6 +522,95 @@ def test_lm_head_outputs_must_not_overlap_inputs(lib):
     assert res[0][0] == rz.RZ_ELAUNCH
     for rc, msg in res[1:]:
         assert rc == rz.RZ_EINVAL and "overlap" in msg, msg
+
+
+
+def test_topk_workspace_bytes():
+    # One candidate (32-bit key + int32 index) per slice of 2048 values and
+    # selected entry: 151936 values are 75 slices.
+    assert rz.rz_topk_f32_workspace_bytes(151936, 40) == 75 * 40 * 8
+    assert rz.rz_topk_f32_workspace_bytes(1, 1) == 8
+    assert rz.rz_topk_f32_workspace_bytes(100, 100) == 100 * 8
+    assert rz.rz_topk_f32_workspace_bytes(262144, 128) == 16384 * 8
+    assert rz.rz_topk_f32_workspace_bytes(524288, 64) == 16384 * 8
+    assert rz.rz_topk_f32_workspace_bytes(1 << 24, 2) == 16384 * 8
+    for bad in ((0, 1), (7, 8), (10, 0), (1000, 129), (262145, 128), (524289, 64),
+                ((1 << 24) + 1, 1), ((1 << 24), 3)):
+        assert rz.rz_topk_f32_workspace_bytes(*bad) == 0, bad
+
+
+TK = 75 * 40 * 8    # workspace for 151936 values, k = 40
+@pytest.mark.parametrize("args,code", [
+    ((None, 151936, 40, IDX, None, WS, TK, None), rz.RZ_EINVAL),           # null values
+    ((Y, 151936, 40, IDX, None, None, TK, None), rz.RZ_EINVAL),            # null workspace
+    ((Y, 151936, 40, None, None, WS, TK, None), rz.RZ_EINVAL),             # no output
+    ((Y, 151936, 0, IDX, None, WS, TK, None), rz.RZ_EINVAL),               # k 0
+    ((Y, 151936, 129, IDX, None, WS, 1 << 20, None), rz.RZ_EINVAL),        # k above 128
+    ((Y, 7, 8, IDX, None, WS, 64, None), rz.RZ_EINVAL),                    # k above n
+    ((Y, 300000, 128, IDX, None, WS, 1 << 20, None), rz.RZ_EINVAL),        # 18816 candidates
+    ((Y, 0, 1, IDX, None, WS, 8, None), rz.RZ_EDIM),
+    ((Y, (1 << 24) + 1, 1, IDX, None, WS, 1 << 20, None), rz.RZ_EDIM),
+    ((Y, 151936, 40, IDX, None, WS, TK - 1, None), rz.RZ_EINVAL),          # short workspace
+    ((Y + 2, 151936, 40, IDX, None, WS, TK, None), rz.RZ_EALIGN),
+    ((Y, 151936, 40, IDX + 2, None, WS, TK, None), rz.RZ_EALIGN),
+    ((Y, 151936, 40, None, IDX + 2, WS, TK, None), rz.RZ_EALIGN),
+    ((Y, 151936, 40, IDX, None, WS + 2, TK, None), rz.RZ_EALIGN),
+    ((Y, 151936, 40, IDX, None, Y + 64, TK, None), rz.RZ_EINVAL),          # workspace on values
+    ((Y, 151936, 40, Y + 4, None, WS, TK, None), rz.RZ_EINVAL),            # idx on values
+    ((Y, 151936, 40, WS + 8, None, WS, TK, None), rz.RZ_EINVAL),           # idx in workspace
+    ((Y, 151936, 40, IDX, IDX + 64, WS, TK, None), rz.RZ_EINVAL),          # val on idx
+    ((Y, 151936, 40, None, Y + 4, WS, TK, None), rz.RZ_EINVAL),            # val on values
+])
+def test_topk_rejects(lib, args, code):
+    assert _rc("rz_topk_f32", *args) == code
+    assert _rc.last.startswith("rz_topk_f32"), _rc.last
+
+
+def test_topk_accepts_limits_and_exact_workspace(lib):
+    res = run_isolated([("rz_topk_f32", [Y, 151936, 40, IDX, IDX + 160, WS, TK, None]),
+                        ("rz_topk_f32", [Y, 1, 1, IDX, None, WS, 8, None]),
+                        ("rz_topk_f32", [Y, 128, 128, None, IDX, WS, 1024, None]),
+                        ("rz_topk_f32", [Y, 262144, 128, IDX, None, WS, 131072, None]),
+                        ("rz_topk_f32", [Y, 524288, 64, IDX, None, WS, 131072, None]),
+                        ("rz_topk_f32", [Y, 1 << 24, 2, IDX, None, WS, 131072, None])])
+    assert [rc for rc, _ in res] == [rz.RZ_ELAUNCH] * 6, res
+
+
+LM_TK = [P, H, 0, None, Y, 151936, 1024, 40, IDX, IDX + 160, WS, TK, None]
+@pytest.mark.parametrize("change,code", [
+    ({0: None}, rz.RZ_EINVAL),                        # null weights
+    ({6: 1000}, rz.RZ_EDIM),                          # in_dim not a multiple of 32
+    ({2: 2}, rz.RZ_EINVAL),                           # x_format
+    ({7: 0}, rz.RZ_EINVAL),                           # k 0
+    ({7: 129}, rz.RZ_EINVAL),                         # k above 128
+    ({8: None, 9: None}, rz.RZ_EINVAL),               # no top-k output
+    ({10: None}, rz.RZ_EINVAL),                       # no workspace
+    ({11: TK - 1}, rz.RZ_EINVAL),                     # short workspace
+    ({5: 600000, 7: 128}, rz.RZ_EINVAL),              # too many candidates
+    ({10: P + 64}, rz.RZ_EINVAL),                     # workspace on the weights
+    ({10: Y + 64}, rz.RZ_EINVAL),                     # workspace on the logits
+    ({8: H + 8}, rz.RZ_EINVAL),                       # idx on x
+    ({3: W_FAR, 9: W_FAR + 64}, rz.RZ_EINVAL),        # val on the bias
+    ({8: Y + 8}, rz.RZ_EINVAL),                       # idx on the logits
+    ({8: IDX + 2}, rz.RZ_EALIGN),
+    ({10: WS + 2}, rz.RZ_EALIGN),
+])
+def test_lm_head_topk_rejects(lib, change, code):
+    args = list(LM_TK)
+    for i, v in change.items():
+        args[i] = v
+    assert _rc("rz_lm_head_q4_0_topk", *args) == code
+    assert _rc.last.startswith("rz_lm_head_q4_0_topk"), _rc.last
+
+
+def test_lm_head_topk_accepts(lib):
+    q8 = list(LM_TK)
+    q8[2] = 1
+    bias = list(LM_TK)
+    bias[3] = W_FAR
+    res = run_isolated([("rz_lm_head_q4_0_topk", LM_TK), ("rz_lm_head_q4_0_topk", q8),
+                        ("rz_lm_head_q4_0_topk", bias)])
+    assert [rc for rc, _ in res] == [rz.RZ_ELAUNCH] * 3, res
 
 
 @pytest.mark.parametrize("args,code", [

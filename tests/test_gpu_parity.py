@@ -1200,6 +1200,139 @@ def test_lm_head_bias_is_logits(fmt, out_dim, in_dim):
     assert int(host(i2)[0]) == idx and host(v2)[0] == val
 
 
+# ------------------------------------------------------------------ top-k
+def gpu_topk(values, k, want_idx=True, want_val=True):
+    torch = __import__("torch")
+    n = values.size
+    idx = torch.full((k,), -7, dtype=torch.int32, device="cuda") if want_idx else None
+    val = empty_f32(k) if want_val else None
+    ws = empty_bytes(rz.rz_topk_f32_workspace_bytes(n, k))
+    rz.rz_topk_f32(dev_f32(values), n, k, idx, val, ws)
+    return (host(idx) if want_idx else None), (host(val) if want_val else None)
+
+
+def _topk_values(kind, n, seed):
+    g = np.random.default_rng(seed)
+    if kind == "normal":        # logits-like, all distinct with high probability
+        return g.standard_normal(n).astype(np.float32)
+    if kind == "ties":          # seven values only: long runs of equal values
+        return g.integers(-3, 4, n).astype(np.float32)
+    if kind == "zeros":         # -0 and +0 mixed under a few negatives: ties across signs
+        v = np.where(g.random(n) < 0.5, np.float32(-0.0), np.float32(0.0)).astype(np.float32)
+        v[g.random(n) < 0.1] = -1.0
+        return v
+    if kind == "ulps":          # 1 + j ulp, j < 4096: keys differ in their low 12 bits only
+        return (1.0 + g.integers(0, 4096, n) * 2.0 ** -23).astype(np.float32)
+    if kind == "ascending":     # the largest values in the last slice
+        return np.arange(n, dtype=np.float32) * np.float32(0.5)
+    if kind == "descending":
+        return -np.arange(n, dtype=np.float32)
+    raise ValueError(kind)
+
+
+def _check_topk(values, k):
+    idx, val = gpu_topk(values, k)
+    want_i, want_v = oracle.topk_first(values, k)
+    mm = first_mismatch(idx, want_i.astype(np.int32))
+    assert mm is None, "topk index %s gpu=%r oracle=%r (%d differ)" % mm
+    # the values bit for bit (the sign of a zero included)
+    assert np.array_equal(val.view(np.uint32), want_v.astype(np.float32).view(np.uint32))
+
+
+_TOPK_CASES = [(n, k) for n in (1, 7, 128, 1000, 2048, 2049, 4097, 20000, 151936, 262144)
+               for k in (1, 5, 40, 128) if k <= n]
+
+
+@pytest.mark.parametrize("kind", ["normal", "ties", "zeros", "ulps", "ascending", "descending"])
+@pytest.mark.parametrize("n,k", _TOPK_CASES)
+def test_topk_matches_oracle(kind, n, k):
+    """One slice (n up to 2048, padded), several slices with a ragged last one,
+    and 128 slices of 2048 at k = 128 (16384 candidates, the merge's
+    capacity): indices and values equal to the oracle's."""
+    banner("topk", kind, n, k)
+    _check_topk(_topk_values(kind, n, n * 131 + k), k)
+
+
+def test_topk_optional_outputs_and_workspace_reuse():
+    """Only indices, only values, and one workspace used by calls of different
+    sizes in a row (it holds no state)."""
+    banner("topk options")
+    torch = __import__("torch")
+    v = _topk_values("normal", 151936, 70)
+    want_i, want_v = oracle.topk_first(v, 40)
+    i_only, _ = gpu_topk(v, 40, want_val=False)
+    _, v_only = gpu_topk(v, 40, want_idx=False)
+    assert np.array_equal(i_only, want_i) and np.array_equal(v_only, want_v)
+    ws = empty_bytes(rz.rz_topk_f32_workspace_bytes(262144, 128))
+    idx = torch.full((128,), -7, dtype=torch.int32, device="cuda")
+    for n, k in ((262144, 128), (5000, 3), (151936, 40)):
+        vals = _topk_values("ties", n, n)
+        rz.rz_topk_f32(dev_f32(vals), n, k, idx, None, ws)
+        assert np.array_equal(host(idx)[:k], oracle.topk_first(vals, k)[0])
+
+
+@pytest.mark.parametrize("n,k", [(524288, 64), (1 << 20, 32), (1 << 24, 1), (1 << 24, 2)])
+def test_topk_planted_at_largest_sizes(n, k):
+    """Sizes the oracle's sort would take minutes over: values drawn from
+    [-1, 1), then k entries set above 1 at spread-out positions (two of them
+    equal, so their order is by index).  The top k are exactly those entries,
+    largest first."""
+    banner("topk planted", n, k)
+    g = np.random.default_rng(n + k)
+    v = (g.random(n, dtype=np.float32) * 2 - 1).astype(np.float32)
+    pos = np.sort(g.choice(n, size=k, replace=False))
+    planted = 2.0 + np.arange(k, dtype=np.float32)
+    planted[-1] = planted[0] if k > 1 else planted[-1]   # a tie between the first and last position
+    v[pos] = planted
+    order = sorted(range(k), key=lambda j: (-float(planted[j]), int(pos[j])))
+    want_i = pos[order].astype(np.int32)
+    idx, val = gpu_topk(v, k)
+    assert np.array_equal(idx, want_i), (idx[:8], want_i[:8])
+    assert np.array_equal(val, v[want_i])
+
+
+def test_topk_merge_capacity_boundaries():
+    """The largest n the merge takes at k = 128 and 64 (16384 candidates) and
+    the rejection one value beyond."""
+    banner("topk capacity")
+    for n, k in ((262144, 128), (524288, 64)):
+        assert rz.rz_topk_f32_workspace_bytes(n, k) == 16384 * 8
+        assert rz.rz_topk_f32_workspace_bytes(n + 1, k) == 0
+        with pytest.raises(rz.RzError):
+            rz.rz_topk_f32(dev_f32(np.zeros(n + 1, np.float32)), n + 1, k,
+                           empty_f32(k), None, empty_bytes(1 << 17))
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_lm_head_topk_full(fmt):
+    """151936 x 1024 with bias: the logits bit-equal to rz_lm_head_q4_0's, the
+    top 40 equal to the oracle's selection over those logits, and k = 1 the
+    greedy token."""
+    banner("lm head topk", fmt)
+    torch = __import__("torch")
+    w = synth.WORKLOADS["lm_head_q4_0"]
+    out_dim, in_dim = w["out_dim"], w["in_dim"]
+    blob = synth.q4_0_weights(synth.rng(3, synth.T_W0), out_dim, in_dim)
+    x = _padded(synth.activation(synth.rng(3, synth.T_ACT), w["n"]), in_dim)
+    xin = x if fmt == 0 else oracle.q8_1_to_bytes(oracle.quantize_q8_1(x))
+    bias = synth.activation(synth.rng(3, 8), out_dim)
+    lg, best, best_v = gpu_lm_head(blob, xin, fmt, bias)
+    wd, bd = dev_bytes(blob), dev_f32(bias)
+    xd = dev_f32(xin) if fmt == 0 else dev_bytes(xin)
+    for k in (1, 40, 128):
+        logits = empty_f32(out_dim)
+        idx = torch.full((k,), -7, dtype=torch.int32, device="cuda")
+        val = empty_f32(k)
+        ws = empty_bytes(rz.rz_topk_f32_workspace_bytes(out_dim, k))
+        rz.rz_lm_head_q4_0_topk(wd, xd, fmt, bd, logits, out_dim, in_dim, k, idx, val, ws)
+        got = host(logits)
+        assert np.array_equal(got.view(np.uint32), lg.view(np.uint32))
+        want_i, want_v = oracle.topk_first(got, k)
+        assert np.array_equal(host(idx), want_i.astype(np.int32))
+        assert np.array_equal(host(val).view(np.uint32), want_v.view(np.uint32))
+        assert int(host(idx)[0]) == best and host(val)[0] == best_v
+
+
 @pytest.mark.parametrize("hidden,inter", [(256, 16384), (16384, 256)])
 def test_gelu_ffn_bias_is_output(hidden, inter):
     """up_bias may be h and down_bias may be y: the same h and y as with
