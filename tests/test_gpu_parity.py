@@ -1587,8 +1587,9 @@ def test_minimum_alignments_bit_identical():
 def test_graph_replays_match_eager(fused):
     """A decode-layer-shaped sequence -- RMSNorm + Q8_1, the attention
     projections in one launch, the O projection with its residual, RMSNorm
-    again, the SwiGLU chain with its residual, and the LM head with bias and
-    greedy token -- captured in one HIP graph and replayed three times, with
+    again, the SwiGLU chain with its residual, the LM head with bias and
+    greedy token, and the top 40 of its logits -- captured in one HIP graph
+    and replayed three times, with
     eager work and synchronisations between replays, gives every replay the
     bytes of the eager run.  Nothing in the library records memsets or
     allocations, so the graph has kernel nodes only.  `fused`: the RMSNorm runs
@@ -1615,7 +1616,10 @@ def test_graph_replays_match_eager(fused):
     idx = torch.empty(1, dtype=torch.int32, device="cuda")
     val = torch.empty(1, dtype=torch.float32, device="cuda")
     ws = torch.empty(rz.rz_lm_head_q4_0_workspace_bytes(V, H, 0), dtype=torch.uint8, device="cuda")
-    outs = (hidden, xq, q, k_, v, h, hq, logits, idx, val)
+    tk_idx = torch.empty(40, dtype=torch.int32, device="cuda")
+    tk_val = torch.empty(40, dtype=torch.float32, device="cuda")
+    tk_ws = torch.empty(rz.rz_topk_f32_workspace_bytes(V, 40), dtype=torch.uint8, device="cuda")
+    outs = (hidden, xq, q, k_, v, h, hq, logits, idx, val, tk_idx, tk_val)
 
     def layer(fused):
         hidden.copy_(x0)
@@ -1639,6 +1643,7 @@ def test_graph_replays_match_eager(fused):
             rz.rz_rmsnorm_q8_1(hidden, gam2, 1e-5, H, H, 1, None, xq)
             rz.rz_swiglu_ffn_q4k_add(wg, wu, wd, xq, h, hq, hidden, hidden, None, H, I)
         rz.rz_lm_head_q4_0(wl, hidden, 0, bias, logits, V, H, idx, val, ws)
+        rz.rz_topk_f32(logits, V, 40, tk_idx, tk_val, tk_ws)
 
     layer(False)
     torch.cuda.synchronize()
