@@ -1304,6 +1304,34 @@ def test_topk_merge_capacity_boundaries():
 
 
 @pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("out_dim,in_dim,k", [(7, 64, 7), (1000, 1024, 40), (3000, 16384, 128),
+                                              (4100, 32768, 5)])
+def test_lm_head_topk_shapes(fmt, out_dim, in_dim, k):
+    """Small vocabularies (k = out_dim), one column pass and several (the
+    selection runs on the finished logits): logits bit-equal to
+    rz_lm_head_q4_0's, the top k equal to the oracle's selection over them."""
+    banner("lm head topk", fmt, out_dim, in_dim, k)
+    torch = __import__("torch")
+    blob = synth.q4_0_weights(synth.rng(64, in_dim), out_dim, in_dim)
+    x = synth.activation(synth.rng(64, 1), in_dim)
+    xin = x if fmt == 0 else oracle.q8_1_to_bytes(oracle.quantize_q8_1(x))
+    bias = synth.activation(synth.rng(64, 2), out_dim)
+    lg, _, _ = gpu_lm_head(blob, xin, fmt, bias)
+    xd = dev_f32(xin) if fmt == 0 else dev_bytes(xin)
+    logits = empty_f32(out_dim)
+    idx = torch.full((k,), -7, dtype=torch.int32, device="cuda")
+    val = empty_f32(k)
+    ws = empty_bytes(rz.rz_topk_f32_workspace_bytes(out_dim, k))
+    rz.rz_lm_head_q4_0_topk(dev_bytes(blob), xd, fmt, dev_f32(bias), logits, out_dim, in_dim, k,
+                            idx, val, ws)
+    got = host(logits)
+    assert np.array_equal(got.view(np.uint32), lg.view(np.uint32))
+    want_i, want_v = oracle.topk_first(got, k)
+    assert np.array_equal(host(idx), want_i.astype(np.int32))
+    assert np.array_equal(host(val).view(np.uint32), want_v.view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
 def test_lm_head_topk_full(fmt):
     """151936 x 1024 with bias: the logits bit-equal to rz_lm_head_q4_0's, the
     top 40 equal to the oracle's selection over those logits, and k = 1 the
