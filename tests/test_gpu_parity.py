@@ -1241,14 +1241,18 @@ def _check_topk(values, k):
 
 _TOPK_CASES = [(n, k) for n in (1, 7, 128, 1000, 2048, 2049, 4097, 20000, 151936, 262144)
                for k in (1, 5, 40, 128) if k <= n]
+# the merge's shape changes at 2048, 4096 and 8192 candidates (slices x k):
+# exactly each, and one slice more
+_TOPK_CASES += [(n, 128) for n in (32768, 32769, 65536, 65537, 131072, 131073)]
 
 
 @pytest.mark.parametrize("kind", ["normal", "ties", "zeros", "ulps", "ascending", "descending"])
 @pytest.mark.parametrize("n,k", _TOPK_CASES)
 def test_topk_matches_oracle(kind, n, k):
     """One slice (n up to 2048, padded), several slices with a ragged last one,
-    and 128 slices of 2048 at k = 128 (16384 candidates, the merge's
-    capacity): indices and values equal to the oracle's."""
+    128 slices of 2048 at k = 128 (16384 candidates, the merge's capacity),
+    and candidate counts on both sides of each change of the merge's shape:
+    indices and values equal to the oracle's."""
     banner("topk", kind, n, k)
     _check_topk(_topk_values(kind, n, n * 131 + k), k)
 
