@@ -1706,6 +1706,68 @@ def test_graph_replays_match_eager(fused):
             assert np.array_equal(_bits(t), eager[k]), "replay %d: output %d differs from eager" % (rep, k)
 
 
+def test_concurrent_streams_match_sequential():
+    """The library keeps no state between calls: three independent call chains
+    issued on three streams (default priority) at once -- quantize + GEMV with
+    the Q8_1 side output, the SwiGLU chain with its residual, and the LM head
+    with bias and its top 40 -- repeated with no synchronisation between the
+    rounds, give every round the bytes of the same chains run one after
+    another on one stream."""
+    import torch
+    banner("concurrent streams")
+    H, I, V = 4096, 2816, 20000
+    g = lambda k: synth.rng(90, k)
+    w1 = dev_bytes(synth.q4k_weights(g(1), 14336, H))
+    wg, wu = (dev_bytes(synth.q4k_weights(g(k), I, H)) for k in (2, 3))
+    wd = dev_bytes(synth.q4k_weights(g(4), H, I))
+    wl = dev_bytes(synth.q4_0_weights(g(5), V, H))
+    x1, x2, x3 = (dev_f32(synth.activation(g(10 + k), H)) for k in range(3))
+    bias = dev_f32(synth.activation(g(14), V))
+
+    def buffers():
+        return dict(xq1=torch.empty(rz.q8_1_nbytes(H), dtype=torch.uint8, device="cuda"),
+                    y1=torch.empty(14336, dtype=torch.float32, device="cuda"),
+                    xq2=torch.empty(rz.q8_1_nbytes(H), dtype=torch.uint8, device="cuda"),
+                    h=torch.empty(I, dtype=torch.float32, device="cuda"),
+                    hq=torch.empty(rz.q8_1_nbytes(I), dtype=torch.uint8, device="cuda"),
+                    hid=torch.empty(H, dtype=torch.float32, device="cuda"),
+                    logits=torch.empty(V, dtype=torch.float32, device="cuda"),
+                    ti=torch.empty(40, dtype=torch.int32, device="cuda"),
+                    tv=torch.empty(40, dtype=torch.float32, device="cuda"),
+                    ws=torch.empty(rz.rz_topk_f32_workspace_bytes(V, 40), dtype=torch.uint8,
+                                   device="cuda"))
+
+    def chain(b, which, stream):
+        if which == 0:
+            rz.rz_q4k_q8_gemv_f32(w1, x1, H, b["xq1"], b["y1"], 14336, H, stream=stream)
+        elif which == 1:
+            b["hid"].copy_(x2)
+            rz.rz_q8_1_quantize(x2, H, H, 1, b["xq2"], stream=stream)
+            rz.rz_swiglu_ffn_q4k_add(wg, wu, wd, b["xq2"], b["h"], b["hq"], b["hid"], b["hid"],
+                                     None, H, I, stream=stream)
+        else:
+            rz.rz_lm_head_q4_0_topk(wl, x3, 0, bias, b["logits"], V, H, 40, b["ti"], b["tv"],
+                                    b["ws"], stream=stream)
+
+    ref = buffers()
+    for which in range(3):
+        chain(ref, which, None)
+    torch.cuda.synchronize()
+    want = {k: _bits(t) for k, t in ref.items() if k != "ws"}
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    rounds = [buffers() for _ in range(4)]
+    torch.cuda.synchronize()
+    for b in rounds:
+        for which, st in enumerate(streams):
+            with torch.cuda.stream(st):
+                chain(b, which, st)
+    torch.cuda.synchronize()
+    for n, b in enumerate(rounds):
+        for k, t in b.items():
+            if k != "ws":
+                assert np.array_equal(_bits(t), want[k]), "round %d: %s differs" % (n, k)
+
+
 # ------------------------------------------------------------------ RMSNorm fused into the GEMV
 @pytest.mark.parametrize("in_dim,n,out_dims", [
     (1024, 1000, [300, 64]),               # four teams a row
