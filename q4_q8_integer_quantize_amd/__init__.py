@@ -51,8 +51,11 @@ def library_path() -> str:
     return os.path.join(_HERE, "librz.so")
 
 
-def load_library() -> ctypes.CDLL:
-    """Load librz.so (built in-tree).  Raises if it is missing."""
+def load_library(preload_torch: bool = True) -> ctypes.CDLL:
+    """Load librz.so (built in-tree).  Raises if it is missing.  preload_torch
+    False skips importing torch first; only for processes that never run a
+    kernel (host-side argument checks), where a second HIP runtime is
+    harmless."""
     global _LIB
     if _LIB is not None:
         return _LIB
@@ -60,6 +63,16 @@ def load_library() -> ctypes.CDLL:
     if not os.path.exists(path):
         raise RuntimeError("librz.so is not built (%s); run "
                            "`python -m q4_q8_integer_quantize_amd.build`" % path)
+    # One HIP runtime per process: torch ships its own libamdhip64 and asks
+    # for it by its unversioned name, so if librz.so (which asks for
+    # libamdhip64.so.7) came first, torch would load a second copy and the two
+    # would not share devices or memory.  With torch loaded first, librz.so
+    # binds to torch's copy.
+    if preload_torch:
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
     lib = ctypes.CDLL(path)
     vp, i = ctypes.c_void_p, ctypes.c_int
     lib.rz_q8_1_quantize.argtypes = [vp, i, i, i, vp, vp]

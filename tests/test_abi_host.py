@@ -66,7 +66,7 @@ _CHILD = r"""
 import json, sys
 sys.path.insert(0, sys.argv[1])
 import q4_q8_integer_quantize_amd as rz
-lib = rz.load_library()
+lib = rz.load_library(preload_torch=False)   # no kernel runs here
 out = []
 import ctypes
 def conv(a):

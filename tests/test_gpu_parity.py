@@ -1257,6 +1257,34 @@ def test_topk_matches_oracle(kind, n, k):
     _check_topk(_topk_values(kind, n, n * 131 + k), k)
 
 
+def _topk_random_cases(count=40, seed=2024):
+    g = np.random.default_rng(seed)
+    kinds = ("normal", "ties", "zeros", "ulps", "ascending", "descending", "heavy")
+    cases = []
+    while len(cases) < count:
+        n = int(np.exp(g.uniform(0, np.log(200000))))
+        k = int(g.integers(1, min(n, 128) + 1))
+        if rz.rz_topk_f32_workspace_bytes(n, k) == 0:
+            continue
+        cases.append((n, k, kinds[int(g.integers(len(kinds)))], int(g.integers(1 << 30))))
+    return cases
+
+
+@pytest.mark.parametrize("n,k,kind,seed", _topk_random_cases())
+def test_topk_random_shapes(n, k, kind, seed):
+    """Seeded random sizes (log-uniform n up to 200000, k up to 128) and value
+    patterns, including heavy-tailed values (a Cauchy draw, so the keys span
+    many binades) and many equal values: indices and values equal to the
+    oracle's."""
+    banner("topk random", n, k, kind, seed)
+    if kind == "heavy":
+        v = np.random.default_rng(seed).standard_cauchy(n).astype(np.float32)
+        v[~np.isfinite(v)] = 0.0
+    else:
+        v = _topk_values(kind, n, seed)
+    _check_topk(v, k)
+
+
 def test_topk_optional_outputs_and_workspace_reuse():
     """Only indices, only values, and one workspace used by calls of different
     sizes in a row (it holds no state)."""
@@ -1704,6 +1732,28 @@ def test_graph_replays_match_eager(fused):
         torch.cuda.synchronize()
         for k, t in enumerate(outs):
             assert np.array_equal(_bits(t), eager[k]), "replay %d: output %d differs from eager" % (rep, k)
+
+
+def test_library_loaded_before_torch():
+    """A process that loads librz.so before importing torch (here through a
+    size query, which touches no device) still runs kernels on torch's
+    tensors: the binding imports torch first, so both use one HIP runtime."""
+    import subprocess
+    import sys
+    banner("library before torch")
+    child = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "import q4_q8_integer_quantize_amd as rz\n"
+        "assert rz.rz_topk_f32_workspace_bytes(3824, 12) > 0\n"
+        "import torch\n"
+        "v = torch.arange(3824, dtype=torch.float32, device='cuda')\n"
+        "i = torch.empty(12, dtype=torch.int32, device='cuda')\n"
+        "ws = torch.empty(rz.rz_topk_f32_workspace_bytes(3824, 12), dtype=torch.uint8, device='cuda')\n"
+        "rz.rz_topk_f32(v, 3824, 12, i, None, ws)\n"
+        "assert i.cpu().tolist() == list(range(3823, 3811, -1)), i.cpu().tolist()\n"
+        "print('ok')\n" % str(__import__("pathlib").Path(__file__).resolve().parents[1]))
+    res = subprocess.run([sys.executable, "-c", child], capture_output=True, text=True, timeout=100)
+    assert res.returncode == 0 and res.stdout.strip().endswith("ok"), res.stderr[-2000:]
 
 
 def test_concurrent_streams_match_sequential():
