@@ -79,6 +79,94 @@ def oracle_q4k(blob, xq, n_tokens=1):
     return np.stack(ys), np.stack(ts)
 
 
+# ------------------------------------------------------------------ seeded random shapes
+def _random_shapes(count, seed, max_k, step, budget, max_tokens=1):
+    """(out_dim, in_dim, n, n_tokens, seed) with log-uniform out_dim, in_dim a
+    multiple of `step` up to max_k steps, n <= in_dim (a ragged tail of zeros)
+    and out_dim * in_dim * n_tokens within `budget` (oracle time)."""
+    g = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < count:
+        nt = int(g.integers(1, max_tokens + 1))
+        in_dim = step * int(g.integers(1, max_k + 1))
+        hi = max(1, min(4000, budget // (in_dim * nt)))
+        out_dim = int(np.exp(g.uniform(0, np.log(hi + 1))))
+        out_dim = max(1, min(out_dim, hi))
+        n = int(g.integers(max(1, in_dim - step + 1), in_dim + 1))
+        cases.append((out_dim, in_dim, n, nt, int(g.integers(1 << 30))))
+    return cases
+
+
+@pytest.mark.parametrize("out_dim,in_dim,n,n_tokens,seed",
+                         _random_shapes(24, 71, 80, 256, 24_000_000, max_tokens=8))
+def test_q4k_q8_gemv_random_shapes(out_dim, in_dim, n, n_tokens, seed):
+    """rz_q4k_q8_gemv on seeded random shapes: 1..8 tokens (3 and more on the
+    matrix cores), rows up to 20480 values (column chunks past the register
+    window), ragged row counts and activation tails; every output of every
+    token within the bound of the oracle."""
+    banner("q4k random", out_dim, in_dim, n, n_tokens)
+    blob = synth.q4k_weights(synth.rng(72, seed), out_dim, in_dim)
+    X = synth.activation(np.random.default_rng(seed), in_dim, n_tokens=n_tokens)
+    X = X.reshape(n_tokens, in_dim)
+    X[:, n:] = 0.0
+    xq = oracle.quantize_q8_1(X if n_tokens > 1 else X[0])
+    Y = gpu_q4k(blob, oracle.q8_1_to_bytes(xq), n_tokens)
+    y_ref, terms = oracle_q4k(blob, xq, n_tokens)
+    for t in range(n_tokens):
+        assert_within(Y[t], y_ref[t], terms[t], "token %d" % t)
+
+
+@pytest.mark.parametrize("out_dim,in_dim,n,n_tokens,seed",
+                         _random_shapes(16, 73, 64, 256, 16_000_000))
+def test_q4k_q8_gemv_f32_random_shapes(out_dim, in_dim, n, n_tokens, seed):
+    """The fused quantize + GEMV on seeded random shapes, n <= in_dim values
+    (zero tail, dword activation loads when n is not a multiple of 4): the
+    Q8_1 side output byte-equal to the oracle's, y within its bound."""
+    banner("q4k f32 random", out_dim, in_dim, n)
+    blob = synth.q4k_weights(synth.rng(74, seed), out_dim, in_dim)
+    x = synth.activation(np.random.default_rng(seed), n)
+    xq_ref = oracle.quantize_q8_1(x, in_dim)
+    xq = empty_bytes(rz.q8_1_nbytes(in_dim))
+    y = empty_f32(out_dim)
+    rz.rz_q4k_q8_gemv_f32(dev_bytes(blob), dev_f32(x), n, xq, y, out_dim, in_dim)
+    assert np.array_equal(host(xq), oracle.q8_1_to_bytes(xq_ref).reshape(-1))
+    y_ref, terms = oracle.gemv_q4k_q8_int(blob, xq_ref)
+    assert_within(host(y), y_ref, terms, "fused")
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("out_dim,in_dim,n,n_tokens,seed",
+                         _random_shapes(12, 75, 600, 64, 24_000_000))
+def test_q4_0_gemv_random_shapes(fmt, out_dim, in_dim, n, n_tokens, seed):
+    """rz_q4_0_gemv on seeded random shapes, rows up to 38400 values (several
+    column chunks in both formats), both activation formats, within the bound
+    of the oracle."""
+    banner("q4_0 random", fmt, out_dim, in_dim, n)
+    blob = synth.q4_0_weights(synth.rng(76, seed), out_dim, in_dim)
+    x = _padded(synth.activation(np.random.default_rng(seed), n), in_dim)
+    if fmt == 0:
+        y_ref, terms = oracle.gemv_q4_0_f32(blob, x)
+        y = gpu_q4_0(blob, x, 0)
+    else:
+        xq = oracle.quantize_q8_1(x)
+        y_ref, terms = oracle.gemv_q4_0_q8_int(blob, xq)
+        y = gpu_q4_0(blob, oracle.q8_1_to_bytes(xq), 1)
+    assert_within(y, y_ref, terms, "q4_0 fmt %d" % fmt)
+
+
+@pytest.mark.parametrize("out_dim,in_dim,n,n_tokens,seed",
+                         _random_shapes(12, 77, 80, 256, 16_000_000))
+def test_q4k_xf32_random_shapes(out_dim, in_dim, n, n_tokens, seed):
+    """rz_q4k_gemv (fp32 activation, no Q8_1) on seeded random shapes with a
+    ragged activation length n, within the bound of the oracle's fp32 form."""
+    banner("q4k xf32 random", out_dim, in_dim, n)
+    blob = synth.q4k_weights(synth.rng(78, seed), out_dim, in_dim)
+    x = synth.activation(np.random.default_rng(seed), n)
+    y = gpu_q4k_xf32(blob, x)
+    y_ref, terms = oracle.gemv_q4k_f32(blob, _padded(x, in_dim))
+    assert_within(y, y_ref, terms, "xf32")
+
+
 # ------------------------------------------------------------------ Q8_1
 def test_q8_1_hand_worked_blocks_gpu():
     banner("q8_1 hand-worked blocks")
