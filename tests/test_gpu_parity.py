@@ -1549,6 +1549,91 @@ def test_gelu_ffn_chain(hidden, inter, biases):
     assert_within(y_gpu, st["y"], st["y_terms"] + extra / oracle.GEMV_REL, "chain y")
 
 
+def _rand_cases(seed, count, draw):
+    g = np.random.default_rng(seed)
+    return [draw(g) for _ in range(count)]
+
+
+def _draw_swiglu(g):
+    while True:
+        hidden, inter = 256 * int(g.integers(1, 17)), 256 * int(g.integers(1, 41))
+        if hidden * inter <= 8_000_000:
+            return hidden, inter
+
+
+@pytest.mark.parametrize("hidden,inter", _rand_cases(91, 10, _draw_swiglu))
+def test_swiglu_ffn_chain_random_shapes(hidden, inter):
+    """The staged SwiGLU checks of test_swiglu_ffn_chain on seeded random
+    hidden and intermediate sizes."""
+    test_swiglu_ffn_chain(hidden, inter)
+
+
+def _draw_rmsnorm(g):
+    n = int(np.exp(g.uniform(0, np.log(20480))))
+    n_padded = 32 * ((n + 31) // 32) + 32 * int(g.integers(0, 3))
+    return n, min(n_padded, 20480), int(g.integers(1, 5)), float(10.0 ** g.integers(-3, 4))
+
+
+@pytest.mark.parametrize("n,n_padded,nt,scale", _rand_cases(92, 12, _draw_rmsnorm))
+def test_rmsnorm_q8_1_random_shapes(n, n_padded, nt, scale):
+    """The checks of test_rmsnorm_q8_1_matches_oracle on seeded random lengths,
+    paddings, token counts and scales."""
+    test_rmsnorm_q8_1_matches_oracle(n, n_padded, nt, scale)
+
+
+def _draw_gelu(g):
+    while True:
+        hidden, inter = 64 * int(g.integers(1, 41)), 64 * int(g.integers(1, 257))
+        if hidden * inter <= 8_000_000:
+            return hidden, inter, bool(g.integers(0, 2))
+
+
+@pytest.mark.parametrize("hidden,inter,biases", _rand_cases(93, 10, _draw_gelu))
+def test_gelu_ffn_chain_random_shapes(hidden, inter, biases):
+    """The staged GELU FFN checks of test_gelu_ffn_chain on seeded random sizes,
+    with and without biases."""
+    test_gelu_ffn_chain(hidden, inter, biases)
+
+
+def _draw_multi(g):
+    k = int(g.integers(1, 9))
+    in_dim = 256 * int(g.integers(1, 65))
+    outs = [int(np.exp(g.uniform(0, np.log(700)))) for _ in range(k)]
+    return int(g.integers(1, 3)), outs, in_dim
+
+
+@pytest.mark.parametrize("n_tokens,out_dims,in_dim", _rand_cases(94, 12, _draw_multi))
+def test_q4k_multi_random_shapes(n_tokens, out_dims, in_dim):
+    """The checks of test_q4k_multi_matches_single_calls on seeded random
+    matrix counts, row counts and row lengths."""
+    test_q4k_multi_matches_single_calls(n_tokens, out_dims, in_dim)
+
+
+def _draw_lm_head(g):
+    while True:
+        out_dim = int(np.exp(g.uniform(0, np.log(30000))))
+        in_dim = 64 * int(g.integers(1, 401))
+        if out_dim * in_dim <= 12_000_000:
+            return out_dim, in_dim, int(g.integers(0, 2)), bool(g.integers(0, 2)), int(g.integers(1 << 30))
+
+
+@pytest.mark.parametrize("out_dim,in_dim,fmt,with_bias,seed", _rand_cases(95, 14, _draw_lm_head))
+def test_lm_head_random_shapes(out_dim, in_dim, fmt, with_bias, seed):
+    """The LM head with and without bias, both activation formats, on seeded
+    random vocabulary sizes and row lengths (up to 25600 values: several
+    column passes): logits and greedy token as in test_lm_head_shapes."""
+    banner("lm head random", fmt, out_dim, in_dim, with_bias)
+    g = np.random.default_rng(seed)
+    blob = synth.q4_0_weights(synth.rng(96, seed), out_dim, in_dim)
+    x = synth.activation(g, in_dim)
+    bias = synth.activation(g, out_dim) if with_bias else None
+    if fmt == 0:
+        _check_lm_head(blob, x, 0, bias, x)
+    else:
+        xq = oracle.quantize_q8_1(x)
+        _check_lm_head(blob, oracle.q8_1_to_bytes(xq), 1, bias, xq)
+
+
 def test_gelu_ffn_zero_up_weights():
     """Zero up weights: h = gelu(up_bias) exactly as the oracle rounds it, up to
     the device exp; with no up bias h is exactly 0 and y is the down bias."""
