@@ -2146,6 +2146,82 @@ def test_q4k_q8_gemv_f32_add_bit_identical(out_dim, n, in_dim):
     assert_within(host(y), oracle.residual_add(r, y_o), t_o + np.abs(r), "f32 add y")
 
 
+def _draw_add(g):
+    while True:
+        nt = int(g.integers(1, 9))
+        in_dim = 256 * int(g.integers(1, 81))
+        out_dim = int(np.exp(g.uniform(0, np.log(3000))))
+        if out_dim * in_dim * nt <= 24_000_000:
+            return out_dim, in_dim, nt
+
+
+@pytest.mark.parametrize("out_dim,in_dim,nt", _rand_cases(97, 12, _draw_add))
+def test_q4k_gemv_add_random_shapes(out_dim, in_dim, nt):
+    """The residual checks of test_q4k_gemv_add on seeded random shapes and
+    token counts (1-2 on the dot4 kernel, 3-8 on the matrix cores, column
+    passes past the register window)."""
+    test_q4k_gemv_add(out_dim, in_dim, nt)
+
+
+def _draw_fused(g):
+    while True:
+        in_dim = 256 * int(g.integers(1, 65))
+        n = int(g.integers(max(1, in_dim - 255), in_dim + 1))
+        out_dim = int(np.exp(g.uniform(0, np.log(6000))))
+        if out_dim * in_dim <= 24_000_000:
+            return out_dim, n, in_dim
+
+
+@pytest.mark.parametrize("out_dim,n,in_dim", _rand_cases(98, 10, _draw_fused))
+def test_q4k_gemv_f32_two_step_random_shapes(out_dim, n, in_dim):
+    """The checks of test_q4k_gemv_f32_matches_two_step_and_oracle (bit-equal
+    to quantize then GEMV, side output equal to the oracle's bytes) on seeded
+    random shapes and ragged activation lengths."""
+    test_q4k_gemv_f32_matches_two_step_and_oracle(out_dim, n, in_dim)
+
+
+@pytest.mark.parametrize("out_dim,n,in_dim", _rand_cases(99, 8, _draw_fused))
+def test_q4k_q8_gemv_f32_add_random_shapes(out_dim, n, in_dim):
+    """The checks of test_q4k_q8_gemv_f32_add_bit_identical on seeded random
+    shapes."""
+    test_q4k_q8_gemv_f32_add_bit_identical(out_dim, n, in_dim)
+
+
+def _draw_norm_ffn(g):
+    while True:
+        hidden, inter = 256 * int(g.integers(1, 33)), 256 * int(g.integers(1, 41))
+        if hidden * inter <= 12_000_000:
+            return hidden, inter
+
+
+@pytest.mark.parametrize("hidden,inter", _rand_cases(100, 8, _draw_norm_ffn))
+def test_rmsnorm_swiglu_ffn_add_random_shapes(hidden, inter):
+    """The checks of test_rmsnorm_swiglu_ffn_add_bit_identical on seeded
+    random sizes."""
+    test_rmsnorm_swiglu_ffn_add_bit_identical(hidden, inter)
+
+
+@pytest.mark.parametrize("hidden,inter", _rand_cases(101, 8, _draw_swiglu))
+def test_swiglu_ffn_f32_chain_random_shapes(hidden, inter):
+    """The staged checks of test_swiglu_ffn_f32_chain on seeded random sizes."""
+    test_swiglu_ffn_f32_chain(hidden, inter)
+
+
+def _draw_norm_multi(g):
+    k = int(g.integers(1, 9))
+    in_dim = 256 * int(g.integers(1, 65))
+    n = int(g.integers(max(1, in_dim - 255), in_dim + 1))
+    outs = [int(np.exp(g.uniform(0, np.log(2000)))) for _ in range(k)]
+    return in_dim, n, outs
+
+
+@pytest.mark.parametrize("in_dim,n,out_dims", _rand_cases(102, 10, _draw_norm_multi))
+def test_rmsnorm_q4k_q8_gemv_multi_random_shapes(in_dim, n, out_dims):
+    """The checks of test_rmsnorm_q4k_q8_gemv_multi_bit_identical on seeded
+    random matrix sets, row lengths and ragged activation lengths."""
+    test_rmsnorm_q4k_q8_gemv_multi_bit_identical(in_dim, n, out_dims)
+
+
 def test_minimum_alignments_fused_entries():
     """The RMSNorm-prologue entries and quantize + GEMV + residual on buffers
     at exactly the alignments include/rz.h requires (Q4_K and Q8_1 16 bytes,
