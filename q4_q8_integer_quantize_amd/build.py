@@ -1,5 +1,6 @@
-"""Build librz.so (the HIP kernels and the C ABI) in-tree for gfx950, and the
-benchmark's streaming-read helper librz_stream_read.so.
+"""Build librz.so (the HIP kernels and the C ABI) in-tree for gfx950, the
+benchmark's streaming-read helper librz_stream_read.so, and the plain C program
+tests/native/abi_consumer that drives librz.so through include/rz.h alone.
 
     python -m q4_q8_integer_quantize_amd.build
 
@@ -23,6 +24,9 @@ LIB = os.path.join(PKG, "librz.so")
 # measurement helper for bench.py (a plain streaming read), outside librz.so
 READ_SRC = "stream_read.hip"
 READ_LIB = os.path.join(PKG, "librz_stream_read.so")
+# a C consumer of the ABI (no Python, no torch), run by the tests
+CONSUMER_SRC = os.path.join(ROOT, "tests", "native", "abi_consumer.c")
+CONSUMER = os.path.join(ROOT, "tests", "native", "abi_consumer")
 
 SOURCES = ["q8_1_quantize.hip", "q4k_gemv.hip", "q4k_gemv_f32.hip", "q4k_gemm_mfma.hip",
            "q4k_gemv_multi.hip", "q4_0_gemv.hip", "swiglu_ffn.hip", "rmsnorm_q8_1.hip",
@@ -62,9 +66,26 @@ def build(verbose: bool = True) -> str:
         objs = list(ex.map(_compile, SOURCES))
     _link(objs, LIB)
     _link([_compile(READ_SRC)], READ_LIB)
+    build_consumer(CONSUMER)
     if verbose:
-        print("built", LIB, "and", READ_LIB)
+        print("built", LIB, READ_LIB, "and", CONSUMER)
     return LIB
+
+
+def build_consumer(out: str) -> str:
+    """Compile tests/native/abi_consumer.c with the host C compiler against
+    include/rz.h, librz.so and the HIP runtime; returns ``out``."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    pkg_from_out = os.path.relpath(PKG, os.path.dirname(os.path.abspath(out)))
+    cmd = ["gcc", "-std=c11", "-O1", "-Wall", "-Wextra", "-Werror",
+           "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(rocm, "include"), "-I", INCLUDE,
+           CONSUMER_SRC, "-L", PKG, "-lrz", "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/" + pkg_from_out, "-Wl,-rpath," + os.path.join(rocm, "lib"),
+           "-o", out]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("gcc failed on the ABI consumer:\n%s\n%s" % (" ".join(cmd), res.stderr))
+    return out
 
 
 def _link(objs: list[str], lib: str) -> None:

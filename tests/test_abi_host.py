@@ -736,3 +736,14 @@ def test_q4k_q8_gemv_f32_add_accepts_in_place(lib):
                         ("rz_q4k_q8_gemv_f32_add", _fa(r=_b(4))),                   # r is y
                         ("rz_q4k_q8_gemv_f32_add", _fa(xq=_b(2), n=4000))])
     assert [rc for rc, _ in res] == [rz.RZ_ELAUNCH] * 3, res
+
+
+def test_c_consumer_host_paths(tmp_path):
+    """The plain C consumer of include/rz.h compiles with -Werror against the
+    header, links librz.so and the HIP runtime without Python, and its
+    host-side checks (version, the error codes and message of rejected
+    arguments, no HIP call) pass here."""
+    from q4_q8_integer_quantize_amd import build as rzbuild
+    exe = rzbuild.build_consumer(str(tmp_path / "abi_consumer"))
+    res = subprocess.run([exe, "host"], capture_output=True, text=True, timeout=60)
+    assert res.returncode == 0 and "passed: 0 failure(s)" in res.stdout, res.stdout + res.stderr

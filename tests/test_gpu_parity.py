@@ -12,6 +12,8 @@ Inputs are seeded synthetic tensors (synth/); weights are fed to both sides,
 and the GEMV tests give the GPU the oracle's own Q8_1 bytes so that a GEMV
 failure is never a quantize failure in disguise.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -1927,6 +1929,19 @@ def test_library_loaded_before_torch():
         "print('ok')\n" % str(__import__("pathlib").Path(__file__).resolve().parents[1]))
     res = subprocess.run([sys.executable, "-c", child], capture_output=True, text=True, timeout=100)
     assert res.returncode == 0 and res.stdout.strip().endswith("ok"), res.stderr[-2000:]
+
+
+def test_c_consumer_without_python():
+    """tests/native/abi_consumer (built by the package build from plain C
+    against include/rz.h, librz.so and the HIP runtime, no torch) quantizes,
+    multiplies the hand-worked Q4_K super-blocks of the golden fixture
+    (43600, 90064, 46464, exact) and takes their top 2 on device 0."""
+    import subprocess
+    banner("C consumer")
+    exe = os.path.join(os.path.dirname(os.path.abspath(__file__)), "native", "abi_consumer")
+    assert os.path.exists(exe), "tests/native/abi_consumer is not built (run the package build)"
+    res = subprocess.run([exe, "gpu"], capture_output=True, text=True, timeout=100)
+    assert res.returncode == 0 and "passed: 0 failure(s)" in res.stdout, res.stdout + res.stderr
 
 
 def test_concurrent_streams_match_sequential():
