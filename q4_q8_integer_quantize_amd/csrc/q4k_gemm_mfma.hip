@@ -137,13 +137,62 @@ __global__ __launch_bounds__(256) void q4k_q8_gemm_mfma_kernel(Q4KGemvArgs a) {
   // (d, s) records: tokens 2g, 2g+1
   const uint32_t r_lane0 = (2u * g) * kSlotStride, r_lane1 = (2u * g + 1u) * kSlotStride;
 
+  // The LDS operands of one super-block: the four A operands and, per MFMA,
+  // the (d, s) records of tokens 2g, 2g+1 for its two sub-blocks.
+  struct TileLds {
+    i32x4 A[4];
+    float2 R[4][4];
+  };
+  auto lds_reads = [&](uint32_t sbl, TileLds& L) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        L.A[2 * p + e] = *(const i32x4_a8*)(xs_lds + a_lane + (sbl * 8u + (uint32_t)(4 * p + e)) * kQ8Bytes);
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        // sub-blocks of MFMA (p, e): j0 = 4p + e (half 0), j1 = 4p + 2 + e (half 1)
+        const uint32_t j0 = (uint32_t)(4 * p + e), j1 = j0 + 2u;
+        float2(&r)[4] = L.R[2 * p + e];
+        r[0] = *(const float2*)(xs_lds + r_lane0 + (sbl * 8u + j0) * kQ8Bytes);
+        r[1] = *(const float2*)(xs_lds + r_lane0 + (sbl * 8u + j1) * kQ8Bytes);
+        r[2] = *(const float2*)(xs_lds + r_lane1 + (sbl * 8u + j0) * kQ8Bytes);
+        r[3] = *(const float2*)(xs_lds + r_lane1 + (sbl * 8u + j1) * kQ8Bytes);
+      }
+  };
+
   float y0 = 0.0f, y1 = 0.0f;   // tokens 2g and 2g+1 of row n
   const i32x4 zero = {0, 0, 0, 0};
+  // A super-block's LDS reads are all issued before its MFMAs, so that their
+  // latencies overlap instead of stalling between the MFMAs (outputs
+  // unchanged; 10.9-11.1 against 11.2-11.3 us at 4096 -> 14336, where the
+  // reads had been interleaved with the MFMAs; issuing them one super-block
+  // ahead measured no better and takes 12 more VGPRs).
+  TileLds cur;
 #pragma unroll
   for (int k = 0; k < NS; ++k) {
     if (k + P < NS) load_mfma_tile(tl[k + P], src, row_off, sbw0 + k + P, g);
     __builtin_amdgcn_sched_barrier(0);
     const uint32_t sbl = kpart * NS + k;   // super-block within the chunk
+    lds_reads(sbl, cur);
+    __builtin_amdgcn_sched_barrier(0);
+    i32x4 D[4];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const u32x4 Q = tl[k].q[p];
+      const uint32_t w0 = Q.x, w1 = Q.y, w2 = Q.z, w3 = Q.w;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const i32x4 B = e == 0 ? (i32x4){(int)(w0 & 0x0F0F0F0Fu), (int)(w1 & 0x0F0F0F0Fu),
+                                         (int)(w2 & 0x0F0F0F0Fu), (int)(w3 & 0x0F0F0F0Fu)}
+                               : (i32x4){(int)((w0 >> 4) & 0x0F0F0F0Fu), (int)((w1 >> 4) & 0x0F0F0F0Fu),
+                                         (int)((w2 >> 4) & 0x0F0F0F0Fu), (int)((w3 >> 4) & 0x0F0F0F0Fu)};
+        D[2 * p + e] = __builtin_amdgcn_mfma_i32_16x16x64_i8(cur.A[2 * p + e], B, zero, 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
     const u32x4 H = tl[k].hd;
     const uint32_t hx = H.x;
     const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)(hx & 0xffffu));
@@ -151,39 +200,25 @@ __global__ __launch_bounds__(256) void q4k_q8_gemm_mfma_kernel(Q4KGemvArgs a) {
     const Q4KScales sc = q4k_scales_bytes(H);
     float s0 = 0.0f, s1 = 0.0f, n0 = 0.0f, n1 = 0.0f;
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const u32x4 Q = tl[k].q[p];
-      const uint32_t w0 = Q.x, w1 = Q.y, w2 = Q.z, w3 = Q.w;
+    for (int p = 0; p < 2; ++p)
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        // sub-blocks of this MFMA: j0 = 4p + e (half 0), j1 = 4p + 2 + e (half 1)
-        const int j0 = 4 * p + e, j1 = 4 * p + 2 + e;
-        const uint32_t blk0 = sbl * 8u + (uint32_t)(4 * p + e);   // block of j0 in the chunk
-        const i32x4 A = *(const i32x4_a8*)(xs_lds + a_lane + blk0 * kQ8Bytes);
-        const i32x4 B = e == 0 ? (i32x4){(int)(w0 & 0x0F0F0F0Fu), (int)(w1 & 0x0F0F0F0Fu),
-                                         (int)(w2 & 0x0F0F0F0Fu), (int)(w3 & 0x0F0F0F0Fu)}
-                               : (i32x4){(int)((w0 >> 4) & 0x0F0F0F0Fu), (int)((w1 >> 4) & 0x0F0F0F0Fu),
-                                         (int)((w2 >> 4) & 0x0F0F0F0Fu), (int)((w3 >> 4) & 0x0F0F0F0Fu)};
-        const i32x4 D = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, zero, 0, 0, 0);
-        const float2 x00 = *(const float2*)(xs_lds + r_lane0 + (sbl * 8u + j0) * kQ8Bytes);
-        const float2 x01 = *(const float2*)(xs_lds + r_lane0 + (sbl * 8u + j1) * kQ8Bytes);
-        const float2 x10 = *(const float2*)(xs_lds + r_lane1 + (sbl * 8u + j0) * kQ8Bytes);
-        const float2 x11 = *(const float2*)(xs_lds + r_lane1 + (sbl * 8u + j1) * kQ8Bytes);
+        const int q = 2 * p + e, j0 = 4 * p + e, j1 = 4 * p + 2 + e;
         const int sc0 = (int)byte_of(j0 < 4 ? sc.sc_lo : sc.sc_hi, j0 & 3);
         const int sc1 = (int)byte_of(j1 < 4 ? sc.sc_lo : sc.sc_hi, j1 & 3);
         const float fm0 = (float)byte_of(j0 < 4 ? sc.m_lo : sc.m_hi, j0 & 3);
         const float fm1 = (float)byte_of(j1 < 4 ? sc.m_lo : sc.m_hi, j1 & 3);
-        const int d0 = D.x, d1 = D.y, d2 = D.z, d3 = D.w;
-        s0 = fmaf(x00.x, (float)__mul24(sc0, d0), s0);
-        s0 = fmaf(x01.x, (float)__mul24(sc1, d1), s0);
-        s1 = fmaf(x10.x, (float)__mul24(sc0, d2), s1);
-        s1 = fmaf(x11.x, (float)__mul24(sc1, d3), s1);
-        n0 = fmaf(x00.y, fm0, n0);
-        n0 = fmaf(x01.y, fm1, n0);
-        n1 = fmaf(x10.y, fm0, n1);
-        n1 = fmaf(x11.y, fm1, n1);
+        const float2(&r)[4] = cur.R[q];
+        const i32x4 Dq = D[q];
+        s0 = fmaf(r[0].x, (float)__mul24(sc0, Dq.x), s0);
+        s0 = fmaf(r[1].x, (float)__mul24(sc1, Dq.y), s0);
+        s1 = fmaf(r[2].x, (float)__mul24(sc0, Dq.z), s1);
+        s1 = fmaf(r[3].x, (float)__mul24(sc1, Dq.w), s1);
+        n0 = fmaf(r[0].y, fm0, n0);
+        n0 = fmaf(r[1].y, fm1, n0);
+        n1 = fmaf(r[2].y, fm0, n1);
+        n1 = fmaf(r[3].y, fm1, n1);
       }
-    }
     y0 = __builtin_fmaf((float)d, s0, y0);
     y0 = __builtin_fmaf((float)dmin, -n0, y0);
     y1 = __builtin_fmaf((float)d, s1, y1);
@@ -245,7 +280,11 @@ hipError_t launch_mfma_chunk(const Q4KGemvArgs& a, bool acc, hipStream_t st) {
 // whole row segments remove that stall, but every such variant built was
 // slower in total (11.3-14.3 us against 11.2): the integer MFMAs and the
 // rescale that consumes their sums then bound it, and this form overlaps them
-// with its loads best.
+// with its loads best.  Measured on this kernel itself: with the weight loads
+// replaced by register values it still takes 8.6 us (the activation copy, the
+// LDS reads and the rescale), and with the MFMAs replaced by a vector add 11.0
+// us, no faster than with them.  Workgroups of 2, 6 and 8 waves (fewer copies
+// of the activation for 8) measured 13.0, 15.4 and 11.3 us against 11.0.
 hipError_t launch_q4k_q8_gemm_mfma(const uint8_t* w, const uint8_t* xq, float* y, int out_dim,
                                    int in_dim, int n_tokens, hipStream_t stream, const float* r) {
   Q4KGemvArgs a;
