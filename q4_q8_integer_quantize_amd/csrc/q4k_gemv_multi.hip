@@ -149,21 +149,46 @@ __global__ __launch_bounds__(256) void q4k_q8_gemv_multi_kernel(Q4KMultiArgs a) 
   }
 }
 
-// NORM: every workgroup redoes the RMSNorm and the quantize.  Up to 4096 row
-// groups take one group a wave, with the weights requested after the row (the
-// Q, K, V set, 3072 groups: 6.72 us, against 6.92-6.93 us at one or two groups
-// a wave with the weights requested first and 7.07-7.10 us at four; the
-// unfused pair of launches takes 8.1 us; outputs bit-identical).  Larger sets
-// take 8 groups a wave, so that fewer, deeper waves pay for the prologue.
+// NORM: every workgroup redoes the RMSNorm and the quantize (32 KB of x and
+// gamma from L2 at in_dim 4096), so fewer workgroups pay for less of it; but
+// the row groups must still spread evenly over the 256 CUs, and deeper waves
+// expose more latency.  Measured at in_dim 4096 in one process (launch
+// durations in us, outputs bit-identical for every G):
+//   groups   G = 1    2      3      4      8
+//   2048      5.78   5.60    -     6.98  10.05
+//   3072      6.94   7.08   6.47   7.16  10.16
+//   4096      8.10   7.25    -     7.32  10.19
+//   5120      9.20   8.66   8.99  10.04  10.29
+//   6144     10.42   8.80   9.27   9.93  10.37
+//   8192     13.00  10.85  11.25  10.28  10.65
+// The rule that picks each row's best: up to 1024 groups, one a wave; else
+// the smallest G of 2, 3, 4 whose grid fills whole rounds of 256 workgroups
+// (the last at least 90% full), at most three; else one group a wave up to
+// 4096 groups, two while that grid is at most 768 workgroups, and eight
+// beyond.  (Before this, one group a wave up to 4096 groups and eight beyond.)
+// The weights are requested once the row of x and gamma has arrived (LATE),
+// so the row's loads do not queue behind them (5.60 against 5.81 us at 2048
+// groups; no worse elsewhere).
+static int multi_norm_groups_per_wave(long groups) {
+  if (groups <= 1024) return 1;
+  for (int g = 2; g <= 4; ++g) {
+    const long wgs = (groups + 4L * g - 1) / (4L * g);
+    const long rounds = (wgs + 255) / 256;
+    if (rounds <= 3 && wgs * 10 >= (rounds * 256 - 256) * 10 + 256 * 9) return g;
+  }
+  if (groups <= 4096) return 1;
+  if ((groups + 7) / 8 <= 768) return 2;
+  return 8;
+}
+
 template <int TPR, int S, int G, bool XV>
 static hipError_t launch_multi_norm_g(const Q4KMultiArgs& a, hipStream_t st) {
   constexpr int R = S <= 2 ? 2 : 1;
   constexpr int P = G > 2 ? 2 : (G > 1 ? G - 1 : 1);
-  constexpr bool LATE = G == 1;
   const size_t lds = (size_t)S * TPR * 8 * kQ8Bytes;   // every slot, zero blocks past the row
   const long waves = ((long)a.group0[a.n_mats] + G - 1) / G;
   const unsigned grid = (unsigned)((waves + 3) / 4);
-  hipLaunchKernelGGL((q4k_q8_gemv_multi_kernel<TPR, S, R, 1, G, P, false, true, XV, LATE>),
+  hipLaunchKernelGGL((q4k_q8_gemv_multi_kernel<TPR, S, R, 1, G, P, false, true, XV, true>),
                      dim3(grid), dim3(256), lds, st, a);
   return hipGetLastError();
 }
@@ -177,8 +202,13 @@ static hipError_t run_multi_norm(Q4KMultiArgs a, hipStream_t st) {
     a.group0[j + 1] = a.group0[j] + (j < a.n_mats ? ((uint32_t)a.out_dim[j] + rows_per_group - 1) /
                                                        rows_per_group
                                                  : 0u);
-  if (a.group0[a.n_mats] <= 4096) return launch_multi_norm_g<TPR, S, 1, XV>(a, st);
-  return launch_multi_norm_g<TPR, S, 8, XV>(a, st);
+  switch (multi_norm_groups_per_wave(a.group0[a.n_mats])) {
+    case 1: return launch_multi_norm_g<TPR, S, 1, XV>(a, st);
+    case 2: return launch_multi_norm_g<TPR, S, 2, XV>(a, st);
+    case 3: return launch_multi_norm_g<TPR, S, 3, XV>(a, st);
+    case 4: return launch_multi_norm_g<TPR, S, 4, XV>(a, st);
+    default: return launch_multi_norm_g<TPR, S, 8, XV>(a, st);
+  }
 }
 
 template <int TPR, int S>
