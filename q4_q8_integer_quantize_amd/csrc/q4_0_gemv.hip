@@ -439,19 +439,36 @@ __global__ __launch_bounds__(THREADS) void argmax_merge_kernel(const float* __re
   }
 }
 
-// Waves a workgroup: eight when the staged activation is 128 pairs or more
-// (every workgroup copies it into LDS, so larger workgroups copy it less
-// often; 160-pair rows: 7.7 against 8.1 us), else four (48 pairs: 6.5 against
-// 7.4 us with eight).
+// Waves a workgroup.  Four, unless the activation staged in LDS is 128 pairs
+// or more (32 KB and up): every workgroup copies it, so larger workgroups copy
+// it less often, and then the count of 8, 10, 12 or 16 whose grid gives the
+// CUs the smallest even share of waves, ceil(workgroups / 256) * waves a
+// workgroup (the smaller count on a tie).  Measured, one process, outputs
+// bit-identical: 160-pair rows (2560 x 10240, 2560 waves) 6.70 us at 10 (256
+// workgroups) against 7.43 at 8, 7.46 at 16 and 7.81 at 4; 48-pair rows
+// (10240 x 2560) 6.18 us at 4 against 6.58-6.74 at 5, 8 and 10.
 template <int LPR, int S, bool Q8>
-constexpr int q40_wpb() { return (!Q8 && S * LPR >= 128) ? 8 : 4; }
+constexpr bool q40_heavy_stage() { return !Q8 && S * LPR >= 128; }
 
-template <int LPR, int S, int R, int G, bool Q8>
-static hipError_t launch_q40_g(const Q40Args& a, long groups, bool epi, hipStream_t st) {
+static int q40_heavy_wpb(long waves) {
+  static const int kCand[] = {8, 10, 12, 16};
+  int best = 8;
+  long best_share = -1;
+  for (int w : kCand) {
+    const long wgs = (waves + w - 1) / w;
+    const long share = (wgs + 255) / 256 * w;
+    if (best_share < 0 || share < best_share) {
+      best = w;
+      best_share = share;
+    }
+  }
+  return best;
+}
+
+template <int LPR, int S, int R, int G, bool Q8, int WPB>
+static hipError_t launch_q40_w(const Q40Args& a, long waves, bool epi, hipStream_t st) {
   constexpr int P = G > 2 ? 2 : (G > 1 ? G - 1 : 1);
-  constexpr int WPB = q40_wpb<LPR, S, Q8>();
   static_assert(Q8 || xl_lds_bytes<S, LPR>() <= 65536, "staged activation within 64 KiB of LDS");
-  const long waves = (groups + G - 1) / G;
   const unsigned grid = (unsigned)((waves + WPB - 1) / WPB);
   const dim3 block(64 * WPB);
   const size_t lds = Q8 ? 0 : xl_lds_bytes<S, LPR>();
@@ -467,6 +484,21 @@ static hipError_t launch_q40_g(const Q40Args& a, long groups, bool epi, hipStrea
     hipLaunchKernelGGL((q4_0_gemv_kernel<LPR, S, R, G, P, Q8, false, false, WPB>), dim3(grid), block, lds, st, a);
   }
   return hipGetLastError();
+}
+
+template <int LPR, int S, int R, int G, bool Q8>
+static hipError_t launch_q40_g(const Q40Args& a, long groups, bool epi, hipStream_t st) {
+  const long waves = (groups + G - 1) / G;
+  if constexpr (q40_heavy_stage<LPR, S, Q8>()) {
+    switch (q40_heavy_wpb(waves)) {
+      case 10: return launch_q40_w<LPR, S, R, G, Q8, 10>(a, waves, epi, st);
+      case 12: return launch_q40_w<LPR, S, R, G, Q8, 12>(a, waves, epi, st);
+      case 16: return launch_q40_w<LPR, S, R, G, Q8, 16>(a, waves, epi, st);
+      default: return launch_q40_w<LPR, S, R, G, Q8, 8>(a, waves, epi, st);
+    }
+  } else {
+    return launch_q40_w<LPR, S, R, G, Q8, 4>(a, waves, epi, st);
+  }
 }
 
 // Pairs a launch covers: Q8_1 x keeps up to 4 pairs a lane in registers (64
@@ -493,7 +525,7 @@ constexpr int kXlChunkPairs = 224;
 // stream best (the 151936 x 1024 LM head with fp32 x, launches of the two
 // shapes interleaved: 18.1 us against 20.2 us at two groups a wave).
 struct Q40Shape {
-  int lpr, s, r, g, wpb;
+  int lpr, s, r, g;
 };
 
 static int pow2_at_least(int v) {
@@ -518,7 +550,6 @@ static Q40Shape q40_shape(int np, bool q8) {
     sh.r = 1;
   }
   sh.g = 1;
-  sh.wpb = (!q8 && sh.s * sh.lpr >= 128) ? 8 : 4;   // q40_wpb
   return sh;
 }
 
@@ -627,7 +658,8 @@ long q4_0_lm_head_partials(int out_dim, int in_dim, int x_format) {
   const long rows_per_group = (long)(kWave / sh.lpr) * sh.r;
   const long groups = (out_dim + rows_per_group - 1) / rows_per_group;
   const long waves = (groups + sh.g - 1) / sh.g;
-  return (waves + sh.wpb - 1) / sh.wpb;
+  const int wpb = (!q8 && sh.s * sh.lpr >= 128) ? q40_heavy_wpb(waves) : 4;   // launch_q40_g
+  return (waves + wpb - 1) / wpb;
 }
 
 hipError_t launch_q4_0_lm_head(const uint8_t* w, const void* x, int x_format, const float* bias,
