@@ -21,6 +21,8 @@
 //
 // SWI: the row groups alternate gate and up rows of the same rows, and the
 // epilogue stores h = silu(g) * u = g / (1 + exp(-g)) * u.
+#include <utility>
+
 #include "q4k_gemv.h"
 #include "rz_launch.h"
 
@@ -240,8 +242,6 @@ __global__ __launch_bounds__(256) void q4k_xf32_kernel(XF32Args a) {
   }
 }
 
-constexpr long kXF32TargetWaves = 1024;   // about one wave per SIMD
-
 template <int TPR, int S, int R, int G, bool SWI>
 static hipError_t launch_xf32_g(const XF32Args& a, long groups, hipStream_t st) {
   constexpr int P = G > 2 ? 2 : (G > 1 ? G - 1 : 1);
@@ -255,27 +255,51 @@ static hipError_t launch_xf32_g(const XF32Args& a, long groups, hipStream_t st) 
   return hipGetLastError();
 }
 
-// Steps per wave: the smallest power of two (at most 8) that keeps the grid at
-// about one wave per SIMD.  Rows per group: two for the one-slot window, one
-// for the two-slot window (measured at 4096 -> 14336: 9.9 us against 11.0 for
-// two rows, whose extra tile registers cost occupancy).
+// Steps a wave (SWI: even, a gate and an up group per pair), 1..16: the count
+// that gives the CUs the smallest even share of steps, ceil(workgroups / 256)
+// * 4 waves * G, the larger count on a tie.  Measured in one process, outputs
+// bit-identical, against the former rule (the smallest power of two up to 8
+// that keeps about 1024 waves):
+//   GEMV 4096 -> 14336:   G = 14 (256 workgroups)  9.45 us; G = 8 9.96, 7 9.63, 4 10.60
+//   GEMV 4096 -> 11008:   G = 11 (251)             7.69 us; G = 8 9.67-9.83, 12 8.03, 6 8.27
+//   gate/up 4096 -> 14336: G = 14 (512)           16.10 us; G = 8 17.57, 28 17.98, 6 17.90
+//   gate/up 4096 -> 11008: G = 12 (459)           13.91 us; G = 8 14.49, 6 14.31, 14 14.76
+static int xf32_steps_per_wave(long steps, bool swi) {
+  int best = swi ? 2 : 1;
+  long best_share = -1;
+  for (int g = best; g <= 16; g += swi ? 2 : 1) {
+    const long wgs = ((steps + g - 1) / g + 3) / 4;
+    const long share = (wgs + 255) / 256 * 4L * g;
+    if (best_share < 0 || share <= best_share) {
+      best = g;
+      best_share = share;
+    }
+  }
+  return best;
+}
+
+template <int TPR, int S, int R, bool SWI, int... Is>
+static hipError_t launch_xf32_any(int g, const XF32Args& a, long groups, hipStream_t st,
+                                  std::integer_sequence<int, Is...>) {
+  // candidate i is G = i + 1, or 2 (i + 1) for SWI
+  hipError_t e = hipErrorInvalidValue;
+  ((g == (SWI ? 2 : 1) * (Is + 1) ? (e = launch_xf32_g<TPR, S, R, (SWI ? 2 : 1) * (Is + 1), SWI>(a, groups, st), 0)
+                                  : 0),
+   ...);
+  return e;
+}
+
+// Rows per group: two for the one-slot window, one for the two-slot window
+// (measured at 4096 -> 14336: 9.9 us against 11.0 for two rows, whose extra
+// tile registers cost occupancy).
 template <int TPR, int S, bool SWI>
 static hipError_t run_xf32(const XF32Args& a, hipStream_t st) {
   constexpr int R = S == 1 ? 2 : 1;
   constexpr long rows_per_group = (long)(8 / TPR) * R;
   const long groups = (a.out_dim + rows_per_group - 1) / rows_per_group;
-  const long steps = SWI ? 2 * groups : groups;
-  const long per_wave = (steps + kXF32TargetWaves - 1) / kXF32TargetWaves;
-  if constexpr (SWI) {
-    if (per_wave <= 2) return launch_xf32_g<TPR, S, R, 2, SWI>(a, groups, st);
-    if (per_wave <= 4) return launch_xf32_g<TPR, S, R, 4, SWI>(a, groups, st);
-    return launch_xf32_g<TPR, S, R, 8, SWI>(a, groups, st);
-  } else {
-    if (per_wave <= 1) return launch_xf32_g<TPR, S, R, 1, SWI>(a, groups, st);
-    if (per_wave <= 2) return launch_xf32_g<TPR, S, R, 2, SWI>(a, groups, st);
-    if (per_wave <= 4) return launch_xf32_g<TPR, S, R, 4, SWI>(a, groups, st);
-    return launch_xf32_g<TPR, S, R, 8, SWI>(a, groups, st);
-  }
+  const int g = xf32_steps_per_wave(SWI ? 2 * groups : groups, SWI);
+  return launch_xf32_any<TPR, S, R, SWI>(g, a, groups, st,
+                                         std::make_integer_sequence<int, SWI ? 8 : 16>{});
 }
 
 // Register window: 2 slots (64 activation values per lane; a chunk of 16
