@@ -441,9 +441,10 @@ __global__ __launch_bounds__(THREADS) void argmax_merge_kernel(const float* __re
 
 // Waves a workgroup.  Four, unless the activation staged in LDS is 128 pairs
 // or more (32 KB and up): every workgroup copies it, so larger workgroups copy
-// it less often, and then the count of 8, 10, 12 or 16 whose grid gives the
-// CUs the smallest even share of waves, ceil(workgroups / 256) * waves a
-// workgroup (the smaller count on a tie).  Measured, one process, outputs
+// it less often, and then the count of 8, 10 or 12 whose grid gives the CUs
+// the smallest even share of waves, ceil(workgroups / 256) * waves a
+// workgroup (the smaller count on a tie; 16 never does better than 8 by this
+// measure).  Measured, one process, outputs
 // bit-identical: 160-pair rows (2560 x 10240, 2560 waves) 6.70 us at 10 (256
 // workgroups) against 7.43 at 8, 7.46 at 16 and 7.81 at 4; 48-pair rows
 // (10240 x 2560) 6.18 us at 4 against 6.58-6.74 at 5, 8 and 10.
@@ -451,7 +452,7 @@ template <int LPR, int S, bool Q8>
 constexpr bool q40_heavy_stage() { return !Q8 && S * LPR >= 128; }
 
 static int q40_heavy_wpb(long waves) {
-  static const int kCand[] = {8, 10, 12, 16};
+  static const int kCand[] = {8, 10, 12};
   int best = 8;
   long best_share = -1;
   for (int w : kCand) {
@@ -493,7 +494,6 @@ static hipError_t launch_q40_g(const Q40Args& a, long groups, bool epi, hipStrea
     switch (q40_heavy_wpb(waves)) {
       case 10: return launch_q40_w<LPR, S, R, G, Q8, 10>(a, waves, epi, st);
       case 12: return launch_q40_w<LPR, S, R, G, Q8, 12>(a, waves, epi, st);
-      case 16: return launch_q40_w<LPR, S, R, G, Q8, 16>(a, waves, epi, st);
       default: return launch_q40_w<LPR, S, R, G, Q8, 8>(a, waves, epi, st);
     }
   } else {

@@ -681,6 +681,8 @@ def test_q4_0_hand_worked_block_gpu():
     (33, 8192),      # fp32: 32 lanes x 4 pairs
     (9, 10240),      # fp32: 64 lanes x 3 pairs, 32 of 192 slots idle
     (5, 12288),      # fp32: 64 lanes x 3 pairs, all busy
+    (3072, 10240),   # fp32: 3072 one-row waves in 12-wave workgroups (256)
+    (2560, 10240),   # fp32: 2560 one-row waves in 10-wave workgroups (256)
     (17, 16384),     # fp32: two column chunks
     (40, 20480),     # both formats chunked
 ])
@@ -2013,7 +2015,10 @@ def test_concurrent_streams_match_sequential():
     (4096, 4096, [4096, 1024, 1024]),      # the Q, K, V projections
     (5120, 4999, [700, 128]),              # three slots, ragged n
     (16384, 16384, [129]),
-    (1024, 1024, [8200, 100]),             # over 4096 row groups: 8 groups a wave
+    (4096, 4096, [2048, 1024, 1024]),      # 2048 row groups: 2 groups a wave
+    (4096, 4000, [3000, 2000, 1000]),      # 3000 row groups: 3 groups a wave
+    (4096, 4096, [4096, 4096, 8192]),      # 8192 row groups: 4 groups a wave
+    (1024, 1024, [30000, 100]),            # 7525 row groups: 8 groups a wave
 ])
 def test_rmsnorm_q4k_q8_gemv_multi_bit_identical(in_dim, n, out_dims):
     """One launch (RMSNorm + Q8_1 in every workgroup, then the GEMVs) equals
