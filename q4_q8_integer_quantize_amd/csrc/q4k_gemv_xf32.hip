@@ -260,10 +260,10 @@ static hipError_t launch_xf32_g(const XF32Args& a, long groups, hipStream_t st) 
 // * 4 waves * G, the larger count on a tie.  Measured in one process, outputs
 // bit-identical, against the former rule (the smallest power of two up to 8
 // that keeps about 1024 waves):
-//   GEMV 4096 -> 14336:   G = 14 (256 workgroups)  9.45 us; G = 8 9.96, 7 9.63, 4 10.60
-//   GEMV 4096 -> 11008:   G = 11 (251)             7.69 us; G = 8 9.67-9.83, 12 8.03, 6 8.27
-//   gate/up 4096 -> 14336: G = 14 (512)           16.10 us; G = 8 17.57, 28 17.98, 6 17.90
-//   gate/up 4096 -> 11008: G = 12 (459)           13.91 us; G = 8 14.49, 6 14.31, 14 14.76
+//   GEMV 4096 -> 14336:    G = 14 (256 workgroups) 8.9-9.5 us; G = 8 9.8-10.0, 7 9.4-9.6, 4 10.4-10.6
+//   GEMV 4096 -> 11008:    G = 11 (251)            7.7-7.8 us; G = 8 9.6-9.8, 12 8.0, 6 8.3
+//   gate/up 4096 -> 14336: G = 14 (512)          16.0-16.1 us; G = 8 17.5-17.6, 28 17.5-18.0, 6 17.4-17.9
+//   gate/up 4096 -> 11008: G = 12 (459)          13.9 us;      G = 8 14.2-14.5, 6 14.3, 14 14.8
 static int xf32_steps_per_wave(long steps, bool swi) {
   int best = swi ? 2 : 1;
   long best_share = -1;
