@@ -441,7 +441,8 @@ def test_q4k_batch_integer_exact_bit_exact(n_tokens, out_dim, in_dim):
 # ------------------------------------------------------------------ fused quantize + GEMV
 @pytest.mark.parametrize("out_dim,n,in_dim", [
     (3, 200, 256), (65, 512, 512), (896, 896, 1024), (129, 1280, 1280), (1000, 3000, 3072),
-    (1024, 4096, 4096), (14336, 4096, 4096), (4096, 14336, 14336), (77, 16384, 16384),
+    (1024, 4096, 4096), (2047, 4000, 4096), (2048, 4096, 4096),   # one / two rows a group
+    (14336, 4096, 4096), (4096, 14336, 14336), (77, 16384, 16384),
 ])
 def test_q4k_gemv_f32_matches_two_step_and_oracle(out_dim, n, in_dim):
     """One launch (quantize in LDS + GEMV) equals rz_q8_1_quantize followed by
