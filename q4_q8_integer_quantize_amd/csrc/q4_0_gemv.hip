@@ -97,18 +97,32 @@ __device__ __forceinline__ void load_x40_q8(X40Q8<S>& xs, const Q40Args& a, int 
 // (one per byte position) keep the fma chains short; they are added pairwise
 // at the end.
 __device__ __forceinline__ float block_dot_f32(const uint32_t qs[4], const float* x) {
+  // Two nibbles masked into the two halves of a dword are two fp16 denormals
+  // whose values are exactly q * 2^-24, and v_fma_mix_f32 converts an fp16
+  // half to fp32 inside the fma: one instruction a weight where a byte
+  // conversion and an fma took two.  Every partial sum is then exactly 2^-24
+  // times the one of fp32 weights (rounding commutes with a power-of-two
+  // scale away from underflow), and accumulator b still takes byte b's low,
+  // then high nibble of each dword in turn, so the result, scaled back by
+  // 2^24, equals the former byte-conversion sum bit for bit.
   float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const uint32_t lo = opaque_and(qs[k], 0x0F0F0F0Fu);
-    const uint32_t hi = opaque_and(qs[k] >> 4, 0x0F0F0F0Fu);
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      acc[b] = fmaf((float)((lo >> (8 * b)) & 0xffu), x[4 * k + b], acc[b]);
-      acc[b] = fmaf((float)((hi >> (8 * b)) & 0xffu), x[16 + 4 * k + b], acc[b]);
-    }
+    const uint32_t w = qs[k];
+    const uint32_t l02 = opaque_and(w, 0x000F000Fu);          // low nibbles of bytes 0, 2
+    const uint32_t h02 = opaque_and(w >> 4, 0x000F000Fu);     // high nibbles of bytes 0, 2
+    const uint32_t l13 = opaque_and(w >> 8, 0x000F000Fu);     // low nibbles of bytes 1, 3
+    const uint32_t h13 = opaque_and(w >> 12, 0x000F000Fu);    // high nibbles of bytes 1, 3
+    acc[0] = fmaf(f16_lo(l02), x[4 * k + 0], acc[0]);
+    acc[0] = fmaf(f16_lo(h02), x[16 + 4 * k + 0], acc[0]);
+    acc[1] = fmaf(f16_lo(l13), x[4 * k + 1], acc[1]);
+    acc[1] = fmaf(f16_lo(h13), x[16 + 4 * k + 1], acc[1]);
+    acc[2] = fmaf(f16_hi(l02), x[4 * k + 2], acc[2]);
+    acc[2] = fmaf(f16_hi(h02), x[16 + 4 * k + 2], acc[2]);
+    acc[3] = fmaf(f16_hi(l13), x[4 * k + 3], acc[3]);
+    acc[3] = fmaf(f16_hi(h13), x[16 + 4 * k + 3], acc[3]);
   }
-  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  return ((acc[0] + acc[1]) + (acc[2] + acc[3])) * 0x1p24f;
 }
 
 __device__ __forceinline__ int block_dot_q8(const uint32_t qs[4], const int* q8) {
