@@ -10,7 +10,7 @@
 //
 // Per 32-value sub-block j of a super-block a lane evaluates, in fp32,
 //   d * (sc_j * sum_l q_l x_l) - dmin * (m_j * sum_l x_l)
-// (the nibbles convert to float exactly, v_cvt_f32_ubyte).  Lane roles are
+// (the nibbles enter the fmas exactly, as fp16 denormals q * 2^-24).  Lane roles are
 // those of the Q8_1 kernel (q4k_gemv.h): lane i of a team reads qs bytes
 // 16i..16i+15, i.e. positions 16h..16h+15 of sub-blocks 2c (low nibbles) and
 // 2c+1 (high nibbles), and after adding its partner's half owns sub-block
@@ -132,20 +132,31 @@ __device__ __forceinline__ void tile_dot_xf32(float (&part)[R], const WTile<S, R
                            __builtin_amdgcn_ubfe(a_sc, ro.sh_sc, ro.len_lo));
       const int m = (int)((__builtin_amdgcn_ubfe(H.z, ro.sh_hi, ro.len_hi) << 4) |
                           __builtin_amdgcn_ubfe(a_m, ro.sh_m, ro.len_lo));
-      // two partial sums per half (even and odd bytes)
+      // two partial sums per half (even and odd bytes).  The nibbles enter as
+      // fp16 denormals, exactly q * 2^-24, two to a dword, and v_fma_mix_f32
+      // converts them inside the fma (one instruction a weight instead of a
+      // byte conversion and an fma); each partial sum takes the same products
+      // in the same order as with fp32 weights, so it is exactly 2^-24 times
+      // that sum, and the scale back by 2^24 gives the same bits.
       float pl[2] = {0.0f, 0.0f}, ph[2] = {0.0f, 0.0f};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const uint32_t lo = opaque_and(wt.qs[r][s][k], 0x0F0F0F0Fu);
-        const uint32_t hi = opaque_and(wt.qs[r][s][k] >> 4, 0x0F0F0F0Fu);
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          pl[b & 1] = fmaf((float)((lo >> (8 * b)) & 0xffu), xs.lo[s][4 * k + b], pl[b & 1]);
-          ph[b & 1] = fmaf((float)((hi >> (8 * b)) & 0xffu), xs.hi[s][4 * k + b], ph[b & 1]);
-        }
+        const uint32_t w = wt.qs[r][s][k];
+        const uint32_t l02 = opaque_and(w, 0x000F000Fu);         // low nibbles of bytes 0, 2
+        const uint32_t h02 = opaque_and(w >> 4, 0x000F000Fu);    // high nibbles of bytes 0, 2
+        const uint32_t l13 = opaque_and(w >> 8, 0x000F000Fu);    // low nibbles of bytes 1, 3
+        const uint32_t h13 = opaque_and(w >> 12, 0x000F000Fu);   // high nibbles of bytes 1, 3
+        pl[0] = fmaf(f16_lo(l02), xs.lo[s][4 * k + 0], pl[0]);
+        ph[0] = fmaf(f16_lo(h02), xs.hi[s][4 * k + 0], ph[0]);
+        pl[1] = fmaf(f16_lo(l13), xs.lo[s][4 * k + 1], pl[1]);
+        ph[1] = fmaf(f16_lo(h13), xs.hi[s][4 * k + 1], ph[1]);
+        pl[0] = fmaf(f16_hi(l02), xs.lo[s][4 * k + 2], pl[0]);
+        ph[0] = fmaf(f16_hi(h02), xs.hi[s][4 * k + 2], ph[0]);
+        pl[1] = fmaf(f16_hi(l13), xs.lo[s][4 * k + 3], pl[1]);
+        ph[1] = fmaf(f16_hi(h13), xs.hi[s][4 * k + 3], ph[1]);
       }
-      const float sl = pl[0] + pl[1];
-      const float sh = ph[0] + ph[1];
+      const float sl = (pl[0] + pl[1]) * 0x1p24f;
+      const float sh = (ph[0] + ph[1]) * 0x1p24f;
       const float keep = ro.h ? sh : sl;
       const float send = ro.h ? sl : sh;
       const float qx = keep + xor1_f(send);
