@@ -97,22 +97,26 @@ __device__ __forceinline__ void load_x40_q8(X40Q8<S>& xs, const Q40Args& a, int 
 // (one per byte position) keep the fma chains short; they are added pairwise
 // at the end.
 __device__ __forceinline__ float block_dot_f32(const uint32_t qs[4], const float* x) {
-  // Two nibbles masked into the two halves of a dword are two fp16 denormals
-  // whose values are exactly q * 2^-24, and v_fma_mix_f32 converts an fp16
-  // half to fp32 inside the fma: one instruction a weight where a byte
-  // conversion and an fma took two.  Every partial sum is then exactly 2^-24
-  // times the one of fp32 weights (rounding commutes with a power-of-two
-  // scale away from underflow), and accumulator b still takes byte b's low,
-  // then high nibble of each dword in turn, so the result, scaled back by
-  // 2^24, equals the former byte-conversion sum bit for bit.
+  // Two nibbles masked into the two halves of a dword are two fp16 denormals,
+  // and v_fma_mix_f32 converts an fp16 half to fp32 inside the fma: one
+  // instruction a weight where a byte conversion and an fma took two.  A low
+  // nibble masked in place is exactly q * 2^-24; a high nibble masked in
+  // place is 16 q * 2^-24, against its activation (values 16..31 of the
+  // block) staged already scaled by 2^-4.  Every product is then exactly
+  // q * x * 2^-24, every partial sum exactly 2^-24 times the one of fp32
+  // weights (rounding commutes with a power-of-two scale away from
+  // underflow), and accumulator b still takes byte b's low, then high nibble
+  // of each dword in turn, so the result, scaled back by 2^24, equals the
+  // byte-conversion sum bit for bit.
   float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const uint32_t w = qs[k];
-    const uint32_t l02 = opaque_and(w, 0x000F000Fu);          // low nibbles of bytes 0, 2
-    const uint32_t h02 = opaque_and(w >> 4, 0x000F000Fu);     // high nibbles of bytes 0, 2
-    const uint32_t l13 = opaque_and(w >> 8, 0x000F000Fu);     // low nibbles of bytes 1, 3
-    const uint32_t h13 = opaque_and(w >> 12, 0x000F000Fu);    // high nibbles of bytes 1, 3
+    const uint32_t w8 = w >> 8;
+    const uint32_t l02 = opaque_and(w, 0x000F000Fu);     // low nibbles of bytes 0, 2
+    const uint32_t h02 = opaque_and(w, 0x00F000F0u);     // high nibbles of bytes 0, 2, x16
+    const uint32_t l13 = opaque_and(w8, 0x000F000Fu);    // low nibbles of bytes 1, 3
+    const uint32_t h13 = opaque_and(w8, 0x00F000F0u);    // high nibbles of bytes 1, 3, x16
     acc[0] = fmaf(f16_lo(l02), x[4 * k + 0], acc[0]);
     acc[0] = fmaf(f16_lo(h02), x[16 + 4 * k + 0], acc[0]);
     acc[1] = fmaf(f16_lo(l13), x[4 * k + 1], acc[1]);
@@ -291,7 +295,17 @@ __global__ __launch_bounds__(64 * WPB) void q4_0_gemv_kernel(Q40Args a) {
       const float bsum = group_sum_dpp<8>(part);
       if (g < kChunks) {
         uint8_t* pair = xl + (g >> 4) * kPairStride;
-        *(u32x4*)(pair + 16 * (g & 15)) = v;
+        // values 16..31 of each block, the high nibbles' partners, are staged
+        // scaled by 2^-4 (exact away from underflow; block_dot_f32 takes
+        // those nibbles in place, as 16 q); the block sums are unscaled
+        u32x4 vs = v;
+        if (g & 4) {
+          vs.x = __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, v0) * 0x1p-4f);
+          vs.y = __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, v1) * 0x1p-4f);
+          vs.z = __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, v2) * 0x1p-4f);
+          vs.w = __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, v3) * 0x1p-4f);
+        }
+        *(u32x4*)(pair + 16 * (g & 15)) = vs;
         if ((g & 7) == 7) *(float*)(pair + 256 + 4 * ((g & 15) >> 3)) = bsum;
       }
     }

@@ -102,7 +102,10 @@ __device__ __forceinline__ float sum16(const float (&v)[16]) {
   return (a[0] + a[1]) + (a[2] + a[3]);
 }
 
-// sum of x over the sub-block each lane owns (its half plus its partner's).
+// sum of x over the sub-block each lane owns (its half plus its partner's);
+// then the high-nibble partners are scaled by 2^-4 (exact away from
+// underflow), because tile_dot_xf32 takes the high nibbles in place, as
+// 16 q * 2^-24.
 template <int S>
 __device__ __forceinline__ void finish_x(XF32Slots<S>& xs, const LaneRole& ro) {
 #pragma unroll
@@ -111,6 +114,8 @@ __device__ __forceinline__ void finish_x(XF32Slots<S>& xs, const LaneRole& ro) {
     const float keep = ro.h ? sh : sl;
     const float send = ro.h ? sl : sh;
     xs.sj[s] = keep + xor1_f(send);
+#pragma unroll
+    for (int l = 0; l < 16; ++l) xs.hi[s][l] *= 0x1p-4f;
   }
 }
 
@@ -133,19 +138,23 @@ __device__ __forceinline__ void tile_dot_xf32(float (&part)[R], const WTile<S, R
       const int m = (int)((__builtin_amdgcn_ubfe(H.z, ro.sh_hi, ro.len_hi) << 4) |
                           __builtin_amdgcn_ubfe(a_m, ro.sh_m, ro.len_lo));
       // two partial sums per half (even and odd bytes).  The nibbles enter as
-      // fp16 denormals, exactly q * 2^-24, two to a dword, and v_fma_mix_f32
-      // converts them inside the fma (one instruction a weight instead of a
-      // byte conversion and an fma); each partial sum takes the same products
-      // in the same order as with fp32 weights, so it is exactly 2^-24 times
-      // that sum, and the scale back by 2^24 gives the same bits.
+      // fp16 denormals, two to a dword, and v_fma_mix_f32 converts them inside
+      // the fma (one instruction a weight instead of a byte conversion and an
+      // fma): a low nibble masked in place is exactly q * 2^-24, a high nibble
+      // masked in place 16 q * 2^-24 against its activation scaled by 2^-4
+      // (finish_x), so every product is exactly q * x * 2^-24.  Each partial
+      // sum takes the same products in the same order as with fp32 weights,
+      // so it is exactly 2^-24 times that sum, and the scale back by 2^24
+      // gives the same bits.
       float pl[2] = {0.0f, 0.0f}, ph[2] = {0.0f, 0.0f};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const uint32_t w = wt.qs[r][s][k];
-        const uint32_t l02 = opaque_and(w, 0x000F000Fu);         // low nibbles of bytes 0, 2
-        const uint32_t h02 = opaque_and(w >> 4, 0x000F000Fu);    // high nibbles of bytes 0, 2
-        const uint32_t l13 = opaque_and(w >> 8, 0x000F000Fu);    // low nibbles of bytes 1, 3
-        const uint32_t h13 = opaque_and(w >> 12, 0x000F000Fu);   // high nibbles of bytes 1, 3
+        const uint32_t w8 = w >> 8;
+        const uint32_t l02 = opaque_and(w, 0x000F000Fu);    // low nibbles of bytes 0, 2
+        const uint32_t h02 = opaque_and(w, 0x00F000F0u);    // high nibbles of bytes 0, 2, x16
+        const uint32_t l13 = opaque_and(w8, 0x000F000Fu);   // low nibbles of bytes 1, 3
+        const uint32_t h13 = opaque_and(w8, 0x00F000F0u);   // high nibbles of bytes 1, 3, x16
         pl[0] = fmaf(f16_lo(l02), xs.lo[s][4 * k + 0], pl[0]);
         ph[0] = fmaf(f16_lo(h02), xs.hi[s][4 * k + 0], ph[0]);
         pl[1] = fmaf(f16_lo(l13), xs.lo[s][4 * k + 1], pl[1]);
