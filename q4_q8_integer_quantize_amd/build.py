@@ -6,7 +6,10 @@ tests/native/abi_consumer that drives librz.so through include/rz.h alone.
 
 Every source is compiled by hipcc with packed-fp32 instructions disabled, IEEE
 fp32 division and no fast-math (the Q8_1 codes depend on correctly rounded
-division and ties-to-even rounding).
+division and ties-to-even rounding).  The fp32-activation kernels also need
+fp16 denormals preserved (they take 4-bit weights as fp16 denormals into
+v_fma_mix_f32), which is the default for these flags; do not add a flag that
+flushes fp16 denormals.
 """
 from __future__ import annotations
 
