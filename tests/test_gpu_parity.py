@@ -1040,6 +1040,42 @@ def test_q4k_gemv_xf32_matches_oracle(out_dim, n, in_dim):
     assert_within(y, y_ref, terms, "q4k_gemv fp32 x")
 
 
+def _wide_activation(seed, n):
+    """N(0,1) values scaled by 2^k, k uniform in -20..20, about 6% exact zeros."""
+    g = np.random.default_rng(seed)
+    x = g.standard_normal(n) * np.exp2(g.integers(-20, 21, n).astype(np.float64))
+    x[g.random(n) < 0.06] = 0.0
+    return x.astype(np.float32)
+
+
+@pytest.mark.parametrize("out_dim,in_dim", [(300, 4096), (33, 14336), (1024, 1024)])
+def test_q4k_gemv_xf32_wide_range_activation(out_dim, in_dim):
+    """Activations spanning 2^-20 .. 2^20 with zeros: the 4-bit weights enter
+    the fmas as fp16 denormals (q * 2^-24, high nibbles as 16 q * 2^-24 against
+    activations prescaled by 2^-4), exact in this range; every output stays
+    within the bound of the float64 definition."""
+    banner("q4k_gemv_xf32 wide range", out_dim, in_dim)
+    blob = synth.q4k_weights(synth.rng(96, in_dim), out_dim, in_dim)
+    x = _wide_activation(97 + in_dim, in_dim)
+    y = gpu_q4k_xf32(blob, x)
+    y_ref, terms = oracle.gemv_q4k_f32(blob, x)
+    assert_within(y, y_ref, terms, "q4k_gemv fp32 x, wide range")
+
+
+@pytest.mark.parametrize("out_dim,in_dim", [(257, 1024), (9, 10240), (130, 4096)])
+def test_q4_0_fp32_wide_range_activation(out_dim, in_dim):
+    """The Q4_0 fp32-activation path on activations spanning 2^-20 .. 2^20 with
+    zeros (its nibbles also enter the fmas as fp16 denormals, with the staged
+    high-nibble activations prescaled by 2^-4): within the bound of the
+    float64 definition."""
+    banner("q4_0 fp32 wide range", out_dim, in_dim)
+    blob = synth.q4_0_weights(synth.rng(98, in_dim), out_dim, in_dim)
+    x = _wide_activation(99 + in_dim, in_dim)
+    y = gpu_q4_0(blob, x, 0)
+    y_ref, terms = oracle.gemv_q4_0_f32(blob, x)
+    assert_within(y, y_ref, terms, "q4_0 fp32 x, wide range")
+
+
 @pytest.mark.parametrize("out_dim,in_dim", [(5, 256), (64, 1024), (300, 4096), (40, 14336)])
 def test_q4k_gemv_xf32_integer_exact_bit_exact(out_dim, in_dim):
     """d = dmin = 1 and small integer activations: every product and partial sum
